@@ -1,0 +1,515 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (CPU only).
+
+Each test ties one part of the oracle to something other than itself: a library routine for a
+special case (numpy's Philox, scipy's softmax, an optimiser for Theorem 12), brute force on tiny
+inputs, the lossless theorem integrated exactly over the uniforms with the oracle treated as a
+black box, the pages' worked example (Theorem 19) and closed forms.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.optimize
+import scipy.special
+import scipy.stats
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------------------------------
+# Philox4x64-10 against numpy's independent implementation
+# ------------------------------------------------------------------------------------------
+def _numpy_philox_block(ctr, key):
+    """numpy's Philox4x64 increments its counter before each block: start one below."""
+    c = [int(x) for x in ctr]
+    prev = list(c)
+    for i in range(4):  # subtract one with borrow
+        if prev[i] > 0:
+            prev[i] -= 1
+            break
+        prev[i] = (1 << 64) - 1
+    bg = np.random.Philox(key=0)
+    st = bg.state
+    st["state"]["counter"] = np.array(prev, dtype=np.uint64)
+    st["state"]["key"] = np.array([int(k) for k in key], dtype=np.uint64)
+    st["buffer_pos"] = 4
+    bg.state = st
+    return bg.random_raw(4)
+
+
+@pytest.mark.parametrize("ctr,key", [
+    ([1, 0, 0, 0], [1, 2]),
+    ([0, 0, 0, 0], [0, 0]),
+    ([5, 7, 11, 13], [0xDEADBEEF, 42]),
+    ([0, 1, 0, 0], [0xC0FFEE03, 0]),
+    ([(1 << 64) - 1, (1 << 64) - 1, 3, 9], [(1 << 64) - 1, 1 << 63]),
+    ([123456789, 15, 5, 0], [0xC0FFEE01, 0]),
+])
+def test_philox_matches_numpy(ctr, key):
+    assert (oracle.philox4x64_10(ctr, key) == _numpy_philox_block(ctr, key)).all()
+
+
+def test_uniforms_open_interval_and_uniform():
+    U = oracle.uniforms(0xC0FFEE01, 0, 20000, 4)
+    assert U.min() > 0.0 and U.max() < 1.0
+    for lane in range(3):
+        counts, _ = np.histogram(U[:, :, lane].ravel(), bins=64, range=(0.0, 1.0))
+        assert scipy.stats.chisquare(counts).pvalue > 1e-4
+
+
+# ------------------------------------------------------------------------------------------
+# Processing: temperature, top-k, softmax, nucleus
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [0.25, 0.8, 1.0, 2.5])
+def test_softmax_matches_scipy(T):
+    rng = np.random.default_rng(1)
+    z = rng.normal(0, 3, 4096)
+    p, bad, _, n = oracle.process_row(z, T, 0, 1.0)
+    assert not bad and n == 4096
+    # the temperature is an fp32 request parameter
+    np.testing.assert_allclose(p, scipy.special.softmax(z / float(np.float32(T))), rtol=1e-12, atol=1e-300)
+
+
+def _brute_order(z):
+    return sorted(range(len(z)), key=lambda i: (-z[i], i))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_and_nucleus_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    V = 9
+    z = rng.integers(-3, 3, V).astype(np.float64)  # integer logits force ties
+    for T in (0.7, 1.0):
+        for top_k in (0, 1, 3, 5, 9, 12):
+            for top_p in (0.1, 0.5, 0.77, 0.95, 1.0):
+                p, bad, _, _ = oracle.process_row(z, T, top_k, top_p)
+                order = _brute_order(z)
+                kept = order[: top_k] if 0 < top_k < V else order
+                Tf = float(np.float32(T))
+                e = {i: np.exp((z[i] - z[order[0]]) / Tf) for i in kept}
+                S = sum(e.values())
+                if top_p < 1.0:
+                    cum, nuc = 0.0, []
+                    for i in kept:
+                        nuc.append(i)
+                        cum += e[i]
+                        if cum >= float(np.float32(top_p)) * S:
+                            break
+                else:
+                    nuc = kept
+                Sn = sum(e[i] for i in nuc)
+                ref = np.zeros(V)
+                for i in nuc:
+                    ref[i] = e[i] / Sn
+                np.testing.assert_allclose(p, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_bad_rows():
+    p, bad, _, _ = oracle.process_row([0.0, np.nan, 1.0], 1.0, 0, 1.0)
+    assert bad
+    p, bad, _, _ = oracle.process_row([0.0, np.inf, 1.0], 1.0, 0, 1.0)
+    assert bad
+    p, bad, _, _ = oracle.process_row([-np.inf, -np.inf], 1.0, 0, 1.0)
+    assert bad
+    p, bad, _, n = oracle.process_row([-np.inf, 3.0, -np.inf], 1.0, 0, 0.5)
+    assert not bad and n == 1 and p[1] == 1.0
+
+
+# ------------------------------------------------------------------------------------------
+# Saguaro sampling: Theorem 19 worked example, and Theorem 15 monotonicity
+# ------------------------------------------------------------------------------------------
+def test_theorem19_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "theorem19.json")))
+    pt = np.array(g["p_target"])
+    pd = np.array(g["p_draft"])
+    C = g["C_num"] / g["C_den"]
+    # logits = ln p at T = 1 reproduce p exactly up to rounding
+    q, *_ = oracle.process_row(np.log(pt), 1.0, 0, 1.0)
+    p, *_ = oracle.process_row(np.log(pd), 1.0, 0, 1.0)
+    pp, Z, ids, deg = oracle.downweight_probs(np.log(pd), p, g["F"], C)
+    assert not deg
+    assert sorted(ids.tolist()) == [0, 1]
+    np.testing.assert_allclose(pp, g["p_draft_after"], atol=1e-14)
+    np.testing.assert_allclose(Z, 1.0 / 3.0, atol=1e-14)
+    assert abs(np.minimum(p, q).sum() - g["alpha_before"]) < 1e-14
+    assert abs(np.minimum(pp, q).sum() - g["alpha_after"]) < 1e-14
+    assert np.flatnonzero(np.maximum(q - p, 0) > 1e-12).tolist() == g["residual_support_before"]
+    assert np.flatnonzero(np.maximum(q - pp, 0) > 1e-12).tolist() == g["residual_support_after"]
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_theorem15_monotone_in_C(seed):
+    rng = np.random.default_rng(200 + seed)
+    V, F = 64, 4
+    zq = rng.normal(0, 2, V)
+    zp = zq + rng.normal(0, 1, V)
+    q, *_ = oracle.process_row(zq, 1.0, 0, 1.0)
+    p, *_ = oracle.process_row(zp, 1.0, 0, 1.0)
+    mass_on_S, frac_on_S = [], []
+    for C in np.linspace(1.0, 0.0, 21):
+        pp, Z, ids, deg = oracle.downweight_probs(zp, p, F, C)
+        assert not deg
+        r = np.maximum(q - pp, 0)
+        mass_on_S.append(r[ids].sum())
+        frac_on_S.append(r[ids].sum() / r.sum())
+    # residual mass (and its share) on the downweighted set never decrease as C -> 0
+    assert np.all(np.diff(mass_on_S) >= -1e-15)
+    assert np.all(np.diff(frac_on_S) >= -1e-15)
+    assert mass_on_S[-1] > mass_on_S[0]
+
+
+def test_downweight_set_is_top_F_with_mass():
+    z = np.array([1.0, 3.0, 3.0, -np.inf, 2.0, 0.5])
+    p, *_ = oracle.process_row(z, 1.0, 0, 1.0)
+    pp, Z, ids, _ = oracle.downweight_probs(z, p, 3, 0.5)
+    assert ids.tolist() == [1, 2, 4]        # ties by id, -inf carries no mass
+    # nucleus leaves fewer than F tokens with mass: the set stops there
+    p2, *_ = oracle.process_row(z, 1.0, 0, 0.3)
+    _, _, ids2, _ = oracle.downweight_probs(z, p2, 3, 0.5)
+    assert ids2.tolist()[0] == 1 and ids2.tolist()[2] == -1
+
+
+# ------------------------------------------------------------------------------------------
+# Lossless theorem by exact integration over the uniforms (oracle as a black box)
+# ------------------------------------------------------------------------------------------
+def _tile(a, n):
+    return np.ascontiguousarray(np.repeat(a[None], n, axis=0))
+
+
+def _bisect(decide, n, iters=64):
+    """Per probe, sup{x in (0,1): decide(x) is True}, decide monotone (True for small x)."""
+    lo = np.zeros(n)
+    hi = np.ones(n)
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        d = decide(mid)
+        lo = np.where(d, mid, lo)
+        hi = np.where(d, hi, mid)
+    # never True -> 0, never False -> 1, else the bracket's midpoint (width 2^-64)
+    return np.where(lo == 0.0, 0.0, np.where(hi == 1.0, 1.0, 0.5 * (lo + hi)))
+
+
+def exact_law(zd, zt, T=1.0, top_k=0, top_p=1.0, F=0, C=1.0):
+    """Law of the oracle's output over s ~ p' and the uniforms, integrated exactly.
+
+    Returns (law, p', q): law maps (k, emitted tokens) -> probability.
+    """
+    K, V = zd.shape
+    # inputs are given to the oracle as fp32; the distributions below come from the same values
+    q = [oracle.process_row(zt[j].astype(np.float32).astype(np.float64), T, top_k, top_p)[0] for j in range(K + 1)]
+    pp = []
+    for j in range(K):
+        zz = zd[j].astype(np.float32).astype(np.float64)
+        pj = oracle.process_row(zz, T, top_k, top_p)[0]
+        pp.append(oracle.downweight_probs(zz, pj, F, C)[0])
+    seqs = [s for s in itertools.product(range(V), repeat=K) if np.prod([pp[j][s[j]] for j in range(K)]) > 0]
+    N = len(seqs)
+    tok = np.array(seqs, dtype=np.int32)
+    prm = oracle.params_array(T, top_k, top_p, B=N)
+    D = _tile(zd.astype(np.float32), N)
+    Tt = _tile(zt.astype(np.float32), N)
+    ps = np.array([np.prod([pp[j][s[j]] for j in range(K)]) for s in seqs])
+
+    def run(U, tokens=tok):
+        n = U.shape[0]
+        return oracle.verify(D[:n], Tt[:n], oracle.FP32, K, prm[:n], F=F, C=C, tokens=tokens, U=U)
+
+    # acceptance thresholds a[n, j] with the earlier positions accepting
+    a = np.zeros((N, K))
+    for j in range(K):
+        def dec(x, j=j):
+            U = np.full((N, K + 1, 3), 0.5)
+            U[:, :j, 0] = np.maximum(a[:, :j] * 0.5, 1e-300)
+            U[:, j, 0] = np.maximum(x, 1e-300)
+            return run(U).k > j
+        a[:, j] = _bisect(dec, N)
+    # law of t* as a function of v at each stopping position m: cut points by bisection
+    law = {}
+    for m in range(K + 1):
+        reach = np.prod(a[:, :m], axis=1) * ((1.0 - a[:, m]) if m < K else 1.0)
+        idx = np.flatnonzero(reach * ps > 0)
+        if len(idx) == 0:
+            continue
+        n_i = len(idx)
+        cuts = np.zeros((n_i, V + 1))
+        cuts[:, V] = 1.0
+        for y in range(V - 1):
+            def dec(x, y=y):
+                U = np.full((n_i, K + 1, 3), 0.5)
+                U[:, :m, 0] = np.maximum(a[idx, :m] * 0.5, 1e-300)
+                if m < K:
+                    U[:, m, 0] = 0.5 * (1.0 + a[idx, m])
+                U[:, m, 1] = np.maximum(x, 1e-300)
+                r = oracle.verify(D[:n_i], Tt[:n_i], oracle.FP32, K, prm[:n_i], F=F, C=C,
+                                  tokens=tok[idx], U=U)
+                assert (r.k == m).all()
+                return r.t <= y
+            cuts[:, y + 1] = _bisect(dec, n_i)
+        width = np.diff(cuts, axis=1)
+        for row, n in enumerate(idx):
+            for y in range(V):
+                w = ps[n] * reach[n] * width[row, y]
+                if w > 0:
+                    key = (m,) + tuple(int(x) for x in tok[n, :m]) + (y,)
+                    law[key] = law.get(key, 0.0) + w
+    return law, pp, q
+
+
+def _check_lossless(law, pp, q, K, V):
+    total = sum(law.values())
+    assert abs(total - 1.0) < 1e-12
+    # each depth's emitted token, given the output reaches that depth, has law q_j
+    for d in range(K + 1):
+        reach = 0.0
+        dist = np.zeros(V)
+        for key, w in law.items():
+            m = key[0]
+            if m >= d:
+                dist[key[1 + d]] += w
+                reach += w
+        if reach > 1e-9:
+            assert np.abs(dist / reach - q[d]).sum() < 1e-11, (d, dist / reach, q[d])
+    # the joint law in closed form: prod_{i<m} min(p', q)(y_i) * (q_m - p'_m)+(y_m), or q_K at m = K
+    for key, w in law.items():
+        m, ys = key[0], key[1:]
+        ref = np.prod([min(pp[i][ys[i]], q[i][ys[i]]) for i in range(m)])
+        ref *= max(q[m][ys[m]] - pp[m][ys[m]], 0.0) if m < K else q[K][ys[K]]
+        assert abs(w - ref) < 1e-12
+    # acceptance-length law: P(k >= j) = prod_{i<j} alpha_i, alpha_i = sum min(p'_i, q_i)
+    alpha = [np.minimum(pp[i], q[i]).sum() for i in range(K)]
+    for j in range(K + 1):
+        pk = sum(w for key, w in law.items() if key[0] >= j)
+        assert abs(pk - np.prod(alpha[:j])) < 1e-12
+
+
+@pytest.mark.parametrize("V,K,T,top_k,top_p,F,C,seed", [
+    (4, 1, 1.0, 0, 1.0, 0, 1.0, 0),
+    (8, 2, 1.0, 0, 1.0, 0, 1.0, 1),
+    (4, 3, 0.8, 0, 1.0, 0, 1.0, 2),
+    (5, 2, 1.0, 3, 1.0, 0, 1.0, 3),
+    (6, 2, 1.0, 0, 0.8, 0, 1.0, 4),
+    (5, 2, 0.9, 0, 1.0, 2, 0.3, 5),
+    (6, 2, 1.0, 4, 0.9, 1, 0.5, 6),
+])
+def test_lossless_exact_enumeration(V, K, T, top_k, top_p, F, C, seed):
+    rng = np.random.default_rng(300 + seed)
+    zt = rng.normal(0, 1.5, (K + 1, V))
+    zd = zt[:K] + rng.normal(0, 0.8, (K, V))
+    law, pp, q = exact_law(zd, zt, T, top_k, top_p, F, C)
+    _check_lossless(law, pp, q, K, V)
+
+
+def test_mass_identity_random_rows():
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        V = int(rng.integers(2, 3000))
+        zq = rng.normal(0, 2, V)
+        zp = zq + rng.normal(0, 1, V)
+        T = float(rng.uniform(0.3, 1.5))
+        tk = int(rng.integers(0, V + 2))
+        tp = float(rng.uniform(0.2, 1.0))
+        q, *_ = oracle.process_row(zq, T, tk, tp)
+        p, *_ = oracle.process_row(zp, T, tk, tp)
+        pp, *_ = oracle.downweight_probs(zp, p, int(rng.integers(0, 6)), float(rng.uniform(0, 1)))
+        for d in (p, pp):
+            assert abs(np.minimum(d, q).sum() + np.maximum(q - d, 0).sum() - 1.0) < 1e-13
+
+
+def test_chi_square_monte_carlo():
+    """10^6 Philox-driven rounds with sampled draft tokens against the exact law of (k, t*)."""
+    rng = np.random.default_rng(11)
+    V, K, N = 6, 2, 1_000_000
+    zt = rng.normal(0, 1.2, (K + 1, V)).astype(np.float32)
+    zd = (zt[:K] + rng.normal(0, 0.8, (K, V))).astype(np.float32)
+    law, pp, q = exact_law(zd.astype(np.float64), zt.astype(np.float64), 1.0, 0, 1.0, 1, 0.5)
+    _check_lossless(law, pp, q, K, V)
+    prm = oracle.params_array(1.0, 0, 1.0, B=N)
+    r = oracle.verify(_tile(zd, N), _tile(zt, N), oracle.FP32, K, prm, F=1, C=0.5, tokens=None,
+                      seed=0x5EED, round_=3)
+    exp = np.zeros((K + 1, V))
+    for key, w in law.items():
+        exp[key[0], key[-1]] += w
+    obs = np.zeros((K + 1, V))
+    np.add.at(obs, (r.k, r.t), 1)
+    mask = exp.ravel() > 0
+    assert obs.ravel()[~mask].sum() == 0
+    stat = scipy.stats.chisquare(obs.ravel()[mask], exp.ravel()[mask] * N)
+    assert stat.pvalue > 1e-4, stat
+
+
+# ------------------------------------------------------------------------------------------
+# Greedy verification
+# ------------------------------------------------------------------------------------------
+def test_greedy_longest_argmax_prefix():
+    rng = np.random.default_rng(5)
+    V, K, B = 50, 4, 64
+    zt = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    zd = (zt[:, :K] + rng.normal(0, 0.5, (B, K, V))).astype(np.float32)
+    amax = zt.argmax(axis=2)
+    tok = np.zeros((B, K), np.int32)
+    want_k = rng.integers(0, K + 1, B)
+    for b in range(B):
+        for j in range(K):
+            tok[b, j] = amax[b, j] if j < want_k[b] else (amax[b, j] + 1 + rng.integers(0, V - 1)) % V
+    prm = oracle.params_array(0.0, 0, 1.0, B=B)
+    r = oracle.verify(zd, zt, oracle.FP32, K, prm, tokens=tok, seed=1)
+    assert (r.k == want_k).all()
+    assert (r.t == amax[np.arange(B), want_k]).all()
+    # the stochastic rule at a tiny temperature with well separated logits reduces to the same
+    zt2 = zt.copy()
+    zd2 = zd.copy()
+    for b in range(B):
+        for j in range(K + 1):
+            zt2[b, j, amax[b, j]] += 60.0
+    prm2 = oracle.params_array(0.05, 0, 1.0, B=B)
+    r2 = oracle.verify(zd2, zt2, oracle.FP32, K, prm2, tokens=tok, seed=1)
+    assert (r2.k == want_k).all() and (r2.t == r.t).all()
+
+
+def test_greedy_samples_draft_argmax():
+    rng = np.random.default_rng(6)
+    V, K, B = 40, 3, 16
+    zt = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    zd = zt[:, :K].copy()
+    prm = oracle.params_array(0.0, 0, 1.0, B=B)
+    r = oracle.verify(zd, zt, oracle.FP32, K, prm, tokens=None, seed=1)
+    assert (r.tokens == zd.argmax(axis=2)).all()
+    assert (r.k == K).all()
+
+
+# ------------------------------------------------------------------------------------------
+# Status bits and near-tie flags
+# ------------------------------------------------------------------------------------------
+def test_status_and_flags():
+    V, K = 4, 2
+    zt = np.log(np.array([[0.25, 0.25, 0.25, 0.25], [0.4, 0.3, 0.2, 0.1], [0.1, 0.2, 0.3, 0.4]], np.float64))
+    zd = np.log(np.array([[0.5, 0.2, 0.2, 0.1], [0.1, 0.2, 0.3, 0.4]], np.float64))
+    prm = oracle.params_array(1.0, 0, 1.0, B=1)
+    U = np.full((1, K + 1, 3), 0.5)
+    # u * p(s0) = 0.5 * 0.5 = 0.25 = q(s0): a near tie of the acceptance test
+    r = oracle.verify(zd[None].astype(np.float32), zt[None].astype(np.float32), oracle.FP32, K, prm,
+                      tokens=[[0, 1]], U=U)
+    assert r.flags[0] & oracle.FL_NEAR_ACCEPT
+    # invalid token
+    r = oracle.verify(zd[None].astype(np.float32), zt[None].astype(np.float32), oracle.FP32, K, prm,
+                      tokens=[[0, 9]], U=U)
+    assert r.status[0] & oracle.ST_BAD_TOKEN and r.k[0] == 0 and r.t[0] == -1
+    # NaN logit
+    zbad = zt.copy()
+    zbad[1, 2] = np.nan
+    r = oracle.verify(zd[None].astype(np.float32), zbad[None].astype(np.float32), oracle.FP32, K, prm,
+                      tokens=[[0, 1]], U=U)
+    assert r.status[0] & oracle.ST_BAD_LOGIT and r.t[0] == -1
+    # token outside the draft's support (top-k 1 keeps token 0 only): accepted iff q(s) > 0
+    prm1 = oracle.params_array(1.0, 1, 1.0, B=1)
+    r = oracle.verify(zd[None].astype(np.float32), zt[None].astype(np.float32), oracle.FP32, K, prm1,
+                      tokens=[[3, 1]], U=U)
+    assert r.status[0] & oracle.ST_OUTSIDE_DRAFT_SUPPORT
+    assert r.k[0] == 0   # q_0 under top-k 1 keeps token 0 only, so q(3) = 0
+    # identical draft and target rows: never a rejection, bonus token from q_K
+    r = oracle.verify(zt[None, :K].astype(np.float32), zt[None].astype(np.float32), oracle.FP32, K, prm,
+                      tokens=[[0, 1]], U=np.full((1, K + 1, 3), 0.999))
+    assert r.k[0] == K and r.W[0] == 0.0
+
+
+# ------------------------------------------------------------------------------------------
+# Theorem 12 fan-out
+# ------------------------------------------------------------------------------------------
+def test_fanout_golden_and_closed_form():
+    g = json.load(open(os.path.join(GOLDEN, "fanout.json")))
+    for c in g["cases"]:
+        real, ints = oracle.fanout(c["K"], c["budget"], c["a"], c["r"])
+        assert ints.tolist() == c["F_int"]
+        assert abs(real.sum() - c["budget"]) < 1e-12
+        assert ints.sum() == c["budget"]
+
+
+@pytest.mark.parametrize("K,budget,a,r", [(5, 32, 0.7, 1.0), (4, 23, 0.6, 0.5), (7, 100, 0.85, 2.0), (3, 8, 0.3, 1.0)])
+def test_fanout_is_the_optimum(K, budget, a, r):
+    """F maximises sum_k P_k (1 - F_k^-r) under sum F_k = B, P_k = a^k (1-a) (k<K), a^K."""
+    real, ints = oracle.fanout(K, budget, a, r)
+    P = np.array([a ** k * (1 - a) for k in range(K)] + [a ** K])
+    assert abs(P.sum() - 1.0) < 1e-12
+    obj = lambda F: -np.sum(P * (1.0 - np.power(F, -r)))
+    res = scipy.optimize.minimize(obj, np.full(K + 1, budget / (K + 1)), method="SLSQP",
+                                  bounds=[(1e-6, budget)] * (K + 1),
+                                  constraints=[{"type": "eq", "fun": lambda F: F.sum() - budget}],
+                                  options={"ftol": 1e-14, "maxiter": 1000})
+    assert res.success
+    np.testing.assert_allclose(real, res.x, rtol=2e-4)
+    assert obj(real) <= obj(res.x) + 1e-12
+    assert ints.sum() == budget and np.all(np.abs(ints - real) < 1.0)
+
+
+# ------------------------------------------------------------------------------------------
+# Cache build / lookup / branch reuse
+# ------------------------------------------------------------------------------------------
+def test_cache_build_brute_force():
+    rng = np.random.default_rng(9)
+    B, K, V = 5, 3, 12
+    draft = rng.integers(-2, 3, (B, K + 1, V)).astype(np.float32)  # many ties
+    draft[0, 1, 4] = np.nan
+    tok = rng.integers(0, V, (B, K)).astype(np.int32)
+    fan = np.array([3, 2, 4, 5], np.int32)
+    cache = oracle.cache_build(draft, oracle.FP32, K, tok, fan)
+    for b in range(B):
+        off = 0
+        for k in range(K + 1):
+            z = draft[b, k]
+            order = sorted([i for i in range(V) if not np.isnan(z[i])], key=lambda i: (-z[i], i))
+            order += [i for i in range(V) if np.isnan(z[i])]
+            if k < K:
+                order = [i for i in order if i != tok[b, k]]
+            assert cache[b, off:off + fan[k]].tolist() == order[: fan[k]]
+            off += fan[k]
+
+
+def test_cache_lookup_definition():
+    fan = np.array([2, 1, 3], np.int32)  # K = 2, budget 6
+    cache = np.array([[10, 11, 20, 30, 31, 32], [5, 6, 7, 8, 9, 4]], np.int32)
+    slot, hit, batch = oracle.cache_lookup(0, cache, fan, 2, 2, k=[2, 1], t=[31, 7])
+    assert slot.tolist() == [4, 2] and hit.tolist() == [1, 1] and batch.tolist() == [2, 1]
+    slot, hit, batch = oracle.cache_lookup(0, cache, fan, 2, 2, k=[0, 1], t=[20, 7])
+    assert slot.tolist() == [-1, 2] and batch.tolist() == [1, 0]
+
+
+def test_branch_reuse_definition():
+    kappa, gamma = 3, 3
+    br = np.array([[[1, 2, 3], [1, 5, 6], [1, 2, 9]],
+                   [[4, 4, 4], [7, 7, 7], [4, 8, 8]]], np.int32)
+    shape = np.array([kappa, gamma], np.int32)
+    # request 0: chain 0 accepted 2 then correction 9 -> branch 2; request 1: k=1, t*=8 -> branch 2
+    k = np.array([[2, 0, 0], [1, 0, 0]], np.int32)
+    t = np.array([[9, 0, 0], [8, 0, 0]], np.int32)
+    slot, hit, batch = oracle.cache_lookup(1, br, shape, 0, 2, k, t)
+    assert slot.tolist() == [2, 2] and batch.tolist() == [2, 1]
+    k[0, 0], t[0, 0] = 1, 7   # (1, 7) is no path
+    k[1, 0] = gamma           # every token accepted: FULL
+    slot, hit, batch = oracle.cache_lookup(1, br, shape, 0, 2, k, t)
+    assert slot.tolist() == [-1, -2] and hit.tolist() == [0, 0]
+
+
+def test_corollary16_whole_batch_hit():
+    """Requests hit independently, so the all-hit frequency is the product of the hit rates."""
+    rng = np.random.default_rng(12)
+    B, K, V, R = 3, 2, 24, 3000
+    zt = rng.normal(0, 1.5, (B, K + 1, V)).astype(np.float32)
+    zd = np.concatenate([zt[:, :K] + rng.normal(0, 0.6, (B, K, V)), zt[:, K:] + rng.normal(0, 0.6, (B, 1, V))],
+                        axis=1).astype(np.float32)
+    fan = np.array([3, 2, 2], np.int32)
+    prm = oracle.params_array(1.0, 0, 1.0, B=B)
+    hits = np.zeros((R, B), bool)
+    for rd in range(R):
+        r = oracle.verify(zd[:, :K], zt, oracle.FP32, K, prm, F=2, C=0.3, tokens=None, seed=77, round_=rd)
+        cache = oracle.cache_build(zd, oracle.FP32, K, r.tokens, fan)
+        _, hit, batch = oracle.cache_lookup(0, cache, fan, K, B, r.k, r.t)
+        hits[rd] = hit.astype(bool)
+        assert batch[1] == int(hit.all())
+    ph = hits.mean(axis=0)
+    allhit = hits.all(axis=1).mean()
+    se = np.sqrt(np.prod(ph) * (1 - np.prod(ph)) / R)
+    assert abs(allhit - np.prod(ph)) < 5 * se + 1e-3
