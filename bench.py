@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Throughput of the verification + Saguaro outcome-cache hot path on one MI355X.
+
+One step = the whole path over one batch: spec_verify (temperature / nucleus processing of 16
+requests x (5 draft + 6 target) rows of V = 128256 bf16 logits, sigma_{4, 0.3} downweight,
+acceptance scan, residual / bonus sampling), saguaro_cache_build (fan-out 32 over the 6 draft
+rows) and saguaro_cache_lookup.  Inputs are synthetic (Zipf-shaped rows, see
+lossless_speculative_sampling_amd/synth.py) and already resident in HBM; R copies of the batch
+totalling more than twice the 256 MB Infinity Cache are rotated so reads come from HBM.
+
+Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lossless_speculative_sampling_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_bytes_per_launch):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds_target=15.0):
+    """The oracle as it stands on the host cores, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    nthreads = oracle.threads_used(0)
+    wc = w.without_cache_row()
+    fan = np.array(oracle.fanout(w.K, w.budget, w.a, w.r)[1], np.int32)
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        r = oracle.verify(wc.draft, wc.target, w.dtype, w.K, w.params(), F=w.F, C=float(np.float32(w.C)),
+                          tokens=None, seed=w.seed, round_=steps, nthreads=nthreads)
+        cache = oracle.cache_build(w.draft, w.dtype, w.K, r.tokens, fan, nthreads=nthreads)
+        oracle.cache_lookup(0, cache, fan, w.K, w.B, r.k, r.t)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds_target or steps >= 50:
+            break
+    return {"value": w.B * w.K * steps / el, "unit": "verified positions/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{steps} full steps (B={w.B}, K={w.K}, V={w.V}: verify with sampled draft tokens + cache "
+                      f"build + lookup) in {el:.1f} s, fp64, std::thread over requests/rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lossless_speculative_sampling_amd import capi, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
+    B, K, V = w.B, w.K, w.V
+    step_bytes = int(w.draft.nbytes + w.target.nbytes)          # every logit once (cache row included)
+    verify_bytes = int(B * K * V * 2 + B * (K + 1) * V * 2)     # rows spec_verify reads
+    copies = max(2, -(-2 * MALL_BYTES // step_bytes) + 1)
+    d0 = torch.from_numpy(w.draft.view(np.int16)).to(dev)
+    t0 = torch.from_numpy(w.target.view(np.int16)).to(dev)
+    drafts = [d0] + [d0.clone() for _ in range(copies - 1)]
+    targets = [t0] + [t0.clone() for _ in range(copies - 1)]
+    prm = capi.params_tensor(w.temperature, w.top_k, w.top_p, device=dev)
+    tokens = torch.zeros((B, K), dtype=torch.int32, device=dev)
+    ws = torch.empty(capi.spec_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    out = capi.VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                         torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                         tokens)
+    # draft tokens: the drafter's proposals, sampled once from the processed draft (untimed)
+    capi.spec_verify(d0, t0, K, prm, tokens, F=w.F, C=w.C, seed=w.seed, flags=capi.SPEC_SAMPLE_DRAFT,
+                     workspace=ws, out=out)
+    torch.cuda.synchronize()
+    fan = capi.saguaro_fanout(K, w.budget, w.a, w.r)
+    cache = torch.empty((B, w.budget), dtype=torch.int32, device=dev)
+    import ctypes
+    L = capi.load().cdll
+    fan_c = (ctypes.c_int32 * (K + 1))(*fan)
+    slot = torch.empty(B, dtype=torch.int32, device=dev)
+    hit = torch.empty(B, dtype=torch.uint8, device=dev)
+    batch = torch.empty(2, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i, ev=None):
+        d, t = drafts[i % copies], targets[i % copies]
+        if ev is not None:
+            ev[0].record()
+        rc = L.spec_verify(d.data_ptr(), K + 1, t.data_ptr(), capi.SPEC_BF16, B, K, V, prm.data_ptr(), w.F,
+                           ctypes.c_float(w.C), tokens.data_ptr(), w.seed, i, 0, out.k.data_ptr(),
+                           out.tstar.data_ptr(), out.resid_mass.data_ptr(), out.status.data_ptr(), ws.data_ptr(),
+                           ws.numel(), stream)
+        if ev is not None:
+            ev[1].record()
+        rc |= L.saguaro_cache_build(d.data_ptr(), capi.SPEC_BF16, B, K, V, tokens.data_ptr(), w.budget, w.a, w.r,
+                                    None, cache.data_ptr(), stream)
+        rc |= L.saguaro_cache_lookup(0, cache.data_ptr(), ctypes.cast(fan_c, ctypes.c_void_p), K, B,
+                                     out.k.data_ptr(), out.tstar.data_ptr(), slot.data_ptr(), hit.data_ptr(),
+                                     batch.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"library call failed rc={rc}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # whole-step timing
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    # the dominant kernel (spec_verify) alone, bracketed per launch on the same stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    vt = sorted(a.elapsed_time(b) for a, b in evs)
+    verify_ms = sum(vt) / len(vt)
+
+    achieved = verify_bytes / (verify_ms * 1e-3) / 1e9
+    positions = B * K
+    res = {
+        "metric": "verified positions/sec and achieved HBM GB/s (% peak), B=16 K=5 V=128256 bf16",
+        "value": positions / (ms_step * 1e-3),
+        "unit": "verified positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "saguaro verify + outcome cache: B=16 requests, K=5, V=128256 bf16 Zipf logits, "
+                               "top-p 0.95, T~U[0.6,1], sigma F=4 C=0.3, fan-out budget 32 (a=0.7, r=1)",
+                   "B": B, "K": K, "V": V, "logit_bytes_per_step": step_bytes, "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "kernel": "spec_verify", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(verify_bytes),
+                     "algorithmic_bytes_per_launch": verify_bytes, "avg_launch_ms": verify_ms,
+                     "p10_ms": vt[len(vt) // 10], "p90_ms": vt[(len(vt) * 9) // 10]},
+        "secondary": {"logit_GBps_whole_step": step_bytes / (ms_step * 1e-3) / 1e9,
+                      "committed_tokens_per_s": float(out.k.float().add(1).sum().item()) / (ms_step * 1e-3)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+/* specverify.h - C ABI of the MI355X (gfx950) speculative-sampling verification library.
+ *
+ * The library computes, on one GPU, the data-parallel hot path of lossless speculative sampling
+ * and of Saguaro's outcome cache:
+ *
+ *   spec_verify          - per request: temperature / top-k / nucleus processing of draft and
+ *                          target rows, optional Saguaro downweight sigma_{F,C} of the draft, the
+ *                          min(1, q/p) acceptance scan with first-rejection cutoff, and the
+ *                          correction token from the normalised residual (q - p)+ (or the bonus
+ *                          token from the target's extra position when every draft token is
+ *                          accepted).  Outputs the verification outcome (k, t*).
+ *   saguaro_downweight   - sigma_{F,C} of the processed draft rows (the downweighted set, its
+ *                          normaliser and, optionally, the full distribution).
+ *   saguaro_cache_build  - the geometric fan-out F_k (Theorem 12) and, per verify depth k, the
+ *                          F_k guessed outcome tokens.
+ *   saguaro_cache_lookup - hit / miss of the verified outcome (k, t*) against the cache, or the
+ *                          branch-reuse test of a branch-complete tree.
+ *
+ * Sources (notation p = draft, q = target, as on the DeepMind page):
+ *   [SpS]   "Accelerating LLM Decoding with Speculative Sampling" (DeepMind, arXiv 2302.01318),
+ *           knowledge-base reading, sections 1, 3 and 6.
+ *   [SSD]   "Speculative Speculative Decoding" reading notes, sections 1.3, 2.2, 4.3, 4.4, 5.1, 7.1.
+ *   [SSD-H] hyper.ai summary of arXiv 2603.03251, "Method" (fan-out closed form, sigma_{F,C}).
+ *   [MSD]   "Mirror Speculative Decoding" reading notes, sections 2, 3.2 and 3.3.
+ *
+ * Conventions for every entry point:
+ *   - Array pointers are HIP device memory owned by the caller (unless marked "host"); the
+ *     library never allocates, frees or retains them, and keeps no state between calls.
+ *   - Every call is asynchronous on `stream` (0 = the default stream); outputs are valid once
+ *     the stream has reached them.  Calls on different streams with disjoint outputs and
+ *     workspaces may run concurrently.
+ *   - Host-detectable argument errors return a negative SPEC_E* code and launch nothing.
+ *     Data-dependent conditions are reported per request in status bits (a kernel cannot
+ *     return an error code).
+ *   - Logits are row-major and contiguous with the vocabulary fastest: draft [B][Kd][V],
+ *     target [B][K+1][V]; element type SPEC_FP32 (float) or SPEC_BF16 (bfloat16 bits).
+ *   - Token order used by every selection (top-k, nucleus, the downweighted set, cache ranks,
+ *     greedy argmax): logit descending, then token id ascending on equal logits.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+enum {
+    SPEC_OK = 0,
+    SPEC_EINVAL = -1,      /* null pointer, size < 1, F outside [0, SPEC_MAX_F], C outside [0, 1], ... */
+    SPEC_EDTYPE = -2,      /* dtype is neither SPEC_FP32 nor SPEC_BF16 */
+    SPEC_EWORKSPACE = -3,  /* workspace null or smaller than spec_workspace_bytes() */
+    SPEC_EHIP = -4         /* a kernel launch failed (hipGetLastError after the launch) */
+};
+
+enum { SPEC_FP32 = 0, SPEC_BF16 = 1 };
+
+#define SPEC_MAX_F 64          /* largest downweighted set */
+#define SPEC_MAX_FANOUT 1024   /* largest cache width for one depth */
+
+/* Per-request processing, applied to the draft AND the target rows of that request ([SpS]
+ * section 6: temperature, top-k and nucleus act on both distributions before the correction).
+ * Order: temperature, then top-k, then softmax, then nucleus.
+ *   temperature  > 0, or 0 for greedy verification (argmax match, [MSD] section 2)
+ *   top_k        <= 0 or >= V: off; else keep exactly top_k tokens (ties by lower id)
+ *   top_p        in (0, 1): keep the smallest prefix of the token order whose mass reaches
+ *                top_p; >= 1: off.  temperature < 0, NaN or top_p <= 0 sets SPEC_ST_BAD_PARAM. */
+typedef struct {
+    float temperature;
+    int32_t top_k;
+    float top_p;
+} spec_params;
+
+/* flags for spec_verify */
+enum {
+    SPEC_SAMPLE_DRAFT = 1  /* draft_tokens is an output: s_j is drawn from the processed (and
+                              downweighted) draft row j by inverse CDF in token-id order with
+                              Philox lane 2, or is the draft argmax when temperature is 0 */
+};
+
+/* per-request status bits (out_status) */
+enum {
+    SPEC_ST_EMPTY_RESIDUAL = 8,            /* rejection with no residual mass: t* drawn from q_k */
+    SPEC_ST_OUTSIDE_DRAFT_SUPPORT = 16,    /* an evaluated draft token has p'(s) = 0; it is
+                                              accepted iff q(s) > 0 */
+    SPEC_ST_BAD_LOGIT = 32,                /* NaN / +inf logit, or a row with no finite logit:
+                                              k = 0, t* = -1 */
+    SPEC_ST_BAD_TOKEN = 64,                /* a draft token outside [0, V): k = 0, t* = -1 */
+    SPEC_ST_DEGENERATE_DOWNWEIGHT = 128,   /* C = 0 and the set holds all the draft mass: the
+                                              row is left undownweighted */
+    SPEC_ST_BAD_PARAM = 256                /* invalid spec_params: k = 0, t* = -1 */
+};
+
+/* Uniforms.  Counter-based Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and counter
+ * (round, b, j, 0) gives the block of request b and position j = 0..K; word w of the block
+ * becomes the uniform ((w >> 12) + 0.5) * 2^-52 in (0, 1).  Word 0: acceptance u_j; word 1:
+ * residual / bonus v_j; word 2: draft sampling (SPEC_SAMPLE_DRAFT). */
+
+/* Bytes of scratch spec_verify needs for B requests of K draft positions over V tokens.
+ * Pure host function; the workspace needs no initialisation and holds nothing between calls. */
+size_t spec_workspace_bytes(int B, int K, int V);
+
+/* spec_verify - batched speculative-sampling verification ([SpS] sections 1 and 3; [SSD]
+ * section 2.2; outcome (k, t*) as in [SSD] section 1.3).
+ *
+ * For each request b, with p_j the processed draft row j after sigma_{F,C} (F > 0 and C < 1;
+ * [SSD-H] Method, [SSD] section 4.4) and q_j the processed target row j:
+ *   for j = 0..K-1: accept s_j iff u_j * p_j(s_j) < q_j(s_j); stop at the first rejection.
+ *   k = number of accepted tokens.  k < K: t* ~ (q_k - p_k)+ / sum (q_k - p_k)+ with v_k;
+ *   k = K: t* ~ q_K with v_K.  Sampling is the inverse CDF in token-id order: the first token
+ *   whose running mass exceeds v times the total.  Greedy requests (temperature 0) accept s_j
+ *   iff it is the argmax of q_j and take t* = argmax q_k.
+ *
+ *   draft_logits    [B][draft_rows][V]; draft_rows = K or K+1 (row K, used by the cache, is
+ *                   ignored here)
+ *   target_logits   [B][K+1][V]
+ *   params          [B] spec_params (device)
+ *   F, C            downweighted set size (0 = off) and factor in [0, 1] (1 = off)
+ *   draft_tokens    [B][K] int32: read, or written when flags has SPEC_SAMPLE_DRAFT
+ *   seed, round     Philox key and first counter word
+ *   out_k           [B] int32 in [0, K]
+ *   out_tstar       [B] int32 correction / bonus token, -1 for bad requests
+ *   out_resid_mass  [B] float: sum (q_k - p_k)+ when k < K, else 0 (nullable)
+ *   out_status      [B] uint32 status bits (nullable)
+ *   workspace       >= spec_workspace_bytes(B, K, V) bytes of device memory
+ * Returns SPEC_OK or a negative SPEC_E* code. */
+int spec_verify(const void* draft_logits, int draft_rows, const void* target_logits, int dtype, int B, int K,
+                int V, const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,
+                uint64_t round, uint32_t flags, int32_t* out_k, int32_t* out_tstar, float* out_resid_mass,
+                uint32_t* out_status, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* saguaro_downweight - Saguaro sampling sigma_{F,C} ([SSD-H] Method; [SSD] section 4.4 with the
+ * Theorem 19 example): on each processed draft row j < K the first F tokens of the token order
+ * that carry mass form the set S; with P_S their mass, Z = 1 - (1 - C) P_S and
+ * p'_i = p_i C / Z on S, p_i / Z elsewhere.
+ *   out_ids    [B][K][F] int32, S in rank order, -1 past its end
+ *   out_Z      [B][K] float (nullable)
+ *   out_probs  [B][K][V] float, the full p' (nullable; for tests)
+ *   out_status [B][K] uint32 (nullable): SPEC_ST_BAD_LOGIT / _BAD_PARAM / _DEGENERATE_DOWNWEIGHT */
+int saguaro_downweight(const void* draft_logits, int draft_rows, int dtype, int B, int K, int V,
+                       const spec_params* params, int F, float C, int32_t* out_ids, float* out_Z, float* out_probs,
+                       uint32_t* out_status, hipStream_t stream);
+
+/* Host helper: the Theorem 12 fan-out ([SSD] section 4.3; [SSD-H] Method).  Real values
+ * F_k = F0 a^{k/(1+r)} (k < K) and F_K = F0 a^{K/(1+r)} (1 - a)^{-1/(1+r)} with F0 such that
+ * they sum to `budget`; integers by largest remainder (ties to the smaller k) so that they
+ * sum to the budget exactly.  a in (0, 1), r > -1.  out_fanout [K+1] host. */
+int saguaro_fanout(int K, int budget, double a, double r, int32_t* out_fanout);
+
+/* saguaro_cache_build - the outcome cache's token sets ([SSD] section 5.1; [SSD-H] Method).
+ * For depth k < K: the first F_k tokens of draft row k in token order other than the drafted
+ * token s_k; for depth K: the first F_K tokens of draft row K.  NaN logits rank last.
+ *   draft_logits     [B][K+1][V]
+ *   draft_tokens     [B][K]
+ *   out_fanout_host  [K+1] host, the fan-out used (nullable)
+ *   out_cache        [B][budget] int32, depth-major, rank order, -1 past a row's end */
+int saguaro_cache_build(const void* draft_logits, int dtype, int B, int K, int V, const int32_t* draft_tokens,
+                        int budget, double a, double r, int32_t* out_fanout_host, int32_t* out_cache,
+                        hipStream_t stream);
+
+/* saguaro_cache_lookup - hit / miss of the verified outcome.
+ * mode 0 ([SSD-H] Method: cache lookup; [SSD] section 7.1): cache [B][sum F] from
+ *   saguaro_cache_build, fanout_or_shape = the [K+1] fan-out (host), k / tstar [B];
+ *   out_slot[b] = offset(k_b) + rank of t*_b in C_{k_b}, or -1 on a miss.
+ * mode 1 ([MSD] sections 3.2-3.3, branch-complete tree): cache = branch tokens [B][kappa][gamma],
+ *   fanout_or_shape = {kappa, gamma} (host), k / tstar [B][kappa] per chain, chain 0 of each
+ *   request being the verified path; out_slot[b] = lowest branch whose first k+1 tokens equal
+ *   (accepted tokens, t*), -1 if none, -2 when all gamma tokens were accepted.
+ *   out_hit [B] uint8 (slot >= 0); out_batch [2] int32 = {hits, 1 if every request hit}. */
+int saguaro_cache_lookup(int mode, const int32_t* cache, const int32_t* fanout_or_shape, int K, int B,
+                         const int32_t* k, const int32_t* tstar, int32_t* out_slot, uint8_t* out_hit,
+                         int32_t* out_batch, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

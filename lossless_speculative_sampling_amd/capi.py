@@ -1,0 +1,191 @@
+"""Thin ctypes binding of libspecverify.so (include/specverify.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors supply device pointers and the current HIP stream;
+every step of the path runs in the library's kernels.  There is no CPU fallback - a missing
+or unloadable library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libspecverify.so")
+
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP = 0, -1, -2, -3, -4
+SPEC_FP32, SPEC_BF16 = 0, 1
+SPEC_SAMPLE_DRAFT = 1
+SPEC_MAX_F = 64
+ST_EMPTY_RESIDUAL = 8
+ST_OUTSIDE_DRAFT_SUPPORT = 16
+ST_BAD_LOGIT = 32
+ST_BAD_TOKEN = 64
+ST_DEGENERATE_DOWNWEIGHT = 128
+ST_BAD_PARAM = 256
+
+EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
+           "saguaro_cache_lookup")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_U64 = ctypes.c_uint64
+_D = ctypes.c_double
+
+
+class SpecError(RuntimeError):
+    def __init__(self, fn: str, rc: int):
+        names = {SPEC_EINVAL: "SPEC_EINVAL", SPEC_EDTYPE: "SPEC_EDTYPE", SPEC_EWORKSPACE: "SPEC_EWORKSPACE",
+                 SPEC_EHIP: "SPEC_EHIP"}
+        super().__init__(f"{fn} returned {names.get(rc, rc)}")
+        self.rc = rc
+
+
+class Lib:
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(f"HIP library {path} is not built (run __graft_entry__.build())")
+        self.cdll = L = ctypes.CDLL(path)
+        L.spec_workspace_bytes.argtypes = [_I, _I, _I]
+        L.spec_workspace_bytes.restype = ctypes.c_size_t
+        L.spec_verify.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64, ctypes.c_uint32,
+                                  _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.saguaro_downweight.argtypes = [_P, _I, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P]
+        L.saguaro_fanout.argtypes = [_I, _I, _D, _D, _P]
+        L.saguaro_cache_build.argtypes = [_P, _I, _I, _I, _I, _P, _I, _D, _D, _P, _P, _P]
+        L.saguaro_cache_lookup.argtypes = [_I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]
+        for fn in EXPORTS[1:]:
+            getattr(L, fn).restype = _I
+
+
+_lib: Optional[Lib] = None
+
+
+def load(path: str = LIB_PATH) -> Lib:
+    global _lib
+    if _lib is None:
+        _lib = Lib(path)
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != SPEC_OK:
+        raise SpecError(fn, rc)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SPEC_FP32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return SPEC_BF16
+    raise ValueError(f"unsupported logit dtype {t.dtype}")
+
+
+def spec_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(load().cdll.spec_workspace_bytes(B, K, V))
+
+
+def params_tensor(temperature, top_k, top_p, device="cuda") -> torch.Tensor:
+    """[B] spec_params packed as int32 words {float T, int32 top_k, float top_p}."""
+    T = torch.as_tensor(temperature, dtype=torch.float32).reshape(-1)
+    k = torch.as_tensor(top_k, dtype=torch.int32).reshape(-1)
+    p = torch.as_tensor(top_p, dtype=torch.float32).reshape(-1)
+    B = max(T.numel(), k.numel(), p.numel())
+    T, k, p = T.expand(B), k.expand(B), p.expand(B)
+    rec = torch.stack([T.view(torch.int32), k, p.view(torch.int32)], dim=1).contiguous()
+    return rec.to(device)
+
+
+@dataclass
+class VerifyOut:
+    k: torch.Tensor
+    tstar: torch.Tensor
+    resid_mass: torch.Tensor
+    status: torch.Tensor
+    tokens: torch.Tensor
+
+
+def spec_verify(draft: torch.Tensor, target: torch.Tensor, K: int, params: torch.Tensor, tokens: torch.Tensor,
+                F: int = 0, C: float = 1.0, seed: int = 0, round_: int = 0, flags: int = 0,
+                workspace: Optional[torch.Tensor] = None, out: Optional[VerifyOut] = None, stream=None) -> VerifyOut:
+    """draft [B][Kd][V] and target [B][K+1][V] device logits; tokens [B][K] int32 (in, or out under
+    SPEC_SAMPLE_DRAFT).  Returns the outputs (allocated here unless `out` is given)."""
+    B, Kd, V = draft.shape
+    dev = draft.device
+    if out is None:
+        out = VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                        torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                        tokens)
+    need = spec_workspace_bytes(B, K, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = load().cdll.spec_verify(_ptr(draft), Kd, _ptr(target), dtype_code(draft), B, K, V, _ptr(params), F,
+                                 ctypes.c_float(C), _ptr(tokens), seed, round_, flags, _ptr(out.k), _ptr(out.tstar),
+                                 _ptr(out.resid_mass), _ptr(out.status), _ptr(workspace), workspace.numel(),
+                                 _stream(stream))
+    _check("spec_verify", rc)
+    out.tokens = tokens
+    return out
+
+
+def saguaro_downweight(draft: torch.Tensor, K: int, params: torch.Tensor, F: int, C: float, want_probs=False,
+                       stream=None):
+    B, Kd, V = draft.shape
+    dev = draft.device
+    ids = torch.empty((B, K, max(F, 1)), dtype=torch.int32, device=dev)
+    Z = torch.empty((B, K), dtype=torch.float32, device=dev)
+    st = torch.empty((B, K), dtype=torch.int32, device=dev)
+    probs = torch.empty((B, K, V), dtype=torch.float32, device=dev) if want_probs else None
+    rc = load().cdll.saguaro_downweight(_ptr(draft), Kd, dtype_code(draft), B, K, V, _ptr(params), F,
+                                        ctypes.c_float(C), _ptr(ids), _ptr(Z), _ptr(probs), _ptr(st), _stream(stream))
+    _check("saguaro_downweight", rc)
+    return ids[:, :, :F], Z, probs, st
+
+
+def saguaro_fanout(K: int, budget: int, a: float, r: float) -> list[int]:
+    buf = (ctypes.c_int32 * (K + 1))()
+    _check("saguaro_fanout", load().cdll.saguaro_fanout(K, budget, a, r, ctypes.cast(buf, _P)))
+    return list(buf)
+
+
+def saguaro_cache_build(draft: torch.Tensor, K: int, tokens: torch.Tensor, budget: int, a: float, r: float,
+                        stream=None):
+    B, Kd, V = draft.shape
+    fan = (ctypes.c_int32 * (K + 1))()
+    cache = torch.empty((B, max(budget, 1)), dtype=torch.int32, device=draft.device)
+    rc = load().cdll.saguaro_cache_build(_ptr(draft), dtype_code(draft), B, K, V, _ptr(tokens), budget, a, r,
+                                         ctypes.cast(fan, _P), _ptr(cache), _stream(stream))
+    _check("saguaro_cache_build", rc)
+    return cache[:, :budget], list(fan)
+
+
+def saguaro_cache_lookup(mode: int, cache: torch.Tensor, fanout_or_shape, K: int, B: int, k: torch.Tensor,
+                         tstar: torch.Tensor, stream=None):
+    dev = cache.device
+    fs = (ctypes.c_int32 * len(fanout_or_shape))(*[int(x) for x in fanout_or_shape])
+    slot = torch.empty(B, dtype=torch.int32, device=dev)
+    hit = torch.empty(B, dtype=torch.uint8, device=dev)
+    batch = torch.empty(2, dtype=torch.int32, device=dev)
+    rc = load().cdll.saguaro_cache_lookup(mode, _ptr(cache), ctypes.cast(fs, _P), K, B, _ptr(k), _ptr(tstar),
+                                          _ptr(slot), _ptr(hit), _ptr(batch), _stream(stream))
+    _check("saguaro_cache_lookup", rc)
+    return slot, hit, batch

@@ -1,0 +1,154 @@
+// The C ABI: argument validation, workspace layout and kernel launches.
+#include <cmath>
+#include <cstring>
+
+#include "generic.h"
+
+using namespace sv;
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool valid_dtype(int dtype) { return dtype == SPEC_FP32 || dtype == SPEC_BF16; }
+
+int launch_status() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP; }
+
+// Theorem 12 allocation (SSD reading notes section 4.3; hyper.ai summary, Method):
+// weights a^{k/(1+r)} for k < K and a^{K/(1+r)} (1-a)^{-1/(1+r)} for k = K, scaled to the
+// budget, then rounded by largest remainder with ties to the smaller depth.
+int fanout_host(int K, int budget, double a, double r, int32_t* out) {
+    if (K < 1 || K > kMaxK || budget < 0 || !(a > 0.0 && a < 1.0) || !(r > -1.0)) return SPEC_EINVAL;
+    const double e = 1.0 / (1.0 + r);
+    double w[kMaxK + 1], sum = 0.0;
+    for (int k = 0; k <= K; ++k) {
+        w[k] = std::pow(a, (double)k * e);
+        if (k == K) w[k] *= std::pow(1.0 - a, -e);
+        sum += w[k];
+    }
+    double frac[kMaxK + 1];
+    int total = 0;
+    for (int k = 0; k <= K; ++k) {
+        const double real = (double)budget * w[k] / sum;
+        const double fl = std::floor(real);
+        out[k] = (int32_t)fl;
+        frac[k] = real - fl;
+        total += out[k];
+    }
+    for (int extra = budget - total; extra > 0; --extra) {
+        int best = -1;
+        for (int k = 0; k <= K; ++k)
+            if (frac[k] >= 0.0 && (best < 0 || frac[k] > frac[best])) best = k;
+        out[best] += 1;
+        frac[best] = -1.0;
+    }
+    return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_workspace_bytes(int B, int K, int V) {
+    if (B < 1 || K < 1 || V < 1) return 0;
+    return align_up((size_t)B * (K + 1) * sizeof(UnitRec), 256);
+}
+
+int spec_verify(const void* draft_logits, int draft_rows, const void* target_logits, int dtype, int B, int K,
+                int V, const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,
+                uint64_t round, uint32_t flags, int32_t* out_k, int32_t* out_tstar, float* out_resid_mass,
+                uint32_t* out_status, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!draft_logits || !target_logits || !params || !draft_tokens || !out_k || !out_tstar) return SPEC_EINVAL;
+    if (B < 1 || K < 1 || V < 1 || (draft_rows != K && draft_rows != K + 1)) return SPEC_EINVAL;
+    if (F < 0 || F > SPEC_MAX_F || !(C >= 0.0f && C <= 1.0f)) return SPEC_EINVAL;
+    if ((flags & ~(uint32_t)SPEC_SAMPLE_DRAFT) != 0) return SPEC_EINVAL;
+    if (!valid_dtype(dtype)) return SPEC_EDTYPE;
+    const size_t need = spec_workspace_bytes(B, K, V);
+    if (!workspace || workspace_bytes < need) return SPEC_EWORKSPACE;
+    VerifyArgs a{draft_logits, target_logits, draft_rows, dtype, B, K, V, params, F, C, draft_tokens, seed,
+                 round, flags, out_k, out_tstar, out_resid_mass, out_status, static_cast<UnitRec*>(workspace)};
+    hipLaunchKernelGGL(generic_unit_kernel, dim3((unsigned)(B * (K + 1))), dim3(kRowThreadsHost), 0, stream, a);
+    if (launch_status() != SPEC_OK) return SPEC_EHIP;
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, a);
+    return launch_status();
+}
+
+int saguaro_downweight(const void* draft_logits, int draft_rows, int dtype, int B, int K, int V,
+                       const spec_params* params, int F, float C, int32_t* out_ids, float* out_Z, float* out_probs,
+                       uint32_t* out_status, hipStream_t stream) {
+    if (!draft_logits || !params || (F > 0 && !out_ids)) return SPEC_EINVAL;
+    if (B < 1 || K < 1 || V < 1 || draft_rows < K) return SPEC_EINVAL;
+    if (F < 0 || F > SPEC_MAX_F || !(C >= 0.0f && C <= 1.0f)) return SPEC_EINVAL;
+    if (!valid_dtype(dtype)) return SPEC_EDTYPE;
+    DownweightArgs a{draft_logits, draft_rows, dtype, B, K, V, params, F, C, out_ids, out_Z, out_probs, out_status};
+    hipLaunchKernelGGL(downweight_kernel, dim3((unsigned)(B * K)), dim3(kRowThreadsHost), 0, stream, a);
+    return launch_status();
+}
+
+int saguaro_fanout(int K, int budget, double a, double r, int32_t* out_fanout) {
+    if (!out_fanout) return SPEC_EINVAL;
+    return fanout_host(K, budget, a, r, out_fanout);
+}
+
+int saguaro_cache_build(const void* draft_logits, int dtype, int B, int K, int V, const int32_t* draft_tokens,
+                        int budget, double a, double r, int32_t* out_fanout_host, int32_t* out_cache,
+                        hipStream_t stream) {
+    if (!draft_logits || !draft_tokens || !out_cache || B < 1 || K < 1 || V < 1) return SPEC_EINVAL;
+    if (!valid_dtype(dtype)) return SPEC_EDTYPE;
+    CacheArgs c{};
+    const int rc = fanout_host(K, budget, a, r, c.fanout.f);
+    if (rc != SPEC_OK) return rc;
+    c.fanout.off[0] = 0;
+    for (int k = 0; k <= K; ++k) {
+        if (c.fanout.f[k] > SPEC_MAX_FANOUT) return SPEC_EINVAL;
+        c.fanout.off[k + 1] = c.fanout.off[k] + c.fanout.f[k];
+    }
+    if (out_fanout_host) std::memcpy(out_fanout_host, c.fanout.f, sizeof(int32_t) * (K + 1));
+    c.draft = draft_logits;
+    c.dtype = dtype;
+    c.B = B;
+    c.K = K;
+    c.V = V;
+    c.tokens = draft_tokens;
+    c.budget = budget;
+    c.out_cache = out_cache;
+    if (budget == 0) return SPEC_OK;
+    hipLaunchKernelGGL(cache_build_kernel, dim3((unsigned)(B * (K + 1))), dim3(kRowThreadsHost), 0, stream, c);
+    return launch_status();
+}
+
+int saguaro_cache_lookup(int mode, const int32_t* cache, const int32_t* fanout_or_shape, int K, int B,
+                         const int32_t* k, const int32_t* tstar, int32_t* out_slot, uint8_t* out_hit,
+                         int32_t* out_batch, hipStream_t stream) {
+    if (!cache || !fanout_or_shape || !k || !tstar || !out_slot || !out_hit || B < 1) return SPEC_EINVAL;
+    LookupArgs l{};
+    l.mode = mode;
+    l.cache = cache;
+    l.B = B;
+    l.K = K;
+    l.k = k;
+    l.tstar = tstar;
+    l.out_slot = out_slot;
+    l.out_hit = out_hit;
+    l.out_batch = out_batch;
+    if (mode == 0) {
+        if (K < 1 || K > kMaxK) return SPEC_EINVAL;
+        l.fanout.off[0] = 0;
+        for (int x = 0; x <= K; ++x) {
+            if (fanout_or_shape[x] < 0) return SPEC_EINVAL;
+            l.fanout.f[x] = fanout_or_shape[x];
+            l.fanout.off[x + 1] = l.fanout.off[x] + fanout_or_shape[x];
+        }
+        l.budget = l.fanout.off[K + 1];
+    } else if (mode == 1) {
+        l.kappa = fanout_or_shape[0];
+        l.gamma = fanout_or_shape[1];
+        if (l.kappa < 1 || l.gamma < 1) return SPEC_EINVAL;
+    } else {
+        return SPEC_EINVAL;
+    }
+    hipLaunchKernelGGL(cache_lookup_kernel, dim3(1), dim3(1024), 0, stream, l);
+    return launch_status();
+}
+
+}  // extern "C"

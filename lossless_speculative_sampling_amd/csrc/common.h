@@ -1,0 +1,180 @@
+// Device-side building blocks of the gfx950 verification kernels: order keys, the Philox
+// stream, element loads and workgroup reductions for 64-wide wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/specverify.h"
+
+namespace sv {
+
+constexpr int kWave = 64;
+
+// Per-request status bits (values fixed by the C ABI).
+constexpr uint32_t kStEmptyResidual = SPEC_ST_EMPTY_RESIDUAL;
+constexpr uint32_t kStOutside = SPEC_ST_OUTSIDE_DRAFT_SUPPORT;
+constexpr uint32_t kStBadLogit = SPEC_ST_BAD_LOGIT;
+constexpr uint32_t kStBadToken = SPEC_ST_BAD_TOKEN;
+constexpr uint32_t kStDegenerate = SPEC_ST_DEGENERATE_DOWNWEIGHT;
+constexpr uint32_t kStBadParam = SPEC_ST_BAD_PARAM;
+
+// ------------------------------------------------------------------------------------------
+// Token order: a 32-bit key that grows with the logit.  -0 is folded onto +0 so that equal
+// logits tie (and fall back to the lower token id); NaN gets key 0, below -inf.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key_bits(uint32_t u) {
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;  // NaN
+    if (u == 0x80000000u) u = 0u;                      // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t order_key(float x) { return order_key_bits(__float_as_uint(x)); }
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+constexpr uint32_t kKeyPosInf = 0xFF800000u;  // order_key(+inf)
+
+// Element i of a logit row, widened to fp32 (bf16 -> fp32 is exact).
+__device__ __forceinline__ float load_logit(const void* row, int dtype, int i) {
+    if (dtype == SPEC_BF16) {
+        uint32_t h = static_cast<const uint16_t*>(row)[i];
+        return __uint_as_float(h << 16);
+    }
+    return static_cast<const float*>(row)[i];
+}
+
+// ------------------------------------------------------------------------------------------
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw: "Parallel Random Numbers: As Easy as 1, 2, 3",
+// SC'11).  Two 64x64 -> 128-bit products per round, Weyl key schedule between rounds.
+// ------------------------------------------------------------------------------------------
+struct Block4 {
+    uint64_t w[4];
+};
+
+__device__ __forceinline__ Block4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t key0,
+                                                uint64_t key1) {
+    const uint64_t mulA = 0xD2E7470EE14C6C93ull, mulB = 0xCA5A826395121157ull;
+    const uint64_t weylA = 0x9E3779B97F4A7C15ull, weylB = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t pa_hi = __umul64hi(mulA, c0), pa_lo = mulA * c0;
+        const uint64_t pb_hi = __umul64hi(mulB, c2), pb_lo = mulB * c2;
+        const uint64_t n0 = pb_hi ^ c1 ^ key0;
+        const uint64_t n2 = pa_hi ^ c3 ^ key1;
+        c0 = n0;
+        c1 = pb_lo;
+        c2 = n2;
+        c3 = pa_lo;
+        key0 += weylA;
+        key1 += weylB;
+    }
+    Block4 b;
+    b.w[0] = c0;
+    b.w[1] = c1;
+    b.w[2] = c2;
+    b.w[3] = c3;
+    return b;
+}
+
+// Uniform in (0, 1) from one 64-bit word: the top 52 bits plus half an ulp (exact in fp64).
+__device__ __forceinline__ double word_to_uniform(uint64_t w) {
+    return ((double)(w >> 12) + 0.5) * 0x1.0p-52;
+}
+
+// The uniforms of request b, position j: word 0 acceptance, 1 residual/bonus, 2 draft sampling.
+__device__ __forceinline__ double uniform_at(uint64_t seed, uint64_t round, uint64_t b, uint64_t j, int word) {
+    Block4 x = philox4x64_10(round, b, j, 0, seed, 0);
+    return word_to_uniform(x.w[word]);
+}
+
+// ------------------------------------------------------------------------------------------
+// Wavefront / workgroup reductions (wave64).  `red` is LDS scratch of >= 2 * waves entries.
+// ------------------------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        T w = __shfl_xor(v, o, kWave);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_min(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        T w = __shfl_xor(v, o, kWave);
+        v = w < v ? w : v;
+    }
+    return v;
+}
+
+template <typename T, int OP>  // OP 0 sum, 1 max, 2 min
+__device__ __forceinline__ T wave_reduce(T v) {
+    if (OP == 0) return wave_sum(v);
+    if (OP == 1) return wave_max(v);
+    return wave_min(v);
+}
+
+// Workgroup reduction; every thread gets the result.  Deterministic (fixed tree).
+template <typename T, int OP>
+__device__ __forceinline__ T block_reduce(T v, T* red) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    v = wave_reduce<T, OP>(v);
+    __syncthreads();  // red may still be read by a previous reduction
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    T r = red[0];
+    for (int w = 1; w < nwaves; ++w) {
+        T x = red[w];
+        if (OP == 0) r += x;
+        else if (OP == 1) r = x > r ? x : r;
+        else r = x < r ? x : r;
+    }
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* red) { return block_reduce<T, 0>(v, red); }
+template <typename T>
+__device__ __forceinline__ T block_max(T v, T* red) { return block_reduce<T, 1>(v, red); }
+template <typename T>
+__device__ __forceinline__ T block_min(T v, T* red) { return block_reduce<T, 2>(v, red); }
+
+// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
+template <typename T>
+__device__ __forceinline__ T block_exclusive_scan(T v, T* red, T* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    T inc = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        T y = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += y;
+    }
+    T exc = __shfl_up(inc, 1, kWave);
+    if (lane == 0) exc = T(0);
+    __syncthreads();
+    if (lane == kWave - 1) red[wave] = inc;
+    __syncthreads();
+    T before = T(0), all = T(0);
+    for (int w = 0; w < nwaves; ++w) {
+        T x = red[w];
+        if (w < wave) before += x;
+        all += x;
+    }
+    *total = all;
+    return before + exc;
+}
+
+}  // namespace sv

@@ -1,0 +1,282 @@
+// General-path kernels: one 1024-thread workgroup per (request b, position j) unit.
+//
+// Unit j < K processes target row j and draft row j (plus the downweight), decides the
+// acceptance of s_j with its uniform u_j and, if s_j is rejected, samples the correction token
+// from the normalised residual (q_j - p_j)+ with v_j.  Unit K samples the bonus token from q_K.
+// Because the Philox counter is keyed by (b, j), every unit can draw its own candidate without
+// waiting for the earlier positions; the finalize kernel then takes k = the first rejected
+// position and t* = that unit's candidate, which is exactly the sequential rule of the DeepMind
+// speculative-sampling page (section 3) and the SSD reading notes (section 2.2).
+#include "generic.h"
+#include "rowproc.h"
+
+namespace sv {
+
+__global__ __launch_bounds__(kRowThreads) void generic_unit_kernel(VerifyArgs a) {
+    __shared__ RowShared sh;
+    __shared__ RowStats stq, stp;
+    const int unit = blockIdx.x;
+    const int b = unit / (a.K + 1);
+    const int j = unit % (a.K + 1);
+    UnitRec* rec = a.units + unit;
+    const spec_params prm = a.params[b];
+    const bool param_ok = prm.temperature >= 0.0f && !isinf(prm.temperature) && prm.top_p > 0.0f;
+    if (!param_ok) {
+        if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, kStBadParam, -1};
+        return;
+    }
+    const size_t tstride = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
+    const char* trow = static_cast<const char*>(a.target) + ((size_t)b * (a.K + 1) + j) * tstride;
+    RowRef rq{trow, a.dtype, a.V};
+    process_row(rq, prm.temperature, prm.top_k, prm.top_p, 0, 1.0, false, stq, sh);
+    RowRef rp{nullptr, a.dtype, a.V};
+    if (j < a.K) {
+        rp.row = static_cast<const char*>(a.draft) + ((size_t)b * a.draft_rows + j) * tstride;
+        const bool dw = a.F > 0 && a.C < 1.0f;
+        process_row(rp, prm.temperature, prm.top_k, prm.top_p, a.F, (double)a.C, dw, stp, sh);
+    }
+    if (stq.bad || (j < a.K && stp.bad)) {
+        if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, kStBadLogit, -1};
+        return;
+    }
+    uint32_t status = (j < a.K && stp.degenerate) ? kStDegenerate : 0u;
+    const bool greedy = stq.greedy != 0;
+
+    if (j == a.K) {  // bonus position
+        int t;
+        if (greedy) {
+            t = stq.argmax;
+        } else {
+            const double v = uniform_at(a.seed, a.round, b, j, 1);
+            double tot;
+            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
+        }
+        if (threadIdx.x == 0) *rec = UnitRec{1, t, 0.0f, status, -1};
+        return;
+    }
+
+    // draft token s_j (sampled here under SPEC_SAMPLE_DRAFT)
+    int s;
+    if (a.flags & SPEC_SAMPLE_DRAFT) {
+        if (greedy) {
+            s = stp.argmax;
+        } else {
+            const double x = uniform_at(a.seed, a.round, b, j, 2);
+            double tot;
+            s = inverse_cdf(rp, x, [&](int i, float z) { return rs_prob_dw(stp, z, i); }, sh, &tot);
+        }
+        if (threadIdx.x == 0) a.tokens[(size_t)b * a.K + j] = s;
+    } else {
+        s = a.tokens[(size_t)b * a.K + j];
+    }
+    if (s < 0 || s >= a.V) {
+        if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, status | kStBadToken, s};
+        return;
+    }
+
+    bool accept;
+    if (greedy) {
+        accept = (s == stq.argmax);
+    } else {
+        const double ps = rs_prob_dw(stp, load_logit(rp.row, a.dtype, s), s);
+        const double qs = rs_prob(stq, load_logit(rq.row, a.dtype, s), s);
+        if (!(ps > 0.0)) status |= kStOutside;
+        const double u = uniform_at(a.seed, a.round, b, j, 0);
+        accept = u * ps < qs;
+    }
+    if (accept) {
+        if (threadIdx.x == 0) *rec = UnitRec{1, -1, 0.0f, status, s};
+        return;
+    }
+    int t;
+    double W = 0.0;
+    if (greedy) {
+        t = stq.argmax;
+    } else {
+        const double v = uniform_at(a.seed, a.round, b, j, 1);
+        // residual (q - p')+ at this position; rows are read pairwise by token id
+        auto resid = [&](int i, float zq) {
+            const double q = rs_prob(stq, zq, i);
+            const double p = rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i);
+            return q > p ? q - p : 0.0;
+        };
+        t = inverse_cdf(rq, v, resid, sh, &W);
+        if (t < 0) {  // no residual mass: fall back to q itself
+            status |= kStEmptyResidual;
+            double tot;
+            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
+        }
+    }
+    if (threadIdx.x == 0) *rec = UnitRec{0, t, (float)W, status, s};
+}
+
+// Per request: k = first rejected position (K if none), t* = that unit's candidate.
+__global__ void finalize_kernel(VerifyArgs a) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= a.B) return;
+    const UnitRec* u = a.units + (size_t)b * (a.K + 1);
+    uint32_t any = 0, deg = 0;
+    for (int j = 0; j <= a.K; ++j) {
+        any |= u[j].status;
+        if (j < a.K) deg |= u[j].status & kStDegenerate;
+    }
+    int k = 0, t = -1;
+    float W = 0.0f;
+    uint32_t st;
+    if (any & kStBadParam) {
+        st = kStBadParam;
+    } else if (any & kStBadLogit) {
+        st = kStBadLogit;
+    } else if (any & kStBadToken) {
+        st = deg | kStBadToken;
+    } else {
+        st = deg;
+        k = a.K;
+        for (int j = 0; j < a.K; ++j) {
+            st |= u[j].status & kStOutside;
+            if (!u[j].accept) {
+                k = j;
+                break;
+            }
+        }
+        t = u[k].tcand;
+        W = u[k].W;
+        st |= u[k].status & kStEmptyResidual;
+    }
+    a.out_k[b] = k;
+    a.out_t[b] = t;
+    if (a.out_W) a.out_W[b] = W;
+    if (a.out_status) a.out_status[b] = st;
+}
+
+// saguaro_downweight: one workgroup per draft row j < K.
+__global__ __launch_bounds__(kRowThreads) void downweight_kernel(DownweightArgs a) {
+    __shared__ RowShared sh;
+    __shared__ RowStats st;
+    const int row = blockIdx.x;
+    const int b = row / a.K, j = row % a.K;
+    const spec_params prm = a.params[b];
+    const bool param_ok = prm.temperature >= 0.0f && !isinf(prm.temperature) && prm.top_p > 0.0f;
+    const size_t stride = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
+    RowRef r{static_cast<const char*>(a.draft) + ((size_t)b * a.draft_rows + j) * stride, a.dtype, a.V};
+    uint32_t status = 0;
+    if (!param_ok) {
+        status = kStBadParam;
+    } else {
+        process_row(r, prm.temperature, prm.top_k, prm.top_p, a.F, (double)a.C, a.F > 0, st, sh);
+        if (st.bad) status = kStBadLogit;
+        else if (st.degenerate) status = kStDegenerate;
+    }
+    const bool valid = status == 0 || status == kStDegenerate;
+    if (threadIdx.x == 0) {
+        for (int f = 0; f < a.F; ++f) a.out_ids[(size_t)row * a.F + f] = valid ? st.ids[f] : -1;
+        if (a.out_Z) a.out_Z[row] = valid ? (float)st.Z : 1.0f;
+        if (a.out_status) a.out_status[row] = status;
+    }
+    if (a.out_probs) {
+        float* out = a.out_probs + (size_t)row * a.V;
+        for (int i = threadIdx.x; i < a.V; i += blockDim.x)
+            out[i] = valid ? (float)rs_prob_dw(st, load_logit(r.row, a.dtype, i), i) : 0.0f;
+    }
+}
+
+// saguaro_cache_build: one workgroup per (request b, depth k).  The first F_k (+1 when the
+// drafted token must be skipped) tokens of draft row k in token order, NaN last.
+__global__ __launch_bounds__(kRowThreads) void cache_build_kernel(CacheArgs a) {
+    __shared__ RowShared sh;
+    __shared__ RowStats st;
+    __shared__ int picked[SPEC_MAX_FANOUT + 1];
+    __shared__ uint32_t pkey[SPEC_MAX_FANOUT + 1];
+    __shared__ int npicked;
+    const int b = blockIdx.x / (a.K + 1);
+    const int k = blockIdx.x % (a.K + 1);
+    const int Fk = a.fanout.f[k];
+    const int off = a.fanout.off[k];
+    int32_t* out = a.out_cache + (size_t)b * a.budget + off;
+    if (Fk <= 0) return;
+    const size_t stride = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
+    RowRef r{static_cast<const char*>(a.draft) + ((size_t)b * (a.K + 1) + k) * stride, a.dtype, a.V};
+    const int excl = (k < a.K) ? a.tokens[(size_t)b * a.K + k] : -1;
+    const int want = min(a.V, Fk + (excl >= 0 && excl < a.V ? 1 : 0));
+    uint32_t tau;
+    double above, rem;
+    int cnt;
+    auto all = [](uint32_t, int, float) { return true; };
+    radix_select<false>(r, st, all, (double)want, sh, &tau, &above, &cnt, &rem);
+    const int n = (int)rem;
+    const int idc = (n >= cnt) ? a.V - 1 : nth_id_at_key(r, tau, n, all, sh);
+    if (threadIdx.x == 0) npicked = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.V; i += blockDim.x) {
+        const uint32_t key = order_key(load_logit(r.row, a.dtype, i));
+        if (key > tau || (key == tau && i <= idc)) {
+            const int slot = atomicAdd(&npicked, 1);
+            if (slot <= SPEC_MAX_FANOUT) {
+                picked[slot] = i;
+                pkey[slot] = key;
+            }
+        }
+    }
+    __syncthreads();
+    const int np = min(npicked, want);
+    bool excl_picked = false;
+    for (int y = 0; y < np; ++y) excl_picked |= (picked[y] == excl);
+    // rank of each picked token in (key desc, id asc) order, less one past the drafted token
+    for (int x = threadIdx.x; x < np; x += blockDim.x) {
+        const int id = picked[x];
+        if (id == excl) continue;
+        const uint32_t key = pkey[x];
+        int rank = 0;
+        for (int y = 0; y < np; ++y) {
+            const uint32_t ky = pkey[y];
+            if ((ky > key || (ky == key && picked[y] < id)) && picked[y] != excl) ++rank;
+        }
+        if (rank < Fk) out[rank] = id;
+    }
+    // rows shorter than the fan-out: pad with -1
+    const int written = min(Fk, np - (excl_picked ? 1 : 0));
+    for (int x = written + threadIdx.x; x < Fk; x += blockDim.x) out[x] = -1;
+}
+
+// saguaro_cache_lookup: a single workgroup loops over the requests and reduces the batch stats.
+__global__ __launch_bounds__(1024) void cache_lookup_kernel(LookupArgs a) {
+    __shared__ int red[32];
+    int hits = 0;
+    for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
+        int res = -1;
+        if (a.mode == 0) {
+            const int k = a.k[b], t = a.tstar[b];
+            if (k >= 0 && k <= a.K && t >= 0) {
+                const int32_t* c = a.cache + (size_t)b * a.budget + a.fanout.off[k];
+                for (int f = 0; f < a.fanout.f[k]; ++f)
+                    if (c[f] == t) {
+                        res = a.fanout.off[k] + f;
+                        break;
+                    }
+            }
+        } else {
+            const int kappa = a.kappa, gamma = a.gamma;
+            const int32_t* br = a.cache + (size_t)b * kappa * gamma;
+            const int k = a.k[(size_t)b * kappa], t = a.tstar[(size_t)b * kappa];
+            if (k == gamma) {
+                res = -2;
+            } else if (k >= 0 && k < gamma && t >= 0) {
+                for (int jb = 0; jb < kappa && res < 0; ++jb) {
+                    bool ok = br[(size_t)jb * gamma + k] == t;
+                    for (int d = 0; d < k && ok; ++d) ok = br[(size_t)jb * gamma + d] == br[d];
+                    if (ok) res = jb;
+                }
+            }
+        }
+        a.out_slot[b] = res;
+        a.out_hit[b] = res >= 0 ? 1 : 0;
+        hits += res >= 0 ? 1 : 0;
+    }
+    const int total = block_sum<int>(hits, red);
+    if (threadIdx.x == 0 && a.out_batch) {
+        a.out_batch[0] = total;
+        a.out_batch[1] = total == a.B ? 1 : 0;
+    }
+}
+
+}  // namespace sv

@@ -1,0 +1,384 @@
+// Whole-workgroup processing of one logit row read from global memory: temperature, top-k,
+// softmax, nucleus and the Saguaro downweight, with exact radix selection on the 32-bit order
+// key and fp64 masses.  Used by every entry point for fp32 rows and as the general path
+// (any V, any parameters); the register-resident bf16 path lives in fastpath.hip.
+//
+// Processing follows the DeepMind speculative-sampling page, section 6 (temperature, top-k
+// and nucleus act on draft and target alike, before the correction), in the order
+// temperature -> top-k -> softmax -> nucleus.  The downweight is Saguaro sampling
+// sigma_{F,C} from the SSD pages (reading notes section 4.4; hyper.ai summary, Method).
+#pragma once
+
+#include "common.h"
+#include "generic.h"
+
+namespace sv {
+
+constexpr int kRowThreads = kRowThreadsHost;
+
+// Row statistics, uniform across the workgroup (lives in LDS).
+struct RowStats {
+    int bad;       // NaN / +inf / no finite logit
+    int greedy;    // temperature 0
+    int argmax;    // lowest id among the largest logits
+    float m;       // largest logit
+    double T;
+    uint32_t kk;   // top-k: kept iff key > kk, or key == kk and id <= idk
+    int idk;
+    uint32_t kp;   // nucleus: in iff kept and (key > kp, or key == kp and id <= idp)
+    int idp;
+    double S;      // normaliser over the nucleus
+    // downweighted set: in nucleus, mass > 0, and key > kF or (key == kF and id <= idF)
+    int nS;
+    uint32_t kF;
+    int idF;
+    double C;      // factor on the set (1 when off)
+    double Z;      // normaliser after the downweight (1 when off)
+    int degenerate;
+    int ids[SPEC_MAX_F];
+};
+
+struct RowShared {
+    uint32_t hcnt[256];
+    double hmass[256];
+    double redd[32];
+    unsigned long long redu[32];
+    int redi[32];
+    int sel_digit;
+    double sel_acc;
+    int found;
+    int list_n;
+    int list[SPEC_MAX_F + 1];
+    uint32_t list_key[SPEC_MAX_F + 1];
+};
+
+struct RowRef {
+    const void* row;
+    int dtype;
+    int V;
+};
+
+__device__ __forceinline__ bool rs_kept(const RowStats& s, uint32_t key, int i) {
+    return key > s.kk || (key == s.kk && i <= s.idk);
+}
+__device__ __forceinline__ bool rs_in(const RowStats& s, uint32_t key, int i) {
+    return rs_kept(s, key, i) && (key > s.kp || (key == s.kp && i <= s.idp));
+}
+__device__ __forceinline__ double rs_mass(const RowStats& s, float z) {
+    return exp(((double)z - (double)s.m) / s.T);
+}
+__device__ __forceinline__ bool rs_in_set(const RowStats& s, uint32_t key, int i, double e) {
+    return s.nS > 0 && rs_in(s, key, i) && e > 0.0 && (key > s.kF || (key == s.kF && i <= s.idF));
+}
+// processed probability p_i (before the downweight)
+__device__ __forceinline__ double rs_prob(const RowStats& s, float z, int i) {
+    if (s.greedy) return i == s.argmax ? 1.0 : 0.0;
+    const uint32_t key = order_key(z);
+    if (!rs_in(s, key, i)) return 0.0;
+    return rs_mass(s, z) / s.S;
+}
+// processed probability after the downweight, p'_i = p_i f_i / Z
+__device__ __forceinline__ double rs_prob_dw(const RowStats& s, float z, int i) {
+    if (s.greedy) return i == s.argmax ? 1.0 : 0.0;
+    const uint32_t key = order_key(z);
+    if (!rs_in(s, key, i)) return 0.0;
+    const double e = rs_mass(s, z);
+    const double p = e / s.S;
+    const double f = rs_in_set(s, key, i, e) ? s.C : 1.0;
+    return p * f / s.Z;
+}
+
+// Radix selection over the 32-bit key, 8 bits per pass from the top.  Walking keys from the
+// largest down over elements accepted by `filt`, weighted by 1 (COUNT) or by the element's
+// mass e_i, finds the key tau at which the running weight first reaches `need`.
+// Outputs: tau, the weight strictly above tau, the number of filtered elements at tau and the
+// weight still needed inside tau.
+template <bool MASS, typename Filter>
+__device__ void radix_select(const RowRef& r, const RowStats& st, Filter filt, double need, RowShared& sh,
+                             uint32_t* tau_out, double* above_out, int* cnt_out, double* rem_out) {
+    uint32_t prefix = 0, pmask = 0;
+    double above = 0.0, rem = need;
+    int cnt_at = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int d = threadIdx.x; d < 256; d += blockDim.x) {
+            sh.hcnt[d] = 0;
+            sh.hmass[d] = 0.0;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
+            const float z = load_logit(r.row, r.dtype, i);
+            const uint32_t key = order_key(z);
+            if ((key & pmask) != prefix || !filt(key, i, z)) continue;
+            const int d = (key >> shift) & 255;
+            atomicAdd(&sh.hcnt[d], 1u);
+            if (MASS) atomicAdd(&sh.hmass[d], rs_mass(st, z));
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double acc = 0.0;
+            int pick = -1, last_nz = -1;
+            double acc_last = 0.0;
+            for (int d = 255; d >= 0; --d) {
+                const double w = MASS ? sh.hmass[d] : (double)sh.hcnt[d];
+                if (sh.hcnt[d] == 0) continue;
+                if (acc + w >= rem) {
+                    pick = d;
+                    break;
+                }
+                last_nz = d;
+                acc_last = acc;
+                acc += w;
+            }
+            if (pick < 0) {  // rounding left the target just out of reach: take the lowest bin
+                pick = last_nz;
+                acc = acc_last;
+            }
+            sh.sel_digit = pick;
+            sh.sel_acc = acc;
+        }
+        __syncthreads();
+        const int d = sh.sel_digit;
+        above += sh.sel_acc;
+        rem -= sh.sel_acc;
+        cnt_at = d >= 0 ? (int)sh.hcnt[d] : 0;
+        prefix |= (uint32_t)(d < 0 ? 0 : d) << shift;
+        pmask |= 0xFFu << shift;
+        __syncthreads();
+    }
+    *tau_out = prefix;
+    *above_out = above;
+    *cnt_out = cnt_at;
+    *rem_out = rem;
+}
+
+// The n-th (1-based) smallest id among elements with key == tau accepted by `filt`.
+// Threads own contiguous id segments, so a workgroup scan of their counts locates it.
+template <typename Filter>
+__device__ int nth_id_at_key(const RowRef& r, uint32_t tau, int n, Filter filt, RowShared& sh) {
+    const int seg = (r.V + blockDim.x - 1) / blockDim.x;
+    const int lo = threadIdx.x * seg;
+    const int hi = min(r.V, lo + seg);
+    int c = 0;
+    for (int i = lo; i < hi; ++i) {
+        const float z = load_logit(r.row, r.dtype, i);
+        if (order_key(z) == tau && filt(order_key(z), i, z)) ++c;
+    }
+    int total;
+    const int before = block_exclusive_scan<int>(c, sh.redi, &total);
+    if (threadIdx.x == 0) sh.found = r.V - 1;
+    __syncthreads();
+    if (before < n && before + c >= n) {
+        int cc = before;
+        for (int i = lo; i < hi; ++i) {
+            const float z = load_logit(r.row, r.dtype, i);
+            if (order_key(z) == tau && filt(order_key(z), i, z) && ++cc == n) {
+                sh.found = i;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    const int res = sh.found;
+    __syncthreads();
+    return res;
+}
+
+// Inverse CDF in token-id order over non-negative weights w(i, z): the first i with w_i > 0
+// whose running sum exceeds x * total (the last i with w_i > 0 if rounding never crosses).
+// Returns -1 when every weight is 0.  *total_out gets the total.
+template <typename Weight>
+__device__ int inverse_cdf(const RowRef& r, double x, Weight wfn, RowShared& sh, double* total_out) {
+    const int seg = (r.V + blockDim.x - 1) / blockDim.x;
+    const int lo = threadIdx.x * seg;
+    const int hi = min(r.V, lo + seg);
+    double own = 0.0;
+    for (int i = lo; i < hi; ++i) {
+        const double w = wfn(i, load_logit(r.row, r.dtype, i));
+        if (w > 0.0) own += w;
+    }
+    double total;
+    const double before = block_exclusive_scan<double>(own, sh.redd, &total);
+    const double target = x * total;
+    const int cand = (own > 0.0 && before <= target) ? (int)threadIdx.x : -1;
+    const int owner = block_max<int>(cand, sh.redi);
+    if (threadIdx.x == 0) sh.found = -1;
+    __syncthreads();
+    if ((int)threadIdx.x == owner) {
+        double cum = before;
+        int pick = -1;
+        for (int i = lo; i < hi; ++i) {
+            const double w = wfn(i, load_logit(r.row, r.dtype, i));
+            if (!(w > 0.0)) continue;
+            cum += w;
+            pick = i;
+            if (cum > target) break;
+        }
+        sh.found = pick;
+    }
+    __syncthreads();
+    const int res = sh.found;
+    *total_out = total;
+    __syncthreads();
+    return res;
+}
+
+// Processes row r with (T, top_k, top_p) into st (LDS).  When `want_set`, also forms the
+// downweighted set of the first F tokens with mass and its normaliser Z for factor C.
+__device__ void process_row(const RowRef& r, float T, int top_k, float top_p, int F, double C, bool want_set,
+                            RowStats& st, RowShared& sh) {
+    // pass 1: bad logits and the (largest key, lowest id) pair
+    unsigned long long best = 0;
+    int bad = 0, finite = 0;
+    for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
+        const float z = load_logit(r.row, r.dtype, i);
+        const uint32_t u = __float_as_uint(z);
+        if ((u & 0x7FFFFFFFu) > 0x7F800000u || u == 0x7F800000u) bad = 1;
+        if ((u & 0x7F800000u) != 0x7F800000u) finite = 1;
+        const unsigned long long pk = ((unsigned long long)order_key(z) << 32) | (unsigned long long)(~(uint32_t)i);
+        best = pk > best ? pk : best;
+    }
+    bad = block_max<int>(bad, sh.redi);
+    finite = block_max<int>(finite, sh.redi);
+    best = block_max<unsigned long long>(best, sh.redu);
+    if (threadIdx.x == 0) {
+        st.bad = (bad || !finite) ? 1 : 0;
+        st.argmax = (int)(~(uint32_t)(best & 0xFFFFFFFFull));
+        st.m = key_to_float((uint32_t)(best >> 32));
+        st.greedy = (T == 0.0f) ? 1 : 0;
+        st.T = (double)T;
+        st.kk = 0;
+        st.idk = r.V - 1;
+        st.kp = 0;
+        st.idp = r.V - 1;
+        st.S = 1.0;
+        st.nS = 0;
+        st.kF = 0xFFFFFFFFu;
+        st.idF = -1;
+        st.C = 1.0;
+        st.Z = 1.0;
+        st.degenerate = 0;
+        for (int f = 0; f < SPEC_MAX_F; ++f) st.ids[f] = -1;
+    }
+    __syncthreads();
+    if (st.bad || st.greedy) return;
+
+    // top-k: exactly top_k tokens, ties by lower id
+    if (top_k > 0 && top_k < r.V) {
+        uint32_t tau;
+        double above, rem;
+        int cnt;
+        radix_select<false>(r, st, [](uint32_t, int, float) { return true; }, (double)top_k, sh, &tau, &above, &cnt,
+                            &rem);
+        const int n = (int)rem;
+        const int idk = (n >= cnt) ? r.V - 1 : nth_id_at_key(r, tau, n, [](uint32_t, int, float) { return true; }, sh);
+        if (threadIdx.x == 0) {
+            st.kk = tau;
+            st.idk = idk;
+        }
+        __syncthreads();
+    }
+
+    // softmax normaliser over the kept tokens
+    double s = 0.0;
+    for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
+        const float z = load_logit(r.row, r.dtype, i);
+        if (rs_kept(st, order_key(z), i)) s += rs_mass(st, z);
+    }
+    const double S_kept = block_sum<double>(s, sh.redd);
+
+    // nucleus: the smallest prefix of the order whose mass reaches top_p * S
+    double S_nuc = S_kept;
+    if ((double)top_p < 1.0) {
+        const double need = (double)top_p * S_kept;
+        uint32_t tau;
+        double above, rem;
+        int cnt;
+        auto kept = [&st](uint32_t key, int i, float) { return rs_kept(st, key, i); };
+        radix_select<true>(r, st, kept, need, sh, &tau, &above, &cnt, &rem);
+        const double e_tau = exp(((double)key_to_float(tau) - (double)st.m) / st.T);
+        int n = cnt;
+        if (e_tau > 0.0) {
+            const double q = ceil((need - above) / e_tau);
+            n = q < 1.0 ? 1 : (q > (double)cnt ? cnt : (int)q);
+        }
+        const int idp = (n >= cnt) ? r.V - 1 : nth_id_at_key(r, tau, n, kept, sh);
+        S_nuc = above + (double)n * e_tau;
+        if (threadIdx.x == 0) {
+            st.kp = tau;
+            st.idp = idp;
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) st.S = S_nuc;
+    __syncthreads();
+
+    if (!want_set || F <= 0) return;
+    // downweighted set: the first F tokens of the order that carry mass
+    int c = 0;
+    for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
+        const float z = load_logit(r.row, r.dtype, i);
+        if (rs_in(st, order_key(z), i) && rs_mass(st, z) > 0.0) ++c;
+    }
+    const int n_pos = block_sum<int>(c, sh.redi);
+    const int Fp = F < n_pos ? F : n_pos;
+    if (Fp <= 0) return;
+    auto pos = [&st](uint32_t key, int i, float z) { return rs_in(st, key, i) && rs_mass(st, z) > 0.0; };
+    uint32_t tau;
+    double above, rem;
+    int cnt;
+    radix_select<false>(r, st, pos, (double)Fp, sh, &tau, &above, &cnt, &rem);
+    const int n = (int)rem;
+    const int idF = (n >= cnt) ? r.V - 1 : nth_id_at_key(r, tau, n, pos, sh);
+    if (threadIdx.x == 0) {
+        st.kF = tau;
+        st.idF = idF;
+        st.nS = Fp;
+        sh.list_n = 0;
+    }
+    __syncthreads();
+    double ps = 0.0;
+    for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
+        const float z = load_logit(r.row, r.dtype, i);
+        const uint32_t key = order_key(z);
+        const double e = rs_mass(st, z);
+        if (rs_in_set(st, key, i, e)) {
+            const int slot = atomicAdd(&sh.list_n, 1);
+            if (slot < SPEC_MAX_F) {
+                sh.list[slot] = i;
+                sh.list_key[slot] = key;
+            }
+            ps += e / st.S;
+        }
+    }
+    const double P_S = block_sum<double>(ps, sh.redd);
+    if (threadIdx.x == 0) {
+        const int nl = sh.list_n < SPEC_MAX_F ? sh.list_n : SPEC_MAX_F;
+        // rank order: key descending, id ascending
+        for (int a = 1; a < nl; ++a) {
+            const int id = sh.list[a];
+            const uint32_t k = sh.list_key[a];
+            int b = a - 1;
+            while (b >= 0 && (sh.list_key[b] < k || (sh.list_key[b] == k && sh.list[b] > id))) {
+                sh.list[b + 1] = sh.list[b];
+                sh.list_key[b + 1] = sh.list_key[b];
+                --b;
+            }
+            sh.list[b + 1] = id;
+            sh.list_key[b + 1] = k;
+        }
+        for (int f = 0; f < nl; ++f) st.ids[f] = sh.list[f];
+        if (C < 1.0) {
+            const double Z = 1.0 - (1.0 - C) * P_S;
+            if (Z > 0.0) {
+                st.C = C;
+                st.Z = Z;
+            } else {
+                st.degenerate = 1;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+}  // namespace sv

@@ -22,6 +22,7 @@ ST_OUTSIDE_DRAFT_SUPPORT = 16
 ST_BAD_LOGIT = 32
 ST_BAD_TOKEN = 64
 ST_DEGENERATE_DOWNWEIGHT = 128
+ST_BAD_PARAM = 256
 FL_NEAR_ACCEPT = 1
 FL_NEAR_CDF = 2
 FL_NEAR_NUCLEUS = 4

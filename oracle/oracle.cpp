@@ -106,6 +106,7 @@ enum : uint32_t {
     ST_BAD_LOGIT = 32,
     ST_BAD_TOKEN = 64,
     ST_DEGENERATE_DOWNWEIGHT = 128,
+    ST_BAD_PARAM = 256,
 };
 // oracle-only near-boundary flags (parity excludes flagged requests and counts them)
 enum : uint32_t { FL_NEAR_ACCEPT = 1, FL_NEAR_CDF = 2, FL_NEAR_NUCLEUS = 4 };
@@ -218,9 +219,9 @@ double downweight(Proc& pr, int F, double C, int32_t* ids, bool* degenerate) {
     }
     double Z = 0.0;
     for (int i = 0; i < V; ++i) Z += pr.p[i] * factor[i];
-    if (!(Z > 0.0)) {
+    if (!(Z > 0.0)) {  // the row is left as it was; its normaliser is 1
         *degenerate = true;
-        return Z;
+        return 1.0;
     }
     for (int i = 0; i < V; ++i) pr.p[i] = pr.p[i] * factor[i] / Z;
     return Z;
@@ -260,6 +261,12 @@ Request verify_one(const void* draft, int draft_rows, const void* target, int dt
                    const Params& prm, int F, double C, int32_t* tokens, bool sample_draft,
                    const double* U) {
     Request out;
+    if (!(prm.temperature >= 0.0f) || std::isinf(prm.temperature) || !(prm.top_p > 0.0f)) {
+        out.status |= ST_BAD_PARAM;
+        out.k = 0;
+        out.t = -1;
+        return out;
+    }
     std::vector<double> z;
     std::vector<Proc> q(K + 1), p(K);
     bool bad = false;
@@ -372,12 +379,8 @@ void parallel_for(int n, int nthreads, Fn fn) {
     for (auto& x : th) x.join();
 }
 
-bool params_ok(const Params* prm, int B) {
-    for (int b = 0; b < B; ++b) {
-        if (!(prm[b].temperature >= 0.0f) || std::isinf(prm[b].temperature)) return false;
-        if (!(prm[b].top_p > 0.0f)) return false;
-    }
-    return true;
+bool param_ok(const Params& prm) {
+    return prm.temperature >= 0.0f && !std::isinf(prm.temperature) && prm.top_p > 0.0f;
 }
 
 }  // namespace
@@ -430,16 +433,20 @@ int orc_downweight(const void* draft, int draft_rows, int dtype, int B, int K, i
                    int nthreads) {
     const Params* prm = static_cast<const Params*>(params);
     if (!draft || B < 1 || K < 1 || V < 1 || draft_rows < K || F < 0 || !(C >= 0.0 && C <= 1.0)) return -1;
-    if (!params_ok(prm, B)) return -1;
     parallel_for(B * K, nthreads, [&](int bj) {
         int b = bj / K, j = bj % K;
         std::vector<double> z;
         load_row(draft, dtype, (size_t)b * draft_rows + j, V, z);
-        Proc pr = process(z, prm[b]);
+        const bool pok = param_ok(prm[b]);
+        Proc pr;
+        if (pok) pr = process(z, prm[b]);
         std::vector<int32_t> ids(F > 0 ? F : 1, -1);
         uint32_t st = 0;
         double Z = 1.0;
-        if (pr.bad) {
+        if (!pok) {
+            st |= ST_BAD_PARAM;
+            pr.bad = true;
+        } else if (pr.bad) {
             st |= ST_BAD_LOGIT;
         } else {
             bool deg = false;
@@ -466,7 +473,6 @@ int orc_verify_u(const void* draft, int draft_rows, const void* target, int dtyp
     if (!draft || !target || !tokens || !U || B < 1 || K < 1 || V < 1 || draft_rows < K || F < 0 ||
         !(C >= 0.0 && C <= 1.0) || (dtype != kFP32 && dtype != kBF16))
         return -1;
-    if (!params_ok(prm, B)) return -1;
     parallel_for(B, nthreads, [&](int b) {
         Request r = verify_one(draft, draft_rows, target, dtype, b, K, V, prm[b], F, C, tokens + (size_t)b * K,
                                sample_draft != 0, U + (size_t)b * (K + 1) * 3);

@@ -1,0 +1,114 @@
+"""Host-side checks of the C-ABI library (no GPU): exports, host helpers, argument errors."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from lossless_speculative_sampling_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "specverify.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(capi.LIB_PATH)
+    names = _declared_functions()
+    assert set(names) == set(capi.EXPORTS)
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_workspace_bytes():
+    assert capi.spec_workspace_bytes(0, 5, 10) == 0
+    a = capi.spec_workspace_bytes(16, 5, 128256)
+    b = capi.spec_workspace_bytes(32, 5, 128256)
+    assert 0 < a <= b and a % 256 == 0
+
+
+@pytest.mark.parametrize("K,budget,a,r", [(5, 32, 0.7, 1.0), (4, 23, 0.6, 0.5), (7, 100, 0.85, 2.0), (3, 8, 0.3, 1.0),
+                                          (1, 1, 0.5, 1.0), (6, 0, 0.9, 0.0), (12, 257, 0.95, 3.0)])
+def test_library_fanout_matches_oracle(K, budget, a, r):
+    assert capi.saguaro_fanout(K, budget, a, r) == oracle.fanout(K, budget, a, r)[1].tolist()
+
+
+def test_fanout_rejects_bad_arguments():
+    for args in [(0, 10, 0.5, 1.0), (5, -1, 0.5, 1.0), (5, 10, 1.0, 1.0), (5, 10, 0.0, 1.0), (5, 10, 0.5, -1.0)]:
+        with pytest.raises(capi.SpecError):
+            capi.saguaro_fanout(*args)
+
+
+def _verify_rc(**kw):
+    L = capi.load().cdll
+    fake = ctypes.c_void_p(0x1000)
+    args = dict(draft=fake, draft_rows=5, target=fake, dtype=1, B=16, K=5, V=128, params=fake, F=4, C=0.3,
+                tokens=fake, seed=1, round_=0, flags=0, out_k=fake, out_t=fake, out_W=None, out_st=None,
+                ws=fake, ws_bytes=1 << 20)
+    args.update(kw)
+    return L.spec_verify(args["draft"], args["draft_rows"], args["target"], args["dtype"], args["B"], args["K"],
+                         args["V"], args["params"], args["F"], ctypes.c_float(args["C"]), args["tokens"], args["seed"],
+                         args["round_"], args["flags"], args["out_k"], args["out_t"], args["out_W"], args["out_st"],
+                         args["ws"], args["ws_bytes"], None)
+
+
+def test_verify_argument_errors_return_before_launch():
+    assert _verify_rc(draft=None) == capi.SPEC_EINVAL
+    assert _verify_rc(tokens=None) == capi.SPEC_EINVAL
+    assert _verify_rc(B=0) == capi.SPEC_EINVAL
+    assert _verify_rc(K=0) == capi.SPEC_EINVAL
+    assert _verify_rc(V=0) == capi.SPEC_EINVAL
+    assert _verify_rc(draft_rows=4) == capi.SPEC_EINVAL
+    assert _verify_rc(draft_rows=7) == capi.SPEC_EINVAL
+    assert _verify_rc(F=-1) == capi.SPEC_EINVAL
+    assert _verify_rc(F=capi.SPEC_MAX_F + 1) == capi.SPEC_EINVAL
+    assert _verify_rc(C=1.5) == capi.SPEC_EINVAL
+    assert _verify_rc(C=float("nan")) == capi.SPEC_EINVAL
+    assert _verify_rc(flags=2) == capi.SPEC_EINVAL
+    assert _verify_rc(dtype=7) == capi.SPEC_EDTYPE
+    assert _verify_rc(ws=None) == capi.SPEC_EWORKSPACE
+    assert _verify_rc(ws_bytes=capi.spec_workspace_bytes(16, 5, 128) - 1) == capi.SPEC_EWORKSPACE
+
+
+def test_other_entry_points_argument_errors():
+    L = capi.load().cdll
+    fake = ctypes.c_void_p(0x1000)
+    assert L.saguaro_downweight(None, 5, 1, 16, 5, 128, fake, 4, ctypes.c_float(0.3), fake, None, None, None,
+                                None) == capi.SPEC_EINVAL
+    assert L.saguaro_downweight(fake, 5, 3, 16, 5, 128, fake, 4, ctypes.c_float(0.3), fake, None, None, None,
+                                None) == capi.SPEC_EDTYPE
+    assert L.saguaro_downweight(fake, 4, 1, 16, 5, 128, fake, 4, ctypes.c_float(0.3), fake, None, None, None,
+                                None) == capi.SPEC_EINVAL
+    assert L.saguaro_cache_build(fake, 1, 16, 5, 128, fake, 32, 1.5, 1.0, None, fake, None) == capi.SPEC_EINVAL
+    assert L.saguaro_cache_build(fake, 9, 16, 5, 128, fake, 32, 0.7, 1.0, None, fake, None) == capi.SPEC_EDTYPE
+    assert L.saguaro_cache_build(fake, 1, 16, 5, 128, None, 32, 0.7, 1.0, None, fake, None) == capi.SPEC_EINVAL
+    shape = (ctypes.c_int32 * 2)(0, 7)
+    assert L.saguaro_cache_lookup(1, fake, ctypes.cast(shape, ctypes.c_void_p), 0, 4, fake, fake, fake, fake, None,
+                                  None) == capi.SPEC_EINVAL
+    assert L.saguaro_cache_lookup(2, fake, ctypes.cast(shape, ctypes.c_void_p), 0, 4, fake, fake, fake, fake, None,
+                                  None) == capi.SPEC_EINVAL
+    assert L.saguaro_cache_lookup(0, fake, None, 5, 4, fake, fake, fake, fake, None, None) == capi.SPEC_EINVAL
+
+
+def test_generator_shapes_and_determinism():
+    from lossless_speculative_sampling_amd import synth
+    a = synth.saguaro(B=2, K=3, V=1000)
+    b = synth.saguaro(B=2, K=3, V=1000)
+    assert a.draft.shape == (2, 4, 1000) and a.target.shape == (2, 4, 1000)
+    assert (a.draft == b.draft).all() and (a.target == b.target).all()
+    assert a.draft.dtype == np.uint16
+    c = a.without_cache_row()
+    assert c.draft.shape == (2, 3, 1000) and c.draft.flags.c_contiguous
+    t = synth.tree(n_req=2, kappa=3, gamma=2, V=300)
+    assert t.draft.shape == (6, 2, 300) and t.tokens.shape == (6, 2)
+    # branch j shares rows and tokens with branch 0 up to depth j-1 and differs at depth j-1
+    assert (t.draft[1, 0] == t.draft[0, 0]).all() and t.tokens[1, 0] != t.tokens[0, 0]
+    assert t.tokens[2, 0] == t.tokens[0, 0] and t.tokens[2, 1] != t.tokens[0, 1]
+    x = np.array([1.0, -2.5, 3.14159, 1e-30, -0.0], np.float32)
+    assert np.allclose(synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x)), x, rtol=1 / 128)

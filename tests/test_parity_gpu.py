@@ -1,0 +1,187 @@
+"""GPU <-> oracle parity through the C ABI (needs an MI355X).
+
+Integers (k, t*, sampled draft tokens, status bits, downweighted sets, cache token sets, hit
+flags, slots, branch reuse) must be equal on every request the oracle does not flag as a near
+tie (a uniform, or the nucleus target, within 1e-6 relative of a boundary); floats within 1e-5
+relative (fp32 inputs) or 2e-3 (bf16 inputs).  Flagged requests are counted and reported.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lossless_speculative_sampling_amd import capi, synth
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {synth.FP32: 1e-5, synth.BF16: 2e-3}
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(w, tokens=None, seed=None, round_=0):
+    sample = tokens is None
+    prm = capi.params_tensor(w.temperature, w.top_k, w.top_p)
+    tok = torch.zeros((w.B, w.K), dtype=torch.int32, device="cuda") if sample else dev(np.asarray(tokens, np.int32))
+    out = capi.spec_verify(dev(w.draft), dev(w.target), w.K, prm, tok, F=w.F, C=w.C,
+                           seed=w.seed if seed is None else seed, round_=round_,
+                           flags=capi.SPEC_SAMPLE_DRAFT if sample else 0)
+    torch.cuda.synchronize()
+    return (out.k.cpu().numpy(), out.tstar.cpu().numpy(), out.resid_mass.cpu().numpy(),
+            out.status.cpu().numpy().astype(np.uint32), out.tokens.cpu().numpy())
+
+
+def run_oracle(w, tokens=None, seed=None, round_=0):
+    return oracle.verify(w.draft, w.target, w.dtype, w.K, w.params(), F=w.F, C=float(np.float32(w.C)),
+                         tokens=tokens, seed=w.seed if seed is None else seed, round_=round_)
+
+
+def check_verify(w, tokens=None, seed=None, round_=0, label=""):
+    say(f"[parity] {label} {w.name} B={w.B} K={w.K} V={w.V} dtype={w.dtype} sample={tokens is None}")
+    k, t, W, st, tok = run_gpu(w, tokens, seed, round_)
+    o = run_oracle(w, tokens, seed, round_)
+    ok = o.flags == 0
+    bad = np.flatnonzero(ok & ((k != o.k) | (t != o.t) | (st != o.status)))
+    assert len(bad) == 0, (f"{len(bad)} mismatches, first {bad[:5]}: gpu k={k[bad[:5]]} t={t[bad[:5]]} "
+                           f"st={st[bad[:5]]} | oracle k={o.k[bad[:5]]} t={o.t[bad[:5]]} st={o.status[bad[:5]]}")
+    if tokens is None:
+        good = ok & ((o.status & (oracle.ST_BAD_LOGIT | oracle.ST_BAD_PARAM)) == 0)
+        assert (tok[good] == o.tokens[good]).all()
+    np.testing.assert_allclose(W[ok], o.W[ok], rtol=RTOL[w.dtype], atol=1e-6)
+    say(f"[parity] {label} ok: flagged {int((~ok).sum())} of {w.B}; mean k {k.mean():.3f}")
+    return o, int((~ok).sum())
+
+
+def test_vanilla_fp32_ten_thousand_rounds():
+    check_verify(synth.vanilla(B=10000), label="vanilla")
+
+
+def test_llama_vocab_bf16_nucleus():
+    check_verify(synth.llama(B=12), label="llama")
+
+
+def test_saguaro_full_size_sampled_and_given_tokens():
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=False)
+    o, _ = check_verify(w, label="saguaro-sampled")
+    check_verify(w, tokens=o.tokens, label="saguaro-given")
+    # also with the cache row present in the draft tensor
+    w4 = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
+    check_verify(w4, tokens=o.tokens, label="saguaro-cache-row")
+
+
+def test_deterministic_repeat():
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=False)
+    a = run_gpu(w)
+    b = run_gpu(w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_downweight_parity():
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=False)
+    say("[parity] downweight B=16 K=5 V=128256")
+    prm = capi.params_tensor(w.temperature, w.top_k, w.top_p)
+    ids, Z, probs, st = capi.saguaro_downweight(dev(w.draft), w.K, prm, w.F, w.C, want_probs=True)
+    torch.cuda.synchronize()
+    oids, oZ, oprobs, ost = oracle.downweight(w.draft, w.dtype, w.K, w.params(), w.F, float(np.float32(w.C)),
+                                              want_probs=True)
+    assert (ids.cpu().numpy() == oids).all()
+    assert (st.cpu().numpy().astype(np.uint32) == ost).all()
+    np.testing.assert_allclose(Z.cpu().numpy(), oZ, rtol=1e-6)
+    np.testing.assert_allclose(probs.cpu().numpy(), oprobs, rtol=2e-6, atol=1e-12)
+
+
+def test_cache_build_and_lookup():
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
+    say("[parity] cache build + lookup B=16 K=5 V=128256 budget=32")
+    o = run_oracle(w.without_cache_row())
+    cache, fan = capi.saguaro_cache_build(dev(w.draft), w.K, dev(o.tokens), w.budget, w.a, w.r)
+    torch.cuda.synchronize()
+    assert fan == [7, 6, 5, 4, 4, 6]
+    ocache = oracle.cache_build(w.draft, w.dtype, w.K, o.tokens, np.array(fan, np.int32))
+    assert (cache.cpu().numpy() == ocache).all()
+    slot, hit, batch = capi.saguaro_cache_lookup(0, cache, fan, w.K, w.B, dev(o.k), dev(o.t))
+    torch.cuda.synchronize()
+    oslot, ohit, obatch = oracle.cache_lookup(0, ocache, fan, w.K, w.B, o.k, o.t)
+    assert (slot.cpu().numpy() == oslot).all() and (hit.cpu().numpy() == ohit).all()
+    assert (batch.cpu().numpy() == obatch).all()
+    say(f"[parity] cache ok: hits {int(obatch[0])}/{w.B}")
+
+
+def test_tree_chains_and_branch_reuse():
+    w = synth.tree(n_req=4)
+    say(f"[parity] tree chains B={w.B} gamma={w.K} V={w.V} top-k 50")
+    o, _ = check_verify(w, tokens=w.tokens, label="tree")
+    shape = [w.kappa, w.gamma]
+    n_req = w.B // w.kappa
+    br = dev(w.tokens)
+    slot, hit, batch = capi.saguaro_cache_lookup(1, br, shape, 0, n_req, dev(o.k), dev(o.t))
+    torch.cuda.synchronize()
+    oslot, ohit, obatch = oracle.cache_lookup(1, w.tokens, shape, 0, n_req, o.k, o.t)
+    assert (slot.cpu().numpy() == oslot).all() and (batch.cpu().numpy() == obatch).all()
+
+
+# ------------------------------------------------------------------------------------------
+# edge cases
+# ------------------------------------------------------------------------------------------
+def _work(draft, target, dtype, K, T, tk, tp, F=0, C=1.0, seed=99):
+    B, _, V = draft.shape
+    Tv, kv, pv = (np.broadcast_to(np.asarray(x), (B,)).copy() for x in (T, tk, tp))
+    return synth.Workload("edge", dtype, B, K, V, np.ascontiguousarray(draft), np.ascontiguousarray(target),
+                          Tv.astype(np.float32), kv.astype(np.int32), pv.astype(np.float32), F=F, C=C, seed=seed)
+
+
+@pytest.mark.parametrize("dtype", [synth.FP32, synth.BF16])
+@pytest.mark.parametrize("V", [1, 2, 63, 1000, 4097])
+def test_shapes_and_parameter_mix(dtype, V):
+    rng = np.random.default_rng(V * 7 + dtype)
+    B, K = 24, 3
+    d, t = synth.random_rows(rng, B, K, V, dtype)
+    T = rng.choice([0.0, 0.5, 1.0, 1.7], B)
+    tk = rng.choice([0, 1, 2, 5, V, V + 3], B)
+    tp = rng.choice([0.01, 0.3, 0.9, 1.0, 1.5], B)
+    w = _work(d, t, dtype, K, T, tk, tp, F=2, C=0.4)
+    check_verify(w, label=f"mix V={V}")
+    check_verify(w, tokens=rng.integers(0, V, (B, K)), label=f"mix-given V={V}")
+
+
+def test_special_rows_and_bad_inputs():
+    rng = np.random.default_rng(5)
+    B, K, V = 12, 2, 300
+    d, t = synth.random_rows(rng, B, K, V, synth.FP32)
+    d[0] = -np.inf
+    d[0, :, 17] = 1.0                 # one finite draft logit per row
+    t[1, 1, 5] = np.nan               # NaN -> bad logit
+    t[2, 0] = -np.inf                 # a target row with no finite logit
+    d[3] *= 1e4                       # masses underflow to exactly 0
+    t[3] *= 1e4
+    d[4] = np.round(d[4])             # heavy ties
+    t[4] = np.round(t[4])
+    T = np.ones(B, np.float32)
+    T[5] = -1.0                       # bad parameter
+    tp = np.full(B, 0.9, np.float32)
+    tp[6] = 0.0                       # bad parameter
+    tk = np.zeros(B, np.int32)
+    tk[7] = 2                         # with F = 4, C = 0: the set holds all mass -> degenerate
+    w = _work(d, t, synth.FP32, K, T, tk, tp, F=4, C=0.0)
+    check_verify(w, label="special-sampled")
+    tok = rng.integers(0, V, (B, K)).astype(np.int32)
+    tok[8, 1] = V                     # bad token
+    tok[9, 0] = -1
+    check_verify(w, tokens=tok, label="special-given")
+
+
+def test_vocabulary_of_one():
+    d = np.zeros((2, 1, 1), np.float32)
+    t = np.zeros((2, 2, 1), np.float32)
+    w = _work(d, t, synth.FP32, 1, [1.0, 0.0], 0, 1.0)
+    o, _ = check_verify(w, label="V=1")
+    assert (o.k == 1).all() and (o.t == 0).all()
