@@ -114,7 +114,7 @@ def main():
     targets = [t0] + [t0.clone() for _ in range(copies - 1)]
     prm = capi.params_tensor(w.temperature, w.top_k, w.top_p, device=dev)
     tokens = torch.zeros((B, K), dtype=torch.int32, device=dev)
-    ws = torch.empty(capi.spec_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    ws = capi.new_workspace(B, K, V, dev)
     out = capi.VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                          torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                          tokens)

@@ -93,7 +93,10 @@ enum {
     SPEC_ST_BAD_TOKEN = 64,                /* a draft token outside [0, V): k = 0, t* = -1 */
     SPEC_ST_DEGENERATE_DOWNWEIGHT = 128,   /* C = 0 and the set holds all the draft mass: the
                                               row is left undownweighted */
-    SPEC_ST_BAD_PARAM = 256                /* invalid spec_params: k = 0, t* = -1 */
+    SPEC_ST_BAD_PARAM = 256,               /* invalid spec_params: k = 0, t* = -1 */
+    SPEC_ST_SYNC_TIMEOUT = 512             /* a workgroup rendezvous gave up waiting (never expected;
+                                              results of the request are invalid and the workspace
+                                              must be zero-filled again) */
 };
 
 /* Uniforms.  Counter-based Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and counter
@@ -101,8 +104,10 @@ enum {
  * becomes the uniform ((w >> 12) + 0.5) * 2^-52 in (0, 1).  Word 0: acceptance u_j; word 1:
  * residual / bonus v_j; word 2: draft sampling (SPEC_SAMPLE_DRAFT). */
 
-/* Bytes of scratch spec_verify needs for B requests of K draft positions over V tokens.
- * Pure host function; the workspace needs no initialisation and holds nothing between calls. */
+/* Bytes of scratch spec_verify needs for B requests of K draft positions over V tokens (pure
+ * host function).  The workspace must be zero-filled before its first use; every call that
+ * completes leaves it zero-filled again, so it can be reused without clearing.  It carries no
+ * results between calls.  One workspace serves one call at a time. */
 size_t spec_workspace_bytes(int B, int K, int V);
 
 /* spec_verify - batched speculative-sampling verification ([SpS] sections 1 and 3; [SSD]

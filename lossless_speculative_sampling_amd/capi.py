@@ -26,6 +26,7 @@ ST_BAD_LOGIT = 32
 ST_BAD_TOKEN = 64
 ST_DEGENERATE_DOWNWEIGHT = 128
 ST_BAD_PARAM = 256
+ST_SYNC_TIMEOUT = 512
 
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
            "saguaro_cache_lookup")
@@ -115,6 +116,11 @@ def params_tensor(temperature, top_k, top_p, device="cuda") -> torch.Tensor:
     return rec.to(device)
 
 
+def new_workspace(B: int, K: int, V: int, device="cuda") -> torch.Tensor:
+    """Zero-filled spec_verify workspace (the library leaves it zero-filled after every call)."""
+    return torch.zeros(max(spec_workspace_bytes(B, K, V), 1), dtype=torch.uint8, device=device)
+
+
 @dataclass
 class VerifyOut:
     k: torch.Tensor
@@ -135,9 +141,8 @@ def spec_verify(draft: torch.Tensor, target: torch.Tensor, K: int, params: torch
         out = VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                         torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                         tokens)
-    need = spec_workspace_bytes(B, K, V)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = new_workspace(B, K, V, dev)
     rc = load().cdll.spec_verify(_ptr(draft), Kd, _ptr(target), dtype_code(draft), B, K, V, _ptr(params), F,
                                  ctypes.c_float(C), _ptr(tokens), seed, round_, flags, _ptr(out.k), _ptr(out.tstar),
                                  _ptr(out.resid_mass), _ptr(out.status), _ptr(workspace), workspace.numel(),

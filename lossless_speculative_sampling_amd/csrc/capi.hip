@@ -2,6 +2,7 @@
 #include <cmath>
 #include <cstring>
 
+#include "fastpath.h"
 #include "generic.h"
 
 using namespace sv;
@@ -51,7 +52,7 @@ extern "C" {
 
 size_t spec_workspace_bytes(int B, int K, int V) {
     if (B < 1 || K < 1 || V < 1) return 0;
-    return align_up((size_t)B * (K + 1) * sizeof(UnitRec), 256);
+    return align_up((size_t)B * (K + 1) * sizeof(UnitRec), 256) + fast::fast_plan(B, K, V).ws_bytes;
 }
 
 int spec_verify(const void* draft_logits, int draft_rows, const void* target_logits, int dtype, int B, int K,
@@ -67,6 +68,10 @@ int spec_verify(const void* draft_logits, int draft_rows, const void* target_log
     if (!workspace || workspace_bytes < need) return SPEC_EWORKSPACE;
     VerifyArgs a{draft_logits, target_logits, draft_rows, dtype, B, K, V, params, F, C, draft_tokens, seed,
                  round, flags, out_k, out_tstar, out_resid_mass, out_status, static_cast<UnitRec*>(workspace)};
+    if (fast::fast_path_applies(a)) {
+        const size_t gen = align_up((size_t)B * (K + 1) * sizeof(UnitRec), 256);
+        return fast::fast_verify(a, static_cast<char*>(workspace) + gen, workspace_bytes - gen, stream);
+    }
     hipLaunchKernelGGL(generic_unit_kernel, dim3((unsigned)(B * (K + 1))), dim3(kRowThreadsHost), 0, stream, a);
     if (launch_status() != SPEC_OK) return SPEC_EHIP;
     hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, a);

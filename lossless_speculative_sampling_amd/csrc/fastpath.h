@@ -1,0 +1,63 @@
+// Register-resident bf16 verification path (one kernel per call).
+//
+// A (request b, position j) unit covers draft row j and target row j (target row K alone for
+// j = K).  Each unit is split into slices of kSliceCols token columns; the slices of a unit
+// run on one XCD (workgroup b -> XCD b % 8), hold their columns in registers, count every
+// distinct bf16 logit in LDS, publish compact summaries, meet once at a unit barrier through
+// that XCD's L2, resolve the exact processed distributions redundantly, and, when the draft
+// token is rejected (or at the bonus position), sum the residual (q - p)+ over 512-column
+// chunks.  The last slice of a request to finish picks k and t*.
+#pragma once
+
+#include "generic.h"
+
+namespace sv {
+namespace fast {
+
+constexpr int kThreads = 512;                  // workgroup size (8 waves)
+constexpr int kColsPerThread = 32;             // per row
+constexpr int kLoads = kColsPerThread / 8;     // 16-byte loads per row per thread
+constexpr int kSliceCols = kThreads * kColsPerThread;  // 16384
+constexpr int kChunkCols = 512;                // one wave x one 16-byte load per lane
+constexpr int kChunks = kSliceCols / kChunkCols;       // 32 per slice
+constexpr int kXcd = 8;                        // XCDs on MI355X
+
+// Exact bins: one per bf16 value with |z| in [2^-6, 2^5), plus zero.  Negative values occupy
+// bins [0, kNegBins) in ascending value order, zero bin kZeroBin, positive values
+// [kPosBase, kPosBase + kNegBins).  Bins are grouped by 64 (aligned), zero in its own group.
+constexpr int kExpLo = 121;                    // bf16 exponent field of 2^-6
+constexpr int kExpHi = 132;                    // first exponent outside (2^5)
+constexpr int kNegBins = (kExpHi - kExpLo) * 128;      // 1408
+constexpr int kGroup = 64;
+constexpr int kZeroBin = kNegBins;                     // 1408
+constexpr int kPosBase = kNegBins + kGroup;            // 1472
+constexpr int kBins = kPosBase + kNegBins;             // 2880 (padded)
+constexpr int kGroups = kBins / kGroup;                // 45
+constexpr int kNegGroups = kNegBins / kGroup;          // 22
+constexpr int kZeroGroup = kNegGroups;                 // 22
+// Segments in descending value order: huge positive specials, positive groups (high to low),
+// tiny positive specials, the zero group, tiny negative specials, negative groups (high to
+// low), huge negative specials.
+constexpr int kSegs = kGroups + 4;                     // 49
+constexpr int kSegHugePos = 0;
+constexpr int kSegTinyPos = 1 + kNegGroups;            // 23
+constexpr int kSegZero = kSegTinyPos + 1;              // 24
+constexpr int kSegTinyNeg = kSegZero + 1;              // 25
+constexpr int kSegHugeNeg = kSegs - 1;                 // 48
+
+constexpr int kTop = 64;        // per slice-row candidate list (top by token order)
+constexpr int kSpecial = 64;    // per slice-row finite values outside the exact bins
+
+struct FastPlan {
+    int nS;          // slices per row
+    int units;       // B * (K + 1)
+    int grid;        // workgroups launched
+    size_t ws_bytes; // fast workspace bytes
+};
+
+FastPlan fast_plan(int B, int K, int V);
+bool fast_path_applies(const VerifyArgs& a);
+int fast_verify(const VerifyArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace fast
+}  // namespace sv

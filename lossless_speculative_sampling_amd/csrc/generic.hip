@@ -16,98 +16,7 @@ __global__ __launch_bounds__(kRowThreads) void generic_unit_kernel(VerifyArgs a)
     __shared__ RowShared sh;
     __shared__ RowStats stq, stp;
     const int unit = blockIdx.x;
-    const int b = unit / (a.K + 1);
-    const int j = unit % (a.K + 1);
-    UnitRec* rec = a.units + unit;
-    const spec_params prm = a.params[b];
-    const bool param_ok = prm.temperature >= 0.0f && !isinf(prm.temperature) && prm.top_p > 0.0f;
-    if (!param_ok) {
-        if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, kStBadParam, -1};
-        return;
-    }
-    const size_t tstride = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
-    const char* trow = static_cast<const char*>(a.target) + ((size_t)b * (a.K + 1) + j) * tstride;
-    RowRef rq{trow, a.dtype, a.V};
-    process_row(rq, prm.temperature, prm.top_k, prm.top_p, 0, 1.0, false, stq, sh);
-    RowRef rp{nullptr, a.dtype, a.V};
-    if (j < a.K) {
-        rp.row = static_cast<const char*>(a.draft) + ((size_t)b * a.draft_rows + j) * tstride;
-        const bool dw = a.F > 0 && a.C < 1.0f;
-        process_row(rp, prm.temperature, prm.top_k, prm.top_p, a.F, (double)a.C, dw, stp, sh);
-    }
-    if (stq.bad || (j < a.K && stp.bad)) {
-        if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, kStBadLogit, -1};
-        return;
-    }
-    uint32_t status = (j < a.K && stp.degenerate) ? kStDegenerate : 0u;
-    const bool greedy = stq.greedy != 0;
-
-    if (j == a.K) {  // bonus position
-        int t;
-        if (greedy) {
-            t = stq.argmax;
-        } else {
-            const double v = uniform_at(a.seed, a.round, b, j, 1);
-            double tot;
-            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
-        }
-        if (threadIdx.x == 0) *rec = UnitRec{1, t, 0.0f, status, -1};
-        return;
-    }
-
-    // draft token s_j (sampled here under SPEC_SAMPLE_DRAFT)
-    int s;
-    if (a.flags & SPEC_SAMPLE_DRAFT) {
-        if (greedy) {
-            s = stp.argmax;
-        } else {
-            const double x = uniform_at(a.seed, a.round, b, j, 2);
-            double tot;
-            s = inverse_cdf(rp, x, [&](int i, float z) { return rs_prob_dw(stp, z, i); }, sh, &tot);
-        }
-        if (threadIdx.x == 0) a.tokens[(size_t)b * a.K + j] = s;
-    } else {
-        s = a.tokens[(size_t)b * a.K + j];
-    }
-    if (s < 0 || s >= a.V) {
-        if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, status | kStBadToken, s};
-        return;
-    }
-
-    bool accept;
-    if (greedy) {
-        accept = (s == stq.argmax);
-    } else {
-        const double ps = rs_prob_dw(stp, load_logit(rp.row, a.dtype, s), s);
-        const double qs = rs_prob(stq, load_logit(rq.row, a.dtype, s), s);
-        if (!(ps > 0.0)) status |= kStOutside;
-        const double u = uniform_at(a.seed, a.round, b, j, 0);
-        accept = u * ps < qs;
-    }
-    if (accept) {
-        if (threadIdx.x == 0) *rec = UnitRec{1, -1, 0.0f, status, s};
-        return;
-    }
-    int t;
-    double W = 0.0;
-    if (greedy) {
-        t = stq.argmax;
-    } else {
-        const double v = uniform_at(a.seed, a.round, b, j, 1);
-        // residual (q - p')+ at this position; rows are read pairwise by token id
-        auto resid = [&](int i, float zq) {
-            const double q = rs_prob(stq, zq, i);
-            const double p = rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i);
-            return q > p ? q - p : 0.0;
-        };
-        t = inverse_cdf(rq, v, resid, sh, &W);
-        if (t < 0) {  // no residual mass: fall back to q itself
-            status |= kStEmptyResidual;
-            double tot;
-            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
-        }
-    }
-    if (threadIdx.x == 0) *rec = UnitRec{0, t, (float)W, status, s};
+    unit_verify(a, unit / (a.K + 1), unit % (a.K + 1), a.units + unit, sh, stq, stp);
 }
 
 // Per request: k = first rejected position (K if none), t* = that unit's candidate.

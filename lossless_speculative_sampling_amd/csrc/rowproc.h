@@ -225,7 +225,7 @@ __device__ int inverse_cdf(const RowRef& r, double x, Weight wfn, RowShared& sh,
 
 // Processes row r with (T, top_k, top_p) into st (LDS).  When `want_set`, also forms the
 // downweighted set of the first F tokens with mass and its normaliser Z for factor C.
-__device__ void process_row(const RowRef& r, float T, int top_k, float top_p, int F, double C, bool want_set,
+__device__ inline void process_row(const RowRef& r, float T, int top_k, float top_p, int F, double C, bool want_set,
                             RowStats& st, RowShared& sh) {
     // pass 1: bad logits and the (largest key, lowest id) pair
     unsigned long long best = 0;
@@ -379,6 +379,101 @@ __device__ void process_row(const RowRef& r, float T, int top_k, float top_p, in
         }
     }
     __syncthreads();
+}
+
+// The verification of one (request b, position j) unit by the whole workgroup; the record is
+// written by thread 0.  Shared by the general kernel and the fast kernel's fallback.
+__device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* rec, RowShared& sh, RowStats& stq,
+                            RowStats& stp) {
+    const spec_params prm = a.params[b];
+    const bool param_ok = prm.temperature >= 0.0f && !isinf(prm.temperature) && prm.top_p > 0.0f;
+    if (!param_ok) {
+        if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, kStBadParam, -1};
+        return;
+    }
+    const size_t tstride = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
+    const char* trow = static_cast<const char*>(a.target) + ((size_t)b * (a.K + 1) + j) * tstride;
+    RowRef rq{trow, a.dtype, a.V};
+    process_row(rq, prm.temperature, prm.top_k, prm.top_p, 0, 1.0, false, stq, sh);
+    RowRef rp{nullptr, a.dtype, a.V};
+    if (j < a.K) {
+        rp.row = static_cast<const char*>(a.draft) + ((size_t)b * a.draft_rows + j) * tstride;
+        const bool dw = a.F > 0 && a.C < 1.0f;
+        process_row(rp, prm.temperature, prm.top_k, prm.top_p, a.F, (double)a.C, dw, stp, sh);
+    }
+    if (stq.bad || (j < a.K && stp.bad)) {
+        if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, kStBadLogit, -1};
+        return;
+    }
+    uint32_t status = (j < a.K && stp.degenerate) ? kStDegenerate : 0u;
+    const bool greedy = stq.greedy != 0;
+
+    if (j == a.K) {  // bonus position
+        int t;
+        if (greedy) {
+            t = stq.argmax;
+        } else {
+            const double v = uniform_at(a.seed, a.round, b, j, 1);
+            double tot;
+            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
+        }
+        if (threadIdx.x == 0) *rec = UnitRec{1, t, 0.0f, status, -1};
+        return;
+    }
+
+    // draft token s_j (sampled here under SPEC_SAMPLE_DRAFT)
+    int s;
+    if (a.flags & SPEC_SAMPLE_DRAFT) {
+        if (greedy) {
+            s = stp.argmax;
+        } else {
+            const double x = uniform_at(a.seed, a.round, b, j, 2);
+            double tot;
+            s = inverse_cdf(rp, x, [&](int i, float z) { return rs_prob_dw(stp, z, i); }, sh, &tot);
+        }
+        if (threadIdx.x == 0) a.tokens[(size_t)b * a.K + j] = s;
+    } else {
+        s = a.tokens[(size_t)b * a.K + j];
+    }
+    if (s < 0 || s >= a.V) {
+        if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, status | kStBadToken, s};
+        return;
+    }
+
+    bool accept;
+    if (greedy) {
+        accept = (s == stq.argmax);
+    } else {
+        const double ps = rs_prob_dw(stp, load_logit(rp.row, a.dtype, s), s);
+        const double qs = rs_prob(stq, load_logit(rq.row, a.dtype, s), s);
+        if (!(ps > 0.0)) status |= kStOutside;
+        const double u = uniform_at(a.seed, a.round, b, j, 0);
+        accept = u * ps < qs;
+    }
+    if (accept) {
+        if (threadIdx.x == 0) *rec = UnitRec{1, -1, 0.0f, status, s};
+        return;
+    }
+    int t;
+    double W = 0.0;
+    if (greedy) {
+        t = stq.argmax;
+    } else {
+        const double v = uniform_at(a.seed, a.round, b, j, 1);
+        // residual (q - p')+ at this position; rows are read pairwise by token id
+        auto resid = [&](int i, float zq) {
+            const double q = rs_prob(stq, zq, i);
+            const double p = rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i);
+            return q > p ? q - p : 0.0;
+        };
+        t = inverse_cdf(rq, v, resid, sh, &W);
+        if (t < 0) {  // no residual mass: fall back to q itself
+            status |= kStEmptyResidual;
+            double tot;
+            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
+        }
+    }
+    if (threadIdx.x == 0) *rec = UnitRec{0, t, (float)W, status, s};
 }
 
 }  // namespace sv

@@ -111,7 +111,11 @@ enum : uint32_t {
 // oracle-only near-boundary flags (parity excludes flagged requests and counts them)
 enum : uint32_t { FL_NEAR_ACCEPT = 1, FL_NEAR_CDF = 2, FL_NEAR_NUCLEUS = 4 };
 
+// Near-tie bands.  A uniform within 1e-6 relative of an acceptance or CDF boundary flags the
+// request.  The nucleus cut compares fp64 masses (per-value sums of exact counts on the GPU,
+// rounding ~1e-15), so its band is 1e-9 of the row mass.
 const double kNearRel = 1e-6;
+const double kNearNucleus = 1e-9;
 
 // Token order used by every selection: logit descending, token id ascending on equal logits
 // (IEEE equality, so -0 and +0 tie).
@@ -181,7 +185,7 @@ Proc process(const std::vector<double>& z, const Params& prm) {
                 break;
             }
         }
-        if (cum - target <= kNearRel * S || target - prev <= kNearRel * S) r.near_cut = true;
+        if (cum - target <= kNearNucleus * S || target - prev <= kNearNucleus * S) r.near_cut = true;
         for (int t = cut; t < n_kept; ++t) e[r.order[t]] = 0.0;
         n_kept = cut;
     }

@@ -185,3 +185,87 @@ def test_vocabulary_of_one():
     w = _work(d, t, synth.FP32, 1, [1.0, 0.0], 0, 1.0)
     o, _ = check_verify(w, label="V=1")
     assert (o.k == 1).all() and (o.t == 0).all()
+
+
+# ------------------------------------------------------------------------------------------
+# bf16 rows with V a multiple of 8 and given draft tokens take the register-resident path
+# ------------------------------------------------------------------------------------------
+def _zipf_work(rng, B, K, V, T, tk, tp, F=0, C=1.0, noise=0.8, seed=1234):
+    target = synth.zipf_rows(rng, B * (K + 1), V).reshape(B, K + 1, V)
+    draft = target[:, :K] + noise * rng.standard_normal((B, K, V), dtype=np.float32)
+    w = _work(synth.f32_to_bf16_bits(draft), synth.f32_to_bf16_bits(target), synth.BF16, K, T, tk, tp, F=F, C=C,
+              seed=seed)
+    return w
+
+
+def _oracle_tokens(w):
+    return run_oracle(w).tokens
+
+
+def test_fast_llama_given_tokens():
+    w = synth.llama(B=24)
+    check_verify(w, tokens=_oracle_tokens(w), label="fast-llama")
+
+
+@pytest.mark.parametrize("V", [2048, 4096, 16392, 40000, 151936])
+def test_fast_parameter_mix(V):
+    rng = np.random.default_rng(V)
+    B, K = 24, 3
+    T = rng.choice([0.0, 0.6, 1.0, 1.5], B)
+    tk = rng.choice([0, 1, 5, 64, 65, 200, 3000], B)
+    tp = rng.choice([0.05, 0.5, 0.9, 0.99, 1.0], B)
+    w = _zipf_work(rng, B, K, V, T, tk, tp, F=4, C=0.3)
+    check_verify(w, tokens=_oracle_tokens(w), label=f"fast-mix V={V}")
+    check_verify(w, tokens=rng.integers(0, V, (B, K)), label=f"fast-mix-random V={V}")
+
+
+def test_fast_ties_and_large_sets():
+    rng = np.random.default_rng(77)
+    B, K, V = 16, 2, 20000
+    t = np.round(rng.normal(0, 2, (B, K + 1, V))).astype(np.float32)  # ~15 distinct values
+    d = np.round(t[:, :K] + rng.normal(0, 1, (B, K, V))).astype(np.float32)
+    T = rng.choice([0.5, 1.0, 2.0], B)
+    tk = rng.choice([0, 30, 64, 500, 15000], B)
+    tp = rng.choice([0.3, 0.8, 1.0], B)
+    w = _work(synth.f32_to_bf16_bits(d), synth.f32_to_bf16_bits(t), synth.BF16, K, T, tk, tp, F=64, C=0.2)
+    check_verify(w, tokens=_oracle_tokens(w), label="fast-ties")
+
+
+def test_fast_special_values_and_fallback():
+    rng = np.random.default_rng(78)
+    B, K, V = 12, 2, 32768
+    target = synth.zipf_rows(rng, B * (K + 1), V).reshape(B, K + 1, V)
+    draft = target[:, :K] + 0.7 * rng.standard_normal((B, K, V), dtype=np.float32)
+    # values outside the exact bins: tiny, zero, huge; masked tokens
+    for arr in (target, draft):
+        idx = rng.integers(0, V, (arr.shape[0], arr.shape[1], 20))
+        vals = rng.choice([1e-3, -1e-3, 0.0, -0.0, 40.0, -40.0, 1e4, -1e4, 5e-5], idx.shape).astype(np.float32)
+        np.put_along_axis(arr, idx, vals, axis=2)
+        mask = rng.integers(0, V, (arr.shape[0], arr.shape[1], 50))
+        np.put_along_axis(arr, mask, -np.inf, axis=2)
+    target[3, 1, :400] = 2e-4   # > 64 finite specials in one slice: general path for that unit
+    draft[5, 0, 100:300] = -100.0
+    target[7, 2, 11] = 60.0     # a huge maximum
+    T = np.full(B, 1.0, np.float32)
+    tk = rng.choice([0, 3, 100], B)
+    tp = rng.choice([0.9, 0.999, 1.0], B)
+    w = _work(synth.f32_to_bf16_bits(draft), synth.f32_to_bf16_bits(target), synth.BF16, K, T, tk, tp, F=4, C=0.3)
+    check_verify(w, tokens=_oracle_tokens(w), label="fast-specials")
+    check_verify(w, tokens=rng.integers(0, V, (B, K)), label="fast-specials-random")
+
+
+def test_fast_workspace_reuse_and_determinism():
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
+    tok = dev(_oracle_tokens(w.without_cache_row()))
+    prm = capi.params_tensor(w.temperature, w.top_k, w.top_p)
+    ws = capi.new_workspace(w.B, w.K, w.V)
+    outs = []
+    for rnd in (0, 1, 0):
+        o = capi.spec_verify(dev(w.draft), dev(w.target), w.K, prm, tok, F=w.F, C=w.C, seed=w.seed, round_=rnd,
+                             workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((o.k.cpu().numpy().copy(), o.tstar.cpu().numpy().copy(), o.status.cpu().numpy().copy()))
+    assert all(np.array_equal(x, y) for x, y in zip(outs[0], outs[2]))
+    o1 = run_oracle(w.without_cache_row(), tokens=tok.cpu().numpy(), round_=1)
+    ok = o1.flags == 0
+    assert (outs[1][0][ok] == o1.k[ok]).all() and (outs[1][1][ok] == o1.t[ok]).all()
