@@ -116,6 +116,31 @@ __device__ __forceinline__ T wave_min(T v) {
     return v;
 }
 
+template <typename T>
+__device__ __forceinline__ T wave_or(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Inclusive prefix sum over the lanes of a wave in lane order; *excl gets the exclusive one.
+template <typename T>
+__device__ __forceinline__ T wave_scan(T v, T* excl) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        T y = __shfl_up(v, o, kWave);
+        if (lane >= o) v += y;
+    }
+    T e = __shfl_up(v, 1, kWave);
+    *excl = lane == 0 ? T(0) : e;
+    return v;
+}
+
+// Lowest / highest set lane of a ballot (-1 when empty).
+__device__ __forceinline__ int first_lane(uint64_t m) { return m ? __builtin_ctzll(m) : -1; }
+__device__ __forceinline__ int last_lane(uint64_t m) { return m ? 63 - __builtin_clzll(m) : -1; }
+
 template <typename T, int OP>  // OP 0 sum, 1 max, 2 min
 __device__ __forceinline__ T wave_reduce(T v) {
     if (OP == 0) return wave_sum(v);

@@ -135,7 +135,7 @@ struct UnitFast {
 };
 
 struct Layout {
-    size_t ctr, flag, req, parts, units, idcut, chunks, total;
+    size_t req, parts, units, idcut, chunks, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -143,8 +143,6 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 
 __host__ __device__ inline Layout layout(int B, int units, int nS) {
     Layout L;
     size_t o = 0;
-    L.ctr = o;    o += align256((size_t)units * 128);           // unit arrival counters (one line each)
-    L.flag = o;   o += align256((size_t)units * 128);           // unit release flags
     L.req = o;    o += align256((size_t)B * 128);               // request arrival counters
     L.parts = o;  o += align256((size_t)units * nS * 2 * sizeof(RowPart));
     L.units = o;  o += align256((size_t)units * sizeof(UnitFast));
@@ -163,53 +161,18 @@ struct FastArgs {
 };
 
 // ------------------------------------------------------------------------------------------
-// L2-local synchronisation between the slices of a unit (all on one XCD)
+// Request arrival counter in the XCD's L2 (every workgroup of a request runs on one XCD)
 // ------------------------------------------------------------------------------------------
-constexpr unsigned kSpinLimit = 1u << 20;
-
 __device__ __forceinline__ unsigned l2_fetch_add(unsigned* p, unsigned v) {
     unsigned old;
     asm volatile("s_waitcnt vmcnt(0)\n\tglobal_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
                  : "=v"(old) : "v"(p), "v"(v) : "memory");
     return old;
 }
-__device__ __forceinline__ void l2_store_add(unsigned* p, unsigned v) {
-    asm volatile("s_waitcnt vmcnt(0)\n\tglobal_atomic_add %0, %1, off\n\ts_waitcnt vmcnt(0)" :: "v"(p), "v"(v) : "memory");
-}
-__device__ __forceinline__ unsigned l2_read(unsigned* p) { return l2_fetch_add(p, 0u); }
 
-// Every slice of the unit arrives; the last one raises the unit's flag; the others poll it.
-// Returns false when the wait gave up (the unit's results are then flagged).  Data published
-// before the barrier is read after it with non-temporal loads (ldnt), which bypass the CU's
-// vector L1 and are served by the shared L2; a plain load could return a stale L1 line.
 // Every wave waits until its own global stores have reached L2; __syncthreads() alone orders
 // only LDS traffic, so this must precede the workgroup barrier in front of an arrival.
 __device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-__device__ __forceinline__ bool unit_barrier(unsigned* ctr, unsigned* flag, int nS) {
-    __shared__ int ok;
-    drain_stores();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        ok = 1;
-        const unsigned old = l2_fetch_add(ctr, 1u);
-        if (old + 1 == (unsigned)nS) {
-            l2_store_add(flag, 1u);
-        } else {
-            unsigned spins = 0;
-            while (l2_read(flag) == 0u) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > kSpinLimit) {
-                    ok = 0;
-                    break;
-                }
-            }
-        }
-    }
-    __syncthreads();
-    return ok != 0;
-}
-
 
 // ------------------------------------------------------------------------------------------
 // Loads of data published by other workgroups (non-temporal: bypass L1, served by L2)
@@ -283,7 +246,10 @@ struct Smem {
             uint32_t okey[kTop];
             int32_t oid[kTop];
             uint32_t fine[kGroup];
-            uint32_t slice_cnt[32];
+            uint32_t fine8[kWaves][kGroup];
+            int32_t toff[32];
+            int32_t tcnt[32];
+            int32_t ttotal;
         } m;
         RowShared generic;
     } u;
@@ -296,17 +262,27 @@ struct Smem {
     uint32_t n_top;
     uint32_t flags[2];
     uint32_t neginf[2];
-    uint32_t maxbin[2];
     int32_t scan[kWaves + 1];
     double redd[kWaves];
     int32_t redi[kWaves];
     RowView rv[2];
-    uint32_t key_s[2];
-    float z_s[2];
     uint32_t s_bits[2];   // bf16 bits of token s in each row
+    // values handed between the steps of one helper
+    uint32_t tau;
+    int need;
+    int cut_seg;
+    int cut_cnt_above;
+    int cut_nin;
+    double cut_above;
+    double cut_mass_above;
+    double cut_w;
+    double cut_mass;
     int last;
     int found;
-    uint32_t cnt_tmp;
+    uint32_t fin[2 * sizeof(RowFinal) / 4];
+    int fk, ft, fmode, fc;
+    uint32_t fstatus;
+    double fW, ftarget, fbase;
 };
 
 __device__ __forceinline__ RowPart* part_of(const FastArgs& f, int unit, int slice, int r) {
@@ -324,154 +300,45 @@ __device__ __forceinline__ bool cut_keeps(const Cut& c, uint32_t key, int col) {
 // ------------------------------------------------------------------------------------------
 // Phase A helpers
 // ------------------------------------------------------------------------------------------
-// Thread 0: walks this slice's row r from the largest key down over the exact bins (hist[r])
-// and the specials, until `L` elements are counted; returns the key of the L-th element and how
-// many elements at that key are needed (0 when the row holds fewer than L finite elements).
-__device__ __forceinline__ void local_threshold(Smem& sm, int r, int L, uint32_t* tau_out, int* need_out) {
-    int cum = 0;
-    for (int sg = 0; sg < kSegs; ++sg) {
-        const int g = group_of_seg(sg);
-        if (g >= 0) {
-            for (int bb = kGroup - 1; bb >= 0; --bb) {
-                const int bin = g * kGroup + bb;
-                const int c = (int)sm.u.hist[r][bin];
-                if (c == 0) continue;
-                if (cum + c >= L) {
-                    *tau_out = bin_key(bin);
-                    *need_out = L - cum;
-                    return;
-                }
-                cum += c;
-            }
-        } else {
-            const int n = min((int)sm.n_sp[r], kSpecial);
-            uint32_t prev = 0xFFFFFFFFu;  // walk this segment's distinct keys downwards
-            while (true) {
-                uint32_t best = 0;
-                int c = 0;
-                for (int i = 0; i < n; ++i) {
-                    const uint32_t k = sm.sp_key[r][i];
-                    if (special_seg(k) != sg || k >= prev) continue;
-                    if (c == 0 || k > best) {
-                        best = k;
-                        c = 1;
-                    } else if (k == best) {
-                        ++c;
-                    }
-                }
-                if (c == 0) break;
-                if (cum + c >= L) {
-                    *tau_out = best;
-                    *need_out = L - cum;
-                    return;
-                }
-                cum += c;
-                prev = best;
-            }
-        }
-    }
-    *tau_out = 0;
-    *need_out = 0;
+// Segment of any finite order key.
+__device__ __forceinline__ int seg_of_key(uint32_t k) {
+    return key_is_binned(k) ? seg_of_group(key_bin(k) / kGroup) : special_seg(k);
 }
 
-// The first L elements (token order: key desc, id asc) of row r in this slice, sorted, into
-// sm.top_key / sm.top_id; sm.n_top gets their number.  v holds the slice's columns of row r.
-__device__ __forceinline__ void local_top(Smem& sm, int r, int L, int c0, int V, const u32x4 (&v)[kLoads]) {
-    __shared__ uint32_t s_tau;
-    __shared__ int s_need;
-    if (threadIdx.x == 0) {
-        local_threshold(sm, r, L, &s_tau, &s_need);
-        sm.n_top = 0;
-    }
-    __syncthreads();
-    const uint32_t tau = s_tau;
-    const int need = s_need;
-    // every element strictly above tau (fewer than L of them), any order
-    uint32_t tiemask = 0;
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int col = col_of(c0, q, e);
-            const uint32_t w = v[q][e >> 1];
-            const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-            if (col >= V || (h & 0x7FFFu) >= 0x7F80u) continue;  // past the row, inf, NaN
-            const uint32_t k = key16(h);
-            if (k > tau) {
-                const int slot = (int)atomicAdd(&sm.n_top, 1u);
-                if (slot < kTop) {
-                    sm.top_key[slot] = k;
-                    sm.top_id[slot] = col;
-                }
-            } else if (k == tau && need > 0) {
-                tiemask |= 1u << (q * 8 + e);
-            }
-        }
-    __syncthreads();
-    int base = min((int)sm.n_top, kTop);
-    int need_left = need;
-    // then the first `need` elements at tau in token order (uniform loop)
-    for (int q = 0; q < kLoads && need_left > 0; ++q) {
-        const uint32_t mq = (tiemask >> (q * 8)) & 0xFFu;
-        int total;
-        const int before = block_exclusive_scan<int>(__popc(mq), sm.scan, &total);
-        int k = 0;
-        for (int e = 0; e < 8; ++e) {
-            if (!(mq & (1u << e))) continue;
-            const int rank = before + k++;
-            const int slot = base + rank;
-            if (rank < need_left && slot < kTop) {
-                sm.top_key[slot] = tau;
-                sm.top_id[slot] = col_of(c0, q, e);
-            }
-        }
-        const int took = min(total, need_left);
-        base += took;
-        need_left -= took;
-    }
-    __syncthreads();
-    const int n = min(base, kTop);
-    // sort: key desc, id asc (rank by counting)
-    uint32_t mk = 0;
-    int mi = 0, rank = 0;
-    if ((int)threadIdx.x < n) {
-        mk = sm.top_key[threadIdx.x];
-        mi = sm.top_id[threadIdx.x];
-        for (int i = 0; i < n; ++i) {
-            const uint32_t k2 = sm.top_key[i];
-            const int i2 = sm.top_id[i];
-            rank += (k2 > mk || (k2 == mk && i2 < mi)) ? 1 : 0;
-        }
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < n) {
-        sm.top_key[rank] = mk;
-        sm.top_id[rank] = mi;
-    }
-    if (threadIdx.x == 0) sm.n_top = (uint32_t)n;
-    __syncthreads();
-}
+// Bin of lane `lane` in a walk over group g in descending key order.
+__device__ __forceinline__ int bin_of_sel(int g, int lane) { return g * kGroup + (kGroup - 1 - lane); }
 
 // ------------------------------------------------------------------------------------------
 // Phase C: combining the slices' summaries of one row (every slice computes the same view)
 // ------------------------------------------------------------------------------------------
-// Merged candidates of the unit's slices for row r, sorted (key desc, id asc); returns their
-// number (<= kMergeCap).  Source: each slice's top list.
+// Merged candidates of the unit's slices for row r, sorted (key desc, id asc), into
+// sm.u.m.okey / oid; returns their number (<= want).  Source: each slice's top list.
 __device__ __forceinline__ int merge_tops(const FastArgs& f, Smem& sm, int unit, int r, int want) {
-    // gather
-    int n = 0;
-    for (int t = 0; t < f.nS; ++t) {
-        const RowPart* P = part_of(f, unit, t, r);
-        const int nt = (int)ldnt(&P->n_top);
-        for (int i = threadIdx.x; i < nt; i += blockDim.x) {
-            if (n + i < kMergeCap) {
-                sm.u.m.key[n + i] = ldnt(&P->top_key[i]);
-                sm.u.m.id[n + i] = ldnt(&P->top_id[i]);
+    const int lane = threadIdx.x & (kWave - 1);
+    if (threadIdx.x < kWave) {  // list lengths and offsets, one lane per slice
+        const int nt = lane < f.nS ? (int)ldnt(&part_of(f, unit, lane, r)->n_top) : 0;
+        int ex;
+        const int in = wave_scan(nt, &ex);
+        if (lane < f.nS) {
+            sm.u.m.toff[lane] = ex;
+            sm.u.m.tcnt[lane] = nt;
+        }
+        const int tot = __shfl(in, kWave - 1, kWave);
+        if (lane == 0) sm.u.m.ttotal = tot;
+    }
+    __syncthreads();
+    const int n = min(sm.u.m.ttotal, kMergeCap);
+    for (int i = threadIdx.x; i < f.nS * kTop; i += blockDim.x) {  // all entries at once
+        const int t = i / kTop, x = i % kTop;
+        if (x < sm.u.m.tcnt[t]) {
+            const int d = sm.u.m.toff[t] + x;
+            if (d < kMergeCap) {
+                const RowPart* P = part_of(f, unit, t, r);
+                sm.u.m.key[d] = ldnt(&P->top_key[x]);
+                sm.u.m.id[d] = ldnt(&P->top_id[x]);
             }
         }
-        n += nt;
     }
-    n = min(n, kMergeCap);
     __syncthreads();
     // rank every entry; keep those with rank < want
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
@@ -527,116 +394,114 @@ __device__ __forceinline__ int merge_specials(const FastArgs& f, Smem& sm, int u
     return n;
 }
 
-// Fine counts of group g of row r summed over the slices into sm.u.m.fine[64].
+// Fine counts of group g of row r summed over the slices into sm.u.m.fine[64]: wave w reads
+// slices w, w + 8, ...; the eight partial sums are added in a fixed order.
 __device__ __forceinline__ void merge_fine(const FastArgs& f, Smem& sm, int unit, int r, int g) {
+    const int bb = threadIdx.x & (kGroup - 1);
+    const int w = threadIdx.x / kGroup;
+    uint32_t c = 0;
+    for (int t = w; t < f.nS; t += kWaves) c += ldnt_u16(&part_of(f, unit, t, r)->fine[g * kGroup + bb]);
+    sm.u.m.fine8[w][bb] = c;
+    __syncthreads();
     if (threadIdx.x < kGroup) {
-        uint32_t c = 0;
-        for (int t = 0; t < f.nS; ++t) c += ldnt_u16(&part_of(f, unit, t, r)->fine[g * kGroup + threadIdx.x]);
-        sm.u.m.fine[threadIdx.x] = c;
+        uint32_t s = 0;
+#pragma unroll
+        for (int x = 0; x < kWaves; ++x) s += sm.u.m.fine8[x][threadIdx.x];
+        sm.u.m.fine[threadIdx.x] = s;
     }
     __syncthreads();
 }
 
-// Slice owning the take-th element at bin `bin` of row r (in token order), and how many of
-// that bin's elements it holds before it; fills c.owner and c.owner_take.
+// Wave 0: the slice holding the take-th element (token order) of bin `bin` of row r, and how
+// many of that bin's elements it keeps: c.owner, c.owner_take (one lane per slice).
 __device__ __forceinline__ void tie_owner(const FastArgs& f, int unit, int r, int bin, Cut& c) {
-    int acc = 0;
-    c.owner = f.nS - 1;
-    c.owner_take = 0;
-    for (int t = 0; t < f.nS; ++t) {
-        const int n = (int)ldnt_u16(&part_of(f, unit, t, r)->fine[bin]);
-        if (acc + n >= c.take) {
-            c.owner = t;
-            c.owner_take = c.take - acc;
-            return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int take = c.take;
+    const int n = lane < f.nS ? (int)ldnt_u16(&part_of(f, unit, lane, r)->fine[bin]) : 0;
+    int ex;
+    const int in = wave_scan(n, &ex);
+    const int t = first_lane(__ballot(lane < f.nS && in >= take));
+    if (t < 0) {
+        if (lane == 0) {
+            c.owner = f.nS - 1;
+            c.owner_take = 0;
         }
-        acc += n;
+    } else if (lane == t) {
+        c.owner = t;
+        c.owner_take = take - ex;
     }
 }
 
-// Finds the cut where the running weight over the row, walked from the largest key down,
-// first reaches `need`.  Weights are counts (MASS false) or masses cnt * e (MASS true);
-// elements are restricted to the `lim` cut when given (nucleus inside a top-k set).
-// Thread 0 computes; the result is broadcast through sm.rv[r].  Returns the weight above the
-// cut plus that of the taken elements (the kept mass for MASS).
+// The cut where the running weight over row r, walked from the largest key down, first
+// reaches `need`.  Weights are counts (MASS false) or masses cnt * e (MASS true); elements
+// are restricted to the `lim` cut when given (nucleus inside a top-k set).  The walk is a
+// prefix scan over the 49 segments, then over the 64 bins of the crossing group (or the
+// specials of the crossing segment).  Results: *out (LDS), sm.cut_w (weight kept),
+// sm.cut_mass (mass kept), sm.cut_nin (elements kept).
 template <bool MASS>
-__device__ __forceinline__ double find_cut(const FastArgs& f, Smem& sm, int unit, int r, double need, const Cut* lim, Cut* out,
-                           int* n_in_out) {
-    RowView& rv = sm.rv[r];
-    __shared__ int s_seg;
-    __shared__ double s_above;
-    __shared__ int s_cnt_above;
-    // 1. crossing segment (segments below the limit's segment weigh nothing; the limit's own
-    //    segment is resolved exactly below)
-    if (threadIdx.x == 0) {
-        double acc = 0.0;
-        int cnt = 0;
-        int pick = kSegs - 1;
-        const int lim_seg = lim ? (key_is_binned(lim->key) ? seg_of_group(key_bin(lim->key) / kGroup) : special_seg(lim->key)) : kSegs;
-        // (callers pass no limit for a cut that keeps everything)
-        double acc_before = 0.0;
-        int cnt_before = 0;
-        bool crossed = false;
-        for (int sg = 0; sg < kSegs; ++sg) {
-            if (sg >= lim_seg) {
-                pick = sg;
-                acc_before = acc;
-                cnt_before = cnt;
-                crossed = true;
-                break;
-            }
-            const double w = MASS ? rv.seg_mass[sg] : (double)rv.seg_count[sg];
-            if (rv.seg_count[sg] == 0) continue;
-            if (acc + w >= need) {
-                pick = sg;
-                acc_before = acc;
-                cnt_before = cnt;
-                crossed = true;
-                break;
-            }
-            // rounding may leave the target beyond the last segment: remember this one
-            pick = sg;
-            acc_before = acc;
-            cnt_before = cnt;
-            acc += w;
-            cnt += (int)rv.seg_count[sg];
+__device__ __forceinline__ void find_cut(const FastArgs& f, Smem& sm, int unit, int r, double need, bool has_lim,
+                                         const Cut lim_cut, Cut* out) {
+    const Cut* lim = has_lim ? &lim_cut : nullptr;
+    const RowView& rv = sm.rv[r];
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool w0 = threadIdx.x < kWave;
+    // 1. crossing segment; the walk stops at the limit's segment, which is resolved below
+    if (w0) {
+        const int lim_seg = lim ? seg_of_key(lim->key) : kSegs;
+        const bool live = lane < kSegs && lane < lim_seg;
+        const uint32_t cnt = lane < kSegs ? rv.seg_count[lane] : 0u;
+        const double ms = live ? rv.seg_mass[lane] : 0.0;
+        const double w = live ? (MASS ? ms : (double)cnt) : 0.0;
+        double wex, mex;
+        int cex;
+        const double win = wave_scan(w, &wex);
+        wave_scan(ms, &mex);
+        wave_scan(live ? (int)cnt : 0, &cex);
+        const bool cross = lane < kSegs && (lane >= lim_seg || (cnt > 0 && win >= need));
+        int pick = first_lane(__ballot(cross));
+        if (pick < 0) {  // rounding left the target beyond the last segment: its last non-empty one
+            pick = last_lane(__ballot(lane < kSegs && cnt > 0));
+            if (pick < 0) pick = kSegs - 1;
         }
-        (void)crossed;
-        s_seg = pick;
-        s_above = acc_before;
-        s_cnt_above = cnt_before;
+        const double wa = __shfl(wex, pick, kWave);
+        const double ma = __shfl(mex, pick, kWave);
+        const int ca = __shfl(cex, pick, kWave);
+        if (lane == 0) {
+            sm.cut_seg = pick;
+            sm.cut_above = wa;
+            sm.cut_mass_above = ma;
+            sm.cut_cnt_above = ca;
+        }
     }
     __syncthreads();
-    const int sg = s_seg;
+    const int sg = sm.cut_seg;
     const int g = group_of_seg(sg);
-    double above = s_above;
-    int cnt_above = s_cnt_above;
-    __shared__ double s_res;
-    __shared__ int s_nin;
     if (g >= 0) {
         merge_fine(f, sm, unit, r, g);
-        if (threadIdx.x == 0) {
-            Cut c;
-            c.explicit_id = -1;
-            c.key = 0;
-            c.take = 0;
-            bool done = false;
-            double kept_w = above;
-            int last_bin = -1, last_n = 0;
-            double last_e = 0.0;
-            for (int bb = kGroup - 1; bb >= 0 && !done; --bb) {
-                const int bin = g * kGroup + bb;
-                int n = (int)sm.u.m.fine[bb];
-                if (n == 0) continue;
-                const uint32_t key = bin_key(bin);
-                if (lim) {
-                    if (key < lim->key) break;
-                    if (key == lim->key) n = min(n, lim->take);
-                }
-                const double e = MASS ? mass_of(key16_value(key), rv.m, rv.T) : 1.0;
-                const double w = (double)n * e;
-                if (above + w >= need || (lim && key == lim->key)) {
-                    int take = n;
+        if (w0) {
+            const int bb = kGroup - 1 - lane;  // lane order = descending key
+            const int bin = g * kGroup + bb;
+            const uint32_t key = bin_key(bin);
+            int n = (int)sm.u.m.fine[bb];
+            const bool at_lim = lim && key == lim->key;
+            if (lim && key < lim->key) n = 0;
+            if (at_lim) n = min(n, lim->take);
+            const double e = n > 0 ? mass_of(key16_value(key), rv.m, rv.T) : 0.0;
+            const double w = MASS ? (double)n * e : (double)n;
+            double wex, mex;
+            int nex;
+            const double win = wave_scan(w, &wex);
+            wave_scan((double)n * e, &mex);
+            wave_scan(n, &nex);
+            const double above0 = sm.cut_above;
+            const uint64_t hc = __ballot(n > 0 && (above0 + win >= need || at_lim));
+            const bool done = hc != 0;
+            // not done: rounding left the target just beyond the group; cut at its lowest bin
+            const int sel = done ? first_lane(hc) : last_lane(__ballot(n > 0));
+            if (lane == sel) {
+                const double above = above0 + wex;
+                int take = n;
+                if (done && above + w >= need) {
                     if (MASS) {
                         if (e > 0.0) {
                             const double q = ceil((need - above) / e);
@@ -646,58 +511,56 @@ __device__ __forceinline__ double find_cut(const FastArgs& f, Smem& sm, int unit
                         take = (int)(need - above);
                         take = take < 1 ? 1 : (take > n ? n : take);
                     }
-                    if (above + w < need) take = n;  // the limit ends the walk first
-                    c.key = key;
-                    c.take = take;
-                    c.count_above = cnt_above;
-                    kept_w = above + (double)take * e;
-                    done = true;
-                } else {
-                    above += w;
-                    cnt_above += n;
-                    last_bin = bin;
-                    last_n = n;
-                    last_e = e;
                 }
+                Cut c;
+                c.key = key;
+                c.take = take;
+                c.explicit_id = -1;
+                c.owner = 0;
+                c.owner_take = 0;
+                c.eff = 0;
+                c.count_above = sm.cut_cnt_above + nex;
+                *out = c;
+                sm.cut_w = above + (MASS ? (double)take * e : (double)take);
+                sm.cut_mass = sm.cut_mass_above + mex + (double)take * e;
+                sm.cut_nin = c.count_above + take;
             }
-            if (!done) {  // rounding left the target just beyond the group: cut at its lowest bin
-                if (last_bin >= 0) {
-                    above -= (double)last_n * last_e;
-                    cnt_above -= last_n;
-                    c.key = bin_key(last_bin);
-                    c.take = last_n;
-                } else {
-                    c.key = 0;
-                    c.take = 0;
-                }
-                c.count_above = cnt_above;
-                kept_w = above + (double)last_n * last_e;
+            if (sel < 0 && lane == 0) {
+                Cut c;
+                c.key = 0u;
+                c.take = 0;
+                c.explicit_id = -1;
+                c.owner = 0;
+                c.owner_take = 0;
+                c.eff = 0;
+                c.count_above = sm.cut_cnt_above;
+                *out = c;
+                sm.cut_w = above0;
+                sm.cut_mass = sm.cut_mass_above;
+                sm.cut_nin = sm.cut_cnt_above;
             }
-            *out = c;
-            s_res = kept_w;
-            s_nin = cnt_above + c.take;
+            if (sel >= 0) tie_owner(f, unit, r, bin_of_sel(g, sel), *out);
         }
         __syncthreads();
-        if (out->key != 0 && out->explicit_id < 0) {
-            if (threadIdx.x == 0) tie_owner(f, unit, r, key_bin(out->key), *out);
-            __syncthreads();
-        }
     } else {
         const int n = merge_specials(f, sm, unit, r, sg);
-        if (threadIdx.x == 0) {
+        if (threadIdx.x == 0) {  // rare: finite values outside the exact bins
+            double above = sm.cut_above, mass = sm.cut_mass_above;
             Cut c;
-            c.key = 0;
+            c.key = 0u;
             c.take = 0;
             c.explicit_id = -1;
             c.owner = 0;
             c.owner_take = 0;
-            double kept_w = above;
+            c.eff = 0;
+            c.count_above = sm.cut_cnt_above;
             int i = 0;
             for (; i < n; ++i) {
                 const uint32_t key = sm.u.m.key[i];
                 if (lim && (key < lim->key || (key == lim->key && lim->explicit_id >= 0 && sm.u.m.id[i] > lim->explicit_id))) break;
-                const double w = MASS ? mass_of(key16_value(key), rv.m, rv.T) : 1.0;
-                above += w;
+                const double e = mass_of(key16_value(key), rv.m, rv.T);
+                above += MASS ? e : 1.0;
+                mass += e;
                 if (above >= need) {
                     c.key = key;
                     c.explicit_id = sm.u.m.id[i];
@@ -709,18 +572,13 @@ __device__ __forceinline__ double find_cut(const FastArgs& f, Smem& sm, int unit
                 c.key = sm.u.m.key[i - 1];
                 c.explicit_id = sm.u.m.id[i - 1];
             }
-            c.count_above = cnt_above;
-            kept_w = above;
             *out = c;
-            s_res = kept_w;
-            s_nin = cnt_above + i;
+            sm.cut_w = above;
+            sm.cut_mass = mass;
+            sm.cut_nin = sm.cut_cnt_above + i;
         }
         __syncthreads();
     }
-    const double res = s_res;
-    if (n_in_out) *n_in_out = s_nin;
-    __syncthreads();
-    return res;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -788,21 +646,22 @@ __device__ __forceinline__ int effective_id(Smem& sm, const Cut& c, int slice, c
     return local_nth_at_key(sm, v, c0, V, c.key, c.owner_take);
 }
 
-// Global rank (0-based, token order) of token s among the elements of row r with key == key_s.
+// Global rank (0-based, token order) of token s among the elements of row r with
+// key == key_s.  Wave-level: every wave computes it, one lane per preceding slice.
 __device__ __forceinline__ int global_rank_s(const FastArgs& f, int unit, int r, uint32_t key_s, int s) {
+    const int lane = threadIdx.x & (kWave - 1);
     const int owner = s / kSliceCols;
     int acc = 0;
-    if (key_is_binned(key_s)) {
-        const int bin = key_bin(key_s);
-        for (int t = 0; t < owner && t < f.nS; ++t) acc += (int)ldnt_u16(&part_of(f, unit, t, r)->fine[bin]);
-    } else {
-        for (int t = 0; t < owner && t < f.nS; ++t) {
-            const RowPart* P = part_of(f, unit, t, r);
+    if (lane < owner && lane < f.nS) {
+        const RowPart* P = part_of(f, unit, lane, r);
+        if (key_is_binned(key_s)) {
+            acc = (int)ldnt_u16(&P->fine[key_bin(key_s)]);
+        } else {
             const int ns = min((int)ldnt(&P->n_special), kSpecial);
             for (int i = 0; i < ns; ++i) acc += (ldnt(&P->sp_key[i]) == key_s) ? 1 : 0;
         }
     }
-    return acc + (int)ldnt(&part_of(f, unit, owner, r)->rank_s);
+    return wave_sum(acc) + (int)ldnt(&part_of(f, unit, owner, r)->rank_s);
 }
 
 __device__ __forceinline__ bool cut_keeps_s(const FastArgs& f, int unit, int r, const Cut& c, uint32_t key_s, int s) {
@@ -813,50 +672,54 @@ __device__ __forceinline__ bool cut_keeps_s(const FastArgs& f, int unit, int r, 
 }
 
 // ------------------------------------------------------------------------------------------
-// Combine one row (all threads)
+// Combine one row (all threads; every slice of the unit derives the same view)
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ void combine_row(const FastArgs& f, Smem& sm, int unit, int r, const spec_params& prm, bool draft) {
     RowView& rv = sm.rv[r];
     const VerifyArgs& a = f.a;
     const double T = (double)prm.temperature;
-    if (threadIdx.x == 0) {
-        float m = -__builtin_inff();
-        uint32_t fl = 0, nfin = 0;
-        int has_sp = 0;
-        for (int t = 0; t < f.nS; ++t) {
-            const RowPart* P = part_of(f, unit, t, r);
-            const float mt = ldnt(&P->m);
-            fl |= ldnt(&P->flags);
-            nfin += ldnt(&P->n_finite);
-            has_sp |= ldnt(&P->n_special) > 0 ? 1 : 0;
-            m = mt > m ? mt : m;
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool w0 = threadIdx.x < kWave;
+    if (w0) {  // slice headers, one lane per slice
+        float mt = -__builtin_inff();
+        uint32_t fl = 0, nf = 0, nsp = 0;
+        double St = 0.0;
+        if (lane < f.nS) {
+            const RowPart* P = part_of(f, unit, lane, r);
+            mt = ldnt(&P->m);
+            fl = ldnt(&P->flags);
+            nf = ldnt(&P->n_finite);
+            nsp = ldnt(&P->n_special);
+            St = ldnt(&P->S);
         }
-        rv.m = m;
-        rv.T = T;
-        rv.bad = ((fl & 1u) || nfin == 0) ? 1 : 0;
-        rv.overflow = (fl & 2u) ? 1 : 0;
-        rv.n_finite = nfin;
-        rv.greedy = prm.temperature == 0.0f ? 1 : 0;
-        rv.has_special = has_sp;
-        rv.argmax = -1;
-        double S = 0.0;
-        for (int t = 0; t < f.nS && t < 32; ++t) {
-            const RowPart* P = part_of(f, unit, t, r);
-            const float mt = ldnt(&P->m);
-            rv.sc[t] = (T > 0.0 && mt > -__builtin_inff()) ? exp(((double)mt - (double)m) / T) : 0.0;
-            S += rv.sc[t] * ldnt(&P->S);
+        const float m = wave_max(mt);
+        const uint32_t flo = wave_or(fl);
+        const uint32_t nfin = wave_sum(nf);
+        const bool has_sp = __ballot(nsp > 0) != 0;
+        const double sc = (lane < f.nS && T > 0.0 && mt > -__builtin_inff()) ? exp(((double)mt - (double)m) / T) : 0.0;
+        const double S = wave_sum(sc * St);
+        if (lane < 32) rv.sc[lane] = sc;
+        if (lane == 0) {
+            rv.m = m;
+            rv.T = T;
+            rv.bad = ((flo & 1u) || nfin == 0) ? 1 : 0;
+            rv.overflow = (flo & 2u) ? 1 : 0;
+            rv.n_finite = nfin;
+            rv.greedy = prm.temperature == 0.0f ? 1 : 0;
+            rv.has_special = has_sp ? 1 : 0;
+            rv.argmax = -1;
+            rv.S_all = S;
+            rv.has_k = (prm.top_k > 0 && prm.top_k < a.V) ? 1 : 0;
+            rv.has_p = ((double)prm.top_p < 1.0) ? 1 : 0;
+            rv.ck = Cut{0, 0, -1, 0, 0, a.V - 1, 0};
+            rv.cp = Cut{0, 0, -1, 0, 0, a.V - 1, 0};
+            rv.nset = 0;
+            rv.kF = 0xFFFFFFFFu;
+            rv.idF = -1;
+            rv.C = 1.0;
+            rv.Z = 1.0;
+            rv.degenerate = 0;
         }
-        rv.S_all = S;
-        rv.has_k = (prm.top_k > 0 && prm.top_k < a.V) ? 1 : 0;
-        rv.has_p = ((double)prm.top_p < 1.0) ? 1 : 0;
-        rv.ck = Cut{0, 0, -1, 0, 0, a.V - 1, 0};
-        rv.cp = Cut{0, 0, -1, 0, 0, a.V - 1, 0};
-        rv.nset = 0;
-        rv.kF = 0xFFFFFFFFu;
-        rv.idF = -1;
-        rv.C = 1.0;
-        rv.Z = 1.0;
-        rv.degenerate = 0;
     }
     __syncthreads();
     if (rv.bad || rv.overflow) return;
@@ -874,21 +737,32 @@ __device__ __forceinline__ void combine_row(const FastArgs& f, Smem& sm, int uni
         return;
     }
     if (rv.has_k && (uint32_t)prm.top_k > rv.n_finite) {  // -inf tokens would be kept
+        __syncthreads();
         if (threadIdx.x == 0) rv.overflow = 1;
         __syncthreads();
         return;
     }
-    // merged segment weights
-    for (int sg = threadIdx.x; sg < kSegs; sg += blockDim.x) {
+    // merged segment weights: eight lanes per segment, slices t, t + 8, ... each
+    {
+        const int sg = threadIdx.x / 8, t0 = threadIdx.x % 8;
         double ms = 0.0;
         uint32_t cs = 0;
-        for (int t = 0; t < f.nS && t < 32; ++t) {
-            const RowPart* P = part_of(f, unit, t, r);
-            ms += rv.sc[t] * ldnt(&P->seg_mass[sg]);
-            cs += ldnt(&P->seg_count[sg]);
+        if (sg < kSegs) {
+            for (int t = t0; t < f.nS; t += 8) {
+                const RowPart* P = part_of(f, unit, t, r);
+                ms += rv.sc[t] * ldnt(&P->seg_mass[sg]);
+                cs += ldnt(&P->seg_count[sg]);
+            }
         }
-        rv.seg_mass[sg] = ms;
-        rv.seg_count[sg] = cs;
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+            ms += __shfl_xor(ms, o, kWave);
+            cs += __shfl_xor(cs, o, kWave);
+        }
+        if (sg < kSegs && t0 == 0) {
+            rv.seg_mass[sg] = ms;
+            rv.seg_count[sg] = cs;
+        }
     }
     __syncthreads();
     // top-k
@@ -897,116 +771,77 @@ __device__ __forceinline__ void combine_row(const FastArgs& f, Smem& sm, int uni
             rv.S_kept = rv.S_all;
             rv.n_kept = (int)rv.n_finite;
         }
-        __syncthreads();
     } else if (small_k) {
-        if (threadIdx.x == 0) {
-            double s = 0.0;
-            for (int i = 0; i < prm.top_k; ++i) s += mass_of(key16_value(sm.u.m.okey[i]), rv.m, T);
-            rv.S_kept = s;
-            rv.n_kept = prm.top_k;
-            rv.ck = Cut{sm.u.m.okey[prm.top_k - 1], 0, sm.u.m.oid[prm.top_k - 1], 0, 0, sm.u.m.oid[prm.top_k - 1], 0};
-        }
-        __syncthreads();
-    } else {
-        Cut c;
-        int nin = 0;
-        find_cut<false>(f, sm, unit, r, (double)prm.top_k, nullptr, &sm.rv[r].ck, &nin);
-        // kept mass: segments above the cut plus the taken part of the cut's bin / specials
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            c = rv.ck;
-            double s = 0.0;
-            const int cut_seg = key_is_binned(c.key) ? seg_of_group(key_bin(c.key) / kGroup) : special_seg(c.key);
-            for (int sg = 0; sg < cut_seg; ++sg) s += rv.seg_mass[sg];
-            rv.S_kept = s;  // completed below with the cut segment's kept part
-            rv.n_kept = nin;
-        }
-        __syncthreads();
-        // the cut segment's kept mass
-        {
-            const Cut c2 = rv.ck;
-            if (key_is_binned(c2.key)) {
-                const int g = key_bin(c2.key) / kGroup;
-                merge_fine(f, sm, unit, r, g);
-                if (threadIdx.x == 0) {
-                    double s = 0.0;
-                    for (int bb = kGroup - 1; bb >= 0; --bb) {
-                        const int bin = g * kGroup + bb;
-                        const uint32_t key = bin_key(bin);
-                        const int n = (int)sm.u.m.fine[bb];
-                        if (n == 0 || key < c2.key) continue;
-                        const int take = key == c2.key ? c2.take : n;
-                        s += (double)take * mass_of(key16_value(key), rv.m, T);
-                    }
-                    rv.S_kept += s;
-                }
-            } else {
-                const int n = merge_specials(f, sm, unit, r, special_seg(c2.key));
-                if (threadIdx.x == 0) {
-                    double s = 0.0;
-                    for (int i = 0; i < n; ++i) {
-                        const uint32_t key = sm.u.m.key[i];
-                        if (key < c2.key || (key == c2.key && sm.u.m.id[i] > c2.explicit_id)) break;
-                        s += mass_of(key16_value(key), rv.m, T);
-                    }
-                    rv.S_kept += s;
-                }
+        if (w0) {
+            const int kk = prm.top_k;
+            const double e = lane < kk ? mass_of(key16_value(sm.u.m.okey[lane]), rv.m, T) : 0.0;
+            const double s = wave_sum(e);
+            if (lane == 0) {
+                rv.S_kept = s;
+                rv.n_kept = kk;
+                rv.ck = Cut{sm.u.m.okey[kk - 1], 0, sm.u.m.oid[kk - 1], 0, 0, sm.u.m.oid[kk - 1], 0};
             }
-            __syncthreads();
+        }
+    } else {
+        find_cut<false>(f, sm, unit, r, (double)prm.top_k, false, rv.ck, &rv.ck);
+        if (threadIdx.x == 0) {
+            rv.S_kept = sm.cut_mass;
+            rv.n_kept = sm.cut_nin;
         }
     }
+    __syncthreads();
     // nucleus
     if (!rv.has_p) {
         if (threadIdx.x == 0) {
             rv.S = rv.S_kept;
             rv.n_nuc = rv.n_kept;
         }
-        __syncthreads();
     } else if (small_k) {
-        if (threadIdx.x == 0) {
+        if (w0) {
+            const int kk = prm.top_k;
             const double need = (double)prm.top_p * rv.S_kept;
-            double cum = 0.0;
-            int i = 0;
-            for (; i < prm.top_k; ++i) {
-                cum += mass_of(key16_value(sm.u.m.okey[i]), rv.m, T);
-                if (cum >= need) break;
+            const double e = lane < kk ? mass_of(key16_value(sm.u.m.okey[lane]), rv.m, T) : 0.0;
+            double ex;
+            const double in = wave_scan(e, &ex);
+            int i = first_lane(__ballot(lane < kk && in >= need));
+            if (i < 0) i = kk - 1;
+            const double cum = __shfl(in, i, kWave);
+            if (lane == 0) {
+                rv.cp = Cut{sm.u.m.okey[i], 0, sm.u.m.oid[i], 0, 0, sm.u.m.oid[i], 0};
+                rv.S = cum;
+                rv.n_nuc = i + 1;
             }
-            if (i >= prm.top_k) i = prm.top_k - 1;
-            rv.cp = Cut{sm.u.m.okey[i], 0, sm.u.m.oid[i], 0, 0, sm.u.m.oid[i], 0};
-            rv.S = cum;
-            rv.n_nuc = i + 1;
         }
-        __syncthreads();
     } else {
-        int nin = 0;
         const Cut lim = rv.ck;
         const bool use_lim = rv.has_k && lim.key != 0;
-        const double kept = find_cut<true>(f, sm, unit, r, (double)prm.top_p * rv.S_kept, use_lim ? &lim : nullptr,
-                                           &sm.rv[r].cp, &nin);
+        find_cut<true>(f, sm, unit, r, (double)prm.top_p * rv.S_kept, use_lim, lim, &rv.cp);
         if (threadIdx.x == 0) {
-            rv.S = kept;
-            rv.n_nuc = nin;
+            rv.S = sm.cut_w;
+            rv.n_nuc = sm.cut_nin;
         }
-        __syncthreads();
     }
+    __syncthreads();
     // downweighted set: the first F elements of the processed order that carry mass
     if (want_set) {
-        if (threadIdx.x == 0) {
-            int n = min(min(a.F, rv.n_nuc), nm);
-            while (n > 0 && !(mass_of(key16_value(sm.u.m.okey[n - 1]), rv.m, T) > 0.0)) --n;
-            rv.nset = n;
-            if (n > 0) {
-                rv.kF = sm.u.m.okey[n - 1];
-                rv.idF = sm.u.m.oid[n - 1];
-                double ps = 0.0;
-                for (int i = 0; i < n; ++i) ps += mass_of(key16_value(sm.u.m.okey[i]), rv.m, T) / rv.S;
-                const double Cd = (double)a.C;
-                const double Z = 1.0 - (1.0 - Cd) * ps;
-                if (Z > 0.0) {
-                    rv.C = Cd;
-                    rv.Z = Z;
-                } else {
-                    rv.degenerate = 1;
+        if (w0) {
+            const int n0 = min(min(a.F, rv.n_nuc), nm);
+            const double e = lane < n0 ? mass_of(key16_value(sm.u.m.okey[lane]), rv.m, T) : 0.0;
+            const int n = last_lane(__ballot(lane < n0 && e > 0.0)) + 1;
+            const double ps = wave_sum(lane < n ? e / rv.S : 0.0);
+            if (lane == 0) {
+                rv.nset = n;
+                if (n > 0) {
+                    rv.kF = sm.u.m.okey[n - 1];
+                    rv.idF = sm.u.m.oid[n - 1];
+                    const double Cd = (double)a.C;
+                    const double Z = 1.0 - (1.0 - Cd) * ps;
+                    if (Z > 0.0) {
+                        rv.C = Cd;
+                        rv.Z = Z;
+                    } else {
+                        rv.degenerate = 1;
+                    }
                 }
             }
         }
@@ -1014,7 +849,7 @@ __device__ __forceinline__ void combine_row(const FastArgs& f, Smem& sm, int uni
     }
 }
 
-// Processed probability of token s in row r (after the combine).
+// Processed probability of token s in row r (after the combine; wave-level).
 __device__ __forceinline__ double prob_of_s(const FastArgs& f, Smem& sm, int unit, int r, int s, bool draft) {
     const RowView& rv = sm.rv[r];
     const uint32_t h = sm.s_bits[r];
@@ -1038,106 +873,6 @@ __device__ __forceinline__ int list_len(const VerifyArgs& a, const spec_params& 
     if (!greedy && prm.top_k > 0 && prm.top_k < a.V && prm.top_k <= kTop) want = max(want, prm.top_k);
     if (!greedy && draft && a.F > 0 && a.C < 1.0f) want = max(want, a.F);
     return want;
-}
-
-// Phase A for row r: counts are in sm.u.hist[r]; publishes the slice summary.
-__device__ __forceinline__ void publish_row(const FastArgs& f, Smem& sm, int unit, int slice, int r, const spec_params& prm, bool draft,
-                            int c0, const u32x4 (&v)[kLoads], int s_tok) {
-    const VerifyArgs& a = f.a;
-    RowPart* P = part_of(f, unit, slice, r);
-    const double T = (double)prm.temperature;
-    const int nsp = min((int)sm.n_sp[r], kSpecial);
-    // largest key: highest non-empty bin or special
-    uint32_t mk = 0;
-    for (int b = threadIdx.x; b < kBins; b += blockDim.x)
-        if (sm.u.hist[r][b] != 0) mk = max(mk, bin_key(b));
-    for (int i = threadIdx.x; i < nsp; i += blockDim.x) mk = max(mk, sm.sp_key[r][i]);
-    mk = block_max<uint32_t>(mk, reinterpret_cast<uint32_t*>(sm.redi));
-    const float m = mk ? key16_value(mk) : -__builtin_inff();
-    // per-group counts and masses (relative to this slice's largest logit)
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    for (int g = wave; g < kGroups; g += kWaves) {
-        const int bin = g * kGroup + lane;
-        const uint32_t c = sm.u.hist[r][bin];
-        double ms = 0.0;
-        if (c != 0 && T > 0.0) ms = (double)c * mass_of(key16_value(bin_key(bin)), m, T);
-        ms = wave_sum(ms);
-        const uint32_t cs = wave_sum(c);
-        if (lane == 0) {
-            const int sg = seg_of_group(g);
-            sm.segm[sg] = ms;
-            sm.segc[sg] = cs;
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int sps[4] = {kSegHugePos, kSegTinyPos, kSegTinyNeg, kSegHugeNeg};
-        for (int x = 0; x < 4; ++x) {
-            sm.segm[sps[x]] = 0.0;
-            sm.segc[sps[x]] = 0;
-        }
-        for (int i = 0; i < nsp; ++i) {
-            const uint32_t k = sm.sp_key[r][i];
-            const int sg = special_seg(k);
-            if (T > 0.0) sm.segm[sg] += mass_of(key16_value(k), m, T);
-            sm.segc[sg] += 1;
-        }
-        double S = 0.0;
-        uint32_t nfin = 0;
-        for (int sg = 0; sg < kSegs; ++sg) {
-            S += sm.segm[sg];
-            nfin += sm.segc[sg];
-        }
-        P->m = m;
-        P->maxkey = mk;
-        P->flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u);
-        P->n_neginf = sm.neginf[r];
-        P->n_finite = nfin;
-        P->n_special = (uint32_t)nsp;
-        P->S = S;
-    }
-    for (int sg = threadIdx.x; sg < kSegs; sg += blockDim.x) {
-        P->seg_mass[sg] = sm.segm[sg];
-        P->seg_count[sg] = sm.segc[sg];
-    }
-    for (int i = threadIdx.x; i < nsp; i += blockDim.x) {
-        P->sp_key[i] = sm.sp_key[r][i];
-        P->sp_id[i] = sm.sp_id[r][i];
-    }
-    // fine counts, two per dword (a slice holds < 65536 columns)
-    uint32_t* fine32 = reinterpret_cast<uint32_t*>(P->fine);
-    for (int i = threadIdx.x; i < kBins / 2; i += blockDim.x)
-        fine32[i] = (sm.u.hist[r][2 * i] & 0xFFFFu) | (sm.u.hist[r][2 * i + 1] << 16);
-    // rank of the draft token among equal keys in the slice that holds it
-    uint32_t rank = 0;
-    if (s_tok >= 0 && s_tok / kSliceCols == slice) {
-        const uint32_t ks = key16(sm.s_bits[r]);
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = col_of(c0, q, e);
-                const uint32_t w = v[q][e >> 1];
-                const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-                rank += (col < s_tok && (h & 0x7FFFu) < 0x7F80u && key16(h) == ks) ? 1u : 0u;
-            }
-        rank = block_sum<uint32_t>(rank, reinterpret_cast<uint32_t*>(sm.redi));
-    }
-    if (threadIdx.x == 0) P->rank_s = rank;
-    // leading candidates
-    const int want = list_len(a, prm, draft);
-    if (want > 0) {
-        local_top(sm, r, want, c0, a.V, v);
-        for (int i = threadIdx.x; i < (int)sm.n_top; i += blockDim.x) {
-            P->top_key[i] = sm.top_key[i];
-            P->top_id[i] = sm.top_id[i];
-        }
-        if (threadIdx.x == 0) P->n_top = sm.n_top;
-    } else if (threadIdx.x == 0) {
-        P->n_top = 0;
-    }
-    __syncthreads();
 }
 
 // Residual (rejected draft position) or target (bonus position) mass of this slice over
@@ -1231,110 +966,120 @@ __device__ __forceinline__ void residual_chunks(const FastArgs& f, Smem& sm, int
     }
 }
 
-// The general algorithm for one unit (out of line: a rare path).
-__device__ __noinline__ void fallback_unit(const VerifyArgs& a, int b, int j, Smem& sm) {
+// The general algorithm for one unit (out of line: a rare path).  The arguments come by
+// value so that no pointer to the kernel's own arguments escapes (which would move them to
+// scratch memory for the whole kernel).
+__device__ __noinline__ void fallback_unit(VerifyArgs a, int b, int j, Smem& sm) {
     unit_verify(a, b, j, &sm.urec, sm.u.generic, sm.gst[0], sm.gst[1]);
 }
 
 // ------------------------------------------------------------------------------------------
 // Finaliser: the last workgroup of a request picks k and t*
 // ------------------------------------------------------------------------------------------
-__device__ __noinline__ void finalize_request(const FastArgs& f, Smem& sm, int b) {
+__device__ __forceinline__ void finalize_request(const FastArgs& f, Smem& sm, int b) {
     const VerifyArgs& a = f.a;
     const int K = a.K;
-    UnitFast* U = reinterpret_cast<UnitFast*>(f.ws + f.L.units);
+    const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + (size_t)b * (K + 1);
     const int32_t* IC = reinterpret_cast<const int32_t*>(f.ws + f.L.idcut);
-    __shared__ int s_k, s_t, s_mode, s_c;
-    __shared__ uint32_t s_status;
-    __shared__ double s_W, s_target, s_base;
-    if (threadIdx.x == 0) {
-        uint32_t any = 0, deg = 0;
-        for (int j = 0; j <= K; ++j) {
-            const uint32_t st = ldnt(&U[b * (K + 1) + j].status);
-            any |= st;
-            if (j < K) deg |= st & kStDegenerate;
+    const int lane = threadIdx.x & (kWave - 1);
+    // 1. the verdicts of the request's K + 1 units (one lane each): status and k
+    if (threadIdx.x < kWave) {
+        uint32_t st = 0;
+        int acc = 1;
+        if (lane <= K) {
+            st = ldnt(&U[lane].status);
+            acc = ldnt(&U[lane].accept);
         }
-        int k = 0, mode = 0;  // mode 0: done, 1: chunk search, 2: empty residual
+        const uint32_t any = wave_or(st);
+        const uint32_t deg = wave_or(lane < K ? (st & kStDegenerate) : 0u);
+        int k = first_lane(__ballot(lane < K && !acc));
+        if (k < 0) k = K;
+        const uint32_t outside = wave_or((lane < K && lane <= k) ? (st & kStOutside) : 0u);
         uint32_t status;
-        int t = -1;
-        double W = 0.0;
-        if (any & SPEC_ST_SYNC_TIMEOUT) {
-            status = SPEC_ST_SYNC_TIMEOUT;
-        } else if (any & kStBadParam) {
+        bool normal = false;
+        if (any & kStBadParam) {
             status = kStBadParam;
         } else if (any & kStBadLogit) {
             status = kStBadLogit;
         } else if (any & kStBadToken) {
             status = deg | kStBadToken;
         } else {
-            status = deg;
-            k = K;
-            for (int j = 0; j < K; ++j) {
-                const UnitFast* u = &U[b * (K + 1) + j];
-                status |= ldnt(&u->status) & kStOutside;
-                if (!ldnt(&u->accept)) {
-                    k = j;
-                    break;
-                }
-            }
-            const UnitFast* uk = &U[b * (K + 1) + k];
-            if (ldnt(&uk->fallback)) {
-                t = ldnt(&uk->tcand);
-                W = (double)ldnt(&uk->W);
-                status |= ldnt(&uk->status) & kStEmptyResidual;
-            } else if (ldnt(&uk->rq.greedy)) {
-                t = ldnt(&uk->rq.argmax);
-            } else {
-                const double* ch = reinterpret_cast<const double*>(f.ws + f.L.chunks) +
-                                   (size_t)(b * (K + 1) + k) * f.nS * kChunks;
-                const int n = f.nS * kChunks;
-                for (int c = 0; c < n; ++c) W += ldnt(&ch[c]);
-                const double v = uniform_at(a.seed, a.round, (uint64_t)b, (uint64_t)k, 1);
-                const double target = v * W;
-                if (W > 0.0) {
-                    double cum = 0.0, base = 0.0;
-                    int pick = -1;
-                    for (int c = 0; c < n; ++c) {
-                        const double x = ldnt(&ch[c]);
-                        if (x > 0.0 && cum <= target) {
-                            pick = c;
-                            base = cum;
-                        }
-                        cum += x;
-                    }
-                    s_c = pick;
-                    s_base = base;
-                    s_target = target;
-                    mode = 1;
-                } else {
-                    status |= kStEmptyResidual;
-                    s_target = v;
-                    mode = 2;
-                }
-            }
-            if (k == K) W = 0.0;
+            status = deg | outside;
+            normal = true;
         }
-        s_k = k;
-        s_t = t;
-        s_W = W;
-        s_status = status;
-        s_mode = mode;
+        if (lane == 0) {
+            sm.fk = normal ? k : 0;
+            sm.fstatus = status;
+            sm.fmode = normal ? -1 : 0;
+            sm.ft = -1;
+            sm.fW = 0.0;
+        }
     }
     __syncthreads();
-    const int k = s_k;
-    const int mode = s_mode;
+    const int k = sm.fk;
+    int mode = 0;  // 0: done, 1: scan of one chunk, 2: empty residual (scan of the target row)
+    if (sm.fmode < 0) {
+        const UnitFast* uk = &U[k];
+        const int fb = ldnt(&uk->fallback);
+        const int greedy = ldnt(&uk->rq.greedy);
+        if (fb) {
+            if (threadIdx.x == 0) {
+                sm.ft = ldnt(&uk->tcand);
+                sm.fW = k == K ? 0.0 : (double)ldnt(&uk->W);
+                sm.fstatus |= ldnt(&uk->status) & kStEmptyResidual;
+            }
+        } else if (greedy) {
+            if (threadIdx.x == 0) sm.ft = ldnt(&uk->rq.argmax);
+        } else {
+            // the unit's chunk sums in token order, two per thread
+            const double* ch = reinterpret_cast<const double*>(f.ws + f.L.chunks) + (size_t)(b * (K + 1) + k) * f.nS * kChunks;
+            const int n = f.nS * kChunks;
+            const int c0 = 2 * threadIdx.x;
+            const double x0 = c0 < n ? ldnt(&ch[c0]) : 0.0;
+            const double x1 = c0 + 1 < n ? ldnt(&ch[c0 + 1]) : 0.0;
+            double W;
+            const double before = block_exclusive_scan<double>(x0 + x1, sm.redd, &W);
+            const double v = uniform_at(a.seed, a.round, (uint64_t)b, (uint64_t)k, 1);
+            if (W > 0.0) {
+                // the last chunk with mass whose preceding mass is <= v * W
+                const double target = v * W;
+                int pick = -1;
+                if (x0 > 0.0 && before <= target) pick = c0;
+                if (x1 > 0.0 && before + x0 <= target) pick = c0 + 1;
+                pick = block_max<int>(pick, sm.redi);
+                if (pick >= 0 && (pick >> 1) == (int)threadIdx.x) sm.fbase = (pick & 1) ? before + x0 : before;
+                if (threadIdx.x == 0) {
+                    sm.fc = pick;
+                    sm.ftarget = target;
+                    sm.fW = k == K ? 0.0 : W;
+                }
+                mode = 1;
+            } else {
+                if (threadIdx.x == 0) {
+                    sm.fstatus |= kStEmptyResidual;
+                    sm.ftarget = v;
+                    sm.fW = 0.0;
+                }
+                mode = 2;
+            }
+        }
+    }
+    __syncthreads();
     if (mode != 0) {
         const int unit = b * (K + 1) + k;
-        const UnitFast* uk = &U[unit];
+        // the row statistics of unit k (published by its slice 0), staged through LDS
+        constexpr int kWords = (int)(sizeof(RowFinal) / 4);
+        if ((int)threadIdx.x < 2 * kWords)
+            sm.fin[threadIdx.x] = ldnt(reinterpret_cast<const uint32_t*>(&U[k].rq) + threadIdx.x);
+        __syncthreads();
         RowFinal rq, rp;
-        // copy the row statistics (published by slice 0 of that unit)
         {
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(&uk->rq);
             uint32_t* dq = reinterpret_cast<uint32_t*>(&rq);
             uint32_t* dp = reinterpret_cast<uint32_t*>(&rp);
-            for (int i = 0; i < (int)(sizeof(RowFinal) / 4); ++i) {
-                dq[i] = ldnt(&src[i]);
-                dp[i] = ldnt(&src[i + sizeof(RowFinal) / 4]);
+#pragma unroll
+            for (int i = 0; i < kWords; ++i) {
+                dq[i] = sm.fin[i];
+                dp[i] = sm.fin[kWords + i];
             }
         }
         const int idk_q = ldnt(&IC[unit * 4 + 0]), idp_q = ldnt(&IC[unit * 4 + 1]);
@@ -1346,17 +1091,16 @@ __device__ __noinline__ void finalize_request(const FastArgs& f, Smem& sm, int b
         int lo, hi;
         double base;
         if (mode == 1) {
-            const int c = s_c;
+            const int c = sm.fc;
             const int slice = c / kChunks, within = c % kChunks;
             lo = slice * kSliceCols + (within / kWaves) * (kThreads * 8) + (within % kWaves) * kChunkCols;
             hi = min(lo + kChunkCols, a.V);
-            base = s_base;
+            base = sm.fbase;
         } else {
             lo = 0;
             hi = a.V;
             base = 0.0;
         }
-        const double target = mode == 1 ? s_target : 0.0;
         // mode 2 needs the total of q first
         double total_q = 0.0;
         if (mode == 2) {
@@ -1365,7 +1109,7 @@ __device__ __noinline__ void finalize_request(const FastArgs& f, Smem& sm, int b
                 acc += final_prob(rq, idk_q, idp_q, trow[col], col, false);
             total_q = block_sum<double>(acc, sm.redd);
         }
-        const double tgt = mode == 1 ? target : s_target * total_q;
+        const double tgt = mode == 1 ? sm.ftarget : sm.ftarget * total_q;
         int best = 0x7FFFFFFF, last = -1;
         for (int c0 = lo; c0 < hi; c0 += blockDim.x) {
             const int col = c0 + threadIdx.x;
@@ -1392,43 +1136,444 @@ __device__ __noinline__ void finalize_request(const FastArgs& f, Smem& sm, int b
             }
         }
         last = block_max<int>(last, sm.redi);
-        if (threadIdx.x == 0) s_t = best != 0x7FFFFFFF ? best : last;
+        if (threadIdx.x == 0) sm.ft = best != 0x7FFFFFFF ? best : last;
         __syncthreads();
     }
     if (threadIdx.x == 0) {
         a.out_k[b] = k;
-        a.out_t[b] = s_t;
-        if (a.out_W) a.out_W[b] = (float)s_W;
-        if (a.out_status) a.out_status[b] = s_status;
-        // leave the request's counters zeroed for the next call
+        a.out_t[b] = sm.ft;
+        if (a.out_W) a.out_W[b] = (float)sm.fW;
+        if (a.out_status) a.out_status[b] = sm.fstatus;
+        // leave the request's counter zeroed for the next call
         *reinterpret_cast<unsigned*>(f.ws + f.L.req + (size_t)b * 128) = 0u;
-        for (int j = 0; j <= K; ++j) {
-            const int unit = b * (K + 1) + j;
-            *reinterpret_cast<unsigned*>(f.ws + f.L.ctr + (size_t)unit * 128) = 0u;
-            *reinterpret_cast<unsigned*>(f.ws + f.L.flag + (size_t)unit * 128) = 0u;
-        }
     }
 }
 
 // ------------------------------------------------------------------------------------------
-// The kernel
+// Placement: request b runs on XCD b % 8 (workgroup index modulo 8 picks the XCD); its
+// (K + 1) units x nS slices follow in order.  Both kernels use the same map, so a slice's
+// summary is written and read through one L2.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_verify_kernel(FastArgs f) {
-    __shared__ Smem sm;
-    const VerifyArgs& a = f.a;
-    // placement: request b runs on XCD b % 8; its (K+1) units x nS slices follow in order
+struct Place {
+    int b, j, slice, unit, per_req;
+};
+__device__ __forceinline__ Place place_of(const FastArgs& f) {
+    Place p;
     const int x = blockIdx.x % kXcd;
     const int l = blockIdx.x / kXcd;
-    const int per_req = (a.K + 1) * f.nS;
-    const int b = (l / per_req) * kXcd + x;
-    if (b >= a.B) return;
-    const int j = (l / f.nS) % (a.K + 1);
-    const int slice = l % f.nS;
-    const int unit = b * (a.K + 1) + j;
+    p.per_req = (f.a.K + 1) * f.nS;
+    p.b = (l / p.per_req) * kXcd + x;
+    p.j = (l / f.nS) % (f.a.K + 1);
+    p.slice = l % f.nS;
+    p.unit = p.b * (f.a.K + 1) + p.j;
+    return p;
+}
+
+__device__ __forceinline__ bool params_ok(const spec_params& prm) {
+    return prm.temperature >= 0.0f && !isinf(prm.temperature) && prm.top_p > 0.0f;
+}
+
+// Columns [c0, c0 + kSliceCols) of a row, 16 bytes per load (zero past the row's end).
+__device__ __forceinline__ void load_slice(const uint16_t* row, int c0, int V, u32x4 (&v)[kLoads]) {
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        const int col = col_of(c0, q, 0);
+        v[q] = col < V ? *reinterpret_cast<const u32x4*>(row + col) : u32x4{0, 0, 0, 0};
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Count kernel: every slice of every unit loads its columns, counts them and publishes its
+// summaries (no waiting on other workgroups).
+// ------------------------------------------------------------------------------------------
+struct CountSmem {
+    double segm[kSegs];
+    uint32_t segc[2][kSegs];
+    union {
+        uint32_t hist[2][kBins];
+    } u;
+    uint32_t sp_key[2][kSpecial];
+    int32_t sp_id[2][kSpecial];
+    uint32_t n_sp[2];
+    uint32_t top_key[2][kTop];
+    int32_t top_id[2][kTop];
+    uint32_t n_top[2];
+    uint32_t rank_s[2];
+    uint32_t flags[2];
+    uint32_t neginf[2];
+    int32_t scan[kWaves + 1];
+    double redd[kWaves];
+    int32_t redi[kWaves];
+    uint32_t s_bits[2];
+    uint32_t tau;
+    int need;
+};
+
+// Per-segment element counts of row r into sm.segc[r]: one wave per group of 64 bins, the
+// last wave also sorts the specials into their four segments.  (Callers synchronise.)
+__device__ __forceinline__ void seg_counts(CountSmem& sm, int r) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+#pragma unroll 1
+    for (int g = wave; g < kGroups; g += kWaves) {
+        const uint32_t cs = wave_sum(sm.u.hist[r][g * kGroup + lane]);
+        if (lane == 0) sm.segc[r][seg_of_group(g)] = cs;
+    }
+    if (wave == kWaves - 1) {
+        const int nsp = min((int)sm.n_sp[r], kSpecial);
+        const int sg = lane < nsp ? special_seg(sm.sp_key[r][lane]) : -1;
+        const int sps[4] = {kSegHugePos, kSegTinyPos, kSegTinyNeg, kSegHugeNeg};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const uint32_t cx = (uint32_t)__popcll(__ballot(sg == sps[x]));
+            if (lane == 0) sm.segc[r][sps[x]] = cx;
+        }
+    }
+}
+
+// Wave 0: the key of the L-th element (token order) of row r in this slice, and how many
+// elements at that key are taken, into sm.tau / sm.need; (0, 0) when the slice holds fewer
+// than L finite elements.  Scans the segment counts, then the 64 bins of the crossing group,
+// or the specials of the crossing segment.
+__device__ __forceinline__ void local_threshold(CountSmem& sm, int r, int L) {
+    const int lane = threadIdx.x & (kWave - 1);
+    if (lane == 0) {
+        sm.tau = 0u;
+        sm.need = 0;
+    }
+    const int c = lane < kSegs ? (int)sm.segc[r][lane] : 0;
+    int cex;
+    const int cin = wave_scan(c, &cex);
+    const uint64_t hit = __ballot(lane < kSegs && cin >= L);
+    if (hit == 0) return;
+    const int sg = first_lane(hit);
+    const int rem = L - __shfl(cex, sg, kWave);
+    const int g = group_of_seg(sg);
+    if (g >= 0) {
+        const int bin = bin_of_sel(g, lane);  // lane order = descending key
+        const int n = (int)sm.u.hist[r][bin];
+        int nex;
+        const int nin = wave_scan(n, &nex);
+        const int i = first_lane(__ballot(nin >= rem));
+        if (lane == i) {
+            sm.tau = bin_key(bin);
+            sm.need = rem - nex;
+        }
+    } else {
+        const int nsp = min((int)sm.n_sp[r], kSpecial);
+        uint32_t k = 0;
+        bool mine = false;
+        if (lane < nsp) {
+            k = sm.sp_key[r][lane];
+            mine = special_seg(k) == sg;
+        }
+        int gt = 0, eq = 0;
+        for (int i = 0; i < nsp; ++i) {
+            const uint32_t k2 = sm.sp_key[r][i];
+            if (special_seg(k2) != sg) continue;
+            gt += k2 > k ? 1 : 0;
+            eq += k2 == k ? 1 : 0;
+        }
+        if (mine && gt < rem && gt + eq >= rem) {
+            sm.tau = k;
+            sm.need = rem - gt;
+        }
+    }
+}
+
+// The first L elements (token order: key desc, id asc) of row r in this slice, sorted, into
+// sm.top_key[r] / sm.top_id[r]; sm.n_top[r] gets their number.
+__device__ __forceinline__ void local_top(CountSmem& sm, int r, int L, int c0, int V, const u32x4 (&v)[kLoads]) {
+    if (threadIdx.x < kWave) local_threshold(sm, r, L);
+    if (threadIdx.x == 0) sm.n_top[r] = 0;
+    __syncthreads();
+    const uint32_t tau = sm.tau;
+    const int need = sm.need;
+    // every element strictly above tau (fewer than L of them), any order
+    uint32_t tiemask = 0;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int col = col_of(c0, q, e);
+            const uint32_t w = v[q][e >> 1];
+            const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+            if (col >= V || (h & 0x7FFFu) >= 0x7F80u) continue;  // past the row, inf, NaN
+            const uint32_t k = key16(h);
+            if (k > tau) {
+                const int slot = (int)atomicAdd(&sm.n_top[r], 1u);
+                if (slot < kTop) {
+                    sm.top_key[r][slot] = k;
+                    sm.top_id[r][slot] = col;
+                }
+            } else if (k == tau && need > 0) {
+                tiemask |= 1u << (q * 8 + e);
+            }
+        }
+    __syncthreads();
+    int base = min((int)sm.n_top[r], kTop);
+    int need_left = need;
+    // then the first `need` elements at tau in token order (uniform loop)
+    for (int q = 0; q < kLoads && need_left > 0; ++q) {
+        const uint32_t mq = (tiemask >> (q * 8)) & 0xFFu;
+        int total;
+        const int before = block_exclusive_scan<int>(__popc(mq), sm.scan, &total);
+        int k = 0;
+        for (int e = 0; e < 8; ++e) {
+            if (!(mq & (1u << e))) continue;
+            const int rank = before + k++;
+            const int slot = base + rank;
+            if (rank < need_left && slot < kTop) {
+                sm.top_key[r][slot] = tau;
+                sm.top_id[r][slot] = col_of(c0, q, e);
+            }
+        }
+        const int took = min(total, need_left);
+        base += took;
+        need_left -= took;
+    }
+    __syncthreads();
+    const int n = min(base, kTop);
+    // sort: key desc, id asc (rank by counting)
+    uint32_t mk = 0;
+    int mi = 0, rank = 0;
+    if ((int)threadIdx.x < n) {
+        mk = sm.top_key[r][threadIdx.x];
+        mi = sm.top_id[r][threadIdx.x];
+        for (int i = 0; i < n; ++i) {
+            const uint32_t k2 = sm.top_key[r][i];
+            const int i2 = sm.top_id[r][i];
+            rank += (k2 > mk || (k2 == mk && i2 < mi)) ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < n) {
+        sm.top_key[r][rank] = mk;
+        sm.top_id[r][rank] = mi;
+    }
+    if (threadIdx.x == 0) sm.n_top[r] = (uint32_t)n;
+    __syncthreads();
+}
+
+// Rank of the draft token among the elements of row r with its key that precede it in this
+// slice (the slice holding the token only), into sm.rank_s[r].
+__device__ __forceinline__ void local_rank(CountSmem& sm, int r, int c0, int s_tok, const u32x4 (&v)[kLoads]) {
+    const uint32_t ks = key16(sm.s_bits[r]);
+    uint32_t rank = 0;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int col = col_of(c0, q, e);
+            const uint32_t w = v[q][e >> 1];
+            const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+            rank += (col < s_tok && (h & 0x7FFFu) < 0x7F80u && key16(h) == ks) ? 1u : 0u;
+        }
+    rank = block_sum<uint32_t>(rank, reinterpret_cast<uint32_t*>(sm.redi));
+    if (threadIdx.x == 0) sm.rank_s[r] = rank;
+}
+
+// Publishes the summary of row r (its element passes are done): largest logit, per-segment
+// counts and masses, specials, the fine counts, the candidate list and the token's rank.
+__device__ __forceinline__ void publish_row(const FastArgs& f, CountSmem& sm, int unit, int slice, int r,
+                                            const spec_params& prm) {
+    RowPart* P = part_of(f, unit, slice, r);
+    const double T = (double)prm.temperature;
+    const int nsp = min((int)sm.n_sp[r], kSpecial);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    // largest key: highest non-empty bin or special
+    uint32_t mk = 0;
+#pragma unroll 1
+    for (int b = threadIdx.x; b < kBins; b += blockDim.x)
+        if (sm.u.hist[r][b] != 0) mk = max(mk, bin_key(b));
+    if ((int)threadIdx.x < nsp) mk = max(mk, sm.sp_key[r][threadIdx.x]);
+    mk = block_max<uint32_t>(mk, reinterpret_cast<uint32_t*>(sm.redi));
+    const float m = mk ? key16_value(mk) : -__builtin_inff();
+    // per-group masses (relative to this slice's largest logit), one wave per group
+#pragma unroll 1
+    for (int g = wave; g < kGroups; g += kWaves) {
+        const int bin = g * kGroup + lane;
+        const uint32_t c = sm.u.hist[r][bin];
+        double ms = 0.0;
+        if (c != 0 && T > 0.0) ms = (double)c * mass_of(key16_value(bin_key(bin)), m, T);
+        ms = wave_sum(ms);
+        if (lane == 0) sm.segm[seg_of_group(g)] = ms;
+    }
+    // the four special segments, one lane per special
+    if (wave == kWaves - 1) {
+        int sg = -1;
+        double ms = 0.0;
+        if (lane < nsp) {
+            const uint32_t k = sm.sp_key[r][lane];
+            sg = special_seg(k);
+            if (T > 0.0) ms = mass_of(key16_value(k), m, T);
+        }
+        const int sps[4] = {kSegHugePos, kSegTinyPos, kSegTinyNeg, kSegHugeNeg};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const double sx = wave_sum(sg == sps[x] ? ms : 0.0);
+            if (lane == 0) sm.segm[sps[x]] = sx;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const double S = wave_sum(lane < kSegs ? sm.segm[lane] : 0.0);
+        const uint32_t nfin = wave_sum(lane < kSegs ? sm.segc[r][lane] : 0u);
+        if (lane == 0) {
+            P->m = m;
+            P->maxkey = mk;
+            P->flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u);
+            P->n_neginf = sm.neginf[r];
+            P->n_finite = nfin;
+            P->n_special = (uint32_t)nsp;
+            P->S = S;
+            P->rank_s = sm.rank_s[r];
+            P->n_top = sm.n_top[r];
+        }
+    }
+    for (int sg = threadIdx.x; sg < kSegs; sg += blockDim.x) {
+        P->seg_mass[sg] = sm.segm[sg];
+        P->seg_count[sg] = sm.segc[r][sg];
+    }
+    if ((int)threadIdx.x < nsp) {
+        P->sp_key[threadIdx.x] = sm.sp_key[r][threadIdx.x];
+        P->sp_id[threadIdx.x] = sm.sp_id[r][threadIdx.x];
+    }
+    if ((int)threadIdx.x < (int)sm.n_top[r]) {
+        P->top_key[threadIdx.x] = sm.top_key[r][threadIdx.x];
+        P->top_id[threadIdx.x] = sm.top_id[r][threadIdx.x];
+    }
+    // fine counts, two per dword (a slice holds < 65536 columns)
+    uint32_t* fine32 = reinterpret_cast<uint32_t*>(P->fine);
+#pragma unroll 1
+    for (int i = threadIdx.x; i < kBins / 2; i += blockDim.x)
+        fine32[i] = (sm.u.hist[r][2 * i] & 0xFFFFu) | (sm.u.hist[r][2 * i + 1] << 16);
+    __syncthreads();  // segm is reused by the next row
+}
+
+// Counts this thread's columns of row r into sm.u.hist[r].  Values in the exact bins take
+// the straight path; the rest (zero, specials, -inf, +inf, NaN) are marked in a bit mask and
+// handled in a second, normally empty, loop.  TAIL: the slice ends inside the row.
+template <bool TAIL>
+__device__ __forceinline__ void count_row(CountSmem& sm, int r, int c0, int V, const u32x4 (&v)[kLoads]) {
+    uint32_t rare = 0;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t w = v[q][e >> 1];
+            const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+            const uint32_t off = (h & 0x7FFFu) - (uint32_t)(kExpLo << 7);
+            const bool in = off < (uint32_t)kNegBins && (!TAIL || col_of(c0, q, e) < V);
+            if (in) atomicAdd(&sm.u.hist[r][(h & 0x8000u) ? (kNegBins - 1 - (int)off) : (kPosBase + (int)off)], 1u);
+            else if (!TAIL || col_of(c0, q, e) < V) rare |= 1u << (q * 8 + e);
+        }
+    uint32_t bad = 0, ninf = 0;
+    while (rare) {
+        const int i = __builtin_ctz(rare);
+        rare &= rare - 1;
+        const int q = i >> 3, e = i & 7;
+        const uint32_t w = v[q][e >> 1];
+        const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+        int bin;
+        const int kind = classify(h, &bin);
+        if (kind == kKindBin) {
+            atomicAdd(&sm.u.hist[r][bin], 1u);
+        } else if (kind == kKindSpecial) {
+            const uint32_t slot = atomicAdd(&sm.n_sp[r], 1u);
+            if (slot < (uint32_t)kSpecial) {
+                sm.sp_key[r][slot] = key16(h);
+                sm.sp_id[r][slot] = col_of(c0, q, e);
+            }
+        } else if (kind == kKindNegInf) {
+            ++ninf;
+        } else {
+            bad = 1;
+        }
+    }
+    if (bad) atomicOr(&sm.flags[r], 1u);
+    if (ninf) atomicAdd(&sm.neginf[r], ninf);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void fast_count_kernel(FastArgs f) {
+    __shared__ CountSmem sm;
+    const VerifyArgs& a = f.a;
+    const Place P = place_of(f);
+    if (P.b >= a.B) return;
+    const int j = P.j, slice = P.slice, unit = P.unit;
+    const int c0 = slice * kSliceCols;
+    const bool two = j < a.K;
+    const spec_params prm = a.params[P.b];
+    if (!params_ok(prm)) return;  // the resolve kernel reports BAD_PARAM without reading summaries
+    const size_t stride = (size_t)a.V;
+    const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)P.b * (a.K + 1) + j) * stride;
+    const uint16_t* drow = two ? static_cast<const uint16_t*>(a.draft) + ((size_t)P.b * a.draft_rows + j) * stride : nullptr;
+    const int s_tok = two ? a.tokens[(size_t)P.b * a.K + j] : -1;
+    const bool tok_ok = !two || (s_tok >= 0 && s_tok < a.V);
+
+    u32x4 vq[kLoads], vp[kLoads];
+    load_slice(trow, c0, a.V, vq);
+    if (two) load_slice(drow, c0, a.V, vp);
+    for (int i = threadIdx.x; i < 2 * kBins; i += blockDim.x) (&sm.u.hist[0][0])[i] = 0u;
+    if (threadIdx.x < 2) {
+        sm.n_sp[threadIdx.x] = 0;
+        sm.flags[threadIdx.x] = 0;
+        sm.neginf[threadIdx.x] = 0;
+        sm.s_bits[threadIdx.x] = 0;
+    }
+    // the draft token's bits, needed for its rank by the slice that holds it
+    if (threadIdx.x == kWave && two && tok_ok && s_tok / kSliceCols == slice) {
+        sm.s_bits[0] = trow[s_tok];
+        sm.s_bits[1] = drow[s_tok];
+    }
+    __syncthreads();
+    const int ncols = min(kSliceCols, a.V - c0);
+    if (ncols == kSliceCols) {
+        count_row<false>(sm, 0, c0, a.V, vq);
+        if (two) count_row<false>(sm, 1, c0, a.V, vp);
+    } else {
+        count_row<true>(sm, 0, c0, a.V, vq);
+        if (two) count_row<true>(sm, 1, c0, a.V, vp);
+    }
+    if (threadIdx.x < 2) {
+        sm.n_top[threadIdx.x] = 0;
+        sm.rank_s[threadIdx.x] = 0;
+    }
+    __syncthreads();
+    seg_counts(sm, 0);
+    if (two) seg_counts(sm, 1);
+    __syncthreads();
+    // passes over the columns (registers) first, so the columns are dead for the summaries
+    const bool holds_s = two && tok_ok && s_tok / kSliceCols == slice;
+    const int want_q = list_len(a, prm, false), want_p = two ? list_len(a, prm, true) : 0;
+    if (want_q > 0) local_top(sm, 0, want_q, c0, a.V, vq);
+    if (holds_s) local_rank(sm, 0, c0, s_tok, vq);
+    if (two) {
+        if (want_p > 0) local_top(sm, 1, want_p, c0, a.V, vp);
+        if (holds_s) local_rank(sm, 1, c0, s_tok, vp);
+    }
+    __syncthreads();
+    publish_row(f, sm, unit, slice, 0, prm);
+    if (two) publish_row(f, sm, unit, slice, 1, prm);
+}
+
+// ------------------------------------------------------------------------------------------
+// Resolve kernel: every slice combines its unit's summaries into the exact processed
+// distributions (redundantly), tests acceptance and, where the unit needs it, re-reads its
+// columns to sum the residual over 512-column chunks; the last workgroup of a request to
+// finish picks k and t*.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_resolve_kernel(FastArgs f) {
+    __shared__ Smem sm;
+    const VerifyArgs& a = f.a;
+    const Place P = place_of(f);
+    if (P.b >= a.B) return;
+    const int b = P.b, j = P.j, slice = P.slice, unit = P.unit;
     const int c0 = slice * kSliceCols;
     const bool two = j < a.K;
     const spec_params prm = a.params[b];
-    const bool param_ok = prm.temperature >= 0.0f && !isinf(prm.temperature) && prm.top_p > 0.0f;
+    const bool param_ok = params_ok(prm);
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)b * (a.K + 1) + j) * stride;
     const uint16_t* drow = two ? static_cast<const uint16_t*>(a.draft) + ((size_t)b * a.draft_rows + j) * stride : nullptr;
@@ -1437,81 +1582,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     UnitFast* U = reinterpret_cast<UnitFast*>(f.ws + f.L.units) + unit;
     int32_t* IC = reinterpret_cast<int32_t*>(f.ws + f.L.idcut) + unit * 4;
 
-    // ---- phase A: load, count, publish ----
-    u32x4 vq[kLoads], vp[kLoads];
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) {
-        const int col = col_of(c0, q, 0);
-        vq[q] = col < a.V ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(trow + col)) : u32x4{0, 0, 0, 0};
-        vp[q] = (two && col < a.V) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(drow + col))
-                                   : u32x4{0, 0, 0, 0};
-    }
-    for (int i = threadIdx.x; i < 2 * kBins; i += blockDim.x) (&sm.u.hist[0][0])[i] = 0u;
-    if (threadIdx.x < 2) {
-        sm.n_sp[threadIdx.x] = 0;
-        sm.flags[threadIdx.x] = 0;
-        sm.neginf[threadIdx.x] = 0;
-        sm.s_bits[threadIdx.x] = 0;
-    }
-    if (threadIdx.x == 0 && two && tok_ok) {
+    if (threadIdx.x < 2) sm.s_bits[threadIdx.x] = 0;
+    __syncthreads();
+    if (threadIdx.x == kWave && two && tok_ok) {  // a lane outside wave 0, which loads the headers
         sm.s_bits[0] = trow[s_tok];
         sm.s_bits[1] = drow[s_tok];
     }
-    __syncthreads();
-    if (param_ok) {
-        for (int r = 0; r < (two ? 2 : 1); ++r) {
-            uint32_t bad = 0, ninf = 0;
-#pragma unroll
-            for (int q = 0; q < kLoads; ++q)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int col = col_of(c0, q, e);
-                    const uint32_t w = r == 0 ? vq[q][e >> 1] : vp[q][e >> 1];
-                    const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-                    if (col >= a.V) continue;
-                    const uint32_t off = (h & 0x7FFFu) - (uint32_t)(kExpLo << 7);
-                    if (off < (uint32_t)kNegBins) {
-                        const int bin = (h & 0x8000u) ? (kNegBins - 1 - (int)off) : (kPosBase + (int)off);
-                        atomicAdd(&sm.u.hist[r][bin], 1u);
-                    } else {
-                        int bin;
-                        const int kind = classify(h, &bin);
-                        if (kind == kKindBin) {
-                            atomicAdd(&sm.u.hist[r][bin], 1u);
-                        } else if (kind == kKindSpecial) {
-                            const uint32_t slot = atomicAdd(&sm.n_sp[r], 1u);
-                            if (slot < (uint32_t)kSpecial) {
-                                sm.sp_key[r][slot] = key16(h);
-                                sm.sp_id[r][slot] = col;
-                            }
-                        } else if (kind == kKindNegInf) {
-                            ++ninf;
-                        } else {
-                            bad = 1;
-                        }
-                    }
-                }
-            if (bad) atomicOr(&sm.flags[r], 1u);
-            if (ninf) atomicAdd(&sm.neginf[r], ninf);
-        }
-        __syncthreads();
-        publish_row(f, sm, unit, slice, 0, prm, false, c0, vq, two && tok_ok ? s_tok : -1);
-        if (two) publish_row(f, sm, unit, slice, 1, prm, true, c0, vp, tok_ok ? s_tok : -1);
-    }
 
-    // ---- unit barrier ----
-    unsigned* ctr = reinterpret_cast<unsigned*>(f.ws + f.L.ctr + (size_t)unit * 128);
-    unsigned* flag = reinterpret_cast<unsigned*>(f.ws + f.L.flag + (size_t)unit * 128);
-    const bool synced = unit_barrier(ctr, flag, f.nS);
-
-    // ---- phase C: combine, accept, residual ----
     uint32_t status = 0;
     int accept = 0;
     bool need_resid = false;
     bool fb_unit = false;
-    if (!synced) {
-        status = SPEC_ST_SYNC_TIMEOUT;
-    } else if (!param_ok) {
+    if (!param_ok) {
         status = kStBadParam;
     } else {
         combine_row(f, sm, unit, 0, prm, false);
@@ -1560,12 +1642,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
                     if (r == 0) U->rq = rf;
                     else U->rp = rf;
                     // explicit and trivial id cuts (histogram cuts are written by their owner)
-                    const Cut* cs[2] = {&rv.ck, &rv.cp};
-                    const int has[2] = {rv.has_k, rv.has_p};
-                    for (int c = 0; c < 2; ++c) {
-                        if (!has[c] || cs[c]->key == 0) IC[r * 2 + c] = a.V - 1;
-                        else if (cs[c]->explicit_id >= 0) IC[r * 2 + c] = cs[c]->explicit_id;
-                    }
+                    if (!rv.has_k || rv.ck.key == 0) IC[r * 2 + 0] = a.V - 1;
+                    else if (rv.ck.explicit_id >= 0) IC[r * 2 + 0] = rv.ck.explicit_id;
+                    if (!rv.has_p || rv.cp.key == 0) IC[r * 2 + 1] = a.V - 1;
+                    else if (rv.cp.explicit_id >= 0) IC[r * 2 + 1] = rv.cp.explicit_id;
                 }
                 U->fallback = 0;
                 U->tcand = -1;
@@ -1578,6 +1658,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         U->status = status;
     }
     if (need_resid) {
+        u32x4 vq[kLoads], vp[kLoads];
+        load_slice(trow, c0, a.V, vq);
+        if (two) load_slice(drow, c0, a.V, vp);
         int eff[2][2];
         for (int r = 0; r < (two ? 2 : 1); ++r) {
             const RowView& rv = sm.rv[r];
@@ -1613,7 +1696,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     if (threadIdx.x == 0) {
         unsigned* rc = reinterpret_cast<unsigned*>(f.ws + f.L.req + (size_t)b * 128);
         const unsigned old = l2_fetch_add(rc, 1u);
-        sm.last = (old + 1 == (unsigned)per_req) ? 1 : 0;
+        sm.last = (old + 1 == (unsigned)P.per_req) ? 1 : 0;
     }
     __syncthreads();
     if (sm.last) finalize_request(f, sm, b);
@@ -1637,7 +1720,7 @@ bool fast_path_applies(const VerifyArgs& a) {
     if (a.V % 8 != 0 || a.V < 2048) return false;
     if ((reinterpret_cast<uintptr_t>(a.draft) & 15) || (reinterpret_cast<uintptr_t>(a.target) & 15)) return false;
     const int nS = (a.V + kSliceCols - 1) / kSliceCols;
-    return nS <= 32;
+    return nS * kTop <= kMergeCap;  // every slice's candidate list fits the merge buffer
 }
 
 int fast_verify(const VerifyArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -1649,7 +1732,8 @@ int fast_verify(const VerifyArgs& a, void* ws, size_t ws_bytes, hipStream_t stre
     f.units = p.units;
     f.ws = static_cast<char*>(ws);
     f.L = layout(a.B, p.units, p.nS);
-    hipLaunchKernelGGL(fast_verify_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, stream, f);
+    hipLaunchKernelGGL(fast_count_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, stream, f);
+    hipLaunchKernelGGL(fast_resolve_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, stream, f);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
