@@ -93,10 +93,7 @@ enum {
     SPEC_ST_BAD_TOKEN = 64,                /* a draft token outside [0, V): k = 0, t* = -1 */
     SPEC_ST_DEGENERATE_DOWNWEIGHT = 128,   /* C = 0 and the set holds all the draft mass: the
                                               row is left undownweighted */
-    SPEC_ST_BAD_PARAM = 256,               /* invalid spec_params: k = 0, t* = -1 */
-    SPEC_ST_SYNC_TIMEOUT = 512             /* a workgroup rendezvous gave up waiting (never expected;
-                                              results of the request are invalid and the workspace
-                                              must be zero-filled again) */
+    SPEC_ST_BAD_PARAM = 256                /* invalid spec_params: k = 0, t* = -1 */
 };
 
 /* Uniforms.  Counter-based Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and counter
