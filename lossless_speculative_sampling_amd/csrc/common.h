@@ -89,57 +89,106 @@ __device__ __forceinline__ double uniform_at(uint64_t seed, uint64_t round, uint
 }
 
 // ------------------------------------------------------------------------------------------
-// Wavefront / workgroup reductions (wave64).  `red` is LDS scratch of >= 2 * waves entries.
+// Cross-lane moves.  Reductions and scans use DPP (operand permutations inside VALU
+// instructions) and v_readlane, never ds_bpermute: those go through the LDS unit, where they
+// queue behind other workgroups' histogram atomics.
 // ------------------------------------------------------------------------------------------
+enum : int {
+    kDppQuadSwap1 = 0xB1,      // quad_perm [1,0,3,2]: lane ^ 1
+    kDppQuadSwap2 = 0x4E,      // quad_perm [2,3,0,1]: lane ^ 2
+    kDppRowShr1 = 0x111,
+    kDppRowShr2 = 0x112,
+    kDppRowShr4 = 0x114,
+    kDppRowShr8 = 0x118,
+    kDppWaveShr1 = 0x138,      // lane i <- lane i - 1 across the wave
+    kDppRowMirror = 0x140,     // within 16 lanes: i <- 15 - i
+    kDppRowHalfMirror = 0x141, // within 8 lanes: i <- 7 - i
+    kDppRowBcast15 = 0x142,    // lane 15 of each row -> the next row
+    kDppRowBcast31 = 0x143,    // lane 31 -> rows 2 and 3
+};
+
+// v from the lane that DPP control CTRL names; 0 where the source lane does not exist or the
+// row is masked off (ROW_MASK).
+template <int CTRL, int ROW_MASK = 0xF, typename T>
+__device__ __forceinline__ T dpp(T v) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+    if constexpr (sizeof(T) == 4) {
+        int u;
+        __builtin_memcpy(&u, &v, 4);
+        u = __builtin_amdgcn_update_dpp(0, u, CTRL, ROW_MASK, 0xF, true);
+        T r;
+        __builtin_memcpy(&r, &u, 4);
+        return r;
+    } else {
+        int u[2];
+        __builtin_memcpy(u, &v, 8);
+        u[0] = __builtin_amdgcn_update_dpp(0, u[0], CTRL, ROW_MASK, 0xF, true);
+        u[1] = __builtin_amdgcn_update_dpp(0, u[1], CTRL, ROW_MASK, 0xF, true);
+        T r;
+        __builtin_memcpy(&r, u, 8);
+        return r;
+    }
+}
+
+// v of lane `lane` (a wave-uniform index) in every lane.
+template <typename T>
+__device__ __forceinline__ T wave_bcast(T v, int lane) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+    if constexpr (sizeof(T) == 4) {
+        int u;
+        __builtin_memcpy(&u, &v, 4);
+        u = __builtin_amdgcn_readlane(u, lane);
+        T r;
+        __builtin_memcpy(&r, &u, 4);
+        return r;
+    } else {
+        int u[2];
+        __builtin_memcpy(u, &v, 8);
+        u[0] = __builtin_amdgcn_readlane(u[0], lane);
+        u[1] = __builtin_amdgcn_readlane(u[1], lane);
+        T r;
+        __builtin_memcpy(&r, u, 8);
+        return r;
+    }
+}
+
+// Butterfly over each row of 16 lanes, then the four row results; fixed order, so every
+// wave of every workgroup combining the same values gets the same bits.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce(T v, Op op) {
+    v = op(v, dpp<kDppQuadSwap1>(v));
+    v = op(v, dpp<kDppQuadSwap2>(v));
+    v = op(v, dpp<kDppRowHalfMirror>(v));
+    v = op(v, dpp<kDppRowMirror>(v));
+    const T r0 = wave_bcast(v, 0), r1 = wave_bcast(v, 16), r2 = wave_bcast(v, 32), r3 = wave_bcast(v, 48);
+    return op(op(r0, r1), op(r2, r3));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    return wave_allreduce(v, [](T a, T b) { return a + b; });
 }
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        T w = __shfl_xor(v, o, kWave);
-        v = w > v ? w : v;
-    }
-    return v;
+    return wave_allreduce(v, [](T a, T b) { return b > a ? b : a; });
 }
 template <typename T>
 __device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        T w = __shfl_xor(v, o, kWave);
-        v = w < v ? w : v;
-    }
-    return v;
+    return wave_allreduce(v, [](T a, T b) { return b < a ? b : a; });
 }
-
 template <typename T>
 __device__ __forceinline__ T wave_or(T v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
-    return v;
+    return wave_allreduce(v, [](T a, T b) { return a | b; });
 }
 
-// Inclusive prefix sum over the lanes of a wave in lane order; *excl gets the exclusive one.
+// Sum over each aligned group of 8 lanes, in every lane of the group.
 template <typename T>
-__device__ __forceinline__ T wave_scan(T v, T* excl) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        T y = __shfl_up(v, o, kWave);
-        if (lane >= o) v += y;
-    }
-    T e = __shfl_up(v, 1, kWave);
-    *excl = lane == 0 ? T(0) : e;
+__device__ __forceinline__ T group8_sum(T v) {
+    v += dpp<kDppQuadSwap1>(v);
+    v += dpp<kDppQuadSwap2>(v);
+    v += dpp<kDppRowHalfMirror>(v);
     return v;
 }
-
-// Lowest / highest set lane of a ballot (-1 when empty).
-__device__ __forceinline__ int first_lane(uint64_t m) { return m ? __builtin_ctzll(m) : -1; }
-__device__ __forceinline__ int last_lane(uint64_t m) { return m ? 63 - __builtin_clzll(m) : -1; }
 
 template <typename T, int OP>  // OP 0 sum, 1 max, 2 min
 __device__ __forceinline__ T wave_reduce(T v) {
@@ -147,6 +196,23 @@ __device__ __forceinline__ T wave_reduce(T v) {
     if (OP == 1) return wave_max(v);
     return wave_min(v);
 }
+
+// Inclusive prefix sum over the lanes of a wave in lane order; *excl gets the exclusive one.
+template <typename T>
+__device__ __forceinline__ T wave_scan(T v, T* excl) {
+    v += dpp<kDppRowShr1>(v);
+    v += dpp<kDppRowShr2>(v);
+    v += dpp<kDppRowShr4>(v);
+    v += dpp<kDppRowShr8>(v);
+    v += dpp<kDppRowBcast15, 0xA>(v);
+    v += dpp<kDppRowBcast31, 0xC>(v);
+    *excl = dpp<kDppWaveShr1>(v);
+    return v;
+}
+
+// Lowest / highest set lane of a ballot (-1 when empty).
+__device__ __forceinline__ int first_lane(uint64_t m) { return m ? __builtin_ctzll(m) : -1; }
+__device__ __forceinline__ int last_lane(uint64_t m) { return m ? 63 - __builtin_clzll(m) : -1; }
 
 // Workgroup reduction; every thread gets the result.  Deterministic (fixed tree).
 template <typename T, int OP>
@@ -181,14 +247,8 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* red, T* total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nwaves = blockDim.x / kWave;
-    T inc = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        T y = __shfl_up(inc, o, kWave);
-        if (lane >= o) inc += y;
-    }
-    T exc = __shfl_up(inc, 1, kWave);
-    if (lane == 0) exc = T(0);
+    T exc;
+    const T inc = wave_scan(v, &exc);
     __syncthreads();
     if (lane == kWave - 1) red[wave] = inc;
     __syncthreads();

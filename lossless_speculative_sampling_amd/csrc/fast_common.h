@@ -1,0 +1,286 @@
+// Device-side pieces shared by the two kernels of the bf16 verification path: the bf16 value
+// classes and their exact bins, the workspace records, the workgroup placement and the
+// packed bin computation.
+#pragma once
+
+#include "fastpath.h"
+
+namespace sv {
+namespace fast {
+
+// ------------------------------------------------------------------------------------------
+// bf16 values, bins and segments
+// ------------------------------------------------------------------------------------------
+enum : int { kKindBin = 0, kKindSpecial = 1, kKindNegInf = 2, kKindBad = 3 };
+
+__device__ __forceinline__ int classify(uint32_t h, int* bin) {
+    const uint32_t mag = h & 0x7FFFu;
+    const uint32_t e = mag >> 7;
+    if (e >= (uint32_t)kExpLo && e < (uint32_t)kExpHi) {
+        const int off = (int)mag - (kExpLo << 7);
+        *bin = (h & 0x8000u) ? (kNegBins - 1 - off) : (kPosBase + off);
+        return kKindBin;
+    }
+    if (mag == 0) {
+        *bin = kZeroBin;
+        return kKindBin;
+    }
+    if (mag < 0x7F80u) return kKindSpecial;
+    if (mag == 0x7F80u && (h & 0x8000u)) return kKindNegInf;
+    return kKindBad;  // +inf or NaN
+}
+
+// 16-bit order key of a bf16 value (grows with the value; -0 folded onto +0).
+__device__ __forceinline__ uint32_t key16(uint32_t h) {
+    if (h == 0x8000u) h = 0;
+    return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+}
+__device__ __forceinline__ float key16_value(uint32_t k) {
+    const uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+    return __uint_as_float(h << 16);
+}
+__device__ __forceinline__ uint32_t bin_key(int bin) {
+    if (bin < kNegBins) return key16(0x8000u | (uint32_t)((kExpLo << 7) + (kNegBins - 1 - bin)));
+    if (bin < kPosBase) return 0x8000u;
+    return key16((uint32_t)((kExpLo << 7) + (bin - kPosBase)));
+}
+// bin of an order key known to be in the exact range (or zero)
+__device__ __forceinline__ int key_bin(uint32_t k) {
+    const uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+    int b = -1;
+    classify(h, &b);
+    return b;
+}
+__device__ __forceinline__ bool key_is_binned(uint32_t k) {
+    const uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+    int b;
+    return classify(h, &b) == kKindBin;
+}
+__host__ __device__ constexpr int seg_of_group(int g) {
+    return g < kNegGroups ? (kSegTinyNeg + 1 + (kNegGroups - 1 - g)) : (g == kZeroGroup ? kSegZero : 1 + (kGroups - 1 - g));
+}
+__host__ __device__ constexpr int group_of_seg(int s) {
+    return (s >= 1 && s < kSegTinyPos) ? (kGroups - s)
+           : (s == kSegZero ? kZeroGroup : ((s > kSegTinyNeg && s < kSegHugeNeg) ? (kNegGroups - 1 - (s - kSegTinyNeg - 1)) : -1));
+}
+static_assert(group_of_seg(seg_of_group(0)) == 0, "segment map");
+static_assert(group_of_seg(seg_of_group(kNegGroups - 1)) == kNegGroups - 1, "segment map");
+static_assert(group_of_seg(seg_of_group(kZeroGroup)) == kZeroGroup, "segment map");
+static_assert(group_of_seg(seg_of_group(kZeroGroup + 1)) == kZeroGroup + 1, "segment map");
+static_assert(group_of_seg(seg_of_group(kGroups - 1)) == kGroups - 1, "segment map");
+static_assert(seg_of_group(kGroups - 1) == 1 && seg_of_group(kNegGroups - 1) == kSegTinyNeg + 1, "segment order");
+static_assert(seg_of_group(0) == kSegHugeNeg - 1, "segment order");
+
+// segment of a special (finite, outside the exact bins) key
+__device__ __forceinline__ int special_seg(uint32_t k) {
+    const bool pos = (k & 0x8000u) != 0;
+    const uint32_t h = pos ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+    const bool huge = ((h & 0x7FFFu) >> 7) >= (uint32_t)kExpHi;
+    return pos ? (huge ? kSegHugePos : kSegTinyPos) : (huge ? kSegHugeNeg : kSegTinyNeg);
+}
+
+// ------------------------------------------------------------------------------------------
+// Workspace records
+// ------------------------------------------------------------------------------------------
+struct alignas(16) RowPart {  // one slice of one row, written by the count kernel
+    float m;            // largest finite logit of the slice, -inf when none
+    uint32_t flags;     // 1: NaN or +inf seen, 2: special list overflow
+    uint32_t n_finite;
+    uint32_t n_special;
+    uint32_t n_top;
+    uint32_t cnt_s;     // elements with the draft token's key that precede it: all of them in a
+                        // slice before the token's, those with a lower id in the token's slice
+    uint32_t s_bits;    // bf16 bits of the row at the draft token (0 without a token)
+    uint32_t n_neginf;
+    double S;           // sum of exp((z - m)/T) over the slice's finite elements
+    double seg_mass[kSegs];
+    uint32_t seg_count[kSegs];
+    uint32_t top_key[kTop];
+    int32_t top_id[kTop];
+    uint32_t sp_key[kSpecial];
+    int32_t sp_id[kSpecial];
+    uint16_t fine[kBins];
+};
+static_assert(offsetof(RowPart, S) == 32, "header layout: 2 x 16 bytes, then S");
+
+struct RowFinal {  // enough to evaluate any element's processed probability
+    float m;
+    float T;
+    double S;      // normaliser of the processed distribution
+    double C;      // factor on the downweighted set (1 when off)
+    double Z;      // normaliser after the downweight (1 when off)
+    uint32_t kk;   // top-k cut key (id cut in UnitFast::idcut[.][0])
+    uint32_t kp;   // nucleus cut key (id cut in UnitFast::idcut[.][1])
+    uint32_t kF;   // downweighted set: key > kF, or key == kF and id <= idF (nS > 0)
+    int32_t idF;
+    int32_t nS;
+    int32_t argmax;
+    int32_t greedy;
+    int32_t has_special;  // slices hold finite values outside the bins (finalizer recomputes them)
+};
+
+struct UnitFast {
+    int32_t accept;
+    uint32_t status;
+    int32_t fallback;   // processed by the general algorithm: tcand / W are final
+    int32_t tcand;
+    float W;
+    int32_t pad;
+    RowFinal rq, rp;
+};
+
+struct Layout {
+    size_t req, parts, units, idcut, chunks, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+__host__ __device__ inline Layout layout(int B, int units, int nS) {
+    Layout L;
+    size_t o = 0;
+    L.req = o;    o += align256((size_t)B * 128);               // request arrival counters
+    L.parts = o;  o += align256((size_t)units * nS * 2 * sizeof(RowPart));
+    L.units = o;  o += align256((size_t)units * sizeof(UnitFast));
+    L.idcut = o;  o += align256((size_t)units * 4 * sizeof(int32_t));
+    L.chunks = o; o += align256((size_t)units * nS * kChunks * sizeof(double));
+    L.total = o;
+    return L;
+}
+
+struct FastArgs {
+    VerifyArgs a;
+    int nS;
+    int units;
+    char* ws;
+    Layout L;
+};
+
+// ------------------------------------------------------------------------------------------
+// Request arrival counter in the XCD's L2 (every workgroup of a request runs on one XCD)
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ unsigned l2_fetch_add(unsigned* p, unsigned v) {
+    unsigned old;
+    asm volatile("s_waitcnt vmcnt(0)\n\tglobal_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
+                 : "=v"(old) : "v"(p), "v"(v) : "memory");
+    return old;
+}
+
+// Every wave waits until its own global stores have reached L2; __syncthreads() alone orders
+// only LDS traffic, so this must precede the workgroup barrier in front of an arrival.
+__device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ------------------------------------------------------------------------------------------
+// Loads of data published by other workgroups (non-temporal: bypass L1, served by L2)
+// ------------------------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T ldnt(const T* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint32_t ldnt_u16(const uint16_t* p) {
+    // u16 via the enclosing aligned dword
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3));
+    return (a & 2) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Columns of a slice are held as: load q, thread t, element e  ->  c0 + q*kThreads*8 + t*8 + e,
+// so (q, t, e) in lexicographic order is token-id order.
+__device__ __forceinline__ int col_of(int c0, int q, int e) { return c0 + q * kThreads * 8 + (int)threadIdx.x * 8 + e; }
+
+// ------------------------------------------------------------------------------------------
+// Workgroup geometry
+// ------------------------------------------------------------------------------------------
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMergeCap = 1024;   // merged candidates per row (top lists or one segment's specials)
+constexpr int kMaxSlices = kMergeCap / kTop;  // 16
+
+__device__ __forceinline__ RowPart* part_of(const FastArgs& f, int unit, int slice, int r) {
+    return reinterpret_cast<RowPart*>(f.ws + f.L.parts) + ((size_t)unit * f.nS + slice) * 2 + r;
+}
+
+// e of a finite value relative to the row's largest logit
+__device__ __forceinline__ double mass_of(float z, float m, double T) { return exp(((double)z - (double)m) / T); }
+
+// Segment of any finite order key.
+__device__ __forceinline__ int seg_of_key(uint32_t k) {
+    return key_is_binned(k) ? seg_of_group(key_bin(k) / kGroup) : special_seg(k);
+}
+
+// Bin of lane `lane` in a walk over group g in descending key order.
+__device__ __forceinline__ int bin_of_sel(int g, int lane) { return g * kGroup + (kGroup - 1 - lane); }
+
+// ------------------------------------------------------------------------------------------
+// Number of leading candidates each slice lists for a row (identical in phase A and combine)
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int list_len(const VerifyArgs& a, const spec_params& prm, bool draft) {
+    const bool greedy = prm.temperature == 0.0f;
+    int want = greedy ? 1 : 0;
+    if (!greedy && prm.top_k > 0 && prm.top_k < a.V && prm.top_k <= kTop) want = max(want, prm.top_k);
+    if (!greedy && draft && a.F > 0 && a.C < 1.0f) want = max(want, a.F);
+    return want;
+}
+
+// ------------------------------------------------------------------------------------------
+// Placement: request b runs on XCD b % 8 (workgroup index modulo 8 picks the XCD); its
+// (K + 1) units x nS slices follow in order.  Both kernels use the same map, so a slice's
+// summary is written and read through one L2.
+// ------------------------------------------------------------------------------------------
+struct Place {
+    int b, j, slice, unit, per_req;
+};
+__device__ __forceinline__ Place place_of(const FastArgs& f) {
+    Place p;
+    const int x = blockIdx.x % kXcd;
+    const int l = blockIdx.x / kXcd;
+    p.per_req = (f.a.K + 1) * f.nS;
+    p.b = (l / p.per_req) * kXcd + x;
+    p.j = (l / f.nS) % (f.a.K + 1);
+    p.slice = l % f.nS;
+    p.unit = p.b * (f.a.K + 1) + p.j;
+    return p;
+}
+
+__device__ __forceinline__ bool params_ok(const spec_params& prm) {
+    return prm.temperature >= 0.0f && !isinf(prm.temperature) && prm.top_p > 0.0f;
+}
+
+// Columns [c0, c0 + kSliceCols) of a row, 16 bytes per load (zero past the row's end).
+__device__ __forceinline__ void load_slice(const uint16_t* row, int c0, int V, u32x4 (&v)[kLoads]) {
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        const int col = col_of(c0, q, 0);
+        v[q] = col < V ? *reinterpret_cast<const u32x4*>(row + col) : u32x4{0, 0, 0, 0};
+    }
+}
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+
+// Histogram rows in LDS: 4 words of padding, the kBins exact bins, 4 words of padding.  Words
+// 3 and kBins + 4 collect every value outside the exact bins (the packed count below sends
+// them there), so the count needs no branch; a second pass settles them when either is
+// non-zero.
+constexpr int kHistLead = 4;
+constexpr int kHistRow = kHistLead + kBins + 4;   // 2888 words, rows 16-byte aligned
+static_assert(kHistRow % 4 == 0, "16-byte aligned histogram rows");
+
+// Byte offsets, within a padded histogram row, of the bins of the two bf16 values packed in
+// w (low half, high half), computed two at a time with packed 16-bit operations.  A value
+// outside the exact bins lands in a padding word (kHistLead - 1 or kHistLead + kBins).
+__device__ __forceinline__ uint32_t hist_offsets2(uint32_t w) {
+    constexpr uint16_t kBase = kExpLo << 7;                                 // 0x3C80
+    constexpr uint16_t kNegAdd = (uint16_t)(4 * (kHistLead + kNegBins - 1) + 1);  // with ~(4 off)
+    constexpr uint16_t kPosAdd = (uint16_t)(4 * (kHistLead + kPosBase));
+    u16x2 off = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu) - (u16x2)kBase;  // wraps below the range
+    off = __builtin_elementwise_min(off, (u16x2)(uint16_t)kNegBins) << (u16x2)(uint16_t)2;
+    const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, w) >> (i16x2)(int16_t)15);
+    const uint32_t x = __builtin_bit_cast(uint32_t, off) ^ neg;             // negative: 0xFFFF - 4 off
+    const uint32_t add = (neg & ((uint32_t)kNegAdd * 0x10001u)) | (~neg & ((uint32_t)kPosAdd * 0x10001u));
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, x) + __builtin_bit_cast(u16x2, add));
+}
+
+void launch_count(const FastArgs& f, int grid, hipStream_t stream);
+void launch_resolve(const FastArgs& f, int grid, hipStream_t stream);
+
+}  // namespace fast
+}  // namespace sv
