@@ -15,6 +15,9 @@
  *                          F_k guessed outcome tokens.
  *   saguaro_cache_lookup - hit / miss of the verified outcome (k, t*) against the cache, or the
  *                          branch-reuse test of a branch-complete tree.
+ *   saguaro_verify_cache - spec_verify and saguaro_cache_build fused: one pass over the draft
+ *                          rows serves both (the cache's token sets are the leading tokens of
+ *                          the same rows the verification reads).
  *
  * Sources (notation p = draft, q = target, as on the DeepMind page):
  *   [SpS]   "Accelerating LLM Decoding with Speculative Sampling" (DeepMind, arXiv 2302.01318),
@@ -164,6 +167,24 @@ int saguaro_fanout(int K, int budget, double a, double r, int32_t* out_fanout);
 int saguaro_cache_build(const void* draft_logits, int dtype, int B, int K, int V, const int32_t* draft_tokens,
                         int budget, double a, double r, int32_t* out_fanout_host, int32_t* out_cache,
                         hipStream_t stream);
+
+/* saguaro_verify_cache - spec_verify followed by saguaro_cache_build on the same inputs, in
+ * one pass over the logits ([SSD] sections 4.3 and 5.1: the cache is built from the draft
+ * distributions the verification reads).  Outputs are exactly those of
+ *   spec_verify(draft_logits, K + 1, target_logits, dtype, B, K, V, params, F, C, draft_tokens,
+ *               seed, round, flags, out_k, out_tstar, out_resid_mass, out_status, workspace, ...)
+ *   saguaro_cache_build(draft_logits, dtype, B, K, V, draft_tokens, budget, a, r,
+ *                       out_fanout_host, out_cache, stream)
+ * (with SPEC_SAMPLE_DRAFT the cache leaves out the drafted tokens this call samples).
+ *   draft_logits  [B][K+1][V] (draft row K feeds the cache only)
+ *   workspace     spec_workspace_bytes(B, K, V) bytes, same contract as spec_verify
+ * Return codes: as spec_verify and saguaro_cache_build (SPEC_EINVAL also for a null out_cache
+ * or an invalid fan-out). */
+int saguaro_verify_cache(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
+                         const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,
+                         uint64_t round, uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host,
+                         int32_t* out_k, int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status,
+                         int32_t* out_cache, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* saguaro_cache_lookup - hit / miss of the verified outcome.
  * mode 0 ([SSD-H] Method: cache lookup; [SSD] section 7.1): cache [B][sum F] from

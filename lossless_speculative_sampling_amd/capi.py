@@ -28,7 +28,7 @@ ST_DEGENERATE_DOWNWEIGHT = 128
 ST_BAD_PARAM = 256
 
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
-           "saguaro_cache_lookup")
+           "saguaro_cache_lookup", "saguaro_verify_cache")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -57,6 +57,9 @@ class Lib:
         L.saguaro_fanout.argtypes = [_I, _I, _D, _D, _P]
         L.saguaro_cache_build.argtypes = [_P, _I, _I, _I, _I, _P, _I, _D, _D, _P, _P, _P]
         L.saguaro_cache_lookup.argtypes = [_I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]
+        L.saguaro_verify_cache.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
+                                           ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                           _P]
         for fn in EXPORTS[1:]:
             getattr(L, fn).restype = _I
 
@@ -180,6 +183,35 @@ def saguaro_cache_build(draft: torch.Tensor, K: int, tokens: torch.Tensor, budge
                                          ctypes.cast(fan, _P), _ptr(cache), _stream(stream))
     _check("saguaro_cache_build", rc)
     return cache[:, :budget], list(fan)
+
+
+def saguaro_verify_cache(draft: torch.Tensor, target: torch.Tensor, K: int, params: torch.Tensor, tokens: torch.Tensor,
+                         budget: int, a: float, r: float, F: int = 0, C: float = 1.0, seed: int = 0, round_: int = 0,
+                         flags: int = 0, workspace: Optional[torch.Tensor] = None, out: Optional[VerifyOut] = None,
+                         cache: Optional[torch.Tensor] = None, stream=None):
+    """spec_verify + saguaro_cache_build in one pass; draft [B][K+1][V].  Returns (VerifyOut,
+    cache [B][budget], fan-out list)."""
+    B, Kd, V = draft.shape
+    if Kd != K + 1:
+        raise ValueError("draft must hold K + 1 rows")
+    dev = draft.device
+    if out is None:
+        out = VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                        torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                        tokens)
+    if workspace is None:
+        workspace = new_workspace(B, K, V, dev)
+    if cache is None:
+        cache = torch.empty((B, max(budget, 1)), dtype=torch.int32, device=dev)
+    fan = (ctypes.c_int32 * (K + 1))()
+    rc = load().cdll.saguaro_verify_cache(_ptr(draft), _ptr(target), dtype_code(draft), B, K, V, _ptr(params), F,
+                                          ctypes.c_float(C), _ptr(tokens), seed, round_, flags, budget, a, r,
+                                          ctypes.cast(fan, _P), _ptr(out.k), _ptr(out.tstar), _ptr(out.resid_mass),
+                                          _ptr(out.status), _ptr(cache), _ptr(workspace), workspace.numel(),
+                                          _stream(stream))
+    _check("saguaro_verify_cache", rc)
+    out.tokens = tokens
+    return out, cache[:, :budget], list(fan)
 
 
 def saguaro_cache_lookup(mode: int, cache: torch.Tensor, fanout_or_shape, K: int, B: int, k: torch.Tensor,

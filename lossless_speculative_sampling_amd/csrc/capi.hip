@@ -122,6 +122,52 @@ int saguaro_cache_build(const void* draft_logits, int dtype, int B, int K, int V
     return launch_status();
 }
 
+int saguaro_verify_cache(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
+                         const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed, uint64_t round,
+                         uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host, int32_t* out_k,
+                         int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status, int32_t* out_cache,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!draft_logits || !target_logits || !params || !draft_tokens || !out_k || !out_tstar || !out_cache)
+        return SPEC_EINVAL;
+    if (B < 1 || K < 1 || V < 1) return SPEC_EINVAL;
+    if (F < 0 || F > SPEC_MAX_F || !(C >= 0.0f && C <= 1.0f)) return SPEC_EINVAL;
+    if ((flags & ~(uint32_t)SPEC_SAMPLE_DRAFT) != 0) return SPEC_EINVAL;
+    if (!valid_dtype(dtype)) return SPEC_EDTYPE;
+    CacheArgs c{};
+    const int frc = fanout_host(K, budget, a, r, c.fanout.f);
+    if (frc != SPEC_OK) return frc;
+    c.fanout.off[0] = 0;
+    for (int k = 0; k <= K; ++k) {
+        if (c.fanout.f[k] > SPEC_MAX_FANOUT) return SPEC_EINVAL;
+        c.fanout.off[k + 1] = c.fanout.off[k] + c.fanout.f[k];
+    }
+    const size_t need = spec_workspace_bytes(B, K, V);
+    if (!workspace || workspace_bytes < need) return SPEC_EWORKSPACE;
+    if (out_fanout_host) std::memcpy(out_fanout_host, c.fanout.f, sizeof(int32_t) * (K + 1));
+    c.draft = draft_logits;
+    c.dtype = dtype;
+    c.B = B;
+    c.K = K;
+    c.V = V;
+    c.tokens = draft_tokens;
+    c.budget = budget;
+    c.out_cache = out_cache;
+    VerifyArgs v{draft_logits, target_logits, K + 1, dtype, B, K, V, params, F, C, draft_tokens, seed,
+                 round, flags, out_k, out_tstar, out_resid_mass, out_status, static_cast<UnitRec*>(workspace)};
+    if (fast::fast_cache_applies(v, c)) {
+        const size_t gen = align_up((size_t)B * (K + 1) * sizeof(UnitRec), 256);
+        return fast::fast_verify_cache(v, c, static_cast<char*>(workspace) + gen, workspace_bytes - gen, stream);
+    }
+    // otherwise the two calls one after the other (the drafted tokens are final after the first)
+    const int vrc = spec_verify(draft_logits, K + 1, target_logits, dtype, B, K, V, params, F, C, draft_tokens, seed,
+                                round, flags, out_k, out_tstar, out_resid_mass, out_status, workspace, workspace_bytes,
+                                stream);
+    if (vrc != SPEC_OK) return vrc;
+    if (budget == 0) return SPEC_OK;
+    hipLaunchKernelGGL(cache_build_kernel, dim3((unsigned)(B * (K + 1))), dim3(kRowThreadsHost), 0, stream, c);
+    return launch_status();
+}
+
 int saguaro_cache_lookup(int mode, const int32_t* cache, const int32_t* fanout_or_shape, int K, int B,
                          const int32_t* k, const int32_t* tstar, int32_t* out_slot, uint8_t* out_hit,
                          int32_t* out_batch, hipStream_t stream) {

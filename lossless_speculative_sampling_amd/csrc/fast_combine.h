@@ -1,0 +1,601 @@
+// Settling one (request, position) unit from its slices' summaries: the exact processed
+// distributions of the target and draft rows (temperature, top-k, softmax, nucleus; DeepMind
+// speculative-sampling page, section 6), the Saguaro downweighted set of the draft row (SSD
+// reading notes, section 4.4), and the processed probabilities of the draft token that the
+// acceptance test compares.  Run by the last slice of a unit to finish counting.
+#pragma once
+
+#include "fast_common.h"
+
+namespace sv {
+namespace fast {
+
+struct Cut {       // a cut in token order: keep key > key, and part of the elements at key
+    uint32_t key;
+    int take;         // histogram cut: elements kept at `key` (the first `take` in token order)
+    int explicit_id;  // >= 0: explicit cut, the id of the last kept element at `key`
+    int owner;        // histogram cut: slice holding the last kept element at `key`
+    int owner_take;   // elements at `key` that slice keeps
+    int count_above;  // elements with a larger key
+};
+
+struct RowView {   // the combined view of one row, identical in every slice of the unit
+    int bad, overflow, greedy, argmax;
+    float m;
+    double invT;               // 1 / temperature
+    double sc[kMaxSlices];     // per-slice rescale exp((m_t - m)/T)
+    int n_top[kMaxSlices];     // per-slice candidate list lengths
+    double seg_mass[kSegs];
+    uint32_t seg_count[kSegs];
+    uint32_t n_finite;
+    int has_special;
+    int want;                  // candidates each slice lists
+    int nm;                    // merged candidates (okey / oid)
+    double S_all, S_kept, S;
+    int has_k, has_p, small_k; // top-k / nucleus active; top-k settled by the merged list
+    Cut ck, cp;
+    int n_kept;                // elements kept by top-k (or all finite)
+    int n_nuc;                 // elements in the nucleus
+    int nset;                  // downweighted set size (0: off)
+    uint32_t kF;
+    int idF;
+    double C, Z;
+    int degenerate;
+    // draft token s: its value and its rank among the elements with its key (token order)
+    uint32_t s_bits;
+    int rank_s;
+    // a histogram cut in progress (0 none, 1 top-k count cut, 2 nucleus mass cut)
+    int pend;
+    int pend_seg;
+    int pend_cnt_above;
+    double pend_need;
+    double pend_above;
+    double pend_mass_above;
+};
+
+// LDS of the unit settle step (the last slice of a unit), laid over the histograms.
+struct UnitSmem {
+    RowView rv[2];
+    uint32_t key[2][kMergeCap];   // every slice's candidate list, slice-major; specials staging
+    int32_t id[2][kMergeCap];
+    uint32_t okey[2][kTop];       // merged candidates in token order
+    int32_t oid[2][kTop];
+    union {
+        struct {                  // every slice's segment arrays, as loaded
+            double mass[2][kMaxSlices][kSegs];
+            uint32_t count[2][kMaxSlices][kSegs];
+        } seg;
+        struct {
+            uint16_t fine_ps[2][kMaxSlices][kGroup];  // per-slice counts of a cut's group
+            uint32_t spk[kMergeCap];                  // one segment's specials, merged
+            int32_t spi[kMergeCap];
+        };
+    };
+    int sp_n;
+};
+
+// ------------------------------------------------------------------------------------------
+// Combining the slices' summaries (every slice of the unit derives the same view).  One round
+// trip to L2 brings every slice header, segment array and candidate list of both rows; a
+// second one, only when a cut falls inside a group of bins, brings that group's counts.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ void init_row(RowView& rv, const VerifyArgs& a, const spec_params& prm) {
+    rv.invT = inv_temperature(prm.temperature);
+    rv.greedy = prm.temperature == 0.0f ? 1 : 0;
+    rv.argmax = -1;
+    rv.has_k = (prm.top_k > 0 && prm.top_k < a.V) ? 1 : 0;
+    rv.has_p = ((double)prm.top_p < 1.0) ? 1 : 0;
+    rv.small_k = rv.has_k && prm.top_k <= kTop;
+    rv.ck = Cut{0u, 0, -1, 0, 0, 0};
+    rv.cp = Cut{0u, 0, -1, 0, 0, 0};
+    rv.nset = 0;
+    rv.kF = 0xFFFFFFFFu;
+    rv.idF = -1;
+    rv.C = 1.0;
+    rv.Z = 1.0;
+    rv.degenerate = 0;
+    rv.pend = 0;
+}
+
+// Round trip 1 and what follows from it alone: row maxima, normalisers, flags, merged segment
+// weights and merged candidate lists of both rows.
+__device__ __forceinline__ void combine_load(const FastArgs& f, UnitSmem& us, int unit, int j, int rows, const spec_params& prm) {
+    const VerifyArgs& a = f.a;
+    const double T = (double)prm.temperature;
+    const int nS = f.nS;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    int want[2];
+    want[0] = list_len(a, prm, false);
+    want[1] = rows > 1 ? draft_list_len(f, prm, j) : 0;
+    // -- issue every load --
+    // headers: wave r, one lane per slice (two 16-byte words and S)
+    u32x4 h0 = {0, 0, 0, 0}, h1 = {0, 0, 0, 0};
+    double St = 0.0;
+    if (wave < rows && lane < nS) {
+        const RowPart* P = part_of(f, unit, lane, wave);
+        h0 = ldnt(reinterpret_cast<const u32x4*>(P));
+        h1 = ldnt(reinterpret_cast<const u32x4*>(P) + 1);
+        St = ldnt(&P->S);
+    }
+    // segment arrays, as loaded: 64 lanes per (row, slice), one word each
+    constexpr int kPairs = 2 * kMaxSlices;                       // (row, slice)
+    constexpr int kSegLoads = kPairs * kWave / kThreads;         // 4
+    double ms[kSegLoads];
+    uint32_t cs[kSegLoads];
+#pragma unroll
+    for (int it = 0; it < kSegLoads; ++it) {
+        const int i = threadIdx.x + it * kThreads;
+        const int r = i >> 10, t = (i >> 6) & (kMaxSlices - 1), sg = i & (kWave - 1);
+        ms[it] = 0.0;
+        cs[it] = 0u;
+        if (r < rows && t < nS && sg < kSegs) {
+            const RowPart* P = part_of(f, unit, t, r);
+            ms[it] = ldnt(&P->seg_mass[sg]);
+            cs[it] = ldnt(&P->seg_count[sg]);
+        }
+    }
+    // candidate lists: 64 slots per (row, slice); entries past a slice's n_top are ignored
+    uint32_t ck_[kSegLoads];
+    int32_t ci_[kSegLoads];
+#pragma unroll
+    for (int it = 0; it < kSegLoads; ++it) {
+        const int i = threadIdx.x + it * kThreads;
+        const int r = i >> 10, t = (i >> 6) & (kMaxSlices - 1), x = i & (kWave - 1);
+        ck_[it] = 0u;
+        ci_[it] = 0;
+        if (r < rows && t < nS && x < want[r]) {
+            const RowPart* P = part_of(f, unit, t, r);
+            ck_[it] = ldnt(&P->top_key[x]);
+            ci_[it] = ldnt(&P->top_id[x]);
+        }
+    }
+    // -- row headers (wave r) --
+    if (wave < rows) {
+        RowView& rv = us.rv[wave];
+        const float mt = lane < nS ? __uint_as_float(h0[0]) : -__builtin_inff();
+        const uint32_t fl = h0[1], nf = h0[2], nsp = h0[3], ntop = h1[0], cnt = h1[1];
+        const float m = wave_max(mt);
+        const uint32_t flo = wave_or(fl);
+        const uint32_t nfin = wave_sum(nf);
+        const int rank = (int)wave_sum(cnt);
+        const bool has_sp = __ballot(nsp > 0u) != 0;
+        const double sc = (lane < nS && T > 0.0 && mt > -__builtin_inff()) ? mass_of(mt, m, inv_temperature(prm.temperature)) : 0.0;
+        const double S = wave_sum(sc * St);
+        const uint32_t sbits = wave_bcast(h1[2], 0);
+        if (lane < kMaxSlices) {
+            rv.sc[lane] = sc;
+            rv.n_top[lane] = lane < nS ? (int)ntop : 0;
+        }
+        if (lane == 0) {
+            init_row(rv, a, prm);
+            rv.m = m;
+            rv.bad = ((flo & 1u) || nfin == 0) ? 1 : 0;
+            rv.overflow = (flo & 2u) ? 1 : 0;
+            rv.n_finite = nfin;
+            rv.has_special = has_sp ? 1 : 0;
+            rv.S_all = S;
+            rv.want = want[wave];
+            rv.s_bits = sbits;
+            rv.rank_s = rank;
+        }
+    }
+    // -- segment arrays and candidates to LDS --
+#pragma unroll
+    for (int it = 0; it < kSegLoads; ++it) {
+        const int i = threadIdx.x + it * kThreads;
+        const int r = i >> 10, t = (i >> 6) & (kMaxSlices - 1), x = i & (kWave - 1);
+        if (r < rows && t < nS) {
+            if (x < kSegs) {
+                us.seg.mass[r][t][x] = ms[it];
+                us.seg.count[r][t][x] = cs[it];
+            }
+            if (x < want[r]) {
+                us.key[r][t * kTop + x] = ck_[it];
+                us.id[r][t * kTop + x] = ci_[it];
+            }
+        }
+    }
+    __syncthreads();
+    // -- merged segment weights (rescaled to the row maximum), slices in order --
+    {
+        const int r = threadIdx.x >> 6, sg = threadIdx.x & (kWave - 1);
+        if (r < rows && sg < kSegs) {
+            const RowView& rv = us.rv[r];
+            double w = 0.0;
+            uint32_t c = 0u;
+            for (int t = 0; t < nS; ++t) {
+                w += rv.sc[t] * us.seg.mass[r][t][sg];
+                c += us.seg.count[r][t][sg];
+            }
+            us.rv[r].seg_mass[sg] = w;
+            us.rv[r].seg_count[sg] = c;
+        }
+    }
+    // -- merged candidate lists: rank of every entry by binary search in the other lists --
+    for (int r = 0; r < rows; ++r) {
+        const int per = want[r];
+        if (per == 0) continue;
+        const RowView& rv = us.rv[r];
+        for (int i = threadIdx.x; i < nS * kTop; i += blockDim.x) {
+            const int t = i >> 6, x = i & (kTop - 1);
+            if (x >= rv.n_top[t]) continue;
+            const uint32_t k = us.key[r][i];
+            const int id = us.id[r][i];
+            int rank = x;
+            for (int t2 = 0; t2 < nS; ++t2) {
+                if (t2 == t) continue;
+                int lo = 0, hi = rv.n_top[t2];
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    const uint32_t k2 = us.key[r][t2 * kTop + mid];
+                    const bool before = k2 > k || (k2 == k && us.id[r][t2 * kTop + mid] < id);
+                    if (before) lo = mid + 1;
+                    else hi = mid;
+                }
+                rank += lo;
+            }
+            if (rank < per) {
+                us.okey[r][rank] = k;
+                us.oid[r][rank] = id;
+            }
+        }
+        if (threadIdx.x == 0) {
+            int tot = 0;
+            for (int t = 0; t < nS; ++t) tot += rv.n_top[t];
+            us.rv[r].nm = min(tot, per);
+        }
+    }
+    __syncthreads();
+}
+
+// Wave-level: the crossing segment of a cut that keeps `need` weight (counts or masses) from
+// the top of row rv, restricted to the `lim` cut when given; records it as rv's pending cut.
+template <bool MASS>
+__device__ __forceinline__ void seg_walk(RowView& rv, double need, bool has_lim, const Cut& lim) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int lim_seg = has_lim ? seg_of_key(lim.key) : kSegs;
+    const bool live = lane < kSegs && lane < lim_seg;
+    const uint32_t cnt = lane < kSegs ? rv.seg_count[lane] : 0u;
+    const double ms = live ? rv.seg_mass[lane] : 0.0;
+    const double w = live ? (MASS ? ms : (double)cnt) : 0.0;
+    double wex, mex;
+    int cex;
+    const double win = wave_scan(w, &wex);
+    wave_scan(ms, &mex);
+    wave_scan(live ? (int)cnt : 0, &cex);
+    // the walk stops at the limit's segment, which is resolved by the group walk
+    const bool cross = lane < kSegs && (lane >= lim_seg || (cnt > 0u && win >= need));
+    int pick = first_lane(__ballot(cross));
+    if (pick < 0) {  // rounding left the target beyond the last segment: its last non-empty one
+        pick = last_lane(__ballot(lane < kSegs && cnt > 0u));
+        if (pick < 0) pick = kSegs - 1;
+    }
+    const double wa = wave_bcast(wex, pick);
+    const double ma = wave_bcast(mex, pick);
+    const int ca = wave_bcast(cex, pick);
+    if (lane == 0) {
+        rv.pend = MASS ? 2 : 1;
+        rv.pend_seg = pick;
+        rv.pend_need = need;
+        rv.pend_above = wa;
+        rv.pend_mass_above = ma;
+        rv.pend_cnt_above = ca;
+    }
+}
+
+// Wave-level: settles rv's pending cut inside its group from the per-slice counts in
+// us.fine_ps[r]; writes *out and returns (weight kept, mass kept, elements kept) through
+// the row view (S_kept / n_kept for a count cut, S / n_nuc for a mass cut).
+template <bool MASS>
+__device__ __forceinline__ void group_walk(const FastArgs& f, UnitSmem& us, int r, bool has_lim, const Cut& lim, Cut* out) {
+    RowView& rv = us.rv[r];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = group_of_seg(rv.pend_seg);
+    const int bb = kGroup - 1 - lane;  // lane order = descending key
+    const int bin = g * kGroup + bb;
+    const uint32_t key = bin_key(bin);
+    int n = 0;
+    for (int t = 0; t < f.nS; ++t) n += us.fine_ps[r][t][bb];
+    const bool at_lim = has_lim && key == lim.key;
+    if (has_lim && key < lim.key) n = 0;
+    if (at_lim) n = min(n, lim.take);
+    const double e = n > 0 ? mass_of(key16_value(key), rv.m, rv.invT) : 0.0;
+    const double w = MASS ? (double)n * e : (double)n;
+    double wex, mex;
+    int nex;
+    const double win = wave_scan(w, &wex);
+    wave_scan((double)n * e, &mex);
+    wave_scan(n, &nex);
+    const double need = rv.pend_need, above0 = rv.pend_above;
+    const uint64_t hc = __ballot(n > 0 && (above0 + win >= need || at_lim));
+    const bool done = hc != 0;
+    // not done: rounding left the target just beyond the group; cut at its lowest bin
+    const int sel = done ? first_lane(hc) : last_lane(__ballot(n > 0));
+    Cut c{0u, 0, -1, 0, 0, rv.pend_cnt_above};
+    double kept_w = above0, kept_m = rv.pend_mass_above;
+    int kept_n = rv.pend_cnt_above;
+    if (sel >= 0) {
+        const double above = above0 + wave_bcast(wex, sel);
+        const double e_s = wave_bcast(e, sel);
+        const int n_s = wave_bcast(n, sel);
+        const int nex_s = wave_bcast(nex, sel);
+        int take = n_s;
+        if (done && above + (MASS ? (double)n_s * e_s : (double)n_s) >= need) {
+            if (MASS) {
+                if (e_s > 0.0) {
+                    const double q = ceil((need - above) / e_s);
+                    take = q < 1.0 ? 1 : (q > (double)n_s ? n_s : (int)q);
+                }
+            } else {
+                take = (int)(need - above);
+                take = take < 1 ? 1 : (take > n_s ? n_s : take);
+            }
+        }
+        c.key = bin_key(g * kGroup + (kGroup - 1 - sel));
+        c.take = take;
+        c.count_above = rv.pend_cnt_above + nex_s;
+        kept_w = above + (MASS ? (double)take * e_s : (double)take);
+        kept_m = rv.pend_mass_above + wave_bcast(mex, sel) + (double)take * e_s;
+        kept_n = c.count_above + take;
+        // the slice holding the last kept element at the cut key
+        const int bsel = kGroup - 1 - sel;
+        const int nt = lane < f.nS ? (int)us.fine_ps[r][lane][bsel] : 0;
+        int tex;
+        const int tin = wave_scan(nt, &tex);
+        const int own = first_lane(__ballot(lane < f.nS && tin >= take));
+        if (own < 0) {
+            c.owner = f.nS - 1;
+            c.owner_take = 0;
+        } else {
+            c.owner = own;
+            c.owner_take = take - wave_bcast(tex, own);
+        }
+    }
+    if (lane == 0) {
+        *out = c;
+        if (MASS) {
+            rv.S = kept_w;
+            rv.n_nuc = kept_n;
+        } else {
+            rv.S_kept = kept_m;
+            rv.n_kept = kept_n;
+        }
+        rv.pend = 0;
+    }
+}
+
+// Specials of segment sg of row r from every slice, sorted (key desc, id asc) into
+// us.spk / spi; returns their number.  (Rare: finite values outside the exact bins.)
+__device__ __forceinline__ int merge_specials(const FastArgs& f, UnitSmem& us, int unit, int r, int sg) {
+    if (threadIdx.x == 0) us.sp_n = 0;
+    __syncthreads();
+    constexpr int kCap = kMergeCap;
+    for (int i = threadIdx.x; i < f.nS * kSpecial; i += blockDim.x) {
+        const RowPart* P = part_of(f, unit, i / kSpecial, r);
+        const int x = i % kSpecial;
+        if (x >= min((int)ldnt(&P->n_special), kSpecial)) continue;
+        const uint32_t k = ldnt(&P->sp_key[x]);
+        if (special_seg(k) != sg) continue;
+        const int slot = atomicAdd(&us.sp_n, 1);
+        if (slot < kCap) {
+            us.key[0][slot] = k;  // staging (the candidate lists are no longer needed)
+            us.id[0][slot] = ldnt(&P->sp_id[x]);
+        }
+    }
+    __syncthreads();
+    const int n = min(us.sp_n, kCap);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const uint32_t k = us.key[0][i];
+        const int id = us.id[0][i];
+        int rank = 0;
+        for (int x = 0; x < n; ++x) {
+            const uint32_t k2 = us.key[0][x];
+            rank += (k2 > k || (k2 == k && us.id[0][x] < id)) ? 1 : 0;
+        }
+        us.spk[rank] = k;
+        us.spi[rank] = id;
+    }
+    __syncthreads();
+    return n;
+}
+
+// Block-level (rare): settles rv's pending cut when it falls among the specials of a segment.
+template <bool MASS>
+__device__ __forceinline__ void special_walk(const FastArgs& f, UnitSmem& us, int unit, int r, bool has_lim, const Cut& lim,
+                                             Cut* out) {
+    RowView& rv = us.rv[r];
+    const int n = merge_specials(f, us, unit, r, rv.pend_seg);
+    if (threadIdx.x == 0) {
+        double above = rv.pend_above, mass = rv.pend_mass_above;
+        const double need = rv.pend_need;
+        Cut c{0u, 0, -1, 0, 0, rv.pend_cnt_above};
+        int i = 0;
+        for (; i < n; ++i) {
+            const uint32_t key = us.spk[i];
+            if (has_lim && (key < lim.key || (key == lim.key && lim.explicit_id >= 0 && us.spi[i] > lim.explicit_id))) break;
+            const double e = mass_of(key16_value(key), rv.m, rv.invT);
+            above += MASS ? e : 1.0;
+            mass += e;
+            if (above >= need) {
+                c.key = key;
+                c.explicit_id = us.spi[i];
+                ++i;
+                break;
+            }
+        }
+        if (c.explicit_id < 0 && i > 0) {  // the limit (or rounding) ends the walk
+            c.key = us.spk[i - 1];
+            c.explicit_id = us.spi[i - 1];
+        }
+        *out = c;
+        if (MASS) {
+            rv.S = above;
+            rv.n_nuc = rv.pend_cnt_above + i;
+        } else {
+            rv.S_kept = mass;
+            rv.n_kept = rv.pend_cnt_above + i;
+        }
+        rv.pend = 0;
+    }
+    __syncthreads();
+}
+
+// Wave-level step of row r after its top-k is settled: the nucleus, settled at once or left
+// as a pending cut.
+__device__ __forceinline__ void nucleus_step(UnitSmem& us, int r, const spec_params& prm) {
+    RowView& rv = us.rv[r];
+    const int lane = threadIdx.x & (kWave - 1);
+    if (!rv.has_p) {
+        if (lane == 0) {
+            rv.S = rv.S_kept;
+            rv.n_nuc = rv.n_kept;
+        }
+    } else if (rv.small_k) {  // inside the merged list
+        const int kk = prm.top_k;
+        const double need = (double)prm.top_p * rv.S_kept;
+        const double e = lane < kk ? mass_of(key16_value(us.okey[r][lane]), rv.m, rv.invT) : 0.0;
+        double ex;
+        const double in = wave_scan(e, &ex);
+        int i = first_lane(__ballot(lane < kk && in >= need));
+        if (i < 0) i = kk - 1;
+        const double cum = wave_bcast(in, i);
+        if (lane == 0) {
+            rv.cp = Cut{us.okey[r][i], 0, us.oid[r][i], 0, 0, 0};
+            rv.S = cum;
+            rv.n_nuc = i + 1;
+        }
+    } else {
+        const bool use_lim = rv.has_k && rv.ck.key != 0u;
+        seg_walk<true>(rv, (double)prm.top_p * rv.S_kept, use_lim, rv.ck);
+    }
+}
+
+// Both rows' processed distributions: maxima, normalisers, top-k and nucleus cuts, and (dw)
+// the draft row's downweighted set.  All threads.
+__device__ __forceinline__ void combine(const FastArgs& f, UnitSmem& us, int unit, int j, int rows, const spec_params& prm,
+                                        bool dw) {
+    const VerifyArgs& a = f.a;
+    combine_load(f, us, unit, j, rows, prm);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    // top-k, then the nucleus where it needs no group counts (wave r for row r)
+    if (wave < rows) {
+        RowView& rv = us.rv[wave];
+        const int r = wave;
+        if (rv.bad || rv.overflow) {
+            // nothing to settle
+        } else if (rv.greedy) {
+            if (lane == 0) rv.argmax = rv.nm > 0 ? us.oid[r][0] : -1;
+        } else if (rv.has_k && (uint32_t)prm.top_k > rv.n_finite) {  // -inf tokens would be kept
+            if (lane == 0) rv.overflow = 1;
+        } else {
+            if (!rv.has_k) {
+                if (lane == 0) {
+                    rv.S_kept = rv.S_all;
+                    rv.n_kept = (int)rv.n_finite;
+                }
+            } else if (rv.small_k) {
+                const int kk = prm.top_k;
+                const double e = lane < kk ? mass_of(key16_value(us.okey[r][lane]), rv.m, rv.invT) : 0.0;
+                const double s = wave_sum(e);
+                if (lane == 0) {
+                    rv.S_kept = s;
+                    rv.n_kept = kk;
+                    rv.ck = Cut{us.okey[r][kk - 1], 0, us.oid[r][kk - 1], 0, 0, 0};
+                }
+            } else {
+                seg_walk<false>(rv, (double)prm.top_k, false, rv.ck);
+            }
+            if (rv.pend == 0) nucleus_step(us, r, prm);
+        }
+    }
+    __syncthreads();
+    // pending histogram cuts: load their groups' per-slice counts, settle, repeat (a top-k cut
+    // can leave a nucleus cut behind it)
+    for (int round = 0; round < 2; ++round) {
+        const bool p0 = us.rv[0].pend != 0;
+        const bool p1 = rows > 1 && us.rv[1].pend != 0;
+        if (!p0 && !p1) break;
+        const int g0 = p0 ? group_of_seg(us.rv[0].pend_seg) : -1;
+        const int g1 = p1 ? group_of_seg(us.rv[1].pend_seg) : -1;
+        for (int i = threadIdx.x; i < 2 * f.nS * kGroup; i += blockDim.x) {
+            const int r = i / (f.nS * kGroup), t = (i / kGroup) % f.nS, bb = i % kGroup;
+            const int g = r == 0 ? g0 : g1;
+            if (g >= 0) us.fine_ps[r][t][bb] = (uint16_t)ldnt_u16(&part_of(f, unit, t, r)->fine[g * kGroup + bb]);
+        }
+        __syncthreads();
+        for (int r = 0; r < rows; ++r) {
+            RowView& rv = us.rv[r];
+            if (rv.pend == 0) continue;
+            const bool count_cut = rv.pend == 1;
+            const bool use_lim = !count_cut && rv.has_k && rv.ck.key != 0u;
+            const Cut lim = rv.ck;
+            if (group_of_seg(rv.pend_seg) >= 0) {
+                if (wave == r) {
+                    if (count_cut) group_walk<false>(f, us, r, false, lim, &rv.ck);
+                    else group_walk<true>(f, us, r, use_lim, lim, &rv.cp);
+                }
+            } else {
+                if (count_cut) special_walk<false>(f, us, unit, r, false, lim, &rv.ck);
+                else special_walk<true>(f, us, unit, r, use_lim, lim, &rv.cp);
+            }
+            __syncthreads();
+            if (count_cut && wave == r) nucleus_step(us, r, prm);
+        }
+        __syncthreads();
+    }
+    // downweighted set: the first F elements of the processed order that carry mass
+    if (dw && rows > 1 && wave == 1) {
+        RowView& rv = us.rv[1];
+        const bool want_set = a.F > 0 && a.C < 1.0f && !rv.greedy && !rv.bad && !rv.overflow;
+        if (want_set) {
+            const int n0 = min(min(a.F, rv.n_nuc), rv.nm);
+            const double e = lane < n0 ? mass_of(key16_value(us.okey[1][lane]), rv.m, rv.invT) : 0.0;
+            const int n = last_lane(__ballot(lane < n0 && e > 0.0)) + 1;
+            const double ps = wave_sum(lane < n ? e / rv.S : 0.0);
+            if (lane == 0) {
+                rv.nset = n;
+                if (n > 0) {
+                    rv.kF = us.okey[1][n - 1];
+                    rv.idF = us.oid[1][n - 1];
+                    const double Cd = (double)a.C;
+                    const double Z = 1.0 - (1.0 - Cd) * ps;
+                    if (Z > 0.0) {
+                        rv.C = Cd;
+                        rv.Z = Z;
+                    } else {
+                        rv.degenerate = 1;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ bool cut_keeps_s(const RowView& rv, const Cut& c, uint32_t key_s, int s) {
+    if (key_s > c.key) return true;
+    if (key_s < c.key) return false;
+    if (c.explicit_id >= 0) return s <= c.explicit_id;
+    return rv.rank_s < c.take;
+}
+
+// Processed probability of token s in row r (after the combine).
+__device__ __forceinline__ double prob_of_s(const UnitSmem& us, int r, int s, bool draft) {
+    const RowView& rv = us.rv[r];
+    const uint32_t h = rv.s_bits;
+    if ((h & 0x7FFFu) >= 0x7F80u) return 0.0;
+    const uint32_t key = key16(h);
+    if (rv.has_k && !cut_keeps_s(rv, rv.ck, key, s)) return 0.0;
+    if (rv.has_p && !cut_keeps_s(rv, rv.cp, key, s)) return 0.0;
+    const double e = mass_of(__uint_as_float(h << 16), rv.m, rv.invT);
+    const double p = e / rv.S;
+    if (!draft) return p;
+    const double fct = (rv.nset > 0 && e > 0.0 && in_cut_id(rv.kF, rv.idF, key, s)) ? rv.C : 1.0;
+    return (p * fct) / rv.Z;
+}
+
+
+}  // namespace fast
+}  // namespace sv

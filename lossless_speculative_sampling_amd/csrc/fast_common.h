@@ -105,7 +105,8 @@ static_assert(offsetof(RowPart, S) == 32, "header layout: 2 x 16 bytes, then S")
 
 struct RowFinal {  // enough to evaluate any element's processed probability
     float m;
-    float T;
+    float pad;
+    double invT;   // 1 / temperature
     double S;      // normaliser of the processed distribution
     double C;      // factor on the downweighted set (1 when off)
     double Z;      // normaliser after the downweight (1 when off)
@@ -119,18 +120,35 @@ struct RowFinal {  // enough to evaluate any element's processed probability
     int32_t has_special;  // slices hold finite values outside the bins (finalizer recomputes them)
 };
 
-struct UnitFast {
+// One truncation cut of one row as the resolve kernel needs it: elements with a larger key
+// are kept; at the cut key the first elements in token order up to the one at explicit_id
+// (explicit cut) or the first owner_take of slice `owner` and all of earlier slices
+// (histogram cut).
+struct UnitCut {
+    uint32_t key;        // 0: the cut keeps every finite element
+    int32_t explicit_id; // >= 0: explicit cut
+    int32_t owner;       // slice holding the last kept element at `key`
+    int32_t owner_take;  // elements at `key` that slice keeps (histogram cut)
+};
+
+struct UnitFast {       // written by the last slice of the unit in the count kernel
     int32_t accept;
     uint32_t status;
-    int32_t fallback;   // processed by the general algorithm: tcand / W are final
-    int32_t tcand;
-    float W;
+    int32_t fallback;    // the counts cannot settle this unit: its request takes the general path
     int32_t pad;
     RowFinal rq, rp;
+    UnitCut cut[2][2];   // [row: target, draft][top-k, nucleus]
+};
+
+struct ReqFast {        // written by the last unit of the request in the count kernel
+    int32_t mode;        // 0: outputs written, 1: residual of unit k, 2: general path
+    int32_t k;
+    uint32_t status;
+    int32_t pad;
 };
 
 struct Layout {
-    size_t req, parts, units, idcut, chunks, total;
+    size_t unit_ctr, req_ctr, res_ctr, parts, units, reqs, idcut, chunks, gen, cache_gen, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -138,11 +156,16 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 
 __host__ __device__ inline Layout layout(int B, int units, int nS) {
     Layout L;
     size_t o = 0;
-    L.req = o;    o += align256((size_t)B * 128);               // request arrival counters
-    L.parts = o;  o += align256((size_t)units * nS * 2 * sizeof(RowPart));
-    L.units = o;  o += align256((size_t)units * sizeof(UnitFast));
-    L.idcut = o;  o += align256((size_t)units * 4 * sizeof(int32_t));
-    L.chunks = o; o += align256((size_t)units * nS * kChunks * sizeof(double));
+    L.unit_ctr = o; o += align256((size_t)units * 128);   // unit arrival counters (count kernel)
+    L.req_ctr = o;  o += align256((size_t)B * 128);       // request arrival counters (count kernel)
+    L.res_ctr = o;  o += align256((size_t)B * 128);       // request arrival counters (resolve kernel)
+    L.parts = o;    o += align256((size_t)units * nS * 2 * sizeof(RowPart));
+    L.units = o;    o += align256((size_t)units * sizeof(UnitFast));
+    L.reqs = o;     o += align256((size_t)B * sizeof(ReqFast));
+    L.idcut = o;    o += align256((size_t)B * 4 * sizeof(int32_t));
+    L.chunks = o;   o += align256((size_t)B * nS * kChunks * sizeof(double));
+    L.gen = o;      o += align256((size_t)units * sizeof(UnitRec));  // general-path unit results
+    L.cache_gen = o; o += align256((size_t)units * sizeof(int32_t)); // cache rows for the general selection
     L.total = o;
     return L;
 }
@@ -153,6 +176,12 @@ struct FastArgs {
     int units;
     char* ws;
     Layout L;
+    // the Saguaro outcome cache, built from the same pass over the draft rows (draft row K is
+    // read by the bonus position's unit)
+    int cache;
+    int budget;
+    int32_t* out_cache;
+    Fanout fan;
 };
 
 // ------------------------------------------------------------------------------------------
@@ -198,8 +227,15 @@ __device__ __forceinline__ RowPart* part_of(const FastArgs& f, int unit, int sli
     return reinterpret_cast<RowPart*>(f.ws + f.L.parts) + ((size_t)unit * f.nS + slice) * 2 + r;
 }
 
-// e of a finite value relative to the row's largest logit
-__device__ __forceinline__ double mass_of(float z, float m, double T) { return exp(((double)z - (double)m) / T); }
+// e of a finite value relative to the row's largest logit: exp((z - m) / T), with the
+// division taken as a product with invT = 1 / T (the same everywhere on this path).
+__device__ __forceinline__ double inv_temperature(float T) { return T > 0.0f ? 1.0 / (double)T : 0.0; }
+__device__ __forceinline__ double mass_of(float z, float m, double invT) { return exp(((double)z - (double)m) * invT); }
+
+// Keep test of a cut at (cut_key, cut_id): a larger key, or the cut key and an id no larger.
+__device__ __forceinline__ bool in_cut_id(uint32_t cut_key, int cut_id, uint32_t key, int col) {
+    return key > cut_key || (key == cut_key && col <= cut_id);
+}
 
 // Segment of any finite order key.
 __device__ __forceinline__ int seg_of_key(uint32_t k) {
@@ -217,6 +253,14 @@ __device__ __forceinline__ int list_len(const VerifyArgs& a, const spec_params& 
     int want = greedy ? 1 : 0;
     if (!greedy && prm.top_k > 0 && prm.top_k < a.V && prm.top_k <= kTop) want = max(want, prm.top_k);
     if (!greedy && draft && a.F > 0 && a.C < 1.0f) want = max(want, a.F);
+    return want;
+}
+
+// Candidates each slice lists for the draft row of position j: the downweighted set's and,
+// with the cache, F_j + 1 (F_K at the bonus position, which has no drafted token to skip).
+__device__ __forceinline__ int draft_list_len(const FastArgs& f, const spec_params& prm, int j) {
+    int want = j < f.a.K ? list_len(f.a, prm, true) : 0;
+    if (f.cache && f.fan.f[j] > 0 && prm.temperature >= 0.0f) want = max(want, f.fan.f[j] + (j < f.a.K ? 1 : 0));
     return want;
 }
 

@@ -1,19 +1,23 @@
 // Count kernel of the bf16 verification path: every slice of every (request, position) unit
 // loads its token columns of the target row (and the draft row), counts every distinct bf16
 // value in LDS and publishes a compact summary for the resolve kernel.
-#include "fast_common.h"
+#include "fast_combine.h"
 
 namespace sv {
 namespace fast {
 
 // ------------------------------------------------------------------------------------------
 // Count kernel: every slice of every unit loads its columns, counts them and publishes its
-// summaries (no waiting on other workgroups).
+// summaries; the last slice of a unit to finish settles the unit, and the last unit of a
+// request to be settled decides the request (no workgroup waits on another).
 // ------------------------------------------------------------------------------------------
 struct CountSmem {
     double segm[kSegs];
     uint32_t segc[2][kSegs];
-    uint32_t hraw[2][kHistRow];
+    union {
+        uint32_t hraw[2][kHistRow];   // counting
+        UnitSmem us;                  // settling the unit (the histograms are published by then)
+    };
     __device__ __forceinline__ uint32_t* hist(int r) { return &hraw[r][kHistLead]; }
     uint32_t sp_key[2][kSpecial];
     int32_t sp_id[2][kSpecial];
@@ -32,6 +36,8 @@ struct CountSmem {
     int need;
     int ties;      // elements of the slice at key tau
     uint32_t maxkey;
+    int last;
+    int rare[2];
 };
 
 // Per-segment element counts of both rows into sm.segc: a thread adds 8 bins, eight lanes a
@@ -236,6 +242,7 @@ __device__ __forceinline__ void publish_row(const FastArgs& f, CountSmem& sm, in
                                             const spec_params& prm) {
     RowPart* P = part_of(f, unit, slice, r);
     const double T = (double)prm.temperature;
+    const double invT = inv_temperature(prm.temperature);
     const int nsp = min((int)sm.n_sp[r], kSpecial);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -269,7 +276,7 @@ __device__ __forceinline__ void publish_row(const FastArgs& f, CountSmem& sm, in
         const int bin = g * kGroup + lane;
         const uint32_t c = sm.hist(r)[bin];
         double ms = 0.0;
-        if (c != 0 && T > 0.0) ms = (double)c * mass_of(key16_value(bin_key(bin)), m, T);
+        if (c != 0 && T > 0.0) ms = (double)c * mass_of(key16_value(bin_key(bin)), m, invT);
         ms = wave_sum(ms);
         if (lane == 0) sm.segm[seg_of_group(g)] = ms;
     }
@@ -280,7 +287,7 @@ __device__ __forceinline__ void publish_row(const FastArgs& f, CountSmem& sm, in
         if (lane < nsp) {
             const uint32_t k = sm.sp_key[r][lane];
             sg = special_seg(k);
-            if (T > 0.0) ms = mass_of(key16_value(k), m, T);
+            if (T > 0.0) ms = mass_of(key16_value(k), m, invT);
         }
         const int sps[4] = {kSegHugePos, kSegTinyPos, kSegTinyNeg, kSegHugeNeg};
 #pragma unroll
@@ -295,7 +302,7 @@ __device__ __forceinline__ void publish_row(const FastArgs& f, CountSmem& sm, in
         const uint32_t nfin = wave_sum(lane < kSegs ? sm.segc[r][lane] : 0u);
         if (lane == 0) {
             P->m = m;
-            P->flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u);
+            P->flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u) | (sm.rare[r] ? 4u : 0u);
             P->n_finite = nfin;
             P->n_special = (uint32_t)nsp;
             P->n_top = sm.n_top[r];
@@ -326,24 +333,28 @@ __device__ __forceinline__ void publish_row(const FastArgs& f, CountSmem& sm, in
 }
 
 // Counts this thread's columns of row r: every value goes to its bin or a padding word (one
-// LDS add each, no branch).
-__device__ __forceinline__ void count_row(CountSmem& sm, int r, const u32x4 (&v)[kLoads]) {
+// LDS add each, no branch).  Vectors past the row's end (zero fill) are skipped.
+__device__ __forceinline__ void count_row(CountSmem& sm, int r, int c0, int V, const u32x4 (&v)[kLoads]) {
     char* base = reinterpret_cast<char*>(&sm.hraw[r][0]);
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q)
+    for (int q = 0; q < kLoads; ++q) {
+        if (col_of(c0, q, 0) >= V) continue;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint32_t o = hist_offsets2(v[q][d]);
             atomicAdd(reinterpret_cast<uint32_t*>(base + (o & 0xFFFFu)), 1u);
             atomicAdd(reinterpret_cast<uint32_t*>(base + (o >> 16)), 1u);
         }
+    }
 }
 
 // Second pass over the values the packed count sent to the padding words: zeros, specials,
 // -inf, +inf, NaN (and the zero fill past the row's end).
 __device__ __forceinline__ void count_rare(CountSmem& sm, int r, int c0, int V, const u32x4 (&v)[kLoads]) {
     uint32_t bad = 0, ninf = 0;
+#pragma unroll
     for (int q = 0; q < kLoads; ++q)
+#pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int col = col_of(c0, q, e);
             const uint32_t w = v[q][e >> 1];
@@ -370,6 +381,158 @@ __device__ __forceinline__ void count_rare(CountSmem& sm, int r, int c0, int V, 
     if (ninf) atomicAdd(&sm.neginf[r], ninf);
 }
 
+// The last slice of a unit: combine, acceptance test, unit record.
+__device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, const Place& P, const spec_params& prm,
+                                            bool param_ok, bool two, int s_tok, bool tok_ok) {
+    const VerifyArgs& a = f.a;
+    const int unit = P.unit;
+    UnitSmem& us = sm.us;
+    uint32_t status = 0;
+    int accept = 0, fallback = 0;
+    if (!param_ok) {
+        status = kStBadParam;
+    } else {
+        const bool vd = P.j < a.K;  // the draft row is verified (not only listed for the cache)
+        combine(f, us, unit, P.j, two ? 2 : 1, prm, vd);
+        const bool bad = us.rv[0].bad || (vd && us.rv[1].bad);
+        fallback = (!bad && (us.rv[0].overflow || (vd && us.rv[1].overflow))) ? 1 : 0;
+        if (bad) {
+            status = kStBadLogit;
+        } else if (!fallback) {
+            if (vd && us.rv[1].degenerate) status |= kStDegenerate;
+            if (!tok_ok) {
+                status |= kStBadToken;
+            } else if (vd) {
+                if (us.rv[0].greedy) {
+                    accept = (s_tok == us.rv[0].argmax) ? 1 : 0;
+                } else {
+                    const double ps = prob_of_s(us, 1, s_tok, true);
+                    const double qs = prob_of_s(us, 0, s_tok, false);
+                    if (!(ps > 0.0)) status |= kStOutside;
+                    const double u = uniform_at(a.seed, a.round, (uint64_t)P.b, (uint64_t)P.j, 0);
+                    accept = (u * ps < qs) ? 1 : 0;
+                }
+            } else {
+                accept = 1;  // bonus position
+            }
+        }
+    }
+    // the outcome cache's depth-j list: the first F_j candidates of the draft row in token order,
+    // less the drafted token; rows the candidate lists cannot settle (NaN or +inf, too many
+    // specials, too few finite values) go to the general selection in the resolve kernel
+    if (f.cache && f.fan.f[P.j] > 0) {
+        const int Fj = f.fan.f[P.j];
+        const int want = Fj + (P.j < a.K ? 1 : 0);
+        const RowView& rv = us.rv[1];
+        const bool general = !param_ok || rv.bad || rv.overflow || rv.nm < min(want, a.V);
+        if (threadIdx.x == 0) reinterpret_cast<int32_t*>(f.ws + f.L.cache_gen)[unit] = general ? 1 : 0;
+        if (!general && threadIdx.x < kWave) {
+            const int lane = threadIdx.x;
+            const int excl = (P.j < a.K && tok_ok) ? s_tok : -1;
+            const int n = rv.nm;
+            const int id = lane < n ? us.oid[1][lane] : -1;
+            const uint64_t ex = __ballot(lane < n && id == excl);
+            const int xpos = first_lane(ex);  // -1: the drafted token is not listed
+            int32_t* out = f.out_cache + (size_t)P.b * f.budget + f.fan.off[P.j];
+            if (lane < n && lane != xpos) {
+                const int pos = (xpos >= 0 && lane > xpos) ? lane - 1 : lane;
+                if (pos < Fj) out[pos] = id;
+            }
+            const int got = min(Fj, n - (xpos >= 0 ? 1 : 0));
+            for (int x = got + lane; x < Fj; x += kWave) out[x] = -1;
+        }
+    }
+    if (threadIdx.x == 0) {
+        UnitFast* U = reinterpret_cast<UnitFast*>(f.ws + f.L.units) + unit;
+        U->accept = accept;
+        U->status = status;
+        U->fallback = fallback;
+        if (param_ok) {
+            for (int r = 0; r < (two ? 2 : 1); ++r) {
+                const RowView& rv = us.rv[r];
+                RowFinal rf;
+                rf.m = rv.m;
+                rf.invT = rv.invT;
+                rf.S = rv.S;
+                rf.C = rv.C;
+                rf.Z = rv.Z;
+                rf.kk = rv.has_k ? rv.ck.key : 0u;
+                rf.kp = rv.has_p ? rv.cp.key : 0u;
+                rf.kF = rv.kF;
+                rf.idF = rv.idF;
+                rf.nS = rv.nset;
+                rf.argmax = rv.argmax;
+                rf.greedy = rv.greedy;
+                rf.has_special = rv.has_special;
+                if (r == 0) U->rq = rf;
+                else U->rp = rf;
+                const Cut* cs[2] = {&rv.ck, &rv.cp};
+                const int on[2] = {rv.has_k, rv.has_p};
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    UnitCut uc;
+                    uc.key = on[c] ? cs[c]->key : 0u;
+                    uc.explicit_id = cs[c]->explicit_id;
+                    uc.owner = cs[c]->explicit_id >= 0 ? cs[c]->explicit_id / kSliceCols : cs[c]->owner;
+                    uc.owner_take = cs[c]->owner_take;
+                    U->cut[r][c] = uc;
+                }
+            }
+        }
+    }
+}
+
+// The last unit of a request: k, the status, and the outputs when no residual is needed.
+__device__ __forceinline__ void decide_request(const FastArgs& f, int b) {
+    const VerifyArgs& a = f.a;
+    const int K = a.K;
+    const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + (size_t)b * (K + 1);
+    const int lane = threadIdx.x & (kWave - 1);
+    if (threadIdx.x >= kWave) return;
+    uint32_t st = 0;
+    int acc = 1, fb = 0;
+    if (lane <= K) {
+        st = ldnt(&U[lane].status);
+        acc = ldnt(&U[lane].accept);
+        fb = ldnt(&U[lane].fallback);
+    }
+    const bool any_fb = __ballot(fb != 0) != 0;
+    const uint32_t any = wave_or(st);
+    const uint32_t deg = wave_or(lane < K ? (st & kStDegenerate) : 0u);
+    int k = first_lane(__ballot(lane < K && !acc));
+    if (k < 0) k = K;
+    const uint32_t outside = wave_or((lane < K && lane <= k) ? (st & kStOutside) : 0u);
+    int mode = 0, t = -1, kk = 0;
+    uint32_t status;
+    if (any_fb) {
+        mode = 2;
+        status = 0;
+    } else if (any & kStBadParam) {
+        status = kStBadParam;
+    } else if (any & kStBadLogit) {
+        status = kStBadLogit;
+    } else if (any & kStBadToken) {
+        status = deg | kStBadToken;
+    } else {
+        status = deg | outside;
+        kk = k;
+        if (ldnt(&U[k].rq.greedy)) t = ldnt(&U[k].rq.argmax);
+        else mode = 1;
+    }
+    if (lane == 0) {
+        ReqFast* R = reinterpret_cast<ReqFast*>(f.ws + f.L.reqs) + b;
+        R->mode = mode;
+        R->k = kk;
+        R->status = status;
+        if (mode == 0) {
+            a.out_k[b] = kk;
+            a.out_t[b] = t;
+            if (a.out_W) a.out_W[b] = 0.0f;
+            if (a.out_status) a.out_status[b] = status;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void fast_count_kernel(FastArgs f) {
     __shared__ CountSmem sm;
     const VerifyArgs& a = f.a;
@@ -377,59 +540,89 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     if (P.b >= a.B) return;
     const int j = P.j, slice = P.slice, unit = P.unit;
     const int c0 = slice * kSliceCols;
-    const bool two = j < a.K;
+    // the draft row of position j: verified (j < K) or, at the bonus position, only listed for
+    // the outcome cache
+    const bool two = j < a.K || (f.cache && f.fan.f[j] > 0);
     const spec_params prm = a.params[P.b];
-    if (!params_ok(prm)) return;  // the resolve kernel reports BAD_PARAM without reading summaries
+    const bool param_ok = params_ok(prm);
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)P.b * (a.K + 1) + j) * stride;
     const uint16_t* drow = two ? static_cast<const uint16_t*>(a.draft) + ((size_t)P.b * a.draft_rows + j) * stride : nullptr;
-    const int s_tok = two ? a.tokens[(size_t)P.b * a.K + j] : -1;
-    const bool tok_ok = !two || (s_tok >= 0 && s_tok < a.V);
+    const int s_tok = j < a.K ? a.tokens[(size_t)P.b * a.K + j] : -1;
+    const bool tok_ok = j == a.K || (s_tok >= 0 && s_tok < a.V);
 
-    u32x4 vq[kLoads], vp[kLoads];
-    load_slice(trow, c0, a.V, vq);
-    if (two) load_slice(drow, c0, a.V, vp);
-    for (int i = threadIdx.x; i < 2 * kHistRow / 4; i += blockDim.x)
-        reinterpret_cast<u32x4*>(&sm.hraw[0][0])[i] = u32x4{0, 0, 0, 0};
-    if (threadIdx.x < 2) {
-        sm.n_sp[threadIdx.x] = 0;
-        sm.flags[threadIdx.x] = 0;
-        sm.neginf[threadIdx.x] = 0;
+    if (param_ok) {  // (a request with bad parameters is reported without its summaries)
+        u32x4 vq[kLoads], vp[kLoads];
+        load_slice(trow, c0, a.V, vq);
+        if (two) load_slice(drow, c0, a.V, vp);
+        for (int i = threadIdx.x; i < 2 * kHistRow / 4; i += blockDim.x)
+            reinterpret_cast<u32x4*>(&sm.hraw[0][0])[i] = u32x4{0, 0, 0, 0};
+        if (threadIdx.x < 2) {
+            sm.n_sp[threadIdx.x] = 0;
+            sm.flags[threadIdx.x] = 0;
+            sm.neginf[threadIdx.x] = 0;
+        }
+        // the rows' values at the draft token (every slice counts the token's key); one thread
+        // writes both words, zero without a token
+        if (threadIdx.x == kWave) {
+            const bool has = j < a.K && tok_ok;
+            sm.s_bits[0] = has ? trow[s_tok] : 0u;
+            sm.s_bits[1] = has ? drow[s_tok] : 0u;
+        }
+        __syncthreads();
+        count_row(sm, 0, c0, a.V, vq);
+        if (two) count_row(sm, 1, c0, a.V, vp);
+        __syncthreads();
+        const bool rare0 = (sm.hraw[0][kHistLead - 1] | sm.hraw[0][kHistLead + kBins]) != 0;
+        const bool rare1 = two && (sm.hraw[1][kHistLead - 1] | sm.hraw[1][kHistLead + kBins]) != 0;
+        if (rare0) count_rare(sm, 0, c0, a.V, vq);
+        if (rare1) count_rare(sm, 1, c0, a.V, vp);
+        if (threadIdx.x < 2) {
+            sm.n_top[threadIdx.x] = 0;
+            sm.cnt_s[threadIdx.x] = 0;
+            sm.rare[threadIdx.x] = threadIdx.x == 0 ? rare0 : rare1;
+        }
+        __syncthreads();
+        seg_counts(sm, two ? 2 : 1);
+        __syncthreads();
+        // passes over the columns (registers) first, so the columns are dead for the summaries
+        const bool holds_s = j < a.K && tok_ok && s_tok >= c0;  // at or after this slice: count its key
+        const int want_q = list_len(a, prm, false), want_p = two ? draft_list_len(f, prm, j) : 0;
+        if (want_q > 0) local_top(sm, 0, want_q, c0, a.V, vq);
+        if (holds_s) local_rank(sm, 0, c0, s_tok, vq);
+        if (two) {
+            if (want_p > 0) local_top(sm, 1, want_p, c0, a.V, vp);
+            if (holds_s) local_rank(sm, 1, c0, s_tok, vp);
+        }
+        __syncthreads();
+        publish_row(f, sm, unit, slice, 0, prm);
+        if (two) publish_row(f, sm, unit, slice, 1, prm);
     }
-    // the rows' values at the draft token (every slice counts the token's key); one thread
-    // writes both words, zero without a token
-    if (threadIdx.x == kWave) {
-        const bool has = two && tok_ok;
-        sm.s_bits[0] = has ? trow[s_tok] : 0u;
-        sm.s_bits[1] = has ? drow[s_tok] : 0u;
+
+    // ---- unit rendezvous: the last slice of the unit settles it ----
+    drain_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned* uc = reinterpret_cast<unsigned*>(f.ws + f.L.unit_ctr + (size_t)unit * 128);
+        const unsigned old = l2_fetch_add(uc, 1u);
+        sm.last = (old + 1 == (unsigned)f.nS) ? 1 : 0;
+        if (sm.last) *uc = 0u;  // every slice has arrived: ready for the next call
     }
     __syncthreads();
-    count_row(sm, 0, vq);
-    if (two) count_row(sm, 1, vp);
+    if (!sm.last) return;
+    settle_unit(f, sm, P, prm, param_ok, two, s_tok, tok_ok);
+
+    // ---- request rendezvous: the last unit of the request decides k ----
+    drain_stores();
     __syncthreads();
-    const bool rare0 = (sm.hraw[0][kHistLead - 1] | sm.hraw[0][kHistLead + kBins]) != 0;
-    const bool rare1 = two && (sm.hraw[1][kHistLead - 1] | sm.hraw[1][kHistLead + kBins]) != 0;
-    if (rare0) count_rare(sm, 0, c0, a.V, vq);
-    if (rare1) count_rare(sm, 1, c0, a.V, vp);
-    if (threadIdx.x < 2) {
-        sm.n_top[threadIdx.x] = 0;
-        sm.cnt_s[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+        unsigned* rc = reinterpret_cast<unsigned*>(f.ws + f.L.req_ctr + (size_t)P.b * 128);
+        const unsigned old = l2_fetch_add(rc, 1u);
+        sm.last = (old + 1 == (unsigned)(a.K + 1)) ? 1 : 0;
+        if (sm.last) *rc = 0u;
     }
     __syncthreads();
-    seg_counts(sm, two ? 2 : 1);
-    __syncthreads();
-    // passes over the columns (registers) first, so the columns are dead for the summaries
-    const bool holds_s = two && tok_ok && s_tok >= c0;  // at or after this slice: count its key
-    const int want_q = list_len(a, prm, false), want_p = two ? list_len(a, prm, true) : 0;
-    if (want_q > 0) local_top(sm, 0, want_q, c0, a.V, vq);
-    if (holds_s) local_rank(sm, 0, c0, s_tok, vq);
-    if (two) {
-        if (want_p > 0) local_top(sm, 1, want_p, c0, a.V, vp);
-        if (holds_s) local_rank(sm, 1, c0, s_tok, vp);
-    }
-    __syncthreads();
-    publish_row(f, sm, unit, slice, 0, prm);
-    if (two) publish_row(f, sm, unit, slice, 1, prm);
+    if (sm.last) decide_request(f, P.b);
 }
 
 void launch_count(const FastArgs& f, int grid, hipStream_t stream) {

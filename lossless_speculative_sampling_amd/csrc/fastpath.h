@@ -58,6 +58,10 @@ struct FastPlan {
 FastPlan fast_plan(int B, int K, int V);
 bool fast_path_applies(const VerifyArgs& a);
 int fast_verify(const VerifyArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
+// The same pass also builds the Saguaro outcome cache (cache != nullptr); fast_cache_applies
+// says whether every depth's list fits the per-slice candidate lists.
+bool fast_cache_applies(const VerifyArgs& a, const CacheArgs& c);
+int fast_verify_cache(const VerifyArgs& a, const CacheArgs& c, void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace fast
 }  // namespace sv

@@ -35,7 +35,7 @@ bool fast_path_applies(const VerifyArgs& a) {
     return nS * kTop <= kMergeCap;  // every slice's candidate list fits the merge buffer
 }
 
-int fast_verify(const VerifyArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t ws_bytes, hipStream_t stream) {
     const FastPlan p = fast_plan(a.B, a.K, a.V);
     if (ws_bytes < p.ws_bytes) return SPEC_EWORKSPACE;
     FastArgs f;
@@ -44,9 +44,29 @@ int fast_verify(const VerifyArgs& a, void* ws, size_t ws_bytes, hipStream_t stre
     f.units = p.units;
     f.ws = static_cast<char*>(ws);
     f.L = layout(a.B, p.units, p.nS);
+    f.cache = c ? 1 : 0;
+    f.budget = c ? c->budget : 0;
+    f.out_cache = c ? c->out_cache : nullptr;
+    if (c) f.fan = c->fanout;
+    else f.fan = Fanout{};
     launch_count(f, p.grid, stream);
     launch_resolve(f, p.grid, stream);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+int fast_verify(const VerifyArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return launch_fast(a, nullptr, ws, ws_bytes, stream);
+}
+
+bool fast_cache_applies(const VerifyArgs& a, const CacheArgs& c) {
+    if (!fast_path_applies(a) || a.draft_rows != a.K + 1 || c.budget < 1) return false;
+    for (int k = 0; k <= a.K; ++k)
+        if (c.fanout.f[k] + (k < a.K ? 1 : 0) > kTop) return false;  // a slice lists at most kTop
+    return true;
+}
+
+int fast_verify_cache(const VerifyArgs& a, const CacheArgs& c, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return launch_fast(a, &c, ws, ws_bytes, stream);
 }
 
 }  // namespace fast

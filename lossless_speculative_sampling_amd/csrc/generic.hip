@@ -89,62 +89,12 @@ __global__ __launch_bounds__(kRowThreads) void downweight_kernel(DownweightArgs 
     }
 }
 
-// saguaro_cache_build: one workgroup per (request b, depth k).  The first F_k (+1 when the
-// drafted token must be skipped) tokens of draft row k in token order, NaN last.
+// saguaro_cache_build: one workgroup per (request b, depth k).
 __global__ __launch_bounds__(kRowThreads) void cache_build_kernel(CacheArgs a) {
     __shared__ RowShared sh;
     __shared__ RowStats st;
-    __shared__ int picked[SPEC_MAX_FANOUT + 1];
-    __shared__ uint32_t pkey[SPEC_MAX_FANOUT + 1];
-    __shared__ int npicked;
-    const int b = blockIdx.x / (a.K + 1);
-    const int k = blockIdx.x % (a.K + 1);
-    const int Fk = a.fanout.f[k];
-    const int off = a.fanout.off[k];
-    int32_t* out = a.out_cache + (size_t)b * a.budget + off;
-    if (Fk <= 0) return;
-    const size_t stride = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
-    RowRef r{static_cast<const char*>(a.draft) + ((size_t)b * (a.K + 1) + k) * stride, a.dtype, a.V};
-    const int excl = (k < a.K) ? a.tokens[(size_t)b * a.K + k] : -1;
-    const int want = min(a.V, Fk + (excl >= 0 && excl < a.V ? 1 : 0));
-    uint32_t tau;
-    double above, rem;
-    int cnt;
-    auto all = [](uint32_t, int, float) { return true; };
-    radix_select<false>(r, st, all, (double)want, sh, &tau, &above, &cnt, &rem);
-    const int n = (int)rem;
-    const int idc = (n >= cnt) ? a.V - 1 : nth_id_at_key(r, tau, n, all, sh);
-    if (threadIdx.x == 0) npicked = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < a.V; i += blockDim.x) {
-        const uint32_t key = order_key(load_logit(r.row, a.dtype, i));
-        if (key > tau || (key == tau && i <= idc)) {
-            const int slot = atomicAdd(&npicked, 1);
-            if (slot <= SPEC_MAX_FANOUT) {
-                picked[slot] = i;
-                pkey[slot] = key;
-            }
-        }
-    }
-    __syncthreads();
-    const int np = min(npicked, want);
-    bool excl_picked = false;
-    for (int y = 0; y < np; ++y) excl_picked |= (picked[y] == excl);
-    // rank of each picked token in (key desc, id asc) order, less one past the drafted token
-    for (int x = threadIdx.x; x < np; x += blockDim.x) {
-        const int id = picked[x];
-        if (id == excl) continue;
-        const uint32_t key = pkey[x];
-        int rank = 0;
-        for (int y = 0; y < np; ++y) {
-            const uint32_t ky = pkey[y];
-            if ((ky > key || (ky == key && picked[y] < id)) && picked[y] != excl) ++rank;
-        }
-        if (rank < Fk) out[rank] = id;
-    }
-    // rows shorter than the fan-out: pad with -1
-    const int written = min(Fk, np - (excl_picked ? 1 : 0));
-    for (int x = written + threadIdx.x; x < Fk; x += blockDim.x) out[x] = -1;
+    __shared__ CacheShared cs;
+    cache_row(a, blockIdx.x / (a.K + 1), blockIdx.x % (a.K + 1), sh, st, cs);
 }
 
 // saguaro_cache_lookup: a single workgroup loops over the requests and reduces the batch stats.

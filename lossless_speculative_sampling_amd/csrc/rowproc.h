@@ -476,4 +476,64 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
     if (threadIdx.x == 0) *rec = UnitRec{0, t, (float)W, status, s};
 }
 
+// ------------------------------------------------------------------------------------------
+// Saguaro outcome cache, one (request b, depth k) row: C_k = the first F_k tokens of draft row
+// k in token order (raw logit descending, id ascending, NaN last), leaving out the drafted
+// token s_k; C_K from draft row K (SSD reading notes, section 4.3).  Any workgroup size.
+// ------------------------------------------------------------------------------------------
+struct CacheShared {
+    int picked[SPEC_MAX_FANOUT + 1];
+    uint32_t pkey[SPEC_MAX_FANOUT + 1];
+    int npicked;
+};
+
+__device__ inline void cache_row(const CacheArgs& a, int b, int k, RowShared& sh, RowStats& st, CacheShared& cs) {
+    const int Fk = a.fanout.f[k];
+    const int off = a.fanout.off[k];
+    int32_t* out = a.out_cache + (size_t)b * a.budget + off;
+    if (Fk <= 0) return;
+    const size_t stride = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
+    RowRef r{static_cast<const char*>(a.draft) + ((size_t)b * (a.K + 1) + k) * stride, a.dtype, a.V};
+    const int excl = (k < a.K) ? a.tokens[(size_t)b * a.K + k] : -1;
+    const int want = min(a.V, Fk + (excl >= 0 && excl < a.V ? 1 : 0));
+    uint32_t tau;
+    double above, rem;
+    int cnt;
+    auto all = [](uint32_t, int, float) { return true; };
+    radix_select<false>(r, st, all, (double)want, sh, &tau, &above, &cnt, &rem);
+    const int n = (int)rem;
+    const int idc = (n >= cnt) ? a.V - 1 : nth_id_at_key(r, tau, n, all, sh);
+    if (threadIdx.x == 0) cs.npicked = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.V; i += blockDim.x) {
+        const uint32_t key = order_key(load_logit(r.row, a.dtype, i));
+        if (key > tau || (key == tau && i <= idc)) {
+            const int slot = atomicAdd(&cs.npicked, 1);
+            if (slot <= SPEC_MAX_FANOUT) {
+                cs.picked[slot] = i;
+                cs.pkey[slot] = key;
+            }
+        }
+    }
+    __syncthreads();
+    const int np = min(cs.npicked, want);
+    bool excl_picked = false;
+    for (int y = 0; y < np; ++y) excl_picked |= (cs.picked[y] == excl);
+    // rank of each picked token in (key desc, id asc) order, less one past the drafted token
+    for (int x = threadIdx.x; x < np; x += blockDim.x) {
+        const int id = cs.picked[x];
+        if (id == excl) continue;
+        const uint32_t key = cs.pkey[x];
+        int rank = 0;
+        for (int y = 0; y < np; ++y) {
+            const uint32_t ky = cs.pkey[y];
+            if ((ky > key || (ky == key && cs.picked[y] < id)) && cs.picked[y] != excl) ++rank;
+        }
+        if (rank < Fk) out[rank] = id;
+    }
+    // rows shorter than the fan-out: pad with -1
+    const int written = min(Fk, np - (excl_picked ? 1 : 0));
+    for (int x = written + threadIdx.x; x < Fk; x += blockDim.x) out[x] = -1;
+}
+
 }  // namespace sv

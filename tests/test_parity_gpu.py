@@ -116,6 +116,61 @@ def test_cache_build_and_lookup():
     say(f"[parity] cache ok: hits {int(obatch[0])}/{w.B}")
 
 
+def _check_fused(w, tokens=None, label=""):
+    """saguaro_verify_cache against the oracle's verify and cache build on the same inputs."""
+    say(f"[parity] fused verify+cache {label} B={w.B} K={w.K} V={w.V} budget={w.budget} sample={tokens is None}")
+    sample = tokens is None
+    prm = capi.params_tensor(w.temperature, w.top_k, w.top_p)
+    tok = torch.zeros((w.B, w.K), dtype=torch.int32, device="cuda") if sample else dev(np.asarray(tokens, np.int32))
+    out, cache, fan = capi.saguaro_verify_cache(dev(w.draft), dev(w.target), w.K, prm, tok, w.budget, w.a, w.r,
+                                                F=w.F, C=w.C, seed=w.seed, flags=capi.SPEC_SAMPLE_DRAFT if sample else 0)
+    torch.cuda.synchronize()
+    k, t = out.k.cpu().numpy(), out.tstar.cpu().numpy()
+    st, tk = out.status.cpu().numpy().astype(np.uint32), out.tokens.cpu().numpy()
+    o = run_oracle(w, tokens)
+    ok = o.flags == 0
+    bad = np.flatnonzero(ok & ((k != o.k) | (t != o.t) | (st != o.status)))
+    assert len(bad) == 0, f"{len(bad)} verify mismatches, first {bad[:5]}"
+    if sample:
+        good = ok & ((o.status & (oracle.ST_BAD_LOGIT | oracle.ST_BAD_PARAM)) == 0)
+        assert (tk[good] == o.tokens[good]).all()
+    np.testing.assert_allclose(out.resid_mass.cpu().numpy()[ok], o.W[ok], rtol=RTOL[w.dtype], atol=1e-6)
+    # the cache depends only on the draft rows and the drafted tokens the call used
+    ocache = oracle.cache_build(w.draft, w.dtype, w.K, tk, np.array(fan, np.int32))
+    gcache = cache.cpu().numpy()
+    rows = np.flatnonzero((gcache != ocache).any(axis=1))
+    assert len(rows) == 0, f"cache mismatch in requests {rows[:5]}: gpu {gcache[rows[0]]} oracle {ocache[rows[0]]}"
+    say(f"[parity] fused {label} ok: flagged {int((~ok).sum())} of {w.B}")
+    return o
+
+
+def test_fused_verify_and_cache_full_size():
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
+    o = _check_fused(w, label="sampled")
+    _check_fused(w, tokens=o.tokens, label="given")
+    for seed_off in (1, 2):
+        w2 = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
+        w2.seed += seed_off
+        _check_fused(w2, label=f"seed+{seed_off}")
+
+
+def test_fused_verify_and_cache_special_rows():
+    rng = np.random.default_rng(11)
+    B, K, V = 10, 3, 20480
+    d, t = synth.random_rows(rng, B, K, V, synth.BF16, draft_rows=K + 1)
+    # ties at the top of a cache row, a NaN and a +inf draft row, -inf spread, tiny values
+    d[0, 1, :50] = d[0, 1].max()
+    d[1, 0, 7] = synth.f32_to_bf16_bits(np.array([np.nan], np.float32))[0]
+    d[2, K, 100] = synth.f32_to_bf16_bits(np.array([np.inf], np.float32))[0]
+    d[3, 2, ::3] = synth.f32_to_bf16_bits(np.array([-np.inf], np.float32))[0]
+    d[4, 0, :300] = synth.f32_to_bf16_bits(np.array([1e-5], np.float32))[0]
+    w = _work(d, t, synth.BF16, K, rng.choice([0.0, 0.7, 1.0], B), rng.choice([0, 3, 40, 200], B),
+              rng.choice([0.5, 0.95, 1.0], B), F=3, C=0.5)
+    w.budget, w.a, w.r = 24, 0.6, 1.0
+    _check_fused(w, tokens=rng.integers(0, V, (B, K)), label="special rows")
+    _check_fused(w, label="special rows sampled")
+
+
 def test_tree_chains_and_branch_reuse():
     w = synth.tree(n_req=4)
     say(f"[parity] tree chains B={w.B} gamma={w.K} V={w.V} top-k 50")
