@@ -10,6 +10,16 @@
 namespace sv {
 namespace fast {
 
+// A bin at which this slice decides elements one by one: its table entry holds the value of
+// the elements up to column thr; later elements of the bin take alt (0 past a cut, the value
+// outside the downweighted set past its boundary).
+struct TieRole {
+    uint32_t off;  // byte offset of the bin's table entry (kNoTie: none)
+    int thr;
+    double alt;
+};
+constexpr uint32_t kNoTie = 0xFFFFFFFFu;
+
 struct ResSmem {
     union {
         double tab[2][kHistRow];   // per-bin values of q and p' in the padded histogram layout
@@ -22,6 +32,8 @@ struct ResSmem {
     RowStats gst[2];
     UnitRec urec;
     RowFinal rf[2];
+    double inv[2][2];              // [row][1 / S, 1 / Z]
+    TieRole tie[2][3];             // [row][set boundary, top-k tie, top-p tie] this slice decides
     UnitCut cut[2][2];
     uint32_t flags[2];             // this slice's RowPart flags of each row
     int eff[2][2];                 // this slice's id cut at each cut key (V-1 all, -1 none)
@@ -34,14 +46,14 @@ struct ResSmem {
     double ftarget, fbase;
 };
 
-// The n-th (1-based) element of this slice, in token order, whose key equals `key`.
+// The n-th (1-based) element of this slice, in token order, whose key equals `key`: every
+// thread counts its matches per 16-byte load (4 loads x 16 bits in one 64-bit word), one
+// workgroup scan orders them, and the thread holding the n-th reports its column.
 __device__ __forceinline__ int local_nth_at_key(ResSmem& sm, const u32x4 (&v)[kLoads], int c0, int V, uint32_t key, int n) {
-    if (threadIdx.x == 0) sm.found = -1;
-    __syncthreads();
-    int base = 0;
+    uint32_t mask[kLoads];
+    uint64_t packed = 0;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
-        if (base >= n) break;  // uniform
         uint32_t mq = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -50,17 +62,24 @@ __device__ __forceinline__ int local_nth_at_key(ResSmem& sm, const u32x4 (&v)[kL
             const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
             if (col < V && (h & 0x7FFFu) < 0x7F80u && key16(h) == key) mq |= 1u << e;
         }
-        int total;
-        const int before = block_exclusive_scan<int>(__popc(mq), sm.scan, &total);
-        if (base + before < n && base + before + __popc(mq) >= n) {
-            int k = base + before;
+        mask[q] = mq;
+        packed |= (uint64_t)__popc(mq) << (16 * q);
+    }
+    if (threadIdx.x == 0) sm.found = -1;
+    uint64_t total;
+    const uint64_t before = block_exclusive_scan<uint64_t>(packed, reinterpret_cast<uint64_t*>(sm.redd), &total);
+    // token order is (load q, thread, element): the loads before q contribute their totals
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        const int bq = base + (int)((before >> (16 * q)) & 0xFFFFu);
+        const int cq = __popc(mask[q]);
+        if (bq < n && bq + cq >= n) {
+            int k = bq;
             for (int e = 0; e < 8; ++e)
-                if ((mq & (1u << e)) && ++k == n) {
-                    sm.found = col_of(c0, q, e);
-                    break;
-                }
+                if ((mask[q] & (1u << e)) && ++k == n) sm.found = col_of(c0, q, e);
         }
-        base += total;
+        base += (int)((total >> (16 * q)) & 0xFFFFu);
     }
     __syncthreads();
     const int r = sm.found;
@@ -68,19 +87,23 @@ __device__ __forceinline__ int local_nth_at_key(ResSmem& sm, const u32x4 (&v)[kL
     return r;
 }
 
-// Processed probability of one element from the row's final statistics and id cuts
-// (operation order ((e / S) * f) / Z, the same as the per-bin tables).
-__device__ __forceinline__ double final_prob(const RowFinal& rf, int idk, int idp, uint32_t h, int col, bool draft) {
+// Processed probability of one element from the row's final statistics, id cuts and its mass
+// e: q = e / S, p' = ((e / S) * f) / Z, the divisions taken as products with 1 / S and 1 / Z.
+__device__ __forceinline__ double prob_from_mass(const RowFinal& rf, const double (&inv)[2], int idk, int idp, uint32_t key,
+                                                 int col, double e, bool draft) {
+    if (!in_cut_id(rf.kk, idk, key, col) || !in_cut_id(rf.kp, idp, key, col)) return 0.0;
+    const double p = e * inv[0];
+    if (!draft) return p;
+    const double fct = (rf.nS > 0 && e > 0.0 && in_cut_id(rf.kF, rf.idF, key, col)) ? rf.C : 1.0;
+    return (p * fct) * inv[1];
+}
+
+__device__ __forceinline__ double final_prob(const RowFinal& rf, const double (&inv)[2], int idk, int idp, uint32_t h, int col,
+                                             bool draft) {
     const uint32_t mag = h & 0x7FFFu;
     if (mag >= 0x7F80u) return 0.0;  // -inf (rows with NaN or +inf never get here)
     if (rf.greedy) return col == rf.argmax ? 1.0 : 0.0;
-    const uint32_t key = key16(h);
-    if (!in_cut_id(rf.kk, idk, key, col) || !in_cut_id(rf.kp, idp, key, col)) return 0.0;
-    const double e = mass_of(__uint_as_float(h << 16), rf.m, rf.invT);
-    const double p = e / rf.S;
-    if (!draft) return p;
-    const double fct = (rf.nS > 0 && e > 0.0 && in_cut_id(rf.kF, rf.idF, key, col)) ? rf.C : 1.0;
-    return (p * fct) / rf.Z;
+    return prob_from_mass(rf, inv, idk, idp, key16(h), col, mass_of(__uint_as_float(h << 16), rf.m, rf.invT), draft);
 }
 
 // Whether this slice's elements at a cut key are kept: all (before the owner), none (after),
@@ -93,46 +116,110 @@ constexpr double kMarkQ = 1e300;    // in the target table: (q - p)+ and q becom
 constexpr double kMarkP = -1e300;   // in the draft table: (q - p)+ becomes huge
 constexpr double kMarkSeen = 1e299;
 
-// Per-bin values of row r for this slice: q = e / S, p' = ((e / S) * f) / Z, with every cut
-// key resolved as this slice sees it.  Where this slice decides elements at a key one by one
-// (it holds the last kept element at a cut key, or the draft row's downweighted-set
-// boundary), and in the padding words when the slice holds values outside the exact bins,
-// the entry is a marker.  Bins above the row maximum hold no element and bins below the cuts
-// are 0, so only bins between them need an exp.
-__device__ __forceinline__ void build_table(ResSmem& sm, int r, int slice, bool draft) {
-    const RowFinal& rf = sm.rf[r];
-    const UnitCut& ck = sm.cut[r][0];
-    const UnitCut& cp = sm.cut[r][1];
-    const uint32_t kmax = key16(__float_as_uint(rf.m) >> 16);
-    const uint32_t klow = max(ck.key, cp.key);
-    const int ownerF = rf.nS > 0 ? rf.idF / kSliceCols : -1;
-    const double mark = r == 0 ? kMarkQ : kMarkP;
-    const bool rare = (sm.flags[r] & 4u) != 0;
-    const uint32_t own_k = (ck.key != 0u && ck.owner == slice) ? ck.key : 0xFFFFFFFFu;
-    const uint32_t own_p = (cp.key != 0u && cp.owner == slice) ? cp.key : 0xFFFFFFFFu;
-    const uint32_t own_F = (draft && ownerF == slice) ? rf.kF : 0xFFFFFFFFu;
-    double* t = &sm.u.tab[r][0];
-    for (int i = threadIdx.x; i < kHistRow; i += blockDim.x) {
-        const int bin = i - kHistLead;
-        double v = 0.0;
-        if (bin >= 0 && bin < kBins) {
-            const uint32_t key = bin_key(bin);
-            if (key == own_k || key == own_p || key == own_F) {
-                v = mark;
-            } else if (key >= klow && key <= kmax && (key > ck.key || slice_keeps(ck, slice)) &&
-                       (key > cp.key || slice_keeps(cp, slice))) {
-                const double e = mass_of(key16_value(key), rf.m, rf.invT);
-                v = e / rf.S;
-                if (draft) {
-                    const bool in_set = rf.nS > 0 && e > 0.0 && (key > rf.kF || (key == rf.kF && slice <= ownerF));
-                    v = (v * (in_set ? rf.C : 1.0)) / rf.Z;
-                }
-            }
-        } else if (rare) {
-            v = mark;
-        }
-        t[i] = v;
+// Per-bin values of both rows for this slice: q = e / S, p' = ((e / S) * f) / Z (as
+// final_prob), with every cut key resolved as this slice sees it.  Where this slice decides
+// elements of a bin one by one (it holds the last kept element at a cut key, or the draft
+// row's downweighted-set boundary) the entry holds the value of the earliest elements and a
+// tie role records where and how the later ones differ.  The padding words hold a marker when
+// the slice has values outside the exact bins.  One wave per group of 64 bins: groups wholly
+// below the cuts are 0 and groups above the row maximum hold no element, so only the groups
+// in between need their exps.
+__device__ __forceinline__ void build_tables(ResSmem& sm, bool two, int slice) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    uint32_t klow[2], kmax[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        klow[r] = max(sm.cut[r][0].key, sm.cut[r][1].key);
+        kmax[r] = key16(__float_as_uint(sm.rf[r].m) >> 16);
     }
+    const int ownerF = (two && sm.rf[1].nS > 0) ? sm.rf[1].idF / kSliceCols : -1;
+    for (int g = wave; g < kGroups; g += kWaves) {
+        const uint32_t glo = bin_key(g * kGroup), ghi = bin_key(g * kGroup + kGroup - 1);
+        const bool need0 = ghi >= klow[0] && glo <= kmax[0];
+        const bool need1 = two && ghi >= klow[1] && glo <= kmax[1];
+        const int bin = g * kGroup + lane;
+        const uint32_t key = bin_key(bin);
+        // both rows' masses in one step (two independent exp chains)
+        double e0 = 0.0, e1 = 0.0;
+        if (need0 || need1) {
+            const float z = key16_value(key);
+            e0 = mass_of(z, sm.rf[0].m, sm.rf[0].invT);
+            if (two) e1 = mass_of(z, sm.rf[1].m, sm.rf[1].invT);
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            if (r == 1 && !two) break;
+            const RowFinal& rf = sm.rf[r];
+            const UnitCut& ck = sm.cut[r][0];
+            const UnitCut& cp = sm.cut[r][1];
+            const double e = r == 0 ? e0 : e1;
+            // zero never reaches its bins (the packed offsets send it to the padding words)
+            const bool real = g != kZeroGroup;
+            const bool own_k = real && ck.key != 0u && ck.owner == slice && key == ck.key;
+            const bool own_p = real && cp.key != 0u && cp.owner == slice && key == cp.key;
+            const bool own_F = real && r == 1 && ownerF == slice && key == rf.kF;
+            double v = 0.0;
+            if (key >= klow[r] && key <= kmax[r] && (key > ck.key || slice_keeps(ck, slice)) &&
+                (key > cp.key || slice_keeps(cp, slice))) {
+                const double pv = e * sm.inv[r][0];
+                v = pv;
+                if (r == 1) {
+                    const bool in_set = rf.nS > 0 && e > 0.0 && (key > rf.kF || (key == rf.kF && slice <= ownerF));
+                    v = (pv * (in_set ? rf.C : 1.0)) * sm.inv[r][1];
+                }
+                const uint32_t off = 8u * (uint32_t)(kHistLead + bin);
+                if (own_F) sm.tie[r][0] = TieRole{off, rf.idF, pv * sm.inv[r][1]};
+                if (own_k) sm.tie[r][1] = TieRole{off, sm.eff[r][0], 0.0};
+                if (own_p) sm.tie[r][2] = TieRole{off, sm.eff[r][1], 0.0};
+            }
+            if (r == 0 ? (need0 || ghi < klow[0]) : (need1 || ghi < klow[1])) sm.u.tab[r][kHistLead + bin] = v;
+        }
+    }
+    // padding words: values outside the exact bins
+    if ((int)threadIdx.x < (two ? 4 : 2)) {
+        const int r = threadIdx.x >> 1;
+        const double v = (sm.flags[r] & 4u) ? (r == 0 ? kMarkQ : kMarkP) : 0.0;
+        sm.u.tab[r][(threadIdx.x & 1) ? kHistLead + kBins : kHistLead - 1] = v;
+    }
+}
+
+// The tie roles of a row as the workgroup reads them: uniform values.
+struct Ties {
+    uint32_t off[3];
+    int thr[3];
+    double alt[3];
+    int any;
+};
+__device__ __forceinline__ Ties load_ties(const ResSmem& sm, int r) {
+    Ties t;
+    t.any = 0;
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        t.off[x] = __builtin_amdgcn_readfirstlane(sm.tie[r][x].off);
+        t.thr[x] = __builtin_amdgcn_readfirstlane(sm.tie[r][x].thr);
+        const double alt = sm.tie[r][x].alt;
+        t.alt[x] = __hiloint2double(__builtin_amdgcn_readfirstlane(__double2hiint(alt)),
+                                    __builtin_amdgcn_readfirstlane(__double2loint(alt)));
+        t.any |= t.off[x] != kNoTie;
+    }
+    return t;
+}
+// Applies the roles (boundary first, then the cuts) to the values v0, v1 of the two elements
+// at table offsets o (low, high half) and columns col, col + 1.
+__device__ __forceinline__ void apply_ties(const Ties& t, uint32_t o, int col, double& v0, double& v1) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        if (t.off[x] == kNoTie || col + 1 <= t.thr[x]) continue;
+        if ((o & 0xFFFFu) == t.off[x] && col > t.thr[x]) v0 = t.alt[x];
+        if ((o >> 16) == t.off[x]) v1 = t.alt[x];
+    }
+}
+__device__ __forceinline__ double apply_ties1(const Ties& t, uint32_t o16, int col, double v) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+        if (o16 == t.off[x] && col > t.thr[x]) v = t.alt[x];
+    return v;
 }
 
 // Byte offsets of the two fp64 table entries of the bf16 values packed in w.
@@ -153,17 +240,22 @@ __device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, i
     const char* tq = reinterpret_cast<const char*>(&sm.u.tab[0][0]);
     const char* tp = reinterpret_cast<const char*>(&sm.u.tab[1][0]);
     double* out = reinterpret_cast<double*>(f.ws + f.L.chunks) + ((size_t)b * f.nS + slice) * kChunks;
+    const Ties tiq = load_ties(sm, 0);
+    const Ties tip = load_ties(sm, 1);
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
         double s = 0.0;
-        if (col_of(c0, q, 0) < a.V) {
+        const int cq = col_of(c0, q, 0);
+        if (cq < a.V) {
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const uint32_t oq = tab_offsets2(vq[q][d]);
-                const double q0 = tab_at(tq, oq & 0xFFFFu), q1 = tab_at(tq, oq >> 16);
+                double q0 = tab_at(tq, oq & 0xFFFFu), q1 = tab_at(tq, oq >> 16);
+                if (tiq.any) apply_ties(tiq, oq, cq + 2 * d, q0, q1);
                 if (two) {
                     const uint32_t op = tab_offsets2(vp[q][d]);
-                    const double p0 = tab_at(tp, op & 0xFFFFu), p1 = tab_at(tp, op >> 16);
+                    double p0 = tab_at(tp, op & 0xFFFFu), p1 = tab_at(tp, op >> 16);
+                    if (tip.any) apply_ties(tip, op, cq + 2 * d, p0, p1);
                     s += max(q0 - p0, 0.0);
                     s += max(q1 - p1, 0.0);
                 } else {
@@ -171,18 +263,25 @@ __device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, i
                     s += q1;
                 }
             }
-            if (s > kMarkSeen) {  // rare: decide these columns exactly
+            if (s > kMarkSeen) {  // rare: values outside the exact bins, decided exactly
                 s = 0.0;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int col = col_of(c0, q, e);
+                    const int col = cq + e;
                     const uint32_t wq = vq[q][e >> 1];
                     const uint32_t hq = (e & 1) ? (wq >> 16) : (wq & 0xFFFFu);
-                    const double qe = final_prob(sm.rf[0], sm.eff[0][0], sm.eff[0][1], hq, col, false);
+                    const uint32_t oq = tab_offsets2(hq) & 0xFFFFu;
+                    double qe = tab_at(tq, oq);
+                    qe = qe > kMarkSeen ? final_prob(sm.rf[0], sm.inv[0], sm.eff[0][0], sm.eff[0][1], hq, col, false)
+                                        : apply_ties1(tiq, oq, col, qe);
                     if (two) {
                         const uint32_t wp = vp[q][e >> 1];
                         const uint32_t hp = (e & 1) ? (wp >> 16) : (wp & 0xFFFFu);
-                        s += max(qe - final_prob(sm.rf[1], sm.eff[1][0], sm.eff[1][1], hp, col, true), 0.0);
+                        const uint32_t op = tab_offsets2(hp) & 0xFFFFu;
+                        double pe = tab_at(tp, op);
+                        pe = pe < -kMarkSeen ? final_prob(sm.rf[1], sm.inv[1], sm.eff[1][0], sm.eff[1][1], hp, col, true)
+                                             : apply_ties1(tip, op, col, pe);
+                        s += max(qe - pe, 0.0);
                     } else {
                         s += qe;
                     }
@@ -247,7 +346,7 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
     double total_q = 0.0;
     if (mode == 2) {
         double acc = 0.0;
-        for (int col = threadIdx.x; col < a.V; col += blockDim.x) acc += final_prob(rq, idk_q, idp_q, trow[col], col, false);
+        for (int col = threadIdx.x; col < a.V; col += blockDim.x) acc += final_prob(rq, sm.inv[0], idk_q, idp_q, trow[col], col, false);
         total_q = block_sum<double>(acc, sm.redd);
     }
     const double tgt = mode == 1 ? sm.ftarget : sm.ftarget * total_q;
@@ -256,9 +355,9 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
         const int col = c0 + threadIdx.x;
         double w = 0.0;
         if (col < hi) {
-            const double qv = final_prob(rq, idk_q, idp_q, trow[col], col, false);
+            const double qv = final_prob(rq, sm.inv[0], idk_q, idp_q, trow[col], col, false);
             if (mode == 1 && drow) {
-                const double pv = final_prob(rp, idk_p, idp_p, drow[col], col, true);
+                const double pv = final_prob(rp, sm.inv[1], idk_p, idp_p, drow[col], col, true);
                 w = qv > pv ? qv - pv : 0.0;
             } else {
                 w = qv;
@@ -353,26 +452,32 @@ __device__ __forceinline__ void general_request(const FastArgs& f, ResSmem& sm, 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_resolve_kernel(FastArgs f) {
     __shared__ ResSmem sm;
     const VerifyArgs& a = f.a;
-    const Place P = place_of(f);
-    if (P.b >= a.B) return;
-    const int b = P.b, j = P.j, slice = P.slice, unit = P.unit;
+    // placement as in the count kernel (request b on XCD b % 8), R = max(nS, K + 1)
+    // workgroups per request; workgroup w of a request is slice w of unit k (residual) or
+    // unit w (general algorithm, cache rows)
+    const int R = max(f.nS, a.K + 1);
+    const int x = blockIdx.x % kXcd, l = blockIdx.x / kXcd;
+    const int b = (l / R) * kXcd + x, w = l % R;
+    if (b >= a.B) return;
     // outcome-cache rows the count kernel's candidate lists could not settle
-    if (f.cache && slice == 0 && reinterpret_cast<const int32_t*>(f.ws + f.L.cache_gen)[unit]) {
+    if (f.cache && w <= a.K && reinterpret_cast<const int32_t*>(f.ws + f.L.cache_gen)[b * (a.K + 1) + w]) {
         CacheArgs c{a.draft, a.dtype, a.B, a.K, a.V, a.tokens, f.budget, f.fan, f.out_cache};
-        cache_row(c, b, j, sm.u.cache.rs, sm.gst[0], sm.u.cache.cs);
+        cache_row(c, b, w, sm.u.cache.rs, sm.gst[0], sm.u.cache.cs);
         __syncthreads();
     }
-    const ReqFast* R = reinterpret_cast<const ReqFast*>(f.ws + f.L.reqs) + b;
-    const int mode = R->mode;
+    const ReqFast* Rq = reinterpret_cast<const ReqFast*>(f.ws + f.L.reqs) + b;
+    const int mode = Rq->mode;
     if (mode == 0) return;  // decided by the count kernel
     if (mode == 2) {
-        if (slice == 0) general_request(f, sm, b, j);
+        if (w <= a.K) general_request(f, sm, b, w);
         return;
     }
-    // mode 1: the residual of unit k
-    const int k = R->k;
-    if (j != k) return;
-    const uint32_t status = R->status;
+    // mode 1: the residual of unit k, slice w
+    const int k = Rq->k;
+    const int slice = w;
+    if (slice >= f.nS) return;
+    const int unit = b * (a.K + 1) + k;
+    const uint32_t status = Rq->status;
     const bool two = k < a.K;
     const int c0 = slice * kSliceCols;
     const size_t stride = (size_t)a.V;
@@ -398,8 +503,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         if ((int)threadIdx.x < ncut) reinterpret_cast<uint32_t*>(&sm.cut[0][0])[threadIdx.x] = ldnt(srcc + threadIdx.x);
         if (!two && threadIdx.x >= kWave && threadIdx.x < kWave + 2) sm.cut[1][threadIdx.x - kWave] = UnitCut{0u, -1, 0, 0};
         if (threadIdx.x < 2) sm.flags[threadIdx.x] = (threadIdx.x == 0 || two) ? ldnt(&part_of(f, unit, slice, threadIdx.x)->flags) : 0u;
+        if (threadIdx.x >= kWave && threadIdx.x < kWave + 6) sm.tie[(threadIdx.x - kWave) / 3][(threadIdx.x - kWave) % 3].off = kNoTie;
     }
     __syncthreads();
+    if (threadIdx.x < 2) {
+        sm.inv[threadIdx.x][0] = 1.0 / sm.rf[threadIdx.x].S;
+        sm.inv[threadIdx.x][1] = 1.0 / sm.rf[threadIdx.x].Z;
+    }
     // this slice's id cut at each cut key; the owner of a histogram cut finds its id
     int32_t* IC = reinterpret_cast<int32_t*>(f.ws + f.L.idcut) + b * 4;
     for (int r = 0; r < 2; ++r) {
@@ -421,8 +531,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
             }
         }
     }
-    build_table(sm, 0, slice, false);
-    if (two) build_table(sm, 1, slice, true);
+    __syncthreads();  // 1 / S and 1 / Z
+    build_tables(sm, two, slice);
     __syncthreads();
     residual_slice(f, sm, b, slice, c0, two, vq, vp);
     if (!arrive_last(f, sm, b, f.nS)) return;

@@ -51,7 +51,8 @@ constexpr int kSpecial = 64;    // per slice-row finite values outside the exact
 struct FastPlan {
     int nS;          // slices per row
     int units;       // B * (K + 1)
-    int grid;        // workgroups launched
+    int grid;        // workgroups of the count kernel
+    int grid_resolve;// workgroups of the resolve kernel
     size_t ws_bytes; // fast workspace bytes
 };
 

@@ -23,6 +23,7 @@ FastPlan fast_plan(int B, int K, int V) {
     p.units = B * (K + 1);
     const int reqs_per_xcd = (B + kXcd - 1) / kXcd;
     p.grid = kXcd * reqs_per_xcd * (K + 1) * p.nS;
+    p.grid_resolve = kXcd * reqs_per_xcd * max(p.nS, K + 1);
     p.ws_bytes = layout(B, p.units, p.nS).total;
     return p;
 }
@@ -50,7 +51,7 @@ static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t
     if (c) f.fan = c->fanout;
     else f.fan = Fanout{};
     launch_count(f, p.grid, stream);
-    launch_resolve(f, p.grid, stream);
+    launch_resolve(f, p.grid_resolve, stream);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
