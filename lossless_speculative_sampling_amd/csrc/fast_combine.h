@@ -30,6 +30,7 @@ struct RowView {   // the combined view of one row, identical in every slice of 
     uint32_t n_finite;
     int has_special;
     int want;                  // candidates each slice lists
+    int total;                 // candidates all slices listed
     int nm;                    // merged candidates (okey / oid)
     double S_all, S_kept, S;
     int has_k, has_p, small_k; // top-k / nucleus active; top-k settled by the merged list
@@ -151,6 +152,7 @@ __device__ __forceinline__ void combine_load(const FastArgs& f, UnitSmem& us, in
         }
     }
     // -- row headers (wave r) --
+    int list_start = 0;  // wave r, lane t: where slice t's candidates start in the row's merge
     if (wave < rows) {
         RowView& rv = us.rv[wave];
         const float mt = lane < nS ? __uint_as_float(h0[0]) : -__builtin_inff();
@@ -163,6 +165,8 @@ __device__ __forceinline__ void combine_load(const FastArgs& f, UnitSmem& us, in
         const double sc = (lane < nS && T > 0.0 && mt > -__builtin_inff()) ? mass_of(mt, m, inv_temperature(prm.temperature)) : 0.0;
         const double S = wave_sum(sc * St);
         const uint32_t sbits = wave_bcast(h1[2], 0);
+        const int total = wave_scan(lane < nS ? (int)ntop : 0, &list_start);
+        const int row_total = wave_bcast(total, kWave - 1);
         if (lane < kMaxSlices) {
             rv.sc[lane] = sc;
             rv.n_top[lane] = lane < nS ? (int)ntop : 0;
@@ -176,6 +180,7 @@ __device__ __forceinline__ void combine_load(const FastArgs& f, UnitSmem& us, in
             rv.has_special = has_sp ? 1 : 0;
             rv.S_all = S;
             rv.want = want[wave];
+            rv.total = row_total;
             rv.s_bits = sbits;
             rv.rank_s = rank;
         }
@@ -212,39 +217,100 @@ __device__ __forceinline__ void combine_load(const FastArgs& f, UnitSmem& us, in
             us.rv[r].seg_count[sg] = c;
         }
     }
-    // -- merged candidate lists: rank of every entry by binary search in the other lists --
-    for (int r = 0; r < rows; ++r) {
-        const int per = want[r];
-        if (per == 0) continue;
-        const RowView& rv = us.rv[r];
+    // -- merged candidate lists --
+    int total[2] = {0, 0};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) total[r] = (r < rows && want[r] > 0) ? __builtin_amdgcn_readfirstlane(us.rv[r].total) : 0;
+    // up to 64 candidates of a row: wave r holds one per lane and ranks each against all
+    // others through lane reads
+    if (wave < rows && want[wave] > 0 && total[wave] <= kWave) {
+        const int r = wave;
+        int t = 0, x = lane;
+        for (int u = 0; u < nS; ++u) {
+            const int st = wave_bcast(list_start, u);
+            if (lane >= st) {
+                t = u;
+                x = lane - st;
+            }
+        }
+        const bool live = lane < total[r];
+        const uint32_t k = live ? us.key[r][t * kTop + x] : 0u;
+        const int32_t id = live ? us.id[r][t * kTop + x] : 0;
+        const uint64_t ord = ((uint64_t)k << 32) | (uint32_t)~id;  // token order (ids are non-negative)
+        // lanes past the candidates hold key 0, below every candidate: reading them adds nothing
+        int rank = 0;
+        for (int y = 0; y < total[r]; y += 4) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) rank += wave_bcast(ord, y + d) > ord ? 1 : 0;
+        }
+        if (live && rank < want[r]) {
+            us.okey[r][rank] = k;
+            us.oid[r][rank] = id;
+        }
+    }
+    // more: rank of every entry by branch-free binary searches in the other lists, up to 8
+    // lists and both rows in lock-step so the LDS reads overlap
+    if (total[0] > kWave || total[1] > kWave) {
         for (int i = threadIdx.x; i < nS * kTop; i += blockDim.x) {
             const int t = i >> 6, x = i & (kTop - 1);
-            if (x >= rv.n_top[t]) continue;
-            const uint32_t k = us.key[r][i];
-            const int id = us.id[r][i];
-            int rank = x;
-            for (int t2 = 0; t2 < nS; ++t2) {
-                if (t2 == t) continue;
-                int lo = 0, hi = rv.n_top[t2];
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    const uint32_t k2 = us.key[r][t2 * kTop + mid];
-                    const bool before = k2 > k || (k2 == k && us.id[r][t2 * kTop + mid] < id);
-                    if (before) lo = mid + 1;
-                    else hi = mid;
+            uint32_t k[2];
+            int32_t id[2];
+            uint64_t ord[2];
+            int rank[2];
+            bool live[2];
+    #pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                live[r] = r < rows && want[r] > 0 && total[r] > kWave && x < us.rv[r].n_top[t];
+                k[r] = live[r] ? us.key[r][i] : 0u;
+                id[r] = live[r] ? us.id[r][i] : 0;
+                ord[r] = ((uint64_t)k[r] << 32) | (uint32_t)~id[r];
+                rank[r] = x;
+            }
+            for (int tb = 0; tb < nS; tb += 8) {
+                int pos[2][8], n[2][8];
+                int nmax = 0;
+    #pragma unroll
+                for (int r = 0; r < 2; ++r)
+    #pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int t2 = tb + u;
+                        const int nt = (r < rows && want[r] > 0 && total[r] > kWave && t2 < nS) ? us.rv[r].n_top[t2] : 0;
+                        nmax = max(nmax, nt);  // uniform: the same lists for every thread
+                        pos[r][u] = 0;
+                        n[r][u] = (live[r] && t2 != t) ? nt : 0;
+                    }
+                int step = 1;
+                while (step * 2 <= nmax) step *= 2;
+                for (; step > 0 && nmax > 0; step >>= 1) {
+                    // every probe reads an address inside its list, so the reads need no branch
+    #pragma unroll
+                    for (int r = 0; r < 2; ++r)
+    #pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int probe = pos[r][u] + step;
+                            const int e = min(tb + u, kMaxSlices - 1) * kTop + min(probe, kTop) - 1;
+                            // token order as one 64-bit comparison (ids are non-negative)
+                            const uint64_t o2 = ((uint64_t)us.key[r][e] << 32) | (uint32_t)~us.id[r][e];
+                            pos[r][u] = ((probe <= n[r][u]) & (o2 > ord[r])) ? probe : pos[r][u];
+                        }
                 }
-                rank += lo;
+    #pragma unroll
+                for (int r = 0; r < 2; ++r)
+    #pragma unroll
+                    for (int u = 0; u < 8; ++u) rank[r] += pos[r][u];
             }
-            if (rank < per) {
-                us.okey[r][rank] = k;
-                us.oid[r][rank] = id;
+    #pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                if (live[r] && rank[r] < want[r]) {
+                    us.okey[r][rank[r]] = k[r];
+                    us.oid[r][rank[r]] = id[r];
+                }
             }
         }
-        if (threadIdx.x == 0) {
-            int tot = 0;
-            for (int t = 0; t < nS; ++t) tot += rv.n_top[t];
-            us.rv[r].nm = min(tot, per);
-        }
+    }
+    if (threadIdx.x < (unsigned)rows) {
+        const int r = threadIdx.x;
+        us.rv[r].nm = min(total[r], want[r]);
     }
     __syncthreads();
 }
@@ -525,24 +591,31 @@ __device__ __forceinline__ void combine(const FastArgs& f, UnitSmem& us, int uni
             if (g >= 0) us.fine_ps[r][t][bb] = (uint16_t)ldnt_u16(&part_of(f, unit, t, r)->fine[g * kGroup + bb]);
         }
         __syncthreads();
-        for (int r = 0; r < rows; ++r) {
-            RowView& rv = us.rv[r];
-            if (rv.pend == 0) continue;
-            const bool count_cut = rv.pend == 1;
-            const bool use_lim = !count_cut && rv.has_k && rv.ck.key != 0u;
-            const Cut lim = rv.ck;
-            if (group_of_seg(rv.pend_seg) >= 0) {
-                if (wave == r) {
-                    if (count_cut) group_walk<false>(f, us, r, false, lim, &rv.ck);
-                    else group_walk<true>(f, us, r, use_lim, lim, &rv.cp);
-                }
-            } else {
-                if (count_cut) special_walk<false>(f, us, unit, r, false, lim, &rv.ck);
-                else special_walk<true>(f, us, unit, r, use_lim, lim, &rv.cp);
-            }
-            __syncthreads();
-            if (count_cut && wave == r) nucleus_step(us, r, prm);
+        // the rows' pending cuts as they stand before the walks
+        bool count_cut[2], in_groups[2], pend[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            pend[r] = r == 0 ? p0 : p1;
+            count_cut[r] = pend[r] && us.rv[r].pend == 1;
+            in_groups[r] = pend[r] && group_of_seg(us.rv[r].pend_seg) >= 0;
         }
+        // cuts inside an exact group: wave r walks row r, both rows at once
+        if (wave < rows && in_groups[wave]) {
+            RowView& rv = us.rv[wave];
+            const Cut lim = rv.ck;
+            if (count_cut[wave]) group_walk<false>(f, us, wave, false, lim, &rv.ck);
+            else group_walk<true>(f, us, wave, rv.has_k && rv.ck.key != 0u, lim, &rv.cp);
+        }
+        // cuts among the special values: the whole workgroup, one row at a time
+        for (int r = 0; r < rows; ++r) {
+            if (!pend[r] || in_groups[r]) continue;
+            RowView& rv = us.rv[r];
+            const Cut lim = rv.ck;
+            if (count_cut[r]) special_walk<false>(f, us, unit, r, false, lim, &rv.ck);
+            else special_walk<true>(f, us, unit, r, rv.has_k && rv.ck.key != 0u, lim, &rv.cp);
+        }
+        __syncthreads();
+        if (wave < rows && count_cut[wave]) nucleus_step(us, wave, prm);
         __syncthreads();
     }
     // downweighted set: the first F elements of the processed order that carry mass

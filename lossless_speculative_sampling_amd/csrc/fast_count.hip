@@ -38,6 +38,7 @@ struct CountSmem {
     uint32_t maxkey;
     int last;
     int rare[2];
+    double u_acc;  // the acceptance draw of the unit's position
 };
 
 // Per-segment element counts of both rows into sm.segc: a thread adds 8 bins, eight lanes a
@@ -409,7 +410,7 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
                     const double ps = prob_of_s(us, 1, s_tok, true);
                     const double qs = prob_of_s(us, 0, s_tok, false);
                     if (!(ps > 0.0)) status |= kStOutside;
-                    const double u = uniform_at(a.seed, a.round, (uint64_t)P.b, (uint64_t)P.j, 0);
+                    const double u = sm.u_acc;
                     accept = (u * ps < qs) ? 1 : 0;
                 }
             } else {
@@ -551,10 +552,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     const int s_tok = j < a.K ? a.tokens[(size_t)P.b * a.K + j] : -1;
     const bool tok_ok = j == a.K || (s_tok >= 0 && s_tok < a.V);
 
+    // the acceptance draw of position j, in the shadow of the first loads (wave 1 only; the
+    // empty asm keeps it here rather than where the settle step reads it)
+    double u_acc = 0.0;
     if (param_ok) {  // (a request with bad parameters is reported without its summaries)
         u32x4 vq[kLoads], vp[kLoads];
         load_slice(trow, c0, a.V, vq);
         if (two) load_slice(drow, c0, a.V, vp);
+        if (j < a.K && threadIdx.x / kWave == 1) {
+            u_acc = uniform_at(a.seed, a.round, (uint64_t)P.b, (uint64_t)j, 0);
+            asm volatile("" ::"s"(u_acc));
+        }
         for (int i = threadIdx.x; i < 2 * kHistRow / 4; i += blockDim.x)
             reinterpret_cast<u32x4*>(&sm.hraw[0][0])[i] = u32x4{0, 0, 0, 0};
         if (threadIdx.x < 2) {
@@ -610,6 +618,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     }
     __syncthreads();
     if (!sm.last) return;
+    if (threadIdx.x == kWave) sm.u_acc = u_acc;  // read after the settle step's first barrier
     settle_unit(f, sm, P, prm, param_ok, two, s_tok, tok_ok);
 
     // ---- request rendezvous: the last unit of the request decides k ----
