@@ -37,54 +37,113 @@ struct ResSmem {
     UnitCut cut[2][2];
     uint32_t flags[2];             // this slice's RowPart flags of each row
     int eff[2][2];                 // this slice's id cut at each cut key (V-1 all, -1 none)
+    uint64_t nth_scan[kWaves][4];  // per-wave match counts of the owned cut keys
     int32_t scan[kWaves + 1];
     double redd[kWaves];
     int32_t redi[kWaves];
-    int found;
     int last;
     int fc;
     double ftarget, fbase;
 };
 
-// The n-th (1-based) element of this slice, in token order, whose key equals `key`: every
-// thread counts its matches per 16-byte load (4 loads x 16 bits in one 64-bit word), one
-// workgroup scan orders them, and the thread holding the n-th reports its column.
-__device__ __forceinline__ int local_nth_at_key(ResSmem& sm, const u32x4 (&v)[kLoads], int c0, int V, uint32_t key, int n) {
-    uint32_t mask[kLoads];
-    uint64_t packed = 0;
+// This slice's id cut at every cut key of both rows (row r, cut c): V - 1 (keeps all), -1
+// (keeps none), the explicit id, or, at a histogram cut this slice owns, the column of the
+// owner_take-th element at the cut key in token order.  The owned cuts share one pass: packed
+// bf16 comparisons count each thread's matches per 16-byte load, one workgroup scan of four
+// 64-bit words (one per cut, four 16-bit load counts each) orders them, and the threads
+// holding the wanted elements report their columns.
+__device__ __forceinline__ void slice_id_cuts(ResSmem& sm, const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads], int c0, int V,
+                                              int slice, bool two) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    bool own[4];
+    int res[4];
+    uint32_t masks[4];
+    uint64_t packed[4];
+    bool any = false;
+    // elements per load that lie inside the row (the tail slice is zero-filled past V)
+    uint32_t valid[kLoads];
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
-        uint32_t mq = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int col = col_of(c0, q, e);
-            const uint32_t w = v[q][e >> 1];
-            const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-            if (col < V && (h & 0x7FFFu) < 0x7F80u && key16(h) == key) mq |= 1u << e;
-        }
-        mask[q] = mq;
-        packed |= (uint64_t)__popc(mq) << (16 * q);
+        const int left = V - col_of(c0, q, 0);
+        valid[q] = left >= 8 ? 0xFFu : (left <= 0 ? 0u : ((1u << left) - 1u));
     }
-    if (threadIdx.x == 0) sm.found = -1;
-    uint64_t total;
-    const uint64_t before = block_exclusive_scan<uint64_t>(packed, reinterpret_cast<uint64_t*>(sm.redd), &total);
-    // token order is (load q, thread, element): the loads before q contribute their totals
-    int base = 0;
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) {
-        const int bq = base + (int)((before >> (16 * q)) & 0xFFFFu);
-        const int cq = __popc(mask[q]);
-        if (bq < n && bq + cq >= n) {
-            int k = bq;
-            for (int e = 0; e < 8; ++e)
-                if ((mask[q] & (1u << e)) && ++k == n) sm.found = col_of(c0, q, e);
+    for (int x = 0; x < 4; ++x) {
+        const int r = x >> 1;
+        const UnitCut uc = sm.cut[r][x & 1];
+        own[x] = false;
+        res[x] = V - 1;
+        masks[x] = 0u;
+        packed[x] = 0u;
+        if (uc.key == 0u || (r == 1 && !two)) continue;
+        if (uc.explicit_id >= 0) res[x] = uc.explicit_id;
+        else if (slice > uc.owner) res[x] = -1;
+        else if (slice == uc.owner) own[x] = true;
+        if (!own[x]) continue;
+        any = true;
+        // the key's bf16 pattern; zero's key stands for both signed zeros
+        const uint32_t k = uc.key;
+        const uint32_t hk = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+        const uint32_t keep = hk == 0u ? 0x7FFF7FFFu : 0xFFFFFFFFu;
+        const uint32_t pat = hk * 0x10001u;
+        const u32x4(&v)[kLoads] = r == 0 ? vq : vp;
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) {
+            uint32_t mq = 0;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t y = (v[q][d] & keep) ^ pat;
+                mq |= ((y & 0xFFFFu) == 0u ? 1u : 0u) << (2 * d);
+                mq |= ((y >> 16) == 0u ? 1u : 0u) << (2 * d + 1);
+            }
+            mq &= valid[q];
+            masks[x] |= mq << (8 * q);
+            packed[x] |= (uint64_t)__popc(mq) << (16 * q);
         }
-        base += (int)((total >> (16 * q)) & 0xFFFFu);
     }
-    __syncthreads();
-    const int r = sm.found;
-    __syncthreads();
-    return r;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+        if ((int)threadIdx.x == x) sm.eff[x >> 1][x & 1] = own[x] ? -1 : res[x];  // -1: fewer matches than wanted
+    if (any) {
+        uint64_t before[4], total[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            uint64_t exc;
+            const uint64_t inc = wave_scan(packed[x], &exc);
+            before[x] = exc;
+            if (lane == kWave - 1) sm.nth_scan[wave][x] = inc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            total[x] = 0u;
+            for (int w = 0; w < kWaves; ++w) {
+                const uint64_t t = sm.nth_scan[w][x];
+                if (w < wave) before[x] += t;
+                total[x] += t;
+            }
+        }
+        // token order is (load q, thread, element): the loads before q contribute their totals
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            if (!own[x]) continue;
+            const int n = sm.cut[x >> 1][x & 1].owner_take;
+            int base = 0;
+#pragma unroll
+            for (int q = 0; q < kLoads; ++q) {
+                const uint32_t mq = (masks[x] >> (8 * q)) & 0xFFu;
+                const int bq = base + (int)((before[x] >> (16 * q)) & 0xFFFFu);
+                if (bq < n && bq + __popc(mq) >= n) {
+                    // the (n - bq)-th set bit of mq
+                    uint32_t m = mq;
+                    for (int skip = n - bq - 1; skip > 0; --skip) m &= m - 1u;
+                    sm.eff[x >> 1][x & 1] = col_of(c0, q, __builtin_ctz(m));
+                }
+                base += (int)((total[x] >> (16 * q)) & 0xFFFFu);
+            }
+        }
+    }
 }
 
 // Processed probability of one element from the row's final statistics, id cuts and its mass
@@ -510,26 +569,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         sm.inv[threadIdx.x][0] = 1.0 / sm.rf[threadIdx.x].S;
         sm.inv[threadIdx.x][1] = 1.0 / sm.rf[threadIdx.x].Z;
     }
-    // this slice's id cut at each cut key; the owner of a histogram cut finds its id
-    int32_t* IC = reinterpret_cast<int32_t*>(f.ws + f.L.idcut) + b * 4;
-    for (int r = 0; r < 2; ++r) {
-        for (int c = 0; c < 2; ++c) {
-            const UnitCut uc = sm.cut[r][c];
-            int e = a.V - 1;
-            if (uc.key != 0u) {
-                if (uc.explicit_id >= 0) e = uc.explicit_id;
-                else if (slice < uc.owner) e = a.V - 1;
-                else if (slice > uc.owner) e = -1;
-                else e = local_nth_at_key(sm, r == 0 ? vq : vp, c0, a.V, uc.key, uc.owner_take);
-            }
-            if (threadIdx.x == 0) {
-                sm.eff[r][c] = e;
-                // the id cut the finaliser uses: explicit or none from slice 0, a histogram
-                // cut's from its owner
-                const bool writer = (uc.key == 0u || uc.explicit_id >= 0) ? slice == 0 : slice == uc.owner;
-                if (writer) IC[r * 2 + c] = e;
-            }
-        }
+    // this slice's id cut at each cut key; the owner of a histogram cut publishes its id for
+    // the finaliser (explicit cuts and no cut come from slice 0)
+    slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        const int r = threadIdx.x >> 1, c = threadIdx.x & 1;
+        const UnitCut uc = sm.cut[r][c];
+        const bool writer = (uc.key == 0u || uc.explicit_id >= 0) ? slice == 0 : slice == uc.owner;
+        if (writer) reinterpret_cast<int32_t*>(f.ws + f.L.idcut)[b * 4 + threadIdx.x] = sm.eff[r][c];
     }
     __syncthreads();  // 1 / S and 1 / Z
     build_tables(sm, two, slice);

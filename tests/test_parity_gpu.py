@@ -286,6 +286,26 @@ def test_fast_ties_and_large_sets():
     check_verify(w, tokens=_oracle_tokens(w), label="fast-ties")
 
 
+def test_fast_cut_on_signed_zeros():
+    # most of each row is +0 or -0, so the nucleus (and the downweighted set) end inside the
+    # zero key, whose elements the owner slice orders one by one
+    rng = np.random.default_rng(79)
+    B, K, V = 8, 2, 40000
+    t = np.where(rng.random((B, K + 1, V)) < 0.5, 0.0, -0.0).astype(np.float32)
+    d = np.where(rng.random((B, K, V)) < 0.5, -0.0, 0.0).astype(np.float32)
+    for arr in (t, d):
+        idx = rng.integers(0, V, (arr.shape[0], arr.shape[1], 12))
+        np.put_along_axis(arr, idx, 1.0, axis=2)
+        idx = rng.integers(0, V, (arr.shape[0], arr.shape[1], 3000))
+        np.put_along_axis(arr, idx, -1.0, axis=2)
+    T = np.full(B, 1.0, np.float32)
+    tk = rng.choice([0, 20000], B)
+    tp = rng.choice([0.3, 0.6, 0.9], B)
+    w = _work(synth.f32_to_bf16_bits(d), synth.f32_to_bf16_bits(t), synth.BF16, K, T, tk, tp, F=20, C=0.5)
+    check_verify(w, tokens=_oracle_tokens(w), label="fast-zero-cut")
+    check_verify(w, tokens=rng.integers(0, V, (B, K)), label="fast-zero-cut-random")
+
+
 def test_fast_special_values_and_fallback():
     rng = np.random.default_rng(78)
     B, K, V = 12, 2, 32768
