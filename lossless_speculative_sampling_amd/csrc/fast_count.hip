@@ -12,7 +12,7 @@ namespace fast {
 // request to be settled decides the request (no workgroup waits on another).
 // ------------------------------------------------------------------------------------------
 struct CountSmem {
-    double segm[kSegs];
+    double segm[2][kSegs];
     uint32_t segc[2][kSegs];
     union {
         uint32_t hraw[2][kHistRow];   // counting
@@ -35,7 +35,7 @@ struct CountSmem {
     uint32_t tau;
     int need;
     int ties;      // elements of the slice at key tau
-    uint32_t maxkey;
+    uint32_t maxkey[2];
     int last;
     int rare[2];
     double u_acc;  // the acceptance draw of the unit's position
@@ -237,18 +237,21 @@ __device__ __forceinline__ void local_rank(CountSmem& sm, int r, int c0, int s_t
     if (threadIdx.x == 0) sm.cnt_s[r] = cnt;
 }
 
-// Publishes the summary of row r (its element passes are done): largest logit, per-segment
-// counts and masses, specials, the fine counts, the candidate list and the token's rank.
-__device__ __forceinline__ void publish_row(const FastArgs& f, CountSmem& sm, int unit, int slice, int r,
-                                            const spec_params& prm) {
-    RowPart* P = part_of(f, unit, slice, r);
+// Publishes both rows' slice summaries (RowPart): the largest logit, per-segment counts and
+// masses relative to it, specials, candidate list, the draft token's rank and the fine counts.
+// The rows share a temperature, so where their maxima are close one exp serves a bin of both:
+// exp((z - m1) / T) = exp((z - m0) / T) * exp((m0 - m1) / T).
+__device__ __forceinline__ void publish_rows(const FastArgs& f, CountSmem& sm, int unit, int slice, bool two,
+                                             const spec_params& prm) {
+    const int rows = two ? 2 : 1;
     const double T = (double)prm.temperature;
     const double invT = inv_temperature(prm.temperature);
-    const int nsp = min((int)sm.n_sp[r], kSpecial);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    // largest key: the first non-empty segment, then its highest bin or special (wave 0)
-    if (wave == 0) {
+    // largest key of row r (wave r): the first non-empty segment, then its highest bin or special
+    if (wave < rows) {
+        const int r = wave;
+        const int nsp = min((int)sm.n_sp[r], kSpecial);
         const uint64_t ne = __ballot(lane < kSegs && sm.segc[r][lane] != 0u);
         uint32_t mk = 0;
         if (ne != 0) {
@@ -262,47 +265,75 @@ __device__ __forceinline__ void publish_row(const FastArgs& f, CountSmem& sm, in
                 mk = wave_max((lane < nsp && special_seg(k) == sg) ? k : 0u);
             }
         }
-        if (lane == 0) sm.maxkey = mk;
+        if (lane == 0) sm.maxkey[r] = mk;
     }
     __syncthreads();
-    const uint32_t mk = sm.maxkey;
-    const float m = mk ? key16_value(mk) : -__builtin_inff();
-    // per-group masses (relative to this slice's largest logit), one wave per group
+    float m[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const uint32_t mk = r < rows ? sm.maxkey[r] : 0u;
+        m[r] = mk ? key16_value(mk) : -__builtin_inff();
+    }
+    const double gap = ((double)m[0] - (double)m[1]) * invT;
+    const bool share = two && T > 0.0 && m[0] > -__builtin_inff() && m[1] > -__builtin_inff() && gap < 200.0 && gap > -200.0;
+    const double rho = share ? exp(gap) : 0.0;
+    // per-group masses, one wave per group
 #pragma unroll 1
     for (int g = wave; g < kGroups; g += kWaves) {
-        if (sm.segc[r][seg_of_group(g)] == 0u) {
-            if (lane == 0) sm.segm[seg_of_group(g)] = 0.0;
+        const int sg = seg_of_group(g);
+        const bool ne0 = sm.segc[0][sg] != 0u, ne1 = two && sm.segc[1][sg] != 0u;
+        if (!ne0 && !ne1) {
+            if (lane == 0) sm.segm[0][sg] = sm.segm[1][sg] = 0.0;
             continue;
         }
         const int bin = g * kGroup + lane;
-        const uint32_t c = sm.hist(r)[bin];
-        double ms = 0.0;
-        if (c != 0 && T > 0.0) ms = (double)c * mass_of(key16_value(bin_key(bin)), m, invT);
-        ms = wave_sum(ms);
-        if (lane == 0) sm.segm[seg_of_group(g)] = ms;
+        const uint32_t c0 = sm.hist(0)[bin], c1 = two ? sm.hist(1)[bin] : 0u;
+        const float z = key16_value(bin_key(bin));
+        double e0 = 0.0, e1 = 0.0;
+        if (T > 0.0) {
+            if (share) {
+                e0 = mass_of(z, m[0], invT);
+                e1 = e0 * rho;
+            } else {
+                if (ne0) e0 = mass_of(z, m[0], invT);
+                if (ne1) e1 = mass_of(z, m[1], invT);
+            }
+        }
+        const double ms0 = wave_sum(c0 != 0u ? (double)c0 * e0 : 0.0);
+        const double ms1 = wave_sum(c1 != 0u ? (double)c1 * e1 : 0.0);
+        if (lane == 0) {
+            sm.segm[0][sg] = ms0;
+            sm.segm[1][sg] = ms1;
+        }
     }
-    // the four special segments, one lane per special
-    if (wave == kWaves - 1) {
+    // the four special segments of row r (wave 7 - r), one lane per special
+    if (wave >= kWaves - rows) {
+        const int r = kWaves - 1 - wave;
+        const int nsp = min((int)sm.n_sp[r], kSpecial);
         int sg = -1;
         double ms = 0.0;
         if (lane < nsp) {
             const uint32_t k = sm.sp_key[r][lane];
             sg = special_seg(k);
-            if (T > 0.0) ms = mass_of(key16_value(k), m, invT);
+            if (T > 0.0) ms = mass_of(key16_value(k), m[r], invT);
         }
         const int sps[4] = {kSegHugePos, kSegTinyPos, kSegTinyNeg, kSegHugeNeg};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const double sx = wave_sum(sg == sps[x] ? ms : 0.0);
-            if (lane == 0) sm.segm[sps[x]] = sx;
+            if (lane == 0) sm.segm[r][sps[x]] = sx;
         }
     }
     __syncthreads();
-    if (wave == 0) {
-        const double S = wave_sum(lane < kSegs ? sm.segm[lane] : 0.0);
+    // the records: row r's header from wave r, the arrays from every thread
+    if (wave < rows) {
+        const int r = wave;
+        RowPart* P = part_of(f, unit, slice, r);
+        const int nsp = min((int)sm.n_sp[r], kSpecial);
+        const double S = wave_sum(lane < kSegs ? sm.segm[r][lane] : 0.0);
         const uint32_t nfin = wave_sum(lane < kSegs ? sm.segc[r][lane] : 0u);
         if (lane == 0) {
-            P->m = m;
+            P->m = m[r];
             P->flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u) | (sm.rare[r] ? 4u : 0u);
             P->n_finite = nfin;
             P->n_special = (uint32_t)nsp;
@@ -313,24 +344,27 @@ __device__ __forceinline__ void publish_row(const FastArgs& f, CountSmem& sm, in
             P->S = S;
         }
     }
-    for (int sg = threadIdx.x; sg < kSegs; sg += blockDim.x) {
-        P->seg_mass[sg] = sm.segm[sg];
-        P->seg_count[sg] = sm.segc[r][sg];
-    }
-    if ((int)threadIdx.x < nsp) {
-        P->sp_key[threadIdx.x] = sm.sp_key[r][threadIdx.x];
-        P->sp_id[threadIdx.x] = sm.sp_id[r][threadIdx.x];
-    }
-    if ((int)threadIdx.x < (int)sm.n_top[r]) {
-        P->top_key[threadIdx.x] = sm.top_key[r][threadIdx.x];
-        P->top_id[threadIdx.x] = sm.top_id[r][threadIdx.x];
-    }
-    // fine counts, two per dword (a slice holds < 65536 columns)
-    uint32_t* fine32 = reinterpret_cast<uint32_t*>(P->fine);
+    for (int r = 0; r < rows; ++r) {
+        RowPart* P = part_of(f, unit, slice, r);
+        const int nsp = min((int)sm.n_sp[r], kSpecial);
+        for (int sg = threadIdx.x; sg < kSegs; sg += blockDim.x) {
+            P->seg_mass[sg] = sm.segm[r][sg];
+            P->seg_count[sg] = sm.segc[r][sg];
+        }
+        if ((int)threadIdx.x < nsp) {
+            P->sp_key[threadIdx.x] = sm.sp_key[r][threadIdx.x];
+            P->sp_id[threadIdx.x] = sm.sp_id[r][threadIdx.x];
+        }
+        if ((int)threadIdx.x < (int)sm.n_top[r]) {
+            P->top_key[threadIdx.x] = sm.top_key[r][threadIdx.x];
+            P->top_id[threadIdx.x] = sm.top_id[r][threadIdx.x];
+        }
+        // fine counts, two per dword (a slice holds < 65536 columns)
+        uint32_t* fine32 = reinterpret_cast<uint32_t*>(P->fine);
 #pragma unroll 1
-    for (int i = threadIdx.x; i < kBins / 2; i += blockDim.x)
-        fine32[i] = (sm.hist(r)[2 * i] & 0xFFFFu) | (sm.hist(r)[2 * i + 1] << 16);
-    __syncthreads();  // segm is reused by the next row
+        for (int i = threadIdx.x; i < kBins / 2; i += blockDim.x)
+            fine32[i] = (sm.hist(r)[2 * i] & 0xFFFFu) | (sm.hist(r)[2 * i + 1] << 16);
+    }
 }
 
 // Counts this thread's columns of row r: every value goes to its bin or a padding word (one
@@ -603,8 +637,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
             if (holds_s) local_rank(sm, 1, c0, s_tok, vp);
         }
         __syncthreads();
-        publish_row(f, sm, unit, slice, 0, prm);
-        if (two) publish_row(f, sm, unit, slice, 1, prm);
+        publish_rows(f, sm, unit, slice, two, prm);
     }
 
     // ---- unit rendezvous: the last slice of the unit settles it ----
