@@ -239,8 +239,8 @@ __device__ __forceinline__ void local_rank(CountSmem& sm, int r, int c0, int s_t
 
 // Publishes both rows' slice summaries (RowPart): the largest logit, per-segment counts and
 // masses relative to it, specials, candidate list, the draft token's rank and the fine counts.
-// The rows share a temperature, so where their maxima are close one exp serves a bin of both:
-// exp((z - m1) / T) = exp((z - m0) / T) * exp((m0 - m1) / T).
+// Each row's masses are exp((z - m) / T) with its own maximum m (rows that differ by a shift
+// get identical masses); rows with the same maximum share the exps.
 __device__ __forceinline__ void publish_rows(const FastArgs& f, CountSmem& sm, int unit, int slice, bool two,
                                              const spec_params& prm) {
     const int rows = two ? 2 : 1;
@@ -274,9 +274,7 @@ __device__ __forceinline__ void publish_rows(const FastArgs& f, CountSmem& sm, i
         const uint32_t mk = r < rows ? sm.maxkey[r] : 0u;
         m[r] = mk ? key16_value(mk) : -__builtin_inff();
     }
-    const double gap = ((double)m[0] - (double)m[1]) * invT;
-    const bool share = two && T > 0.0 && m[0] > -__builtin_inff() && m[1] > -__builtin_inff() && gap < 200.0 && gap > -200.0;
-    const double rho = share ? exp(gap) : 0.0;
+    const bool share = two && m[0] == m[1];
     // per-group masses, one wave per group
 #pragma unroll 1
     for (int g = wave; g < kGroups; g += kWaves) {
@@ -292,8 +290,7 @@ __device__ __forceinline__ void publish_rows(const FastArgs& f, CountSmem& sm, i
         double e0 = 0.0, e1 = 0.0;
         if (T > 0.0) {
             if (share) {
-                e0 = mass_of(z, m[0], invT);
-                e1 = e0 * rho;
+                e0 = e1 = mass_of(z, m[0], invT);
             } else {
                 if (ne0) e0 = mass_of(z, m[0], invT);
                 if (ne1) e1 = mass_of(z, m[1], invT);

@@ -20,6 +20,7 @@ struct TieRole {
 };
 constexpr uint32_t kNoTie = 0xFFFFFFFFu;
 
+
 struct ResSmem {
     union {
         double tab[2][kHistRow];   // per-bin values of q and p' in the padded histogram layout
@@ -33,6 +34,9 @@ struct ResSmem {
     UnitRec urec;
     RowFinal rf[2];
     double inv[2][2];              // [row][1 / S, 1 / Z]
+    int glist[kGroups];            // groups whose entries need exps, ascending
+    int gcount;
+    uint64_t gzero[2];             // groups wholly below a row's cuts (entries 0)
     TieRole tie[2][3];             // [row][set boundary, top-k tie, top-p tie] this slice decides
     UnitCut cut[2][2];
     uint32_t flags[2];             // this slice's RowPart flags of each row
@@ -175,65 +179,108 @@ constexpr double kMarkQ = 1e300;    // in the target table: (q - p)+ and q becom
 constexpr double kMarkP = -1e300;   // in the draft table: (q - p)+ becomes huge
 constexpr double kMarkSeen = 1e299;
 
+// The groups of 64 bins whose table entries need exps: those between the lower of a row's
+// cuts and its maximum (a compact list, ascending), and per row the groups wholly below its
+// cuts, whose entries are 0.  Groups above a row's maximum hold none of its elements.  (Wave 0;
+// the caller synchronises.)
+__device__ __forceinline__ void table_groups(ResSmem& sm, bool two) {
+    const int lane = threadIdx.x & (kWave - 1);
+    bool need = false, z0 = false, z1 = false;
+    if (lane < kGroups) {
+        const uint32_t glo = bin_key(lane * kGroup), ghi = bin_key(lane * kGroup + kGroup - 1);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            if (r == 1 && !two) break;
+            const uint32_t klow = max(sm.cut[r][0].key, sm.cut[r][1].key);
+            const uint32_t kmax = key16(__float_as_uint(sm.rf[r].m) >> 16);
+            if (ghi >= klow && glo <= kmax) need = true;
+            else if (ghi < klow) (r == 0 ? z0 : z1) = true;
+        }
+    }
+    const uint64_t m = __ballot(need);
+    if (need) sm.glist[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+    const uint64_t m0 = __ballot(z0 && !need), m1 = __ballot(z1 && !need);
+    if (lane == 0) {
+        sm.gcount = __popcll(m);
+        sm.gzero[0] = m0;
+        sm.gzero[1] = m1;
+    }
+}
+
 // Per-bin values of both rows for this slice: q = e / S, p' = ((e / S) * f) / Z (as
 // final_prob), with every cut key resolved as this slice sees it.  Where this slice decides
 // elements of a bin one by one (it holds the last kept element at a cut key, or the draft
 // row's downweighted-set boundary) the entry holds the value of the earliest elements and a
 // tie role records where and how the later ones differ.  The padding words hold a marker when
-// the slice has values outside the exact bins.  One wave per group of 64 bins: groups wholly
-// below the cuts are 0 and groups above the row maximum hold no element, so only the groups
-// in between need their exps.
+// the slice has values outside the exact bins.
+__device__ __forceinline__ void group_entries(ResSmem& sm, bool two, int slice, int ownerF, int g, const double (&e)[2]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int bin = g * kGroup + lane;
+    const uint32_t key = bin_key(bin);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (r == 1 && !two) break;
+        const RowFinal& rf = sm.rf[r];
+        const UnitCut& ck = sm.cut[r][0];
+        const UnitCut& cp = sm.cut[r][1];
+        const uint32_t klow = max(ck.key, cp.key);
+        const uint32_t kmax = key16(__float_as_uint(rf.m) >> 16);
+        // zero never reaches its bins (the packed offsets send it to the padding words)
+        const bool real = g != kZeroGroup;
+        const bool own_k = real && ck.key != 0u && ck.owner == slice && key == ck.key;
+        const bool own_p = real && cp.key != 0u && cp.owner == slice && key == cp.key;
+        const bool own_F = real && r == 1 && ownerF == slice && key == rf.kF;
+        double v = 0.0;
+        if (key >= klow && key <= kmax && (key > ck.key || slice_keeps(ck, slice)) && (key > cp.key || slice_keeps(cp, slice))) {
+            const double pv = e[r] * sm.inv[r][0];
+            v = pv;
+            if (r == 1) {
+                const bool in_set = rf.nS > 0 && e[r] > 0.0 && (key > rf.kF || (key == rf.kF && slice <= ownerF));
+                v = (pv * (in_set ? rf.C : 1.0)) * sm.inv[r][1];
+            }
+            const uint32_t off = 8u * (uint32_t)(kHistLead + bin);
+            if (own_F) sm.tie[r][0] = TieRole{off, rf.idF, pv * sm.inv[r][1]};
+            if (own_k) sm.tie[r][1] = TieRole{off, sm.eff[r][0], 0.0};
+            if (own_p) sm.tie[r][2] = TieRole{off, sm.eff[r][1], 0.0};
+        }
+        sm.u.tab[r][kHistLead + bin] = v;
+    }
+}
+
+// Builds both tables: the listed groups two per wave and step (independent exp chains; rows
+// with the same maximum share their exps), then the zero groups and the padding words.  The
+// masses are exp((z - m) / T) with each row's own maximum, as final_prob forms them.
 __device__ __forceinline__ void build_tables(ResSmem& sm, bool two, int slice) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    uint32_t klow[2], kmax[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        klow[r] = max(sm.cut[r][0].key, sm.cut[r][1].key);
-        kmax[r] = key16(__float_as_uint(sm.rf[r].m) >> 16);
-    }
     const int ownerF = (two && sm.rf[1].nS > 0) ? sm.rf[1].idF / kSliceCols : -1;
+    const int n = sm.gcount;
+    const float m0 = sm.rf[0].m, m1 = sm.rf[1].m;
+    const bool share = two && m0 == m1;
+    const double invT = sm.rf[0].invT;
+    for (int i = wave; i < n; i += 2 * kWaves) {
+        const bool hb = i + kWaves < n;
+        const int ga = sm.glist[i], gb = hb ? sm.glist[i + kWaves] : ga;
+        const float za = key16_value(bin_key(ga * kGroup + lane)), zb = key16_value(bin_key(gb * kGroup + lane));
+        double ea[2], eb[2];
+        ea[0] = mass_of(za, m0, invT);
+        eb[0] = mass_of(zb, m0, invT);
+        if (share) {
+            ea[1] = ea[0];
+            eb[1] = eb[0];
+        } else if (two) {
+            ea[1] = mass_of(za, m1, invT);
+            eb[1] = mass_of(zb, m1, invT);
+        } else {
+            ea[1] = eb[1] = 0.0;
+        }
+        group_entries(sm, two, slice, ownerF, ga, ea);
+        if (hb) group_entries(sm, two, slice, ownerF, gb, eb);
+    }
+    const uint64_t z0 = sm.gzero[0], z1 = two ? sm.gzero[1] : 0ull;
     for (int g = wave; g < kGroups; g += kWaves) {
-        const uint32_t glo = bin_key(g * kGroup), ghi = bin_key(g * kGroup + kGroup - 1);
-        const bool need0 = ghi >= klow[0] && glo <= kmax[0];
-        const bool need1 = two && ghi >= klow[1] && glo <= kmax[1];
-        const int bin = g * kGroup + lane;
-        const uint32_t key = bin_key(bin);
-        // both rows' masses in one step (two independent exp chains)
-        double e0 = 0.0, e1 = 0.0;
-        if (need0 || need1) {
-            const float z = key16_value(key);
-            e0 = mass_of(z, sm.rf[0].m, sm.rf[0].invT);
-            if (two) e1 = mass_of(z, sm.rf[1].m, sm.rf[1].invT);
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (r == 1 && !two) break;
-            const RowFinal& rf = sm.rf[r];
-            const UnitCut& ck = sm.cut[r][0];
-            const UnitCut& cp = sm.cut[r][1];
-            const double e = r == 0 ? e0 : e1;
-            // zero never reaches its bins (the packed offsets send it to the padding words)
-            const bool real = g != kZeroGroup;
-            const bool own_k = real && ck.key != 0u && ck.owner == slice && key == ck.key;
-            const bool own_p = real && cp.key != 0u && cp.owner == slice && key == cp.key;
-            const bool own_F = real && r == 1 && ownerF == slice && key == rf.kF;
-            double v = 0.0;
-            if (key >= klow[r] && key <= kmax[r] && (key > ck.key || slice_keeps(ck, slice)) &&
-                (key > cp.key || slice_keeps(cp, slice))) {
-                const double pv = e * sm.inv[r][0];
-                v = pv;
-                if (r == 1) {
-                    const bool in_set = rf.nS > 0 && e > 0.0 && (key > rf.kF || (key == rf.kF && slice <= ownerF));
-                    v = (pv * (in_set ? rf.C : 1.0)) * sm.inv[r][1];
-                }
-                const uint32_t off = 8u * (uint32_t)(kHistLead + bin);
-                if (own_F) sm.tie[r][0] = TieRole{off, rf.idF, pv * sm.inv[r][1]};
-                if (own_k) sm.tie[r][1] = TieRole{off, sm.eff[r][0], 0.0};
-                if (own_p) sm.tie[r][2] = TieRole{off, sm.eff[r][1], 0.0};
-            }
-            if (r == 0 ? (need0 || ghi < klow[0]) : (need1 || ghi < klow[1])) sm.u.tab[r][kHistLead + bin] = v;
-        }
+        if ((z0 >> g) & 1ull) sm.u.tab[0][kHistLead + g * kGroup + lane] = 0.0;
+        if ((z1 >> g) & 1ull) sm.u.tab[1][kHistLead + g * kGroup + lane] = 0.0;
     }
     // padding words: values outside the exact bins
     if ((int)threadIdx.x < (two ? 4 : 2)) {
@@ -566,9 +613,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     }
     __syncthreads();
     if (threadIdx.x < 2) {
-        sm.inv[threadIdx.x][0] = 1.0 / sm.rf[threadIdx.x].S;
-        sm.inv[threadIdx.x][1] = 1.0 / sm.rf[threadIdx.x].Z;
+        const int r = threadIdx.x;
+        sm.inv[r][0] = 1.0 / sm.rf[r].S;
+        sm.inv[r][1] = 1.0 / sm.rf[r].Z;
     }
+    if (threadIdx.x >= kWave && threadIdx.x < 2 * kWave) table_groups(sm, two);
     // this slice's id cut at each cut key; the owner of a histogram cut publishes its id for
     // the finaliser (explicit cuts and no cut come from slice 0)
     slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);

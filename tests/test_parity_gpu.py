@@ -306,6 +306,21 @@ def test_fast_cut_on_signed_zeros():
     check_verify(w, tokens=rng.integers(0, V, (B, K)), label="fast-zero-cut-random")
 
 
+def test_fast_shifted_rows_have_empty_residual():
+    # draft logits = target logits + 3 exactly: both rows process to the same distribution, so
+    # every rejection (a token outside the kept set) leaves the residual exactly empty
+    rng = np.random.default_rng(80)
+    B, K, V = 16, 3, 20000
+    t = np.clip(np.round(rng.normal(-4, 2, (B, K + 1, V))), -12, 4).astype(np.float32)
+    d = (t[:, :K] + 3.0).astype(np.float32)
+    T = rng.choice([0.5, 1.0], B)
+    tk = rng.choice([0, 1, 50, 3000], B)
+    tp = rng.choice([0.2, 0.9, 1.0], B)
+    w = _work(synth.f32_to_bf16_bits(d), synth.f32_to_bf16_bits(t), synth.BF16, K, T, tk, tp)
+    o, _ = check_verify(w, tokens=rng.integers(0, V, (B, K)), label="fast-shifted")
+    assert (o.status & capi.ST_EMPTY_RESIDUAL).sum() > 0
+
+
 def test_fast_special_values_and_fallback():
     rng = np.random.default_rng(78)
     B, K, V = 12, 2, 32768
