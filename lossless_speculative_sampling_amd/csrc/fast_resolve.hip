@@ -207,41 +207,76 @@ __device__ __forceinline__ void table_groups(ResSmem& sm, bool two) {
     }
 }
 
+// What the table entries of one row depend on, read once into registers (the entries are
+// written to LDS, so values left in LDS would be re-read after every entry).
+struct RowTab {
+    uint32_t klow, kmax;      // below the cuts / above the maximum
+    uint32_t kk, kp;          // cut keys (0: none)
+    bool keep_k, keep_p;      // this slice keeps its elements at the cut keys
+    uint32_t own_k, own_p;    // cut keys this slice decides one by one (kNoTie: none)
+    uint32_t own_F;           // the set boundary key when this slice decides it (kNoTie: none)
+    uint32_t kF;
+    bool set_on, keep_F;      // the downweighted set exists / this slice's boundary ties are in it
+    int idF, eff_k, eff_p;
+    double inv_S, inv_Z, C;
+};
+
+__device__ __forceinline__ RowTab row_tab(const ResSmem& sm, int r, int slice, int ownerF) {
+    const RowFinal& rf = sm.rf[r];
+    const UnitCut& ck = sm.cut[r][0];
+    const UnitCut& cp = sm.cut[r][1];
+    RowTab t;
+    t.klow = max(ck.key, cp.key);
+    t.kmax = key16(__float_as_uint(rf.m) >> 16);
+    t.kk = ck.key;
+    t.kp = cp.key;
+    t.keep_k = slice_keeps(ck, slice);
+    t.keep_p = slice_keeps(cp, slice);
+    t.own_k = (ck.key != 0u && ck.owner == slice) ? ck.key : kNoTie;
+    t.own_p = (cp.key != 0u && cp.owner == slice) ? cp.key : kNoTie;
+    t.own_F = (r == 1 && ownerF == slice) ? rf.kF : kNoTie;
+    t.kF = rf.kF;
+    t.set_on = r == 1 && rf.nS > 0;
+    t.keep_F = slice <= ownerF;
+    t.idF = rf.idF;
+    t.eff_k = sm.eff[r][0];
+    t.eff_p = sm.eff[r][1];
+    t.inv_S = sm.inv[r][0];
+    t.inv_Z = sm.inv[r][1];
+    t.C = rf.C;
+    return t;
+}
+
 // Per-bin values of both rows for this slice: q = e / S, p' = ((e / S) * f) / Z (as
 // final_prob), with every cut key resolved as this slice sees it.  Where this slice decides
 // elements of a bin one by one (it holds the last kept element at a cut key, or the draft
 // row's downweighted-set boundary) the entry holds the value of the earliest elements and a
 // tie role records where and how the later ones differ.  The padding words hold a marker when
 // the slice has values outside the exact bins.
-__device__ __forceinline__ void group_entries(ResSmem& sm, bool two, int slice, int ownerF, int g, const double (&e)[2]) {
+__device__ __forceinline__ void group_entries(ResSmem& sm, bool two, const RowTab (&rt)[2], int g, const double (&e)[2]) {
     const int lane = threadIdx.x & (kWave - 1);
     const int bin = g * kGroup + lane;
     const uint32_t key = bin_key(bin);
+    // zero never reaches its bins (the packed offsets send it to the padding words)
+    const bool real = g != kZeroGroup;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         if (r == 1 && !two) break;
-        const RowFinal& rf = sm.rf[r];
-        const UnitCut& ck = sm.cut[r][0];
-        const UnitCut& cp = sm.cut[r][1];
-        const uint32_t klow = max(ck.key, cp.key);
-        const uint32_t kmax = key16(__float_as_uint(rf.m) >> 16);
-        // zero never reaches its bins (the packed offsets send it to the padding words)
-        const bool real = g != kZeroGroup;
-        const bool own_k = real && ck.key != 0u && ck.owner == slice && key == ck.key;
-        const bool own_p = real && cp.key != 0u && cp.owner == slice && key == cp.key;
-        const bool own_F = real && r == 1 && ownerF == slice && key == rf.kF;
+        const RowTab& t = rt[r];
         double v = 0.0;
-        if (key >= klow && key <= kmax && (key > ck.key || slice_keeps(ck, slice)) && (key > cp.key || slice_keeps(cp, slice))) {
-            const double pv = e[r] * sm.inv[r][0];
+        if (key >= t.klow && key <= t.kmax && (key > t.kk || t.keep_k) && (key > t.kp || t.keep_p)) {
+            const double pv = e[r] * t.inv_S;
             v = pv;
             if (r == 1) {
-                const bool in_set = rf.nS > 0 && e[r] > 0.0 && (key > rf.kF || (key == rf.kF && slice <= ownerF));
-                v = (pv * (in_set ? rf.C : 1.0)) * sm.inv[r][1];
+                const bool in_set = t.set_on && e[r] > 0.0 && (key > t.kF || (key == t.kF && t.keep_F));
+                v = (pv * (in_set ? t.C : 1.0)) * t.inv_Z;
             }
-            const uint32_t off = 8u * (uint32_t)(kHistLead + bin);
-            if (own_F) sm.tie[r][0] = TieRole{off, rf.idF, pv * sm.inv[r][1]};
-            if (own_k) sm.tie[r][1] = TieRole{off, sm.eff[r][0], 0.0};
-            if (own_p) sm.tie[r][2] = TieRole{off, sm.eff[r][1], 0.0};
+            if (real && (key == t.own_F || key == t.own_k || key == t.own_p)) {
+                const uint32_t off = 8u * (uint32_t)(kHistLead + bin);
+                if (key == t.own_F) sm.tie[r][0] = TieRole{off, t.idF, pv * t.inv_Z};
+                if (key == t.own_k) sm.tie[r][1] = TieRole{off, t.eff_k, 0.0};
+                if (key == t.own_p) sm.tie[r][2] = TieRole{off, t.eff_p, 0.0};
+            }
         }
         sm.u.tab[r][kHistLead + bin] = v;
     }
@@ -254,6 +289,7 @@ __device__ __forceinline__ void build_tables(ResSmem& sm, bool two, int slice) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int ownerF = (two && sm.rf[1].nS > 0) ? sm.rf[1].idF / kSliceCols : -1;
+    const RowTab rt[2] = {row_tab(sm, 0, slice, ownerF), row_tab(sm, 1, slice, ownerF)};
     const int n = sm.gcount;
     const float m0 = sm.rf[0].m, m1 = sm.rf[1].m;
     const bool share = two && m0 == m1;
@@ -274,8 +310,8 @@ __device__ __forceinline__ void build_tables(ResSmem& sm, bool two, int slice) {
         } else {
             ea[1] = eb[1] = 0.0;
         }
-        group_entries(sm, two, slice, ownerF, ga, ea);
-        if (hb) group_entries(sm, two, slice, ownerF, gb, eb);
+        group_entries(sm, two, rt, ga, ea);
+        if (hb) group_entries(sm, two, rt, gb, eb);
     }
     const uint64_t z0 = sm.gzero[0], z1 = two ? sm.gzero[1] : 0ull;
     for (int g = wave; g < kGroups; g += kWaves) {
