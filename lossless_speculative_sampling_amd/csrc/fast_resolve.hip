@@ -372,9 +372,10 @@ __device__ __forceinline__ double tab_at(const char* base, uint32_t off) {
     return *reinterpret_cast<const double*>(base + off);
 }
 
-// Residual of unit k over this slice's columns, per 512-column chunk: table lookups for every
-// element; a thread's 8 columns of one chunk that met a marker are recomputed exactly.
-__device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, int b, int slice, int c0, bool two,
+// Residual of unit k over this workgroup's half of the slice (its half of the loads), per
+// 512-column chunk: table lookups for every element; a thread's 8 columns of one chunk that
+// met a marker are recomputed exactly.
+__device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, int b, int slice, int half, int c0, bool two,
                                                const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads]) {
     const VerifyArgs& a = f.a;
     const int lane = threadIdx.x & (kWave - 1);
@@ -384,8 +385,10 @@ __device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, i
     double* out = reinterpret_cast<double*>(f.ws + f.L.chunks) + ((size_t)b * f.nS + slice) * kChunks;
     const Ties tiq = load_ties(sm, 0);
     const Ties tip = load_ties(sm, 1);
+    static_assert(kLoads % 2 == 0, "halves of a slice");
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
+        if (q / (kLoads / 2) != half) continue;
         double s = 0.0;
         const int cq = col_of(c0, q, 0);
         if (cq < a.V) {
@@ -594,37 +597,52 @@ __device__ __forceinline__ void general_request(const FastArgs& f, ResSmem& sm, 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_resolve_kernel(FastArgs f) {
     __shared__ ResSmem sm;
     const VerifyArgs& a = f.a;
-    // placement as in the count kernel (request b on XCD b % 8), R = max(nS, K + 1)
-    // workgroups per request; workgroup w of a request is slice w of unit k (residual) or
-    // unit w (general algorithm, cache rows)
-    const int R = max(f.nS, a.K + 1);
+    // placement as in the count kernel (request b on XCD b % 8), R = max(2 nS, K + 1)
+    // workgroups per request; workgroup w of a request is half w % 2 of slice w / 2 of unit k
+    // (residual) or unit w (general algorithm, cache rows)
+    const int R = max(2 * f.nS, a.K + 1);
     const int x = blockIdx.x % kXcd, l = blockIdx.x / kXcd;
     const int b = (l / R) * kXcd + x, w = l % R;
     if (b >= a.B) return;
+    // the request's decision and this unit's cache flag, loaded together
+    static_assert(sizeof(ReqFast) == 16, "one 16-byte record");
+    const u32x4 req = ldnt(reinterpret_cast<const u32x4*>(f.ws + f.L.reqs) + b);
+    const bool cache_here = f.cache && w <= a.K;
+    const int32_t cgen = cache_here ? ldnt(reinterpret_cast<const int32_t*>(f.ws + f.L.cache_gen) + b * (a.K + 1) + w) : 0;
     // outcome-cache rows the count kernel's candidate lists could not settle
-    if (f.cache && w <= a.K && reinterpret_cast<const int32_t*>(f.ws + f.L.cache_gen)[b * (a.K + 1) + w]) {
+    if (cgen) {
         CacheArgs c{a.draft, a.dtype, a.B, a.K, a.V, a.tokens, f.budget, f.fan, f.out_cache};
         cache_row(c, b, w, sm.u.cache.rs, sm.gst[0], sm.u.cache.cs);
         __syncthreads();
     }
-    const ReqFast* Rq = reinterpret_cast<const ReqFast*>(f.ws + f.L.reqs) + b;
-    const int mode = Rq->mode;
+    const int mode = (int)req[0];
     if (mode == 0) return;  // decided by the count kernel
     if (mode == 2) {
         if (w <= a.K) general_request(f, sm, b, w);
         return;
     }
-    // mode 1: the residual of unit k, slice w
-    const int k = Rq->k;
-    const int slice = w;
+    // mode 1: the residual of unit k, slice w / 2; each half of the slice's loads is summed by
+    // its own workgroup (both load the whole slice: the owner of a cut orders its ties over it)
+    const int k = (int)req[1];
+    const int slice = w >> 1, half = w & 1;
     if (slice >= f.nS) return;
     const int unit = b * (a.K + 1) + k;
-    const uint32_t status = Rq->status;
+    const uint32_t status = req[2];
     const bool two = k < a.K;
     const int c0 = slice * kSliceCols;
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)b * (a.K + 1) + k) * stride;
     const uint16_t* drow = two ? static_cast<const uint16_t*>(a.draft) + ((size_t)b * a.draft_rows + k) * stride : nullptr;
+    // the unit's record (row statistics and cuts) and this slice's flags are loaded before the
+    // slice itself, so that waiting for them does not wait for the slice (loads complete in order)
+    static_assert(offsetof(UnitFast, rp) == offsetof(UnitFast, rq) + sizeof(RowFinal), "rq, rp adjacent");
+    const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + unit;
+    constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
+    const int nrf = two ? 2 * kRf : kRf, ncut = two ? 4 * kCut : 2 * kCut;
+    const uint32_t rf_word = (int)threadIdx.x < nrf ? ldnt(reinterpret_cast<const uint32_t*>(&U->rq) + threadIdx.x) : 0u;
+    const uint32_t cut_word = (int)threadIdx.x < ncut ? ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + threadIdx.x) : 0u;
+    const uint32_t flag_word =
+        (threadIdx.x == 0 || (threadIdx.x == 1 && two)) ? ldnt(&part_of(f, unit, slice, threadIdx.x)->flags) : 0u;
     u32x4 vq[kLoads], vp[kLoads];
     load_slice(trow, c0, a.V, vq);
     if (two) {
@@ -633,20 +651,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
         for (int q = 0; q < kLoads; ++q) vp[q] = u32x4{0, 0, 0, 0};
     }
-    // the unit's record (row statistics and cuts) and this slice's flags
-    {
-        static_assert(offsetof(UnitFast, rp) == offsetof(UnitFast, rq) + sizeof(RowFinal), "rq, rp adjacent");
-        const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + unit;
-        constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(&U->rq);
-        const uint32_t* srcc = reinterpret_cast<const uint32_t*>(&U->cut[0][0]);
-        const int nrf = two ? 2 * kRf : kRf, ncut = two ? 4 * kCut : 2 * kCut;
-        if ((int)threadIdx.x < nrf) reinterpret_cast<uint32_t*>(&sm.rf[0])[threadIdx.x] = ldnt(src + threadIdx.x);
-        if ((int)threadIdx.x < ncut) reinterpret_cast<uint32_t*>(&sm.cut[0][0])[threadIdx.x] = ldnt(srcc + threadIdx.x);
-        if (!two && threadIdx.x >= kWave && threadIdx.x < kWave + 2) sm.cut[1][threadIdx.x - kWave] = UnitCut{0u, -1, 0, 0};
-        if (threadIdx.x < 2) sm.flags[threadIdx.x] = (threadIdx.x == 0 || two) ? ldnt(&part_of(f, unit, slice, threadIdx.x)->flags) : 0u;
-        if (threadIdx.x >= kWave && threadIdx.x < kWave + 6) sm.tie[(threadIdx.x - kWave) / 3][(threadIdx.x - kWave) % 3].off = kNoTie;
-    }
+    if ((int)threadIdx.x < nrf) reinterpret_cast<uint32_t*>(&sm.rf[0])[threadIdx.x] = rf_word;
+    if ((int)threadIdx.x < ncut) reinterpret_cast<uint32_t*>(&sm.cut[0][0])[threadIdx.x] = cut_word;
+    if (!two && threadIdx.x >= kWave && threadIdx.x < kWave + 2) sm.cut[1][threadIdx.x - kWave] = UnitCut{0u, -1, 0, 0};
+    if (threadIdx.x < 2) sm.flags[threadIdx.x] = flag_word;
+    if (threadIdx.x >= kWave && threadIdx.x < kWave + 6) sm.tie[(threadIdx.x - kWave) / 3][(threadIdx.x - kWave) % 3].off = kNoTie;
     __syncthreads();
     if (threadIdx.x < 2) {
         const int r = threadIdx.x;
@@ -662,13 +671,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         const int r = threadIdx.x >> 1, c = threadIdx.x & 1;
         const UnitCut uc = sm.cut[r][c];
         const bool writer = (uc.key == 0u || uc.explicit_id >= 0) ? slice == 0 : slice == uc.owner;
-        if (writer) reinterpret_cast<int32_t*>(f.ws + f.L.idcut)[b * 4 + threadIdx.x] = sm.eff[r][c];
+        if (writer && half == 0) reinterpret_cast<int32_t*>(f.ws + f.L.idcut)[b * 4 + threadIdx.x] = sm.eff[r][c];
     }
     __syncthreads();  // 1 / S and 1 / Z
     build_tables(sm, two, slice);
     __syncthreads();
-    residual_slice(f, sm, b, slice, c0, two, vq, vp);
-    if (!arrive_last(f, sm, b, f.nS)) return;
+    residual_slice(f, sm, b, slice, half, c0, two, vq, vp);
+    if (!arrive_last(f, sm, b, 2 * f.nS)) return;
     finalize_residual(f, sm, b, k, status);
 }
 

@@ -23,7 +23,7 @@ FastPlan fast_plan(int B, int K, int V) {
     p.units = B * (K + 1);
     const int reqs_per_xcd = (B + kXcd - 1) / kXcd;
     p.grid = kXcd * reqs_per_xcd * (K + 1) * p.nS;
-    p.grid_resolve = kXcd * reqs_per_xcd * max(p.nS, K + 1);
+    p.grid_resolve = kXcd * reqs_per_xcd * max(2 * p.nS, K + 1);  // two workgroups per slice
     p.ws_bytes = layout(B, p.units, p.nS).total;
     return p;
 }
