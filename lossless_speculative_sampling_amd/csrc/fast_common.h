@@ -138,6 +138,7 @@ struct UnitFast {       // written by the last slice of the unit in the count ke
     int32_t pad;
     RowFinal rq, rp;
     UnitCut cut[2][2];   // [row: target, draft][top-k, nucleus]
+    double u_res;        // the position's residual / bonus draw (Philox word 1)
 };
 
 struct ReqFast {        // written by the last unit of the request in the count kernel

@@ -39,6 +39,7 @@ struct CountSmem {
     int last;
     int rare[2];
     double u_acc;  // the acceptance draw of the unit's position
+    double u_res;  // its residual / bonus draw
 };
 
 // Per-segment element counts of both rows into sm.segc: a thread adds 8 bins, eight lanes a
@@ -479,6 +480,7 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
         U->accept = accept;
         U->status = status;
         U->fallback = fallback;
+        U->u_res = sm.u_res;
         if (param_ok) {
             for (int r = 0; r < (two ? 2 : 1); ++r) {
                 const RowView& rv = us.rv[r];
@@ -583,16 +585,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     const int s_tok = j < a.K ? a.tokens[(size_t)P.b * a.K + j] : -1;
     const bool tok_ok = j == a.K || (s_tok >= 0 && s_tok < a.V);
 
-    // the acceptance draw of position j, in the shadow of the first loads (wave 1 only; the
-    // empty asm keeps it here rather than where the settle step reads it)
-    double u_acc = 0.0;
+    // the draws of position j (acceptance, residual / bonus: words 0 and 1 of one Philox
+    // block), in the shadow of the first loads (wave 1 only; the empty asm keeps them here
+    // rather than where the settle step reads them)
+    double u_acc = 0.0, u_res = 0.0;
     if (param_ok) {  // (a request with bad parameters is reported without its summaries)
         u32x4 vq[kLoads], vp[kLoads];
         load_slice(trow, c0, a.V, vq);
         if (two) load_slice(drow, c0, a.V, vp);
-        if (j < a.K && threadIdx.x / kWave == 1) {
-            u_acc = uniform_at(a.seed, a.round, (uint64_t)P.b, (uint64_t)j, 0);
-            asm volatile("" ::"s"(u_acc));
+        if (threadIdx.x / kWave == 1) {
+            const Block4 x = philox4x64_10(a.round, (uint64_t)P.b, (uint64_t)j, 0, a.seed, 0);
+            u_acc = word_to_uniform(x.w[0]);
+            u_res = word_to_uniform(x.w[1]);
+            asm volatile("" ::"s"(u_acc), "s"(u_res));
         }
         for (int i = threadIdx.x; i < 2 * kHistRow / 4; i += blockDim.x)
             reinterpret_cast<u32x4*>(&sm.hraw[0][0])[i] = u32x4{0, 0, 0, 0};
@@ -648,7 +653,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     }
     __syncthreads();
     if (!sm.last) return;
-    if (threadIdx.x == kWave) sm.u_acc = u_acc;  // read after the settle step's first barrier
+    if (threadIdx.x == kWave) {  // read after the settle step's first barrier
+        sm.u_acc = u_acc;
+        sm.u_res = u_res;
+    }
     settle_unit(f, sm, P, prm, param_ok, two, s_tok, tok_ok);
 
     // ---- request rendezvous: the last unit of the request decides k ----

@@ -47,7 +47,8 @@ struct ResSmem {
     int32_t redi[kWaves];
     int last;
     int fc;
-    double ftarget, fbase;
+    int fscan[kWaves];
+    double ftarget, fbase, fW;
 };
 
 // This slice's id cut at every cut key of both rows (row r, cut c): V - 1 (keeps all), -1
@@ -438,37 +439,91 @@ __device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, i
     }
 }
 
-// The last slice of unit k: the chunk whose cumulative residual passes v * W, then the token
-// inside it by an exact scan (or, with no residual mass, inverse CDF of q_k).
-__device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm, int b, int k, uint32_t status) {
+// One block of up to blockDim.x consecutive columns of the inverse-CDF scan, each thread one
+// column with weight w: the first column whose cumulative weight (base + preceding weights +
+// its own) exceeds tgt, the last column with weight, and the block's total (two barriers: wave
+// scans, then the waves' totals).
+__device__ __forceinline__ void scan_block(ResSmem& sm, double w, int col, double base, double tgt, int* first, int* last,
+                                           double* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    double excl;
+    const double incl = wave_scan(w, &excl);
+    if (lane == kWave - 1) sm.redd[wave] = incl;
+    __syncthreads();
+    double before = base, all = 0.0;
+    for (int v = 0; v < kWaves; ++v) {
+        const double t = sm.redd[v];
+        if (v < wave) before += t;
+        all += t;
+    }
+    const uint64_t hit = __ballot(w > 0.0 && before + incl > tgt);
+    const uint64_t pos = __ballot(w > 0.0);
+    if (lane == 0) {
+        sm.scan[wave] = hit ? col - lane + first_lane(hit) : 0x7FFFFFFF;
+        sm.fscan[wave] = pos ? col - lane + last_lane(pos) : -1;
+    }
+    __syncthreads();
+    int f = 0x7FFFFFFF, l = -1;
+    for (int v = 0; v < kWaves; ++v) {
+        f = min(f, sm.scan[v]);
+        l = max(l, sm.fscan[v]);
+    }
+    *first = f;
+    *last = l;
+    *total = all;
+    __syncthreads();  // sm.redd / sm.scan / sm.fscan are reused by the next block
+}
+
+// The last workgroup of the request draws t* by inverse CDF over the residual (or q_K), in
+// token order: one wave picks the 512-column chunk from the chunk sums (each lane sums up to 8
+// consecutive chunks), then the workgroup scans that chunk's exact values.  u is the draw.
+__device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm, int b, int k, uint32_t status, double v) {
     const VerifyArgs& a = f.a;
     const int K = a.K;
     const int n = f.nS * kChunks;
     const double* ch = reinterpret_cast<const double*>(f.ws + f.L.chunks) + (size_t)b * f.nS * kChunks;
     const int32_t* IC = reinterpret_cast<const int32_t*>(f.ws + f.L.idcut) + b * 4;
-    const int c = threadIdx.x;
-    const double x = c < n ? ldnt(&ch[c]) : 0.0;
+    const int lane = threadIdx.x & (kWave - 1);
     const int idk_q = ldnt(&IC[0]), idp_q = ldnt(&IC[1]), idk_p = ldnt(&IC[2]), idp_p = ldnt(&IC[3]);
-    double W;
-    const double before = block_exclusive_scan<double>(x, sm.redd, &W);
-    const double v = uniform_at(a.seed, a.round, (uint64_t)b, (uint64_t)k, 1);
-    int mode;
-    if (W > 0.0) {
-        // the last chunk with mass whose preceding mass is <= v * W
-        const double target = v * W;
-        const int pick = block_max<int>((x > 0.0 && before <= target) ? c : -1, sm.redi);
-        if (pick == c) sm.fbase = before;
-        if (threadIdx.x == 0) {
-            sm.fc = pick;
-            sm.ftarget = target;
+    if (threadIdx.x < kWave) {
+        static_assert(kMaxSlices * kChunks <= 8 * kWave, "eight chunks per lane");
+        double x[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int i = lane * 8 + c;
+            x[c] = i < n ? ldnt(&ch[i]) : 0.0;
         }
-        mode = 1;
-    } else {
-        if (threadIdx.x == 0) sm.ftarget = v;
-        status |= kStEmptyResidual;
-        mode = 2;
+        double mine = 0.0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) mine += x[c];
+        double before;
+        const double incl = wave_scan(mine, &before);
+        const double W = wave_bcast(incl, kWave - 1);
+        const double target = v * W;
+        // the last chunk with mass whose preceding mass is <= target
+        int pick = -1;
+        double pbase = 0.0, run = before;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if (x[c] > 0.0 && run <= target) {
+                pick = lane * 8 + c;
+                pbase = run;
+            }
+            run += x[c];
+        }
+        const int best = wave_max(pick);
+        if (pick == best && best >= 0) sm.fbase = pbase;
+        if (lane == 0) {
+            sm.fc = best;
+            sm.ftarget = W > 0.0 ? target : v;
+            sm.fW = W;
+        }
     }
     __syncthreads();
+    const double W = sm.fW;
+    const int mode = W > 0.0 ? 1 : 2;
+    if (mode == 2) status |= kStEmptyResidual;
     const RowFinal& rq = sm.rf[0];
     const RowFinal& rp = sm.rf[1];
     const size_t stride = (size_t)a.V;
@@ -478,9 +533,7 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
     int lo, hi;
     double base;
     if (mode == 1) {
-        const int cc = sm.fc;
-        const int slice = cc / kChunks, within = cc % kChunks;
-        lo = slice * kSliceCols + (within / kWaves) * (kThreads * 8) + (within % kWaves) * kChunkCols;
+        lo = (sm.fc / kChunks) * kSliceCols + (sm.fc % kChunks) * kChunkCols;
         hi = min(lo + kChunkCols, a.V);
         base = sm.fbase;
     } else {
@@ -508,19 +561,16 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
                 w = qv;
             }
         }
+        int fb, lb;
         double tot;
-        const double bef = block_exclusive_scan<double>(w, sm.redd, &tot);
-        const double cum = base + bef + w;
-        if (w > 0.0 && cum > tgt) best = min(best, col);
-        if (w > 0.0) last = max(last, col);
+        scan_block(sm, w, col, base, tgt, &fb, &lb, &tot);
+        last = max(last, lb);
         base += tot;
-        const int bmin = block_min<int>(best, sm.redi);
-        if (bmin != 0x7FFFFFFF) {
-            best = bmin;
+        if (fb != 0x7FFFFFFF) {
+            best = fb;
             break;
         }
     }
-    last = block_max<int>(last, sm.redi);
     if (threadIdx.x == 0) {
         a.out_k[b] = k;
         a.out_t[b] = best != 0x7FFFFFFF ? best : last;
@@ -643,6 +693,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const uint32_t cut_word = (int)threadIdx.x < ncut ? ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + threadIdx.x) : 0u;
     const uint32_t flag_word =
         (threadIdx.x == 0 || (threadIdx.x == 1 && two)) ? ldnt(&part_of(f, unit, slice, threadIdx.x)->flags) : 0u;
+    // the draw for t*, taken by the count kernel with the position's acceptance draw (wave 0,
+    // which picks the chunk, keeps it)
+    const double u_res = threadIdx.x < kWave ? ldnt(&U->u_res) : 0.0;
     u32x4 vq[kLoads], vp[kLoads];
     load_slice(trow, c0, a.V, vq);
     if (two) {
@@ -678,7 +731,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     __syncthreads();
     residual_slice(f, sm, b, slice, half, c0, two, vq, vp);
     if (!arrive_last(f, sm, b, 2 * f.nS)) return;
-    finalize_residual(f, sm, b, k, status);
+    finalize_residual(f, sm, b, k, status, u_res);
 }
 
 void launch_resolve(const FastArgs& f, int grid, hipStream_t stream) {
