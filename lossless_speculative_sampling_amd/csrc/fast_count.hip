@@ -19,6 +19,7 @@ struct CountSmem {
         UnitSmem us;                  // settling the unit (the histograms are published by then)
     };
     __device__ __forceinline__ uint32_t* hist(int r) { return &hraw[r][kHistLead]; }
+    __device__ __forceinline__ const uint32_t* hist(int r) const { return &hraw[r][kHistLead]; }
     uint32_t sp_key[2][kSpecial];
     int32_t sp_id[2][kSpecial];
     uint32_t n_sp[2];
@@ -32,9 +33,6 @@ struct CountSmem {
     double redd[kWaves];
     int32_t redi[kWaves];
     uint32_t s_bits[2];
-    uint32_t tau;
-    int need;
-    int ties;      // elements of the slice at key tau
     uint32_t maxkey[2];
     int last;
     int rare[2];
@@ -69,22 +67,23 @@ __device__ __forceinline__ void seg_counts(CountSmem& sm, int rows) {
     }
 }
 
-// Wave 0: the key of the L-th element (token order) of row r in this slice, and how many
-// elements at that key are taken, into sm.tau / sm.need; (0, 0) when the slice holds fewer
-// than L finite elements.  Scans the segment counts, then the 64 bins of the crossing group,
-// or the specials of the crossing segment.
-__device__ __forceinline__ void local_threshold(CountSmem& sm, int r, int L) {
+// The key of the L-th element (token order) of row r in this slice, how many elements at that
+// key are taken and how many the slice holds at it; (0, 0, 0) when the slice holds fewer than
+// L finite elements.  Scans the segment counts, then the 64 bins of the crossing group, or the
+// specials of the crossing segment.  Every wave computes it for itself (uniform results), so
+// no barrier is needed before the element pass.
+struct Threshold {
+    uint32_t tau;
+    int need, ties;
+};
+__device__ __forceinline__ Threshold local_threshold(const CountSmem& sm, int r, int L) {
     const int lane = threadIdx.x & (kWave - 1);
-    if (lane == 0) {
-        sm.tau = 0u;
-        sm.need = 0;
-        sm.ties = 0;
-    }
+    Threshold th{0u, 0, 0};
     const int c = lane < kSegs ? (int)sm.segc[r][lane] : 0;
     int cex;
     const int cin = wave_scan(c, &cex);
     const uint64_t hit = __ballot(lane < kSegs && cin >= L);
-    if (hit == 0) return;
+    if (hit == 0) return th;
     const int sg = first_lane(hit);
     const int rem = L - wave_bcast(cex, sg);
     const int g = group_of_seg(sg);
@@ -94,11 +93,9 @@ __device__ __forceinline__ void local_threshold(CountSmem& sm, int r, int L) {
         int nex;
         const int nin = wave_scan(n, &nex);
         const int i = first_lane(__ballot(nin >= rem));
-        if (lane == i) {
-            sm.tau = bin_key(bin);
-            sm.need = rem - nex;
-            sm.ties = n;
-        }
+        th.tau = bin_key(wave_bcast(bin, i));
+        th.need = rem - wave_bcast(nex, i);
+        th.ties = wave_bcast(n, i);
     } else {
         const int nsp = min((int)sm.n_sp[r], kSpecial);
         uint32_t k = 0;
@@ -114,24 +111,26 @@ __device__ __forceinline__ void local_threshold(CountSmem& sm, int r, int L) {
             gt += k2 > k ? 1 : 0;
             eq += k2 == k ? 1 : 0;
         }
-        if (mine && gt < rem && gt + eq >= rem) {
-            sm.tau = k;
-            sm.need = rem - gt;
-            sm.ties = eq;
+        const uint64_t at = __ballot(mine && gt < rem && gt + eq >= rem);
+        if (at != 0) {
+            const int x = first_lane(at);
+            th.tau = wave_bcast(k, x);
+            th.need = rem - wave_bcast(gt, x);
+            th.ties = wave_bcast(eq, x);
         }
     }
+    return th;
 }
 
 // The first L elements (token order: key desc, id asc) of row r in this slice, sorted, into
-// sm.top_key[r] / sm.top_id[r]; sm.n_top[r] gets their number.
+// sm.top_key[r] / sm.top_id[r]; sm.n_top[r] gets their number.  sm.n_top[r] starts at 0 (the
+// caller clears it before an earlier barrier) and the caller synchronises afterwards.
 __device__ __forceinline__ void local_top(CountSmem& sm, int r, int L, int c0, int V, const u32x4 (&v)[kLoads]) {
-    if (threadIdx.x < kWave) local_threshold(sm, r, L);
-    if (threadIdx.x == 0) sm.n_top[r] = 0;
-    __syncthreads();
-    const uint32_t tau = sm.tau;
-    const int need = sm.need;
+    const Threshold th = local_threshold(sm, r, L);
+    const uint32_t tau = th.tau;
+    const int need = th.need;
     // when every element at tau is needed the ties need no ordering
-    const bool all_ties = sm.ties == need;
+    const bool all_ties = th.ties == need;
     // pairs of values whose larger order key reaches tau - 1 (-0 has the packed key 0x7FFF,
     // one below +0) are examined one by one; the rest are skipped two at a time
     const uint16_t lo_t = tau > 0u ? (uint16_t)(tau - 1u) : (uint16_t)0;
@@ -164,66 +163,84 @@ __device__ __forceinline__ void local_top(CountSmem& sm, int r, int L, int c0, i
     __syncthreads();
     int base = min((int)sm.n_top[r], kTop);
     int need_left = all_ties ? 0 : need;
-    // then the first `need` elements at tau in token order (uniform loop)
-    for (int q = 0; q < kLoads && need_left > 0; ++q) {
-        const uint32_t mq = (tiemask >> (q * 8)) & 0xFFu;
-        int total;
-        const int before = block_exclusive_scan<int>(__popc(mq), sm.scan, &total);
-        int k = 0;
-        for (int e = 0; e < 8; ++e) {
-            if (!(mq & (1u << e))) continue;
-            const int rank = before + k++;
-            const int slot = base + rank;
-            if (rank < need_left && slot < kTop) {
-                sm.top_key[r][slot] = tau;
-                sm.top_id[r][slot] = col_of(c0, q, e);
+    // then the first `need` elements at tau in token order (uniform loop; rare)
+    if (need_left > 0) {
+        for (int q = 0; q < kLoads && need_left > 0; ++q) {
+            const uint32_t mq = (tiemask >> (q * 8)) & 0xFFu;
+            int total;
+            const int before = block_exclusive_scan<int>(__popc(mq), sm.scan, &total);
+            int k = 0;
+            for (int e = 0; e < 8; ++e) {
+                if (!(mq & (1u << e))) continue;
+                const int rank = before + k++;
+                const int slot = base + rank;
+                if (rank < need_left && slot < kTop) {
+                    sm.top_key[r][slot] = tau;
+                    sm.top_id[r][slot] = col_of(c0, q, e);
+                }
             }
+            const int took = min(total, need_left);
+            base += took;
+            need_left -= took;
         }
-        const int took = min(total, need_left);
-        base += took;
-        need_left -= took;
+        __syncthreads();
     }
-    __syncthreads();
-    const int n = min(base, kTop);
-    // sort: key desc, id asc (rank by counting)
-    uint32_t mk = 0;
-    int mi = 0, rank = 0;
-    if ((int)threadIdx.x < n) {
-        mk = sm.top_key[r][threadIdx.x];
-        mi = sm.top_id[r][threadIdx.x];
-        for (int i = 0; i < n; ++i) {
-            const uint32_t k2 = sm.top_key[r][i];
-            const int i2 = sm.top_id[r][i];
-            rank += (k2 > mk || (k2 == mk && i2 < mi)) ? 1 : 0;
+    // sort (key desc, id asc): wave 0 ranks each entry against the others through lane reads
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const int n = min(base, kTop);
+        const bool live = lane < n;
+        const uint32_t mk = live ? sm.top_key[r][lane] : 0u;
+        const int mi = live ? sm.top_id[r][lane] : 0;
+        const uint64_t ord = ((uint64_t)mk << 32) | (uint32_t)~mi;  // ids are non-negative
+        int rank = 0;
+        for (int y = 0; y < n; y += 4) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) rank += wave_bcast(ord, y + d) > ord ? 1 : 0;  // lanes past n: key 0
         }
+        if (live) {
+            sm.top_key[r][rank] = mk;
+            sm.top_id[r][rank] = mi;
+        }
+        if (lane == 0) sm.n_top[r] = (uint32_t)n;
     }
-    __syncthreads();
-    if ((int)threadIdx.x < n) {
-        sm.top_key[r][rank] = mk;
-        sm.top_id[r][rank] = mi;
-    }
-    if (threadIdx.x == 0) sm.n_top[r] = (uint32_t)n;
-    __syncthreads();
 }
 
-// Elements of row r in this slice with the draft token's key that precede the token (token
-// order): all of them when the slice lies before the token's slice, none after it.
-__device__ __forceinline__ void local_rank(CountSmem& sm, int r, int c0, int s_tok, const u32x4 (&v)[kLoads]) {
-    const uint32_t h_s = sm.s_bits[r];
-    uint32_t cnt = 0;
+// Elements of each row in this slice with the draft token's key that precede the token (token
+// order): all of them when the slice lies before the token's slice (a histogram or specials
+// lookup, no element pass), those left of the token in its own slice (one element pass per
+// row, both rows' counts packed into one workgroup sum).  Callers synchronise.
+__device__ __forceinline__ void local_ranks(CountSmem& sm, bool two, int c0, int s_tok, const u32x4 (&vq)[kLoads],
+                                            const u32x4 (&vp)[kLoads]) {
+    const int rows = two ? 2 : 1;
     if (s_tok >= c0 + kSliceCols) {
-        // the whole slice precedes the token: the count of its key (bin or special)
-        if ((h_s & 0x7FFFu) < 0x7F80u) {
-            const uint32_t ks = key16(h_s);
-            if (key_is_binned(ks)) {
-                cnt = threadIdx.x == 0 ? sm.hist(r)[key_bin(ks)] : 0u;
-            } else {
-                const int nsp = min((int)sm.n_sp[r], kSpecial);
-                cnt = ((int)threadIdx.x < nsp && sm.sp_key[r][threadIdx.x] == ks) ? 1u : 0u;
+        const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+        if (wave < rows) {
+            const int r = wave;
+            const uint32_t h_s = sm.s_bits[r];
+            uint32_t cnt = 0;
+            if ((h_s & 0x7FFFu) < 0x7F80u) {
+                const uint32_t ks = key16(h_s);
+                if (key_is_binned(ks)) {
+                    cnt = sm.hist(r)[key_bin(ks)];
+                } else {
+                    const int nsp = min((int)sm.n_sp[r], kSpecial);
+                    cnt = (uint32_t)__popcll(__ballot(lane < nsp && sm.sp_key[r][lane] == ks));
+                }
             }
+            if (lane == 0) sm.cnt_s[r] = cnt;
         }
-    } else if (s_tok >= c0 && (h_s & 0x7FFFu) < 0x7F80u) {
+        return;
+    }
+    uint32_t packed = 0;  // row 0 in the low half, row 1 in the high half (each < 2^16)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (r == 1 && !two) break;
+        const uint32_t h_s = sm.s_bits[r];
+        if ((h_s & 0x7FFFu) >= 0x7F80u) continue;
         const uint32_t ks = key16(h_s);
+        const u32x4(&v)[kLoads] = r == 0 ? vq : vp;
+        uint32_t cnt = 0;
 #pragma unroll
         for (int q = 0; q < kLoads; ++q)
 #pragma unroll
@@ -233,9 +250,10 @@ __device__ __forceinline__ void local_rank(CountSmem& sm, int r, int c0, int s_t
                 const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
                 cnt += (col < s_tok && (h & 0x7FFFu) < 0x7F80u && key16(h) == ks) ? 1u : 0u;
             }
+        packed += cnt << (16 * r);
     }
-    cnt = block_sum<uint32_t>(cnt, reinterpret_cast<uint32_t*>(sm.redi));
-    if (threadIdx.x == 0) sm.cnt_s[r] = cnt;
+    packed = block_sum<uint32_t>(packed, reinterpret_cast<uint32_t*>(sm.redi));
+    if (threadIdx.x < (unsigned)rows) sm.cnt_s[threadIdx.x] = (packed >> (16 * threadIdx.x)) & 0xFFFFu;
 }
 
 // Publishes both rows' slice summaries (RowPart): the largest logit, per-segment counts and
@@ -633,11 +651,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
         const bool holds_s = j < a.K && tok_ok && s_tok >= c0;  // at or after this slice: count its key
         const int want_q = list_len(a, prm, false), want_p = two ? draft_list_len(f, prm, j) : 0;
         if (want_q > 0) local_top(sm, 0, want_q, c0, a.V, vq);
-        if (holds_s) local_rank(sm, 0, c0, s_tok, vq);
-        if (two) {
-            if (want_p > 0) local_top(sm, 1, want_p, c0, a.V, vp);
-            if (holds_s) local_rank(sm, 1, c0, s_tok, vp);
-        }
+        if (two && want_p > 0) local_top(sm, 1, want_p, c0, a.V, vp);
+        if (holds_s) local_ranks(sm, two, c0, s_tok, vq, vp);
         __syncthreads();
         publish_rows(f, sm, unit, slice, two, prm);
     }
