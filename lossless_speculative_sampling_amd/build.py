@@ -20,11 +20,33 @@ HIPCC_FLAGS = [
     # packed fp32 instructions stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    # per-kernel register report, checked below
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 
 
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def vgpr_spills(report: str) -> dict[str, int]:
+    """Kernels whose VGPRs spill to scratch, from the compiler's resource-usage remarks.
+
+    A spilled vector register is stored under the execution mask of the point where the
+    compiler places the spill; when that point lies inside a branch taken by only some waves
+    or lanes, the others lose the value.  The kernels here are written to fit their register
+    budgets, so any spill is treated as a build error.
+    """
+    spills: dict[str, int] = {}
+    name = None
+    for line in report.splitlines():
+        if "remark: Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+        elif "remark:     VGPRs Spill:" in line and name is not None:
+            n = int(line.split("VGPRs Spill:")[1].split("[")[0])
+            if n:
+                spills[name] = n
+    return spills
 
 
 def build_library(verbose: bool = False) -> str:
@@ -35,9 +57,13 @@ def build_library(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"
-    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
+    out = res.stdout + res.stderr
+    msg = "\n".join(l for l in out.splitlines() if noise not in l and "remark:" not in l and not l.startswith(" "))
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msg}")
+    spills = vgpr_spills(out)
+    if spills:
+        raise RuntimeError(f"vector registers spill to scratch in: {spills}")
     if verbose and msg.strip():
         print(msg)
     os.replace(tmp, LIB)

@@ -608,9 +608,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     // rather than where the settle step reads them)
     double u_acc = 0.0, u_res = 0.0;
     if (param_ok) {  // (a request with bad parameters is reported without its summaries)
+        // (without a draft row the second set re-reads the target and goes unused: unconditional
+        // loads keep the compiler's waits exact)
         u32x4 vq[kLoads], vp[kLoads];
         load_slice(trow, c0, a.V, vq);
-        if (two) load_slice(drow, c0, a.V, vp);
+        load_slice(two ? drow : trow, c0, a.V, vp);
         if (threadIdx.x / kWave == 1) {
             const Block4 x = philox4x64_10(a.round, (uint64_t)P.b, (uint64_t)j, 0, a.seed, 0);
             u_acc = word_to_uniform(x.w[0]);
@@ -624,16 +626,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
             sm.flags[threadIdx.x] = 0;
             sm.neginf[threadIdx.x] = 0;
         }
-        // the rows' values at the draft token (every slice counts the token's key); one thread
-        // writes both words, zero without a token
-        if (threadIdx.x == kWave) {
-            const bool has = j < a.K && tok_ok;
-            sm.s_bits[0] = has ? trow[s_tok] : 0u;
-            sm.s_bits[1] = has ? drow[s_tok] : 0u;
+        // the rows' values at the draft token (every slice counts the token's key), zero without
+        // a token: loaded after the slice, stored once the counts have waited for it anyway
+        uint32_t sb0 = 0u, sb1 = 0u;
+        if (threadIdx.x == kWave && j < a.K && tok_ok) {
+            sb0 = trow[s_tok];
+            sb1 = drow[s_tok];
         }
         __syncthreads();
         count_row(sm, 0, c0, a.V, vq);
         if (two) count_row(sm, 1, c0, a.V, vp);
+        if (threadIdx.x == kWave) {
+            sm.s_bits[0] = sb0;
+            sm.s_bits[1] = sb1;
+        }
         __syncthreads();
         const bool rare0 = (sm.hraw[0][kHistLead - 1] | sm.hraw[0][kHistLead + kBins]) != 0;
         const bool rare1 = two && (sm.hraw[1][kHistLead - 1] | sm.hraw[1][kHistLead + kBins]) != 0;

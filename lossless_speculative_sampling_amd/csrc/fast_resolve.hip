@@ -49,6 +49,7 @@ struct ResSmem {
     int fc;
     int fscan[kWaves];
     double ftarget, fbase, fW;
+    double u_res;                  // the draw for t*
 };
 
 // This slice's id cut at every cut key of both rows (row r, cut c): V - 1 (keeps all), -1
@@ -218,7 +219,7 @@ struct RowTab {
     uint32_t own_F;           // the set boundary key when this slice decides it (kNoTie: none)
     uint32_t kF;
     bool set_on, keep_F;      // the downweighted set exists / this slice's boundary ties are in it
-    int idF, eff_k, eff_p;
+    int idF;
     double inv_S, inv_Z, C;
 };
 
@@ -240,8 +241,6 @@ __device__ __forceinline__ RowTab row_tab(const ResSmem& sm, int r, int slice, i
     t.set_on = r == 1 && rf.nS > 0;
     t.keep_F = slice <= ownerF;
     t.idF = rf.idF;
-    t.eff_k = sm.eff[r][0];
-    t.eff_p = sm.eff[r][1];
     t.inv_S = sm.inv[r][0];
     t.inv_Z = sm.inv[r][1];
     t.C = rf.C;
@@ -275,8 +274,8 @@ __device__ __forceinline__ void group_entries(ResSmem& sm, bool two, const RowTa
             if (real && (key == t.own_F || key == t.own_k || key == t.own_p)) {
                 const uint32_t off = 8u * (uint32_t)(kHistLead + bin);
                 if (key == t.own_F) sm.tie[r][0] = TieRole{off, t.idF, pv * t.inv_Z};
-                if (key == t.own_k) sm.tie[r][1] = TieRole{off, t.eff_k, 0.0};
-                if (key == t.own_p) sm.tie[r][2] = TieRole{off, t.eff_p, 0.0};
+                if (key == t.own_k) sm.tie[r][1] = TieRole{off, 0, 0.0};  // threshold: the id cut, below
+                if (key == t.own_p) sm.tie[r][2] = TieRole{off, 0, 0.0};
             }
         }
         sm.u.tab[r][kHistLead + bin] = v;
@@ -340,7 +339,8 @@ __device__ __forceinline__ Ties load_ties(const ResSmem& sm, int r) {
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
         t.off[x] = __builtin_amdgcn_readfirstlane(sm.tie[r][x].off);
-        t.thr[x] = __builtin_amdgcn_readfirstlane(sm.tie[r][x].thr);
+        // the boundary's threshold is its id; a cut's is this slice's id cut at the cut key
+        t.thr[x] = __builtin_amdgcn_readfirstlane(x == 0 ? sm.tie[r][x].thr : sm.eff[r][x - 1]);
         const double alt = sm.tie[r][x].alt;
         t.alt[x] = __hiloint2double(__builtin_amdgcn_readfirstlane(__double2hiint(alt)),
                                     __builtin_amdgcn_readfirstlane(__double2loint(alt)));
@@ -512,7 +512,7 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
             }
             run += x[c];
         }
-        const int best = wave_max(pick);
+        const int best = max(wave_max(pick), 0);  // (W > 0 always picks a chunk; a guard for NaN sums)
         if (pick == best && best >= 0) sm.fbase = pbase;
         if (lane == 0) {
             sm.fc = best;
@@ -693,21 +693,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const uint32_t cut_word = (int)threadIdx.x < ncut ? ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + threadIdx.x) : 0u;
     const uint32_t flag_word =
         (threadIdx.x == 0 || (threadIdx.x == 1 && two)) ? ldnt(&part_of(f, unit, slice, threadIdx.x)->flags) : 0u;
-    // the draw for t*, taken by the count kernel with the position's acceptance draw (wave 0,
-    // which picks the chunk, keeps it)
-    const double u_res = threadIdx.x < kWave ? ldnt(&U->u_res) : 0.0;
+    // the draw for t*, taken by the count kernel with the position's acceptance draw
+    const double u_res = threadIdx.x == 0 ? ldnt(&U->u_res) : 0.0;
+    // (without a draft row the second set re-reads the target and goes unused: unconditional
+    // loads keep the waits above exact)
     u32x4 vq[kLoads], vp[kLoads];
     load_slice(trow, c0, a.V, vq);
-    if (two) {
-        load_slice(drow, c0, a.V, vp);
-    } else {
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q) vp[q] = u32x4{0, 0, 0, 0};
-    }
+    load_slice(two ? drow : trow, c0, a.V, vp);
     if ((int)threadIdx.x < nrf) reinterpret_cast<uint32_t*>(&sm.rf[0])[threadIdx.x] = rf_word;
     if ((int)threadIdx.x < ncut) reinterpret_cast<uint32_t*>(&sm.cut[0][0])[threadIdx.x] = cut_word;
     if (!two && threadIdx.x >= kWave && threadIdx.x < kWave + 2) sm.cut[1][threadIdx.x - kWave] = UnitCut{0u, -1, 0, 0};
     if (threadIdx.x < 2) sm.flags[threadIdx.x] = flag_word;
+    if (threadIdx.x == 0) sm.u_res = u_res;
     if (threadIdx.x >= kWave && threadIdx.x < kWave + 6) sm.tie[(threadIdx.x - kWave) / 3][(threadIdx.x - kWave) % 3].off = kNoTie;
     __syncthreads();
     if (threadIdx.x < 2) {
@@ -716,6 +713,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         sm.inv[r][1] = 1.0 / sm.rf[r].Z;
     }
     if (threadIdx.x >= kWave && threadIdx.x < 2 * kWave) table_groups(sm, two);
+    __syncthreads();  // 1 / S and 1 / Z, the group list
+    // the tables need no column of the slice: they are built while its loads are in flight
+    build_tables(sm, two, slice);
     // this slice's id cut at each cut key; the owner of a histogram cut publishes its id for
     // the finaliser (explicit cuts and no cut come from slice 0)
     slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);
@@ -726,12 +726,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         const bool writer = (uc.key == 0u || uc.explicit_id >= 0) ? slice == 0 : slice == uc.owner;
         if (writer && half == 0) reinterpret_cast<int32_t*>(f.ws + f.L.idcut)[b * 4 + threadIdx.x] = sm.eff[r][c];
     }
-    __syncthreads();  // 1 / S and 1 / Z
-    build_tables(sm, two, slice);
-    __syncthreads();
     residual_slice(f, sm, b, slice, half, c0, two, vq, vp);
     if (!arrive_last(f, sm, b, 2 * f.nS)) return;
-    finalize_residual(f, sm, b, k, status, u_res);
+    finalize_residual(f, sm, b, k, status, sm.u_res);
 }
 
 void launch_resolve(const FastArgs& f, int grid, hipStream_t stream) {
