@@ -195,6 +195,13 @@ __device__ __forceinline__ unsigned l2_fetch_add(unsigned* p, unsigned v) {
     return old;
 }
 
+__device__ __forceinline__ uint64_t l2_fetch_add64(uint64_t* p, uint64_t v) {
+    uint64_t old;
+    asm volatile("s_waitcnt vmcnt(0)\n\tglobal_atomic_add_x2 %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
+                 : "=v"(old) : "v"(p), "v"(v) : "memory");
+    return old;
+}
+
 // Every wave waits until its own global stores have reached L2; __syncthreads() alone orders
 // only LDS traffic, so this must precede the workgroup barrier in front of an arrival.
 __device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -38,6 +38,7 @@ struct CountSmem {
     int rare[2];
     double u_acc;  // the acceptance draw of the unit's position
     double u_res;  // its residual / bonus draw
+    uint32_t unit_code;  // the settled unit's outcome (unit_code)
 };
 
 // Per-segment element counts of both rows into sm.segc: a thread adds 8 bins, eight lanes a
@@ -432,6 +433,15 @@ __device__ __forceinline__ void count_rare(CountSmem& sm, int r, int c0, int V, 
     if (ninf) atomicAdd(&sm.neginf[r], ninf);
 }
 
+// A unit's outcome in 7 bits for the request rendezvous: accepted, general path, and the
+// status bits the decision reads.
+__device__ __forceinline__ uint32_t unit_code(int accept, int fallback, uint32_t st) {
+    return (accept ? 1u : 0u) | (fallback ? 2u : 0u) | ((st & kStBadParam) ? 4u : 0u) | ((st & kStBadLogit) ? 8u : 0u) |
+           ((st & kStBadToken) ? 16u : 0u) | ((st & kStDegenerate) ? 32u : 0u) | ((st & kStOutside) ? 64u : 0u);
+}
+constexpr int kCodeBits = 7, kCountBits = 4;
+constexpr int kPackedUnits = (64 - kCountBits) / kCodeBits;  // 8: requests with K + 1 <= 8 units
+
 // The last slice of a unit: combine, acceptance test, unit record.
 __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, const Place& P, const spec_params& prm,
                                             bool param_ok, bool two, int s_tok, bool tok_ok) {
@@ -494,6 +504,7 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
         }
     }
     if (threadIdx.x == 0) {
+        sm.unit_code = unit_code(accept, fallback, status);
         UnitFast* U = reinterpret_cast<UnitFast*>(f.ws + f.L.units) + unit;
         U->accept = accept;
         U->status = status;
@@ -531,6 +542,60 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
                 }
             }
         }
+    }
+}
+
+// The last unit of a request, from the units' codes gathered by the rendezvous atomic: k, the
+// status, and the outputs when no residual is needed (thread 0; one load for a greedy
+// request's argmax).
+__device__ __forceinline__ void decide_packed(const FastArgs& f, int b, uint64_t word, bool greedy) {
+    const VerifyArgs& a = f.a;
+    const int K = a.K;
+    bool any_fb = false;
+    uint32_t any = 0, deg = 0;
+    int k = K;
+    for (int j = 0; j <= K; ++j) {
+        const uint32_t c = (uint32_t)(word >> (kCountBits + kCodeBits * j)) & 0x7Fu;
+        any_fb |= (c & 2u) != 0;
+        any |= ((c & 4u) ? kStBadParam : 0u) | ((c & 8u) ? kStBadLogit : 0u) | ((c & 16u) ? kStBadToken : 0u);
+        if (j < K) {
+            if (c & 32u) deg = kStDegenerate;
+            if (k == K && !(c & 1u)) k = j;
+        }
+    }
+    uint32_t outside = 0;
+    for (int j = 0; j < K && j <= k; ++j)
+        if ((word >> (kCountBits + kCodeBits * j)) & 64u) outside = kStOutside;
+    int mode = 0, t = -1, kk = 0;
+    uint32_t status;
+    if (any_fb) {
+        mode = 2;
+        status = 0;
+    } else if (any & kStBadParam) {
+        status = kStBadParam;
+    } else if (any & kStBadLogit) {
+        status = kStBadLogit;
+    } else if (any & kStBadToken) {
+        status = deg | kStBadToken;
+    } else {
+        status = deg | outside;
+        kk = k;
+        if (greedy) {
+            const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + (size_t)b * (K + 1) + k;
+            t = ldnt(&U->rq.argmax);
+        } else {
+            mode = 1;
+        }
+    }
+    ReqFast* R = reinterpret_cast<ReqFast*>(f.ws + f.L.reqs) + b;
+    R->mode = mode;
+    R->k = kk;
+    R->status = status;
+    if (mode == 0) {
+        a.out_k[b] = kk;
+        a.out_t[b] = t;
+        if (a.out_W) a.out_W[b] = 0.0f;
+        if (a.out_status) a.out_status[b] = status;
     }
 }
 
@@ -683,6 +748,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     // ---- request rendezvous: the last unit of the request decides k ----
     drain_stores();
     __syncthreads();
+    if (a.K + 1 <= kPackedUnits) {
+        // the arrival count and every unit's code in one 64-bit word: the last arriver decides
+        // from the atomic's result alone
+        if (threadIdx.x == 0) {
+            uint64_t* rc = reinterpret_cast<uint64_t*>(f.ws + f.L.req_ctr + (size_t)P.b * 128);
+            const uint64_t add = 1ull + ((uint64_t)sm.unit_code << (kCountBits + kCodeBits * P.j));
+            const uint64_t now = l2_fetch_add64(rc, add) + add;
+            if ((now & ((1ull << kCountBits) - 1ull)) == (uint64_t)(a.K + 1)) {
+                *rc = 0ull;  // every unit has arrived: ready for the next call
+                decide_packed(f, P.b, now, prm.temperature == 0.0f);
+            }
+        }
+        return;
+    }
     if (threadIdx.x == 0) {
         unsigned* rc = reinterpret_cast<unsigned*>(f.ws + f.L.req_ctr + (size_t)P.b * 128);
         const unsigned old = l2_fetch_add(rc, 1u);

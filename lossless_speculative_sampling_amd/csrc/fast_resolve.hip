@@ -654,11 +654,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int x = blockIdx.x % kXcd, l = blockIdx.x / kXcd;
     const int b = (l / R) * kXcd + x, w = l % R;
     if (b >= a.B) return;
+    // what the residual needs of every unit (k picks one): row statistics, cuts, this slice's
+    // flags and the draw, one 32-bit word per thread, issued before the decision's own load
+    static_assert(offsetof(UnitFast, rp) == offsetof(UnitFast, rq) + sizeof(RowFinal), "rq, rp adjacent");
+    constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
+    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWDraw = kWFlag + 2, kRecWords = 64;
+    static_assert(kWDraw + 2 <= kRecWords, "one unit's words in a wave");
+    const bool pre = (a.K + 1) * kRecWords <= kThreads;  // otherwise loaded once k is known
+    const int pj = (int)threadIdx.x / kRecWords, pw = (int)threadIdx.x % kRecWords;
+    uint32_t pre_word = 0u;
+    if (pre && pj <= a.K && (w >> 1) < f.nS) {
+        const int uj = b * (a.K + 1) + pj;
+        const UnitFast* Uj = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + uj;
+        if (pw < kWCut) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->rq) + pw);
+        else if (pw < kWFlag) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->cut[0][0]) + (pw - kWCut));
+        else if (pw < kWDraw) pre_word = ldnt(&part_of(f, uj, w >> 1, pw - kWFlag)->flags);
+        else if (pw < kWDraw + 2) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->u_res) + (pw - kWDraw));
+    }
     // the request's decision and this unit's cache flag, loaded together
     static_assert(sizeof(ReqFast) == 16, "one 16-byte record");
     const u32x4 req = ldnt(reinterpret_cast<const u32x4*>(f.ws + f.L.reqs) + b);
     const bool cache_here = f.cache && w <= a.K;
-    const int32_t cgen = cache_here ? ldnt(reinterpret_cast<const int32_t*>(f.ws + f.L.cache_gen) + b * (a.K + 1) + w) : 0;
+    const int32_t cgen_word = ldnt(reinterpret_cast<const int32_t*>(f.ws + f.L.cache_gen) + b * (a.K + 1) + min(w, a.K));
+    const int32_t cgen = cache_here ? cgen_word : 0;
     // outcome-cache rows the count kernel's candidate lists could not settle
     if (cgen) {
         CacheArgs c{a.draft, a.dtype, a.B, a.K, a.V, a.tokens, f.budget, f.fan, f.out_cache};
@@ -683,28 +701,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)b * (a.K + 1) + k) * stride;
     const uint16_t* drow = two ? static_cast<const uint16_t*>(a.draft) + ((size_t)b * a.draft_rows + k) * stride : nullptr;
-    // the unit's record (row statistics and cuts) and this slice's flags are loaded before the
-    // slice itself, so that waiting for them does not wait for the slice (loads complete in order)
-    static_assert(offsetof(UnitFast, rp) == offsetof(UnitFast, rq) + sizeof(RowFinal), "rq, rp adjacent");
-    const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + unit;
-    constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
-    const int nrf = two ? 2 * kRf : kRf, ncut = two ? 4 * kCut : 2 * kCut;
-    const uint32_t rf_word = (int)threadIdx.x < nrf ? ldnt(reinterpret_cast<const uint32_t*>(&U->rq) + threadIdx.x) : 0u;
-    const uint32_t cut_word = (int)threadIdx.x < ncut ? ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + threadIdx.x) : 0u;
-    const uint32_t flag_word =
-        (threadIdx.x == 0 || (threadIdx.x == 1 && two)) ? ldnt(&part_of(f, unit, slice, threadIdx.x)->flags) : 0u;
-    // the draw for t*, taken by the count kernel with the position's acceptance draw
-    const double u_res = threadIdx.x == 0 ? ldnt(&U->u_res) : 0.0;
+    // without the preload: the unit's record (row statistics and cuts), this slice's flags and
+    // the draw for t* (taken by the count kernel with the position's acceptance draw), loaded
+    // before the slice itself so that waiting for them does not wait for the slice
+    uint32_t rec_word = pre_word;
+    int rec_slot = pj == k ? pw : -1;
+    if (!pre) {
+        rec_slot = (int)threadIdx.x < kWDraw + 2 ? (int)threadIdx.x : -1;
+        const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + unit;
+        const int x = (int)threadIdx.x;
+        if (x < kWCut) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->rq) + x);
+        else if (x < kWFlag) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + (x - kWCut));
+        else if (x < kWDraw) rec_word = ldnt(&part_of(f, unit, slice, x - kWFlag)->flags);
+        else if (x < kWDraw + 2) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->u_res) + (x - kWDraw));
+    }
     // (without a draft row the second set re-reads the target and goes unused: unconditional
     // loads keep the waits above exact)
     u32x4 vq[kLoads], vp[kLoads];
     load_slice(trow, c0, a.V, vq);
     load_slice(two ? drow : trow, c0, a.V, vp);
-    if ((int)threadIdx.x < nrf) reinterpret_cast<uint32_t*>(&sm.rf[0])[threadIdx.x] = rf_word;
-    if ((int)threadIdx.x < ncut) reinterpret_cast<uint32_t*>(&sm.cut[0][0])[threadIdx.x] = cut_word;
-    if (!two && threadIdx.x >= kWave && threadIdx.x < kWave + 2) sm.cut[1][threadIdx.x - kWave] = UnitCut{0u, -1, 0, 0};
-    if (threadIdx.x < 2) sm.flags[threadIdx.x] = flag_word;
-    if (threadIdx.x == 0) sm.u_res = u_res;
+    // the record into LDS; without a draft row its cuts keep everything and its flags are 0
+    if (rec_slot >= 0) {
+        if (rec_slot < kWCut) {
+            reinterpret_cast<uint32_t*>(&sm.rf[0])[rec_slot] = rec_word;
+        } else if (rec_slot < kWFlag) {
+            const int x = rec_slot - kWCut;
+            const bool keep_all = !two && x >= 2 * kCut;  // UnitCut{0, -1, 0, 0}
+            reinterpret_cast<uint32_t*>(&sm.cut[0][0])[x] = keep_all ? (x % kCut == 1 ? 0xFFFFFFFFu : 0u) : rec_word;
+        } else if (rec_slot < kWDraw) {
+            sm.flags[rec_slot - kWFlag] = (rec_slot == kWFlag || two) ? rec_word : 0u;
+        } else {
+            reinterpret_cast<uint32_t*>(&sm.u_res)[rec_slot - kWDraw] = rec_word;
+        }
+    }
     if (threadIdx.x >= kWave && threadIdx.x < kWave + 6) sm.tie[(threadIdx.x - kWave) / 3][(threadIdx.x - kWave) % 3].off = kNoTie;
     __syncthreads();
     if (threadIdx.x < 2) {
