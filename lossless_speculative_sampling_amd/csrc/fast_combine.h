@@ -48,6 +48,8 @@ struct RowView {   // the combined view of one row, identical in every slice of 
     // a histogram cut in progress (0 none, 1 top-k count cut, 2 nucleus mass cut)
     int pend;
     int pend_seg;
+    int early;                 // stage A ran before the candidate merge
+    int early_g;               // the group whose per-slice counts were loaded then (-1: none)
     int pend_cnt_above;
     double pend_need;
     double pend_above;
@@ -97,6 +99,8 @@ __device__ __forceinline__ void init_row(RowView& rv, const VerifyArgs& a, const
     rv.degenerate = 0;
     rv.pend = 0;
 }
+
+__device__ __forceinline__ void stage_a(UnitSmem& us, int r, const spec_params& prm);
 
 // Round trip 1 and what follows from it alone: row maxima, normalisers, flags, merged segment
 // weights and merged candidate lists of both rows.
@@ -215,6 +219,36 @@ __device__ __forceinline__ void combine_load(const FastArgs& f, UnitSmem& us, in
             }
             us.rv[r].seg_mass[sg] = w;
             us.rv[r].seg_count[sg] = c;
+        }
+    }
+    // -- early stage A: a row whose cuts need no merged candidate list (no greedy argmax, no
+    //    top-k within the lists) settles them from the segments now (wave r, which merged the
+    //    row's segments), and two other waves load the crossing group's per-slice counts while
+    //    the lists merge --
+    if (wave < rows) {
+        RowView& rv = us.rv[wave];
+        const bool early = !rv.greedy && !(rv.has_k && rv.small_k);
+        if (early) stage_a(us, wave, prm);
+        int g = -1;
+        if (early && rv.pend != 0 && !rv.bad && !rv.overflow) g = group_of_seg(rv.pend_seg);
+        if (lane == 0) {
+            rv.early = early ? 1 : 0;
+            rv.early_g = g;
+        }
+    }
+    __syncthreads();
+    if (wave >= 2 && wave < 2 + rows) {
+        const int r = wave - 2;
+        const int g = us.rv[r].early_g;
+        if (g >= 0) {
+            // two counts per 32-bit word (fine counts start 4-byte aligned in a RowPart)
+            static_assert(offsetof(RowPart, fine) % 4 == 0, "fine counts in 32-bit words");
+            for (int i = lane; i < nS * (kGroup / 2); i += kWave) {
+                const int t = i / (kGroup / 2), pr = i % (kGroup / 2);
+                const uint32_t wd = ldnt(reinterpret_cast<const uint32_t*>(&part_of(f, unit, t, r)->fine[g * kGroup]) + pr);
+                us.fine_ps[r][t][2 * pr] = (uint16_t)(wd & 0xFFFFu);
+                us.fine_ps[r][t][2 * pr + 1] = (uint16_t)(wd >> 16);
+            }
         }
     }
     // -- merged candidate lists --
@@ -537,6 +571,39 @@ __device__ __forceinline__ void nucleus_step(UnitSmem& us, int r, const spec_par
     }
 }
 
+// Stage A of row r (wave r): top-k, then the nucleus where it needs no group counts; a cut
+// that crosses a group is left pending.
+__device__ __forceinline__ void stage_a(UnitSmem& us, int r, const spec_params& prm) {
+    RowView& rv = us.rv[r];
+    const int lane = threadIdx.x & (kWave - 1);
+    if (rv.bad || rv.overflow) {
+        // nothing to settle
+    } else if (rv.greedy) {
+        if (lane == 0) rv.argmax = rv.nm > 0 ? us.oid[r][0] : -1;
+    } else if (rv.has_k && (uint32_t)prm.top_k > rv.n_finite) {  // -inf tokens would be kept
+        if (lane == 0) rv.overflow = 1;
+    } else {
+        if (!rv.has_k) {
+            if (lane == 0) {
+                rv.S_kept = rv.S_all;
+                rv.n_kept = (int)rv.n_finite;
+            }
+        } else if (rv.small_k) {
+            const int kk = prm.top_k;
+            const double e = lane < kk ? mass_of(key16_value(us.okey[r][lane]), rv.m, rv.invT) : 0.0;
+            const double s = wave_sum(e);
+            if (lane == 0) {
+                rv.S_kept = s;
+                rv.n_kept = kk;
+                rv.ck = Cut{us.okey[r][kk - 1], 0, us.oid[r][kk - 1], 0, 0, 0};
+            }
+        } else {
+            seg_walk<false>(rv, (double)prm.top_k, false, rv.ck);
+        }
+        if (rv.pend == 0) nucleus_step(us, r, prm);
+    }
+}
+
 // Both rows' processed distributions: maxima, normalisers, top-k and nucleus cuts, and (dw)
 // the draft row's downweighted set.  All threads.
 __device__ __forceinline__ void combine(const FastArgs& f, UnitSmem& us, int unit, int j, int rows, const spec_params& prm,
@@ -545,37 +612,9 @@ __device__ __forceinline__ void combine(const FastArgs& f, UnitSmem& us, int uni
     combine_load(f, us, unit, j, rows, prm);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    // top-k, then the nucleus where it needs no group counts (wave r for row r)
-    if (wave < rows) {
-        RowView& rv = us.rv[wave];
-        const int r = wave;
-        if (rv.bad || rv.overflow) {
-            // nothing to settle
-        } else if (rv.greedy) {
-            if (lane == 0) rv.argmax = rv.nm > 0 ? us.oid[r][0] : -1;
-        } else if (rv.has_k && (uint32_t)prm.top_k > rv.n_finite) {  // -inf tokens would be kept
-            if (lane == 0) rv.overflow = 1;
-        } else {
-            if (!rv.has_k) {
-                if (lane == 0) {
-                    rv.S_kept = rv.S_all;
-                    rv.n_kept = (int)rv.n_finite;
-                }
-            } else if (rv.small_k) {
-                const int kk = prm.top_k;
-                const double e = lane < kk ? mass_of(key16_value(us.okey[r][lane]), rv.m, rv.invT) : 0.0;
-                const double s = wave_sum(e);
-                if (lane == 0) {
-                    rv.S_kept = s;
-                    rv.n_kept = kk;
-                    rv.ck = Cut{us.okey[r][kk - 1], 0, us.oid[r][kk - 1], 0, 0, 0};
-                }
-            } else {
-                seg_walk<false>(rv, (double)prm.top_k, false, rv.ck);
-            }
-            if (rv.pend == 0) nucleus_step(us, r, prm);
-        }
-    }
+    // top-k, then the nucleus where it needs no group counts (wave r for row r), unless the
+    // row settled them before the candidate merge
+    if (wave < rows && !us.rv[wave].early) stage_a(us, wave, prm);
     __syncthreads();
     // pending histogram cuts: load their groups' per-slice counts, settle, repeat (a top-k cut
     // can leave a nucleus cut behind it)
@@ -583,8 +622,9 @@ __device__ __forceinline__ void combine(const FastArgs& f, UnitSmem& us, int uni
         const bool p0 = us.rv[0].pend != 0;
         const bool p1 = rows > 1 && us.rv[1].pend != 0;
         if (!p0 && !p1) break;
-        const int g0 = p0 ? group_of_seg(us.rv[0].pend_seg) : -1;
-        const int g1 = p1 ? group_of_seg(us.rv[1].pend_seg) : -1;
+        // (round 0: a row whose counts were loaded during the candidate merge has them already)
+        const int g0 = (p0 && !(round == 0 && us.rv[0].early_g >= 0)) ? group_of_seg(us.rv[0].pend_seg) : -1;
+        const int g1 = (p1 && !(round == 0 && us.rv[1].early_g >= 0)) ? group_of_seg(us.rv[1].pend_seg) : -1;
         for (int i = threadIdx.x; i < 2 * f.nS * kGroup; i += blockDim.x) {
             const int r = i / (f.nS * kGroup), t = (i / kGroup) % f.nS, bb = i % kGroup;
             const int g = r == 0 ? g0 : g1;
