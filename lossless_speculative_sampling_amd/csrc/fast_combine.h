@@ -44,6 +44,7 @@ struct RowView {   // the combined view of one row, identical in every slice of 
     int degenerate;
     // draft token s: its value and its rank among the elements with its key (token order)
     uint32_t s_bits;
+    double e_s;                // its mass exp((z_s - m)/T) (0 for -inf or no token)
     int rank_s;
     // a histogram cut in progress (0 none, 1 top-k count cut, 2 nucleus mass cut)
     int pend;
@@ -61,6 +62,7 @@ struct UnitSmem {
     RowView rv[2];
     uint32_t key[2][kMergeCap];   // every slice's candidate list, slice-major; specials staging
     int32_t id[2][kMergeCap];
+    double qs, ps;                // the drafted token's processed probabilities
     uint32_t okey[2][kTop];       // merged candidates in token order
     int32_t oid[2][kTop];
     union {
@@ -239,6 +241,11 @@ __device__ __forceinline__ void combine_load(const FastArgs& f, UnitSmem& us, in
     __syncthreads();
     if (wave >= 2 && wave < 2 + rows) {
         const int r = wave - 2;
+        // the drafted token's mass, off the acceptance test's critical path
+        if (lane == 0) {
+            const uint32_t sb = us.rv[r].s_bits;
+            us.rv[r].e_s = ((sb & 0x7FFFu) < 0x7F80u && T > 0.0) ? mass_of(__uint_as_float(sb << 16), us.rv[r].m, us.rv[r].invT) : 0.0;
+        }
         const int g = us.rv[r].early_g;
         if (g >= 0) {
             // two counts per 32-bit word (fine counts start 4-byte aligned in a RowPart)
@@ -571,6 +578,28 @@ __device__ __forceinline__ void nucleus_step(UnitSmem& us, int r, const spec_par
     }
 }
 
+__device__ __forceinline__ bool cut_keeps_s(const RowView& rv, const Cut& c, uint32_t key_s, int s) {
+    if (key_s > c.key) return true;
+    if (key_s < c.key) return false;
+    if (c.explicit_id >= 0) return s <= c.explicit_id;
+    return rv.rank_s < c.take;
+}
+
+// Processed probability of token s in row r (after the combine).
+__device__ __forceinline__ double prob_of_s(const UnitSmem& us, int r, int s, bool draft) {
+    const RowView& rv = us.rv[r];
+    const uint32_t h = rv.s_bits;
+    if ((h & 0x7FFFu) >= 0x7F80u) return 0.0;
+    const uint32_t key = key16(h);
+    if (rv.has_k && !cut_keeps_s(rv, rv.ck, key, s)) return 0.0;
+    if (rv.has_p && !cut_keeps_s(rv, rv.cp, key, s)) return 0.0;
+    const double e = rv.e_s;
+    const double p = e / rv.S;
+    if (!draft) return p;
+    const double fct = (rv.nset > 0 && e > 0.0 && in_cut_id(rv.kF, rv.idF, key, s)) ? rv.C : 1.0;
+    return (p * fct) / rv.Z;
+}
+
 // Stage A of row r (wave r): top-k, then the nucleus where it needs no group counts; a cut
 // that crosses a group is left pending.
 __device__ __forceinline__ void stage_a(UnitSmem& us, int r, const spec_params& prm) {
@@ -607,7 +636,7 @@ __device__ __forceinline__ void stage_a(UnitSmem& us, int r, const spec_params& 
 // Both rows' processed distributions: maxima, normalisers, top-k and nucleus cuts, and (dw)
 // the draft row's downweighted set.  All threads.
 __device__ __forceinline__ void combine(const FastArgs& f, UnitSmem& us, int unit, int j, int rows, const spec_params& prm,
-                                        bool dw) {
+                                        bool dw, int s_tok) {
     const VerifyArgs& a = f.a;
     combine_load(f, us, unit, j, rows, prm);
     const int lane = threadIdx.x & (kWave - 1);
@@ -684,31 +713,15 @@ __device__ __forceinline__ void combine(const FastArgs& f, UnitSmem& us, int uni
             }
         }
     }
+    // the drafted token's processed probabilities for the acceptance test: lane 0 of wave 0
+    // (target row) and of wave 1 (draft row, after its set)
+    if (dw && rows > 1 && s_tok >= 0 && s_tok < a.V && wave < 2 && lane == 0 && !us.rv[wave].greedy) {
+        const double p = prob_of_s(us, wave, s_tok, wave == 1);
+        if (wave == 0) us.qs = p;
+        else us.ps = p;
+    }
     __syncthreads();
 }
-
-__device__ __forceinline__ bool cut_keeps_s(const RowView& rv, const Cut& c, uint32_t key_s, int s) {
-    if (key_s > c.key) return true;
-    if (key_s < c.key) return false;
-    if (c.explicit_id >= 0) return s <= c.explicit_id;
-    return rv.rank_s < c.take;
-}
-
-// Processed probability of token s in row r (after the combine).
-__device__ __forceinline__ double prob_of_s(const UnitSmem& us, int r, int s, bool draft) {
-    const RowView& rv = us.rv[r];
-    const uint32_t h = rv.s_bits;
-    if ((h & 0x7FFFu) >= 0x7F80u) return 0.0;
-    const uint32_t key = key16(h);
-    if (rv.has_k && !cut_keeps_s(rv, rv.ck, key, s)) return 0.0;
-    if (rv.has_p && !cut_keeps_s(rv, rv.cp, key, s)) return 0.0;
-    const double e = mass_of(__uint_as_float(h << 16), rv.m, rv.invT);
-    const double p = e / rv.S;
-    if (!draft) return p;
-    const double fct = (rv.nset > 0 && e > 0.0 && in_cut_id(rv.kF, rv.idF, key, s)) ? rv.C : 1.0;
-    return (p * fct) / rv.Z;
-}
-
 
 }  // namespace fast
 }  // namespace sv

@@ -454,7 +454,7 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
         status = kStBadParam;
     } else {
         const bool vd = P.j < a.K;  // the draft row is verified (not only listed for the cache)
-        combine(f, us, unit, P.j, two ? 2 : 1, prm, vd);
+        combine(f, us, unit, P.j, two ? 2 : 1, prm, vd, s_tok);
         const bool bad = us.rv[0].bad || (vd && us.rv[1].bad);
         fallback = (!bad && (us.rv[0].overflow || (vd && us.rv[1].overflow))) ? 1 : 0;
         if (bad) {
@@ -467,8 +467,7 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
                 if (us.rv[0].greedy) {
                     accept = (s_tok == us.rv[0].argmax) ? 1 : 0;
                 } else {
-                    const double ps = prob_of_s(us, 1, s_tok, true);
-                    const double qs = prob_of_s(us, 0, s_tok, false);
+                    const double ps = us.ps, qs = us.qs;
                     if (!(ps > 0.0)) status |= kStOutside;
                     const double u = sm.u_acc;
                     accept = (u * ps < qs) ? 1 : 0;
