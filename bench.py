@@ -72,12 +72,87 @@ def cpu_baseline(w, seconds_target=15.0):
                       f"build + lookup) in {el:.1f} s, fp64, std::thread over requests/rows"}
 
 
+def bench_other(name, args):
+    """One JSON line for a configuration other than the headline one: the verification call
+    (plus, for the branch trees, the reuse lookup) timed on rotated inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    from lossless_speculative_sampling_amd import capi, synth
+    dev = torch.device("cuda:0")
+    if name == "c1":
+        w = synth.vanilla(B=10000, K=4, V=1024)
+        desc = "vanilla verify: 10^4 rounds batched (B=10^4), K=4, V=1024 fp32 Gaussian logits, T=1"
+    elif name == "c2":
+        w = synth.llama(B=100, K=5, V=128256)
+        desc = "vanilla verify: 100 rounds batched (B=100), K=5, V=128256 bf16 Zipf logits, T=1, top-p 0.8"
+    elif name == "c3":
+        w = synth.saguaro(B=16, K=5, V=128256, cache_row=False)
+        desc = "saguaro verify: B=16, K=5, V=128256 bf16 Zipf logits, top-p 0.95, sigma F=4 C=0.3"
+    elif name == "c5":
+        w = synth.tree(n_req=64)
+        desc = "branch-tree chains: 64 requests x 8 branches, gamma=7, V=151936 bf16, T=0.8, top-k 50, reuse lookup"
+    else:
+        raise SystemExit(f"unknown config {name}")
+    B, K, V = w.B, w.K, w.V
+    step_bytes = int(w.draft.nbytes + w.target.nbytes)
+    copies = max(1, -(-2 * MALL_BYTES // step_bytes) + 1) if step_bytes < 2 * MALL_BYTES else 1
+    as_dev = (lambda a: torch.from_numpy(a.view(np.int16)).to(dev)) if w.dtype == synth.BF16 else \
+        (lambda a: torch.from_numpy(a).to(dev))
+    d0, t0 = as_dev(w.draft), as_dev(w.target)
+    drafts = [d0] + [d0.clone() for _ in range(copies - 1)]
+    targets = [t0] + [t0.clone() for _ in range(copies - 1)]
+    prm = capi.params_tensor(w.temperature, w.top_k, w.top_p, device=dev)
+    if w.tokens is not None:
+        tokens = torch.from_numpy(w.tokens.astype(np.int32)).to(dev)
+    else:
+        tokens = torch.zeros((B, K), dtype=torch.int32, device=dev)
+        capi.spec_verify(d0, t0, K, prm, tokens, F=w.F, C=w.C, seed=w.seed, flags=capi.SPEC_SAMPLE_DRAFT)
+    ws = capi.new_workspace(B, K, V, dev)
+    out = capi.VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                         torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                         tokens)
+    br = tokens if name == "c5" else None
+
+    def step(i):
+        capi.spec_verify(drafts[i % copies], targets[i % copies], K, prm, tokens, F=w.F, C=w.C, seed=w.seed, round_=i,
+                         workspace=ws, out=out)
+        if br is not None:
+            capi.saguaro_cache_lookup(1, br, [w.kappa, w.gamma], 0, B // w.kappa, out.k, out.tstar)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    vt = sorted(a.elapsed_time(b) for a, b in evs)
+    ms = sum(vt) / len(vt)
+    achieved = step_bytes / (ms * 1e-3) / 1e9
+    res = {"metric": f"verified positions/sec and achieved HBM GB/s (% peak), {name}", "value": B * K / (ms * 1e-3),
+           "unit": "verified positions/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f64", "data": "synthetic",
+           "config": {"workload": desc, "B": B, "K": K, "V": V, "logit_bytes_per_step": step_bytes,
+                      "input_copies_rotated": copies},
+           "roofline": {"bound": "hbm", "kernel": "spec_verify (whole call)", "achieved": achieved,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                        "algorithmic_bytes_per_launch": step_bytes, "avg_launch_ms": ms,
+                        "p10_ms": vt[len(vt) // 10], "p90_ms": vt[(len(vt) * 9) // 10]}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="c4 (default): the headline workload; the others print their own line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
     args = ap.parse_args()
@@ -101,6 +176,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+
+    if args.config != "c4":
+        bench_other(args.config, args)
         return
 
     w = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
