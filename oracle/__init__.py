@@ -57,8 +57,11 @@ def lib():
         L.orc_downweight_probs_f64.argtypes = [P, P, i32, i32, f64, P, P]
         L.orc_downweight_probs_f64.restype = f64
         L.orc_downweight.argtypes = [P, i32, i32, i32, i32, i32, P, i32, f64, P, P, P, P, i32]
-        L.orc_verify_u.argtypes = [P, i32, P, i32, i32, i32, i32, P, i32, f64, P, i32, P, P, P, P, P, P, i32]
-        L.orc_verify.argtypes = [P, i32, P, i32, i32, i32, i32, P, i32, f64, P, i32, u64, u64, P, P, P, P, P, i32]
+        L.orc_verify_u.argtypes = [P, i32, P, i32, i32, i32, i32, P, i32, f64, P, i32, P, P, P, P, P, P, i32, i32]
+        L.orc_verify.argtypes = [P, i32, P, i32, i32, i32, i32, P, i32, f64, P, i32, u64, u64, P, P, P, P, P, i32,
+                                 i32]
+        L.orc_uniform_tokens.argtypes = [P, i32, i32, P]
+        L.orc_backup_plan.argtypes = [i32, P, i32, i32, P, P]
         L.orc_fanout.argtypes = [i32, i32, f64, f64, P, P]
         L.orc_cache_build.argtypes = [P, i32, i32, i32, i32, P, P, P, i32]
         L.orc_cache_lookup.argtypes = [i32, P, P, i32, i32, P, P, P, P, P]
@@ -140,15 +143,21 @@ def _check(rc, name):
 
 
 def verify(draft, target, dtype, K, params, F=0, C=1.0, tokens=None, seed=0, round_=0, U=None,
-           nthreads=0) -> VerifyResult:
+           nthreads=0, uniform_draft=False) -> VerifyResult:
     """draft [B][Kd][V], target [B][K+1][V] (float32 or uint16 bf16 bits).
 
     ``tokens`` None => the draft tokens are sampled from the processed draft (lane 2).
     ``U`` given => explicit uniforms [B][K+1][3] instead of the Philox stream.
+    ``uniform_draft`` => the draft distribution is uniform on [0, V) (``draft`` may be None).
     """
-    draft = np.ascontiguousarray(draft)
     target = np.ascontiguousarray(target)
-    B, Kd, V = draft.shape
+    if draft is None:
+        assert uniform_draft
+        B, _, V = target.shape
+        Kd = K
+    else:
+        draft = np.ascontiguousarray(draft)
+        B, Kd, V = draft.shape
     params = np.ascontiguousarray(params, dtype=PARAMS_DTYPE)
     sample = tokens is None
     tok = np.zeros((B, K), dtype=np.int32) if sample else np.array(tokens, dtype=np.int32, copy=True)
@@ -159,12 +168,12 @@ def verify(draft, target, dtype, K, params, F=0, C=1.0, tokens=None, seed=0, rou
     fl = np.zeros(B, np.uint32)
     if U is None:
         rc = lib().orc_verify(_p(draft), Kd, _p(target), dtype, B, K, V, _p(params), F, C, _p(tok), int(sample),
-                              seed, round_, _p(k), _p(t), _p(W), _p(st), _p(fl), nthreads)
+                              seed, round_, _p(k), _p(t), _p(W), _p(st), _p(fl), nthreads, int(uniform_draft))
     else:
         U = np.ascontiguousarray(U, dtype=np.float64)
         assert U.shape == (B, K + 1, 3)
         rc = lib().orc_verify_u(_p(draft), Kd, _p(target), dtype, B, K, V, _p(params), F, C, _p(tok), int(sample),
-                                _p(U), _p(k), _p(t), _p(W), _p(st), _p(fl), nthreads)
+                                _p(U), _p(k), _p(t), _p(W), _p(st), _p(fl), nthreads, int(uniform_draft))
     _check(rc, "verify")
     return VerifyResult(k, t, W, st, fl, tok)
 
@@ -212,3 +221,20 @@ def cache_lookup(mode, cache, fan_or_shape, K, B, k, t):
     _check(lib().orc_cache_lookup(mode, _p(cache), _p(fs), K, B, _p(k), _p(t), _p(slot), _p(hit), _p(batch)),
            "cache_lookup")
     return slot, hit, batch
+
+
+def uniform_tokens(u, V):
+    """floor(u * V) for uniforms u from the Philox stream (exact)."""
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    out = np.zeros(u.shape, np.int32)
+    lib().orc_uniform_tokens(_p(u), u.size, V, _p(out))
+    return out
+
+
+def backup_plan(B, hit, all_hit, b_star):
+    """(use_backup[B], switch): the batch-aware random-token fallback."""
+    hit = np.ascontiguousarray(hit, dtype=np.uint8)
+    use = np.zeros(B, np.int32)
+    sw = np.zeros(1, np.int32)
+    lib().orc_backup_plan(B, _p(hit), int(all_hit), b_star, _p(use), _p(sw))
+    return use, int(sw[0])

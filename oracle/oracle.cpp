@@ -8,7 +8,9 @@
 //     (Theorem 12, geometric fan-out), 4.4 (Theorem 15 / Theorem 19, Saguaro sampling), 5.1
 //     (cache construction), 7.1 (Corollary 16, whole-batch miss);
 //   * hyper.ai SSD/Saguaro summary, "Method" (the fan-out closed form and sigma_{F,C});
-//   * Mirror-SD reading notes, sections 2 and 3.2 (greedy verify, verification-vs-reuse rule).
+//   * Mirror-SD reading notes, sections 2 and 3.2 (greedy verify, verification-vs-reuse rule);
+//   * SSD reading notes section 7.1 and the hyper.ai summary's fallback paragraph (the
+//     batch-aware switch to a random-token backup speculator on a cache miss).
 //
 // Notation follows the DeepMind page: p = draft distribution, q = target distribution.
 // Only tests/, the smoke check and the bench's CPU-baseline leg may load this library; the
@@ -252,6 +254,15 @@ int inverse_cdf(const std::vector<double>& w, double x, bool* near) {
     return last;
 }
 
+// A token drawn from the uniform distribution on [0, V) by inverse CDF: the least i with
+// (i + 1) / V > u, i.e. floor(u V).  u = (2a + 1) / 2^53 exactly (to_uniform), so the product
+// is taken in 128-bit integers and the floor is exact.
+int32_t uniform_token(double u, int V) {
+    const uint64_t m = (uint64_t)(u * 0x1.0p53);  // 2a + 1, exact
+    const unsigned __int128 prod = (unsigned __int128)m * (uint64_t)V;
+    return (int32_t)(prod >> 53);
+}
+
 struct Request {
     int32_t k = 0;
     int32_t t = -1;
@@ -261,9 +272,12 @@ struct Request {
 };
 
 // The verification of one request, for given uniforms U[j][lane] (j = 0..K).
+// uniform_draft: the draft distribution of every position is the uniform one on [0, V) (the
+// random-token backup speculator): no draft rows are read, the request's temperature, top-k,
+// top-p and sigma_{F,C} do not apply to it, and sampled draft tokens are uniform draws.
 Request verify_one(const void* draft, int draft_rows, const void* target, int dtype, int b, int K, int V,
                    const Params& prm, int F, double C, int32_t* tokens, bool sample_draft,
-                   const double* U) {
+                   const double* U, bool uniform_draft) {
     Request out;
     if (!(prm.temperature >= 0.0f) || std::isinf(prm.temperature) || !(prm.top_p > 0.0f)) {
         out.status |= ST_BAD_PARAM;
@@ -279,7 +293,12 @@ Request verify_one(const void* draft, int draft_rows, const void* target, int dt
         q[j] = process(z, prm);
         bad |= q[j].bad;
     }
+    const double p_uniform = 1.0 / (double)V;
     for (int j = 0; j < K; ++j) {
+        if (uniform_draft) {
+            p[j].p.assign(V, p_uniform);
+            continue;
+        }
         load_row(draft, dtype, (size_t)b * draft_rows + j, V, z);
         p[j] = process(z, prm);
         bad |= p[j].bad;
@@ -293,16 +312,19 @@ Request verify_one(const void* draft, int draft_rows, const void* target, int dt
     const bool greedy = prm.temperature == 0.0f;
     std::vector<int32_t> ids(F > 0 ? F : 1);
     for (int j = 0; j < K; ++j) {
+        if (q[j].near_cut) out.flags |= FL_NEAR_NUCLEUS;
+        if (uniform_draft) continue;
         bool degen = false;
         downweight(p[j], F, C, ids.data(), &degen);
         if (degen) out.status |= ST_DEGENERATE_DOWNWEIGHT;
-        if (q[j].near_cut || p[j].near_cut) out.flags |= FL_NEAR_NUCLEUS;
+        if (p[j].near_cut) out.flags |= FL_NEAR_NUCLEUS;
     }
     if (q[K].near_cut) out.flags |= FL_NEAR_NUCLEUS;
     if (sample_draft) {
         for (int j = 0; j < K; ++j) {
             bool near = false;
-            tokens[j] = greedy ? p[j].argmax : inverse_cdf(p[j].p, U[3 * j + 2], &near);
+            if (uniform_draft) tokens[j] = uniform_token(U[3 * j + 2], V);
+            else tokens[j] = greedy ? p[j].argmax : inverse_cdf(p[j].p, U[3 * j + 2], &near);
             if (near) out.flags |= FL_NEAR_CDF;
         }
     }
@@ -472,14 +494,14 @@ int orc_downweight(const void* draft, int draft_rows, int dtype, int B, int K, i
 int orc_verify_u(const void* draft, int draft_rows, const void* target, int dtype, int B, int K, int V,
                  const void* params, int F, double C, int32_t* tokens, int sample_draft, const double* U,
                  int32_t* out_k, int32_t* out_t, double* out_W, uint32_t* out_status, uint32_t* out_flags,
-                 int nthreads) {
+                 int nthreads, int uniform_draft) {
     const Params* prm = static_cast<const Params*>(params);
-    if (!draft || !target || !tokens || !U || B < 1 || K < 1 || V < 1 || draft_rows < K || F < 0 ||
-        !(C >= 0.0 && C <= 1.0) || (dtype != kFP32 && dtype != kBF16))
+    if ((!draft && !uniform_draft) || !target || !tokens || !U || B < 1 || K < 1 || V < 1 ||
+        (!uniform_draft && draft_rows < K) || F < 0 || !(C >= 0.0 && C <= 1.0) || (dtype != kFP32 && dtype != kBF16))
         return -1;
     parallel_for(B, nthreads, [&](int b) {
         Request r = verify_one(draft, draft_rows, target, dtype, b, K, V, prm[b], F, C, tokens + (size_t)b * K,
-                               sample_draft != 0, U + (size_t)b * (K + 1) * 3);
+                               sample_draft != 0, U + (size_t)b * (K + 1) * 3, uniform_draft != 0);
         out_k[b] = r.k;
         out_t[b] = r.t;
         if (out_W) out_W[b] = r.W;
@@ -493,12 +515,28 @@ int orc_verify_u(const void* draft, int draft_rows, const void* target, int dtyp
 int orc_verify(const void* draft, int draft_rows, const void* target, int dtype, int B, int K, int V,
                const void* params, int F, double C, int32_t* tokens, int sample_draft, uint64_t seed, uint64_t round,
                int32_t* out_k, int32_t* out_t, double* out_W, uint32_t* out_status, uint32_t* out_flags,
-               int nthreads) {
+               int nthreads, int uniform_draft) {
     if (B < 1 || K < 1) return -1;
     std::vector<double> U((size_t)B * (K + 1) * 3);
     orc_uniforms(seed, round, B, K, U.data());
     return orc_verify_u(draft, draft_rows, target, dtype, B, K, V, params, F, C, tokens, sample_draft, U.data(),
-                        out_k, out_t, out_W, out_status, out_flags, nthreads);
+                        out_k, out_t, out_W, out_status, out_flags, nthreads, uniform_draft);
+}
+
+// Uniform draws of the backup speculator (for tests): tokens[n] = floor(u[n] V).
+void orc_uniform_tokens(const double* u, int n, int V, int32_t* out) {
+    for (int i = 0; i < n; ++i) out[i] = uniform_token(u[i], V);
+}
+
+// The batch-aware fallback (SSD reading notes 7.1: on any miss the whole batch waits for the
+// fallback, and the switch between the primary drafter and the fast random-token backup is
+// made by batch size against a critical b*, whose formula the text does not give).  The
+// backup serves this round when some request missed (all-hit = 0) and B >= b_star; then every
+// missed request takes random tokens and requests that hit keep their cached speculation.
+void orc_backup_plan(int B, const uint8_t* hit, int all_hit, int b_star, int32_t* out_use_backup, int32_t* out_switch) {
+    const int sw = (all_hit == 0 && B >= b_star) ? 1 : 0;
+    for (int b = 0; b < B; ++b) out_use_backup[b] = (sw && !hit[b]) ? 1 : 0;
+    *out_switch = sw;
 }
 
 // Theorem 12 fan-out: F_k = F0 a^{k/(1+r)} for k < K, F_K = F0 a^{K/(1+r)} (1-a)^{-1/(1+r)},

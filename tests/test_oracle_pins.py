@@ -193,16 +193,20 @@ def _bisect(decide, n, iters=64):
     return np.where(lo == 0.0, 0.0, np.where(hi == 1.0, 1.0, 0.5 * (lo + hi)))
 
 
-def exact_law(zd, zt, T=1.0, top_k=0, top_p=1.0, F=0, C=1.0):
+def exact_law(zd, zt, T=1.0, top_k=0, top_p=1.0, F=0, C=1.0, uniform=False):
     """Law of the oracle's output over s ~ p' and the uniforms, integrated exactly.
 
-    Returns (law, p', q): law maps (k, emitted tokens) -> probability.
+    ``uniform``: the draft distribution is the uniform one on [0, V) (the backup speculator);
+    zd then only gives the shape.  Returns (law, p', q): law maps (k, emitted tokens) -> probability.
     """
     K, V = zd.shape
     # inputs are given to the oracle as fp32; the distributions below come from the same values
     q = [oracle.process_row(zt[j].astype(np.float32).astype(np.float64), T, top_k, top_p)[0] for j in range(K + 1)]
     pp = []
     for j in range(K):
+        if uniform:
+            pp.append(np.full(V, 1.0 / V))
+            continue
         zz = zd[j].astype(np.float32).astype(np.float64)
         pj = oracle.process_row(zz, T, top_k, top_p)[0]
         pp.append(oracle.downweight_probs(zz, pj, F, C)[0])
@@ -216,7 +220,8 @@ def exact_law(zd, zt, T=1.0, top_k=0, top_p=1.0, F=0, C=1.0):
 
     def run(U, tokens=tok):
         n = U.shape[0]
-        return oracle.verify(D[:n], Tt[:n], oracle.FP32, K, prm[:n], F=F, C=C, tokens=tokens, U=U)
+        return oracle.verify(None if uniform else D[:n], Tt[:n], oracle.FP32, K, prm[:n], F=F, C=C, tokens=tokens,
+                             U=U, uniform_draft=uniform)
 
     # acceptance thresholds a[n, j] with the earlier positions accepting
     a = np.zeros((N, K))
@@ -244,8 +249,8 @@ def exact_law(zd, zt, T=1.0, top_k=0, top_p=1.0, F=0, C=1.0):
                 if m < K:
                     U[:, m, 0] = 0.5 * (1.0 + a[idx, m])
                 U[:, m, 1] = np.maximum(x, 1e-300)
-                r = oracle.verify(D[:n_i], Tt[:n_i], oracle.FP32, K, prm[:n_i], F=F, C=C,
-                                  tokens=tok[idx], U=U)
+                r = oracle.verify(None if uniform else D[:n_i], Tt[:n_i], oracle.FP32, K, prm[:n_i], F=F, C=C,
+                                  tokens=tok[idx], U=U, uniform_draft=uniform)
                 assert (r.k == m).all()
                 return r.t <= y
             cuts[:, y + 1] = _bisect(dec, n_i)
@@ -513,3 +518,78 @@ def test_corollary16_whole_batch_hit():
     allhit = hits.all(axis=1).mean()
     se = np.sqrt(np.prod(ph) * (1 - np.prod(ph)) / R)
     assert abs(allhit - np.prod(ph)) < 5 * se + 1e-3
+
+
+# ------------------------------------------------------------------------------------------
+# Random-token backup speculation (SSD reading notes, section 7.1; hyper.ai summary, fallback)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("V,K,T,top_k,top_p,seed", [
+    (4, 1, 1.0, 0, 1.0, 0),
+    (6, 2, 1.0, 0, 1.0, 1),
+    (5, 2, 0.7, 3, 1.0, 2),
+    (6, 2, 1.0, 0, 0.7, 3),
+])
+def test_uniform_draft_lossless_exact_enumeration(V, K, T, top_k, top_p, seed):
+    # verifying uniform random tokens against the target leaves every emitted token with law q_j:
+    # the lossless law of the speculative-sampling page with p = 1/V at every position
+    rng = np.random.default_rng(900 + seed)
+    zt = rng.normal(0, 1.5, (K + 1, V))
+    zd = np.zeros((K, V))
+    law, pp, q = exact_law(zd, zt, T, top_k, top_p, uniform=True)
+    _check_lossless(law, pp, q, K, V)
+
+
+def test_uniform_token_is_exact_floor_and_inverse_cdf():
+    from fractions import Fraction
+    U = oracle.uniforms(seed=77, round_=3, B=64, K=7)[:, :, 2].ravel()
+    for V in (1, 2, 3, 7, 1000, 128256, 151936, (1 << 31) - 1):
+        t = oracle.uniform_tokens(U, V)
+        for u, ti in zip(U, t):
+            fu = Fraction(float(u))          # the exact dyadic value of the uniform
+            assert ti == (fu * V).numerator // (fu * V).denominator
+            if V <= 1000:                    # inverse CDF of the uniform law by its definition
+                assert ti == min(i for i in range(V) if Fraction(i + 1, V) > fu)
+
+
+def test_uniform_tokens_are_uniform():
+    V, n = 7, 70000
+    U = oracle.uniforms(seed=5, round_=0, B=n // 7, K=6)[:, :, 2].ravel()[:n]
+    counts = np.bincount(oracle.uniform_tokens(U, V), minlength=V)
+    chi2 = ((counts - n / V) ** 2 / (n / V)).sum()
+    assert chi2 < 22.46   # chi^2(6) at p = 0.001
+
+
+def test_uniform_draft_acceptance_and_residual_definitions():
+    # p'(s) = 1/V: accept iff u / V < q(s); the residual is (q - 1/V)+; sampled tokens are the
+    # uniform draws of lane 2
+    rng = np.random.default_rng(31)
+    B, K, V = 40, 3, 50
+    zt = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    prm = oracle.params_array(1.0, 0, 1.0, B=B)
+    r = oracle.verify(None, zt, oracle.FP32, K, prm, tokens=None, seed=11, uniform_draft=True)
+    U = oracle.uniforms(11, 0, B, K)
+    assert (r.tokens == oracle.uniform_tokens(U[:, :K, 2], V)).all()
+    for b in range(B):
+        q = [oracle.process_row(zt[b, j].astype(np.float64))[0] for j in range(K + 1)]
+        k = K
+        for j in range(K):
+            if not (U[b, j, 0] * (1.0 / V) < q[j][r.tokens[b, j]]):
+                k = j
+                break
+        assert r.k[b] == k
+        assert (r.status[b] & oracle.ST_OUTSIDE_DRAFT_SUPPORT) == 0
+        if k < K:
+            w = np.maximum(q[k] - 1.0 / V, 0.0)
+            assert abs(r.W[b] - w.sum()) < 1e-12
+            cum = np.cumsum(w)
+            assert r.t[b] == int(np.argmax(cum > U[b, k, 1] * w.sum())) or r.flags[b] != 0
+
+
+def test_backup_plan_switch():
+    hit = np.array([1, 0, 1, 1, 0, 1], np.uint8)
+    use, sw = oracle.backup_plan(6, hit, all_hit=0, b_star=4)
+    assert sw == 1 and use.tolist() == [0, 1, 0, 0, 1, 0]
+    use, sw = oracle.backup_plan(6, hit, all_hit=0, b_star=7)     # below b*: the primary drafter
+    assert sw == 0 and use.tolist() == [0] * 6
+    use, sw = oracle.backup_plan(6, np.ones(6, np.uint8), all_hit=1, b_star=1)   # every request hit
+    assert sw == 0 and use.tolist() == [0] * 6
