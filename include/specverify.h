@@ -18,6 +18,9 @@
  *   saguaro_verify_cache - spec_verify and saguaro_cache_build fused: one pass over the draft
  *                          rows serves both (the cache's token sets are the leading tokens of
  *                          the same rows the verification reads).
+ *   saguaro_backup_plan  - the batch-aware fallback on a cache miss: which requests take the
+ *                          random-token backup speculator this round (verified by spec_verify
+ *                          with SPEC_UNIFORM_DRAFT).
  *
  * Sources (notation p = draft, q = target, as on the DeepMind page):
  *   [SpS]   "Accelerating LLM Decoding with Speculative Sampling" (DeepMind, arXiv 2302.01318),
@@ -81,9 +84,15 @@ typedef struct {
 
 /* flags for spec_verify */
 enum {
-    SPEC_SAMPLE_DRAFT = 1  /* draft_tokens is an output: s_j is drawn from the processed (and
+    SPEC_SAMPLE_DRAFT = 1, /* draft_tokens is an output: s_j is drawn from the processed (and
                               downweighted) draft row j by inverse CDF in token-id order with
                               Philox lane 2, or is the draft argmax when temperature is 0 */
+    SPEC_UNIFORM_DRAFT = 2 /* the draft distribution of every position is uniform on [0, V):
+                              the random-token backup speculator ([SSD] section 7.1).  No draft
+                              row is read (draft_logits may be NULL), F and C do not apply, and
+                              temperature, top-k and top-p act on the target rows only; with
+                              SPEC_SAMPLE_DRAFT, s_j = floor(u V) for the Philox lane-2 uniform u
+                              (the inverse CDF of the uniform law, taken exactly) */
 };
 
 /* per-request status bits (out_status) */
@@ -106,8 +115,8 @@ enum {
 
 /* Bytes of scratch spec_verify needs for B requests of K draft positions over V tokens (pure
  * host function).  The workspace must be zero-filled before its first use; every call that
- * completes leaves it zero-filled again, so it can be reused without clearing.  It carries no
- * results between calls.  One workspace serves one call at a time. */
+ * completes leaves its arrival counters at zero again, so it can be reused without clearing.
+ * It carries no results between calls.  One workspace serves one call at a time. */
 size_t spec_workspace_bytes(int B, int K, int V);
 
 /* spec_verify - batched speculative-sampling verification ([SpS] sections 1 and 3; [SSD]
@@ -122,7 +131,7 @@ size_t spec_workspace_bytes(int B, int K, int V);
  *   iff it is the argmax of q_j and take t* = argmax q_k.
  *
  *   draft_logits    [B][draft_rows][V]; draft_rows = K or K+1 (row K, used by the cache, is
- *                   ignored here)
+ *                   ignored here); not read with SPEC_UNIFORM_DRAFT
  *   target_logits   [B][K+1][V]
  *   params          [B] spec_params (device)
  *   F, C            downweighted set size (0 = off) and factor in [0, 1] (1 = off)
@@ -185,6 +194,20 @@ int saguaro_verify_cache(const void* draft_logits, const void* target_logits, in
                          uint64_t round, uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host,
                          int32_t* out_k, int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status,
                          int32_t* out_cache, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* saguaro_backup_plan - the batch-aware fallback on a cache miss ([SSD] section 7.1; [SSD-H]
+ * Method, fallback).  Any miss makes the whole batch wait for the fallback, so from a critical
+ * batch size b_star on, the missed requests switch to the fast random-token backup speculator
+ * (verified with SPEC_UNIFORM_DRAFT) while requests that hit keep their cached speculation;
+ * below b_star the primary drafter serves the misses.  The text does not give b_star's formula,
+ * so it is an argument.
+ *   hit             [B] uint8, the lookup's per-request hit flags
+ *   batch           [2] int32, the lookup's {hit count, all-hit flag}
+ *   out_use_backup  [B] int32: 1 where request b takes random tokens this round
+ *   out_switch      [1] int32: 1 when the backup serves this round (a miss and B >= b_star)
+ * Returns SPEC_EINVAL for a null pointer or B < 1. */
+int saguaro_backup_plan(int B, const uint8_t* hit, const int32_t* batch, int b_star, int32_t* out_use_backup,
+                        int32_t* out_switch, hipStream_t stream);
 
 /* saguaro_cache_lookup - hit / miss of the verified outcome.
  * mode 0 ([SSD-H] Method: cache lookup; [SSD] section 7.1): cache [B][sum F] from

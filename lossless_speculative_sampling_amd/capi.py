@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP = 0, -1, -2, -3, -4
 SPEC_FP32, SPEC_BF16 = 0, 1
 SPEC_SAMPLE_DRAFT = 1
+SPEC_UNIFORM_DRAFT = 2
 SPEC_MAX_F = 64
 ST_EMPTY_RESIDUAL = 8
 ST_OUTSIDE_DRAFT_SUPPORT = 16
@@ -28,7 +29,7 @@ ST_DEGENERATE_DOWNWEIGHT = 128
 ST_BAD_PARAM = 256
 
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
-           "saguaro_cache_lookup", "saguaro_verify_cache")
+           "saguaro_cache_lookup", "saguaro_verify_cache", "saguaro_backup_plan")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -57,6 +58,7 @@ class Lib:
         L.saguaro_fanout.argtypes = [_I, _I, _D, _D, _P]
         L.saguaro_cache_build.argtypes = [_P, _I, _I, _I, _I, _P, _I, _D, _D, _P, _P, _P]
         L.saguaro_cache_lookup.argtypes = [_I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]
+        L.saguaro_backup_plan.argtypes = [_I, _P, _P, _I, _P, _P, _P]
         L.saguaro_verify_cache.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
                                            ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                            _P]
@@ -132,20 +134,22 @@ class VerifyOut:
     tokens: torch.Tensor
 
 
-def spec_verify(draft: torch.Tensor, target: torch.Tensor, K: int, params: torch.Tensor, tokens: torch.Tensor,
-                F: int = 0, C: float = 1.0, seed: int = 0, round_: int = 0, flags: int = 0,
+def spec_verify(draft: Optional[torch.Tensor], target: torch.Tensor, K: int, params: torch.Tensor,
+                tokens: torch.Tensor, F: int = 0, C: float = 1.0, seed: int = 0, round_: int = 0, flags: int = 0,
                 workspace: Optional[torch.Tensor] = None, out: Optional[VerifyOut] = None, stream=None) -> VerifyOut:
     """draft [B][Kd][V] and target [B][K+1][V] device logits; tokens [B][K] int32 (in, or out under
-    SPEC_SAMPLE_DRAFT).  Returns the outputs (allocated here unless `out` is given)."""
-    B, Kd, V = draft.shape
-    dev = draft.device
+    SPEC_SAMPLE_DRAFT).  With SPEC_UNIFORM_DRAFT draft may be None.  Returns the outputs (allocated
+    here unless `out` is given)."""
+    B, _, V = target.shape
+    Kd = draft.shape[1] if draft is not None else K
+    dev = target.device
     if out is None:
         out = VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                         torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                         tokens)
     if workspace is None:
         workspace = new_workspace(B, K, V, dev)
-    rc = load().cdll.spec_verify(_ptr(draft), Kd, _ptr(target), dtype_code(draft), B, K, V, _ptr(params), F,
+    rc = load().cdll.spec_verify(_ptr(draft), Kd, _ptr(target), dtype_code(target), B, K, V, _ptr(params), F,
                                  ctypes.c_float(C), _ptr(tokens), seed, round_, flags, _ptr(out.k), _ptr(out.tstar),
                                  _ptr(out.resid_mass), _ptr(out.status), _ptr(workspace), workspace.numel(),
                                  _stream(stream))
@@ -225,3 +229,13 @@ def saguaro_cache_lookup(mode: int, cache: torch.Tensor, fanout_or_shape, K: int
                                           _ptr(slot), _ptr(hit), _ptr(batch), _stream(stream))
     _check("saguaro_cache_lookup", rc)
     return slot, hit, batch
+
+
+def saguaro_backup_plan(hit: torch.Tensor, batch: torch.Tensor, b_star: int, stream=None):
+    """(use_backup [B] int32, switch [1] int32) on the device: the batch-aware random-token fallback."""
+    B = hit.shape[0]
+    use = torch.empty(B, dtype=torch.int32, device=hit.device)
+    sw = torch.empty(1, dtype=torch.int32, device=hit.device)
+    rc = load().cdll.saguaro_backup_plan(B, _ptr(hit), _ptr(batch), b_star, _ptr(use), _ptr(sw), _stream(stream))
+    _check("saguaro_backup_plan", rc)
+    return use, sw

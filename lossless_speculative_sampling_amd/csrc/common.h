@@ -88,6 +88,19 @@ __device__ __forceinline__ double uniform_at(uint64_t seed, uint64_t round, uint
     return word_to_uniform(x.w[word]);
 }
 
+// A draw from the uniform law on [0, V) by inverse CDF, floor(u V), for the uniform u of word
+// w: u = (2 (w >> 12) + 1) / 2^53 exactly, so the floor is taken on the exact 128-bit product.
+__device__ __forceinline__ int uniform_token_of(uint64_t w, int V) {
+    const uint64_t m = 2 * (w >> 12) + 1;
+    const uint64_t lo = m * (uint64_t)V, hi = __umul64hi(m, (uint64_t)V);
+    return (int)((hi << 11) | (lo >> 53));
+}
+// The backup speculator's draft token for request b, position j (word 2, the draft lane).
+__device__ __forceinline__ int uniform_draft_token(uint64_t seed, uint64_t round, uint64_t b, uint64_t j, int V) {
+    Block4 x = philox4x64_10(round, b, j, 0, seed, 0);
+    return uniform_token_of(x.w[2], V);
+}
+
 // ------------------------------------------------------------------------------------------
 // Cross-lane moves.  Reductions and scans use DPP (operand permutations inside VALU
 // instructions) and v_readlane, never ds_bpermute: those go through the LDS unit, where they

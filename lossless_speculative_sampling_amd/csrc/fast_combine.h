@@ -714,8 +714,8 @@ __device__ __forceinline__ void combine(const FastArgs& f, UnitSmem& us, int uni
         }
     }
     // the drafted token's processed probabilities for the acceptance test: lane 0 of wave 0
-    // (target row) and of wave 1 (draft row, after its set)
-    if (dw && rows > 1 && s_tok >= 0 && s_tok < a.V && wave < 2 && lane == 0 && !us.rv[wave].greedy) {
+    // (target row) and of wave 1 (draft row, after its set; none for a uniform draft)
+    if (dw && s_tok >= 0 && s_tok < a.V && wave < rows && lane == 0 && !us.rv[wave].greedy) {
         const double p = prob_of_s(us, wave, s_tok, wave == 1);
         if (wave == 0) us.qs = p;
         else us.ps = p;

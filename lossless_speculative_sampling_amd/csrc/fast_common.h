@@ -180,6 +180,7 @@ struct FastArgs {
     // the Saguaro outcome cache, built from the same pass over the draft rows (draft row K is
     // read by the bonus position's unit)
     int cache;
+    int uniform;  // uniform draft distribution (random-token backup): no draft rows at all
     int budget;
     int32_t* out_cache;
     Fanout fan;

@@ -453,21 +453,22 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
     if (!param_ok) {
         status = kStBadParam;
     } else {
-        const bool vd = P.j < a.K;  // the draft row is verified (not only listed for the cache)
+        const bool vd = P.j < a.K;      // the drafted token is verified here
+        const bool vrow = vd && two;     // against a draft row (not the uniform draft)
         combine(f, us, unit, P.j, two ? 2 : 1, prm, vd, s_tok);
-        const bool bad = us.rv[0].bad || (vd && us.rv[1].bad);
-        fallback = (!bad && (us.rv[0].overflow || (vd && us.rv[1].overflow))) ? 1 : 0;
+        const bool bad = us.rv[0].bad || (vrow && us.rv[1].bad);
+        fallback = (!bad && (us.rv[0].overflow || (vrow && us.rv[1].overflow))) ? 1 : 0;
         if (bad) {
             status = kStBadLogit;
         } else if (!fallback) {
-            if (vd && us.rv[1].degenerate) status |= kStDegenerate;
+            if (vrow && us.rv[1].degenerate) status |= kStDegenerate;
             if (!tok_ok) {
                 status |= kStBadToken;
             } else if (vd) {
                 if (us.rv[0].greedy) {
                     accept = (s_tok == us.rv[0].argmax) ? 1 : 0;
                 } else {
-                    const double ps = us.ps, qs = us.qs;
+                    const double ps = f.uniform ? 1.0 / (double)a.V : us.ps, qs = us.qs;
                     if (!(ps > 0.0)) status |= kStOutside;
                     const double u = sm.u_acc;
                     accept = (u * ps < qs) ? 1 : 0;
@@ -502,6 +503,8 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
             for (int x = got + lane; x < Fj; x += kWave) out[x] = -1;
         }
     }
+    if (threadIdx.x == 0 && P.j < a.K && f.uniform && (a.flags & SPEC_SAMPLE_DRAFT))
+        a.tokens[(size_t)P.b * a.K + P.j] = s_tok;  // the drawn backup token is an output
     if (threadIdx.x == 0) {
         sm.unit_code = unit_code(accept, fallback, status);
         UnitFast* U = reinterpret_cast<UnitFast*>(f.ws + f.L.units) + unit;
@@ -658,13 +661,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     const int c0 = slice * kSliceCols;
     // the draft row of position j: verified (j < K) or, at the bonus position, only listed for
     // the outcome cache
-    const bool two = j < a.K || (f.cache && f.fan.f[j] > 0);
+    const bool two = !f.uniform && (j < a.K || (f.cache && f.fan.f[j] > 0));
     const spec_params prm = a.params[P.b];
     const bool param_ok = params_ok(prm);
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)P.b * (a.K + 1) + j) * stride;
     const uint16_t* drow = two ? static_cast<const uint16_t*>(a.draft) + ((size_t)P.b * a.draft_rows + j) * stride : nullptr;
-    const int s_tok = j < a.K ? a.tokens[(size_t)P.b * a.K + j] : -1;
+    // (the backup speculator's tokens are drawn here: every workgroup of the unit draws the same)
+    const bool draw = f.uniform && (a.flags & SPEC_SAMPLE_DRAFT);
+    const int s_tok = j < a.K ? (draw ? uniform_draft_token(a.seed, a.round, P.b, j, a.V) : a.tokens[(size_t)P.b * a.K + j])
+                              : -1;
     const bool tok_ok = j == a.K || (s_tok >= 0 && s_tok < a.V);
 
     // the draws of position j (acceptance, residual / bonus: words 0 and 1 of one Philox
@@ -695,7 +701,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
         uint32_t sb0 = 0u, sb1 = 0u;
         if (threadIdx.x == kWave && j < a.K && tok_ok) {
             sb0 = trow[s_tok];
-            sb1 = drow[s_tok];
+            sb1 = two ? drow[s_tok] : 0u;  // (no draft row with the uniform draft)
         }
         __syncthreads();
         count_row(sm, 0, c0, a.V, vq);

@@ -377,7 +377,8 @@ __device__ __forceinline__ double tab_at(const char* base, uint32_t off) {
 // 512-column chunk: table lookups for every element; a thread's 8 columns of one chunk that
 // met a marker are recomputed exactly.
 __device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, int b, int slice, int half, int c0, bool two,
-                                               const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads]) {
+                                               bool uni, const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads]) {
+    const double pu = 1.0 / (double)f.a.V;  // the uniform draft's probability
     const VerifyArgs& a = f.a;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -404,6 +405,9 @@ __device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, i
                     if (tip.any) apply_ties(tip, op, cq + 2 * d, p0, p1);
                     s += max(q0 - p0, 0.0);
                     s += max(q1 - p1, 0.0);
+                } else if (uni) {
+                    s += max(q0 - pu, 0.0);
+                    s += max(q1 - pu, 0.0);
                 } else {
                     s += q0;
                     s += q1;
@@ -428,6 +432,8 @@ __device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, i
                         pe = pe < -kMarkSeen ? final_prob(sm.rf[1], sm.inv[1], sm.eff[1][0], sm.eff[1][1], hp, col, true)
                                              : apply_ties1(tip, op, col, pe);
                         s += max(qe - pe, 0.0);
+                    } else if (uni) {
+                        s += max(qe - pu, 0.0);
                     } else {
                         s += qe;
                     }
@@ -528,7 +534,10 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
     const RowFinal& rp = sm.rf[1];
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)b * (K + 1) + k) * stride;
-    const uint16_t* drow = k < K ? static_cast<const uint16_t*>(a.draft) + ((size_t)b * a.draft_rows + k) * stride : nullptr;
+    const bool uni = k < K && f.uniform;
+    const uint16_t* drow =
+        (k < K && !f.uniform) ? static_cast<const uint16_t*>(a.draft) + ((size_t)b * a.draft_rows + k) * stride : nullptr;
+    const double pu = 1.0 / (double)a.V;
     // columns to scan: the picked chunk (mode 1) or the whole target row (mode 2)
     int lo, hi;
     double base;
@@ -557,6 +566,8 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
             if (mode == 1 && drow) {
                 const double pv = final_prob(rp, sm.inv[1], idk_p, idp_p, drow[col], col, true);
                 w = qv > pv ? qv - pv : 0.0;
+            } else if (mode == 1 && uni) {
+                w = qv > pu ? qv - pu : 0.0;
             } else {
                 w = qv;
             }
@@ -696,7 +707,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     if (slice >= f.nS) return;
     const int unit = b * (a.K + 1) + k;
     const uint32_t status = req[2];
-    const bool two = k < a.K;
+    const bool two = k < a.K && !f.uniform;   // a draft row at the rejected position
+    const bool uni = k < a.K && f.uniform;    // the uniform draft there (residual (q - 1/V)+)
     const int c0 = slice * kSliceCols;
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)b * (a.K + 1) + k) * stride;
@@ -755,7 +767,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         const bool writer = (uc.key == 0u || uc.explicit_id >= 0) ? slice == 0 : slice == uc.owner;
         if (writer && half == 0) reinterpret_cast<int32_t*>(f.ws + f.L.idcut)[b * 4 + threadIdx.x] = sm.eff[r][c];
     }
-    residual_slice(f, sm, b, slice, half, c0, two, vq, vp);
+    residual_slice(f, sm, b, slice, half, c0, two, uni, vq, vp);
     if (!arrive_last(f, sm, b, 2 * f.nS)) return;
     finalize_residual(f, sm, b, k, status, sm.u_res);
 }

@@ -29,7 +29,8 @@ FastPlan fast_plan(int B, int K, int V) {
 }
 
 bool fast_path_applies(const VerifyArgs& a) {
-    if (a.dtype != SPEC_BF16 || (a.flags & SPEC_SAMPLE_DRAFT)) return false;
+    // drafted tokens are sampled here only from the uniform draft (random-token backup)
+    if (a.dtype != SPEC_BF16 || ((a.flags & SPEC_SAMPLE_DRAFT) && !(a.flags & SPEC_UNIFORM_DRAFT))) return false;
     if (a.V % 8 != 0 || a.V < 2048) return false;
     if ((reinterpret_cast<uintptr_t>(a.draft) & 15) || (reinterpret_cast<uintptr_t>(a.target) & 15)) return false;
     const int nS = (a.V + kSliceCols - 1) / kSliceCols;
@@ -46,6 +47,7 @@ static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t
     f.ws = static_cast<char*>(ws);
     f.L = layout(a.B, p.units, p.nS);
     f.cache = c ? 1 : 0;
+    f.uniform = (a.flags & SPEC_UNIFORM_DRAFT) ? 1 : 0;
     f.budget = c ? c->budget : 0;
     f.out_cache = c ? c->out_cache : nullptr;
     if (c) f.fan = c->fanout;

@@ -78,4 +78,14 @@ __global__ void downweight_kernel(DownweightArgs a);
 __global__ void cache_build_kernel(CacheArgs a);
 __global__ void cache_lookup_kernel(LookupArgs a);
 
+struct BackupArgs {
+    int B;
+    const uint8_t* hit;
+    const int32_t* batch;
+    int b_star;
+    int32_t* out_use_backup;
+    int32_t* out_switch;
+};
+__global__ void backup_plan_kernel(BackupArgs a);
+
 }  // namespace sv

@@ -138,4 +138,14 @@ __global__ __launch_bounds__(1024) void cache_lookup_kernel(LookupArgs a) {
     }
 }
 
+// The batch-aware fallback on a cache miss (SSD reading notes, section 7.1): any miss makes the
+// whole batch wait, so from the critical batch size b* on the missed requests take the
+// random-token backup; the requests that hit keep their cached speculation.
+__global__ void backup_plan_kernel(BackupArgs a) {
+    const int sw = (a.batch[1] == 0 && a.B >= a.b_star) ? 1 : 0;
+    for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < a.B; b += gridDim.x * blockDim.x)
+        a.out_use_backup[b] = (sw && !a.hit[b]) ? 1 : 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.out_switch = sw;
+}
+
 }  // namespace sv

@@ -395,17 +395,20 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
     const char* trow = static_cast<const char*>(a.target) + ((size_t)b * (a.K + 1) + j) * tstride;
     RowRef rq{trow, a.dtype, a.V};
     process_row(rq, prm.temperature, prm.top_k, prm.top_p, 0, 1.0, false, stq, sh);
+    // with a uniform draft (the random-token backup) p_j(x) = 1/V and no draft row is read
+    const bool uni = (a.flags & SPEC_UNIFORM_DRAFT) != 0;
+    const double p_uni = 1.0 / (double)a.V;
     RowRef rp{nullptr, a.dtype, a.V};
-    if (j < a.K) {
+    if (j < a.K && !uni) {
         rp.row = static_cast<const char*>(a.draft) + ((size_t)b * a.draft_rows + j) * tstride;
         const bool dw = a.F > 0 && a.C < 1.0f;
         process_row(rp, prm.temperature, prm.top_k, prm.top_p, a.F, (double)a.C, dw, stp, sh);
     }
-    if (stq.bad || (j < a.K && stp.bad)) {
+    if (stq.bad || (j < a.K && !uni && stp.bad)) {
         if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, kStBadLogit, -1};
         return;
     }
-    uint32_t status = (j < a.K && stp.degenerate) ? kStDegenerate : 0u;
+    uint32_t status = (j < a.K && !uni && stp.degenerate) ? kStDegenerate : 0u;
     const bool greedy = stq.greedy != 0;
 
     if (j == a.K) {  // bonus position
@@ -424,7 +427,9 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
     // draft token s_j (sampled here under SPEC_SAMPLE_DRAFT)
     int s;
     if (a.flags & SPEC_SAMPLE_DRAFT) {
-        if (greedy) {
+        if (uni) {
+            s = uniform_draft_token(a.seed, a.round, b, j, a.V);
+        } else if (greedy) {
             s = stp.argmax;
         } else {
             const double x = uniform_at(a.seed, a.round, b, j, 2);
@@ -444,7 +449,7 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
     if (greedy) {
         accept = (s == stq.argmax);
     } else {
-        const double ps = rs_prob_dw(stp, load_logit(rp.row, a.dtype, s), s);
+        const double ps = uni ? p_uni : rs_prob_dw(stp, load_logit(rp.row, a.dtype, s), s);
         const double qs = rs_prob(stq, load_logit(rq.row, a.dtype, s), s);
         if (!(ps > 0.0)) status |= kStOutside;
         const double u = uniform_at(a.seed, a.round, b, j, 0);
@@ -463,7 +468,7 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
         // residual (q - p')+ at this position; rows are read pairwise by token id
         auto resid = [&](int i, float zq) {
             const double q = rs_prob(stq, zq, i);
-            const double p = rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i);
+            const double p = uni ? p_uni : rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i);
             return q > p ? q - p : 0.0;
         };
         t = inverse_cdf(rq, v, resid, sh, &W);

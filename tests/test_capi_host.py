@@ -70,7 +70,10 @@ def test_verify_argument_errors_return_before_launch():
     assert _verify_rc(F=capi.SPEC_MAX_F + 1) == capi.SPEC_EINVAL
     assert _verify_rc(C=1.5) == capi.SPEC_EINVAL
     assert _verify_rc(C=float("nan")) == capi.SPEC_EINVAL
-    assert _verify_rc(flags=2) == capi.SPEC_EINVAL
+    assert _verify_rc(flags=4) == capi.SPEC_EINVAL
+    assert _verify_rc(flags=capi.SPEC_UNIFORM_DRAFT, target=None) == capi.SPEC_EINVAL
+    assert _verify_rc(flags=capi.SPEC_UNIFORM_DRAFT, draft=None, dtype=7) == capi.SPEC_EDTYPE
+    assert _verify_rc(flags=capi.SPEC_UNIFORM_DRAFT, draft=None, ws=None) == capi.SPEC_EWORKSPACE
     assert _verify_rc(dtype=7) == capi.SPEC_EDTYPE
     assert _verify_rc(ws=None) == capi.SPEC_EWORKSPACE
     assert _verify_rc(ws_bytes=capi.spec_workspace_bytes(16, 5, 128) - 1) == capi.SPEC_EWORKSPACE
@@ -94,6 +97,9 @@ def test_other_entry_points_argument_errors():
     assert L.saguaro_cache_lookup(2, fake, ctypes.cast(shape, ctypes.c_void_p), 0, 4, fake, fake, fake, fake, None,
                                   None) == capi.SPEC_EINVAL
     assert L.saguaro_cache_lookup(0, fake, None, 5, 4, fake, fake, fake, fake, None, None) == capi.SPEC_EINVAL
+    assert L.saguaro_backup_plan(0, fake, fake, 8, fake, fake, None) == capi.SPEC_EINVAL
+    assert L.saguaro_backup_plan(4, None, fake, 8, fake, fake, None) == capi.SPEC_EINVAL
+    assert L.saguaro_backup_plan(4, fake, fake, 8, fake, None, None) == capi.SPEC_EINVAL
 
 
 def test_generator_shapes_and_determinism():

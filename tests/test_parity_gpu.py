@@ -188,9 +188,10 @@ def test_tree_chains_and_branch_reuse():
 # edge cases
 # ------------------------------------------------------------------------------------------
 def _work(draft, target, dtype, K, T, tk, tp, F=0, C=1.0, seed=99):
-    B, _, V = draft.shape
+    B, _, V = target.shape
     Tv, kv, pv = (np.broadcast_to(np.asarray(x), (B,)).copy() for x in (T, tk, tp))
-    return synth.Workload("edge", dtype, B, K, V, np.ascontiguousarray(draft), np.ascontiguousarray(target),
+    draft = None if draft is None else np.ascontiguousarray(draft)
+    return synth.Workload("edge", dtype, B, K, V, draft, np.ascontiguousarray(target),
                           Tv.astype(np.float32), kv.astype(np.int32), pv.astype(np.float32), F=F, C=C, seed=seed)
 
 
@@ -359,3 +360,86 @@ def test_fast_workspace_reuse_and_determinism():
     o1 = run_oracle(w.without_cache_row(), tokens=tok.cpu().numpy(), round_=1)
     ok = o1.flags == 0
     assert (outs[1][0][ok] == o1.k[ok]).all() and (outs[1][1][ok] == o1.t[ok]).all()
+
+
+# ------------------------------------------------------------------------------------------
+# random-token backup speculation: the draft distribution is uniform on the vocabulary
+# ------------------------------------------------------------------------------------------
+def check_uniform(w, tokens=None, label=""):
+    """Uniform-draft verification (SPEC_UNIFORM_DRAFT, no draft logits) against the oracle."""
+    sample = tokens is None
+    say(f"[parity] uniform {label} B={w.B} K={w.K} V={w.V} dtype={w.dtype} sample={sample}")
+    prm = capi.params_tensor(w.temperature, w.top_k, w.top_p)
+    tok = torch.zeros((w.B, w.K), dtype=torch.int32, device="cuda") if sample else dev(np.asarray(tokens, np.int32))
+    flags = capi.SPEC_UNIFORM_DRAFT | (capi.SPEC_SAMPLE_DRAFT if sample else 0)
+    out = capi.spec_verify(None, dev(w.target), w.K, prm, tok, seed=w.seed, flags=flags)
+    torch.cuda.synchronize()
+    k, t, W = out.k.cpu().numpy(), out.tstar.cpu().numpy(), out.resid_mass.cpu().numpy()
+    st, gtok = out.status.cpu().numpy().astype(np.uint32), out.tokens.cpu().numpy()
+    o = oracle.verify(None, w.target, w.dtype, w.K, w.params(), tokens=tokens, seed=w.seed, uniform_draft=True)
+    ok = o.flags == 0
+    bad = np.flatnonzero(ok & ((k != o.k) | (t != o.t) | (st != o.status)))
+    assert len(bad) == 0, (f"{len(bad)} mismatches, first {bad[:5]}: gpu k={k[bad[:5]]} t={t[bad[:5]]} "
+                           f"st={st[bad[:5]]} | oracle k={o.k[bad[:5]]} t={o.t[bad[:5]]} st={o.status[bad[:5]]}")
+    if sample:
+        # the drafted tokens are uniform draws, independent of the logits: equal on every request
+        assert (gtok == o.tokens).all()
+    np.testing.assert_allclose(W[ok], o.W[ok], rtol=RTOL[w.dtype], atol=1e-6)
+    say(f"[parity] uniform {label} ok: flagged {int((~ok).sum())} of {w.B}; mean k {k.mean():.3f}")
+    return o
+
+
+def test_uniform_draft_full_size():
+    w = synth.saguaro(B=16, K=5, V=128256)
+    o = check_uniform(w, label="saguaro-size")
+    rng = np.random.default_rng(5)
+    check_uniform(w, tokens=rng.integers(0, w.V, (w.B, w.K)), label="saguaro-size-given")
+    # a flat target accepts almost every uniform draft token
+    flat = synth.f32_to_bf16_bits(np.zeros((w.B, w.K + 1, w.V), np.float32))
+    wf = _work(None, flat, synth.BF16, w.K, 1.0, 0, 1.0, seed=7)
+    of = check_uniform(wf, label="flat-target")
+    assert (of.k == w.K).all()
+    assert o.k.mean() < of.k.mean()
+
+
+@pytest.mark.parametrize("V", [2048, 16392, 151936])
+def test_uniform_draft_fast_parameter_mix(V):
+    rng = np.random.default_rng(V + 1)
+    B, K = 24, 3
+    T = rng.choice([0.0, 0.6, 1.0, 1.5], B)
+    tk = rng.choice([0, 1, 5, 64, 200, 3000], B)
+    tp = rng.choice([0.05, 0.5, 0.9, 1.0], B)
+    target = synth.zipf_rows(rng, B * (K + 1), V, slope=0.6).reshape(B, K + 1, V)
+    w = _work(None, synth.f32_to_bf16_bits(target), synth.BF16, K, T, tk, tp, seed=31)
+    check_uniform(w, label=f"fast-mix V={V}")
+    check_uniform(w, tokens=rng.integers(0, V, (B, K)), label=f"fast-mix-given V={V}")
+
+
+@pytest.mark.parametrize("dtype", [synth.FP32, synth.BF16])
+@pytest.mark.parametrize("V", [1, 2, 63, 1000, 4097])
+def test_uniform_draft_generic_shapes(dtype, V):
+    rng = np.random.default_rng(V * 3 + dtype)
+    B, K = 40, 4
+    t = rng.normal(0, 1.5, (B, K + 1, V)).astype(np.float32)
+    if dtype == synth.BF16:
+        t = synth.f32_to_bf16_bits(t)
+    T = rng.choice([0.0, 0.5, 1.0, 2.0], B)
+    tk = rng.choice([0, 1, 3, 50], B)
+    tp = rng.choice([0.2, 0.9, 1.0], B)
+    w = _work(None, t, dtype, K, T, tk, tp, seed=3)
+    check_uniform(w, label=f"generic V={V}")
+    check_uniform(w, tokens=rng.integers(0, V, (B, K)), label=f"generic-given V={V}")
+
+
+def test_backup_plan():
+    rng = np.random.default_rng(11)
+    for B in (1, 7, 64, 1000):
+        for p_hit in (0.0, 0.5, 0.97, 1.0):
+            hit = (rng.random(B) < p_hit).astype(np.uint8)
+            batch = np.array([hit.sum(), int(hit.all())], np.int32)
+            for b_star in (1, 8, 64, 5000):
+                use, sw = capi.saguaro_backup_plan(dev(hit), dev(batch), b_star)
+                o_use, o_sw = oracle.backup_plan(B, hit, int(batch[1]), b_star)
+                assert int(sw.cpu()[0]) == o_sw, (B, p_hit, b_star)
+                assert (use.cpu().numpy() == o_use).all(), (B, p_hit, b_star)
+    say("[parity] backup plan ok")
