@@ -89,21 +89,31 @@ def bench_other(name, args):
     elif name == "c3":
         w = synth.saguaro(B=16, K=5, V=128256, cache_row=False)
         desc = "saguaro verify: B=16, K=5, V=128256 bf16 Zipf logits, top-p 0.95, sigma F=4 C=0.3"
+    elif name == "backup":
+        w = synth.saguaro(B=16, K=5, V=128256, cache_row=False)
+        w.draft = None
+        desc = ("random-token backup round: B=16, K=5, V=128256 bf16 Zipf target logits, top-p 0.95, "
+                "uniform draft, drafted tokens drawn in the call")
     elif name == "c5":
         w = synth.tree(n_req=64)
         desc = "branch-tree chains: 64 requests x 8 branches, gamma=7, V=151936 bf16, T=0.8, top-k 50, reuse lookup"
     else:
         raise SystemExit(f"unknown config {name}")
     B, K, V = w.B, w.K, w.V
-    step_bytes = int(w.draft.nbytes + w.target.nbytes)
+    uniform = w.draft is None
+    step_bytes = int(w.target.nbytes) + (0 if uniform else int(w.draft.nbytes))
     copies = max(1, -(-2 * MALL_BYTES // step_bytes) + 1) if step_bytes < 2 * MALL_BYTES else 1
     as_dev = (lambda a: torch.from_numpy(a.view(np.int16)).to(dev)) if w.dtype == synth.BF16 else \
         (lambda a: torch.from_numpy(a).to(dev))
-    d0, t0 = as_dev(w.draft), as_dev(w.target)
-    drafts = [d0] + [d0.clone() for _ in range(copies - 1)]
+    d0, t0 = (None if uniform else as_dev(w.draft)), as_dev(w.target)
+    drafts = [d0] * copies if uniform else [d0] + [d0.clone() for _ in range(copies - 1)]
     targets = [t0] + [t0.clone() for _ in range(copies - 1)]
     prm = capi.params_tensor(w.temperature, w.top_k, w.top_p, device=dev)
-    if w.tokens is not None:
+    flags = 0
+    if uniform:
+        tokens = torch.zeros((B, K), dtype=torch.int32, device=dev)
+        flags = capi.SPEC_UNIFORM_DRAFT | capi.SPEC_SAMPLE_DRAFT
+    elif w.tokens is not None:
         tokens = torch.from_numpy(w.tokens.astype(np.int32)).to(dev)
     else:
         tokens = torch.zeros((B, K), dtype=torch.int32, device=dev)
@@ -116,7 +126,7 @@ def bench_other(name, args):
 
     def step(i):
         capi.spec_verify(drafts[i % copies], targets[i % copies], K, prm, tokens, F=w.F, C=w.C, seed=w.seed, round_=i,
-                         workspace=ws, out=out)
+                         flags=flags, workspace=ws, out=out)
         if br is not None:
             capi.saguaro_cache_lookup(1, br, [w.kappa, w.gamma], 0, B // w.kappa, out.k, out.tstar)
 
@@ -151,7 +161,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"],
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "backup"],
                     help="c4 (default): the headline workload; the others print their own line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
@@ -184,7 +194,8 @@ def main():
 
     w = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
     B, K, V = w.B, w.K, w.V
-    step_bytes = int(w.draft.nbytes + w.target.nbytes)          # every logit once (cache row included)
+    uniform = w.draft is None
+    step_bytes = int(w.target.nbytes) + (0 if uniform else int(w.draft.nbytes))          # every logit once (cache row included)
     copies = max(2, -(-2 * MALL_BYTES // step_bytes) + 1)
     d0 = torch.from_numpy(w.draft.view(np.int16)).to(dev)
     t0 = torch.from_numpy(w.target.view(np.int16)).to(dev)
