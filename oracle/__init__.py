@@ -66,8 +66,10 @@ def lib():
         L.orc_cache_build.argtypes = [P, i32, i32, i32, i32, P, P, P, i32]
         L.orc_cache_lookup.argtypes = [i32, P, P, i32, i32, P, P, P, P, P]
         L.orc_threads_used.argtypes = [i32]
+        L.orc_signposts.argtypes = [P, i32, i32, i32, i32, P, P, P, i32]
+        L.orc_tree_lookup.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, P]
         for fn in ("orc_downweight", "orc_verify_u", "orc_verify", "orc_fanout", "orc_cache_build",
-                   "orc_cache_lookup", "orc_threads_used"):
+                   "orc_cache_lookup", "orc_threads_used", "orc_signposts", "orc_tree_lookup"):
             getattr(L, fn).restype = i32
         _lib = L
     return _lib
@@ -238,3 +240,31 @@ def backup_plan(B, hit, all_hit, b_star):
     sw = np.zeros(1, np.int32)
     lib().orc_backup_plan(B, _p(hit), int(all_hit), b_star, _p(use), _p(sw))
     return use, int(sw[0])
+
+
+def signposts(logits, dtype, kappa, nthreads=0):
+    """Mirror-SD signposts of early-exit logits [B][V]: (ids [B][kappa], log p~ [B][kappa], status [B])."""
+    logits = np.ascontiguousarray(logits)
+    B, V = logits.shape
+    ids = np.zeros((B, kappa), np.int32)
+    lp = np.zeros((B, kappa), np.float64)
+    st = np.zeros(B, np.uint32)
+    _check(lib().orc_signposts(_p(logits), dtype, B, V, kappa, _p(ids), _p(lp), _p(st), nthreads), "signposts")
+    return ids, lp, st
+
+
+def tree_lookup(tokens, parents, path, k, t):
+    """Reuse of the committed prefix against draft trees [B][N]: (node [B], hit [B], batch [2])."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    parents = np.ascontiguousarray(parents, dtype=np.int32)
+    path = np.ascontiguousarray(path, dtype=np.int32)
+    k = np.ascontiguousarray(k, dtype=np.int32)
+    t = np.ascontiguousarray(t, dtype=np.int32)
+    B, N = tokens.shape
+    gamma = path.shape[1]
+    node = np.zeros(B, np.int32)
+    hit = np.zeros(B, np.uint8)
+    batch = np.zeros(2, np.int32)
+    _check(lib().orc_tree_lookup(_p(tokens), _p(parents), B, N, gamma, _p(path), _p(k), _p(t), _p(node), _p(hit),
+                                 _p(batch)), "tree_lookup")
+    return node, hit, batch

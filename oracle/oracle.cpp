@@ -10,7 +10,10 @@
 //   * hyper.ai SSD/Saguaro summary, "Method" (the fan-out closed form and sigma_{F,C});
 //   * Mirror-SD reading notes, sections 2 and 3.2 (greedy verify, verification-vs-reuse rule);
 //   * SSD reading notes section 7.1 and the hyper.ai summary's fallback paragraph (the
-//     batch-aware switch to a random-token backup speculator on a cache miss).
+//     batch-aware switch to a random-token backup speculator on a cache miss);
+//   * Mirror-SD reading notes sections 3.1-3.3 (the early-exit signposts: top-kappa tokens of
+//     the layer-l_e distribution with their log-probabilities; reuse of a committed prefix
+//     against a draft tree that branches below its roots, as in the worked example).
 //
 // Notation follows the DeepMind page: p = draft distribution, q = target distribution.
 // Only tests/, the smoke check and the bench's CPU-baseline leg may load this library; the
@@ -537,6 +540,100 @@ void orc_backup_plan(int B, const uint8_t* hit, int all_hit, int b_star, int32_t
     const int sw = (all_hit == 0 && B >= b_star) ? 1 : 0;
     for (int b = 0; b < B; ++b) out_use_backup[b] = (sw && !hit[b]) ? 1 : 0;
     *out_switch = sw;
+}
+
+// Mirror-SD signposts (reading notes 3.1, 3.3): the LM head at the early-exit layer gives a
+// distribution p~ over the vocabulary; the message to the draft is its kappa most likely tokens
+// with their log-probabilities.  Read here as the softmax of the given logits at temperature 1,
+// tokens in the common order (logit descending, id ascending), log p~(v) = z_v - m - log S with
+// m the row maximum and S = sum_i exp(z_i - m).  Entries past the vocabulary are id -1 with
+// log-probability -inf; a row with a NaN or +inf logit, or no finite one, gets status
+// ST_BAD_LOGIT, ids -1 and NaN log-probabilities.
+int orc_signposts(const void* logits, int dtype, int B, int V, int kappa, int32_t* out_ids, double* out_logp,
+                  uint32_t* out_status, int nthreads) {
+    if (!logits || !out_ids || !out_logp || B < 1 || V < 1 || kappa < 1 || (dtype != kFP32 && dtype != kBF16))
+        return -1;
+    parallel_for(B, nthreads, [&](int b) {
+        std::vector<double> z;
+        load_row(logits, dtype, (size_t)b, V, z);
+        int32_t* ids = out_ids + (size_t)b * kappa;
+        double* lp = out_logp + (size_t)b * kappa;
+        if (row_is_bad(z)) {
+            for (int i = 0; i < kappa; ++i) {
+                ids[i] = -1;
+                lp[i] = std::numeric_limits<double>::quiet_NaN();
+            }
+            if (out_status) out_status[b] = ST_BAD_LOGIT;
+            return;
+        }
+        const std::vector<int> ord = desc_order(z);
+        const double m = z[ord[0]];
+        double S = 0.0;
+        for (int i = 0; i < V; ++i) S += std::exp(z[i] - m);
+        const double logS = std::log(S);
+        for (int i = 0; i < kappa; ++i) {
+            if (i < V) {
+                ids[i] = ord[i];
+                lp[i] = z[ord[i]] - m - logS;
+            } else {
+                ids[i] = -1;
+                lp[i] = -std::numeric_limits<double>::infinity();
+            }
+        }
+        if (out_status) out_status[b] = 0;
+    });
+    return 0;
+}
+
+// Mirror-SD reuse against a draft tree (reading notes 3.2-3.3).  Each request's tree is N nodes
+// (token, parent) with parents listed before their children; parent -1 marks a root (a signpost
+// the draft expanded).  The verified path holds gamma draft tokens; with k accepted and
+// correction t*, the committed prefix is (path[0..k-1], t*).  The reuse node is the lowest
+// node whose chain of ancestors, read from its root down, is exactly that prefix (so it sits at
+// depth k + 1); -1 when none, -2 when all gamma tokens were accepted.  A node with a negative
+// token or a parent outside [-1, n) is not part of the tree, nor is anything below it.
+int orc_tree_lookup(const int32_t* tokens, const int32_t* parents, int B, int N, int gamma, const int32_t* path,
+                    const int32_t* kk, const int32_t* tt, int32_t* out_node, uint8_t* out_hit, int32_t* out_batch) {
+    if (!tokens || !parents || !path || !kk || !tt || !out_node || !out_hit || B < 1 || N < 1 || gamma < 1)
+        return -1;
+    int hits = 0;
+    for (int b = 0; b < B; ++b) {
+        const int32_t* tok = tokens + (size_t)b * N;
+        const int32_t* par = parents + (size_t)b * N;
+        const int k = kk[b], t = tt[b];
+        int res = -1;
+        if (k == gamma) {
+            res = -2;
+        } else if (k >= 0 && k < gamma && t >= 0) {
+            std::vector<int32_t> want(path + (size_t)b * gamma, path + (size_t)b * gamma + k);
+            want.push_back(t);
+            for (int n = 0; n < N && res < 0; ++n) {
+                // ancestors of n, n first; give up once the chain is longer than the prefix
+                std::vector<int32_t> chain;
+                int cur = n;
+                bool valid = true;
+                while (cur != -1) {
+                    if (tok[cur] < 0 || par[cur] < -1 || par[cur] >= cur || (int)chain.size() > k) {
+                        valid = false;
+                        break;
+                    }
+                    chain.push_back(tok[cur]);
+                    cur = par[cur];
+                }
+                if (!valid || (int)chain.size() != k + 1) continue;
+                std::reverse(chain.begin(), chain.end());
+                if (chain == want) res = n;
+            }
+        }
+        out_node[b] = res;
+        out_hit[b] = res >= 0 ? 1 : 0;
+        hits += out_hit[b];
+    }
+    if (out_batch) {
+        out_batch[0] = hits;
+        out_batch[1] = hits == B ? 1 : 0;
+    }
+    return 0;
 }
 
 // Theorem 12 fan-out: F_k = F0 a^{k/(1+r)} for k < K, F_K = F0 a^{K/(1+r)} (1-a)^{-1/(1+r)},

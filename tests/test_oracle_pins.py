@@ -593,3 +593,180 @@ def test_backup_plan_switch():
     assert sw == 0 and use.tolist() == [0] * 6
     use, sw = oracle.backup_plan(6, np.ones(6, np.uint8), all_hit=1, b_star=1)   # every request hit
     assert sw == 0 and use.tolist() == [0] * 6
+
+
+# ------------------------------------------------------------------------------------------
+# Mirror-SD signposts: top-kappa of the early-exit distribution with log-probabilities
+# ------------------------------------------------------------------------------------------
+def _bf16(x):
+    x = np.asarray(x, np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_signposts_brute_force_and_log_softmax():
+    rng = np.random.default_rng(41)
+    for trial in range(60):
+        V = int(rng.integers(1, 40))
+        B = 3
+        z = np.round(rng.normal(0, 2, (B, V)) * 2) / 2          # many ties
+        z[rng.random((B, V)) < 0.1] = -np.inf
+        z[rng.random((B, V)) < 0.1] = -0.0
+        z[:, 0] = np.where(np.isinf(z[:, 0]), 1.0, z[:, 0])       # at least one finite logit
+        z = z.astype(np.float32)
+        kappa = int(rng.integers(1, V + 3))
+        for dtype, arr in ((oracle.FP32, z), (oracle.BF16, _bf16(z))):
+            ids, lp, st = oracle.signposts(arr, dtype, kappa)
+            zz = z if dtype == oracle.FP32 else (arr.astype(np.uint32) << 16).view(np.float32)
+            assert (st == 0).all()
+            for b in range(B):
+                want = sorted(range(V), key=lambda i: (-float(zz[b, i]), i))[:kappa]
+                assert ids[b, :len(want)].tolist() == want
+                assert (ids[b, len(want):] == -1).all() and np.isneginf(lp[b, len(want):]).all()
+                ref = scipy.special.log_softmax(zz[b].astype(np.float64))
+                np.testing.assert_allclose(lp[b, :len(want)], ref[want], rtol=1e-12, atol=1e-12)
+
+
+def test_signposts_special_rows():
+    V = 1000
+    ids, lp, st = oracle.signposts(np.full((1, V), 3.25, np.float32), oracle.FP32, 8)
+    assert ids[0].tolist() == list(range(8))                   # a flat row: ties to the lower id
+    np.testing.assert_allclose(lp[0], -np.log(V), rtol=1e-14)
+    one = np.full((1, V), -np.inf, np.float32)
+    one[0, 417] = -7.0
+    ids, lp, st = oracle.signposts(one, oracle.FP32, 3)
+    assert ids[0, 0] == 417 and lp[0, 0] == 0.0 and np.isneginf(lp[0, 1:]).all()
+    full = np.random.default_rng(3).normal(0, 3, (2, 50)).astype(np.float32)
+    ids, lp, st = oracle.signposts(full, oracle.FP32, 50)      # kappa = V: a distribution
+    np.testing.assert_allclose(np.exp(lp).sum(axis=1), 1.0, rtol=1e-13)
+    assert (np.diff(lp, axis=1) <= 0).all()
+    shifted = (full + np.float32(16.0)).astype(np.float32)
+    ids2, lp2, _ = oracle.signposts(shifted, oracle.FP32, 50)
+    assert (ids2 == ids).all()
+    np.testing.assert_allclose(lp2, lp, atol=1e-5)            # the shift rounds in fp32
+    bad = np.zeros((3, 20), np.float32)
+    bad[0, 5] = np.nan
+    bad[1, 7] = np.inf
+    bad[2, :] = -np.inf
+    ids, lp, st = oracle.signposts(bad, oracle.FP32, 4)
+    assert (st == oracle.ST_BAD_LOGIT).all() and (ids == -1).all() and np.isnan(lp).all()
+
+
+# ------------------------------------------------------------------------------------------
+# Mirror-SD reuse against a draft tree with internal branching
+# ------------------------------------------------------------------------------------------
+def _mirror_example_tree(ex, case, names):
+    """Roots first, the verified branch under root 0, filler branches under the others, then
+    the fork's extra children; returns (tokens, parents)."""
+    gamma = len(ex["verified_path"])
+    tok, par = [], []
+    for r in ex["roots"]:
+        tok.append(names[r]); par.append(-1)
+    depth_node = {1: 0}
+    prev = 0
+    for d, name in enumerate(ex["verified_path"][1:], start=2):
+        tok.append(names[name]); par.append(prev)
+        prev = len(tok) - 1
+        depth_node[d] = prev
+    for r in range(1, len(ex["roots"])):
+        prev = r
+        for d in range(2, gamma + 1):
+            tok.append(names[f"filler{r}_{d}"]); par.append(prev)
+            prev = len(tok) - 1
+    fork = depth_node[ex["fork_parent_depth"]]
+    for name in case["fork_children"]:
+        tok.append(names[name]); par.append(fork)
+    return np.array(tok, np.int32), np.array(par, np.int32)
+
+
+def test_tree_reuse_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "mirror_reuse_example.json")))
+    labels = list(ex["roots"]) + list(ex["verified_path"]) + ["zhong1", "shang4"]
+    labels += [f"filler{r}_{d}" for r in range(8) for d in range(2, 9)]
+    names = {}
+    for lab in labels:
+        names.setdefault(lab, len(names))
+    path = np.array([[names[x] for x in ex["verified_path"]]], np.int32)
+    for case in ex["cases"]:
+        tok, par = _mirror_example_tree(ex, case, names)
+        node, hit, batch = oracle.tree_lookup(tok[None], par[None], path, [case["k"]], [names[case["t"]]])
+        n = int(node[0])
+        if case["expect"] == "full":
+            assert n == -2 and hit[0] == 0, case["name"]
+        elif case["expect"] == "miss":
+            assert n == -1 and hit[0] == 0 and batch.tolist() == [0, 0], case["name"]
+        else:
+            assert n >= 0 and hit[0] == 1 and batch.tolist() == [1, 1], case["name"]
+            assert tok[n] == names[case["t"]]
+            d, cur = 0, n
+            while cur != -1:
+                d, cur = d + 1, par[cur]
+            assert d == case["depth"], case["name"]
+
+
+def _paths_top_down(tok, par):
+    """Brute force: every root-to-node path, walking down from the roots over child lists."""
+    N = len(tok)
+    valid = [tok[n] >= 0 and -1 <= par[n] < n for n in range(N)]
+    kids = {n: [] for n in range(-1, N)}
+    for n in range(N):
+        if valid[n]:
+            kids[int(par[n])].append(n)
+    best = {}
+    stack = [(c, (int(tok[c]),)) for c in kids[-1]]
+    while stack:
+        n, p = stack.pop()
+        best[p] = min(best.get(p, N), n)
+        stack.extend((c, p + (int(tok[c]),)) for c in kids[n])
+    return best
+
+
+def test_tree_reuse_brute_force():
+    rng = np.random.default_rng(17)
+    gamma = 5
+    for trial in range(200):
+        N = int(rng.integers(1, 60))
+        tok = rng.integers(0, 4, N).astype(np.int32)             # small alphabet: many equal paths
+        par = np.array([int(rng.integers(-1, n)) if n else -1 for n in range(N)], np.int32)
+        if trial % 3 == 0:                                       # padding and broken parents
+            tok[rng.random(N) < 0.1] = -1
+            par[rng.random(N) < 0.05] = N + 3
+        best = _paths_top_down(tok, par)
+        B = 8
+        path = rng.integers(0, 4, (B, gamma)).astype(np.int32)
+        k = rng.integers(0, gamma + 1, B).astype(np.int32)
+        t = rng.integers(0, 4, B).astype(np.int32)
+        if best:                                                 # steer some requests onto tree paths
+            keys = list(best)
+            for b in range(0, B, 2):
+                p = keys[int(rng.integers(len(keys)))]
+                if len(p) - 1 < gamma:
+                    k[b] = len(p) - 1
+                    path[b, :k[b]] = p[:-1]
+                    t[b] = p[-1]
+        node, hit, batch = oracle.tree_lookup(np.tile(tok, (B, 1)), np.tile(par, (B, 1)), path, k, t)
+        for b in range(B):
+            if k[b] == gamma:
+                want = -2
+            else:
+                want = best.get(tuple(int(x) for x in path[b, :k[b]]) + (int(t[b]),), -1)
+            assert node[b] == want, (trial, b)
+        assert batch[0] == hit.sum() and batch[1] == int(hit.all())
+
+
+def test_tree_reuse_on_a_comb_is_branch_reuse():
+    # a tree without internal branching is the branch-complete comb: node // gamma is the branch
+    rng = np.random.default_rng(23)
+    B, kappa, gamma = 30, 8, 7
+    br = rng.integers(0, 3, (B, kappa, gamma)).astype(np.int32)
+    k = np.zeros((B, kappa), np.int32)
+    t = np.zeros((B, kappa), np.int32)
+    k[:, 0] = rng.integers(0, gamma + 1, B)
+    t[:, 0] = rng.integers(0, 3, B)
+    slot, hit, batch = oracle.cache_lookup(1, br, [kappa, gamma], 0, B, k, t)
+    tok = br.reshape(B, kappa * gamma)
+    par = np.tile(np.array([-1 if d == 0 else j * gamma + d - 1 for j in range(kappa) for d in range(gamma)],
+                           np.int32), (B, 1))
+    node, hit2, batch2 = oracle.tree_lookup(tok, par, br[:, 0], k[:, 0], t[:, 0])
+    assert (np.where(node >= 0, node // gamma, node) == slot).all()
+    assert (hit2 == hit).all() and (batch2 == batch).all()
