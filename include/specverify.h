@@ -21,13 +21,18 @@
  *   saguaro_backup_plan  - the batch-aware fallback on a cache miss: which requests take the
  *                          random-token backup speculator this round (verified by spec_verify
  *                          with SPEC_UNIFORM_DRAFT).
+ *   mirror_signposts     - Mirror-SD early-exit signposts: the kappa most likely tokens of a
+ *                          logit row with their log-probabilities (the draft's token-channel
+ *                          message).
+ *   mirror_tree_lookup   - reuse of the committed prefix against a draft tree that may branch
+ *                          below its roots.
  *
  * Sources (notation p = draft, q = target, as on the DeepMind page):
  *   [SpS]   "Accelerating LLM Decoding with Speculative Sampling" (DeepMind, arXiv 2302.01318),
  *           knowledge-base reading, sections 1, 3 and 6.
  *   [SSD]   "Speculative Speculative Decoding" reading notes, sections 1.3, 2.2, 4.3, 4.4, 5.1, 7.1.
  *   [SSD-H] hyper.ai summary of arXiv 2603.03251, "Method" (fan-out closed form, sigma_{F,C}).
- *   [MSD]   "Mirror Speculative Decoding" reading notes, sections 2, 3.2 and 3.3.
+ *   [MSD]   "Mirror Speculative Decoding" reading notes, sections 2, 3.1, 3.2 and 3.3.
  *
  * Conventions for every entry point:
  *   - Array pointers are HIP device memory owned by the caller (unless marked "host"); the
@@ -68,6 +73,7 @@ enum { SPEC_FP32 = 0, SPEC_BF16 = 1 };
 
 #define SPEC_MAX_F 64          /* largest downweighted set */
 #define SPEC_MAX_FANOUT 1024   /* largest cache width for one depth */
+#define SPEC_MAX_KAPPA 32      /* most signposts per request */
 
 /* Per-request processing, applied to the draft AND the target rows of that request ([SpS]
  * section 6: temperature, top-k and nucleus act on both distributions before the correction).
@@ -221,6 +227,48 @@ int saguaro_backup_plan(int B, const uint8_t* hit, const int32_t* batch, int b_s
 int saguaro_cache_lookup(int mode, const int32_t* cache, const int32_t* fanout_or_shape, int K, int B,
                          const int32_t* k, const int32_t* tstar, int32_t* out_slot, uint8_t* out_hit,
                          int32_t* out_batch, hipStream_t stream);
+
+/* mirror_signpost_workspace_bytes - device workspace mirror_signposts needs for (B, V, kappa);
+ * 0 for sizes it rejects.  Same contract as the verification workspace: zero-filled before its
+ * first use (hipMemset), left zero-filled by every completed call, one call at a time. */
+size_t mirror_signpost_workspace_bytes(int B, int V, int kappa);
+
+/* mirror_signposts - early-exit signposts ([MSD] sections 3.1 and 3.3: the LM head at the
+ * early-exit layer gives a distribution p~; its top kappa tokens with log p~ form the message to
+ * the draft).  p~ is read as the softmax of the given logits at temperature 1; tokens are
+ * ranked by logit descending, ties to the lower id (-0 ties +0), and
+ * log p~(v) = z_v - m - log sum_i exp(z_i - m), m the row maximum.
+ *   logits         [B][V] device, dtype SPEC_FP32 or SPEC_BF16 (V <= 2^21)
+ *   kappa          1..SPEC_MAX_KAPPA signposts per request
+ *   out_ids        [B][kappa] int32, rank order; -1 past the vocabulary
+ *   out_logp       [B][kappa] float32 log p~ (-inf past the vocabulary or for a -inf logit)
+ *   out_logp_bf16  [B][kappa] bf16 bits, round-to-nearest-even of out_logp (nullable): the
+ *                  message's compact form
+ *   out_status     [B] (nullable): SPEC_ST_BAD_LOGIT for a row with a NaN or +inf logit or no
+ *                  finite one (its ids are -1 and its log-probabilities NaN), else 0
+ *   workspace      mirror_signpost_workspace_bytes(B, V, kappa) bytes
+ * Return codes: SPEC_EINVAL (null pointer, sizes out of range), SPEC_EDTYPE, SPEC_EWORKSPACE,
+ * SPEC_EHIP. */
+int mirror_signposts(const void* logits, int dtype, int B, int V, int kappa, int32_t* out_ids, float* out_logp,
+                     uint16_t* out_logp_bf16, uint32_t* out_status, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* mirror_tree_lookup - reuse against a draft tree ([MSD] sections 3.2-3.3: the committed
+ * prefix, accepted tokens then the correction, is reused when it is one of the paths the draft
+ * precomputed; the worked example forks below a root).  Per request the tree is N nodes listed
+ * parents first: tree_tokens[b][n] and tree_parents[b][n] (-1 for a root, i.e. a signpost the
+ * draft expanded).  A node with a negative token or a parent outside [-1, n) is not part of the
+ * tree, nor is anything below it.
+ *   path_tokens  [B][gamma] the verified chain's draft tokens (gamma <= 1024)
+ *   k, tstar     [B] accepted count and correction token (spec_verify's outputs for the chain)
+ *   out_node     [B] the lowest node whose root path equals (path[0..k-1], t*), so at depth
+ *                k + 1; -1 when there is none (or k, t* out of range), -2 when k == gamma
+ *   out_hit      [B] uint8 (out_node >= 0)
+ *   out_batch    [2] int32 {hits, 1 if every request hit} (nullable)
+ * Returns SPEC_EINVAL for a null pointer or sizes out of range. */
+int mirror_tree_lookup(const int32_t* tree_tokens, const int32_t* tree_parents, int B, int N, int gamma,
+                       const int32_t* path_tokens, const int32_t* k, const int32_t* tstar, int32_t* out_node,
+                       uint8_t* out_hit, int32_t* out_batch, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ SPEC_FP32, SPEC_BF16 = 0, 1
 SPEC_SAMPLE_DRAFT = 1
 SPEC_UNIFORM_DRAFT = 2
 SPEC_MAX_F = 64
+SPEC_MAX_KAPPA = 32
 ST_EMPTY_RESIDUAL = 8
 ST_OUTSIDE_DRAFT_SUPPORT = 16
 ST_BAD_LOGIT = 32
@@ -29,7 +30,8 @@ ST_DEGENERATE_DOWNWEIGHT = 128
 ST_BAD_PARAM = 256
 
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
-           "saguaro_cache_lookup", "saguaro_verify_cache", "saguaro_backup_plan")
+           "saguaro_cache_lookup", "saguaro_verify_cache", "saguaro_backup_plan", "mirror_signpost_workspace_bytes",
+           "mirror_signposts", "mirror_tree_lookup")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -59,6 +61,10 @@ class Lib:
         L.saguaro_cache_build.argtypes = [_P, _I, _I, _I, _I, _P, _I, _D, _D, _P, _P, _P]
         L.saguaro_cache_lookup.argtypes = [_I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P]
         L.saguaro_backup_plan.argtypes = [_I, _P, _P, _I, _P, _P, _P]
+        L.mirror_signpost_workspace_bytes.argtypes = [_I, _I, _I]
+        L.mirror_signpost_workspace_bytes.restype = ctypes.c_size_t
+        L.mirror_signposts.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.mirror_tree_lookup.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
         L.saguaro_verify_cache.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
                                            ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                            _P]
@@ -239,3 +245,50 @@ def saguaro_backup_plan(hit: torch.Tensor, batch: torch.Tensor, b_star: int, str
     rc = load().cdll.saguaro_backup_plan(B, _ptr(hit), _ptr(batch), b_star, _ptr(use), _ptr(sw), _stream(stream))
     _check("saguaro_backup_plan", rc)
     return use, sw
+
+
+
+def mirror_signpost_workspace_bytes(B: int, V: int, kappa: int) -> int:
+    return int(load().cdll.mirror_signpost_workspace_bytes(B, V, kappa))
+
+
+def new_signpost_workspace(B: int, V: int, kappa: int, device="cuda") -> torch.Tensor:
+    n = mirror_signpost_workspace_bytes(B, V, kappa)
+    if n == 0:
+        raise SpecError("mirror_signpost_workspace_bytes", SPEC_EINVAL)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def mirror_signposts(logits: torch.Tensor, kappa: int, want_bf16: bool = False,
+                     workspace: Optional[torch.Tensor] = None, out=None, stream=None):
+    """Early-exit signposts of logits [B][V]: (ids [B][kappa] int32, log p~ [B][kappa] float32,
+    log p~ as bf16 bits [B][kappa] int16 or None, status [B] int32)."""
+    B, V = logits.shape
+    dev = logits.device
+    if workspace is None:
+        workspace = new_signpost_workspace(B, V, kappa, dev)
+    if out is None:
+        out = (torch.empty((B, kappa), dtype=torch.int32, device=dev),
+               torch.empty((B, kappa), dtype=torch.float32, device=dev),
+               torch.empty((B, kappa), dtype=torch.int16, device=dev) if want_bf16 else None,
+               torch.empty(B, dtype=torch.int32, device=dev))
+    ids, lp, lp16, st = out
+    rc = load().cdll.mirror_signposts(_ptr(logits), dtype_code(logits), B, V, kappa, _ptr(ids), _ptr(lp), _ptr(lp16),
+                                      _ptr(st), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("mirror_signposts", rc)
+    return out
+
+
+def mirror_tree_lookup(tokens: torch.Tensor, parents: torch.Tensor, path: torch.Tensor, k: torch.Tensor,
+                       tstar: torch.Tensor, stream=None):
+    """Reuse node of the committed prefix in each request's draft tree [B][N]: (node [B], hit [B], batch [2])."""
+    B, N = tokens.shape
+    gamma = path.shape[1]
+    dev = tokens.device
+    node = torch.empty(B, dtype=torch.int32, device=dev)
+    hit = torch.empty(B, dtype=torch.uint8, device=dev)
+    batch = torch.empty(2, dtype=torch.int32, device=dev)
+    rc = load().cdll.mirror_tree_lookup(_ptr(tokens), _ptr(parents), B, N, gamma, _ptr(path), _ptr(k), _ptr(tstar),
+                                        _ptr(node), _ptr(hit), _ptr(batch), _stream(stream))
+    _check("mirror_tree_lookup", rc)
+    return node, hit, batch

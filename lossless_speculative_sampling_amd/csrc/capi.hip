@@ -4,6 +4,7 @@
 
 #include "fastpath.h"
 #include "generic.h"
+#include "mirror.h"
 
 using namespace sv;
 
@@ -217,6 +218,37 @@ int saguaro_cache_lookup(int mode, const int32_t* cache, const int32_t* fanout_o
         return SPEC_EINVAL;
     }
     hipLaunchKernelGGL(cache_lookup_kernel, dim3(1), dim3(1024), 0, stream, l);
+    return launch_status();
+}
+
+size_t mirror_signpost_workspace_bytes(int B, int V, int kappa) {
+    if (B < 1 || V < 1 || V > mirror::kMaxV || kappa < 1 || kappa > SPEC_MAX_KAPPA) return 0;
+    return mirror::signpost_plan(B, V, kappa).ws_bytes;
+}
+
+int mirror_signposts(const void* logits, int dtype, int B, int V, int kappa, int32_t* out_ids, float* out_logp,
+                     uint16_t* out_logp_bf16, uint32_t* out_status, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    if (!logits || !out_ids || !out_logp) return SPEC_EINVAL;
+    if (B < 1 || V < 1 || V > mirror::kMaxV || kappa < 1 || kappa > SPEC_MAX_KAPPA) return SPEC_EINVAL;
+    if (!valid_dtype(dtype)) return SPEC_EDTYPE;
+    const mirror::SpPlan plan = mirror::signpost_plan(B, V, kappa);
+    if (!workspace || workspace_bytes < plan.ws_bytes) return SPEC_EWORKSPACE;
+    const size_t esz = dtype == SPEC_BF16 ? 2 : 4;
+    const int vec = ((reinterpret_cast<uintptr_t>(logits) & 15) == 0 && ((size_t)V * esz) % 16 == 0) ? 1 : 0;
+    mirror::SignpostArgs a{logits, dtype, B, V, kappa, plan, out_ids, out_logp, out_logp_bf16, out_status,
+                           static_cast<char*>(workspace)};
+    mirror::launch_signposts(a, vec, stream);
+    return launch_status();
+}
+
+int mirror_tree_lookup(const int32_t* tree_tokens, const int32_t* tree_parents, int B, int N, int gamma,
+                       const int32_t* path_tokens, const int32_t* k, const int32_t* tstar, int32_t* out_node,
+                       uint8_t* out_hit, int32_t* out_batch, hipStream_t stream) {
+    if (!tree_tokens || !tree_parents || !path_tokens || !k || !tstar || !out_node || !out_hit) return SPEC_EINVAL;
+    if (B < 1 || N < 1 || gamma < 1 || gamma > mirror::kMaxGamma) return SPEC_EINVAL;
+    mirror::TreeArgs a{tree_tokens, tree_parents, B, N, gamma, path_tokens, k, tstar, out_node, out_hit, out_batch};
+    mirror::launch_tree_lookup(a, stream);
     return launch_status();
 }
 

@@ -186,39 +186,6 @@ struct FastArgs {
     Fanout fan;
 };
 
-// ------------------------------------------------------------------------------------------
-// Request arrival counter in the XCD's L2 (every workgroup of a request runs on one XCD)
-// ------------------------------------------------------------------------------------------
-__device__ __forceinline__ unsigned l2_fetch_add(unsigned* p, unsigned v) {
-    unsigned old;
-    asm volatile("s_waitcnt vmcnt(0)\n\tglobal_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
-                 : "=v"(old) : "v"(p), "v"(v) : "memory");
-    return old;
-}
-
-__device__ __forceinline__ uint64_t l2_fetch_add64(uint64_t* p, uint64_t v) {
-    uint64_t old;
-    asm volatile("s_waitcnt vmcnt(0)\n\tglobal_atomic_add_x2 %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
-                 : "=v"(old) : "v"(p), "v"(v) : "memory");
-    return old;
-}
-
-// Every wave waits until its own global stores have reached L2; __syncthreads() alone orders
-// only LDS traffic, so this must precede the workgroup barrier in front of an arrival.
-__device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// ------------------------------------------------------------------------------------------
-// Loads of data published by other workgroups (non-temporal: bypass L1, served by L2)
-// ------------------------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ T ldnt(const T* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ uint32_t ldnt_u16(const uint16_t* p) {
-    // u16 via the enclosing aligned dword
-    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3));
-    return (a & 2) ? (w >> 16) : (w & 0xFFFFu);
-}
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Columns of a slice are held as: load q, thread t, element e  ->  c0 + q*kThreads*8 + t*8 + e,

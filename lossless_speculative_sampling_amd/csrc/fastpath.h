@@ -20,7 +20,6 @@ constexpr int kLoads = kColsPerThread / 8;     // 16-byte loads per row per thre
 constexpr int kSliceCols = kThreads * kColsPerThread;  // 16384
 constexpr int kChunkCols = 512;                // one wave x one 16-byte load per lane
 constexpr int kChunks = kSliceCols / kChunkCols;       // 32 per slice
-constexpr int kXcd = 8;                        // XCDs on MI355X
 
 // Exact bins: one per bf16 value with |z| in [2^-6, 2^5), plus zero.  Negative values occupy
 // bins [0, kNegBins) in ascending value order, zero bin kZeroBin, positive values

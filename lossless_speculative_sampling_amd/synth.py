@@ -21,6 +21,12 @@ Workloads (the logit recipes are stand-ins for real model logits, which are not 
   depth j-2, takes at depth j-1 the highest-logit draft token other than branch 0's, and
   continues with rows and tokens of its own.  Draft tokens are proposals of a stand-in
   drafter: a Gumbel-max draw over the 50 largest raw draft logits scaled by 1/T.
+* ``mirror``   - bf16 early-exit rows (B = 64, V = 151936, Zipf-shaped) for the signposts, and
+  per request a draft tree in parent-first order: kappa = 8 root tokens, each expanded to a
+  chain of depth gamma = 7, with extra siblings forking off internal nodes (each fork
+  continues to depth gamma), padded to N nodes with token -1.  The verified path is root 0's
+  chain; k is a truncated geometric draw (per-token acceptance 0.7) and t* is, with
+  probability 1/2, the token of a fork off the accepted prefix, else a random token.
 """
 from __future__ import annotations
 
@@ -219,3 +225,67 @@ def random_rows(rng: np.random.Generator, B: int, K: int, V: int, dtype: int, dr
     if dtype == BF16:
         return f32_to_bf16_bits(draft), f32_to_bf16_bits(target)
     return draft, target
+
+
+@dataclass
+class MirrorWorkload:
+    """Early-exit rows [B][V] (bf16 bits) and per-request draft trees [B][N] (parent-first)."""
+    B: int
+    V: int
+    kappa: int
+    gamma: int
+    logits: np.ndarray
+    tokens: np.ndarray
+    parents: np.ndarray
+    path: np.ndarray
+    k: np.ndarray
+    tstar: np.ndarray
+
+
+def mirror(B: int = 64, V: int = 151936, kappa: int = 8, gamma: int = 7, N: int = 128, p_fork: float = 0.25,
+           cfg: int = 6) -> MirrorWorkload:
+    rng = np.random.default_rng(DATA_SEED_BASE + cfg)
+    logits = f32_to_bf16_bits(zipf_rows(rng, B, V))
+    tok = np.full((B, N), -1, np.int32)
+    par = np.full((B, N), -1, np.int32)
+    path = np.zeros((B, gamma), np.int32)
+    kk = np.zeros(B, np.int32)
+    tt = np.zeros(B, np.int32)
+    for b in range(B):
+        nodes = []                                   # (token, parent)
+
+        def chain(parent, depth):                    # nodes from `depth` (1-based) to gamma
+            ids = []
+            for _ in range(depth, gamma + 1):
+                nodes.append((int(rng.integers(0, V)), parent))
+                parent = len(nodes) - 1
+                ids.append(parent)
+            return ids
+
+        roots = rng.choice(V, kappa, replace=False)
+        main = []
+        for j in range(kappa):
+            nodes.append((int(roots[j]), -1))
+        for j in range(kappa):
+            ids = [j] + chain(j, 2)
+            if j == 0:
+                main = ids
+            for d in range(1, gamma):                # forks below internal nodes
+                if rng.random() < p_fork and len(nodes) + gamma - d <= N:
+                    chain(ids[d - 1], d + 1)
+        nodes = nodes[:N]
+        for n, (t_, p_) in enumerate(nodes):
+            tok[b, n], par[b, n] = t_, p_
+        path[b] = [nodes[i][0] for i in main]
+        k = 0
+        while k < gamma and rng.random() < 0.7:
+            k += 1
+        kk[b] = k
+        if k < gamma:
+            parent = main[k - 1] if k > 0 else -1
+            # a rejected draft token is never the correction: forks of the prefix only
+            kids = [n for n, (_, p_) in enumerate(nodes) if p_ == parent and n != main[k]]
+            tt[b] = nodes[int(rng.choice(kids))][0] if kids and rng.random() < 0.5 else int(rng.integers(0, V))
+        else:
+            tt[b] = int(rng.integers(0, V))
+    return MirrorWorkload(B, V, kappa, gamma, logits, tok, par, path, kk, tt)

@@ -118,3 +118,35 @@ def test_generator_shapes_and_determinism():
     assert t.tokens[2, 0] == t.tokens[0, 0] and t.tokens[2, 1] != t.tokens[0, 1]
     x = np.array([1.0, -2.5, 3.14159, 1e-30, -0.0], np.float32)
     assert np.allclose(synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x)), x, rtol=1 / 128)
+
+
+def test_mirror_entry_points_argument_errors():
+    L = capi.load().cdll
+    fake = ctypes.c_void_p(0x1000)
+    assert capi.mirror_signpost_workspace_bytes(64, 151936, 8) > 0
+    assert capi.mirror_signpost_workspace_bytes(64, 151936, capi.SPEC_MAX_KAPPA + 1) == 0
+    assert capi.mirror_signpost_workspace_bytes(0, 100, 8) == 0
+    assert capi.mirror_signpost_workspace_bytes(1, (1 << 21) + 1, 8) == 0
+    ws = capi.mirror_signpost_workspace_bytes(4, 1000, 8)
+
+    def sp(**kw):
+        a = dict(logits=fake, dtype=1, B=4, V=1000, kappa=8, ids=fake, lp=fake, lp16=None, st=None, ws=fake,
+                 ws_bytes=ws)
+        a.update(kw)
+        return L.mirror_signposts(a["logits"], a["dtype"], a["B"], a["V"], a["kappa"], a["ids"], a["lp"], a["lp16"],
+                                  a["st"], a["ws"], a["ws_bytes"], None)
+    assert sp(logits=None) == capi.SPEC_EINVAL
+    assert sp(ids=None) == capi.SPEC_EINVAL
+    assert sp(lp=None) == capi.SPEC_EINVAL
+    assert sp(kappa=0) == capi.SPEC_EINVAL
+    assert sp(kappa=capi.SPEC_MAX_KAPPA + 1) == capi.SPEC_EINVAL
+    assert sp(V=0) == capi.SPEC_EINVAL
+    assert sp(B=0) == capi.SPEC_EINVAL
+    assert sp(dtype=5) == capi.SPEC_EDTYPE
+    assert sp(ws=None) == capi.SPEC_EWORKSPACE
+    assert sp(ws_bytes=ws - 1) == capi.SPEC_EWORKSPACE
+    assert L.mirror_tree_lookup(None, fake, 4, 10, 7, fake, fake, fake, fake, fake, None, None) == capi.SPEC_EINVAL
+    assert L.mirror_tree_lookup(fake, fake, 4, 10, 7, fake, fake, fake, None, fake, None, None) == capi.SPEC_EINVAL
+    assert L.mirror_tree_lookup(fake, fake, 0, 10, 7, fake, fake, fake, fake, fake, None, None) == capi.SPEC_EINVAL
+    assert L.mirror_tree_lookup(fake, fake, 4, 0, 7, fake, fake, fake, fake, fake, None, None) == capi.SPEC_EINVAL
+    assert L.mirror_tree_lookup(fake, fake, 4, 10, 1025, fake, fake, fake, fake, fake, None, None) == capi.SPEC_EINVAL
