@@ -73,7 +73,7 @@ enum { SPEC_FP32 = 0, SPEC_BF16 = 1 };
 
 #define SPEC_MAX_F 64          /* largest downweighted set */
 #define SPEC_MAX_FANOUT 1024   /* largest cache width for one depth */
-#define SPEC_MAX_KAPPA 32      /* most signposts per request */
+#define SPEC_MAX_KAPPA 16      /* most signposts per request */
 
 /* Per-request processing, applied to the draft AND the target rows of that request ([SpS]
  * section 6: temperature, top-k and nucleus act on both distributions before the correction).
@@ -238,7 +238,7 @@ size_t mirror_signpost_workspace_bytes(int B, int V, int kappa);
  * the draft).  p~ is read as the softmax of the given logits at temperature 1; tokens are
  * ranked by logit descending, ties to the lower id (-0 ties +0), and
  * log p~(v) = z_v - m - log sum_i exp(z_i - m), m the row maximum.
- *   logits         [B][V] device, dtype SPEC_FP32 or SPEC_BF16 (V <= 2^21)
+ *   logits         [B][V] device, dtype SPEC_FP32 or SPEC_BF16 (V <= 2^19)
  *   kappa          1..SPEC_MAX_KAPPA signposts per request
  *   out_ids        [B][kappa] int32, rank order; -1 past the vocabulary
  *   out_logp       [B][kappa] float32 log p~ (-inf past the vocabulary or for a -inf logit)

@@ -21,7 +21,7 @@ SPEC_FP32, SPEC_BF16 = 0, 1
 SPEC_SAMPLE_DRAFT = 1
 SPEC_UNIFORM_DRAFT = 2
 SPEC_MAX_F = 64
-SPEC_MAX_KAPPA = 32
+SPEC_MAX_KAPPA = 16
 ST_EMPTY_RESIDUAL = 8
 ST_OUTSIDE_DRAFT_SUPPORT = 16
 ST_BAD_LOGIT = 32

@@ -233,6 +233,7 @@ int mirror_signposts(const void* logits, int dtype, int B, int V, int kappa, int
     if (B < 1 || V < 1 || V > mirror::kMaxV || kappa < 1 || kappa > SPEC_MAX_KAPPA) return SPEC_EINVAL;
     if (!valid_dtype(dtype)) return SPEC_EDTYPE;
     const mirror::SpPlan plan = mirror::signpost_plan(B, V, kappa);
+    if (plan.lds_bytes > 64 * 1024) return SPEC_EINVAL;  // (not reached within the size limits)
     if (!workspace || workspace_bytes < plan.ws_bytes) return SPEC_EWORKSPACE;
     const size_t esz = dtype == SPEC_BF16 ? 2 : 4;
     const int vec = ((reinterpret_cast<uintptr_t>(logits) & 15) == 0 && ((size_t)V * esz) % 16 == 0) ? 1 : 0;

@@ -20,8 +20,7 @@ constexpr int kPer = 32;                        // contiguous columns per lane
 constexpr int kWaveSpan = kWave * kPer;         // 2048 columns per wave
 constexpr int kSliceSpan = kWaves * kWaveSpan;  // 8192 columns per workgroup
 constexpr int kMaxKappa = SPEC_MAX_KAPPA;
-constexpr int kMaxV = 1 << 21;                  // up to 1024 lists per row
-constexpr size_t kLdsCap = 64 * 1024;           // dynamic LDS of one signpost workgroup
+constexpr int kMaxV = 1 << 19;                  // up to 256 lists per row (the merge holds them in LDS)
 constexpr int kTreeThreads = 256;
 constexpr int kTreeLdsNodes = 4096;             // trees up to this size are walked in LDS
 constexpr int kMaxGamma = 1024;
@@ -38,12 +37,24 @@ struct SpPlan {
     size_t rec_stride;      // bytes per list record
     size_t ctr_bytes, ws_bytes;
     size_t wave_lds;        // per-wave LDS of the list phase
-    size_t merge_arrays;    // per-row arrays of the merge (counts, maxima, sums, cursors, result)
-    int merge_in_lds;       // the merge stages every list entry in LDS
-    size_t lds_bytes;
+    size_t lds_bytes;       // dynamic LDS of a workgroup (list phase, then the merge)
 };
 
 __host__ __device__ inline size_t align_to(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// LDS of one wave's list phase: up to 2 kappa staged lanes (32 floats each) and their lane
+// ids, then the elements above the threshold (at most 32 (kappa - 1)) and the first kappa ties.
+__host__ __device__ inline size_t wave_stage_bytes(int kappa) {
+    return align_to((size_t)2 * kappa * kPer * 4 + (size_t)2 * kappa * 4, 8);
+}
+__host__ __device__ inline size_t wave_lds_bytes(int kappa) {
+    return wave_stage_bytes(kappa) + (size_t)kPer * kappa * 8 + (size_t)kappa * 8;
+}
+// LDS of the merge: maxima, counts, top-head lists, sums, kappa^2 candidates, heads, entries.
+__host__ __device__ inline size_t merge_lds_bytes(int L, int kappa) {
+    return align_to((size_t)L * 8 + (size_t)kappa * 4, 8) + (size_t)L * 8 + (size_t)kappa * kappa * 8 +
+           (size_t)L * 8 + (size_t)L * kappa * 8;
+}
 
 __host__ __device__ inline SpPlan signpost_plan(int B, int V, int kappa) {
     SpPlan p;
@@ -52,13 +63,9 @@ __host__ __device__ inline SpPlan signpost_plan(int B, int V, int kappa) {
     p.rec_stride = sizeof(ListHead) + (size_t)kappa * sizeof(uint64_t);
     p.ctr_bytes = align_to((size_t)B * 128, 256);
     p.ws_bytes = p.ctr_bytes + align_to((size_t)B * p.L * p.rec_stride, 256);
-    // staged candidate lanes (kappa x 32 floats), their lane ids, the wave's candidate list
-    p.wave_lds = align_to((size_t)kappa * kPer * 4 + (size_t)kappa * 4, 8) + (size_t)kappa * kPer * 8;
-    p.merge_arrays = (size_t)p.L * (4 + 4 + 8 + 4) + (size_t)kappa * 8;
-    const size_t staged = align_to(p.merge_arrays, 8) + (size_t)p.L * kappa * 8;
+    p.wave_lds = wave_lds_bytes(kappa);
     const size_t lists = kWaves * p.wave_lds;
-    p.merge_in_lds = staged <= kLdsCap ? 1 : 0;
-    const size_t merge = p.merge_in_lds ? staged : p.merge_arrays;
+    const size_t merge = merge_lds_bytes(p.L, kappa);
     p.lds_bytes = lists > merge ? lists : merge;
     return p;
 }

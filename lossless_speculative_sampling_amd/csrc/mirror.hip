@@ -99,6 +99,43 @@ __device__ __forceinline__ void load_lane(const void* row, int c0, int nvalid, f
     }
 }
 
+// exp(x - y) for x <= y in fp32 (the factors that move a sum of exponentials from one maximum
+// to a larger one; relative error ~1e-7).
+__device__ __forceinline__ float exp_diff(float x, float y) {
+    return __builtin_amdgcn_exp2f((x - y) * 1.4426950408889634f);
+}
+
+// LDS of the merge: per list its maximum, count, sum and entries; the top-head lists; the
+// candidate slots.
+struct MergeView {
+    float* m;
+    int* cnt;
+    int* top;
+    double* S;
+    uint64_t* cand;
+    uint64_t* heads;
+    uint64_t* ent;
+};
+__device__ __forceinline__ MergeView merge_view(char* lds, int L, int kappa) {
+    MergeView v;
+    v.m = reinterpret_cast<float*>(lds);
+    v.cnt = reinterpret_cast<int*>(v.m + L);
+    v.top = v.cnt + L;
+    v.S = reinterpret_cast<double*>(lds + align_to((size_t)L * 8 + (size_t)kappa * 4, 8));
+    v.cand = reinterpret_cast<uint64_t*>(v.S + L);
+    v.heads = v.cand + (size_t)kappa * kappa;
+    v.ent = v.heads + L;
+    return v;
+}
+struct MergeRed {
+    float m[kWaves];
+    double S[kWaves];
+    int bad[kWaves];
+    int n[kWaves];   // entries
+    int ne[kWaves];  // non-empty lists
+    int ncand;       // candidates of the final ranking
+};
+
 __device__ __forceinline__ char* list_rec(const SignpostArgs& a, int b, int l) {
     return a.ws + a.plan.ctr_bytes + ((size_t)b * a.plan.L + l) * a.plan.rec_stride;
 }
@@ -106,8 +143,6 @@ __device__ __forceinline__ char* list_rec(const SignpostArgs& a, int b, int l) {
 // One wave: its list of the kappa largest columns, with m_w and S_w.
 template <int DT, bool VEC>
 __device__ void wave_list(const SignpostArgs& a, int b, int s, char* wlds) {
-    using WO = WaveOrder<DT>;
-    using OT = typename WO::T;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int kappa = a.kappa;
@@ -124,15 +159,10 @@ __device__ void wave_list(const SignpostArgs& a, int b, int s, char* wlds) {
         for (int i = 0; i < kPer; ++i) v[i] = -INFINITY;
     }
 
-    // 1. lane maximum (first column on ties), wave maximum, sum of exponentials
+    // 1. lane maximum, wave maximum, sum of exponentials
     float lm = v[0];
-    int li = 0;
 #pragma unroll
-    for (int i = 1; i < kPer; ++i)
-        if (v[i] > lm) {
-            lm = v[i];
-            li = i;
-        }
+    for (int i = 1; i < kPer; ++i) lm = fmaxf(lm, v[i]);
     const bool lane_valid = nvalid > 0;
     const float mw = wave_max(lane_valid ? lm : -INFINITY);
     double Sw = 0.0;
@@ -149,198 +179,239 @@ __device__ void wave_list(const SignpostArgs& a, int b, int s, char* wlds) {
         Sw = wave_sum((double)s0 + (double)s1);
     }
 
-    // 2. tau: the kappa-th largest lane maximum
-    const OT lc = lane_valid ? WO::of(lm, lane * kPer + li, c0 + li) : OT(0);
-    OT cur = lc, tau = 0;
-    int taken = 0;
-    for (int r = 0; r < kappa; ++r) {
-        const OT W = wave_max(cur);
-        if (W == OT(0)) break;
-        tau = W;
-        ++taken;
-        if (cur == W) cur = OT(0);
+    // 2. tau: the kappa-th largest lane maximum, counting ties (bitwise search on the order
+    // key with ballots).  Every element of the wave's top kappa is >= tau; the elements > tau
+    // sit in the (fewer than kappa) lanes whose maximum is > tau, and the elements == tau
+    // needed are the first ones in column order, found in the first kappa lanes whose maximum
+    // is tau.  Lanes are column-contiguous, so lane order is column order.
+    const uint32_t lk = lane_valid ? order_key(lm) : 0u;  // valid keys are > 0 (NaN drops out)
+    const bool all_cand = __popcll(__ballot(lk != 0u)) < kappa;
+    uint32_t tau = 0;
+    if (!all_cand) {
+        const int lo = DT == SPEC_BF16 ? 16 : 0;  // bf16 keys carry 16 bits
+        for (int bit = 31; bit >= lo; --bit) {
+            const uint32_t c = tau | (1u << bit);
+            if (__popcll(__ballot(lk >= c)) >= kappa) tau = c;
+        }
+        if (DT == SPEC_BF16 && !(tau & 0x80000000u)) tau |= 0xFFFFu;  // a negative bf16 value's key
     }
-    const bool all_cand = taken < kappa;  // fewer valid lanes than kappa: every column competes
-    const bool cand_lane = lane_valid && (all_cand || lc >= tau);
+    const float tf = key_to_float(tau);
+    const bool gt_lane = lane_valid && (all_cand || lm > tf);
+    const bool eq_lane = !all_cand && lane_valid && lm == tf;
+    const bool staged = gt_lane || (eq_lane && lane_rank(__ballot(eq_lane)) < kappa);
 
-    // stage the candidate lanes (at most kappa) in LDS
-    float* stage = reinterpret_cast<float*>(wlds);
-    int* slot_lane = reinterpret_cast<int*>(stage + (size_t)kappa * kPer);
-    uint64_t* cand = reinterpret_cast<uint64_t*>(wlds + align_to((size_t)kappa * kPer * 4 + (size_t)kappa * 4, 8));
-    const uint64_t cm = __ballot(cand_lane);
-    const int nl = __popcll(cm);
-    if (cand_lane) {
-        const int slot = lane_rank(cm);
+    float* stage = reinterpret_cast<float*>(wlds);                        // [2 kappa][kPer]
+    int* slot_lane = reinterpret_cast<int*>(stage + (size_t)2 * kappa * kPer);  // [2 kappa]
+    uint64_t* gl = reinterpret_cast<uint64_t*>(wlds + wave_stage_bytes(kappa));  // [kPer kappa]
+    uint64_t* el = gl + (size_t)kPer * kappa;                             // [kappa]
+    const uint64_t sm = __ballot(staged);
+    const int nl = __popcll(sm);
+    if (staged) {
+        const int slot = lane_rank(sm);
 #pragma unroll
         for (int i = 0; i < kPer; ++i) stage[slot * kPer + i] = v[i];
         slot_lane[slot] = lane;
     }
     wave_lds_handover();
 
-    // candidates: staged columns whose order is >= tau
-    int nc = 0;
+    // classify the staged columns in column order: > tau into gl, the first kappa == tau into el
+    int ngt = 0, neq = 0;
     const int total = nl * kPer;
     for (int e0 = 0; e0 < total; e0 += kWave) {
         const int e = e0 + lane;
-        bool take = false;
-        uint64_t key = 0;
+        bool gt = false, eq = false;
+        float z = 0.0f;
+        int col = 0;
         if (e < total) {
-            const int local = slot_lane[e / kPer] * kPer + (e % kPer);
-            const int col = base + local;
-            const float z = stage[e];
+            col = base + slot_lane[e / kPer] * kPer + (e % kPer);
+            z = stage[e];
             if (col < a.V) {
-                take = all_cand || WO::of(z, local, col) >= tau;
-                key = row_order(z, col);
+                gt = all_cand || z > tf;
+                eq = !all_cand && z == tf;
             }
         }
-        const uint64_t tm = __ballot(take);
-        if (take) cand[nc + lane_rank(tm)] = key;
-        nc += __popcll(tm);
+        const uint64_t gm = __ballot(gt), em = __ballot(eq);
+        if ((gm | em) != 0ull) {
+            const uint64_t key = row_order(z, col);
+            if (gt) gl[ngt + lane_rank(gm)] = key;
+            if (eq) {
+                const int r = neq + lane_rank(em);
+                if (r < kappa) el[r] = key;
+            }
+            ngt += __popcll(gm);
+            neq += __popcll(em);
+        }
     }
     wave_lds_handover();
 
-    // 3. exact ranking of the candidates, published in descending order
-    const int keep = min(kappa, nc);
+    // 3. the list: the elements > tau ranked exactly, then those == tau in column order
+    const int keep_gt = min(kappa, ngt);
+    const int keep_eq = min(kappa - keep_gt, min(neq, kappa));
     char* rec = list_rec(a, b, s * kWaves + wave);
     uint64_t* ent = reinterpret_cast<uint64_t*>(rec + sizeof(ListHead));
-    if (nc <= kWave) {
-        const uint64_t mine = lane < nc ? cand[lane] : 0ull;
+    if (ngt <= kWave) {
+        const uint64_t mine = lane < ngt ? gl[lane] : 0ull;
         int rank = 0;
-        for (int i = 0; i < nc; ++i) rank += cand[i] > mine ? 1 : 0;
-        if (lane < nc && rank < keep) ent[rank] = mine;
+        for (int i = 0; i < ngt; ++i) rank += gl[i] > mine ? 1 : 0;
+        if (lane < ngt && rank < keep_gt) ent[rank] = mine;
     } else {
-        for (int r = 0; r < keep; ++r) {
+        for (int r = 0; r < keep_gt; ++r) {
             uint64_t best = 0;
             int bi = -1;
-            for (int i = lane; i < nc; i += kWave) {
-                const uint64_t x = cand[i];
+            for (int i = lane; i < ngt; i += kWave) {
+                const uint64_t x = gl[i];
                 if (x > best) {
                     best = x;
                     bi = i;
                 }
             }
             const uint64_t W = wave_max(best);
-            if (bi >= 0 && best == W) cand[bi] = 0ull;
+            if (bi >= 0 && best == W) gl[bi] = 0ull;
             if (lane == 0) ent[r] = W;
             wave_lds_handover();
         }
     }
+    if (lane < keep_eq) ent[keep_gt + lane] = el[lane];
     if (lane == 0) {
         ListHead h;
         h.m = mw;
-        h.count = keep;
+        h.count = keep_gt + keep_eq;
         h.S = Sw;
         *reinterpret_cast<ListHead*>(rec) = h;
     }
 }
 
-// The last workgroup of a row: merge its lists into the row's signposts.
-__device__ void merge_row(const SignpostArgs& a, int b, char* lds, double* red_d, float* red_f, int* red_i) {
+// The last workgroup of a row: merge its lists into the row's signposts.  Only the lists whose
+// first entry ranks among the kappa largest first entries can hold a top-kappa element (kappa
+// larger heads would precede any other), so their entries (at most kappa^2) are ranked exactly.
+__device__ void merge_row(const SignpostArgs& a, int b, char* lds, MergeRed* red) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int L = a.plan.L, kappa = a.kappa;
-    int* cnt = reinterpret_cast<int*>(lds);
-    float* mlist = reinterpret_cast<float*>(cnt + L);
-    int* cursor = reinterpret_cast<int*>(mlist + L);
-    double* Slist = reinterpret_cast<double*>(lds + align_to((size_t)L * 12, 8));
-    uint64_t* res = reinterpret_cast<uint64_t*>(Slist + L);
-    uint64_t* staged = reinterpret_cast<uint64_t*>(lds + align_to(a.plan.merge_arrays, 8));
+    MergeView mv = merge_view(lds, L, kappa);
 
-    float mloc = -INFINITY;
-    int bad = 0;
+    // every list's header and entries, one round trip to L2
     for (int l = threadIdx.x; l < L; l += kThreads) {
         const char* rec = list_rec(a, b, l);
-        const float ml = ldnt(reinterpret_cast<const float*>(rec));
-        const int c = ldnt(reinterpret_cast<const int32_t*>(rec + 4));
-        const double Sl = ldnt(reinterpret_cast<const double*>(rec + 8));
-        cnt[l] = c;
-        mlist[l] = ml;
-        Slist[l] = Sl;
-        cursor[l] = 0;
-        if (c > 0 && ml > mloc) mloc = ml;
-        if (Sl != Sl) bad = 1;
+        mv.m[l] = ldnt(reinterpret_cast<const float*>(rec));
+        mv.cnt[l] = ldnt(reinterpret_cast<const int32_t*>(rec + 4));
+        mv.S[l] = ldnt(reinterpret_cast<const double*>(rec + 8));
     }
-    const float m = block_max<float>(mloc, red_f);
-    double sp = 0.0;
-    for (int l = threadIdx.x; l < L; l += kThreads)
-        if (mlist[l] > -INFINITY) sp += Slist[l] * exp((double)mlist[l] - (double)m);
-    const double S = block_sum<double>(sp, red_d);
-    bad = block_max<int>(bad | (m == -INFINITY || m == INFINITY ? 1 : 0), red_i);
-    const double logS = log(S);
-
-    const int in_lds = a.plan.merge_in_lds;
-    if (in_lds) {
-        for (int idx = threadIdx.x; idx < L * kappa; idx += kThreads) {
-            const int l = idx / kappa, i = idx - l * kappa;
-            staged[idx] = i < cnt[l]
-                              ? ldnt(reinterpret_cast<const uint64_t*>(list_rec(a, b, l) + sizeof(ListHead)) + i)
-                              : 0ull;
-        }
+    for (int idx = threadIdx.x; idx < L * kappa; idx += kThreads) {
+        const int l = idx / kappa, i = idx - l * kappa;
+        mv.ent[idx] = ldnt(reinterpret_cast<const uint64_t*>(list_rec(a, b, l) + sizeof(ListHead)) + i);
     }
     __syncthreads();
-    if (wave != 0) return;
 
-    auto entry = [&](int l, int i) -> uint64_t {
-        if (i >= cnt[l]) return 0ull;
-        return in_lds ? staged[(size_t)l * kappa + i]
-                      : ldnt(reinterpret_cast<const uint64_t*>(list_rec(a, b, l) + sizeof(ListHead)) + i);
-    };
-    // tournament: each lane holds the lists l = lane (mod 64); the winner advances its cursor
-    uint64_t best = 0;
-    int bl = -1;
-    for (int l = lane; l < L; l += kWave) {
-        const uint64_t x = entry(l, 0);
-        if (x > best) {
-            best = x;
-            bl = l;
-        }
+    // row maximum, sum of exponentials, bad flag, element count: per wave, then across waves
+    float mloc = -INFINITY;
+    int bad = 0, n = 0, ne = 0;
+    for (int l = threadIdx.x; l < L; l += kThreads) {
+        const int c = mv.cnt[l];
+        if (c > 0 && mv.m[l] > mloc) mloc = mv.m[l];
+        if (mv.S[l] != mv.S[l]) bad = 1;
+        n += c;
+        ne += c > 0 ? 1 : 0;
+        mv.heads[l] = c > 0 ? mv.ent[(size_t)l * kappa] : 0ull;
     }
-    int nres = 0;
-    for (; nres < kappa; ++nres) {
-        const uint64_t W = wave_max(best);
-        if (W == 0ull) break;
-        if (lane == 0) res[nres] = W;
-        if (bl >= 0 && best == W) {
-            cursor[bl] += 1;
-            best = 0;
-            bl = -1;
-            for (int l = lane; l < L; l += kWave) {
-                const uint64_t x = entry(l, cursor[l]);
-                if (x > best) {
-                    best = x;
-                    bl = l;
-                }
+    const float mwv = wave_max(mloc);
+    double sp = 0.0;
+    if (mwv != -INFINITY)
+        for (int l = threadIdx.x; l < L; l += kThreads)
+            if (mv.m[l] > -INFINITY) sp += mv.S[l] * (double)exp_diff(mv.m[l], mwv);
+    sp = wave_sum(sp);
+    bad = wave_max(bad);
+    n = wave_sum(n);
+    ne = wave_sum(ne);
+    if (lane == 0) {
+        red->m[wave] = mwv;
+        red->S[wave] = sp;
+        red->bad[wave] = bad;
+        red->n[wave] = n;
+        red->ne[wave] = ne;
+    }
+    __syncthreads();
+    // heads: rank of each list's first entry among all lists' first entries (L is a multiple
+    // of 4, the loads are independent)
+    for (int l = threadIdx.x; l < L; l += kThreads) {
+        const uint64_t h = mv.heads[l];
+        if (h == 0ull) continue;
+        int r = 0;
+#pragma unroll 4
+        for (int j = 0; j < L; j += 4) {
+            r += mv.heads[j] > h ? 1 : 0;
+            r += mv.heads[j + 1] > h ? 1 : 0;
+            r += mv.heads[j + 2] > h ? 1 : 0;
+            r += mv.heads[j + 3] > h ? 1 : 0;
+        }
+        if (r < kappa) mv.top[r] = l;
+    }
+    float m = -INFINITY;
+    int nall = 0, nne = 0;
+    bad = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        m = fmaxf(m, red->m[w]);
+        bad |= red->bad[w];
+        nall += red->n[w];
+        nne += red->ne[w];
+    }
+    double S = 0.0;
+    for (int w = 0; w < kWaves; ++w)
+        if (red->m[w] != -INFINITY) S += red->S[w] * (double)exp_diff(red->m[w], m);
+    bad |= (m == -INFINITY || m == INFINITY) ? 1 : 0;
+    const double logS = log(S);
+    const int nout = min(kappa, nall);   // entries the row has (fewer than kappa only if V < kappa)
+
+    // candidates: every entry of the top-head lists (the non-empty lists with a head rank below
+    // kappa), in slots rank * kappa + i
+    // (entries below the kappa-th largest head cannot make the top kappa: the kappa heads
+    // precede them), compacted through an LDS counter
+    const int nlists = min(kappa, nne);
+    if (threadIdx.x == 0) red->ncand = 0;
+    __syncthreads();  // the top-head lists, the counter
+    const uint64_t floor_h = nlists == kappa ? mv.heads[mv.top[kappa - 1]] : 0ull;
+    for (int j = threadIdx.x; j < nlists * kappa; j += kThreads) {
+        const int r = j / kappa, i = j - r * kappa;
+        const int l = mv.top[r];
+        const uint64_t e = i < mv.cnt[l] ? mv.ent[(size_t)l * kappa + i] : 0ull;
+        if (e != 0ull && e >= floor_h) mv.cand[atomicAdd(&red->ncand, 1)] = e;
+    }
+    __syncthreads();
+    const int ncand = red->ncand;
+    const size_t o0 = (size_t)b * kappa;
+    if (bad) {
+        if (threadIdx.x < kappa) {
+            a.out_ids[o0 + threadIdx.x] = -1;
+            a.out_logp[o0 + threadIdx.x] = __uint_as_float(0x7FC00000u);
+            if (a.out_logp_bf16) a.out_logp_bf16[o0 + threadIdx.x] = 0x7FC0;
+        }
+    } else {
+        for (int j = threadIdx.x; j < ncand; j += kThreads) {
+            const uint64_t c = mv.cand[j];
+            int r = 0;
+#pragma unroll 8
+            for (int i = 0; i < ncand; ++i) r += mv.cand[i] > c ? 1 : 0;
+            if (r < kappa) {
+                const float z = key_to_float((uint32_t)(c >> 32));
+                const float lp = (float)((double)z - (double)m - logS);
+                a.out_ids[o0 + r] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
+                a.out_logp[o0 + r] = lp;
+                if (a.out_logp_bf16) a.out_logp_bf16[o0 + r] = bf16_rne(lp);
             }
         }
-    }
-    wave_lds_handover();
-    if (lane < kappa) {
-        const size_t o = (size_t)b * kappa + lane;
-        int32_t id = -1;
-        float lp;
-        if (bad) {
-            lp = __uint_as_float(0x7FC00000u);
-        } else if (lane < nres) {
-            const uint64_t c = res[lane];
-            id = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
-            const float z = key_to_float((uint32_t)(c >> 32));
-            lp = (float)((double)z - (double)m - logS);
-        } else {
-            lp = -INFINITY;
+        for (int p = nout + (int)threadIdx.x; p < kappa; p += kThreads) {
+            a.out_ids[o0 + p] = -1;
+            a.out_logp[o0 + p] = -INFINITY;
+            if (a.out_logp_bf16) a.out_logp_bf16[o0 + p] = 0xFF80;
         }
-        a.out_ids[o] = id;
-        a.out_logp[o] = lp;
-        if (a.out_logp_bf16) a.out_logp_bf16[o] = bf16_rne(lp);
     }
-    if (lane == 0 && a.out_status) a.out_status[b] = bad ? kStBadLogit : 0u;
+    if (threadIdx.x == 0 && a.out_status) a.out_status[b] = bad ? kStBadLogit : 0u;
 }
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void signpost_kernel(SignpostArgs a) {
     extern __shared__ __align__(16) char lds[];
-    __shared__ double red_d[kWaves];
-    __shared__ float red_f[kWaves];
-    __shared__ int red_i[kWaves];
+    __shared__ MergeRed red;
     __shared__ int last;
     const int nS = a.plan.nS;
     const int x = blockIdx.x % kXcd, l = blockIdx.x / kXcd;
@@ -356,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void signpost_kernel(SignpostArgs a) {
     __syncthreads();
     if (!last) return;
     if (threadIdx.x == 0) *ctr = 0u;  // ready for the next call
-    merge_row(a, b, lds, red_d, red_f, red_i);
+    merge_row(a, b, lds, &red);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -126,7 +126,7 @@ def test_mirror_entry_points_argument_errors():
     assert capi.mirror_signpost_workspace_bytes(64, 151936, 8) > 0
     assert capi.mirror_signpost_workspace_bytes(64, 151936, capi.SPEC_MAX_KAPPA + 1) == 0
     assert capi.mirror_signpost_workspace_bytes(0, 100, 8) == 0
-    assert capi.mirror_signpost_workspace_bytes(1, (1 << 21) + 1, 8) == 0
+    assert capi.mirror_signpost_workspace_bytes(1, (1 << 19) + 1, 8) == 0
     ws = capi.mirror_signpost_workspace_bytes(4, 1000, 8)
 
     def sp(**kw):
