@@ -10,6 +10,7 @@ import ctypes
 import os
 import subprocess
 from dataclasses import dataclass
+from typing import Optional
 
 import numpy as np
 
@@ -26,6 +27,7 @@ ST_BAD_PARAM = 256
 FL_NEAR_ACCEPT = 1
 FL_NEAR_CDF = 2
 FL_NEAR_NUCLEUS = 4
+FL_NEAR_FUZZY = 8
 
 FP32 = 0
 BF16 = 1
@@ -57,9 +59,12 @@ def lib():
         L.orc_downweight_probs_f64.argtypes = [P, P, i32, i32, f64, P, P]
         L.orc_downweight_probs_f64.restype = f64
         L.orc_downweight.argtypes = [P, i32, i32, i32, i32, i32, P, i32, f64, P, P, P, P, i32]
-        L.orc_verify_u.argtypes = [P, i32, P, i32, i32, i32, i32, P, i32, f64, P, i32, P, P, P, P, P, P, i32, i32]
+        L.orc_verify_u.argtypes = [P, i32, P, i32, i32, i32, i32, P, i32, f64, P, i32, P, P, P, P, P, P, i32, i32,
+                                   P, i32, P]
         L.orc_verify.argtypes = [P, i32, P, i32, i32, i32, i32, P, i32, f64, P, i32, u64, u64, P, P, P, P, P, i32,
-                                 i32]
+                                 i32, P, i32, P]
+        L.orc_jsd_bits.argtypes = [P, P, i32]
+        L.orc_jsd_bits.restype = f64
         L.orc_uniform_tokens.argtypes = [P, i32, i32, P]
         L.orc_backup_plan.argtypes = [i32, P, i32, i32, P, P]
         L.orc_fanout.argtypes = [i32, i32, f64, f64, P, P]
@@ -137,6 +142,7 @@ class VerifyResult:
     status: np.ndarray
     flags: np.ndarray
     tokens: np.ndarray
+    div: Optional[np.ndarray] = None
 
 
 def _check(rc, name):
@@ -145,12 +151,14 @@ def _check(rc, name):
 
 
 def verify(draft, target, dtype, K, params, F=0, C=1.0, tokens=None, seed=0, round_=0, U=None,
-           nthreads=0, uniform_draft=False) -> VerifyResult:
+           nthreads=0, uniform_draft=False, tau=None, assisted=False) -> VerifyResult:
     """draft [B][Kd][V], target [B][K+1][V] (float32 or uint16 bf16 bits).
 
     ``tokens`` None => the draft tokens are sampled from the processed draft (lane 2).
     ``U`` given => explicit uniforms [B][K+1][3] instead of the Philox stream.
     ``uniform_draft`` => the draft distribution is uniform on [0, V) (``draft`` may be None).
+    ``tau`` [B] => fuzzy acceptance (PyramidSD) with these thresholds; ``assisted`` => the
+    correction is drawn from q; the result's ``div`` holds the divergences [B][K].
     """
     target = np.ascontiguousarray(target)
     if draft is None:
@@ -168,16 +176,19 @@ def verify(draft, target, dtype, K, params, F=0, C=1.0, tokens=None, seed=0, rou
     W = np.zeros(B, np.float64)
     st = np.zeros(B, np.uint32)
     fl = np.zeros(B, np.uint32)
+    tau_a = None if tau is None else np.ascontiguousarray(np.broadcast_to(np.asarray(tau, np.float64), (B,)))
+    div = None if tau is None else np.zeros((B, K), np.float64)
+    fz = (_p(tau_a), int(assisted), _p(div))
     if U is None:
         rc = lib().orc_verify(_p(draft), Kd, _p(target), dtype, B, K, V, _p(params), F, C, _p(tok), int(sample),
-                              seed, round_, _p(k), _p(t), _p(W), _p(st), _p(fl), nthreads, int(uniform_draft))
+                              seed, round_, _p(k), _p(t), _p(W), _p(st), _p(fl), nthreads, int(uniform_draft), *fz)
     else:
         U = np.ascontiguousarray(U, dtype=np.float64)
         assert U.shape == (B, K + 1, 3)
         rc = lib().orc_verify_u(_p(draft), Kd, _p(target), dtype, B, K, V, _p(params), F, C, _p(tok), int(sample),
-                                _p(U), _p(k), _p(t), _p(W), _p(st), _p(fl), nthreads, int(uniform_draft))
+                                _p(U), _p(k), _p(t), _p(W), _p(st), _p(fl), nthreads, int(uniform_draft), *fz)
     _check(rc, "verify")
-    return VerifyResult(k, t, W, st, fl, tok)
+    return VerifyResult(k, t, W, st, fl, tok, div)
 
 
 def downweight(draft, dtype, K, params, F, C, want_probs=False, nthreads=0):
@@ -268,3 +279,10 @@ def tree_lookup(tokens, parents, path, k, t):
     _check(lib().orc_tree_lookup(_p(tokens), _p(parents), B, N, gamma, _p(path), _p(k), _p(t), _p(node), _p(hit),
                                  _p(batch)), "tree_lookup")
     return node, hit, batch
+
+
+def jsd_bits(p, q):
+    """Jensen-Shannon divergence in bits of two distributions (the oracle's own routine)."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    return float(lib().orc_jsd_bits(_p(p), _p(q), len(p)))

@@ -13,7 +13,10 @@
 //     batch-aware switch to a random-token backup speculator on a cache miss);
 //   * Mirror-SD reading notes sections 3.1-3.3 (the early-exit signposts: top-kappa tokens of
 //     the layer-l_e distribution with their log-probabilities; reuse of a committed prefix
-//     against a draft tree that branches below its roots, as in the worked example).
+//     against a draft tree that branches below its roots, as in the worked example);
+//   * PyramidSD notes, "key designs" 1 and 2 (fuzzy acceptance: a drafted token passes when the
+//     divergence between the verifier's and the drafter's distributions is at most a threshold;
+//     the assisted variant draws the correction from the verifier's own distribution).
 //
 // Notation follows the DeepMind page: p = draft distribution, q = target distribution.
 // Only tests/, the smoke check and the bench's CPU-baseline leg may load this library; the
@@ -114,7 +117,11 @@ enum : uint32_t {
     ST_BAD_PARAM = 256,
 };
 // oracle-only near-boundary flags (parity excludes flagged requests and counts them)
-enum : uint32_t { FL_NEAR_ACCEPT = 1, FL_NEAR_CDF = 2, FL_NEAR_NUCLEUS = 4 };
+enum : uint32_t { FL_NEAR_ACCEPT = 1, FL_NEAR_CDF = 2, FL_NEAR_NUCLEUS = 4, FL_NEAR_FUZZY = 8 };
+
+// A divergence within this absolute distance of the fuzzy threshold flags the request (the
+// divergence is an fp64 sum over the vocabulary; its rounding is ~1e-15).
+const double kNearFuzzy = 1e-9;
 
 // Near-tie bands.  A uniform within 1e-6 relative of an acceptance or CDF boundary flags the
 // request.  The nucleus cut compares fp64 masses (per-value sums of exact counts on the GPU,
@@ -266,6 +273,30 @@ int32_t uniform_token(double u, int V) {
     return (int32_t)(prod >> 53);
 }
 
+// Jensen-Shannon divergence in bits between two distributions over the same tokens:
+// D = 1/2 sum p log2(p / m) + 1/2 sum q log2(q / m), m = (p + q) / 2 (0 log 0 = 0), in [0, 1].
+double jsd_bits(const std::vector<double>& p, const std::vector<double>& q) {
+    double d = 0.0;
+    for (size_t i = 0; i < p.size(); ++i) {
+        const double m = 0.5 * (p[i] + q[i]);
+        if (p[i] > 0.0) d += 0.5 * p[i] * std::log2(p[i] / m);
+        if (q[i] > 0.0) d += 0.5 * q[i] * std::log2(q[i] / m);
+    }
+    return d;
+}
+
+// Fuzzy acceptance (PyramidSD; a reading, the page leaves Div open): Div is the Jensen-Shannon
+// divergence in bits of the processed distributions q_j (verifier) and p'_j (drafter).  Where
+// Div <= tau the drafted token passes outright; elsewhere the lossless test and correction
+// apply, so tau < 0 (or any tau below every divergence) is the lossless rule.  With
+// `assisted`, a rejected position draws its correction from q_j itself.
+struct Fuzzy {
+    bool on = false;
+    double tau = -1.0;
+    bool assisted = false;
+    double* div = nullptr;  // [K] divergences, nullable
+};
+
 struct Request {
     int32_t k = 0;
     int32_t t = -1;
@@ -280,7 +311,7 @@ struct Request {
 // top-p and sigma_{F,C} do not apply to it, and sampled draft tokens are uniform draws.
 Request verify_one(const void* draft, int draft_rows, const void* target, int dtype, int b, int K, int V,
                    const Params& prm, int F, double C, int32_t* tokens, bool sample_draft,
-                   const double* U, bool uniform_draft) {
+                   const double* U, bool uniform_draft, const Fuzzy& fz = Fuzzy()) {
     Request out;
     if (!(prm.temperature >= 0.0f) || std::isinf(prm.temperature) || !(prm.top_p > 0.0f)) {
         out.status |= ST_BAD_PARAM;
@@ -339,12 +370,19 @@ Request verify_one(const void* draft, int draft_rows, const void* target, int dt
             return out;
         }
     }
+    if (fz.on && fz.div)
+        for (int j = 0; j < K; ++j) fz.div[j] = jsd_bits(q[j].p, p[j].p);
     // Acceptance scan: s_j is kept with probability min(1, q(s_j) / p(s_j)); the first
     // rejection ends the scan.
     int k = K;
     for (int j = 0; j < K; ++j) {
         const int s = tokens[j];
         bool accept;
+        if (fz.on) {
+            const double D = fz.div ? fz.div[j] : jsd_bits(q[j].p, p[j].p);
+            if (std::fabs(D - fz.tau) <= kNearFuzzy) out.flags |= FL_NEAR_FUZZY;
+            if (D <= fz.tau) continue;  // fuzzy pass
+        }
         if (greedy) {
             accept = (s == q[j].argmax);
         } else {
@@ -367,7 +405,13 @@ Request verify_one(const void* draft, int draft_rows, const void* target, int dt
         return out;
     }
     bool near = false;
-    if (k < K) {
+    if (k < K && fz.on && fz.assisted) {
+        // assisted correction: from the verifier's distribution at the rejected position
+        double W = 0.0;
+        for (int i = 0; i < V; ++i) W += q[k].p[i] > p[k].p[i] ? q[k].p[i] - p[k].p[i] : 0.0;
+        out.W = W;
+        out.t = inverse_cdf(q[k].p, U[3 * k + 1], &near);
+    } else if (k < K) {
         // correction token: the normalised residual (q - p)+ at the rejected position
         std::vector<double> w(V);
         double W = 0.0;
@@ -494,17 +538,26 @@ int orc_downweight(const void* draft, int draft_rows, int dtype, int B, int K, i
 
 // Verification with explicit uniforms U[B][K+1][3].  tokens[B][K] is read, or written when
 // sample_draft != 0.  Outputs k, t*, residual mass W, status bits and oracle near-tie flags.
+// tau (nullable) [B]: fuzzy thresholds (PyramidSD); assisted: corrections from q; out_div
+// (nullable) [B][K]: the divergences.
 int orc_verify_u(const void* draft, int draft_rows, const void* target, int dtype, int B, int K, int V,
                  const void* params, int F, double C, int32_t* tokens, int sample_draft, const double* U,
                  int32_t* out_k, int32_t* out_t, double* out_W, uint32_t* out_status, uint32_t* out_flags,
-                 int nthreads, int uniform_draft) {
+                 int nthreads, int uniform_draft, const double* tau, int assisted, double* out_div) {
     const Params* prm = static_cast<const Params*>(params);
     if ((!draft && !uniform_draft) || !target || !tokens || !U || B < 1 || K < 1 || V < 1 ||
         (!uniform_draft && draft_rows < K) || F < 0 || !(C >= 0.0 && C <= 1.0) || (dtype != kFP32 && dtype != kBF16))
         return -1;
     parallel_for(B, nthreads, [&](int b) {
+        Fuzzy fz;
+        if (tau) {
+            fz.on = true;
+            fz.tau = tau[b];
+            fz.assisted = assisted != 0;
+            fz.div = out_div ? out_div + (size_t)b * K : nullptr;
+        }
         Request r = verify_one(draft, draft_rows, target, dtype, b, K, V, prm[b], F, C, tokens + (size_t)b * K,
-                               sample_draft != 0, U + (size_t)b * (K + 1) * 3, uniform_draft != 0);
+                               sample_draft != 0, U + (size_t)b * (K + 1) * 3, uniform_draft != 0, fz);
         out_k[b] = r.k;
         out_t[b] = r.t;
         if (out_W) out_W[b] = r.W;
@@ -518,15 +571,20 @@ int orc_verify_u(const void* draft, int draft_rows, const void* target, int dtyp
 int orc_verify(const void* draft, int draft_rows, const void* target, int dtype, int B, int K, int V,
                const void* params, int F, double C, int32_t* tokens, int sample_draft, uint64_t seed, uint64_t round,
                int32_t* out_k, int32_t* out_t, double* out_W, uint32_t* out_status, uint32_t* out_flags,
-               int nthreads, int uniform_draft) {
+               int nthreads, int uniform_draft, const double* tau, int assisted, double* out_div) {
     if (B < 1 || K < 1) return -1;
     std::vector<double> U((size_t)B * (K + 1) * 3);
     orc_uniforms(seed, round, B, K, U.data());
     return orc_verify_u(draft, draft_rows, target, dtype, B, K, V, params, F, C, tokens, sample_draft, U.data(),
-                        out_k, out_t, out_W, out_status, out_flags, nthreads, uniform_draft);
+                        out_k, out_t, out_W, out_status, out_flags, nthreads, uniform_draft, tau, assisted, out_div);
 }
 
 // Uniform draws of the backup speculator (for tests): tokens[n] = floor(u[n] V).
+// Jensen-Shannon divergence in bits of two distributions of length V (for tests).
+double orc_jsd_bits(const double* p, const double* q, int V) {
+    return jsd_bits(std::vector<double>(p, p + V), std::vector<double>(q, q + V));
+}
+
 void orc_uniform_tokens(const double* u, int n, int V, int32_t* out) {
     for (int i = 0; i < n; ++i) out[i] = uniform_token(u[i], V);
 }

@@ -193,7 +193,7 @@ def _bisect(decide, n, iters=64):
     return np.where(lo == 0.0, 0.0, np.where(hi == 1.0, 1.0, 0.5 * (lo + hi)))
 
 
-def exact_law(zd, zt, T=1.0, top_k=0, top_p=1.0, F=0, C=1.0, uniform=False):
+def exact_law(zd, zt, T=1.0, top_k=0, top_p=1.0, F=0, C=1.0, uniform=False, tau=None, assisted=False):
     """Law of the oracle's output over s ~ p' and the uniforms, integrated exactly.
 
     ``uniform``: the draft distribution is the uniform one on [0, V) (the backup speculator);
@@ -221,7 +221,7 @@ def exact_law(zd, zt, T=1.0, top_k=0, top_p=1.0, F=0, C=1.0, uniform=False):
     def run(U, tokens=tok):
         n = U.shape[0]
         return oracle.verify(None if uniform else D[:n], Tt[:n], oracle.FP32, K, prm[:n], F=F, C=C, tokens=tokens,
-                             U=U, uniform_draft=uniform)
+                             U=U, uniform_draft=uniform, tau=tau, assisted=assisted)
 
     # acceptance thresholds a[n, j] with the earlier positions accepting
     a = np.zeros((N, K))
@@ -250,7 +250,7 @@ def exact_law(zd, zt, T=1.0, top_k=0, top_p=1.0, F=0, C=1.0, uniform=False):
                     U[:, m, 0] = 0.5 * (1.0 + a[idx, m])
                 U[:, m, 1] = np.maximum(x, 1e-300)
                 r = oracle.verify(None if uniform else D[:n_i], Tt[:n_i], oracle.FP32, K, prm[:n_i], F=F, C=C,
-                                  tokens=tok[idx], U=U, uniform_draft=uniform)
+                                  tokens=tok[idx], U=U, uniform_draft=uniform, tau=tau, assisted=assisted)
                 assert (r.k == m).all()
                 return r.t <= y
             cuts[:, y + 1] = _bisect(dec, n_i)
@@ -770,3 +770,115 @@ def test_tree_reuse_on_a_comb_is_branch_reuse():
     node, hit2, batch2 = oracle.tree_lookup(tok, par, br[:, 0], k[:, 0], t[:, 0])
     assert (np.where(node >= 0, node // gamma, node) == slot).all()
     assert (hit2 == hit).all() and (batch2 == batch).all()
+
+
+
+# ------------------------------------------------------------------------------------------
+# PyramidSD fuzzy acceptance (Jensen-Shannon divergence in bits against a threshold)
+# ------------------------------------------------------------------------------------------
+import scipy.spatial.distance
+
+
+def test_jsd_matches_scipy():
+    rng = np.random.default_rng(8)
+    for trial in range(200):
+        V = int(rng.integers(1, 30))
+        p = rng.random(V) * (rng.random(V) < 0.7)
+        q = rng.random(V) * (rng.random(V) < 0.7)
+        if p.sum() == 0:
+            p[0] = 1.0
+        if q.sum() == 0:
+            q[-1] = 1.0
+        p /= p.sum()
+        q /= q.sum()
+        ref = scipy.spatial.distance.jensenshannon(p, q, base=2) ** 2   # scipy gives the distance
+        d = oracle.jsd_bits(p, q)
+        assert abs(d - ref) <= 1e-12 and abs(oracle.jsd_bits(q, p) - d) <= 1e-15
+        assert -1e-15 <= d <= 1.0 + 1e-15
+    assert oracle.jsd_bits([1.0, 0.0], [0.0, 1.0]) == 1.0            # disjoint supports
+    assert oracle.jsd_bits([0.3, 0.7], [0.3, 0.7]) == 0.0            # identical
+
+
+def _fuzzy_inputs(rng, B, K, V):
+    zt = rng.normal(0, 1.5, (B, K + 1, V)).astype(np.float32)
+    zd = (zt[:, :K] + rng.normal(0, 1.0, (B, K, V))).astype(np.float32)
+    return zd, zt
+
+
+def test_fuzzy_divergences_and_extremes():
+    rng = np.random.default_rng(12)
+    B, K, V = 30, 3, 40
+    zd, zt = _fuzzy_inputs(rng, B, K, V)
+    T = rng.choice([0.0, 0.7, 1.0], B).astype(np.float32)
+    tk = rng.choice([0, 5], B).astype(np.int32)
+    tp = rng.choice([0.8, 1.0], B).astype(np.float32)
+    prm = oracle.params_array(T, tk, tp)
+    tok = rng.integers(0, V, (B, K))
+    base = oracle.verify(zd, zt, oracle.FP32, K, prm, F=2, C=0.5, tokens=tok, seed=3)
+    # divergences: the Jensen-Shannon divergence of the processed rows (scipy)
+    r = oracle.verify(zd, zt, oracle.FP32, K, prm, F=2, C=0.5, tokens=tok, seed=3, tau=np.full(B, -1.0))
+    for b in range(B):
+        for j in range(K):
+            zz = zd[b, j].astype(np.float64)
+            pj = oracle.process_row(zz, float(T[b]), int(tk[b]), float(tp[b]))[0]
+            pj = oracle.downweight_probs(zz, pj, 2, 0.5)[0] if T[b] > 0 else pj
+            qj = oracle.process_row(zt[b, j].astype(np.float64), float(T[b]), int(tk[b]), float(tp[b]))[0]
+            ref = scipy.spatial.distance.jensenshannon(pj, qj, base=2) ** 2
+            assert abs(r.div[b, j] - ref) <= 1e-12, (b, j)
+    # a threshold below every divergence is the lossless rule
+    assert (r.k == base.k).all() and (r.t == base.t).all() and (r.status == base.status).all()
+    # the divergence never exceeds 1 bit: tau = 1 passes every drafted token
+    full = oracle.verify(zd, zt, oracle.FP32, K, prm, F=2, C=0.5, tokens=tok, seed=3, tau=np.ones(B))
+    assert (full.k == K).all()
+    # more tolerance never shortens the accepted run (same uniforms)
+    mid = oracle.verify(zd, zt, oracle.FP32, K, prm, F=2, C=0.5, tokens=tok, seed=3, tau=np.median(r.div, axis=1))
+    assert (mid.k >= base.k).all() and (mid.k <= full.k).all()
+
+
+def _fuzzy_law_closed_form(pp, q, tau_pass, assisted):
+    """Law of (k, emitted tokens) from the rule: a position whose divergence passes keeps its
+    drafted token; elsewhere s is kept with probability min(1, q/p), and a rejection emits
+    the residual (q - p)+ (or, assisted, beta q with beta the rejection probability)."""
+    K = len(pp)
+    law = {}
+
+    def walk(j, prefix, prob):
+        if prob == 0.0:
+            return
+        if j == K:
+            for y in range(len(q[K])):
+                key = (K,) + prefix + (y,)
+                law[key] = law.get(key, 0.0) + prob * q[K][y]
+            return
+        p_j, q_j = pp[j], q[j]
+        if tau_pass[j]:
+            for x in range(len(p_j)):
+                walk(j + 1, prefix + (x,), prob * p_j[x])
+            return
+        for x in range(len(p_j)):
+            walk(j + 1, prefix + (x,), prob * min(p_j[x], q_j[x]))
+        beta = float(np.maximum(p_j - q_j, 0.0).sum())
+        corr = q_j * beta if assisted else np.maximum(q_j - p_j, 0.0)
+        for y in range(len(q_j)):
+            key = (j,) + prefix + (y,)
+            law[key] = law.get(key, 0.0) + prob * corr[y]
+
+    walk(0, (), 1.0)
+    return law
+
+
+@pytest.mark.parametrize("assisted", [False, True])
+def test_fuzzy_law_exact_enumeration(assisted):
+    rng = np.random.default_rng(21 + assisted)
+    K, V = 2, 3
+    zd = rng.normal(0, 1.2, (K, V))
+    zt = rng.normal(0, 1.2, (K + 1, V))
+    pp = [oracle.process_row(zd[j].astype(np.float32).astype(np.float64), 1.0, 0, 1.0)[0] for j in range(K)]
+    q = [oracle.process_row(zt[j].astype(np.float32).astype(np.float64), 1.0, 0, 1.0)[0] for j in range(K + 1)]
+    div = [scipy.spatial.distance.jensenshannon(pp[j], q[j], base=2) ** 2 for j in range(K)]
+    tau = 0.5 * (div[0] + div[1])            # one position passes, the other is tested
+    law, _, _ = exact_law(zd, zt, tau=tau, assisted=assisted)
+    want = _fuzzy_law_closed_form(pp, q, [d <= tau for d in div], assisted)
+    keys = set(law) | set(want)
+    assert max(abs(law.get(x, 0.0) - want.get(x, 0.0)) for x in keys) < 1e-9
+    assert abs(sum(law.values()) - 1.0) < 1e-9
