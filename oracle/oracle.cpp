@@ -123,10 +123,12 @@ enum : uint32_t { FL_NEAR_ACCEPT = 1, FL_NEAR_CDF = 2, FL_NEAR_NUCLEUS = 4, FL_N
 // divergence is an fp64 sum over the vocabulary; its rounding is ~1e-15).
 const double kNearFuzzy = 1e-9;
 
-// Near-tie bands.  A uniform within 1e-6 relative of an acceptance or CDF boundary flags the
-// request.  The nucleus cut compares fp64 masses (per-value sums of exact counts on the GPU,
-// rounding ~1e-15), so its band is 1e-9 of the row mass.
+// Near-tie bands.  A uniform within 1e-6 relative of an acceptance boundary flags the
+// request.  The inverse CDF and the nucleus cut compare fp64 running sums of masses (on the
+// GPU per-value sums of exact counts or fp64 sums in another order, rounding ~1e-13), so their
+// bands are 1e-9 of the total mass.
 const double kNearRel = 1e-6;
+const double kNearCdf = 1e-9;
 const double kNearNucleus = 1e-9;
 
 // Token order used by every selection: logit descending, token id ascending on equal logits
@@ -256,7 +258,7 @@ int inverse_cdf(const std::vector<double>& w, double x, bool* near) {
         cum += w[i];
         last = i;
         if (cum > target) {
-            if (target - prev <= kNearRel * total || cum - target <= kNearRel * total) *near = true;
+            if (target - prev <= kNearCdf * total || cum - target <= kNearCdf * total) *near = true;
             return i;
         }
     }

@@ -2,7 +2,8 @@
 
 Integers (k, t*, sampled draft tokens, status bits, downweighted sets, cache token sets, hit
 flags, slots, branch reuse) must be equal on every request the oracle does not flag as a near
-tie (a uniform, or the nucleus target, within 1e-6 relative of a boundary); floats within 1e-5
+tie (a uniform within 1e-6 relative of an acceptance boundary, a CDF or nucleus target within
+1e-9 of the total mass); floats within 1e-5
 relative (fp32 inputs) or 2e-3 (bf16 inputs).  Flagged requests are counted and reported.
 """
 import numpy as np
