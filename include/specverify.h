@@ -26,6 +26,9 @@
  *                          message).
  *   mirror_tree_lookup   - reuse of the committed prefix against a draft tree that may branch
  *                          below its roots.
+ *   pyramid_verify       - PyramidSD fuzzy acceptance (lossy, behind its own entry point):
+ *                          spec_verify where a position whose distributions are within a
+ *                          divergence threshold keeps its drafted token outright.
  *
  * Sources (notation p = draft, q = target, as on the DeepMind page):
  *   [SpS]   "Accelerating LLM Decoding with Speculative Sampling" (DeepMind, arXiv 2302.01318),
@@ -33,6 +36,7 @@
  *   [SSD]   "Speculative Speculative Decoding" reading notes, sections 1.3, 2.2, 4.3, 4.4, 5.1, 7.1.
  *   [SSD-H] hyper.ai summary of arXiv 2603.03251, "Method" (fan-out closed form, sigma_{F,C}).
  *   [MSD]   "Mirror Speculative Decoding" reading notes, sections 2, 3.1, 3.2 and 3.3.
+ *   [PSD]   "3-Model Speculative Decoding (PyramidSD)" notes, method, key designs 1 and 2.
  *
  * Conventions for every entry point:
  *   - Array pointers are HIP device memory owned by the caller (unless marked "host"); the
@@ -88,17 +92,20 @@ typedef struct {
     float top_p;
 } spec_params;
 
-/* flags for spec_verify */
+/* flags for spec_verify (and pyramid_verify) */
 enum {
     SPEC_SAMPLE_DRAFT = 1, /* draft_tokens is an output: s_j is drawn from the processed (and
                               downweighted) draft row j by inverse CDF in token-id order with
                               Philox lane 2, or is the draft argmax when temperature is 0 */
-    SPEC_UNIFORM_DRAFT = 2 /* the draft distribution of every position is uniform on [0, V):
+    SPEC_UNIFORM_DRAFT = 2,/* the draft distribution of every position is uniform on [0, V):
                               the random-token backup speculator ([SSD] section 7.1).  No draft
                               row is read (draft_logits may be NULL), F and C do not apply, and
                               temperature, top-k and top-p act on the target rows only; with
                               SPEC_SAMPLE_DRAFT, s_j = floor(u V) for the Philox lane-2 uniform u
                               (the inverse CDF of the uniform law, taken exactly) */
+    SPEC_ASSISTED = 4      /* pyramid_verify only: a rejected position draws its correction from
+                              the verifier's processed distribution q_j itself, not from the
+                              residual ([PSD] key design 2, the assisted variant) */
 };
 
 /* per-request status bits (out_status) */
@@ -269,6 +276,27 @@ int mirror_signposts(const void* logits, int dtype, int B, int V, int kappa, int
 int mirror_tree_lookup(const int32_t* tree_tokens, const int32_t* tree_parents, int B, int N, int gamma,
                        const int32_t* path_tokens, const int32_t* k, const int32_t* tstar, int32_t* out_node,
                        uint8_t* out_hit, int32_t* out_batch, hipStream_t stream);
+
+/* pyramid_verify - fuzzy acceptance ([PSD] key design 1: a drafted token passes when
+ * Div(P_verifier, P_drafter) <= tau; one call per stage, drafter -> qualifier with tau_Q and
+ * qualifier -> target with tau_T).  Div is read as the Jensen-Shannon divergence in bits
+ * (in [0, 1]) of the processed verifier row q_j and the processed, downweighted drafter row
+ * p'_j.  Where Div_j <= tau[b], s_j is kept outright; elsewhere the lossless test of
+ * spec_verify decides and a rejection draws the correction from the residual, or from q_j with
+ * SPEC_ASSISTED.  A threshold below every divergence (e.g. a negative one) is exactly
+ * spec_verify.  The output distribution is NOT the verifier's: this is a lossy variant.
+ * Arguments as spec_verify (verifier_logits in the place of target_logits), plus
+ *   tau        [B] float32 device, per-request thresholds
+ *   flags      SPEC_SAMPLE_DRAFT | SPEC_UNIFORM_DRAFT | SPEC_ASSISTED
+ *   out_div    [B][K] float32 device (nullable): Div_j of every position whose drafted token
+ *              is valid, whether or not the scan reached it
+ * Runs on the general path (one workgroup per position).  Return codes as spec_verify
+ * (SPEC_EINVAL also for a null tau). */
+int pyramid_verify(const void* draft_logits, int draft_rows, const void* verifier_logits, int dtype, int B, int K,
+                   int V, const spec_params* params, int F, float C, const float* tau, int32_t* draft_tokens,
+                   uint64_t seed, uint64_t round, uint32_t flags, int32_t* out_k, int32_t* out_tstar,
+                   float* out_resid_mass, uint32_t* out_status, float* out_div, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,7 @@ SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP = 0, -1, -2, -3, -
 SPEC_FP32, SPEC_BF16 = 0, 1
 SPEC_SAMPLE_DRAFT = 1
 SPEC_UNIFORM_DRAFT = 2
+SPEC_ASSISTED = 4
 SPEC_MAX_F = 64
 SPEC_MAX_KAPPA = 16
 ST_EMPTY_RESIDUAL = 8
@@ -31,7 +32,7 @@ ST_BAD_PARAM = 256
 
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
            "saguaro_cache_lookup", "saguaro_verify_cache", "saguaro_backup_plan", "mirror_signpost_workspace_bytes",
-           "mirror_signposts", "mirror_tree_lookup")
+           "mirror_signposts", "mirror_tree_lookup", "pyramid_verify")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -65,6 +66,8 @@ class Lib:
         L.mirror_signpost_workspace_bytes.restype = ctypes.c_size_t
         L.mirror_signposts.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.mirror_tree_lookup.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+        L.pyramid_verify.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _P, ctypes.c_uint64,
+                                     ctypes.c_uint64, ctypes.c_uint32, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.saguaro_verify_cache.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
                                            ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                            _P]
@@ -292,3 +295,24 @@ def mirror_tree_lookup(tokens: torch.Tensor, parents: torch.Tensor, path: torch.
                                         _ptr(node), _ptr(hit), _ptr(batch), _stream(stream))
     _check("mirror_tree_lookup", rc)
     return node, hit, batch
+
+
+def pyramid_verify(draft: Optional[torch.Tensor], verifier: torch.Tensor, K: int, params: torch.Tensor,
+                   tau: torch.Tensor, tokens: torch.Tensor, F: int = 0, C: float = 1.0, seed: int = 0, round_: int = 0,
+                   flags: int = 0, want_div: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Fuzzy (PyramidSD) verification of one stage: (VerifyOut, divergences [B][K] or None)."""
+    B, _, V = verifier.shape
+    Kd = draft.shape[1] if draft is not None else K
+    dev = verifier.device
+    if workspace is None:
+        workspace = new_workspace(B, K, V, dev)
+    out = VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                    torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                    tokens)
+    div = torch.zeros((B, K), dtype=torch.float32, device=dev) if want_div else None
+    rc = load().cdll.pyramid_verify(_ptr(draft), Kd, _ptr(verifier), dtype_code(verifier), B, K, V, _ptr(params), F,
+                                    ctypes.c_float(C), _ptr(tau), _ptr(tokens), seed, round_, flags, _ptr(out.k),
+                                    _ptr(out.tstar), _ptr(out.resid_mass), _ptr(out.status), _ptr(div),
+                                    _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("pyramid_verify", rc)
+    return out, div

@@ -88,6 +88,34 @@ int spec_verify(const void* draft_logits, int draft_rows, const void* target_log
     return launch_status();
 }
 
+int pyramid_verify(const void* draft_logits, int draft_rows, const void* verifier_logits, int dtype, int B, int K,
+                   int V, const spec_params* params, int F, float C, const float* tau, int32_t* draft_tokens,
+                   uint64_t seed, uint64_t round, uint32_t flags, int32_t* out_k, int32_t* out_tstar,
+                   float* out_resid_mass, uint32_t* out_status, float* out_div, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+    const bool uniform = (flags & SPEC_UNIFORM_DRAFT) != 0;
+    if ((!draft_logits && !uniform) || !verifier_logits || !params || !tau || !draft_tokens || !out_k || !out_tstar)
+        return SPEC_EINVAL;
+    if (B < 1 || K < 1 || V < 1 || (!uniform && draft_rows != K && draft_rows != K + 1)) return SPEC_EINVAL;
+    if (F < 0 || F > SPEC_MAX_F || !(C >= 0.0f && C <= 1.0f)) return SPEC_EINVAL;
+    if ((flags & ~(uint32_t)(SPEC_SAMPLE_DRAFT | SPEC_UNIFORM_DRAFT | SPEC_ASSISTED)) != 0) return SPEC_EINVAL;
+    if (!valid_dtype(dtype)) return SPEC_EDTYPE;
+    if (!workspace || workspace_bytes < spec_workspace_bytes(B, K, V)) return SPEC_EWORKSPACE;
+    if (uniform) {
+        draft_logits = verifier_logits;
+        draft_rows = K + 1;
+        F = 0;
+        C = 1.0f;
+    }
+    VerifyArgs a{draft_logits, verifier_logits, draft_rows, dtype, B, K, V, params, F, C, draft_tokens, seed,
+                 round, flags, out_k, out_tstar, out_resid_mass, out_status, static_cast<UnitRec*>(workspace),
+                 tau, out_div};
+    hipLaunchKernelGGL(generic_unit_kernel, dim3((unsigned)(B * (K + 1))), dim3(kRowThreadsHost), 0, stream, a);
+    if (launch_status() != SPEC_OK) return SPEC_EHIP;
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, a);
+    return launch_status();
+}
+
 int saguaro_backup_plan(int B, const uint8_t* hit, const int32_t* batch, int b_star, int32_t* out_use_backup,
                         int32_t* out_switch, hipStream_t stream) {
     if (!hit || !batch || !out_use_backup || !out_switch || B < 1) return SPEC_EINVAL;

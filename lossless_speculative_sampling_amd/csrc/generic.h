@@ -32,6 +32,10 @@ struct VerifyArgs {
     float* out_W;
     uint32_t* out_status;
     UnitRec* units;
+    // fuzzy acceptance (PyramidSD): per-request thresholds on the Jensen-Shannon divergence of
+    // q_j and p'_j (null: the lossless rule), the divergences out [B][K] (nullable)
+    const float* tau;
+    float* out_div;
 };
 
 struct DownweightArgs {

@@ -445,8 +445,27 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
         return;
     }
 
+    // fuzzy acceptance (PyramidSD notes, key design 1): the drafted token passes when the
+    // Jensen-Shannon divergence (bits) of q_j and p'_j is at most the request's threshold;
+    // otherwise the lossless test below decides
+    bool fuzzy_pass = false;
+    if (a.tau) {
+        double d = 0.0;
+        for (int i = threadIdx.x; i < a.V; i += blockDim.x) {
+            const double q = rs_prob(stq, load_logit(rq.row, a.dtype, i), i);
+            const double p = uni ? p_uni : rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i);
+            const double m = 0.5 * (p + q);
+            if (p > 0.0) d += 0.5 * p * log2(p / m);
+            if (q > 0.0) d += 0.5 * q * log2(q / m);
+        }
+        const double D = block_sum<double>(d, sh.redd);
+        if (threadIdx.x == 0 && a.out_div) a.out_div[(size_t)b * a.K + j] = (float)D;
+        fuzzy_pass = D <= (double)a.tau[b];
+    }
     bool accept;
-    if (greedy) {
+    if (fuzzy_pass) {
+        accept = true;
+    } else if (greedy) {
         accept = (s == stq.argmax);
     } else {
         const double ps = uni ? p_uni : rs_prob_dw(stp, load_logit(rp.row, a.dtype, s), s);
@@ -472,7 +491,11 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
             return q > p ? q - p : 0.0;
         };
         t = inverse_cdf(rq, v, resid, sh, &W);
-        if (t < 0) {  // no residual mass: fall back to q itself
+        if (a.flags & SPEC_ASSISTED) {
+            // assisted correction (PyramidSD notes, key design 2): drawn from q_j itself
+            double tot;
+            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
+        } else if (t < 0) {  // no residual mass: fall back to q itself
             status |= kStEmptyResidual;
             double tot;
             t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);

@@ -27,6 +27,14 @@ Workloads (the logit recipes are stand-ins for real model logits, which are not 
   continues to depth gamma), padded to N nodes with token -1.  The verified path is root 0's
   chain; k is a truncated geometric draw (per-token acceptance 0.7) and t* is, with
   probability 1/2, the token of a fork off the accepted prefix, else a random token.
+* ``pyramid``  - bf16, V = 128256, three models of one family with an entropy gradient (the
+  smaller the model, the flatter its rows).  Stage 1 verifies l_D = 12 drafted tokens against
+  the qualifier (tau_Q = 0.4): qualifier rows 0.8 t + N(0, 1), drafter rows
+  0.55 t + N(0, s^2) with s ~ U[0.8, 1.6] per row.  Stage 2 verifies l_Q = 25 tokens against
+  the target (tau_T = 0.5): target rows t, qualifier rows 0.8 t + N(0, s^2), s ~ U[1, 3] per
+  row.  t is Zipf-shaped; temperature 1, no truncation, B = 16; the drafted tokens of both
+  stages are drawn by the path from the drafting rows.  The per-row noise spreads the
+  divergences across the thresholds.
 """
 from __future__ import annotations
 
@@ -289,3 +297,37 @@ def mirror(B: int = 64, V: int = 151936, kappa: int = 8, gamma: int = 7, N: int 
         else:
             tt[b] = int(rng.integers(0, V))
     return MirrorWorkload(B, V, kappa, gamma, logits, tok, par, path, kk, tt)
+
+
+@dataclass
+class PyramidStage:
+    """One fuzzy verification stage: drafter rows [B][K][V] against verifier rows [B][K+1][V]."""
+    name: str
+    B: int
+    K: int
+    V: int
+    draft: np.ndarray
+    verifier: np.ndarray
+    tau: np.ndarray
+    tokens: Optional[np.ndarray]
+    seed: int
+
+
+def pyramid(B: int = 16, l_d: int = 12, l_q: int = 25, V: int = 128256, tau_q: float = 0.4, tau_t: float = 0.5,
+            cfg: int = 7) -> tuple[PyramidStage, PyramidStage]:
+    rng = np.random.default_rng(DATA_SEED_BASE + cfg)
+    # stage 1: qualifier rows 0.8 t + N(0, 1), drafter rows 0.55 t + N(0, s^2), s ~ U[0.8, 1.6] per row
+    t = zipf_rows(rng, B * (l_d + 1), V).reshape(B, l_d + 1, V)
+    q1 = 0.8 * t + rng.standard_normal(t.shape, dtype=np.float32)
+    s_d = rng.uniform(0.8, 1.6, size=(B, l_d, 1)).astype(np.float32)
+    d1 = 0.55 * t[:, :l_d] + s_d * rng.standard_normal((B, l_d, V), dtype=np.float32)
+    s1 = PyramidStage("draft->qualifier", B, l_d, V, f32_to_bf16_bits(d1), f32_to_bf16_bits(q1),
+                      np.full(B, tau_q, np.float32), None, VERIFY_SEED_BASE + cfg)
+    del t, q1, d1
+    # stage 2: target rows t, qualifier rows 0.8 t + N(0, s^2), s ~ U[1, 3] per row
+    t2 = zipf_rows(rng, B * (l_q + 1), V).reshape(B, l_q + 1, V)
+    s_q = rng.uniform(1.0, 3.0, size=(B, l_q, 1)).astype(np.float32)
+    q2 = 0.8 * t2[:, :l_q] + s_q * rng.standard_normal((B, l_q, V), dtype=np.float32)
+    s2 = PyramidStage("qualifier->target", B, l_q, V, f32_to_bf16_bits(q2), f32_to_bf16_bits(t2),
+                      np.full(B, tau_t, np.float32), None, VERIFY_SEED_BASE + cfg + 1)
+    return s1, s2

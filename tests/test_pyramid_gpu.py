@@ -1,0 +1,110 @@
+"""PyramidSD fuzzy acceptance (pyramid_verify): GPU <-> oracle parity through the C ABI.
+
+Integers (k, t*, status, sampled tokens) are equal on every request the oracle does not flag
+(near acceptance, CDF, nucleus or fuzzy-threshold ties); the residual mass within 1e-5 (fp32)
+/ 2e-3 (bf16) relative; the divergences within 1e-6 absolute (fp64 sums stored as fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lossless_speculative_sampling_amd import capi, synth
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {synth.FP32: 1e-5, synth.BF16: 2e-3}
+BAD = oracle.ST_BAD_LOGIT | oracle.ST_BAD_PARAM | oracle.ST_BAD_TOKEN
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def check_pyramid(draft, verifier, dtype, K, prm, tau, tokens=None, F=0, C=1.0, seed=5, assisted=False,
+                  uniform=False, label=""):
+    B, _, V = verifier.shape
+    sample = tokens is None
+    say(f"[pyramid] {label} B={B} K={K} V={V} dtype={dtype} sample={sample} assisted={assisted}")
+    flags = (capi.SPEC_SAMPLE_DRAFT if sample else 0) | (capi.SPEC_ASSISTED if assisted else 0) | \
+        (capi.SPEC_UNIFORM_DRAFT if uniform else 0)
+    tok = torch.zeros((B, K), dtype=torch.int32, device="cuda") if sample else dev(np.asarray(tokens, np.int32))
+    prm_t = capi.params_tensor(prm["t"], prm["k"], prm["p"])
+    out, div = capi.pyramid_verify(None if uniform else dev(draft), dev(verifier), K, prm_t,
+                                   dev(np.asarray(tau, np.float32)), tok, F=F, C=C, seed=seed, flags=flags,
+                                   want_div=True)
+    torch.cuda.synchronize()
+    k, t, W = out.k.cpu().numpy(), out.tstar.cpu().numpy(), out.resid_mass.cpu().numpy()
+    st, gtok, gdiv = out.status.cpu().numpy().astype(np.uint32), out.tokens.cpu().numpy(), div.cpu().numpy()
+    o = oracle.verify(None if uniform else draft, verifier, dtype, K, prm, F=F, C=float(np.float32(C)),
+                      tokens=tokens, seed=seed, uniform_draft=uniform, tau=np.asarray(tau, np.float64),
+                      assisted=assisted)
+    ok = o.flags == 0
+    bad = np.flatnonzero(ok & ((k != o.k) | (t != o.t) | (st != o.status)))
+    assert len(bad) == 0, (f"{len(bad)} mismatches, first {bad[:5]}: gpu k={k[bad[:5]]} t={t[bad[:5]]} "
+                           f"st={st[bad[:5]]} | oracle k={o.k[bad[:5]]} t={o.t[bad[:5]]} st={o.status[bad[:5]]}")
+    valid = ok & ((o.status & BAD) == 0)
+    if sample:
+        assert (gtok[valid] == o.tokens[valid]).all()
+    np.testing.assert_allclose(W[ok], o.W[ok], rtol=RTOL[dtype], atol=1e-6)
+    np.testing.assert_allclose(gdiv[valid], o.div[valid], rtol=0, atol=1e-6)
+    say(f"[pyramid] {label} ok: flagged {int((~ok).sum())} of {B}; mean k {k.mean():.3f}; "
+        f"mean div {o.div[valid].mean() if valid.any() else 0:.3f}")
+    return o
+
+
+@pytest.mark.parametrize("dtype", [synth.FP32, synth.BF16])
+@pytest.mark.parametrize("V", [1, 2, 63, 1000, 4097])
+def test_pyramid_shapes_and_parameter_mix(dtype, V):
+    rng = np.random.default_rng(V * 11 + dtype)
+    B, K = 24, 3
+    zt = rng.normal(0, 1.5, (B, K + 1, V)).astype(np.float32)
+    zd = (0.7 * zt[:, :K] + rng.normal(0, 1.0, (B, K, V))).astype(np.float32)
+    if dtype == synth.BF16:
+        zt, zd = synth.f32_to_bf16_bits(zt), synth.f32_to_bf16_bits(zd)
+    T = rng.choice([0.0, 0.6, 1.0, 1.5], B).astype(np.float32)
+    tk = rng.choice([0, 1, 5, 50], B).astype(np.int32)
+    tp = rng.choice([0.3, 0.9, 1.0], B).astype(np.float32)
+    prm = oracle.params_array(T, tk, tp)
+    tau = rng.choice([-1.0, 0.05, 0.2, 0.5, 1.0], B).astype(np.float32)
+    for assisted in (False, True):
+        check_pyramid(zd, zt, dtype, K, prm, tau, F=2, C=0.4, assisted=assisted, label=f"mix V={V}")
+        check_pyramid(zd, zt, dtype, K, prm, tau, tokens=rng.integers(0, V, (B, K)), F=2, C=0.4,
+                      assisted=assisted, label=f"mix-given V={V}")
+    check_pyramid(None, zt, dtype, K, prm, tau, uniform=True, label=f"uniform V={V}")
+
+
+def test_pyramid_two_stages_full_size():
+    s1, s2 = synth.pyramid()
+    prm = oracle.params_array(1.0, 0, 1.0, B=s1.B)
+    o1 = check_pyramid(s1.draft, s1.verifier, synth.BF16, s1.K, prm, s1.tau, seed=s1.seed, label=s1.name)
+    o2 = check_pyramid(s2.draft, s2.verifier, synth.BF16, s2.K, prm, s2.tau, seed=s2.seed, label=s2.name)
+    check_pyramid(s2.draft, s2.verifier, synth.BF16, s2.K, prm, s2.tau, tokens=o2.tokens, seed=s2.seed,
+                  assisted=True, label=s2.name + " assisted")
+    # both branches of the rule occur, and a threshold never shortens the accepted run
+    for o, s in ((o1, s1), (o2, s2)):
+        assert (o.div <= s.tau[:, None]).any() and (o.div > s.tau[:, None]).any()
+    o2l = oracle.verify(s2.draft, s2.verifier, synth.BF16, s2.K, prm, tokens=o2.tokens, seed=s2.seed)
+    assert (o2.k >= o2l.k).all()
+
+
+def test_pyramid_negative_threshold_is_spec_verify():
+    rng = np.random.default_rng(4)
+    B, K, V = 16, 4, 3000
+    zt = rng.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    zd = (zt[:, :K] + rng.normal(0, 1, (B, K, V))).astype(np.float32)
+    prm = oracle.params_array(0.8, 0, 0.95, B=B)
+    tok = rng.integers(0, V, (B, K)).astype(np.int32)
+    prm_t = capi.params_tensor(prm["t"], prm["k"], prm["p"])
+    a, _ = capi.pyramid_verify(dev(zd), dev(zt), K, prm_t, dev(np.full(B, -1.0, np.float32)), dev(tok), seed=9)
+    b = capi.spec_verify(dev(zd), dev(zt), K, prm_t, dev(tok), seed=9)
+    torch.cuda.synchronize()
+    for x, y in zip((a.k, a.tstar, a.status), (b.k, b.tstar, b.status)):
+        assert torch.equal(x, y)
