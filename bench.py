@@ -232,13 +232,79 @@ def bench_mirror(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_pyramid(args):
+    """Both PyramidSD stages per step: l_D = 12 drafted tokens against the qualifier
+    (tau_Q = 0.4), then l_Q = 25 tokens against the target (tau_T = 0.5); B = 16, V = 128256
+    bf16, drafted tokens drawn in the calls.  Inputs rotated so that they are read from HBM."""
+    import numpy as np
+    import torch
+
+    from lossless_speculative_sampling_amd import capi, synth
+    dev = torch.device("cuda:0")
+    stages = synth.pyramid()
+    B = stages[0].B
+    step_bytes = sum(int(s.draft.nbytes + s.verifier.nbytes) for s in stages)
+    copies = max(2, -(-2 * MALL_BYTES // step_bytes) + 1)
+    prm = capi.params_tensor(1.0, 0, 1.0, device=dev).expand(B, 3).contiguous()
+    state = []
+    for s in stages:
+        d0 = torch.from_numpy(s.draft.view(np.int16)).to(dev)
+        v0 = torch.from_numpy(s.verifier.view(np.int16)).to(dev)
+        state.append(dict(st=s, d=[d0] + [d0.clone() for _ in range(copies - 1)],
+                          v=[v0] + [v0.clone() for _ in range(copies - 1)],
+                          tau=torch.from_numpy(s.tau).to(dev), tok=torch.zeros((B, s.K), dtype=torch.int32, device=dev),
+                          ws=capi.new_workspace(B, s.K, s.V, dev)))
+
+    def call(x, i):
+        s = x["st"]
+        return capi.pyramid_verify(x["d"][i % copies], x["v"][i % copies], s.K, prm, x["tau"], x["tok"], seed=s.seed,
+                                   round_=i, flags=capi.SPEC_SAMPLE_DRAFT, workspace=x["ws"])[0]
+
+    for i in range(args.warmup):
+        for x in state:
+            call(x, i)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+          for _ in state]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ks = []
+    e0.record()
+    for i in range(args.steps):
+        for x, e in zip(state, ev):
+            e[i][0].record()
+            o = call(x, i)
+            e[i][1].record()
+            ks.append(o.k)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    stage_ms = [sum(a.elapsed_time(b) for a, b in e) / len(e) for e in ev]
+    positions = B * sum(s.K for s in stages)
+    achieved = step_bytes / (sum(stage_ms) * 1e-3) / 1e9
+    res = {"metric": "fuzzy-verified positions/sec and achieved HBM GB/s (% peak), pyramid",
+           "value": positions / (ms_step * 1e-3), "unit": "verified positions/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+           "config": {"workload": "PyramidSD, two fuzzy stages: B=16, V=128256 bf16; draft->qualifier l_D=12, "
+                                  "tau_Q=0.4; qualifier->target l_Q=25, tau_T=0.5; T=1; Jensen-Shannon divergence",
+                      "B": B, "V": stages[0].V, "l_D": stages[0].K, "l_Q": stages[1].K,
+                      "logit_bytes_per_step": step_bytes, "input_copies_rotated": copies,
+                      "stage_ms": stage_ms},
+           "roofline": {"bound": "hbm", "kernel": "pyramid_verify (generic_unit_kernel + finalize_kernel), both stages",
+                        "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                        "traffic": None, "algorithmic_bytes_per_launch": step_bytes,
+                        "avg_launch_ms": sum(stage_ms)},
+           "secondary": {"mean_accepted_per_stage": [float(torch.stack(ks[j::2]).float().mean()) for j in range(2)]}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "backup", "mirror"],
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "backup", "mirror", "pyramid"],
                     help="c4 (default): the headline workload; the others print their own line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
@@ -267,6 +333,9 @@ def main():
 
     if args.config == "mirror":
         bench_mirror(args)
+        return
+    if args.config == "pyramid":
+        bench_pyramid(args)
         return
     if args.config != "c4":
         bench_other(args.config, args)
