@@ -72,6 +72,22 @@ def cpu_baseline(w, seconds_target=15.0):
                       f"build + lookup) in {el:.1f} s, fp64, std::thread over requests/rows"}
 
 
+def timed_oracle(run, unit_count, unit, sample, seconds_target=10.0, max_reps=200):
+    """Repeats run() (one oracle pass over a bounded sample) for about seconds_target."""
+    import oracle
+    nthreads = oracle.threads_used(0)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        run(nthreads, reps)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds_target or reps >= max_reps:
+            break
+    return {"value": unit_count * reps / el, "unit": unit, "cores": nthreads, "kind": "oracle",
+            "sample": f"{reps} x {sample} in {el:.1f} s, fp64, std::thread over requests/rows"}
+
+
 def bench_other(name, args):
     """One JSON line for a configuration other than the headline one: the verification call
     (plus, for the branch trees, the reuse lookup) timed on rotated inputs resident in HBM."""
@@ -152,6 +168,17 @@ def bench_other(name, args):
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                         "algorithmic_bytes_per_launch": step_bytes, "avg_launch_ms": ms,
                         "p10_ms": vt[len(vt) // 10], "p90_ms": vt[(len(vt) * 9) // 10]}}
+    if not args.no_cpu_baseline:
+        import oracle
+        nb = min(B, 16)
+        tok_np = tokens[:nb].cpu().numpy()
+
+        def run(nthreads, rep):
+            oracle.verify(None if uniform else w.draft[:nb], w.target[:nb], w.dtype, K, w.params()[:nb], F=w.F,
+                          C=float(np.float32(w.C)), tokens=None if uniform else tok_np, seed=w.seed, round_=rep,
+                          nthreads=nthreads, uniform_draft=uniform)
+        res["cpu_baseline"] = timed_oracle(run, nb * K, "verified positions/s",
+                                           f"{nb} requests of the workload (K={K}, V={V})")
     print(json.dumps(res), flush=True)
 
 
@@ -229,6 +256,14 @@ def bench_mirror(args):
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                         "algorithmic_bytes_per_launch": step_bytes, "avg_launch_ms": sp_ms,
                         "graph_replays_ms": reps}}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        def run(nthreads, rep):
+            oracle.signposts(w.logits, synth.BF16, kappa, nthreads=nthreads)
+            oracle.tree_lookup(w.tokens, w.parents, w.path, w.k, w.tstar)
+        res["cpu_baseline"] = timed_oracle(run, B, "requests/s",
+                                           f"the whole step (signposts of {B} rows of V={V}, tree lookups)")
     print(json.dumps(res), flush=True)
 
 
@@ -295,6 +330,18 @@ def bench_pyramid(args):
                         "traffic": None, "algorithmic_bytes_per_launch": step_bytes,
                         "avg_launch_ms": sum(stage_ms)},
            "secondary": {"mean_accepted_per_stage": [float(torch.stack(ks[j::2]).float().mean()) for j in range(2)]}}
+    if not args.no_cpu_baseline:
+        import oracle
+        nb = 4
+        prm_np = np.zeros(nb, dtype=oracle.PARAMS_DTYPE)
+        prm_np["t"], prm_np["k"], prm_np["p"] = 1.0, 0, 1.0
+
+        def run(nthreads, rep):
+            for s in stages:
+                oracle.verify(s.draft[:nb], s.verifier[:nb], synth.BF16, s.K, prm_np, tokens=None, seed=s.seed,
+                              round_=rep, nthreads=nthreads, tau=s.tau[:nb].astype(np.float64))
+        res["cpu_baseline"] = timed_oracle(run, nb * sum(s.K for s in stages), "verified positions/s",
+                                           f"both stages for {nb} of the {B} requests")
     print(json.dumps(res), flush=True)
 
 
