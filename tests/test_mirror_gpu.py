@@ -176,3 +176,11 @@ def test_tree_worked_example_and_comb():
     k = rng.integers(0, gamma + 1, B).astype(np.int32)
     t = rng.integers(0, 3, B).astype(np.int32)
     check_tree(br.reshape(B, -1), combp, br[:, 0], k, t, label="comb")
+
+
+def test_signposts_size_limits():
+    rng = np.random.default_rng(17)
+    z = synth.zipf_rows(rng, 3, 1 << 19)                  # the largest vocabulary (256 lists per row)
+    check_signposts(synth.f32_to_bf16_bits(z), synth.BF16, capi.SPEC_MAX_KAPPA, label="V=2^19")
+    w = synth.mirror(B=16)
+    check_signposts(w.logits, synth.BF16, capi.SPEC_MAX_KAPPA, label="kappa=16 early-exit rows")
