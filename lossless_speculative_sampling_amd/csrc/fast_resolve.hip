@@ -594,7 +594,7 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
 // value so that no pointer to the kernel's own arguments escapes (which would move them to
 // scratch memory for the whole kernel).
 __device__ __noinline__ void fallback_unit(VerifyArgs a, int b, int j, ResSmem& sm) {
-    unit_verify(a, b, j, &sm.urec, sm.u.generic, sm.gst[0], sm.gst[1]);
+    unit_verify<1>(a, b, j, &sm.urec, sm.u.generic, sm.gst[0], sm.gst[1]);  // (no loads ahead: registers)
 }
 
 // Request arrival in the XCD's L2; true for the last of `expected` workgroups (which resets
@@ -691,7 +691,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     // outcome-cache rows the count kernel's candidate lists could not settle
     if (cgen) {
         CacheArgs c{a.draft, a.dtype, a.B, a.K, a.V, a.tokens, f.budget, f.fan, f.out_cache};
-        cache_row(c, b, w, sm.u.cache.rs, sm.gst[0], sm.u.cache.cs);
+        cache_row<1>(c, b, w, sm.u.cache.rs, sm.gst[0], sm.u.cache.cs);
         __syncthreads();
     }
     const int mode = (int)req[0];

@@ -58,6 +58,57 @@ struct RowRef {
     int V;
 };
 
+// ------------------------------------------------------------------------------------------
+// Row traversals with A (default kRowAhead) independent loads in flight per thread (a loop that loads one
+// logit per iteration and uses it at once is bound by that load's latency).  Every thread
+// still visits its columns in increasing order, so its accumulations round as in a plain loop.
+// ------------------------------------------------------------------------------------------
+constexpr int kRowAhead = 8;
+
+// columns threadIdx.x, threadIdx.x + blockDim.x, ... of one row (f(i, z)) or of two rows
+// read pairwise by column (f(i, z, z2))
+template <int A = kRowAhead, typename F>
+__device__ __forceinline__ void row_strided(const RowRef& r, F&& f) {
+    const int step = blockDim.x;
+    int i = threadIdx.x;
+    for (; i + (A - 1) * step < r.V; i += A * step) {
+        float z[A];
+#pragma unroll
+        for (int u = 0; u < A; ++u) z[u] = load_logit(r.row, r.dtype, i + u * step);
+#pragma unroll
+        for (int u = 0; u < A; ++u) f(i + u * step, z[u]);
+    }
+    for (; i < r.V; i += step) f(i, load_logit(r.row, r.dtype, i));
+}
+template <int A = kRowAhead, typename F>
+__device__ __forceinline__ void row_strided2(const RowRef& r, const RowRef& r2, F&& f) {
+    const int step = blockDim.x;
+    int i = threadIdx.x;
+    for (; i + (A - 1) * step < r.V; i += A * step) {
+        float z[A], z2[A];
+#pragma unroll
+        for (int u = 0; u < A; ++u) {
+            z[u] = load_logit(r.row, r.dtype, i + u * step);
+            z2[u] = load_logit(r2.row, r2.dtype, i + u * step);
+        }
+#pragma unroll
+        for (int u = 0; u < A; ++u) f(i + u * step, z[u], z2[u]);
+    }
+    for (; i < r.V; i += step) f(i, load_logit(r.row, r.dtype, i), load_logit(r2.row, r2.dtype, i));
+}
+
+// Columns [i0, i0 + A) clipped to hi, loaded ahead (z, z2; 0 past hi).
+template <bool TWO, int A>
+__device__ __forceinline__ void load_ahead(const RowRef& r, const RowRef& r2, int i0, int hi, float (&z)[A],
+                                           float (&z2)[A]) {
+#pragma unroll
+    for (int u = 0; u < A; ++u) {
+        const bool in = i0 + u < hi;
+        z[u] = in ? load_logit(r.row, r.dtype, i0 + u) : 0.0f;
+        z2[u] = (TWO && in) ? load_logit(r2.row, r2.dtype, i0 + u) : 0.0f;
+    }
+}
+
 __device__ __forceinline__ bool rs_kept(const RowStats& s, uint32_t key, int i) {
     return key > s.kk || (key == s.kk && i <= s.idk);
 }
@@ -93,7 +144,7 @@ __device__ __forceinline__ double rs_prob_dw(const RowStats& s, float z, int i) 
 // mass e_i, finds the key tau at which the running weight first reaches `need`.
 // Outputs: tau, the weight strictly above tau, the number of filtered elements at tau and the
 // weight still needed inside tau.
-template <bool MASS, typename Filter>
+template <bool MASS, int A = kRowAhead, typename Filter>
 __device__ void radix_select(const RowRef& r, const RowStats& st, Filter filt, double need, RowShared& sh,
                              uint32_t* tau_out, double* above_out, int* cnt_out, double* rem_out) {
     uint32_t prefix = 0, pmask = 0;
@@ -106,14 +157,13 @@ __device__ void radix_select(const RowRef& r, const RowStats& st, Filter filt, d
             sh.hmass[d] = 0.0;
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
-            const float z = load_logit(r.row, r.dtype, i);
+        row_strided<A>(r, [&](int i, float z) {
             const uint32_t key = order_key(z);
-            if ((key & pmask) != prefix || !filt(key, i, z)) continue;
+            if ((key & pmask) != prefix || !filt(key, i, z)) return;
             const int d = (key >> shift) & 255;
             atomicAdd(&sh.hcnt[d], 1u);
             if (MASS) atomicAdd(&sh.hmass[d], rs_mass(st, z));
-        }
+        });
         __syncthreads();
         if (threadIdx.x == 0) {
             double acc = 0.0;
@@ -154,15 +204,20 @@ __device__ void radix_select(const RowRef& r, const RowStats& st, Filter filt, d
 
 // The n-th (1-based) smallest id among elements with key == tau accepted by `filt`.
 // Threads own contiguous id segments, so a workgroup scan of their counts locates it.
-template <typename Filter>
+template <int A = kRowAhead, typename Filter>
 __device__ int nth_id_at_key(const RowRef& r, uint32_t tau, int n, Filter filt, RowShared& sh) {
     const int seg = (r.V + blockDim.x - 1) / blockDim.x;
     const int lo = threadIdx.x * seg;
     const int hi = min(r.V, lo + seg);
     int c = 0;
-    for (int i = lo; i < hi; ++i) {
-        const float z = load_logit(r.row, r.dtype, i);
-        if (order_key(z) == tau && filt(order_key(z), i, z)) ++c;
+    for (int i0 = lo; i0 < hi; i0 += A) {
+        float z[A], z2[A];
+        load_ahead<false, A>(r, r, i0, hi, z, z2);
+#pragma unroll
+        for (int u = 0; u < A; ++u) {
+            const uint32_t k = order_key(z[u]);
+            if (i0 + u < hi && k == tau && filt(k, i0 + u, z[u])) ++c;
+        }
     }
     int total;
     const int before = block_exclusive_scan<int>(c, sh.redi, &total);
@@ -170,11 +225,16 @@ __device__ int nth_id_at_key(const RowRef& r, uint32_t tau, int n, Filter filt, 
     __syncthreads();
     if (before < n && before + c >= n) {
         int cc = before;
-        for (int i = lo; i < hi; ++i) {
-            const float z = load_logit(r.row, r.dtype, i);
-            if (order_key(z) == tau && filt(order_key(z), i, z) && ++cc == n) {
-                sh.found = i;
-                break;
+        bool done = false;
+        for (int i0 = lo; i0 < hi && !done; i0 += A) {
+            float z[A], z2[A];
+            load_ahead<false, A>(r, r, i0, hi, z, z2);
+            for (int u = 0; u < A && i0 + u < hi && !done; ++u) {
+                const uint32_t k = order_key(z[u]);
+                if (k == tau && filt(k, i0 + u, z[u]) && ++cc == n) {
+                    sh.found = i0 + u;
+                    done = true;
+                }
             }
         }
     }
@@ -184,18 +244,41 @@ __device__ int nth_id_at_key(const RowRef& r, uint32_t tau, int n, Filter filt, 
     return res;
 }
 
-// Inverse CDF in token-id order over non-negative weights w(i, z): the first i with w_i > 0
-// whose running sum exceeds x * total (the last i with w_i > 0 if rounding never crosses).
-// Returns -1 when every weight is 0.  *total_out gets the total.
-template <typename Weight>
-__device__ int inverse_cdf(const RowRef& r, double x, Weight wfn, RowShared& sh, double* total_out) {
+// Inverse CDF in token-id order over non-negative weights w(i, z) (or w(i, z, z2) over two rows
+// read pairwise): the first i with w_i > 0 whose running sum exceeds x * total (the last i with
+// w_i > 0 if rounding never crosses).  Returns -1 when every weight is 0.  *total_out gets the
+// total.  Threads own contiguous column segments; the owner of the crossing walks its segment
+// with its weights computed A at a time.
+template <bool TWO, int A, typename Weight>
+__device__ __forceinline__ void weights_ahead(const RowRef& r, const RowRef& r2, int i0, int hi, Weight& wfn,
+                                              double (&w)[A]) {
+    float z[A], z2[A];
+    load_ahead<TWO, A>(r, r2, i0, hi, z, z2);
+#pragma unroll
+    for (int u = 0; u < A; ++u) {
+        if (i0 + u >= hi) {
+            w[u] = 0.0;
+        } else if constexpr (TWO) {
+            w[u] = wfn(i0 + u, z[u], z2[u]);
+        } else {
+            w[u] = wfn(i0 + u, z[u]);
+        }
+    }
+}
+
+template <bool TWO, int A, typename Weight>
+__device__ int inverse_cdf_rows(const RowRef& r, const RowRef& r2, double x, Weight wfn, RowShared& sh,
+                                double* total_out) {
     const int seg = (r.V + blockDim.x - 1) / blockDim.x;
     const int lo = threadIdx.x * seg;
     const int hi = min(r.V, lo + seg);
     double own = 0.0;
-    for (int i = lo; i < hi; ++i) {
-        const double w = wfn(i, load_logit(r.row, r.dtype, i));
-        if (w > 0.0) own += w;
+    for (int i0 = lo; i0 < hi; i0 += A) {
+        double w[A];
+        weights_ahead<TWO, A>(r, r2, i0, hi, wfn, w);
+#pragma unroll
+        for (int u = 0; u < A; ++u)
+            if (w[u] > 0.0) own += w[u];
     }
     double total;
     const double before = block_exclusive_scan<double>(own, sh.redd, &total);
@@ -207,12 +290,16 @@ __device__ int inverse_cdf(const RowRef& r, double x, Weight wfn, RowShared& sh,
     if ((int)threadIdx.x == owner) {
         double cum = before;
         int pick = -1;
-        for (int i = lo; i < hi; ++i) {
-            const double w = wfn(i, load_logit(r.row, r.dtype, i));
-            if (!(w > 0.0)) continue;
-            cum += w;
-            pick = i;
-            if (cum > target) break;
+        bool done = false;
+        for (int i0 = lo; i0 < hi && !done; i0 += A) {
+            double w[A];
+            weights_ahead<TWO, A>(r, r2, i0, hi, wfn, w);
+            for (int u = 0; u < A && !done; ++u) {
+                if (!(w[u] > 0.0)) continue;
+                cum += w[u];
+                pick = i0 + u;
+                if (cum > target) done = true;
+            }
         }
         sh.found = pick;
     }
@@ -223,21 +310,31 @@ __device__ int inverse_cdf(const RowRef& r, double x, Weight wfn, RowShared& sh,
     return res;
 }
 
+template <int A = kRowAhead, typename Weight>
+__device__ int inverse_cdf(const RowRef& r, double x, Weight wfn, RowShared& sh, double* total_out) {
+    return inverse_cdf_rows<false, A>(r, r, x, wfn, sh, total_out);
+}
+template <int A = kRowAhead, typename Weight>
+__device__ int inverse_cdf2(const RowRef& r, const RowRef& r2, double x, Weight wfn, RowShared& sh,
+                            double* total_out) {
+    return inverse_cdf_rows<true, A>(r, r2, x, wfn, sh, total_out);
+}
+
 // Processes row r with (T, top_k, top_p) into st (LDS).  When `want_set`, also forms the
 // downweighted set of the first F tokens with mass and its normaliser Z for factor C.
+template <int A = kRowAhead>
 __device__ inline void process_row(const RowRef& r, float T, int top_k, float top_p, int F, double C, bool want_set,
                             RowStats& st, RowShared& sh) {
     // pass 1: bad logits and the (largest key, lowest id) pair
     unsigned long long best = 0;
     int bad = 0, finite = 0;
-    for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
-        const float z = load_logit(r.row, r.dtype, i);
+    row_strided<A>(r, [&](int i, float z) {
         const uint32_t u = __float_as_uint(z);
         if ((u & 0x7FFFFFFFu) > 0x7F800000u || u == 0x7F800000u) bad = 1;
         if ((u & 0x7F800000u) != 0x7F800000u) finite = 1;
         const unsigned long long pk = ((unsigned long long)order_key(z) << 32) | (unsigned long long)(~(uint32_t)i);
         best = pk > best ? pk : best;
-    }
+    });
     bad = block_max<int>(bad, sh.redi);
     finite = block_max<int>(finite, sh.redi);
     best = block_max<unsigned long long>(best, sh.redu);
@@ -268,10 +365,10 @@ __device__ inline void process_row(const RowRef& r, float T, int top_k, float to
         uint32_t tau;
         double above, rem;
         int cnt;
-        radix_select<false>(r, st, [](uint32_t, int, float) { return true; }, (double)top_k, sh, &tau, &above, &cnt,
+        radix_select<false, A>(r, st, [](uint32_t, int, float) { return true; }, (double)top_k, sh, &tau, &above, &cnt,
                             &rem);
         const int n = (int)rem;
-        const int idk = (n >= cnt) ? r.V - 1 : nth_id_at_key(r, tau, n, [](uint32_t, int, float) { return true; }, sh);
+        const int idk = (n >= cnt) ? r.V - 1 : nth_id_at_key<A>(r, tau, n, [](uint32_t, int, float) { return true; }, sh);
         if (threadIdx.x == 0) {
             st.kk = tau;
             st.idk = idk;
@@ -281,10 +378,9 @@ __device__ inline void process_row(const RowRef& r, float T, int top_k, float to
 
     // softmax normaliser over the kept tokens
     double s = 0.0;
-    for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
-        const float z = load_logit(r.row, r.dtype, i);
+    row_strided<A>(r, [&](int i, float z) {
         if (rs_kept(st, order_key(z), i)) s += rs_mass(st, z);
-    }
+    });
     const double S_kept = block_sum<double>(s, sh.redd);
 
     // nucleus: the smallest prefix of the order whose mass reaches top_p * S
@@ -295,14 +391,14 @@ __device__ inline void process_row(const RowRef& r, float T, int top_k, float to
         double above, rem;
         int cnt;
         auto kept = [&st](uint32_t key, int i, float) { return rs_kept(st, key, i); };
-        radix_select<true>(r, st, kept, need, sh, &tau, &above, &cnt, &rem);
+        radix_select<true, A>(r, st, kept, need, sh, &tau, &above, &cnt, &rem);
         const double e_tau = exp(((double)key_to_float(tau) - (double)st.m) / st.T);
         int n = cnt;
         if (e_tau > 0.0) {
             const double q = ceil((need - above) / e_tau);
             n = q < 1.0 ? 1 : (q > (double)cnt ? cnt : (int)q);
         }
-        const int idp = (n >= cnt) ? r.V - 1 : nth_id_at_key(r, tau, n, kept, sh);
+        const int idp = (n >= cnt) ? r.V - 1 : nth_id_at_key<A>(r, tau, n, kept, sh);
         S_nuc = above + (double)n * e_tau;
         if (threadIdx.x == 0) {
             st.kp = tau;
@@ -316,10 +412,9 @@ __device__ inline void process_row(const RowRef& r, float T, int top_k, float to
     if (!want_set || F <= 0) return;
     // downweighted set: the first F tokens of the order that carry mass
     int c = 0;
-    for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
-        const float z = load_logit(r.row, r.dtype, i);
+    row_strided<A>(r, [&](int i, float z) {
         if (rs_in(st, order_key(z), i) && rs_mass(st, z) > 0.0) ++c;
-    }
+    });
     const int n_pos = block_sum<int>(c, sh.redi);
     const int Fp = F < n_pos ? F : n_pos;
     if (Fp <= 0) return;
@@ -327,9 +422,9 @@ __device__ inline void process_row(const RowRef& r, float T, int top_k, float to
     uint32_t tau;
     double above, rem;
     int cnt;
-    radix_select<false>(r, st, pos, (double)Fp, sh, &tau, &above, &cnt, &rem);
+    radix_select<false, A>(r, st, pos, (double)Fp, sh, &tau, &above, &cnt, &rem);
     const int n = (int)rem;
-    const int idF = (n >= cnt) ? r.V - 1 : nth_id_at_key(r, tau, n, pos, sh);
+    const int idF = (n >= cnt) ? r.V - 1 : nth_id_at_key<A>(r, tau, n, pos, sh);
     if (threadIdx.x == 0) {
         st.kF = tau;
         st.idF = idF;
@@ -338,8 +433,7 @@ __device__ inline void process_row(const RowRef& r, float T, int top_k, float to
     }
     __syncthreads();
     double ps = 0.0;
-    for (int i = threadIdx.x; i < r.V; i += blockDim.x) {
-        const float z = load_logit(r.row, r.dtype, i);
+    row_strided<A>(r, [&](int i, float z) {
         const uint32_t key = order_key(z);
         const double e = rs_mass(st, z);
         if (rs_in_set(st, key, i, e)) {
@@ -350,7 +444,7 @@ __device__ inline void process_row(const RowRef& r, float T, int top_k, float to
             }
             ps += e / st.S;
         }
-    }
+    });
     const double P_S = block_sum<double>(ps, sh.redd);
     if (threadIdx.x == 0) {
         const int nl = sh.list_n < SPEC_MAX_F ? sh.list_n : SPEC_MAX_F;
@@ -383,6 +477,7 @@ __device__ inline void process_row(const RowRef& r, float T, int top_k, float to
 
 // The verification of one (request b, position j) unit by the whole workgroup; the record is
 // written by thread 0.  Shared by the general kernel and the fast kernel's fallback.
+template <int A = kRowAhead>
 __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* rec, RowShared& sh, RowStats& stq,
                             RowStats& stp) {
     const spec_params prm = a.params[b];
@@ -394,7 +489,7 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
     const size_t tstride = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
     const char* trow = static_cast<const char*>(a.target) + ((size_t)b * (a.K + 1) + j) * tstride;
     RowRef rq{trow, a.dtype, a.V};
-    process_row(rq, prm.temperature, prm.top_k, prm.top_p, 0, 1.0, false, stq, sh);
+    process_row<A>(rq, prm.temperature, prm.top_k, prm.top_p, 0, 1.0, false, stq, sh);
     // with a uniform draft (the random-token backup) p_j(x) = 1/V and no draft row is read
     const bool uni = (a.flags & SPEC_UNIFORM_DRAFT) != 0;
     const double p_uni = 1.0 / (double)a.V;
@@ -402,7 +497,7 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
     if (j < a.K && !uni) {
         rp.row = static_cast<const char*>(a.draft) + ((size_t)b * a.draft_rows + j) * tstride;
         const bool dw = a.F > 0 && a.C < 1.0f;
-        process_row(rp, prm.temperature, prm.top_k, prm.top_p, a.F, (double)a.C, dw, stp, sh);
+        process_row<A>(rp, prm.temperature, prm.top_k, prm.top_p, a.F, (double)a.C, dw, stp, sh);
     }
     if (stq.bad || (j < a.K && !uni && stp.bad)) {
         if (threadIdx.x == 0) *rec = UnitRec{0, -1, 0.0f, kStBadLogit, -1};
@@ -418,7 +513,7 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
         } else {
             const double v = uniform_at(a.seed, a.round, b, j, 1);
             double tot;
-            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
+            t = inverse_cdf<A>(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
         }
         if (threadIdx.x == 0) *rec = UnitRec{1, t, 0.0f, status, -1};
         return;
@@ -434,7 +529,7 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
         } else {
             const double x = uniform_at(a.seed, a.round, b, j, 2);
             double tot;
-            s = inverse_cdf(rp, x, [&](int i, float z) { return rs_prob_dw(stp, z, i); }, sh, &tot);
+            s = inverse_cdf<A>(rp, x, [&](int i, float z) { return rs_prob_dw(stp, z, i); }, sh, &tot);
         }
         if (threadIdx.x == 0) a.tokens[(size_t)b * a.K + j] = s;
     } else {
@@ -451,12 +546,19 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
     bool fuzzy_pass = false;
     if (a.tau) {
         double d = 0.0;
-        for (int i = threadIdx.x; i < a.V; i += blockDim.x) {
-            const double q = rs_prob(stq, load_logit(rq.row, a.dtype, i), i);
-            const double p = uni ? p_uni : rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i);
+        auto term = [&](double q, double p) {
             const double m = 0.5 * (p + q);
             if (p > 0.0) d += 0.5 * p * log2(p / m);
             if (q > 0.0) d += 0.5 * q * log2(q / m);
+        };
+        if constexpr (A == 1) {
+            for (int i = threadIdx.x; i < a.V; i += blockDim.x)
+                term(rs_prob(stq, load_logit(rq.row, a.dtype, i), i),
+                     uni ? p_uni : rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i));
+        } else if (uni) {
+            row_strided<A>(rq, [&](int i, float zq) { term(rs_prob(stq, zq, i), p_uni); });
+        } else {
+            row_strided2<A>(rq, rp, [&](int i, float zq, float zp) { term(rs_prob(stq, zq, i), rs_prob_dw(stp, zp, i)); });
         }
         const double D = block_sum<double>(d, sh.redd);
         if (threadIdx.x == 0 && a.out_div) a.out_div[(size_t)b * a.K + j] = (float)D;
@@ -485,20 +587,32 @@ __device__ inline void unit_verify(const VerifyArgs& a, int b, int j, UnitRec* r
     } else {
         const double v = uniform_at(a.seed, a.round, b, j, 1);
         // residual (q - p')+ at this position; rows are read pairwise by token id
-        auto resid = [&](int i, float zq) {
-            const double q = rs_prob(stq, zq, i);
-            const double p = uni ? p_uni : rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i);
-            return q > p ? q - p : 0.0;
-        };
-        t = inverse_cdf(rq, v, resid, sh, &W);
+        if constexpr (A == 1) {  // one instance for both draft kinds (fewer registers)
+            t = inverse_cdf<A>(rq, v, [&](int i, float zq) {
+                const double q = rs_prob(stq, zq, i);
+                const double p = uni ? p_uni : rs_prob_dw(stp, load_logit(rp.row, a.dtype, i), i);
+                return q > p ? q - p : 0.0;
+            }, sh, &W);
+        } else if (uni) {
+            t = inverse_cdf<A>(rq, v, [&](int i, float zq) {
+                const double q = rs_prob(stq, zq, i);
+                return q > p_uni ? q - p_uni : 0.0;
+            }, sh, &W);
+        } else {
+            t = inverse_cdf2<A>(rq, rp, v, [&](int i, float zq, float zp) {
+                const double q = rs_prob(stq, zq, i);
+                const double p = rs_prob_dw(stp, zp, i);
+                return q > p ? q - p : 0.0;
+            }, sh, &W);
+        }
         if (a.flags & SPEC_ASSISTED) {
             // assisted correction (PyramidSD notes, key design 2): drawn from q_j itself
             double tot;
-            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
+            t = inverse_cdf<A>(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
         } else if (t < 0) {  // no residual mass: fall back to q itself
             status |= kStEmptyResidual;
             double tot;
-            t = inverse_cdf(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
+            t = inverse_cdf<A>(rq, v, [&](int i, float z) { return rs_prob(stq, z, i); }, sh, &tot);
         }
     }
     if (threadIdx.x == 0) *rec = UnitRec{0, t, (float)W, status, s};
@@ -515,6 +629,7 @@ struct CacheShared {
     int npicked;
 };
 
+template <int A = kRowAhead>
 __device__ inline void cache_row(const CacheArgs& a, int b, int k, RowShared& sh, RowStats& st, CacheShared& cs) {
     const int Fk = a.fanout.f[k];
     const int off = a.fanout.off[k];
@@ -528,9 +643,9 @@ __device__ inline void cache_row(const CacheArgs& a, int b, int k, RowShared& sh
     double above, rem;
     int cnt;
     auto all = [](uint32_t, int, float) { return true; };
-    radix_select<false>(r, st, all, (double)want, sh, &tau, &above, &cnt, &rem);
+    radix_select<false, A>(r, st, all, (double)want, sh, &tau, &above, &cnt, &rem);
     const int n = (int)rem;
-    const int idc = (n >= cnt) ? a.V - 1 : nth_id_at_key(r, tau, n, all, sh);
+    const int idc = (n >= cnt) ? a.V - 1 : nth_id_at_key<A>(r, tau, n, all, sh);
     if (threadIdx.x == 0) cs.npicked = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < a.V; i += blockDim.x) {
