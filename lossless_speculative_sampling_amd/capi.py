@@ -51,7 +51,7 @@ class SpecError(RuntimeError):
 class Lib:
     def __init__(self, path: str = LIB_PATH):
         if not os.path.exists(path):
-            raise RuntimeError(f"HIP library {path} is not built (run __graft_entry__.build())")
+            raise RuntimeError(f"HIP library {path} is not built (python -m lossless_speculative_sampling_amd.build)")
         self.cdll = L = ctypes.CDLL(path)
         L.spec_workspace_bytes.argtypes = [_I, _I, _I]
         L.spec_workspace_bytes.restype = ctypes.c_size_t

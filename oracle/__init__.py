@@ -1,7 +1,7 @@
 """CPU oracle of the verification path - TEST INFRASTRUCTURE ONLY.
 
 ctypes binding over ``oracle/liboracle.so`` (built from ``oracle/oracle.cpp`` by
-``oracle.build_oracle()`` or ``__graft_entry__.build()``).  Only tests, the smoke check and the
+``oracle.build_oracle()``, or by the repository's build entry point).  Only tests, the smoke check and the
 bench's CPU-baseline leg use it; the product package never imports it.
 """
 from __future__ import annotations
