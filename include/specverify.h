@@ -237,7 +237,9 @@ int saguaro_cache_lookup(int mode, const int32_t* cache, const int32_t* fanout_o
 
 /* mirror_signpost_workspace_bytes - device workspace mirror_signposts needs for (B, V, kappa);
  * 0 for sizes it rejects.  Same contract as the verification workspace: zero-filled before its
- * first use (hipMemset), left zero-filled by every completed call, one call at a time. */
+ * first use; every completed call leaves its arrival counters at zero again (the rest is
+ * scratch each call writes before reading), so it is reused without clearing; one call at a
+ * time per workspace. */
 size_t mirror_signpost_workspace_bytes(int B, int V, int kappa);
 
 /* mirror_signposts - early-exit signposts ([MSD] sections 3.1 and 3.3: the LM head at the
