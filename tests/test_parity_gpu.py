@@ -444,3 +444,30 @@ def test_backup_plan():
                 assert int(sw.cpu()[0]) == o_sw, (B, p_hit, b_star)
                 assert (use.cpu().numpy() == o_use).all(), (B, p_hit, b_star)
     say("[parity] backup plan ok")
+
+
+# ------------------------------------------------------------------------------------------
+# long drafts (more than 8 positions: the per-unit request rendezvous instead of the packed
+# 64-bit one) and large batches on the bf16 path
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("K", [8, 12, 25])
+def test_fast_long_drafts(K):
+    rng = np.random.default_rng(100 + K)
+    B, V = 12, 16392
+    T = rng.choice([0.0, 0.7, 1.0], B)
+    tk = rng.choice([0, 20, 500], B)
+    tp = rng.choice([0.8, 0.95, 1.0], B)
+    w = _zipf_work(rng, B, K, V, T, tk, tp, F=3, C=0.5, noise=0.3)
+    o, _ = check_verify(w, tokens=_oracle_tokens(w), label=f"fast-long K={K}")
+    assert o.k.max() > 7 or K == 8
+    check_verify(w, tokens=rng.integers(0, V, (B, K)), label=f"fast-long-random K={K}")
+
+
+def test_fast_large_batch():
+    rng = np.random.default_rng(300)
+    B, K, V = 600, 3, 2048
+    T = rng.choice([0.0, 0.5, 1.0], B)
+    tk = rng.choice([0, 1, 8, 100], B)
+    tp = rng.choice([0.5, 0.9, 1.0], B)
+    w = _zipf_work(rng, B, K, V, T, tk, tp, F=2, C=0.2)
+    check_verify(w, tokens=_oracle_tokens(w), label="fast-large-batch")
