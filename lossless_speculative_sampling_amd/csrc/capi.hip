@@ -119,6 +119,10 @@ int pyramid_verify(const void* draft_logits, int draft_rows, const void* verifie
     VerifyArgs a{draft_logits, verifier_logits, draft_rows, dtype, B, K, V, params, F, C, draft_tokens, seed,
                  round, flags, out_k, out_tstar, out_resid_mass, out_status, static_cast<UnitRec*>(workspace),
                  tau, out_div};
+    if (fast::fast_fuzzy_applies(a)) {
+        const size_t gen = align_up((size_t)B * (K + 1) * sizeof(UnitRec), 256);
+        return fast::fast_verify(a, static_cast<char*>(workspace) + gen, workspace_bytes - gen, stream);
+    }
     hipLaunchKernelGGL(generic_unit_kernel, dim3((unsigned)(B * (K + 1))), dim3(general_threads(V)), 0, stream, a);
     if (launch_status() != SPEC_OK) return SPEC_EHIP;
     hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, a);

@@ -142,14 +142,15 @@ struct UnitFast {       // written by the last slice of the unit in the count ke
 };
 
 struct ReqFast {        // written by the last unit of the request in the count kernel
-    int32_t mode;        // 0: outputs written, 1: residual of unit k, 2: general path
+    int32_t mode;        // 0: outputs written, 1: residual of unit k, 2: general path, 3: fuzzy
+                         // acceptance pending (the divergence kernel decides and sets 1)
     int32_t k;
     uint32_t status;
     int32_t pad;
 };
 
 struct Layout {
-    size_t unit_ctr, req_ctr, res_ctr, parts, units, reqs, idcut, chunks, gen, cache_gen, total;
+    size_t unit_ctr, req_ctr, res_ctr, parts, units, reqs, idcut, chunks, gen, cache_gen, div, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -167,6 +168,7 @@ __host__ __device__ inline Layout layout(int B, int units, int nS) {
     L.chunks = o;   o += align256((size_t)B * nS * kChunks * sizeof(double));
     L.gen = o;      o += align256((size_t)units * sizeof(UnitRec));  // general-path unit results
     L.cache_gen = o; o += align256((size_t)units * sizeof(int32_t)); // cache rows for the general selection
+    L.div = o;      o += align256((size_t)units * (2 * nS + 1) * sizeof(double));  // fuzzy: partial and total divergences
     L.total = o;
     return L;
 }
@@ -304,6 +306,7 @@ __device__ __forceinline__ uint32_t hist_offsets2(uint32_t w) {
 
 void launch_count(const FastArgs& f, int grid, hipStream_t stream);
 void launch_resolve(const FastArgs& f, int grid, hipStream_t stream);
+void launch_diverge(const FastArgs& f, int grid, hipStream_t stream);
 
 }  // namespace fast
 }  // namespace sv

@@ -579,6 +579,10 @@ __device__ __forceinline__ void decide_packed(const FastArgs& f, int b, uint64_t
         status = kStBadLogit;
     } else if (any & kStBadToken) {
         status = deg | kStBadToken;
+    } else if (a.tau) {
+        // fuzzy acceptance: the divergence kernel decides (greedy rows: the general path)
+        mode = greedy ? 2 : 3;
+        status = 0;
     } else {
         status = deg | outside;
         kk = k;
@@ -632,6 +636,10 @@ __device__ __forceinline__ void decide_request(const FastArgs& f, int b) {
         status = kStBadLogit;
     } else if (any & kStBadToken) {
         status = deg | kStBadToken;
+    } else if (a.tau) {
+        // fuzzy acceptance: the divergence kernel decides (greedy rows: the general path)
+        mode = ldnt(&U[k].rq.greedy) ? 2 : 3;
+        status = 0;
     } else {
         status = deg | outside;
         kk = k;

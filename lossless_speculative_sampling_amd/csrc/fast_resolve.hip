@@ -772,6 +772,201 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     finalize_residual(f, sm, b, k, status, sm.u_res);
 }
 
+// ------------------------------------------------------------------------------------------
+// Fuzzy acceptance (PyramidSD notes, key design 1): a drafted token passes when the Jensen-
+// Shannon divergence (bits) of the processed verifier row q_j and drafter row p'_j is at most
+// the request's threshold; elsewhere the lossless test the count kernel already ran decides.
+// For every request the count kernel left pending, the two workgroups of each slice of each
+// drafted position sum the divergence over their half of the slice with the same exact
+// per-element values as the residual; the last of a position's workgroups totals it, and the
+// last position of the request finds k and hands the request to the resolve kernel.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ double div_term(double q, double p) {
+    const double m = 0.5 * (p + q);
+    double d = 0.0;
+    if (p > 0.0) d += 0.5 * p * log2(p / m);
+    if (q > 0.0) d += 0.5 * q * log2(q / m);
+    return d;
+}
+
+// This thread's share of the divergence over the workgroup's half of the slice.
+__device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& sm, int half, int c0, bool two,
+                                                  const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads]) {
+    const double pu = 1.0 / (double)f.a.V;
+    const VerifyArgs& a = f.a;
+    const char* tq = reinterpret_cast<const char*>(&sm.u.tab[0][0]);
+    const char* tp = reinterpret_cast<const char*>(&sm.u.tab[1][0]);
+    const Ties tiq = load_ties(sm, 0);
+    const Ties tip = load_ties(sm, 1);
+    double tot = 0.0;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        if (q / (kLoads / 2) != half) continue;
+        const int cq = col_of(c0, q, 0);
+        if (cq >= a.V) continue;
+        double s = 0.0;
+        bool mark = false;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t oq = tab_offsets2(vq[q][d]);
+            double q0 = tab_at(tq, oq & 0xFFFFu), q1 = tab_at(tq, oq >> 16);
+            if (tiq.any) apply_ties(tiq, oq, cq + 2 * d, q0, q1);
+            double p0 = pu, p1 = pu;
+            if (two) {
+                const uint32_t op = tab_offsets2(vp[q][d]);
+                p0 = tab_at(tp, op & 0xFFFFu);
+                p1 = tab_at(tp, op >> 16);
+                if (tip.any) apply_ties(tip, op, cq + 2 * d, p0, p1);
+            }
+            mark |= q0 > kMarkSeen || q1 > kMarkSeen || p0 < -kMarkSeen || p1 < -kMarkSeen;
+            if (!mark) s += div_term(q0, p0) + div_term(q1, p1);
+        }
+        if (mark) {  // rare: values outside the exact bins, decided exactly
+            s = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = cq + e;
+                const uint32_t wq = vq[q][e >> 1];
+                const uint32_t hq = (e & 1) ? (wq >> 16) : (wq & 0xFFFFu);
+                const uint32_t oq = tab_offsets2(hq) & 0xFFFFu;
+                double qe = tab_at(tq, oq);
+                qe = qe > kMarkSeen ? final_prob(sm.rf[0], sm.inv[0], sm.eff[0][0], sm.eff[0][1], hq, col, false)
+                                    : apply_ties1(tiq, oq, col, qe);
+                double pe = pu;
+                if (two) {
+                    const uint32_t wp = vp[q][e >> 1];
+                    const uint32_t hp = (e & 1) ? (wp >> 16) : (wp & 0xFFFFu);
+                    const uint32_t op = tab_offsets2(hp) & 0xFFFFu;
+                    pe = tab_at(tp, op);
+                    pe = pe < -kMarkSeen ? final_prob(sm.rf[1], sm.inv[1], sm.eff[1][0], sm.eff[1][1], hp, col, true)
+                                         : apply_ties1(tip, op, col, pe);
+                }
+                s += div_term(qe, pe);
+            }
+        }
+        tot += s;
+    }
+    return tot;
+}
+
+// The last position of a pending request: k from the fuzzy passes and the units' own tests.
+__device__ __forceinline__ void decide_fuzzy(const FastArgs& f, int b) {
+    const VerifyArgs& a = f.a;
+    const int K = a.K;
+    const int lane = threadIdx.x & (kWave - 1);
+    const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + (size_t)b * (K + 1);
+    const double* D = reinterpret_cast<const double*>(f.ws + f.L.div) + (size_t)f.units * 2 * f.nS +
+                      (size_t)b * (K + 1);
+    uint32_t st = 0;
+    int acc = 1;
+    bool pass = false;
+    if (lane < K) {
+        st = ldnt(&U[lane].status);
+        acc = ldnt(&U[lane].accept);
+        pass = ldnt(&D[lane]) <= (double)a.tau[b];
+    }
+    const uint32_t deg = wave_or(st & kStDegenerate);
+    int k = first_lane(__ballot(lane < K && !pass && !acc));
+    if (k < 0) k = K;
+    // a position that passed on its divergence never took the lossless test
+    const uint32_t outside = wave_or((lane < K && lane <= k && !pass) ? (st & kStOutside) : 0u);
+    if (lane == 0) {
+        ReqFast* Rq = reinterpret_cast<ReqFast*>(f.ws + f.L.reqs) + b;
+        Rq->mode = 1;
+        Rq->k = k;
+        Rq->status = deg | outside;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_diverge_kernel(FastArgs f) {
+    __shared__ ResSmem sm;
+    const VerifyArgs& a = f.a;
+    // placement as in the count kernel (request b on XCD b % 8); workgroup w of a request is half
+    // w % 2 of slice (w / 2) % nS of drafted position w / (2 nS)
+    const int R = 2 * f.nS * a.K;
+    const int x = blockIdx.x % kXcd, l = blockIdx.x / kXcd;
+    const int b = (l / R) * kXcd + x, w = l % R;
+    if (b >= a.B) return;
+    const u32x4 req = ldnt(reinterpret_cast<const u32x4*>(f.ws + f.L.reqs) + b);
+    if ((int)req[0] != 3) return;
+    const int j = w / (2 * f.nS), sw = w % (2 * f.nS), slice = sw >> 1, half = sw & 1;
+    const int unit = b * (a.K + 1) + j;
+    const bool two = !f.uniform;
+    constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
+    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWEnd = kWFlag + 2;
+    static_assert(kWEnd <= kThreads, "one record word per thread");
+    const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + unit;
+    const int t = (int)threadIdx.x;
+    uint32_t rec_word = 0u;
+    if (t < kWCut) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->rq) + t);
+    else if (t < kWFlag) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + (t - kWCut));
+    else if (t < kWEnd) rec_word = ldnt(&part_of(f, unit, slice, t - kWFlag)->flags);
+    const int c0 = slice * kSliceCols;
+    const size_t stride = (size_t)a.V;
+    const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)b * (a.K + 1) + j) * stride;
+    const uint16_t* drow = two ? static_cast<const uint16_t*>(a.draft) + ((size_t)b * a.draft_rows + j) * stride : trow;
+    u32x4 vq[kLoads], vp[kLoads];
+    load_slice(trow, c0, a.V, vq);
+    load_slice(drow, c0, a.V, vp);
+    if (t < kWCut) {
+        reinterpret_cast<uint32_t*>(&sm.rf[0])[t] = rec_word;
+    } else if (t < kWFlag) {
+        const int y = t - kWCut;
+        const bool keep_all = !two && y >= 2 * kCut;  // no draft row: UnitCut{0, -1, 0, 0}
+        reinterpret_cast<uint32_t*>(&sm.cut[0][0])[y] = keep_all ? (y % kCut == 1 ? 0xFFFFFFFFu : 0u) : rec_word;
+    } else if (t < kWEnd) {
+        sm.flags[t - kWFlag] = (t == kWFlag || two) ? rec_word : 0u;
+    }
+    if (t >= kWave && t < kWave + 6) sm.tie[(t - kWave) / 3][(t - kWave) % 3].off = kNoTie;
+    __syncthreads();
+    if (t < 2) {
+        sm.inv[t][0] = 1.0 / sm.rf[t].S;
+        sm.inv[t][1] = 1.0 / sm.rf[t].Z;
+    }
+    if (t >= kWave && t < 2 * kWave) table_groups(sm, two);
+    __syncthreads();
+    build_tables(sm, two, slice);
+    slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);
+    __syncthreads();
+    const double part = block_sum<double>(divergence_slice(f, sm, half, c0, two, vq, vp), sm.redd);
+    double* parts = reinterpret_cast<double*>(f.ws + f.L.div);
+    if (t == 0) parts[(size_t)unit * 2 * f.nS + sw] = part;
+    // the position's arrival (its 2 nS workgroups), then the request's (its K positions)
+    drain_stores();
+    __syncthreads();
+    if (t == 0) {
+        unsigned* uc = reinterpret_cast<unsigned*>(f.ws + f.L.unit_ctr + (size_t)unit * 128);
+        const unsigned old = l2_fetch_add(uc, 1u);
+        sm.last = (old + 1 == (unsigned)(2 * f.nS)) ? 1 : 0;
+        if (sm.last) *uc = 0u;
+    }
+    __syncthreads();
+    if (!sm.last) return;
+    if (t < kWave) {
+        const double v = t < 2 * f.nS ? ldnt(&parts[(size_t)unit * 2 * f.nS + t]) : 0.0;
+        const double Dj = wave_sum(v);  // fixed order: the same bits on every run
+        if (t == 0) {
+            reinterpret_cast<double*>(f.ws + f.L.div)[(size_t)f.units * 2 * f.nS + unit] = Dj;
+            if (a.out_div) a.out_div[(size_t)b * a.K + j] = (float)Dj;
+        }
+    }
+    drain_stores();
+    __syncthreads();
+    if (t == 0) {
+        unsigned* rc = reinterpret_cast<unsigned*>(f.ws + f.L.req_ctr + (size_t)b * 128);
+        const unsigned old = l2_fetch_add(rc, 1u);
+        sm.last = (old + 1 == (unsigned)a.K) ? 1 : 0;
+        if (sm.last) *rc = 0u;
+    }
+    __syncthreads();
+    if (!sm.last || t >= kWave) return;
+    decide_fuzzy(f, b);
+}
+
+void launch_diverge(const FastArgs& f, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL(fast_diverge_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, f);
+}
+
 void launch_resolve(const FastArgs& f, int grid, hipStream_t stream) {
     hipLaunchKernelGGL(fast_resolve_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, f);
 }

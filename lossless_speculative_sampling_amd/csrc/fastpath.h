@@ -52,11 +52,14 @@ struct FastPlan {
     int units;       // B * (K + 1)
     int grid;        // workgroups of the count kernel
     int grid_resolve;// workgroups of the resolve kernel
+    int grid_diverge;// workgroups of the divergence kernel (fuzzy acceptance)
     size_t ws_bytes; // fast workspace bytes
 };
 
 FastPlan fast_plan(int B, int K, int V);
 bool fast_path_applies(const VerifyArgs& a);
+// Fuzzy acceptance (a.tau set) on this path: not the assisted variant, at most 63 positions.
+bool fast_fuzzy_applies(const VerifyArgs& a);
 int fast_verify(const VerifyArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
 // The same pass also builds the Saguaro outcome cache (cache != nullptr); fast_cache_applies
 // says whether every depth's list fits the per-slice candidate lists.

@@ -24,6 +24,7 @@ FastPlan fast_plan(int B, int K, int V) {
     const int reqs_per_xcd = (B + kXcd - 1) / kXcd;
     p.grid = kXcd * reqs_per_xcd * (K + 1) * p.nS;
     p.grid_resolve = kXcd * reqs_per_xcd * max(2 * p.nS, K + 1);  // two workgroups per slice
+    p.grid_diverge = kXcd * reqs_per_xcd * 2 * p.nS * K;           // ... of every drafted position
     p.ws_bytes = layout(B, p.units, p.nS).total;
     return p;
 }
@@ -35,6 +36,10 @@ bool fast_path_applies(const VerifyArgs& a) {
     if ((reinterpret_cast<uintptr_t>(a.draft) & 15) || (reinterpret_cast<uintptr_t>(a.target) & 15)) return false;
     const int nS = (a.V + kSliceCols - 1) / kSliceCols;
     return nS * kTop <= kMergeCap;  // every slice's candidate list fits the merge buffer
+}
+
+bool fast_fuzzy_applies(const VerifyArgs& a) {
+    return fast_path_applies(a) && !(a.flags & SPEC_ASSISTED) && a.K < kWave;
 }
 
 static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -53,6 +58,7 @@ static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t
     if (c) f.fan = c->fanout;
     else f.fan = Fanout{};
     launch_count(f, p.grid, stream);
+    if (a.tau) launch_diverge(f, p.grid_diverge, stream);
     launch_resolve(f, p.grid_resolve, stream);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }

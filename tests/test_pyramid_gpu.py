@@ -108,3 +108,39 @@ def test_pyramid_negative_threshold_is_spec_verify():
     torch.cuda.synchronize()
     for x, y in zip((a.k, a.tstar, a.status), (b.k, b.tstar, b.status)):
         assert torch.equal(x, y)
+
+
+# bf16 rows (V a multiple of 8, at least 2048) with given tokens take the register-resident
+# path: the count kernel defers the decision, a divergence pass sums every position's
+# divergence from the exact per-element values, and the resolve kernel draws the residual
+@pytest.mark.parametrize("V", [2048, 16392, 128256])
+def test_pyramid_fast_path(V):
+    rng = np.random.default_rng(V + 5)
+    B, K = 16, 6
+    zt = synth.zipf_rows(rng, B * (K + 1), V).reshape(B, K + 1, V)
+    s = rng.uniform(0.3, 2.0, size=(B, K, 1)).astype(np.float32)
+    zd = (0.8 * zt[:, :K] + s * rng.standard_normal((B, K, V), dtype=np.float32)).astype(np.float32)
+    zt, zd = synth.f32_to_bf16_bits(zt), synth.f32_to_bf16_bits(zd)
+    T = rng.choice([0.0, 0.6, 1.0, 1.3], B).astype(np.float32)
+    tk = rng.choice([0, 1, 20, 3000], B).astype(np.int32)
+    tp = rng.choice([0.5, 0.95, 1.0], B).astype(np.float32)
+    prm = oracle.params_array(T, tk, tp)
+    probe = oracle.verify(zd, zt, synth.BF16, K, prm, F=2, C=0.4, seed=5, tau=np.full(B, -1.0))
+    tau = np.median(probe.div, axis=1).astype(np.float32)     # about half the positions pass
+    tau[::5] = -1.0
+    tau[1::7] = 1.0
+    tau[(T == 0.0) | (tk == 1)] = 0.5                          # one-hot rows diverge by exactly 0 or 1
+    for tokens, label in ((probe.tokens, "drafted"), (rng.integers(0, V, (B, K)), "random")):
+        check_pyramid(zd, zt, synth.BF16, K, prm, tau, tokens=tokens, F=2, C=0.4, label=f"fast {label} V={V}")
+    check_pyramid(None, zt, synth.BF16, K, prm, tau, tokens=rng.integers(0, V, (B, K)), uniform=True,
+                  label=f"fast uniform V={V}")
+
+
+def test_pyramid_fast_path_full_size_stages():
+    s1, s2 = synth.pyramid()
+    prm = oracle.params_array(1.0, 0, 1.0, B=s1.B)
+    for s in (s1, s2):
+        drafted = oracle.verify(s.draft, s.verifier, synth.BF16, s.K, prm, seed=s.seed, tau=s.tau).tokens
+        o = check_pyramid(s.draft, s.verifier, synth.BF16, s.K, prm, s.tau, tokens=drafted, seed=s.seed,
+                          label=s.name + " given tokens")
+        assert (o.div <= s.tau[:, None]).any() and (o.div > s.tau[:, None]).any()
