@@ -776,10 +776,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 // Fuzzy acceptance (PyramidSD notes, key design 1): a drafted token passes when the Jensen-
 // Shannon divergence (bits) of the processed verifier row q_j and drafter row p'_j is at most
 // the request's threshold; elsewhere the lossless test the count kernel already ran decides.
-// For every request the count kernel left pending, the two workgroups of each slice of each
-// drafted position sum the divergence over their half of the slice with the same exact
-// per-element values as the residual; the last of a position's workgroups totals it, and the
-// last position of the request finds k and hands the request to the resolve kernel.
+// For every request the count kernel left pending, one workgroup per slice of each drafted
+// position sums the divergence over the slice with the same exact per-element values as the
+// residual; the last of a position's workgroups totals it, and the last position of the
+// request finds k and hands the request to the resolve kernel.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ double div_term(double q, double p) {
     const double m = 0.5 * (p + q);
@@ -789,8 +789,8 @@ __device__ __forceinline__ double div_term(double q, double p) {
     return d;
 }
 
-// This thread's share of the divergence over the workgroup's half of the slice.
-__device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& sm, int half, int c0, bool two,
+// This thread's share of the divergence over the slice.
+__device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& sm, int c0, bool two,
                                                   const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads]) {
     const double pu = 1.0 / (double)f.a.V;
     const VerifyArgs& a = f.a;
@@ -801,7 +801,6 @@ __device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& s
     double tot = 0.0;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
-        if (q / (kLoads / 2) != half) continue;
         const int cq = col_of(c0, q, 0);
         if (cq >= a.V) continue;
         double s = 0.0;
@@ -881,15 +880,15 @@ __device__ __forceinline__ void decide_fuzzy(const FastArgs& f, int b) {
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_diverge_kernel(FastArgs f) {
     __shared__ ResSmem sm;
     const VerifyArgs& a = f.a;
-    // placement as in the count kernel (request b on XCD b % 8); workgroup w of a request is half
-    // w % 2 of slice (w / 2) % nS of drafted position w / (2 nS)
-    const int R = 2 * f.nS * a.K;
+    // placement as in the count kernel (request b on XCD b % 8); workgroup w of a request is
+    // slice w % nS of drafted position w / nS
+    const int R = f.nS * a.K;
     const int x = blockIdx.x % kXcd, l = blockIdx.x / kXcd;
     const int b = (l / R) * kXcd + x, w = l % R;
     if (b >= a.B) return;
     const u32x4 req = ldnt(reinterpret_cast<const u32x4*>(f.ws + f.L.reqs) + b);
     if ((int)req[0] != 3) return;
-    const int j = w / (2 * f.nS), sw = w % (2 * f.nS), slice = sw >> 1, half = sw & 1;
+    const int j = w / f.nS, slice = w % f.nS;
     const int unit = b * (a.K + 1) + j;
     const bool two = !f.uniform;
     constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
@@ -928,22 +927,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     build_tables(sm, two, slice);
     slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);
     __syncthreads();
-    const double part = block_sum<double>(divergence_slice(f, sm, half, c0, two, vq, vp), sm.redd);
+    const double part = block_sum<double>(divergence_slice(f, sm, c0, two, vq, vp), sm.redd);
     double* parts = reinterpret_cast<double*>(f.ws + f.L.div);
-    if (t == 0) parts[(size_t)unit * 2 * f.nS + sw] = part;
-    // the position's arrival (its 2 nS workgroups), then the request's (its K positions)
+    if (t == 0) parts[(size_t)unit * 2 * f.nS + slice] = part;
+    // the position's arrival (its nS workgroups), then the request's (its K positions)
     drain_stores();
     __syncthreads();
     if (t == 0) {
         unsigned* uc = reinterpret_cast<unsigned*>(f.ws + f.L.unit_ctr + (size_t)unit * 128);
         const unsigned old = l2_fetch_add(uc, 1u);
-        sm.last = (old + 1 == (unsigned)(2 * f.nS)) ? 1 : 0;
+        sm.last = (old + 1 == (unsigned)f.nS) ? 1 : 0;
         if (sm.last) *uc = 0u;
     }
     __syncthreads();
     if (!sm.last) return;
     if (t < kWave) {
-        const double v = t < 2 * f.nS ? ldnt(&parts[(size_t)unit * 2 * f.nS + t]) : 0.0;
+        const double v = t < f.nS ? ldnt(&parts[(size_t)unit * 2 * f.nS + t]) : 0.0;
         const double Dj = wave_sum(v);  // fixed order: the same bits on every run
         if (t == 0) {
             reinterpret_cast<double*>(f.ws + f.L.div)[(size_t)f.units * 2 * f.nS + unit] = Dj;

@@ -24,7 +24,7 @@ FastPlan fast_plan(int B, int K, int V) {
     const int reqs_per_xcd = (B + kXcd - 1) / kXcd;
     p.grid = kXcd * reqs_per_xcd * (K + 1) * p.nS;
     p.grid_resolve = kXcd * reqs_per_xcd * max(2 * p.nS, K + 1);  // two workgroups per slice
-    p.grid_diverge = kXcd * reqs_per_xcd * 2 * p.nS * K;           // ... of every drafted position
+    p.grid_diverge = kXcd * reqs_per_xcd * p.nS * K;               // one per slice of every drafted position
     p.ws_bytes = layout(B, p.units, p.nS).total;
     return p;
 }
