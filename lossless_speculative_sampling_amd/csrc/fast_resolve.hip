@@ -788,17 +788,24 @@ __device__ __forceinline__ double div_term(double q, double p) {
     if (q > 0.0) d += 0.5 * q * log2(q / m);
     return d;
 }
+// v log2 v, 0 at v = 0.
+__device__ __forceinline__ double xlog2x(double v) { return v > 0.0 ? v * log2(v) : 0.0; }
 
-// This thread's share of the divergence over the slice.
+// This thread's share of the divergence over the slice.  Each element's term is split as
+// (q log2 q + p log2 p) / 2 - m log2 m with m = (q + p) / 2: the first pass sums -m log2 m per
+// element (and whole terms for the rare elements outside the exact bins); the tables then
+// turn in place into per-bin v log2 v, which the second pass sums.  One logarithm per
+// element instead of two, and no division.
 __device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& sm, int c0, bool two,
                                                   const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads]) {
     const double pu = 1.0 / (double)f.a.V;
     const VerifyArgs& a = f.a;
     const char* tq = reinterpret_cast<const char*>(&sm.u.tab[0][0]);
     const char* tp = reinterpret_cast<const char*>(&sm.u.tab[1][0]);
-    const Ties tiq = load_ties(sm, 0);
-    const Ties tip = load_ties(sm, 1);
+    Ties tiq = load_ties(sm, 0);
+    Ties tip = load_ties(sm, 1);
     double tot = 0.0;
+    uint32_t marked = 0u;  // loads whose elements the first pass took whole
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
         const int cq = col_of(c0, q, 0);
@@ -818,9 +825,10 @@ __device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& s
                 if (tip.any) apply_ties(tip, op, cq + 2 * d, p0, p1);
             }
             mark |= q0 > kMarkSeen || q1 > kMarkSeen || p0 < -kMarkSeen || p1 < -kMarkSeen;
-            if (!mark) s += div_term(q0, p0) + div_term(q1, p1);
+            if (!mark) s -= xlog2x(0.5 * (q0 + p0)) + xlog2x(0.5 * (q1 + p1));
         }
         if (mark) {  // rare: values outside the exact bins, decided exactly
+            marked |= 1u << q;
             s = 0.0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -845,7 +853,43 @@ __device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& s
         }
         tot += s;
     }
-    return tot;
+    // every value an unmarked element reads lies in a listed group (the groups wholly below a
+    // row's cuts hold 0, which stays 0), or is a tie's alternative
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int i = (int)threadIdx.x / kWave; i < sm.gcount; i += kWaves) {
+        const int idx = kHistLead + sm.glist[i] * kGroup + lane;
+        sm.u.tab[0][idx] = xlog2x(sm.u.tab[0][idx]);
+        if (two) sm.u.tab[1][idx] = xlog2x(sm.u.tab[1][idx]);
+    }
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+        tiq.alt[x] = xlog2x(tiq.alt[x]);
+        tip.alt[x] = xlog2x(tip.alt[x]);
+    }
+    __syncthreads();
+    const double lpu = 2.0 * xlog2x(pu);  // p log2 p of both elements of a pair, uniform draft
+    double half = 0.0;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        const int cq = col_of(c0, q, 0);
+        if (cq >= a.V || ((marked >> q) & 1u)) continue;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t oq = tab_offsets2(vq[q][d]);
+            double q0 = tab_at(tq, oq & 0xFFFFu), q1 = tab_at(tq, oq >> 16);
+            if (tiq.any) apply_ties(tiq, oq, cq + 2 * d, q0, q1);
+            double pl = lpu;
+            if (two) {
+                const uint32_t op = tab_offsets2(vp[q][d]);
+                double p0 = tab_at(tp, op & 0xFFFFu), p1 = tab_at(tp, op >> 16);
+                if (tip.any) apply_ties(tip, op, cq + 2 * d, p0, p1);
+                pl = p0 + p1;
+            }
+            half += q0 + q1 + pl;
+        }
+    }
+    return tot + 0.5 * half;
 }
 
 // The last position of a pending request: k from the fuzzy passes and the units' own tests.
