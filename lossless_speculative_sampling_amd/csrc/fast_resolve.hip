@@ -791,21 +791,51 @@ __device__ __forceinline__ double div_term(double q, double p) {
 // v log2 v, 0 at v = 0.
 __device__ __forceinline__ double xlog2x(double v) { return v > 0.0 ? v * log2(v) : 0.0; }
 
-// This thread's share of the divergence over the slice.  Each element's term is split as
-// (q log2 q + p log2 p) / 2 - m log2 m with m = (q + p) / 2: the first pass sums -m log2 m per
-// element (and whole terms for the rare elements outside the exact bins); the tables then
-// turn in place into per-bin v log2 v, which the second pass sums.  One logarithm per
-// element instead of two, and no division.
-__device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& sm, int c0, bool two,
-                                                  const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads]) {
+// Base-2 logarithm of the per-element and per-bin terms.  x = 2^e f with f in [1/2, 1); the
+// 8 fraction bits below f's leading one pick an interval of width 2^-9 with centre c_i, and
+// log2 f = log2 c_i + log2(1 + r) with r = f / c_i - 1 (|r| <= 2^-9, one fma with the
+// tabulated 1 / c_i) and log2(1 + r) from the first five terms of its series.  Absolute error
+// about 2e-16 on (0, 1] (about 12 fp64 operations against the library's ~60): each term
+// v log2 v is off by at most v times that, so a sum over a distribution by under 1e-15.
+struct LogTab {
+    double2 e[256];  // {1 / c_i, log2 c_i}
+};
+__device__ __forceinline__ void build_logtab(LogTab& lt) {
+    for (int i = (int)threadIdx.x; i < 256; i += (int)blockDim.x) {
+        const double r = 1.0 / (0.5 + (i + 0.5) / 512.0);
+        lt.e[i] = make_double2(r, -log2(r));
+    }
+}
+__device__ __forceinline__ double log2_tab(double x, const LogTab& lt) {
+    const double f = __builtin_amdgcn_frexp_mant(x);
+    const int e = __builtin_amdgcn_frexp_exp(x);
+    const double2 t = lt.e[(__double2hiint(f) >> 12) & 0xFF];
+    const double r = fma(f, t.x, -1.0);
+    double p = fma(r, 0.2, -0.25);
+    p = fma(r, p, 1.0 / 3.0);
+    p = fma(r, p, -0.5);
+    p = fma(r, p, 1.0);
+    return fma(r * p, 1.4426950408889634, t.y) + (double)e;
+}
+__device__ __forceinline__ double xlog2x_tab(double v, const LogTab& lt) { return v > 0.0 ? v * log2_tab(v, lt) : 0.0; }
+
+// This thread's share of the divergence over the slice, every element's term whole (two
+// logarithms each): the way a slice with more than kDivList elements outside the exact bins
+// takes.  It loads the slice again (from cache), so that the caller's copy is dead here.
+__device__ __forceinline__ double divergence_slice_whole(const FastArgs& f, ResSmem& sm, int c0, bool two,
+                                                        const uint16_t* trow, const uint16_t* drow) {
+    // fresh addresses: reusing the first load's would keep them live over the whole kernel
+    asm volatile("" : "+s"(trow), "+s"(drow), "+s"(c0));
+    u32x4 vq[kLoads], vp[kLoads];
+    load_slice(trow, c0, f.a.V, vq);
+    load_slice(drow, c0, f.a.V, vp);
     const double pu = 1.0 / (double)f.a.V;
     const VerifyArgs& a = f.a;
     const char* tq = reinterpret_cast<const char*>(&sm.u.tab[0][0]);
     const char* tp = reinterpret_cast<const char*>(&sm.u.tab[1][0]);
-    Ties tiq = load_ties(sm, 0);
-    Ties tip = load_ties(sm, 1);
+    const Ties tiq = load_ties(sm, 0);
+    const Ties tip = load_ties(sm, 1);
     double tot = 0.0;
-    uint32_t marked = 0u;  // loads whose elements the first pass took whole
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
         const int cq = col_of(c0, q, 0);
@@ -825,10 +855,9 @@ __device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& s
                 if (tip.any) apply_ties(tip, op, cq + 2 * d, p0, p1);
             }
             mark |= q0 > kMarkSeen || q1 > kMarkSeen || p0 < -kMarkSeen || p1 < -kMarkSeen;
-            if (!mark) s -= xlog2x(0.5 * (q0 + p0)) + xlog2x(0.5 * (q1 + p1));
+            if (!mark) s += div_term(q0, p0) + div_term(q1, p1);
         }
         if (mark) {  // rare: values outside the exact bins, decided exactly
-            marked |= 1u << q;
             s = 0.0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -853,14 +882,99 @@ __device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& s
         }
         tot += s;
     }
-    // every value an unmarked element reads lies in a listed group (the groups wholly below a
-    // row's cuts hold 0, which stays 0), or is a tie's alternative
+    return tot;
+}
+
+constexpr int kDivList = 1024;  // elements outside the exact bins a slice lists
+
+// Where the divergence pass keeps the listed elements: their columns in the slice, and each
+// row's value (table value with the ties applied), or -(h + 1) for a marker entry (h the bf16
+// logit, whose value final_prob forms).
+struct DivList {
+    double q[kDivList];
+    double p[kDivList];
+    uint16_t col[kDivList];
+};
+
+// This thread's share of the divergence over the slice.  Each element's term is split as
+// (q log2 q + p log2 p) / 2 - m log2 m with m = (q + p) / 2: the first pass sums -m log2 m per
+// element; the tables then turn in place into per-bin v log2 v, which the second pass sums.
+// One logarithm (log2_tab) per element instead of two, and no division.  Elements whose
+// value lies outside the exact bins (a marker entry) take the exact term instead: the first
+// pass lists them in thread order (a workgroup scan), and the workgroup shares the list out
+// once the slice is no longer needed in registers, so that a wave is not held up by its few
+// lanes that hold one.
+__device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& sm, int c0, bool two,
+                                                  const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads],
+                                                  DivList& dl, const LogTab& lt, const uint16_t* trow,
+                                                  const uint16_t* drow) {
+    const double pu = 1.0 / (double)f.a.V;
+    const VerifyArgs& a = f.a;
+    const char* tq = reinterpret_cast<const char*>(&sm.u.tab[0][0]);
+    const char* tp = reinterpret_cast<const char*>(&sm.u.tab[1][0]);
+    Ties tiq = load_ties(sm, 0);
+    Ties tip = load_ties(sm, 1);
+    double tot = 0.0;
+    uint32_t odd = 0u;  // bit 8 q + e: element e of load q is outside the exact bins
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        const int cq = col_of(c0, q, 0);
+        if (cq >= a.V) continue;
+        double s = 0.0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t oq = tab_offsets2(vq[q][d]);
+            double q0 = tab_at(tq, oq & 0xFFFFu), q1 = tab_at(tq, oq >> 16);
+            if (tiq.any) apply_ties(tiq, oq, cq + 2 * d, q0, q1);
+            double p0 = pu, p1 = pu;
+            if (two) {
+                const uint32_t op = tab_offsets2(vp[q][d]);
+                p0 = tab_at(tp, op & 0xFFFFu);
+                p1 = tab_at(tp, op >> 16);
+                if (tip.any) apply_ties(tip, op, cq + 2 * d, p0, p1);
+            }
+            const bool x0 = q0 > kMarkSeen || p0 < -kMarkSeen, x1 = q1 > kMarkSeen || p1 < -kMarkSeen;
+            odd |= ((x0 ? 1u : 0u) | (x1 ? 2u : 0u)) << (8 * q + 2 * d);
+            s -= xlog2x_tab(x0 ? 0.0 : 0.5 * (q0 + p0), lt) + xlog2x_tab(x1 ? 0.0 : 0.5 * (q1 + p1), lt);
+        }
+        tot += s;
+    }
+    int n_all;
+    const int base = block_exclusive_scan<int>(__popc(odd), sm.redi, &n_all);
+    if (n_all > kDivList) return divergence_slice_whole(f, sm, c0, two, trow, drow);
+    if (odd) {
+        int i = base;
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (!((odd >> (8 * q + e)) & 1u)) continue;
+                const int col = col_of(c0, q, e);
+                const uint32_t hq = (vq[q][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t oq = tab_offsets2(hq) & 0xFFFFu;
+                const double qv = tab_at(tq, oq);
+                double pv = pu;
+                if (two) {
+                    const uint32_t hp = (vp[q][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    const uint32_t op = tab_offsets2(hp) & 0xFFFFu;
+                    pv = tab_at(tp, op);
+                    pv = pv < -kMarkSeen ? -(double)(hp + 1u) : apply_ties1(tip, op, col, pv);
+                }
+                dl.q[i] = qv > kMarkSeen ? -(double)(hq + 1u) : apply_ties1(tiq, oq, col, qv);
+                dl.p[i] = pv;
+                dl.col[i] = (uint16_t)(col - c0);
+                ++i;
+            }
+        }
+    }
+    // every value an element inside the exact bins reads lies in a listed group (the groups
+    // wholly below a row's cuts hold 0, which stays 0), or is a tie's alternative
     __syncthreads();
     const int lane = threadIdx.x & (kWave - 1);
     for (int i = (int)threadIdx.x / kWave; i < sm.gcount; i += kWaves) {
         const int idx = kHistLead + sm.glist[i] * kGroup + lane;
-        sm.u.tab[0][idx] = xlog2x(sm.u.tab[0][idx]);
-        if (two) sm.u.tab[1][idx] = xlog2x(sm.u.tab[1][idx]);
+        sm.u.tab[0][idx] = xlog2x_tab(sm.u.tab[0][idx], lt);
+        if (two) sm.u.tab[1][idx] = xlog2x_tab(sm.u.tab[1][idx], lt);
     }
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
@@ -868,26 +982,36 @@ __device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& s
         tip.alt[x] = xlog2x(tip.alt[x]);
     }
     __syncthreads();
-    const double lpu = 2.0 * xlog2x(pu);  // p log2 p of both elements of a pair, uniform draft
+    const double lpu = xlog2x(pu);  // p log2 p of every element, uniform draft
     double half = 0.0;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
         const int cq = col_of(c0, q, 0);
-        if (cq >= a.V || ((marked >> q) & 1u)) continue;
+        if (cq >= a.V) continue;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint32_t oq = tab_offsets2(vq[q][d]);
             double q0 = tab_at(tq, oq & 0xFFFFu), q1 = tab_at(tq, oq >> 16);
             if (tiq.any) apply_ties(tiq, oq, cq + 2 * d, q0, q1);
-            double pl = lpu;
+            double p0 = lpu, p1 = lpu;
             if (two) {
                 const uint32_t op = tab_offsets2(vp[q][d]);
-                double p0 = tab_at(tp, op & 0xFFFFu), p1 = tab_at(tp, op >> 16);
+                p0 = tab_at(tp, op & 0xFFFFu);
+                p1 = tab_at(tp, op >> 16);
                 if (tip.any) apply_ties(tip, op, cq + 2 * d, p0, p1);
-                pl = p0 + p1;
             }
-            half += q0 + q1 + pl;
+            const uint32_t x = odd >> (8 * q + 2 * d);
+            half += ((x & 1u) ? 0.0 : q0 + p0) + ((x & 2u) ? 0.0 : q1 + p1);
         }
+    }
+    for (int i = (int)threadIdx.x; i < n_all; i += kThreads) {
+        const int col = c0 + (int)dl.col[i];
+#pragma unroll 1
+        for (int r = 0; r < 2; ++r) {  // the marker entries' values, in place
+            double* v = r ? &dl.p[i] : &dl.q[i];
+            if (*v < 0.0) *v = final_prob(sm.rf[r], sm.inv[r], sm.eff[r][0], sm.eff[r][1], (uint32_t)(-*v) - 1u, col, r == 1);
+        }
+        tot += div_term(dl.q[i], dl.p[i]);
     }
     return tot + 0.5 * half;
 }
@@ -923,6 +1047,8 @@ __device__ __forceinline__ void decide_fuzzy(const FastArgs& f, int b) {
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_diverge_kernel(FastArgs f) {
     __shared__ ResSmem sm;
+    __shared__ DivList dl;
+    __shared__ LogTab lt;
     const VerifyArgs& a = f.a;
     // placement as in the count kernel (request b on XCD b % 8); workgroup w of a request is
     // slice w % nS of drafted position w / nS
@@ -951,6 +1077,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     u32x4 vq[kLoads], vp[kLoads];
     load_slice(trow, c0, a.V, vq);
     load_slice(drow, c0, a.V, vp);
+    build_logtab(lt);
     if (t < kWCut) {
         reinterpret_cast<uint32_t*>(&sm.rf[0])[t] = rec_word;
     } else if (t < kWFlag) {
@@ -971,7 +1098,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     build_tables(sm, two, slice);
     slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);
     __syncthreads();
-    const double part = block_sum<double>(divergence_slice(f, sm, c0, two, vq, vp), sm.redd);
+    const double part = block_sum<double>(divergence_slice(f, sm, c0, two, vq, vp, dl, lt, trow, drow), sm.redd);
     double* parts = reinterpret_cast<double*>(f.ws + f.L.div);
     if (t == 0) parts[(size_t)unit * 2 * f.nS + slice] = part;
     // the position's arrival (its nS workgroups), then the request's (its K positions)

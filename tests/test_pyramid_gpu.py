@@ -136,6 +136,25 @@ def test_pyramid_fast_path(V):
                   label=f"fast uniform V={V}")
 
 
+# Logits near zero (|z| < 2^-6) or of magnitude 32 and more fall outside the exact bins: the
+# divergence pass lists them for the whole workgroup, or, past the list's capacity (1024
+# elements per slice), takes the slice element by element.  Scales from 0.002 (every element
+# outside) to 12 (the far tails outside); the second slice of V = 16392 holds 8 columns.
+def test_pyramid_fast_path_outside_bins():
+    rng = np.random.default_rng(77)
+    B, K, V = 8, 4, 16392
+    scale = np.array([0.002, 0.02, 0.3, 1.0, 2.0, 12.0, 0.05, 0.6], np.float32)[:, None, None]
+    zt = scale * rng.standard_normal((B, K + 1, V), dtype=np.float32)
+    zd = 0.8 * zt[:, :K] + 0.5 * scale * rng.standard_normal((B, K, V), dtype=np.float32)
+    zt, zd = synth.f32_to_bf16_bits(zt.astype(np.float32)), synth.f32_to_bf16_bits(zd.astype(np.float32))
+    prm = oracle.params_array(np.full(B, 1.0, np.float32), np.array([0, 0, 50, 0, 5000, 0, 0, 3], np.int32),
+                              np.array([1.0, 0.9, 1.0, 1.0, 0.95, 1.0, 0.9, 1.0], np.float32))
+    probe = oracle.verify(zd, zt, synth.BF16, K, prm, seed=5, tau=np.full(B, -1.0))
+    tau = np.median(probe.div, axis=1).astype(np.float32)
+    o = check_pyramid(zd, zt, synth.BF16, K, prm, tau, tokens=probe.tokens, label="fast outside bins")
+    assert (o.div <= tau[:, None]).any() and (o.div > tau[:, None]).any()
+
+
 def test_pyramid_fast_path_full_size_stages():
     s1, s2 = synth.pyramid()
     prm = oracle.params_array(1.0, 0, 1.0, B=s1.B)
