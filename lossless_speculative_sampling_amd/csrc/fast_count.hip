@@ -123,19 +123,18 @@ __device__ __forceinline__ Threshold local_threshold(const CountSmem& sm, int r,
     return th;
 }
 
-// The first L elements (token order: key desc, id asc) of row r in this slice, sorted, into
-// sm.top_key[r] / sm.top_id[r]; sm.n_top[r] gets their number.  sm.n_top[r] starts at 0 (the
-// caller clears it before an earlier barrier) and the caller synchronises afterwards.
-__device__ __forceinline__ void local_top(CountSmem& sm, int r, int L, int c0, int V, const u32x4 (&v)[kLoads]) {
-    const Threshold th = local_threshold(sm, r, L);
+// Marks this thread's elements of one row: cand for those above the threshold key (and at it
+// when every element there is needed), ties for those at it otherwise.  Pairs of values whose
+// larger order key is below tau - 1 (-0 has the packed key 0x7FFF, one below +0) are skipped
+// two at a time.
+struct TopMarks {
+    uint32_t cand, ties;
+};
+__device__ __forceinline__ TopMarks top_marks(const Threshold& th, int c0, int V, const u32x4 (&v)[kLoads]) {
     const uint32_t tau = th.tau;
-    const int need = th.need;
-    // when every element at tau is needed the ties need no ordering
-    const bool all_ties = th.ties == need;
-    // pairs of values whose larger order key reaches tau - 1 (-0 has the packed key 0x7FFF,
-    // one below +0) are examined one by one; the rest are skipped two at a time
+    const bool all_ties = th.ties == th.need;
     const uint16_t lo_t = tau > 0u ? (uint16_t)(tau - 1u) : (uint16_t)0;
-    uint32_t tiemask = 0;
+    uint32_t cand = 0u, ties = 0u;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q)
 #pragma unroll
@@ -144,66 +143,109 @@ __device__ __forceinline__ void local_top(CountSmem& sm, int r, int L, int c0, i
             const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, w) >> (i16x2)(int16_t)15);
             const u16x2 k2 = __builtin_bit_cast(u16x2, w ^ (neg | 0x80008000u));
             if (max(k2[0], k2[1]) < lo_t) continue;
+#pragma unroll
             for (int e2 = 0; e2 < 2; ++e2) {
                 const int e = 2 * d + e2;
-                const int col = col_of(c0, q, e);
                 const uint32_t h = e2 ? (w >> 16) : (w & 0xFFFFu);
-                if (col >= V || (h & 0x7FFFu) >= 0x7F80u) continue;  // past the row, inf, NaN
+                if (col_of(c0, q, e) >= V || (h & 0x7FFFu) >= 0x7F80u) continue;  // past the row, inf, NaN
                 const uint32_t k = key16(h);
-                if (k > tau || (k == tau && all_ties && need > 0)) {
-                    const int slot = (int)atomicAdd(&sm.n_top[r], 1u);
-                    if (slot < kTop) {
-                        sm.top_key[r][slot] = k;
-                        sm.top_id[r][slot] = col;
-                    }
-                } else if (k == tau && need > 0) {
-                    tiemask |= 1u << (q * 8 + e);
-                }
+                const bool at = k == tau && th.need > 0;
+                const bool c = k > tau || (at && all_ties);
+                cand |= (c ? 1u : 0u) << (q * 8 + e);
+                ties |= (at && !c ? 1u : 0u) << (q * 8 + e);
             }
         }
-    __syncthreads();
-    int base = min((int)sm.n_top[r], kTop);
-    int need_left = all_ties ? 0 : need;
+    return TopMarks{cand, ties};
+}
+
+// The first L[r] elements (token order: key desc, id asc) of each row r in this slice (none for
+// L[r] = 0), sorted, into sm.top_key[r] / sm.top_id[r]; sm.n_top[r] gets their number.  One
+// pass marks every thread's elements at or above each row's threshold; one workgroup scan of
+// both rows' mark counts (at most L[r] <= 64 each, packed in 16-bit halves) gives each marked
+// element its slot in thread order, so no atomics; the elements at a threshold of which only
+// some are needed follow in token order (rare); then wave r sorts row r's list, both at once.
+// The caller synchronises afterwards.
+__device__ __forceinline__ void local_tops(CountSmem& sm, const int (&L)[2], int c0, int V, const u32x4 (&vq)[kLoads],
+                                           const u32x4 (&vp)[kLoads]) {
+    Threshold th[2] = {{0u, 0, 0}, {0u, 0, 0}};
+    uint32_t cand[2] = {0u, 0u}, ties[2] = {0u, 0u};
+    if (L[0] > 0) {
+        th[0] = local_threshold(sm, 0, L[0]);
+        const TopMarks m = top_marks(th[0], c0, V, vq);
+        cand[0] = m.cand;
+        ties[0] = m.ties;
+    }
+    if (L[1] > 0) {
+        th[1] = local_threshold(sm, 1, L[1]);
+        const TopMarks m = top_marks(th[1], c0, V, vp);
+        cand[1] = m.cand;
+        ties[1] = m.ties;
+    }
+    int total;
+    const int before = block_exclusive_scan<int>(__popc(cand[0]) | (__popc(cand[1]) << 16), sm.scan, &total);
+    int n[2] = {total & 0xFFFF, total >> 16};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        int slot = r ? before >> 16 : before & 0xFFFF;
+        const uint32_t m = cand[r];
+        if (m == 0u) continue;
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (!((m >> (q * 8 + e)) & 1u)) continue;
+                if (slot < kTop) {
+                    const uint32_t w = r ? vp[q][e >> 1] : vq[q][e >> 1];
+                    sm.top_key[r][slot] = key16((w >> (16 * (e & 1))) & 0xFFFFu);
+                    sm.top_id[r][slot] = col_of(c0, q, e);
+                }
+                ++slot;
+            }
+        }
+    }
     // then the first `need` elements at tau in token order (uniform loop; rare)
-    if (need_left > 0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (L[r] <= 0 || th[r].ties == th[r].need) continue;
+        int need_left = th[r].need;
         for (int q = 0; q < kLoads && need_left > 0; ++q) {
-            const uint32_t mq = (tiemask >> (q * 8)) & 0xFFu;
-            int total;
-            const int before = block_exclusive_scan<int>(__popc(mq), sm.scan, &total);
+            const uint32_t mq = (ties[r] >> (q * 8)) & 0xFFu;
+            int cnt;
+            const int pre = block_exclusive_scan<int>(__popc(mq), sm.scan, &cnt);
             int k = 0;
             for (int e = 0; e < 8; ++e) {
                 if (!(mq & (1u << e))) continue;
-                const int rank = before + k++;
-                const int slot = base + rank;
+                const int rank = pre + k++;
+                const int slot = n[r] + rank;
                 if (rank < need_left && slot < kTop) {
-                    sm.top_key[r][slot] = tau;
+                    sm.top_key[r][slot] = th[r].tau;
                     sm.top_id[r][slot] = col_of(c0, q, e);
                 }
             }
-            const int took = min(total, need_left);
-            base += took;
+            const int took = min(cnt, need_left);
+            n[r] += took;
             need_left -= took;
         }
-        __syncthreads();
     }
-    // sort (key desc, id asc): wave 0 ranks each entry against the others through lane reads
-    if (threadIdx.x < kWave) {
-        const int lane = threadIdx.x;
-        const int n = min(base, kTop);
-        const bool live = lane < n;
+    __syncthreads();
+    // sort (key desc, id asc): each lane ranks its entry against the list through broadcast reads
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    if (wave < 2 && (wave ? L[1] : L[0]) > 0) {
+        const int r = wave;
+        const int cnt = min(wave ? n[1] : n[0], kTop);
+        const bool live = lane < cnt;
         const uint32_t mk = live ? sm.top_key[r][lane] : 0u;
         const int mi = live ? sm.top_id[r][lane] : 0;
         const uint64_t ord = ((uint64_t)mk << 32) | (uint32_t)~mi;  // ids are non-negative
         int rank = 0;
-        for (int y = 0; y < n; y += 4) {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) rank += wave_bcast(ord, y + d) > ord ? 1 : 0;  // lanes past n: key 0
-        }
+#pragma unroll 4
+        for (int y = 0; y < cnt; ++y)
+            rank += (((uint64_t)sm.top_key[r][y] << 32) | (uint32_t)~sm.top_id[r][y]) > ord ? 1 : 0;
         if (live) {
             sm.top_key[r][rank] = mk;
             sm.top_id[r][rank] = mi;
         }
-        if (lane == 0) sm.n_top[r] = (uint32_t)n;
+        if (lane == 0) sm.n_top[r] = (uint32_t)cnt;
     }
 }
 
@@ -734,8 +776,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
         // passes over the columns (registers) first, so the columns are dead for the summaries
         const bool holds_s = j < a.K && tok_ok && s_tok >= c0;  // at or after this slice: count its key
         const int want_q = list_len(a, prm, false), want_p = two ? draft_list_len(f, prm, j) : 0;
-        if (want_q > 0) local_top(sm, 0, want_q, c0, a.V, vq);
-        if (two && want_p > 0) local_top(sm, 1, want_p, c0, a.V, vp);
+        if (want_q > 0 || want_p > 0) {
+            const int want[2] = {want_q, want_p};
+            local_tops(sm, want, c0, a.V, vq, vp);
+        }
         if (holds_s) local_ranks(sm, two, c0, s_tok, vq, vp);
         __syncthreads();
         publish_rows(f, sm, unit, slice, two, prm);
