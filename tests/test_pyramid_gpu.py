@@ -155,6 +155,23 @@ def test_pyramid_fast_path_outside_bins():
     assert (o.div <= tau[:, None]).any() and (o.div > tau[:, None]).any()
 
 
+# Long drafts on the bf16 path: 40 drafted positions (one divergence arrival per position, the
+# request's arrival counting to K), mixed thresholds, drafted and random tokens
+def test_pyramid_fast_path_long_draft():
+    rng = np.random.default_rng(40)
+    B, K, V = 3, 40, 16392
+    zt = synth.zipf_rows(rng, B * (K + 1), V).reshape(B, K + 1, V)
+    zd = (0.8 * zt[:, :K] + rng.uniform(0.3, 1.5, (B, K, 1)).astype(np.float32)
+          * rng.standard_normal((B, K, V), dtype=np.float32)).astype(np.float32)
+    zt, zd = synth.f32_to_bf16_bits(zt), synth.f32_to_bf16_bits(zd)
+    prm = oracle.params_array(np.array([1.0, 0.7, 1.2], np.float32), np.array([0, 100, 0], np.int32),
+                              np.array([1.0, 1.0, 0.9], np.float32))
+    probe = oracle.verify(zd, zt, synth.BF16, K, prm, seed=5, tau=np.full(B, -1.0))
+    tau = np.quantile(probe.div, 0.8, axis=1).astype(np.float32)  # most positions pass
+    for tokens, label in ((probe.tokens, "drafted"), (rng.integers(0, V, (B, K)), "random")):
+        check_pyramid(zd, zt, synth.BF16, K, prm, tau, tokens=tokens, label=f"fast long {label}")
+
+
 def test_pyramid_fast_path_full_size_stages():
     s1, s2 = synth.pyramid()
     prm = oracle.params_array(1.0, 0, 1.0, B=s1.B)
