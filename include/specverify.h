@@ -292,8 +292,12 @@ int mirror_tree_lookup(const int32_t* tree_tokens, const int32_t* tree_parents, 
  *   flags      SPEC_SAMPLE_DRAFT | SPEC_UNIFORM_DRAFT | SPEC_ASSISTED
  *   out_div    [B][K] float32 device (nullable): Div_j of every position whose drafted token
  *              is valid, whether or not the scan reached it
- * Runs on the general path (one workgroup per position).  Return codes as spec_verify
- * (SPEC_EINVAL also for a null tau). */
+ * bf16 rows with V a multiple of 8, 2048 <= V <= 262144 and 16-byte aligned logits, given (or
+ * uniform) drafted tokens, no SPEC_ASSISTED and K < 64 take the register-resident path: a
+ * divergence pass runs between its count and resolve kernels.  Everything else runs on the
+ * general path (one workgroup per position).  Both sum the divergence in fp64; the decision
+ * Div_j <= tau[b] is taken on that sum.  Return codes as spec_verify (SPEC_EINVAL also for a
+ * null tau). */
 int pyramid_verify(const void* draft_logits, int draft_rows, const void* verifier_logits, int dtype, int B, int K,
                    int V, const spec_params* params, int F, float C, const float* tau, int32_t* draft_tokens,
                    uint64_t seed, uint64_t round, uint32_t flags, int32_t* out_k, int32_t* out_tstar,
