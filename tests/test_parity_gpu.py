@@ -276,6 +276,20 @@ def test_fast_parameter_mix(V):
     check_verify(w, tokens=rng.integers(0, V, (B, K)), label=f"fast-mix-random V={V}")
 
 
+# The register-resident path's largest vocabulary: 16 slices of 16384 columns, whose candidate
+# lists of 64 (top-k 64) fill the 1024-entry merge buffer exactly; 8 columns more and the call
+# takes the general path (one workgroup per position)
+@pytest.mark.parametrize("V", [262144, 262152])
+def test_fast_path_vocabulary_limit(V):
+    rng = np.random.default_rng(V % 1000)
+    B, K = 6, 2
+    T = np.array([1.0, 0.7, 1.0, 0.0, 1.3, 1.0])
+    tk = np.array([64, 64, 0, 0, 65, 50])
+    tp = np.array([1.0, 0.9, 0.95, 1.0, 1.0, 0.5])
+    w = _zipf_work(rng, B, K, V, T, tk, tp, F=4, C=0.3)
+    check_verify(w, tokens=_oracle_tokens(w), label=f"fast-limit V={V}")
+
+
 def test_fast_ties_and_large_sets():
     rng = np.random.default_rng(77)
     B, K, V = 16, 2, 20000
