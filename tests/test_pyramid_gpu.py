@@ -172,6 +172,22 @@ def test_pyramid_fast_path_long_draft():
         check_pyramid(zd, zt, synth.BF16, K, prm, tau, tokens=tokens, label=f"fast long {label}")
 
 
+# The bf16 fuzzy path's longest draft (K = 63: the request's positions in one wave) and one
+# past it (K = 64, general path)
+@pytest.mark.parametrize("K", [63, 64])
+def test_pyramid_draft_length_limit(K):
+    rng = np.random.default_rng(K)
+    B, V = 2, 2048
+    zt = synth.zipf_rows(rng, B * (K + 1), V).reshape(B, K + 1, V)
+    zd = (0.8 * zt[:, :K] + 0.6 * rng.standard_normal((B, K, V), dtype=np.float32)).astype(np.float32)
+    zt, zd = synth.f32_to_bf16_bits(zt), synth.f32_to_bf16_bits(zd)
+    prm = oracle.params_array(np.array([1.0, 0.8], np.float32), np.array([0, 40], np.int32),
+                              np.array([1.0, 0.95], np.float32))
+    probe = oracle.verify(zd, zt, synth.BF16, K, prm, seed=5, tau=np.full(B, -1.0))
+    tau = np.quantile(probe.div, 0.9, axis=1).astype(np.float32)
+    check_pyramid(zd, zt, synth.BF16, K, prm, tau, tokens=probe.tokens, label=f"draft limit K={K}")
+
+
 def test_pyramid_fast_path_full_size_stages():
     s1, s2 = synth.pyramid()
     prm = oracle.params_array(1.0, 0, 1.0, B=s1.B)
