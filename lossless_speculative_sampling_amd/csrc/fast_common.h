@@ -168,7 +168,7 @@ __host__ __device__ inline Layout layout(int B, int units, int nS) {
     L.chunks = o;   o += align256((size_t)B * nS * kChunks * sizeof(double));
     L.gen = o;      o += align256((size_t)units * sizeof(UnitRec));  // general-path unit results
     L.cache_gen = o; o += align256((size_t)units * sizeof(int32_t)); // cache rows for the general selection
-    L.div = o;      o += align256((size_t)units * (2 * nS + 1) * sizeof(double));  // fuzzy: partial and total divergences
+    L.div = o;      o += align256((size_t)units * (nS + 1) * sizeof(double));  // fuzzy: per-slice parts, then totals
     L.total = o;
     return L;
 }

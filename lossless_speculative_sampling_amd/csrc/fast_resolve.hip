@@ -1022,7 +1022,7 @@ __device__ __forceinline__ void decide_fuzzy(const FastArgs& f, int b) {
     const int K = a.K;
     const int lane = threadIdx.x & (kWave - 1);
     const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + (size_t)b * (K + 1);
-    const double* D = reinterpret_cast<const double*>(f.ws + f.L.div) + (size_t)f.units * 2 * f.nS +
+    const double* D = reinterpret_cast<const double*>(f.ws + f.L.div) + (size_t)f.units * f.nS +
                       (size_t)b * (K + 1);
     uint32_t st = 0;
     int acc = 1;
@@ -1100,7 +1100,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     __syncthreads();
     const double part = block_sum<double>(divergence_slice(f, sm, c0, two, vq, vp, dl, lt, trow, drow), sm.redd);
     double* parts = reinterpret_cast<double*>(f.ws + f.L.div);
-    if (t == 0) parts[(size_t)unit * 2 * f.nS + slice] = part;
+    if (t == 0) parts[(size_t)unit * f.nS + slice] = part;
     // the position's arrival (its nS workgroups), then the request's (its K positions)
     drain_stores();
     __syncthreads();
@@ -1113,10 +1113,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     __syncthreads();
     if (!sm.last) return;
     if (t < kWave) {
-        const double v = t < f.nS ? ldnt(&parts[(size_t)unit * 2 * f.nS + t]) : 0.0;
+        const double v = t < f.nS ? ldnt(&parts[(size_t)unit * f.nS + t]) : 0.0;
         const double Dj = wave_sum(v);  // fixed order: the same bits on every run
         if (t == 0) {
-            reinterpret_cast<double*>(f.ws + f.L.div)[(size_t)f.units * 2 * f.nS + unit] = Dj;
+            reinterpret_cast<double*>(f.ws + f.L.div)[(size_t)f.units * f.nS + unit] = Dj;
             if (a.out_div) a.out_div[(size_t)b * a.K + j] = (float)Dj;
         }
     }
