@@ -183,9 +183,10 @@ constexpr double kMarkSeen = 1e299;
 
 // The groups of 64 bins whose table entries need exps: those between the lower of a row's
 // cuts and its maximum (a compact list, ascending), and per row the groups wholly below its
-// cuts, whose entries are 0.  Groups above a row's maximum hold none of its elements.  (Wave 0;
-// the caller synchronises.)
-__device__ __forceinline__ void table_groups(ResSmem& sm, bool two) {
+// cuts, whose entries are 0.  Groups above a row's maximum hold none of its elements.  With
+// the slice's per-segment counts (segc, nullable), groups the slice holds none of in a row are
+// left out for that row.  (One wave; the caller synchronises.)
+__device__ __forceinline__ void table_groups(ResSmem& sm, bool two, const uint32_t (*segc)[kSegs] = nullptr) {
     const int lane = threadIdx.x & (kWave - 1);
     bool need = false, z0 = false, z1 = false;
     if (lane < kGroups) {
@@ -193,6 +194,7 @@ __device__ __forceinline__ void table_groups(ResSmem& sm, bool two) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             if (r == 1 && !two) break;
+            if (segc && segc[r][seg_of_group(lane)] == 0u) continue;  // none of row r's elements
             const uint32_t klow = max(sm.cut[r][0].key, sm.cut[r][1].key);
             const uint32_t kmax = key16(__float_as_uint(sm.rf[r].m) >> 16);
             if (ghi >= klow && glo <= kmax) need = true;
@@ -1049,6 +1051,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     __shared__ ResSmem sm;
     __shared__ DivList dl;
     __shared__ LogTab lt;
+    __shared__ uint32_t segc[2][kSegs];  // this slice's per-segment element counts of both rows
     const VerifyArgs& a = f.a;
     // placement as in the count kernel (request b on XCD b % 8); workgroup w of a request is
     // slice w % nS of drafted position w / nS
@@ -1070,6 +1073,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     if (t < kWCut) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->rq) + t);
     else if (t < kWFlag) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + (t - kWCut));
     else if (t < kWEnd) rec_word = ldnt(&part_of(f, unit, slice, t - kWFlag)->flags);
+    constexpr int kWSeg = 4 * kWave;  // threads [kWSeg, kWSeg + 2 kSegs): the segment counts
+    static_assert(kWEnd <= kWSeg && kWSeg + 2 * kSegs <= kThreads, "segment-count threads");
+    const int sr = (t - kWSeg) / kSegs, sg = (t - kWSeg) % kSegs;
+    const bool seg_thread = t >= kWSeg && t < kWSeg + 2 * kSegs && (sr == 0 || two);
+    const uint32_t seg_word = seg_thread ? ldnt(&part_of(f, unit, slice, sr)->seg_count[sg]) : 0u;
     const int c0 = slice * kSliceCols;
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)b * (a.K + 1) + j) * stride;
@@ -1088,12 +1096,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         sm.flags[t - kWFlag] = (t == kWFlag || two) ? rec_word : 0u;
     }
     if (t >= kWave && t < kWave + 6) sm.tie[(t - kWave) / 3][(t - kWave) % 3].off = kNoTie;
+    if (seg_thread) segc[sr][sg] = seg_word;
     __syncthreads();
     if (t < 2) {
         sm.inv[t][0] = 1.0 / sm.rf[t].S;
         sm.inv[t][1] = 1.0 / sm.rf[t].Z;
     }
-    if (t >= kWave && t < 2 * kWave) table_groups(sm, two);
+    if (t >= kWave && t < 2 * kWave) table_groups(sm, two, segc);
     __syncthreads();
     build_tables(sm, two, slice);
     slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);
