@@ -93,6 +93,7 @@ struct alignas(16) RowPart {  // one slice of one row, written by the count kern
     uint32_t s_bits;    // bf16 bits of the row at the draft token (0 without a token)
     uint32_t n_neginf;
     double S;           // sum of exp((z - m)/T) over the slice's finite elements
+    uint32_t groups[2]; // bit g (low word first): the slice holds elements in group g of 64 bins
     double seg_mass[kSegs];
     uint32_t seg_count[kSegs];
     uint32_t top_key[kTop];

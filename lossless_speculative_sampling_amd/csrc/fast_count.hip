@@ -391,7 +391,10 @@ __device__ __forceinline__ void publish_rows(const FastArgs& f, CountSmem& sm, i
         const int nsp = min((int)sm.n_sp[r], kSpecial);
         const double S = wave_sum(lane < kSegs ? sm.segm[r][lane] : 0.0);
         const uint32_t nfin = wave_sum(lane < kSegs ? sm.segc[r][lane] : 0u);
+        const uint64_t gm = __ballot(lane < kGroups && sm.segc[r][seg_of_group(lane)] != 0u);
         if (lane == 0) {
+            P->groups[0] = (uint32_t)gm;
+            P->groups[1] = (uint32_t)(gm >> 32);
             P->m = m[r];
             P->flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u) | (sm.rare[r] ? 4u : 0u);
             P->n_finite = nfin;

@@ -40,6 +40,7 @@ struct ResSmem {
     TieRole tie[2][3];             // [row][set boundary, top-k tie, top-p tie] this slice decides
     UnitCut cut[2][2];
     uint32_t flags[2];             // this slice's RowPart flags of each row
+    uint32_t grp[2][2];            // this slice's groups of each row (RowPart::groups)
     int eff[2][2];                 // this slice's id cut at each cut key (V-1 all, -1 none)
     uint64_t nth_scan[kWaves][4];  // per-wave match counts of the owned cut keys
     int32_t scan[kWaves + 1];
@@ -184,9 +185,9 @@ constexpr double kMarkSeen = 1e299;
 // The groups of 64 bins whose table entries need exps: those between the lower of a row's
 // cuts and its maximum (a compact list, ascending), and per row the groups wholly below its
 // cuts, whose entries are 0.  Groups above a row's maximum hold none of its elements.  With
-// the slice's per-segment counts (segc, nullable), groups the slice holds none of in a row are
-// left out for that row.  (One wave; the caller synchronises.)
-__device__ __forceinline__ void table_groups(ResSmem& sm, bool two, const uint32_t (*segc)[kSegs] = nullptr) {
+// sm.grp loaded (slice_groups), groups the slice holds none of in a row are left out for that
+// row.  (One wave; the caller synchronises.)
+__device__ __forceinline__ void table_groups(ResSmem& sm, bool two, bool slice_groups) {
     const int lane = threadIdx.x & (kWave - 1);
     bool need = false, z0 = false, z1 = false;
     if (lane < kGroups) {
@@ -194,7 +195,8 @@ __device__ __forceinline__ void table_groups(ResSmem& sm, bool two, const uint32
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             if (r == 1 && !two) break;
-            if (segc && segc[r][seg_of_group(lane)] == 0u) continue;  // none of row r's elements
+            const uint32_t gw = sm.grp[r][lane >> 5];
+            if (slice_groups && !((gw >> (lane & 31)) & 1u)) continue;  // none of row r's elements
             const uint32_t klow = max(sm.cut[r][0].key, sm.cut[r][1].key);
             const uint32_t kmax = key16(__float_as_uint(sm.rf[r].m) >> 16);
             if (ghi >= klow && glo <= kmax) need = true;
@@ -671,8 +673,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     // flags and the draw, one 32-bit word per thread, issued before the decision's own load
     static_assert(offsetof(UnitFast, rp) == offsetof(UnitFast, rq) + sizeof(RowFinal), "rq, rp adjacent");
     constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
-    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWDraw = kWFlag + 2, kRecWords = 64;
-    static_assert(kWDraw + 2 <= kRecWords, "one unit's words in a wave");
+    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWDraw = kWFlag + 2, kWGrp = kWDraw + 2, kRecWords = 64;
+    static_assert(kWGrp + 4 <= kRecWords, "one unit's words in a wave");
     const bool pre = (a.K + 1) * kRecWords <= kThreads;  // otherwise loaded once k is known
     const int pj = (int)threadIdx.x / kRecWords, pw = (int)threadIdx.x % kRecWords;
     uint32_t pre_word = 0u;
@@ -682,7 +684,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         if (pw < kWCut) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->rq) + pw);
         else if (pw < kWFlag) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->cut[0][0]) + (pw - kWCut));
         else if (pw < kWDraw) pre_word = ldnt(&part_of(f, uj, w >> 1, pw - kWFlag)->flags);
-        else if (pw < kWDraw + 2) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->u_res) + (pw - kWDraw));
+        else if (pw < kWGrp) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->u_res) + (pw - kWDraw));
+        else if (pw < kWGrp + 4) pre_word = ldnt(&part_of(f, uj, w >> 1, (pw - kWGrp) >> 1)->groups[(pw - kWGrp) & 1]);
     }
     // the request's decision and this unit's cache flag, loaded together
     static_assert(sizeof(ReqFast) == 16, "one 16-byte record");
@@ -721,13 +724,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     uint32_t rec_word = pre_word;
     int rec_slot = pj == k ? pw : -1;
     if (!pre) {
-        rec_slot = (int)threadIdx.x < kWDraw + 2 ? (int)threadIdx.x : -1;
+        rec_slot = (int)threadIdx.x < kWGrp + 4 ? (int)threadIdx.x : -1;
         const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + unit;
         const int x = (int)threadIdx.x;
         if (x < kWCut) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->rq) + x);
         else if (x < kWFlag) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + (x - kWCut));
         else if (x < kWDraw) rec_word = ldnt(&part_of(f, unit, slice, x - kWFlag)->flags);
-        else if (x < kWDraw + 2) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->u_res) + (x - kWDraw));
+        else if (x < kWGrp) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->u_res) + (x - kWDraw));
+        else if (x < kWGrp + 4) rec_word = ldnt(&part_of(f, unit, slice, (x - kWGrp) >> 1)->groups[(x - kWGrp) & 1]);
     }
     // (without a draft row the second set re-reads the target and goes unused: unconditional
     // loads keep the waits above exact)
@@ -744,8 +748,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
             reinterpret_cast<uint32_t*>(&sm.cut[0][0])[x] = keep_all ? (x % kCut == 1 ? 0xFFFFFFFFu : 0u) : rec_word;
         } else if (rec_slot < kWDraw) {
             sm.flags[rec_slot - kWFlag] = (rec_slot == kWFlag || two) ? rec_word : 0u;
-        } else {
+        } else if (rec_slot < kWGrp) {
             reinterpret_cast<uint32_t*>(&sm.u_res)[rec_slot - kWDraw] = rec_word;
+        } else {
+            sm.grp[(rec_slot - kWGrp) >> 1][(rec_slot - kWGrp) & 1] = rec_word;  // row 1's unread without two
         }
     }
     if (threadIdx.x >= kWave && threadIdx.x < kWave + 6) sm.tie[(threadIdx.x - kWave) / 3][(threadIdx.x - kWave) % 3].off = kNoTie;
@@ -755,7 +761,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         sm.inv[r][0] = 1.0 / sm.rf[r].S;
         sm.inv[r][1] = 1.0 / sm.rf[r].Z;
     }
-    if (threadIdx.x >= kWave && threadIdx.x < 2 * kWave) table_groups(sm, two);
+    if (threadIdx.x >= kWave && threadIdx.x < 2 * kWave) table_groups(sm, two, true);
     __syncthreads();  // 1 / S and 1 / Z, the group list
     // the tables need no column of the slice: they are built while its loads are in flight
     build_tables(sm, two, slice);
@@ -1051,7 +1057,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     __shared__ ResSmem sm;
     __shared__ DivList dl;
     __shared__ LogTab lt;
-    __shared__ uint32_t segc[2][kSegs];  // this slice's per-segment element counts of both rows
     const VerifyArgs& a = f.a;
     // placement as in the count kernel (request b on XCD b % 8); workgroup w of a request is
     // slice w % nS of drafted position w / nS
@@ -1065,19 +1070,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int unit = b * (a.K + 1) + j;
     const bool two = !f.uniform;
     constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
-    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWEnd = kWFlag + 2;
+    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWGrp = kWFlag + 2, kWEnd = kWGrp + 4;
     static_assert(kWEnd <= kThreads, "one record word per thread");
     const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + unit;
     const int t = (int)threadIdx.x;
     uint32_t rec_word = 0u;
     if (t < kWCut) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->rq) + t);
     else if (t < kWFlag) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + (t - kWCut));
-    else if (t < kWEnd) rec_word = ldnt(&part_of(f, unit, slice, t - kWFlag)->flags);
-    constexpr int kWSeg = 4 * kWave;  // threads [kWSeg, kWSeg + 2 kSegs): the segment counts
-    static_assert(kWEnd <= kWSeg && kWSeg + 2 * kSegs <= kThreads, "segment-count threads");
-    const int sr = (t - kWSeg) / kSegs, sg = (t - kWSeg) % kSegs;
-    const bool seg_thread = t >= kWSeg && t < kWSeg + 2 * kSegs && (sr == 0 || two);
-    const uint32_t seg_word = seg_thread ? ldnt(&part_of(f, unit, slice, sr)->seg_count[sg]) : 0u;
+    else if (t < kWGrp) rec_word = ldnt(&part_of(f, unit, slice, t - kWFlag)->flags);
+    else if (t < kWEnd && (t < kWGrp + 2 || two)) rec_word = ldnt(&part_of(f, unit, slice, (t - kWGrp) >> 1)->groups[(t - kWGrp) & 1]);
     const int c0 = slice * kSliceCols;
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)b * (a.K + 1) + j) * stride;
@@ -1092,17 +1093,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         const int y = t - kWCut;
         const bool keep_all = !two && y >= 2 * kCut;  // no draft row: UnitCut{0, -1, 0, 0}
         reinterpret_cast<uint32_t*>(&sm.cut[0][0])[y] = keep_all ? (y % kCut == 1 ? 0xFFFFFFFFu : 0u) : rec_word;
-    } else if (t < kWEnd) {
+    } else if (t < kWGrp) {
         sm.flags[t - kWFlag] = (t == kWFlag || two) ? rec_word : 0u;
+    } else if (t < kWEnd) {
+        sm.grp[(t - kWGrp) >> 1][(t - kWGrp) & 1] = rec_word;
     }
     if (t >= kWave && t < kWave + 6) sm.tie[(t - kWave) / 3][(t - kWave) % 3].off = kNoTie;
-    if (seg_thread) segc[sr][sg] = seg_word;
     __syncthreads();
     if (t < 2) {
         sm.inv[t][0] = 1.0 / sm.rf[t].S;
         sm.inv[t][1] = 1.0 / sm.rf[t].Z;
     }
-    if (t >= kWave && t < 2 * kWave) table_groups(sm, two, segc);
+    if (t >= kWave && t < 2 * kWave) table_groups(sm, two, true);
     __syncthreads();
     build_tables(sm, two, slice);
     slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);
