@@ -696,7 +696,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     // outcome-cache rows the count kernel's candidate lists could not settle
     if (cgen) {
         CacheArgs c{a.draft, a.dtype, a.B, a.K, a.V, a.tokens, f.budget, f.fan, f.out_cache};
-        cache_row<1>(c, b, w, sm.u.cache.rs, sm.gst[0], sm.u.cache.cs);
+        cache_row<1>(c, b, w, f.fan.f[w], f.fan.off[w], sm.u.cache.rs, sm.gst[0], sm.u.cache.cs);
         __syncthreads();
     }
     const int mode = (int)req[0];

@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kRowThreads) void cache_build_kernel(CacheArgs a) {
     __shared__ RowShared sh;
     __shared__ RowStats st;
     __shared__ CacheShared cs;
-    cache_row(a, blockIdx.x / (a.K + 1), blockIdx.x % (a.K + 1), sh, st, cs);
+    const int k = blockIdx.x % (a.K + 1);
+    cache_row(a, blockIdx.x / (a.K + 1), k, a.fanout.f[k], a.fanout.off[k], sh, st, cs);
 }
 
 // saguaro_cache_lookup: a single workgroup loops over the requests and reduces the batch stats.

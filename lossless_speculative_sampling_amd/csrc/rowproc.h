@@ -629,10 +629,11 @@ struct CacheShared {
     int npicked;
 };
 
+// Fk, off: a.fanout's entries at depth k, read by the caller (a copy of the fan-out arrays
+// indexed by a runtime depth would live in private memory).
 template <int A = kRowAhead>
-__device__ inline void cache_row(const CacheArgs& a, int b, int k, RowShared& sh, RowStats& st, CacheShared& cs) {
-    const int Fk = a.fanout.f[k];
-    const int off = a.fanout.off[k];
+__device__ inline void cache_row(const CacheArgs& a, int b, int k, int Fk, int off, RowShared& sh, RowStats& st,
+                                 CacheShared& cs) {
     int32_t* out = a.out_cache + (size_t)b * a.budget + off;
     if (Fk <= 0) return;
     const size_t stride = (size_t)a.V * (a.dtype == SPEC_BF16 ? 2 : 4);
