@@ -597,7 +597,7 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
 // The general algorithm for one unit (out of line: a rare path).  The arguments come by
 // value so that no pointer to the kernel's own arguments escapes (which would move them to
 // scratch memory for the whole kernel).
-__device__ __noinline__ void fallback_unit(VerifyArgs a, int b, int j, ResSmem& sm) {
+__device__ __forceinline__ void fallback_unit(const VerifyArgs& a, int b, int j, ResSmem& sm) {
     unit_verify<1>(a, b, j, &sm.urec, sm.u.generic, sm.gst[0], sm.gst[1]);  // (no loads ahead: registers)
 }
 

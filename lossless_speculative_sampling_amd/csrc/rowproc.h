@@ -145,7 +145,7 @@ __device__ __forceinline__ double rs_prob_dw(const RowStats& s, float z, int i) 
 // Outputs: tau, the weight strictly above tau, the number of filtered elements at tau and the
 // weight still needed inside tau.
 template <bool MASS, int A = kRowAhead, typename Filter>
-__device__ void radix_select(const RowRef& r, const RowStats& st, Filter filt, double need, RowShared& sh,
+__device__ __forceinline__ void radix_select(const RowRef& r, const RowStats& st, Filter filt, double need, RowShared& sh,
                              uint32_t* tau_out, double* above_out, int* cnt_out, double* rem_out) {
     uint32_t prefix = 0, pmask = 0;
     double above = 0.0, rem = need;
@@ -205,7 +205,7 @@ __device__ void radix_select(const RowRef& r, const RowStats& st, Filter filt, d
 // The n-th (1-based) smallest id among elements with key == tau accepted by `filt`.
 // Threads own contiguous id segments, so a workgroup scan of their counts locates it.
 template <int A = kRowAhead, typename Filter>
-__device__ int nth_id_at_key(const RowRef& r, uint32_t tau, int n, Filter filt, RowShared& sh) {
+__device__ __forceinline__ int nth_id_at_key(const RowRef& r, uint32_t tau, int n, Filter filt, RowShared& sh) {
     const int seg = (r.V + blockDim.x - 1) / blockDim.x;
     const int lo = threadIdx.x * seg;
     const int hi = min(r.V, lo + seg);
@@ -267,7 +267,7 @@ __device__ __forceinline__ void weights_ahead(const RowRef& r, const RowRef& r2,
 }
 
 template <bool TWO, int A, typename Weight>
-__device__ int inverse_cdf_rows(const RowRef& r, const RowRef& r2, double x, Weight wfn, RowShared& sh,
+__device__ __forceinline__ int inverse_cdf_rows(const RowRef& r, const RowRef& r2, double x, Weight wfn, RowShared& sh,
                                 double* total_out) {
     const int seg = (r.V + blockDim.x - 1) / blockDim.x;
     const int lo = threadIdx.x * seg;
@@ -311,11 +311,11 @@ __device__ int inverse_cdf_rows(const RowRef& r, const RowRef& r2, double x, Wei
 }
 
 template <int A = kRowAhead, typename Weight>
-__device__ int inverse_cdf(const RowRef& r, double x, Weight wfn, RowShared& sh, double* total_out) {
+__device__ __forceinline__ int inverse_cdf(const RowRef& r, double x, Weight wfn, RowShared& sh, double* total_out) {
     return inverse_cdf_rows<false, A>(r, r, x, wfn, sh, total_out);
 }
 template <int A = kRowAhead, typename Weight>
-__device__ int inverse_cdf2(const RowRef& r, const RowRef& r2, double x, Weight wfn, RowShared& sh,
+__device__ __forceinline__ int inverse_cdf2(const RowRef& r, const RowRef& r2, double x, Weight wfn, RowShared& sh,
                             double* total_out) {
     return inverse_cdf_rows<true, A>(r, r2, x, wfn, sh, total_out);
 }
