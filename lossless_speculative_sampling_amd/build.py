@@ -37,16 +37,27 @@ def vgpr_spills(report: str) -> dict[str, int]:
     or lanes, the others lose the value.  The kernels here are written to fit their register
     budgets, so any spill is treated as a build error.
     """
-    spills: dict[str, int] = {}
+    return _per_kernel(report, "VGPRs Spill:")
+
+
+def scratch_users(report: str) -> dict[str, int]:
+    """Kernels with private (scratch) memory per lane: an array indexed at run time, a call's
+    stack frame or a spill.  Scratch has to be set up for every wave at launch, which the
+    latency-bound calls here pay for, and none of their paths needs it; any is a build error."""
+    return _per_kernel(report, "ScratchSize [bytes/lane]:")
+
+
+def _per_kernel(report: str, key: str) -> dict[str, int]:
+    found: dict[str, int] = {}
     name = None
     for line in report.splitlines():
         if "remark: Function Name:" in line:
             name = line.split("Function Name:")[1].split("[")[0].strip()
-        elif "remark:     VGPRs Spill:" in line and name is not None:
-            n = int(line.split("VGPRs Spill:")[1].split("[")[0])
+        elif "remark:" in line and key in line and name is not None:
+            n = int(line.split(key)[1].split("[")[0])
             if n:
-                spills[name] = n
-    return spills
+                found[name] = n
+    return found
 
 
 def build_library(verbose: bool = False) -> str:
@@ -64,6 +75,9 @@ def build_library(verbose: bool = False) -> str:
     spills = vgpr_spills(out)
     if spills:
         raise RuntimeError(f"vector registers spill to scratch in: {spills}")
+    scratch = scratch_users(out)
+    if scratch:
+        raise RuntimeError(f"kernels use scratch memory (bytes per lane): {scratch}")
     if verbose and msg.strip():
         print(msg)
     os.replace(tmp, LIB)

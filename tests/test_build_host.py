@@ -1,0 +1,23 @@
+"""The build's resource checks: spills and scratch memory are build errors (CPU only)."""
+from lossless_speculative_sampling_amd import build
+
+REPORT = """\
+k.hip:1:1: remark: Function Name: _Z3fooPf [-Rpass-analysis=kernel-resource-usage]
+k.hip:1:1: remark:     VGPRs: 64 [-Rpass-analysis=kernel-resource-usage]
+k.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+k.hip:1:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+k.hip:9:1: remark: Function Name: _Z3barPf [-Rpass-analysis=kernel-resource-usage]
+k.hip:9:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]
+k.hip:9:1: remark:     ScratchSize [bytes/lane]: 168 [-Rpass-analysis=kernel-resource-usage]
+k.hip:9:1: remark:     VGPRs Spill: 3 [-Rpass-analysis=kernel-resource-usage]
+"""
+
+
+def test_spills_and_scratch_are_reported_per_kernel():
+    assert build.vgpr_spills(REPORT) == {"_Z3barPf": 3}
+    assert build.scratch_users(REPORT) == {"_Z3barPf": 168}
+
+
+def test_clean_report_has_no_findings():
+    clean = "\n".join(l for l in REPORT.splitlines() if "_Z3bar" not in l and "k.hip:9" not in l)
+    assert build.vgpr_spills(clean) == {} and build.scratch_users(clean) == {}
