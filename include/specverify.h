@@ -155,6 +155,9 @@ size_t spec_workspace_bytes(int B, int K, int V);
  *   out_resid_mass  [B] float: sum (q_k - p_k)+ when k < K, else 0 (nullable)
  *   out_status      [B] uint32 status bits (nullable)
  *   workspace       >= spec_workspace_bytes(B, K, V) bytes of device memory
+ * Paths: bf16 logits with V % 8 == 0, 2048 <= V <= 262144, 16-byte aligned rows and K <= 63
+ * take the exact-count path (two launches); every other shape takes the general path (one
+ * workgroup per position).  Both give the same outputs.
  * Returns SPEC_OK or a negative SPEC_E* code. */
 int spec_verify(const void* draft_logits, int draft_rows, const void* target_logits, int dtype, int B, int K,
                 int V, const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,

@@ -47,6 +47,35 @@ def scratch_users(report: str) -> dict[str, int]:
     return _per_kernel(report, "ScratchSize [bytes/lane]:")
 
 
+# kernels whose resource report must be present (a missing report would let a spill through)
+EXPECTED_KERNELS = ("fast_count_kernel", "fast_resolve_kernel", "fast_diverge_kernel", "generic_unit_kernel",
+                    "finalize_kernel", "cache_lookup_kernel", "signpost_kernel")
+
+
+def report_problems(report: str) -> list[str]:
+    """What the compiler's resource report lacks: no per-kernel remarks at all, a kernel without
+    its spill or scratch line, or an expected kernel without a report."""
+    names, seen = [], {}
+    name = None
+    for line in report.splitlines():
+        if "remark: Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+            names.append(name)
+            seen[name] = set()
+        elif "remark:" in line and name is not None:
+            for key in ("VGPRs Spill:", "ScratchSize [bytes/lane]:"):
+                if key in line:
+                    seen[name].add(key)
+    if not names:
+        return ["no kernel-resource-usage remarks in the compiler output"]
+    out = [f"{n}: no '{k}' line" for n in names for k in ("VGPRs Spill:", "ScratchSize [bytes/lane]:")
+           if k not in seen[n]]
+    for k in EXPECTED_KERNELS:
+        if not any(k in n for n in names):
+            out.append(f"no resource report for {k}")
+    return out
+
+
 def _per_kernel(report: str, key: str) -> dict[str, int]:
     found: dict[str, int] = {}
     name = None
@@ -72,6 +101,9 @@ def build_library(verbose: bool = False) -> str:
     msg = "\n".join(l for l in out.splitlines() if noise not in l and "remark:" not in l and not l.startswith(" "))
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msg}")
+    problems = report_problems(out)
+    if problems:
+        raise RuntimeError("kernel resource report incomplete: " + "; ".join(problems[:8]))
     spills = vgpr_spills(out)
     if spills:
         raise RuntimeError(f"vector registers spill to scratch in: {spills}")

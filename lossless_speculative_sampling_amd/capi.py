@@ -114,6 +114,55 @@ def dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported logit dtype {t.dtype}")
 
 
+# ---- argument checks: every shape and dtype the C ABI assumes, so that a wrong tensor raises here
+# instead of being read past its end by the library ----
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _int32(name: str, t: Optional[torch.Tensor], shape: tuple):
+    _need(t is not None, f"{name} is required")
+    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _params(params: torch.Tensor, B: int):
+    _int32("params", params, (B, 3))
+
+
+def _logits(name: str, t: torch.Tensor, dims: int = 3) -> int:
+    _need(t.dim() == dims, f"{name} must be {dims}-D, got shape {tuple(t.shape)}")
+    _need(all(n > 0 for n in t.shape), f"{name} has an empty dimension: {tuple(t.shape)}")
+    return dtype_code(t)
+
+
+def _verify_inputs(draft: Optional[torch.Tensor], target: torch.Tensor, K: int, params: torch.Tensor,
+                   tokens: torch.Tensor, draft_rows=None) -> int:
+    code = _logits("target", target)
+    B, rows, V = target.shape
+    _need(K >= 1 and rows == K + 1, f"target must hold K + 1 = {K + 1} rows per request, got {rows}")
+    if draft is not None:
+        _need(_logits("draft", draft) == code, "draft and target must have the same dtype")
+        _need(draft.shape[0] == B and draft.shape[2] == V, f"draft {tuple(draft.shape)} does not match target "
+                                                           f"{tuple(target.shape)}")
+        allowed = (K, K + 1) if draft_rows is None else (draft_rows,)
+        _need(draft.shape[1] in allowed, f"draft must hold {' or '.join(map(str, allowed))} rows, got {draft.shape[1]}")
+    _params(params, B)
+    _int32("tokens", tokens, (B, K))
+    return code
+
+
+def _verify_out(out, B: int):
+    for name in ("k", "tstar", "status"):
+        _int32(f"out.{name}", getattr(out, name), (B,))
+    _need(out.resid_mass.dtype == torch.float32 and tuple(out.resid_mass.shape) == (B,), "out.resid_mass must be float32 [B]")
+
+
+def _workspace(ws: torch.Tensor):
+    _need(ws.dtype == torch.uint8 and ws.dim() == 1, "workspace must be a 1-D uint8 tensor")
+
+
 def spec_workspace_bytes(B: int, K: int, V: int) -> int:
     return int(load().cdll.spec_workspace_bytes(B, K, V))
 
@@ -149,6 +198,8 @@ def spec_verify(draft: Optional[torch.Tensor], target: torch.Tensor, K: int, par
     """draft [B][Kd][V] and target [B][K+1][V] device logits; tokens [B][K] int32 (in, or out under
     SPEC_SAMPLE_DRAFT).  With SPEC_UNIFORM_DRAFT draft may be None.  Returns the outputs (allocated
     here unless `out` is given)."""
+    _need(draft is not None or bool(flags & SPEC_UNIFORM_DRAFT), "draft logits are required without SPEC_UNIFORM_DRAFT")
+    code = _verify_inputs(draft, target, K, params, tokens)
     B, _, V = target.shape
     Kd = draft.shape[1] if draft is not None else K
     dev = target.device
@@ -156,9 +207,11 @@ def spec_verify(draft: Optional[torch.Tensor], target: torch.Tensor, K: int, par
         out = VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                         torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                         tokens)
+    _verify_out(out, B)
     if workspace is None:
         workspace = new_workspace(B, K, V, dev)
-    rc = load().cdll.spec_verify(_ptr(draft), Kd, _ptr(target), dtype_code(target), B, K, V, _ptr(params), F,
+    _workspace(workspace)
+    rc = load().cdll.spec_verify(_ptr(draft), Kd, _ptr(target), code, B, K, V, _ptr(params), F,
                                  ctypes.c_float(C), _ptr(tokens), seed, round_, flags, _ptr(out.k), _ptr(out.tstar),
                                  _ptr(out.resid_mass), _ptr(out.status), _ptr(workspace), workspace.numel(),
                                  _stream(stream))
@@ -169,7 +222,10 @@ def spec_verify(draft: Optional[torch.Tensor], target: torch.Tensor, K: int, par
 
 def saguaro_downweight(draft: torch.Tensor, K: int, params: torch.Tensor, F: int, C: float, want_probs=False,
                        stream=None):
+    _logits("draft", draft)
     B, Kd, V = draft.shape
+    _need(1 <= K <= Kd, f"K = {K} must lie in [1, {Kd}] (draft rows)")
+    _params(params, B)
     dev = draft.device
     ids = torch.empty((B, K, max(F, 1)), dtype=torch.int32, device=dev)
     Z = torch.empty((B, K), dtype=torch.float32, device=dev)
@@ -189,7 +245,10 @@ def saguaro_fanout(K: int, budget: int, a: float, r: float) -> list[int]:
 
 def saguaro_cache_build(draft: torch.Tensor, K: int, tokens: torch.Tensor, budget: int, a: float, r: float,
                         stream=None):
+    _logits("draft", draft)
     B, Kd, V = draft.shape
+    _need(K >= 1 and Kd == K + 1, f"draft must hold K + 1 = {K + 1} rows per request, got {Kd}")
+    _int32("tokens", tokens, (B, K))
     fan = (ctypes.c_int32 * (K + 1))()
     cache = torch.empty((B, max(budget, 1)), dtype=torch.int32, device=draft.device)
     rc = load().cdll.saguaro_cache_build(_ptr(draft), dtype_code(draft), B, K, V, _ptr(tokens), budget, a, r,
@@ -204,20 +263,23 @@ def saguaro_verify_cache(draft: torch.Tensor, target: torch.Tensor, K: int, para
                          cache: Optional[torch.Tensor] = None, stream=None):
     """spec_verify + saguaro_cache_build in one pass; draft [B][K+1][V].  Returns (VerifyOut,
     cache [B][budget], fan-out list)."""
+    code = _verify_inputs(draft, target, K, params, tokens, draft_rows=K + 1)
     B, Kd, V = draft.shape
-    if Kd != K + 1:
-        raise ValueError("draft must hold K + 1 rows")
     dev = draft.device
     if out is None:
         out = VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                         torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                         tokens)
+    _verify_out(out, B)
     if workspace is None:
         workspace = new_workspace(B, K, V, dev)
+    _workspace(workspace)
     if cache is None:
         cache = torch.empty((B, max(budget, 1)), dtype=torch.int32, device=dev)
+    _need(cache.dtype == torch.int32 and cache.dim() == 2 and cache.shape[0] == B and cache.shape[1] >= budget,
+          f"cache must be int32 [{B}][>= {budget}]")
     fan = (ctypes.c_int32 * (K + 1))()
-    rc = load().cdll.saguaro_verify_cache(_ptr(draft), _ptr(target), dtype_code(draft), B, K, V, _ptr(params), F,
+    rc = load().cdll.saguaro_verify_cache(_ptr(draft), _ptr(target), code, B, K, V, _ptr(params), F,
                                           ctypes.c_float(C), _ptr(tokens), seed, round_, flags, budget, a, r,
                                           ctypes.cast(fan, _P), _ptr(out.k), _ptr(out.tstar), _ptr(out.resid_mass),
                                           _ptr(out.status), _ptr(cache), _ptr(workspace), workspace.numel(),
@@ -230,7 +292,24 @@ def saguaro_verify_cache(draft: torch.Tensor, target: torch.Tensor, K: int, para
 def saguaro_cache_lookup(mode: int, cache: torch.Tensor, fanout_or_shape, K: int, B: int, k: torch.Tensor,
                          tstar: torch.Tensor, stream=None):
     dev = cache.device
-    fs = (ctypes.c_int32 * len(fanout_or_shape))(*[int(x) for x in fanout_or_shape])
+    fs_list = [int(x) for x in fanout_or_shape]
+    _need(cache.dtype == torch.int32, "cache must be int32")
+    if mode == 0:
+        _need(len(fs_list) == K + 1, f"mode 0 takes K + 1 = {K + 1} fan-out entries, got {len(fs_list)}")
+        _need(cache.dim() == 2 and cache.shape[0] == B, f"cache must be [{B}][budget]")
+        _need(cache.shape[1] >= sum(fs_list), f"cache holds {cache.shape[1]} slots, the fan-out needs {sum(fs_list)}")
+        per = 1
+    elif mode == 1:
+        _need(len(fs_list) == 2, "mode 1 takes {kappa, gamma}")
+        _need(cache.numel() == B * fs_list[0] * fs_list[1], "branches must hold B * kappa * gamma tokens")
+        per = fs_list[0]  # k and t* of every chain
+    else:
+        raise ValueError(f"unknown lookup mode {mode}")
+    _need(k.numel() == B * per, f"k must hold {B * per} entries")
+    _need(tstar.numel() == B * per, f"tstar must hold {B * per} entries")
+    _need(k.dtype == torch.int32, "k must be int32")
+    _need(tstar.dtype == torch.int32, "tstar must be int32")
+    fs = (ctypes.c_int32 * len(fs_list))(*fs_list)
     slot = torch.empty(B, dtype=torch.int32, device=dev)
     hit = torch.empty(B, dtype=torch.uint8, device=dev)
     batch = torch.empty(2, dtype=torch.int32, device=dev)
@@ -243,6 +322,8 @@ def saguaro_cache_lookup(mode: int, cache: torch.Tensor, fanout_or_shape, K: int
 def saguaro_backup_plan(hit: torch.Tensor, batch: torch.Tensor, b_star: int, stream=None):
     """(use_backup [B] int32, switch [1] int32) on the device: the batch-aware random-token fallback."""
     B = hit.shape[0]
+    _need(hit.dtype == torch.uint8 and hit.dim() == 1, "hit must be uint8 [B]")
+    _int32("batch", batch, (2,))
     use = torch.empty(B, dtype=torch.int32, device=hit.device)
     sw = torch.empty(1, dtype=torch.int32, device=hit.device)
     rc = load().cdll.saguaro_backup_plan(B, _ptr(hit), _ptr(batch), b_star, _ptr(use), _ptr(sw), _stream(stream))
@@ -266,17 +347,19 @@ def mirror_signposts(logits: torch.Tensor, kappa: int, want_bf16: bool = False,
                      workspace: Optional[torch.Tensor] = None, out=None, stream=None):
     """Early-exit signposts of logits [B][V]: (ids [B][kappa] int32, log p~ [B][kappa] float32,
     log p~ as bf16 bits [B][kappa] int16 or None, status [B] int32)."""
+    code = _logits("logits", logits, dims=2)
     B, V = logits.shape
     dev = logits.device
     if workspace is None:
         workspace = new_signpost_workspace(B, V, kappa, dev)
+    _workspace(workspace)
     if out is None:
         out = (torch.empty((B, kappa), dtype=torch.int32, device=dev),
                torch.empty((B, kappa), dtype=torch.float32, device=dev),
                torch.empty((B, kappa), dtype=torch.int16, device=dev) if want_bf16 else None,
                torch.empty(B, dtype=torch.int32, device=dev))
     ids, lp, lp16, st = out
-    rc = load().cdll.mirror_signposts(_ptr(logits), dtype_code(logits), B, V, kappa, _ptr(ids), _ptr(lp), _ptr(lp16),
+    rc = load().cdll.mirror_signposts(_ptr(logits), code, B, V, kappa, _ptr(ids), _ptr(lp), _ptr(lp16),
                                       _ptr(st), _ptr(workspace), workspace.numel(), _stream(stream))
     _check("mirror_signposts", rc)
     return out
@@ -285,8 +368,15 @@ def mirror_signposts(logits: torch.Tensor, kappa: int, want_bf16: bool = False,
 def mirror_tree_lookup(tokens: torch.Tensor, parents: torch.Tensor, path: torch.Tensor, k: torch.Tensor,
                        tstar: torch.Tensor, stream=None):
     """Reuse node of the committed prefix in each request's draft tree [B][N]: (node [B], hit [B], batch [2])."""
+    _need(tokens.dim() == 2, "tokens must be [B][N]")
     B, N = tokens.shape
+    _int32("tokens", tokens, (B, N))
+    _int32("parents", parents, (B, N))
+    _need(path.dim() == 2 and path.shape[0] == B, "path must be [B][gamma]")
     gamma = path.shape[1]
+    _int32("path", path, (B, gamma))
+    _int32("k", k, (B,))
+    _int32("tstar", tstar, (B,))
     dev = tokens.device
     node = torch.empty(B, dtype=torch.int32, device=dev)
     hit = torch.empty(B, dtype=torch.uint8, device=dev)
@@ -301,16 +391,20 @@ def pyramid_verify(draft: Optional[torch.Tensor], verifier: torch.Tensor, K: int
                    tau: torch.Tensor, tokens: torch.Tensor, F: int = 0, C: float = 1.0, seed: int = 0, round_: int = 0,
                    flags: int = 0, want_div: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """Fuzzy (PyramidSD) verification of one stage: (VerifyOut, divergences [B][K] or None)."""
+    _need(draft is not None or bool(flags & SPEC_UNIFORM_DRAFT), "draft logits are required without SPEC_UNIFORM_DRAFT")
+    code = _verify_inputs(draft, verifier, K, params, tokens)
     B, _, V = verifier.shape
+    _need(tau.dtype == torch.float32 and tuple(tau.shape) == (B,), "tau must be float32 [B]")
     Kd = draft.shape[1] if draft is not None else K
     dev = verifier.device
     if workspace is None:
         workspace = new_workspace(B, K, V, dev)
+    _workspace(workspace)
     out = VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                     torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
                     tokens)
     div = torch.zeros((B, K), dtype=torch.float32, device=dev) if want_div else None
-    rc = load().cdll.pyramid_verify(_ptr(draft), Kd, _ptr(verifier), dtype_code(verifier), B, K, V, _ptr(params), F,
+    rc = load().cdll.pyramid_verify(_ptr(draft), Kd, _ptr(verifier), code, B, K, V, _ptr(params), F,
                                     ctypes.c_float(C), _ptr(tau), _ptr(tokens), seed, round_, flags, _ptr(out.k),
                                     _ptr(out.tstar), _ptr(out.resid_mass), _ptr(out.status), _ptr(div),
                                     _ptr(workspace), workspace.numel(), _stream(stream))

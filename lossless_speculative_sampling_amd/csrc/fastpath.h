@@ -57,6 +57,8 @@ struct FastPlan {
 };
 
 FastPlan fast_plan(int B, int K, int V);
+// bf16 rows, V % 8 == 0 and V >= 2048, 16-byte aligned rows, at most 16 slices per row and
+// K + 1 <= 64 positions per request (longer drafts take the general path).
 bool fast_path_applies(const VerifyArgs& a);
 // Fuzzy acceptance (a.tau set) on this path: not the assisted variant, at most 63 positions.
 bool fast_fuzzy_applies(const VerifyArgs& a);

@@ -33,6 +33,8 @@ bool fast_path_applies(const VerifyArgs& a) {
     // drafted tokens are sampled here only from the uniform draft (random-token backup)
     if (a.dtype != SPEC_BF16 || ((a.flags & SPEC_SAMPLE_DRAFT) && !(a.flags & SPEC_UNIFORM_DRAFT))) return false;
     if (a.V % 8 != 0 || a.V < 2048) return false;
+    // the request decision reads one unit per lane of a single wave: K + 1 <= 64 positions
+    if (a.K + 1 > kWave) return false;
     if ((reinterpret_cast<uintptr_t>(a.draft) & 15) || (reinterpret_cast<uintptr_t>(a.target) & 15)) return false;
     const int nS = (a.V + kSliceCols - 1) / kSliceCols;
     return nS * kTop <= kMergeCap;  // every slice's candidate list fits the merge buffer

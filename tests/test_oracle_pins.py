@@ -882,3 +882,134 @@ def test_fuzzy_law_exact_enumeration(assisted):
     keys = set(law) | set(want)
     assert max(abs(law.get(x, 0.0) - want.get(x, 0.0)) for x in keys) < 1e-9
     assert abs(sum(law.values()) - 1.0) < 1e-9
+
+
+# ------------------------------------------------------------------------------------------
+# The uniforms' counter layout, the near-tie predicates and the readings for degenerate
+# inputs, each against values worked out by hand from their definitions
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,round_,B,K", [
+    (0xC0FFEE03, 0, 5, 4),
+    (0x5EED0001, 17, 3, 6),
+    ((1 << 64) - 3, (1 << 40) + 5, 2, 2),
+])
+def test_uniforms_counter_layout_against_numpy_philox(seed, round_, B, K):
+    """U[b, j, w] is word w of Philox4x64-10 with counter (round, b, j, 0) and key (seed, 0),
+    mapped to ((w >> 12) + 1/2) 2^-52; numpy's generator supplies the words."""
+    U = oracle.uniforms(seed, round_, B, K)
+    for b in range(B):
+        for j in range(K + 1):
+            words = _numpy_philox_block([round_, b, j, 0], [seed, 0])
+            for lane in range(3):
+                expect = (float(int(words[lane]) >> 12) + 0.5) * 2.0 ** -52
+                assert U[b, j, lane] == expect, (b, j, lane)
+
+
+def test_near_nucleus_flag_band():
+    """The nucleus flag is raised exactly when the cut's running mass lies within 1e-9 of the
+    total of top_p * S, on either side of the token that reaches it."""
+    # four equal masses: two tokens reach top_p * S = 2 exactly
+    _, _, near, n = oracle.process_row(np.zeros(4), 1.0, 0, 0.5)
+    assert near and n == 2
+    # the next float32 above 0.5: the target lies 2^-22 past the second breakpoint
+    tp = float(np.nextafter(np.float32(0.5), np.float32(1.0)))
+    _, _, near, n = oracle.process_row(np.zeros(4), 1.0, 0, tp)
+    assert not near and n == 3
+    # above the target: the first token heavier by d, masses (1, e^-d, e^-d, e^-d); the two
+    # leading tokens overshoot top_p * S by d/2 (in units of the leading mass)
+    for d, flagged in ((2e-10, True), (2e-8, False)):
+        z = np.array([np.log1p(d), 0.0, 0.0, 0.0])
+        _, _, near, n = oracle.process_row(z, 1.0, 0, 0.5)
+        assert n == 2 and near == flagged, (d, near, n)
+    # below the target: masses (1, 1/2 + d, 1/2); one token falls short of top_p * S by d/2
+    for d, flagged in ((2e-10, True), (2e-8, False)):
+        z = np.array([np.log(2.0), np.log1p(2 * d), 0.0])
+        _, _, near, n = oracle.process_row(z, 1.0, 0, 0.5)
+        assert n == 2 and near == flagged, (d, near, n)
+
+
+def _bonus_draw(v):
+    """K = 1, V = 4, draft row = target row = four equal logits, drafted token 0 (accepted for
+    any u < 1): the bonus token is the inverse CDF of q_1 = (1/4, 1/4, 1/4, 1/4) at v."""
+    z = np.zeros((1, 2, 4), np.float32)
+    U = np.full((1, 2, 3), 0.5)
+    U[0, 1, 1] = v
+    return oracle.verify(z[:, :1], z, oracle.FP32, 1, oracle.params_array(1.0, 0, 1.0, B=1), tokens=[[0]], U=U)
+
+
+def test_near_cdf_flag_band():
+    # v W lands exactly on the breakpoint after token 1: the draw is token 2, flagged
+    r = _bonus_draw(0.5)
+    assert r.k[0] == 1 and r.t[0] == 2 and r.flags[0] & oracle.FL_NEAR_CDF
+    r = _bonus_draw(0.5 + 2e-10)
+    assert r.t[0] == 2 and r.flags[0] & oracle.FL_NEAR_CDF
+    # outside the 1e-9 band on either side: no flag, the draws on both sides of the breakpoint
+    r = _bonus_draw(0.5 + 5e-9)
+    assert r.t[0] == 2 and not r.flags[0] & oracle.FL_NEAR_CDF
+    r = _bonus_draw(0.5 - 5e-9)
+    assert r.t[0] == 1 and not r.flags[0] & oracle.FL_NEAR_CDF
+
+
+def test_empty_residual_draws_from_the_target():
+    """Reading R7: a rejection whose residual (q - p')+ is empty draws t* from q_k itself.  Draft
+    and target rows agree (top-k 2 keeps q = p = (0.6, 0.4, 0, 0)); the drafted token 2 lies
+    outside both supports, so u p(2) < q(2) fails (reading R8) and W = 0."""
+    z = np.log(np.array([0.6, 0.4, 0.05, 0.05], np.float64)).astype(np.float32)
+    rows = np.stack([z, z])[None]
+    prm = oracle.params_array(1.0, 2, 1.0, B=1)
+    for v, t in ((0.3, 0), (0.7, 1)):
+        U = np.full((1, 2, 3), 0.5)
+        U[0, 0, 1] = v
+        r = oracle.verify(rows[:, :1], rows, oracle.FP32, 1, prm, tokens=[[2]], U=U)
+        assert r.k[0] == 0 and r.t[0] == t and r.W[0] == 0.0
+        assert r.status[0] == oracle.ST_EMPTY_RESIDUAL | oracle.ST_OUTSIDE_DRAFT_SUPPORT
+
+
+def test_bad_parameters_reject_the_request():
+    """Reading R20: a negative, infinite or NaN temperature, or top_p <= 0, yields k = 0,
+    t* = -1 and the bad-parameter status alone; the other requests of the batch are unaffected."""
+    rng = np.random.default_rng(5)
+    B, K, V = 7, 2, 16
+    zt = rng.normal(0, 1, (B, K + 1, V)).astype(np.float32)
+    zd = zt[:, :K] + rng.normal(0, 0.3, (B, K, V)).astype(np.float32)
+    T = np.array([-1.0, np.nan, np.inf, 1.0, 1.0, 1.0, 0.0], np.float32)
+    tp = np.array([1.0, 1.0, 1.0, 0.0, -0.5, 0.9, 1.0], np.float32)
+    prm = oracle.params_array(T, 0, tp)
+    r = oracle.verify(zd, zt, oracle.FP32, K, prm, tokens=np.zeros((B, K), np.int32), seed=3)
+    for b in range(5):
+        assert r.status[b] == oracle.ST_BAD_PARAM and r.k[b] == 0 and r.t[b] == -1
+    for b in (5, 6):
+        assert not r.status[b] & oracle.ST_BAD_PARAM and r.t[b] >= 0
+        one = oracle.verify(zd[b:b + 1], zt[b:b + 1], oracle.FP32, K, prm[b:b + 1],
+                            tokens=np.zeros((1, K), np.int32), U=oracle.uniforms(3, 0, B, K)[b:b + 1])
+        assert (one.k[0], one.t[0], one.status[0]) == (r.k[b], r.t[b], r.status[b])
+
+
+def test_degenerate_downweight_leaves_the_row():
+    """Reading R21: with C = 0 and the downweighted set holding every token with mass, the
+    normaliser 1 - (1 - C) P_S is 0; the row is verified undownweighted, with its status bit.
+    Draft p = (0.6, 0.4, 0, 0), target q = (0.3, 0.7, 0, 0) under top-k 2; drafted token 0."""
+    zd = np.log(np.array([0.6, 0.4, 0.05, 0.05]))
+    zt = np.log(np.array([0.3, 0.7, 0.05, 0.05]))
+    p, _, _, _ = oracle.process_row(zd, 1.0, 2, 1.0)
+    pp, Z, ids, deg = oracle.downweight_probs(zd, p, 4, 0.0)
+    assert deg and Z == 1.0 and list(ids[:2]) == [0, 1] and (pp == p).all()
+    # a proper set (F = 1): p' = (0, 1, 0, 0)
+    pp1, Z1, ids1, deg1 = oracle.downweight_probs(zd, p, 1, 0.0)
+    assert not deg1 and ids1[0] == 0 and abs(Z1 - 0.4) < 1e-15 and pp1[0] == 0.0 and abs(pp1[1] - 1.0) < 1e-15
+    draft = np.stack([zd, zd])[None].astype(np.float32)
+    target = np.stack([zt, zt])[None].astype(np.float32)
+    prm = oracle.params_array(1.0, 2, 1.0, B=1)
+    for u, acc in ((0.45, True), (0.55, False)):  # accept iff u p(0) < q(0): u < 0.3 / 0.6
+        U = np.full((1, 2, 3), 0.5)
+        U[0, 0, 0] = u
+        r = oracle.verify(draft[:, :1], target, oracle.FP32, 1, prm, F=4, C=0.0, tokens=[[0]], U=U)
+        assert r.status[0] & oracle.ST_DEGENERATE_DOWNWEIGHT
+        if acc:
+            assert r.k[0] == 1
+        else:  # residual (q - p)+ = (0, 0.3): W = 0.3 and t* = 1 whatever v is
+            assert r.k[0] == 0 and r.t[0] == 1 and abs(r.W[0] - 0.3) < 1e-6  # float32 logits
+    # with F = 1 the drafted token has p'(0) = 0 and q(0) > 0: accepted for every u (reading R8)
+    U = np.full((1, 2, 3), 0.99)
+    r = oracle.verify(draft[:, :1], target, oracle.FP32, 1, prm, F=1, C=0.0, tokens=[[0]], U=U)
+    assert r.k[0] == 1 and r.status[0] == oracle.ST_OUTSIDE_DRAFT_SUPPORT

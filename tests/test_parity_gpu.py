@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+from flagbound import bound_flagged
 from lossless_speculative_sampling_amd import capi, synth
 
 pytestmark = pytest.mark.gpu
@@ -45,10 +46,11 @@ def run_oracle(w, tokens=None, seed=None, round_=0):
                          tokens=tokens, seed=w.seed if seed is None else seed, round_=round_)
 
 
-def check_verify(w, tokens=None, seed=None, round_=0, label=""):
+def check_verify(w, tokens=None, seed=None, round_=0, label="", allow_flags=None):
     say(f"[parity] {label} {w.name} B={w.B} K={w.K} V={w.V} dtype={w.dtype} sample={tokens is None}")
-    k, t, W, st, tok = run_gpu(w, tokens, seed, round_)
     o = run_oracle(w, tokens, seed, round_)
+    bound_flagged(o.flags, f"{label} {w.name}", allow_flags)
+    k, t, W, st, tok = run_gpu(w, tokens, seed, round_)
     ok = o.flags == 0
     bad = np.flatnonzero(ok & ((k != o.k) | (t != o.t) | (st != o.status)))
     assert len(bad) == 0, (f"{len(bad)} mismatches, first {bad[:5]}: gpu k={k[bad[:5]]} t={t[bad[:5]]} "
@@ -117,18 +119,20 @@ def test_cache_build_and_lookup():
     say(f"[parity] cache ok: hits {int(obatch[0])}/{w.B}")
 
 
-def _check_fused(w, tokens=None, label=""):
+def _check_fused(w, tokens=None, label="", allow_flags=None, round_=0):
     """saguaro_verify_cache against the oracle's verify and cache build on the same inputs."""
     say(f"[parity] fused verify+cache {label} B={w.B} K={w.K} V={w.V} budget={w.budget} sample={tokens is None}")
     sample = tokens is None
+    o = run_oracle(w, tokens, round_=round_)
+    bound_flagged(o.flags, f"fused {label}", allow_flags)
     prm = capi.params_tensor(w.temperature, w.top_k, w.top_p)
     tok = torch.zeros((w.B, w.K), dtype=torch.int32, device="cuda") if sample else dev(np.asarray(tokens, np.int32))
     out, cache, fan = capi.saguaro_verify_cache(dev(w.draft), dev(w.target), w.K, prm, tok, w.budget, w.a, w.r,
-                                                F=w.F, C=w.C, seed=w.seed, flags=capi.SPEC_SAMPLE_DRAFT if sample else 0)
+                                                F=w.F, C=w.C, seed=w.seed, round_=round_,
+                                                flags=capi.SPEC_SAMPLE_DRAFT if sample else 0)
     torch.cuda.synchronize()
     k, t = out.k.cpu().numpy(), out.tstar.cpu().numpy()
     st, tk = out.status.cpu().numpy().astype(np.uint32), out.tokens.cpu().numpy()
-    o = run_oracle(w, tokens)
     ok = o.flags == 0
     bad = np.flatnonzero(ok & ((k != o.k) | (t != o.t) | (st != o.status)))
     assert len(bad) == 0, f"{len(bad)} verify mismatches, first {bad[:5]}"
@@ -373,6 +377,7 @@ def test_fast_workspace_reuse_and_determinism():
         outs.append((o.k.cpu().numpy().copy(), o.tstar.cpu().numpy().copy(), o.status.cpu().numpy().copy()))
     assert all(np.array_equal(x, y) for x, y in zip(outs[0], outs[2]))
     o1 = run_oracle(w.without_cache_row(), tokens=tok.cpu().numpy(), round_=1)
+    bound_flagged(o1.flags, "workspace reuse, round 1")
     ok = o1.flags == 0
     assert (outs[1][0][ok] == o1.k[ok]).all() and (outs[1][1][ok] == o1.t[ok]).all()
 
@@ -380,10 +385,12 @@ def test_fast_workspace_reuse_and_determinism():
 # ------------------------------------------------------------------------------------------
 # random-token backup speculation: the draft distribution is uniform on the vocabulary
 # ------------------------------------------------------------------------------------------
-def check_uniform(w, tokens=None, label=""):
+def check_uniform(w, tokens=None, label="", allow_flags=None):
     """Uniform-draft verification (SPEC_UNIFORM_DRAFT, no draft logits) against the oracle."""
     sample = tokens is None
     say(f"[parity] uniform {label} B={w.B} K={w.K} V={w.V} dtype={w.dtype} sample={sample}")
+    o = oracle.verify(None, w.target, w.dtype, w.K, w.params(), tokens=tokens, seed=w.seed, uniform_draft=True)
+    bound_flagged(o.flags, f"uniform {label}", allow_flags)
     prm = capi.params_tensor(w.temperature, w.top_k, w.top_p)
     tok = torch.zeros((w.B, w.K), dtype=torch.int32, device="cuda") if sample else dev(np.asarray(tokens, np.int32))
     flags = capi.SPEC_UNIFORM_DRAFT | (capi.SPEC_SAMPLE_DRAFT if sample else 0)
@@ -391,7 +398,6 @@ def check_uniform(w, tokens=None, label=""):
     torch.cuda.synchronize()
     k, t, W = out.k.cpu().numpy(), out.tstar.cpu().numpy(), out.resid_mass.cpu().numpy()
     st, gtok = out.status.cpu().numpy().astype(np.uint32), out.tokens.cpu().numpy()
-    o = oracle.verify(None, w.target, w.dtype, w.K, w.params(), tokens=tokens, seed=w.seed, uniform_draft=True)
     ok = o.flags == 0
     bad = np.flatnonzero(ok & ((k != o.k) | (t != o.t) | (st != o.status)))
     assert len(bad) == 0, (f"{len(bad)} mismatches, first {bad[:5]}: gpu k={k[bad[:5]]} t={t[bad[:5]]} "
@@ -485,3 +491,60 @@ def test_fast_large_batch():
     tp = rng.choice([0.5, 0.9, 1.0], B)
     w = _zipf_work(rng, B, K, V, T, tk, tp, F=2, C=0.2)
     check_verify(w, tokens=_oracle_tokens(w), label="fast-large-batch")
+
+
+@pytest.mark.parametrize("K", [63, 64, 100])
+def test_drafts_at_the_wave_limit(K):
+    """K + 1 = 64 positions is the bf16 count path's limit (one request decision wave); K = 64 and
+    K = 100 take the general path.  Request 0 accepts every position (draft rows equal the target
+    rows), request 1 is rejected at position K - 3 (the drafted token's target logit is -inf
+    there, its draft logit finite: past position 63 for K = 100), request 2 has a NaN in its
+    bonus row K, request 3 a +inf in its bonus row."""
+    rng = np.random.default_rng(700 + K)
+    B, V = 4, 2048
+    zt = synth.f32_to_bf16_bits(rng.normal(0, 2.0, (B, K + 1, V)).astype(np.float32))
+    zd = zt[:, :K].copy()
+    tok = rng.integers(0, V, (B, K)).astype(np.int32)
+    jr = K - 3
+    zt[1, jr, tok[1, jr]] = 0xFF80  # -inf in the target only: q(s) = 0 < p(s)
+    zt[2, K, 5] = 0x7FC0            # NaN
+    zt[3, K, 9] = 0x7F80            # +inf
+    w = _work(zd, zt, synth.BF16, K, 1.0, 0, 1.0)
+    o, _ = check_verify(w, tokens=tok, label=f"wave-limit K={K}")
+    assert o.k[0] == K and o.k[1] == jr
+    assert o.status[2] == oracle.ST_BAD_LOGIT and o.status[3] == oracle.ST_BAD_LOGIT
+
+
+def test_fused_given_tokens_twenty_rounds():
+    """The benchmark's call at full size (B = 16, K = 5, V = 128256 with the cache row, given
+    drafted tokens) over the twenty rounds the benchmark times: every round draws its own
+    uniforms from the Philox counter."""
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
+    tok = _oracle_tokens(w.without_cache_row())
+    for rnd in range(20):
+        _check_fused(w, tokens=tok, label=f"given round {rnd}", round_=rnd)
+
+
+def test_tree_chains_full_size():
+    """Config 5 at full size: 64 requests x 8 branches = 512 chains, gamma = 7, V = 151936, top-k 50."""
+    w = synth.tree(n_req=64)
+    o, _ = check_verify(w, tokens=w.tokens, label="tree-full")
+    shape = [w.kappa, w.gamma]
+    n_req = w.B // w.kappa
+    slot, hit, batch = capi.saguaro_cache_lookup(1, dev(w.tokens), shape, 0, n_req, dev(o.k), dev(o.t))
+    torch.cuda.synchronize()
+    oslot, ohit, obatch = oracle.cache_lookup(1, w.tokens, shape, 0, n_req, o.k, o.t)
+    assert (slot.cpu().numpy() == oslot).all() and (batch.cpu().numpy() == obatch).all()
+
+
+def test_llama_two_hundred_rounds_given_tokens():
+    """Config 2 (B = 1, K = 5, V = 128256, top-p 0.8): 200 rounds batched as 200 requests, then
+    twenty single-request calls that step the round counter."""
+    w = synth.llama(B=200)
+    tok = _oracle_tokens(w)
+    check_verify(w, tokens=tok, label="llama-200")
+    for rnd in range(20):
+        b = rnd * 7
+        one = _work(w.draft[b:b + 1], w.target[b:b + 1], w.dtype, w.K, w.temperature[b], w.top_k[b], w.top_p[b],
+                    seed=w.seed)
+        check_verify(one, tokens=tok[b:b + 1], round_=rnd, label=f"llama round {rnd}")

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+from flagbound import bound_flagged
 from lossless_speculative_sampling_amd import capi, synth
 
 pytestmark = pytest.mark.gpu
@@ -29,10 +30,14 @@ def dev(a):
 
 
 def check_pyramid(draft, verifier, dtype, K, prm, tau, tokens=None, F=0, C=1.0, seed=5, assisted=False,
-                  uniform=False, label=""):
+                  uniform=False, label="", allow_flags=None):
     B, _, V = verifier.shape
     sample = tokens is None
     say(f"[pyramid] {label} B={B} K={K} V={V} dtype={dtype} sample={sample} assisted={assisted}")
+    o = oracle.verify(None if uniform else draft, verifier, dtype, K, prm, F=F, C=float(np.float32(C)),
+                      tokens=tokens, seed=seed, uniform_draft=uniform, tau=np.asarray(tau, np.float64),
+                      assisted=assisted)
+    bound_flagged(o.flags, f"pyramid {label}", allow_flags)
     flags = (capi.SPEC_SAMPLE_DRAFT if sample else 0) | (capi.SPEC_ASSISTED if assisted else 0) | \
         (capi.SPEC_UNIFORM_DRAFT if uniform else 0)
     tok = torch.zeros((B, K), dtype=torch.int32, device="cuda") if sample else dev(np.asarray(tokens, np.int32))
@@ -43,9 +48,6 @@ def check_pyramid(draft, verifier, dtype, K, prm, tau, tokens=None, F=0, C=1.0, 
     torch.cuda.synchronize()
     k, t, W = out.k.cpu().numpy(), out.tstar.cpu().numpy(), out.resid_mass.cpu().numpy()
     st, gtok, gdiv = out.status.cpu().numpy().astype(np.uint32), out.tokens.cpu().numpy(), div.cpu().numpy()
-    o = oracle.verify(None if uniform else draft, verifier, dtype, K, prm, F=F, C=float(np.float32(C)),
-                      tokens=tokens, seed=seed, uniform_draft=uniform, tau=np.asarray(tau, np.float64),
-                      assisted=assisted)
     ok = o.flags == 0
     bad = np.flatnonzero(ok & ((k != o.k) | (t != o.t) | (st != o.status)))
     assert len(bad) == 0, (f"{len(bad)} mismatches, first {bad[:5]}: gpu k={k[bad[:5]]} t={t[bad[:5]]} "
@@ -74,10 +76,12 @@ def test_pyramid_shapes_and_parameter_mix(dtype, V):
     tp = rng.choice([0.3, 0.9, 1.0], B).astype(np.float32)
     prm = oracle.params_array(T, tk, tp)
     tau = rng.choice([-1.0, 0.05, 0.2, 0.5, 1.0], B).astype(np.float32)
+    # tau = 1 meets rows whose processed supports are disjoint (top-k 1, greedy): their divergence
+    # is exactly 1, on the threshold, and the oracle flags them (up to 4 of these 24 requests)
     for assisted in (False, True):
-        check_pyramid(zd, zt, dtype, K, prm, tau, F=2, C=0.4, assisted=assisted, label=f"mix V={V}")
+        check_pyramid(zd, zt, dtype, K, prm, tau, F=2, C=0.4, assisted=assisted, label=f"mix V={V}", allow_flags=4)
         check_pyramid(zd, zt, dtype, K, prm, tau, tokens=rng.integers(0, V, (B, K)), F=2, C=0.4,
-                      assisted=assisted, label=f"mix-given V={V}")
+                      assisted=assisted, label=f"mix-given V={V}", allow_flags=4)
     check_pyramid(None, zt, dtype, K, prm, tau, uniform=True, label=f"uniform V={V}")
 
 
@@ -151,7 +155,10 @@ def test_pyramid_fast_path_outside_bins():
                               np.array([1.0, 0.9, 1.0, 1.0, 0.95, 1.0, 0.9, 1.0], np.float32))
     probe = oracle.verify(zd, zt, synth.BF16, K, prm, seed=5, tau=np.full(B, -1.0))
     tau = np.median(probe.div, axis=1).astype(np.float32)
-    o = check_pyramid(zd, zt, synth.BF16, K, prm, tau, tokens=probe.tokens, label="fast outside bins")
+    # the threshold is each request's own median divergence: the flattest rows (scale 0.002) diverge
+    # by ~2e-7 with gaps of ~1e-9, and the top-3 row repeats a divergence, so up to two requests sit
+    # within the oracle's 1e-9 band of their threshold
+    o = check_pyramid(zd, zt, synth.BF16, K, prm, tau, tokens=probe.tokens, label="fast outside bins", allow_flags=2)
     assert (o.div <= tau[:, None]).any() and (o.div > tau[:, None]).any()
 
 
