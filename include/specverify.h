@@ -118,7 +118,11 @@ enum {
     SPEC_ST_BAD_TOKEN = 64,                /* a draft token outside [0, V): k = 0, t* = -1 */
     SPEC_ST_DEGENERATE_DOWNWEIGHT = 128,   /* C = 0 and the set holds all the draft mass: the
                                               row is left undownweighted */
-    SPEC_ST_BAD_PARAM = 256                /* invalid spec_params: k = 0, t* = -1 */
+    SPEC_ST_BAD_PARAM = 256,               /* invalid spec_params: k = 0, t* = -1 */
+    SPEC_ST_PLACEMENT = 512                /* the exact-count path found the workgroups of one
+                                              position on different XCDs (its slices meet in one
+                                              XCD's L2): the request was redone by the general
+                                              path.  Never expected; a guard on the launch map */
 };
 
 /* Uniforms.  Counter-based Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and counter

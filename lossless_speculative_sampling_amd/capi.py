@@ -29,6 +29,7 @@ ST_BAD_LOGIT = 32
 ST_BAD_TOKEN = 64
 ST_DEGENERATE_DOWNWEIGHT = 128
 ST_BAD_PARAM = 256
+ST_PLACEMENT = 512
 
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
            "saguaro_cache_lookup", "saguaro_verify_cache", "saguaro_backup_plan", "mirror_signpost_workspace_bytes",

@@ -18,6 +18,7 @@ constexpr uint32_t kStBadLogit = SPEC_ST_BAD_LOGIT;
 constexpr uint32_t kStBadToken = SPEC_ST_BAD_TOKEN;
 constexpr uint32_t kStDegenerate = SPEC_ST_DEGENERATE_DOWNWEIGHT;
 constexpr uint32_t kStBadParam = SPEC_ST_BAD_PARAM;
+constexpr uint32_t kStPlacement = SPEC_ST_PLACEMENT;
 
 // ------------------------------------------------------------------------------------------
 // Token order: a 32-bit key that grows with the logit.  -0 is folded onto +0 so that equal

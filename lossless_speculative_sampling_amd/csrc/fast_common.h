@@ -83,26 +83,25 @@ __device__ __forceinline__ int special_seg(uint32_t k) {
 // Workspace records
 // ------------------------------------------------------------------------------------------
 struct alignas(16) RowPart {  // one slice of one row, written by the count kernel
-    float m;            // largest finite logit of the slice, -inf when none
-    uint32_t flags;     // 1: NaN or +inf seen, 2: special list overflow
-    uint32_t n_finite;
-    uint32_t n_special;
-    uint32_t n_top;
+    uint32_t flags;     // 1: NaN or +inf seen, 2: special list overflow, 4: values outside the bins
+    uint32_t n_ent;     // occupied exact bins (entries of ent)
+    uint32_t n_special; // finite values outside the exact bins (listed up to kSpecial)
+    uint32_t n_top;     // candidates listed
     uint32_t cnt_s;     // elements with the draft token's key that precede it: all of them in a
                         // slice before the token's, those with a lower id in the token's slice
     uint32_t s_bits;    // bf16 bits of the row at the draft token (0 without a token)
     uint32_t n_neginf;
-    double S;           // sum of exp((z - m)/T) over the slice's finite elements
+    uint32_t xcc;       // XCD the slice's workgroup ran on
     uint32_t groups[2]; // bit g (low word first): the slice holds elements in group g of 64 bins
-    double seg_mass[kSegs];
-    uint32_t seg_count[kSegs];
+    uint32_t pad[2];
     uint32_t top_key[kTop];
     int32_t top_id[kTop];
     uint32_t sp_key[kSpecial];
     int32_t sp_id[kSpecial];
-    uint16_t fine[kBins];
+    uint32_t ent[kBins];  // occupied bins in ascending order: (bin << 16) | count
 };
-static_assert(offsetof(RowPart, S) == 32, "header layout: 2 x 16 bytes, then S");
+static_assert(offsetof(RowPart, groups) == 32 && offsetof(RowPart, top_key) % 16 == 0, "header: 2 x 16 bytes");
+static_assert(offsetof(RowPart, ent) % 16 == 0, "entries 16-byte aligned");
 
 struct RowFinal {  // enough to evaluate any element's processed probability
     float m;
@@ -228,9 +227,10 @@ __device__ __forceinline__ int bin_of_sel(int g, int lane) { return g * kGroup +
 // Number of leading candidates each slice lists for a row (identical in phase A and combine)
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ int list_len(const VerifyArgs& a, const spec_params& prm, bool draft) {
+    // the argmax of a greedy row, the downweighted set of a draft row (top-k and nucleus cuts
+    // come from the counts alone)
     const bool greedy = prm.temperature == 0.0f;
     int want = greedy ? 1 : 0;
-    if (!greedy && prm.top_k > 0 && prm.top_k < a.V && prm.top_k <= kTop) want = max(want, prm.top_k);
     if (!greedy && draft && a.F > 0 && a.C < 1.0f) want = max(want, a.F);
     return want;
 }

@@ -1,7 +1,7 @@
 // Count kernel of the bf16 verification path: every slice of every (request, position) unit
 // loads its token columns of the target row (and the draft row), counts every distinct bf16
 // value in LDS and publishes a compact summary for the resolve kernel.
-#include "fast_combine.h"
+#include "fast_settle.h"
 
 namespace sv {
 namespace fast {
@@ -12,14 +12,11 @@ namespace fast {
 // request to be settled decides the request (no workgroup waits on another).
 // ------------------------------------------------------------------------------------------
 struct CountSmem {
-    double segm[2][kSegs];
-    uint32_t segc[2][kSegs];
-    union {
-        uint32_t hraw[2][kHistRow];   // counting
-        UnitSmem us;                  // settling the unit (the histograms are published by then)
-    };
+    alignas(16) uint32_t hraw[2][kHistRow];  // counting; when settling, the candidate stage and
+                                             // then the unit's merged histograms
     __device__ __forceinline__ uint32_t* hist(int r) { return &hraw[r][kHistLead]; }
     __device__ __forceinline__ const uint32_t* hist(int r) const { return &hraw[r][kHistLead]; }
+    uint32_t segc[2][kSegs];
     uint32_t sp_key[2][kSpecial];
     int32_t sp_id[2][kSpecial];
     uint32_t n_sp[2];
@@ -29,17 +26,20 @@ struct CountSmem {
     uint32_t cnt_s[2];
     uint32_t flags[2];
     uint32_t neginf[2];
+    uint32_t grp[2][2];  // groups of 64 bins the slice holds, per row
     int32_t scan[kWaves + 1];
     double redd[kWaves];
     int32_t redi[kWaves];
     uint32_t s_bits[2];
-    uint32_t maxkey[2];
     int last;
     int rare[2];
     double u_acc;  // the acceptance draw of the unit's position
     double u_res;  // its residual / bonus draw
     uint32_t unit_code;  // the settled unit's outcome (unit_code)
+    uint32_t xcc;        // the XCD this workgroup runs on
+    SettleSmem ss;       // settling the unit
 };
+static_assert(sizeof(StageSmem) <= sizeof(uint32_t) * 2 * kHistRow, "candidate stage fits the histogram rows");
 
 // Per-segment element counts of both rows into sm.segc: a thread adds 8 bins, eight lanes a
 // group of 64; the last wave also sorts each row's specials into their four segments.
@@ -299,133 +299,65 @@ __device__ __forceinline__ void local_ranks(CountSmem& sm, bool two, int c0, int
     if (threadIdx.x < (unsigned)rows) sm.cnt_s[threadIdx.x] = (packed >> (16 * threadIdx.x)) & 0xFFFFu;
 }
 
-// Publishes both rows' slice summaries (RowPart): the largest logit, per-segment counts and
-// masses relative to it, specials, candidate list, the draft token's rank and the fine counts.
-// Each row's masses are exp((z - m) / T) with its own maximum m (rows that differ by a shift
-// get identical masses); rows with the same maximum share the exps.
-__device__ __forceinline__ void publish_rows(const FastArgs& f, CountSmem& sm, int unit, int slice, bool two,
-                                             const spec_params& prm) {
+// Publishes both rows' slice summaries (RowPart): the occupied bins as (bin, count) entries in
+// ascending bin order, the groups of 64 bins the slice holds, the specials, the candidate list,
+// the drafted token's value and rank, and the header.  Thread t reads bins [6t, 6t + 6); one
+// workgroup scan of both rows' entry counts (16-bit halves) places every entry.
+__device__ __forceinline__ void publish_sparse(const FastArgs& f, CountSmem& sm, int unit, int slice, bool two) {
+    constexpr int kPer = 6;
+    constexpr int kPubThreads = kBins / kPer;  // 480
+    static_assert(kPer * kPubThreads == kBins && kPubThreads <= kThreads, "bins per thread");
     const int rows = two ? 2 : 1;
-    const double T = (double)prm.temperature;
-    const double invT = inv_temperature(prm.temperature);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    // largest key of row r (wave r): the first non-empty segment, then its highest bin or special
-    if (wave < rows) {
-        const int r = wave;
-        const int nsp = min((int)sm.n_sp[r], kSpecial);
-        const uint64_t ne = __ballot(lane < kSegs && sm.segc[r][lane] != 0u);
-        uint32_t mk = 0;
-        if (ne != 0) {
-            const int sg = first_lane(ne);
-            const int g = group_of_seg(sg);
-            if (g >= 0) {
-                const int i = first_lane(__ballot(sm.hist(r)[bin_of_sel(g, lane)] != 0u));
-                mk = bin_key(bin_of_sel(g, i));
-            } else {
-                const uint32_t k = lane < nsp ? sm.sp_key[r][lane] : 0u;
-                mk = wave_max((lane < nsp && special_seg(k) == sg) ? k : 0u);
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    uint32_t cnt[2][kPer];
+    int nz[2] = {0, 0};
+    uint64_t gm[2] = {0ull, 0ull};
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            cnt[r][i] = (r < rows && tid < kPubThreads) ? sm.hist(r)[tid * kPer + i] : 0u;
+            if (cnt[r][i] != 0u) {
+                ++nz[r];
+                gm[r] |= 1ull << ((tid * kPer + i) / kGroup);
             }
         }
-        if (lane == 0) sm.maxkey[r] = mk;
-    }
-    __syncthreads();
-    float m[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        const uint32_t mk = r < rows ? sm.maxkey[r] : 0u;
-        m[r] = mk ? key16_value(mk) : -__builtin_inff();
-    }
-    const bool share = two && m[0] == m[1];
-    // per-group masses, one wave per group
-#pragma unroll 1
-    for (int g = wave; g < kGroups; g += kWaves) {
-        const int sg = seg_of_group(g);
-        const bool ne0 = sm.segc[0][sg] != 0u, ne1 = two && sm.segc[1][sg] != 0u;
-        if (!ne0 && !ne1) {
-            if (lane == 0) sm.segm[0][sg] = sm.segm[1][sg] = 0.0;
-            continue;
-        }
-        const int bin = g * kGroup + lane;
-        const uint32_t c0 = sm.hist(0)[bin], c1 = two ? sm.hist(1)[bin] : 0u;
-        const float z = key16_value(bin_key(bin));
-        double e0 = 0.0, e1 = 0.0;
-        if (T > 0.0) {
-            if (share) {
-                e0 = e1 = mass_of(z, m[0], invT);
-            } else {
-                if (ne0) e0 = mass_of(z, m[0], invT);
-                if (ne1) e1 = mass_of(z, m[1], invT);
-            }
-        }
-        const double ms0 = wave_sum(c0 != 0u ? (double)c0 * e0 : 0.0);
-        const double ms1 = wave_sum(c1 != 0u ? (double)c1 * e1 : 0.0);
-        if (lane == 0) {
-            sm.segm[0][sg] = ms0;
-            sm.segm[1][sg] = ms1;
+        const uint32_t lo = wave_or((uint32_t)gm[r]), hi = wave_or((uint32_t)(gm[r] >> 32));
+        if (lane == 0 && r < rows && (lo | hi) != 0u) {
+            atomicOr(&sm.grp[r][0], lo);
+            atomicOr(&sm.grp[r][1], hi);
         }
     }
-    // the four special segments of row r (wave 7 - r), one lane per special
-    if (wave >= kWaves - rows) {
-        const int r = kWaves - 1 - wave;
-        const int nsp = min((int)sm.n_sp[r], kSpecial);
-        int sg = -1;
-        double ms = 0.0;
-        if (lane < nsp) {
-            const uint32_t k = sm.sp_key[r][lane];
-            sg = special_seg(k);
-            if (T > 0.0) ms = mass_of(key16_value(k), m[r], invT);
-        }
-        const int sps[4] = {kSegHugePos, kSegTinyPos, kSegTinyNeg, kSegHugeNeg};
+    int total;
+    const int before = block_exclusive_scan<int>(nz[0] | (nz[1] << 16), sm.scan, &total);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const double sx = wave_sum(sg == sps[x] ? ms : 0.0);
-            if (lane == 0) sm.segm[r][sps[x]] = sx;
-        }
-    }
-    __syncthreads();
-    // the records: row r's header from wave r, the arrays from every thread
-    if (wave < rows) {
-        const int r = wave;
+    for (int r = 0; r < 2; ++r) {
+        if (r >= rows) break;
         RowPart* P = part_of(f, unit, slice, r);
+        int o = (before >> (16 * r)) & 0xFFFF;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (cnt[r][i] != 0u) P->ent[o++] = ((uint32_t)(tid * kPer + i) << 16) | cnt[r][i];
         const int nsp = min((int)sm.n_sp[r], kSpecial);
-        const double S = wave_sum(lane < kSegs ? sm.segm[r][lane] : 0.0);
-        const uint32_t nfin = wave_sum(lane < kSegs ? sm.segc[r][lane] : 0u);
-        const uint64_t gm = __ballot(lane < kGroups && sm.segc[r][seg_of_group(lane)] != 0u);
-        if (lane == 0) {
-            P->groups[0] = (uint32_t)gm;
-            P->groups[1] = (uint32_t)(gm >> 32);
-            P->m = m[r];
-            P->flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u) | (sm.rare[r] ? 4u : 0u);
-            P->n_finite = nfin;
-            P->n_special = (uint32_t)nsp;
-            P->n_top = sm.n_top[r];
-            P->cnt_s = sm.cnt_s[r];
-            P->s_bits = sm.s_bits[r];
-            P->n_neginf = sm.neginf[r];
-            P->S = S;
+        if (tid < nsp) {
+            P->sp_key[tid] = sm.sp_key[r][tid];
+            P->sp_id[tid] = sm.sp_id[r][tid];
         }
-    }
-    for (int r = 0; r < rows; ++r) {
-        RowPart* P = part_of(f, unit, slice, r);
-        const int nsp = min((int)sm.n_sp[r], kSpecial);
-        for (int sg = threadIdx.x; sg < kSegs; sg += blockDim.x) {
-            P->seg_mass[sg] = sm.segm[r][sg];
-            P->seg_count[sg] = sm.segc[r][sg];
+        if (tid < (int)sm.n_top[r]) {
+            P->top_key[tid] = sm.top_key[r][tid];
+            P->top_id[tid] = sm.top_id[r][tid];
         }
-        if ((int)threadIdx.x < nsp) {
-            P->sp_key[threadIdx.x] = sm.sp_key[r][threadIdx.x];
-            P->sp_id[threadIdx.x] = sm.sp_id[r][threadIdx.x];
+        if (tid == r) {
+            const uint32_t flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u) | (sm.rare[r] ? 4u : 0u);
+            reinterpret_cast<u32x4*>(P)[0] = u32x4{flags, (uint32_t)((total >> (16 * r)) & 0xFFFF), (uint32_t)nsp,
+                                                    sm.n_top[r]};
+            reinterpret_cast<u32x4*>(P)[1] = u32x4{sm.cnt_s[r], sm.s_bits[r], sm.neginf[r], sm.xcc};
+            P->groups[0] = sm.grp[r][0];
+            P->groups[1] = sm.grp[r][1];
         }
-        if ((int)threadIdx.x < (int)sm.n_top[r]) {
-            P->top_key[threadIdx.x] = sm.top_key[r][threadIdx.x];
-            P->top_id[threadIdx.x] = sm.top_id[r][threadIdx.x];
-        }
-        // fine counts, two per dword (a slice holds < 65536 columns)
-        uint32_t* fine32 = reinterpret_cast<uint32_t*>(P->fine);
-#pragma unroll 1
-        for (int i = threadIdx.x; i < kBins / 2; i += blockDim.x)
-            fine32[i] = (sm.hist(r)[2 * i] & 0xFFFFu) | (sm.hist(r)[2 * i + 1] << 16);
     }
 }
 
@@ -492,7 +424,7 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
                                             bool param_ok, bool two, int s_tok, bool tok_ok) {
     const VerifyArgs& a = f.a;
     const int unit = P.unit;
-    UnitSmem& us = sm.us;
+    SettleSmem& us = sm.ss;
     uint32_t status = 0;
     int accept = 0, fallback = 0;
     if (!param_ok) {
@@ -500,9 +432,14 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
     } else {
         const bool vd = P.j < a.K;      // the drafted token is verified here
         const bool vrow = vd && two;     // against a draft row (not the uniform draft)
-        combine(f, us, unit, P.j, two ? 2 : 1, prm, vd, s_tok);
+        settle_rows(f, sm, unit, P.j, two ? 2 : 1, prm, vd, s_tok);
         const bool bad = us.rv[0].bad || (vrow && us.rv[1].bad);
         fallback = (!bad && (us.rv[0].overflow || (vrow && us.rv[1].overflow))) ? 1 : 0;
+        // the unit's slices did not share one XCD's L2: the request is redone by the general path
+        if (us.rv[0].xcc_bad || (two && us.rv[1].xcc_bad)) {
+            fallback = 1;
+            if (threadIdx.x == 0) atomicOr(&reinterpret_cast<ReqFast*>(f.ws + f.L.reqs)[P.b].pad, (int32_t)kStPlacement);
+        }
         if (bad) {
             status = kStBadLogit;
         } else if (!fallback) {
@@ -613,11 +550,13 @@ __device__ __forceinline__ void decide_packed(const FastArgs& f, int b, uint64_t
     uint32_t outside = 0;
     for (int j = 0; j < K && j <= k; ++j)
         if ((word >> (kCountBits + kCodeBits * j)) & 64u) outside = kStOutside;
+    ReqFast* R = reinterpret_cast<ReqFast*>(f.ws + f.L.reqs) + b;
+    const uint32_t place = (uint32_t)ldnt(&R->pad);  // set by a unit whose slices were misplaced
     int mode = 0, t = -1, kk = 0;
     uint32_t status;
     if (any_fb) {
         mode = 2;
-        status = 0;
+        status = place;  // the general path reports the rest
     } else if (any & kStBadParam) {
         status = kStBadParam;
     } else if (any & kStBadLogit) {
@@ -638,10 +577,10 @@ __device__ __forceinline__ void decide_packed(const FastArgs& f, int b, uint64_t
             mode = 1;
         }
     }
-    ReqFast* R = reinterpret_cast<ReqFast*>(f.ws + f.L.reqs) + b;
     R->mode = mode;
     R->k = kk;
     R->status = status;
+    R->pad = 0;
     if (mode == 0) {
         a.out_k[b] = kk;
         a.out_t[b] = t;
@@ -670,11 +609,13 @@ __device__ __forceinline__ void decide_request(const FastArgs& f, int b) {
     int k = first_lane(__ballot(lane < K && !acc));
     if (k < 0) k = K;
     const uint32_t outside = wave_or((lane < K && lane <= k) ? (st & kStOutside) : 0u);
+    ReqFast* R = reinterpret_cast<ReqFast*>(f.ws + f.L.reqs) + b;
+    const uint32_t place = (uint32_t)ldnt(&R->pad);  // set by a unit whose slices were misplaced
     int mode = 0, t = -1, kk = 0;
     uint32_t status;
     if (any_fb) {
         mode = 2;
-        status = 0;
+        status = place;  // the general path reports the rest
     } else if (any & kStBadParam) {
         status = kStBadParam;
     } else if (any & kStBadLogit) {
@@ -692,10 +633,10 @@ __device__ __forceinline__ void decide_request(const FastArgs& f, int b) {
         else mode = 1;
     }
     if (lane == 0) {
-        ReqFast* R = reinterpret_cast<ReqFast*>(f.ws + f.L.reqs) + b;
         R->mode = mode;
         R->k = kk;
         R->status = status;
+        R->pad = 0;
         if (mode == 0) {
             a.out_k[b] = kk;
             a.out_t[b] = t;
@@ -748,7 +689,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
             sm.n_sp[threadIdx.x] = 0;
             sm.flags[threadIdx.x] = 0;
             sm.neginf[threadIdx.x] = 0;
+            sm.grp[threadIdx.x][0] = 0;
+            sm.grp[threadIdx.x][1] = 0;
         }
+        if (threadIdx.x == 2) sm.xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;  // XCC_ID
         // the rows' values at the draft token (every slice counts the token's key), zero without
         // a token: loaded after the slice, stored once the counts have waited for it anyway
         uint32_t sb0 = 0u, sb1 = 0u;
@@ -774,18 +718,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
             sm.rare[threadIdx.x] = threadIdx.x == 0 ? rare0 : rare1;
         }
         __syncthreads();
-        seg_counts(sm, two ? 2 : 1);
-        __syncthreads();
         // passes over the columns (registers) first, so the columns are dead for the summaries
         const bool holds_s = j < a.K && tok_ok && s_tok >= c0;  // at or after this slice: count its key
         const int want_q = list_len(a, prm, false), want_p = two ? draft_list_len(f, prm, j) : 0;
         if (want_q > 0 || want_p > 0) {
+            seg_counts(sm, two ? 2 : 1);
+            __syncthreads();
             const int want[2] = {want_q, want_p};
             local_tops(sm, want, c0, a.V, vq, vp);
         }
         if (holds_s) local_ranks(sm, two, c0, s_tok, vq, vp);
         __syncthreads();
-        publish_rows(f, sm, unit, slice, two, prm);
+        publish_sparse(f, sm, unit, slice, two);
     }
 
     // ---- unit rendezvous: the last slice of the unit settles it ----

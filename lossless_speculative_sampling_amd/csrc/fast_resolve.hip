@@ -617,7 +617,7 @@ __device__ __forceinline__ bool arrive_last(const FastArgs& f, ResSmem& sm, int 
 }
 
 // The general algorithm for every unit of request b, and the request's outcome from them.
-__device__ __forceinline__ void general_request(const FastArgs& f, ResSmem& sm, int b, int j) {
+__device__ __forceinline__ void general_request(const FastArgs& f, ResSmem& sm, int b, int j, uint32_t extra) {
     const VerifyArgs& a = f.a;
     UnitRec* G = reinterpret_cast<UnitRec*>(f.ws + f.L.gen) + (size_t)b * (a.K + 1);
     fallback_unit(a, b, j, sm);
@@ -656,7 +656,7 @@ __device__ __forceinline__ void general_request(const FastArgs& f, ResSmem& sm, 
     a.out_k[b] = k;
     a.out_t[b] = t;
     if (a.out_W) a.out_W[b] = W;
-    if (a.out_status) a.out_status[b] = st;
+    if (a.out_status) a.out_status[b] = st | extra;
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_resolve_kernel(FastArgs f) {
@@ -702,7 +702,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int mode = (int)req[0];
     if (mode == 0) return;  // decided by the count kernel
     if (mode == 2) {
-        if (w <= a.K) general_request(f, sm, b, w);
+        if (w <= a.K) general_request(f, sm, b, w, req[2]);
         return;
     }
     // mode 1: the residual of unit k, slice w / 2; each half of the slice's loads is summed by
