@@ -12,8 +12,8 @@ namespace fast {
 // request to be settled decides the request (no workgroup waits on another).
 // ------------------------------------------------------------------------------------------
 struct CountSmem {
-    alignas(16) uint32_t hraw[2][kHistRow];  // counting; when settling, the candidate stage and
-                                             // then the unit's merged histograms
+    alignas(16) uint32_t hraw[2][kHistRow];  // counting; when settling, the unit's merged
+                                             // histograms, then the occupied slots' lists
     __device__ __forceinline__ uint32_t* hist(int r) { return &hraw[r][kHistLead]; }
     __device__ __forceinline__ const uint32_t* hist(int r) const { return &hraw[r][kHistLead]; }
     uint32_t segc[2][kSegs];
@@ -39,7 +39,6 @@ struct CountSmem {
     uint32_t xcc;        // the XCD this workgroup runs on
     SettleSmem ss;       // settling the unit
 };
-static_assert(sizeof(StageSmem) <= sizeof(uint32_t) * 2 * kHistRow, "candidate stage fits the histogram rows");
 
 // Per-segment element counts of both rows into sm.segc: a thread adds 8 bins, eight lanes a
 // group of 64; the last wave also sorts each row's specials into their four segments.
@@ -432,7 +431,7 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
     } else {
         const bool vd = P.j < a.K;      // the drafted token is verified here
         const bool vrow = vd && two;     // against a draft row (not the uniform draft)
-        settle_rows(f, sm, unit, P.j, two ? 2 : 1, prm, vd, s_tok);
+        settle_rows(f, sm, unit, P.slice, P.j, two ? 2 : 1, prm, vd, s_tok);
         const bool bad = us.rv[0].bad || (vrow && us.rv[1].bad);
         fallback = (!bad && (us.rv[0].overflow || (vrow && us.rv[1].overflow))) ? 1 : 0;
         // the unit's slices did not share one XCD's L2: the request is redone by the general path

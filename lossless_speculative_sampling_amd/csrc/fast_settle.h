@@ -4,9 +4,10 @@
 // reading notes, section 4.4), and the processed probabilities of the drafted token that the
 // acceptance test compares.  Run by the last slice of a unit to finish counting.
 //
-// Every slice publishes its occupied bins as (bin, count) entries.  The settle step adds them
-// into one histogram per row, then walks the row's values in descending order once: counts
-// give the maximum and the top-k cut, one fp64 exp per occupied bin gives the masses, the
+// Every slice publishes its occupied bins as (bin, count) entries.  The settling slice adds the
+// other slices' entries to its own histograms, then walks each row's values in descending
+// order: counts give the maximum and the top-k cut and list the occupied values compactly;
+// one fp64 exp per occupied value, spread evenly over the row's threads, gives the masses, the
 // nucleus cut and the normaliser.  The slices' entries at a cut bin say which slice holds the
 // cut's last kept element (its owner) for the resolve kernel.
 #pragma once
@@ -28,7 +29,8 @@ constexpr int kRowThreads = kThreads / 2;                            // a row's 
 constexpr int kSlotsPer = (kSlots + kRowThreads - 1) / kRowThreads;    // 12 consecutive slots per thread
 static_assert(kSlotsPer * kRowThreads >= kSlots, "slots covered");
 constexpr int kSpMerge = 256;   // specials of one row merged in LDS (more: the general path)
-constexpr int kEntIt = 8;       // sparse entries each thread loads with the headers
+constexpr int kEntIt = 12;      // sparse entries each thread loads per batch
+constexpr int kStageCap = 512;  // staged candidates per row: every slice's list
 constexpr int kNone = 0x7FFFFFFF;
 
 __device__ __forceinline__ int slot_bin(int s) {
@@ -79,9 +81,11 @@ struct RowView {   // the settled view of one row
     uint32_t xcc_bad;          // slices of the unit ran on different XCDs
 };
 
+
 struct SettleSmem {
     RowView rv[2];
-    uint32_t hdr[2][kMaxSlices][8];   // each slice's header words
+    alignas(16) uint32_t hdr[2][kMaxSlices][8];   // each slice's header words
+    uint64_t stage[2][kStageCap];     // every slice's candidates, (key << 32) | ~id, slice t at t * want
     uint32_t okey[2][kTop];           // merged candidates in token order
     int32_t oid[2][kTop];
     uint32_t spk[2][kSpMerge];        // every slice's specials of a row
@@ -91,20 +95,12 @@ struct SettleSmem {
     uint32_t agg_key[2][4];
     double agg_m[2][4];
     uint32_t pc[2][2][kMaxSlices];    // per-slice counts at the top-k / nucleus cut bins
-    uint32_t wu[2][4];                // per-row wave partials
+    double cand_e[kTop];              // masses of the draft row's leading candidates
+    uint64_t wq[2][4];                // per-row wave partials of the scans
     double wd[2][4];
-    int wi[2][4];
-    int list_start[2][kMaxSlices];
-    int cross[2];     // the thread of a row whose run holds the nucleus cut
-    double xbase[kThreads];    // each thread's mass and kept count before its run (the crossing
-    uint32_t xcbase[kThreads]; // thread reads its own after a barrier, out of registers)
+    uint32_t wk[2][4];
+    int crossed[2];                   // the nucleus cut was placed
     double qs, ps;                    // the drafted token's processed probabilities
-};
-
-// Candidate lists of every slice, staged for the merge (laid over the histogram rows).
-struct StageSmem {
-    uint32_t key[2][kMergeCap];
-    int32_t id[2][kMergeCap];
 };
 
 // e^x for the masses of the settle step (x <= 0 there), written for a small register
@@ -160,18 +156,17 @@ __device__ __forceinline__ const RowPart* part_u(const FastArgs& f, int unit, in
 
 // Exclusive prefix over the 256 threads of row r in thread order (wave w of the row, lane);
 // *inc gets the inclusive value and *total the row's sum.  Every thread of the workgroup calls
-// it (one barrier); exc of thread u + 1 equals inc of thread u bit for bit.
-template <typename T>
-__device__ __forceinline__ T row_scan(T v, T (*wtot)[4], T* inc, T* total) {
+// it (one barrier).
+__device__ __forceinline__ uint64_t row_scan_u64(uint64_t v, uint64_t (*wtot)[4], uint64_t* inc, uint64_t* total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int r = threadIdx.x / kRowThreads, w = (threadIdx.x % kRowThreads) / kWave;
-    T exc;
-    const T in = wave_scan(v, &exc);
+    uint64_t exc;
+    const uint64_t in = wave_scan(v, &exc);
     if (lane == kWave - 1) wtot[r][w] = in;
     __syncthreads();
-    T before = T(0), all = T(0);
+    uint64_t before = 0, all = 0;
     for (int x = 0; x < 4; ++x) {
-        const T t = wtot[r][x];
+        const uint64_t t = wtot[r][x];
         if (x < w) before += t;
         all += t;
     }
@@ -180,13 +175,38 @@ __device__ __forceinline__ T row_scan(T v, T (*wtot)[4], T* inc, T* total) {
     return before + exc;
 }
 
-__device__ __forceinline__ int row_min(int v, int (*wtot)[4]) {
+// The same for a (mass, count) pair with one barrier.  The exclusive mass of thread u + 1
+// equals the inclusive mass of thread u bit for bit, so the intervals (exc, inc] of the
+// threads with mass tile (0, total] without overlap.
+struct Scan2 {
+    double wexc, winc, wtot;
+    uint32_t kexc, ktot;
+};
+__device__ __forceinline__ Scan2 row_scan2(double w, uint32_t k, SettleSmem& ss) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int r = threadIdx.x / kRowThreads, w = (threadIdx.x % kRowThreads) / kWave;
-    v = wave_min(v);
-    if (lane == 0) wtot[r][w] = v;
+    const int r = threadIdx.x / kRowThreads, wv = (threadIdx.x % kRowThreads) / kWave;
+    double we;
+    uint32_t ke;
+    const double wi = wave_scan(w, &we);
+    const uint32_t ki = wave_scan(k, &ke);
+    if (lane == kWave - 1) {
+        ss.wd[r][wv] = wi;
+        ss.wk[r][wv] = ki;
+    }
     __syncthreads();
-    return min(min(wtot[r][0], wtot[r][1]), min(wtot[r][2], wtot[r][3]));
+    double before = 0.0, all = 0.0;
+    uint32_t kb = 0u, ka = 0u;
+    for (int x = 0; x < 4; ++x) {
+        const double t = ss.wd[r][x];
+        const uint32_t tk = ss.wk[r][x];
+        if (x < wv) {
+            before += t;
+            kb += tk;
+        }
+        all += t;
+        ka += tk;
+    }
+    return Scan2{before + we, before + wi, all, kb + ke, ka};
 }
 
 __device__ __forceinline__ bool cut_keeps_s(const RowView& rv, const Cut& c, uint32_t key_s) {
@@ -195,214 +215,88 @@ __device__ __forceinline__ bool cut_keeps_s(const RowView& rv, const Cut& c, uin
     return rv.rank_s < c.take;
 }
 
-// Processed probability of the drafted token s in row r (after the settle).
-__device__ __forceinline__ double prob_of_s(const SettleSmem& ss, int r, int s, bool draft) {
-    const RowView& rv = ss.rv[r];
-    const uint32_t h = rv.s_bits;
+// Processed probability of the drafted token s (bf16 bits h, rank_s elements of its key before
+// it in token order, mass e) in a row with normaliser S and the given cuts: e / S when both
+// cuts keep it, else 0.
+__device__ __forceinline__ double prob_of_s(uint32_t h, int rank_s, bool has_k, uint32_t kk, int takek, bool has_p,
+                                            uint32_t kp, int takep, double S, double e) {
     if ((h & 0x7FFFu) >= 0x7F80u) return 0.0;
     const uint32_t key = key16(h);
-    if (rv.has_k && !cut_keeps_s(rv, rv.ck, key)) return 0.0;
-    if (rv.has_p && !cut_keeps_s(rv, rv.cp, key)) return 0.0;
-    const double e = rv.e_s;
-    const double p = e / rv.S;
-    if (!draft) return p;
-    const double fct = (rv.nset > 0 && e > 0.0 && in_cut_id(rv.kF, rv.idF, key, s)) ? rv.C : 1.0;
-    return (p * fct) / rv.Z;
+    const bool keep_k = !has_k || key > kk || (key == kk && rank_s < takek);
+    const bool keep_p = !has_p || key > kp || (key == kp && rank_s < takep);
+    return (keep_k && keep_p) ? e / S : 0.0;
 }
 
-// Merges the slices' candidate lists of both rows (staged in st, slice-major) into ss.okey /
-// ss.oid in token order (key desc, id asc), keeping the first want[r]; all threads.
-__device__ __forceinline__ void merge_candidates(SettleSmem& ss, const StageSmem& st, int nS, int rows, int want0,
-                                                 int want1) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    // (two scalars per row, selected by row: indexed private arrays would live in scratch memory)
-    int total0 = 0, total1 = 0;
-    for (int t = 0; t < nS; ++t) {
-        total0 += (int)ss.hdr[0][t][3];
-        total1 += rows > 1 ? (int)ss.hdr[1][t][3] : 0;
-    }
-    if (want0 <= 0) total0 = 0;
-    if (want1 <= 0) total1 = 0;
-#define WANT_OF(r) ((r) ? want1 : want0)
-#define TOTAL_OF(r) ((r) ? total1 : total0)
-    // up to 64 candidates of a row: wave r holds one per lane and ranks each against all
-    // others through lane reads
-    if (wave < rows && WANT_OF(wave) > 0 && TOTAL_OF(wave) <= kWave) {
-        const int r = wave;
-        int t = 0, x = lane;
-        for (int u = 0; u < nS; ++u) {
-            const int stt = ss.list_start[r][u];
-            if (lane >= stt) {
-                t = u;
-                x = lane - stt;
-            }
-        }
-        const bool live = lane < TOTAL_OF(r);
-        const uint32_t k = live ? st.key[r][t * kTop + x] : 0u;
-        const int32_t id = live ? st.id[r][t * kTop + x] : 0;
-        const uint64_t ord = ((uint64_t)k << 32) | (uint32_t)~id;  // token order (ids are non-negative)
-        int rank = 0;
-        for (int y = 0; y < TOTAL_OF(r); y += 4) {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) rank += wave_bcast(ord, y + d) > ord ? 1 : 0;
-        }
-        if (live && rank < WANT_OF(r)) {
-            ss.okey[r][rank] = k;
-            ss.oid[r][rank] = id;
-        }
-    }
-    // more (long lists: top candidates of many slices): the rank of every entry is its position
-    // in its own list plus a binary search in every other list of its row
-    if (total0 > kWave || total1 > kWave) {
-#pragma unroll 1
-        for (int i = threadIdx.x; i < 2 * nS * kTop; i += blockDim.x) {
-            const int r = i / (nS * kTop), t = (i / kTop) % nS, x = i % kTop;
-            if (r >= rows || WANT_OF(r) <= 0 || TOTAL_OF(r) <= kWave || x >= (int)ss.hdr[r][t][3]) continue;
-            const uint32_t k = st.key[r][t * kTop + x];
-            const int32_t id = st.id[r][t * kTop + x];
-            const uint64_t ord = ((uint64_t)k << 32) | (uint32_t)~id;
-            int rank = x;
-#pragma unroll 1
-            for (int t2 = 0; t2 < nS; ++t2) {
-                const int n = t2 == t ? 0 : (int)ss.hdr[r][t2][3];
-                int lo = 0, hi = n;  // entries of list t2 before `ord` in token order: [0, lo)
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    const int e = t2 * kTop + mid;
-                    const uint64_t o2 = ((uint64_t)st.key[r][e] << 32) | (uint32_t)~st.id[r][e];
-                    if (o2 > ord) lo = mid + 1;
-                    else hi = mid;
-                }
-                rank += lo;
-            }
-            if (rank < WANT_OF(r)) {
-                ss.okey[r][rank] = k;
-                ss.oid[r][rank] = id;
-            }
-        }
-    }
-    if (threadIdx.x < (unsigned)rows) ss.rv[threadIdx.x].nm = min(TOTAL_OF(threadIdx.x), WANT_OF(threadIdx.x));
-#undef WANT_OF
-#undef TOTAL_OF
-}
-
-// One thread's run of kSlotsPer consecutive slots of a row, in descending key order: the weight
-// of each slot is its kept count times the per-element mass exp((z - m) / T) (an aggregate of
-// specials carries its summed mass).  Every mass is the same function of (z - m) / T, so rows
-// that differ by a constant shift get bit-identical masses.  The run's counts are read in one
-// batch (each LDS read can queue behind other workgroups' histogram atomics).  With PICK the
-// sweep stops at the first slot whose weight takes the running mass from base to `need`
-// (need >= 0) or at slot `target`, and reports it.
-struct Pick {
-    int i;               // slot index in the run (-1: none)
-    double above, e, w;  // mass before it, its per-element mass, its weight
-    uint32_t cabove, n;  // kept elements before it, kept elements in it
-};
-template <bool PICK>
-__device__ __forceinline__ double sweep_run(const uint32_t* hist_r, const uint32_t* agg_n_r, const double* agg_m_r, int s0,
-                                            float m, double invT, int ks, uint32_t take_k, double base, uint32_t cbase,
-                                            double need, int target, int* last, Pick* pk) {
-    uint32_t c[kSlotsPer];
-#pragma unroll
-    for (int i = 0; i < kSlotsPer; ++i) {
-        const int s = s0 + i;
-        const int b = slot_bin(s);
-        c[i] = s >= kSlots ? 0u : (b >= 0 ? hist_r[b] : agg_n_r[slot_agg(s)]);
-    }
-    double cum = base;
-    uint32_t ccum = cbase;
-    if (PICK) pk->i = -1;
-    *last = -1;
-#pragma unroll 1
-    for (int i = 0; i < kSlotsPer; ++i) {
-        const int s = s0 + i;
-        if (s >= kSlots || s > ks) break;
-        if (c[i] == 0u) continue;
-        const int b = slot_bin(s);
-        uint32_t n;
-        double e = 0.0, w;
-        if (b < 0) {
-            n = c[i];
-            w = agg_m_r[slot_agg(s)];
-        } else {
-            e = mass_lean(key16_value(bin_key(b)), m, invT);
-            n = s == ks ? take_k : c[i];
-            w = (double)n * e;
-        }
-        *last = i;
-        if (PICK && ((need >= 0.0 && w > 0.0 && cum + w >= need) || s == target)) {
-            *pk = Pick{i, cum, e, w, ccum, n};
-            break;
-        }
-        cum += w;
-        ccum += n;
-    }
-    return cum - base;
-}
+// A compact list entry of an occupied scan slot: (slot << 20) | count (a count is at most
+// kMaxSlices * kSliceCols = 2^18).
+constexpr int kListShift = 20;
+constexpr uint32_t kListCount = (1u << kListShift) - 1u;
+static_assert(kMaxSlices * kSliceCols <= (int)kListCount && kSlots < (1 << (32 - kListShift)), "list entry fields");
 
 // ------------------------------------------------------------------------------------------
 // The settle step: both rows' processed distributions (maxima, normalisers, top-k and nucleus
 // cuts with their owner slices), the draft row's downweighted set (dw) and the drafted token's
-// processed probabilities.  All threads; hist(r) of the caller is free LDS (the slice's own
-// histograms are published by now) and holds the merged histograms.
+// processed probabilities.  All threads.  On entry sm.hist(r) holds this slice's (own) counts
+// of row r; the other slices' entries are added to them, and the merged rows are then turned
+// into compact lists of the occupied slots.
 // ------------------------------------------------------------------------------------------
 template <typename Smem>
-__device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int unit, int j, int rows,
+__device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int unit, int own, int j, int rows,
                                             const spec_params& prm, bool dw, int s_tok) {
     const VerifyArgs& a = f.a;
     SettleSmem& ss = sm.ss;
-    StageSmem& st = *reinterpret_cast<StageSmem*>(&sm.hraw[0][0]);
     const int nS = f.nS;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int want0 = list_len(a, prm, false);
     const int want1 = rows > 1 ? draft_list_len(f, prm, j) : 0;
-    // entries each (row, slice) loads with the headers: a power of two, at most kEntIt * kThreads
-    // in all and never past a record's kBins entries
-    int lg = 0;
-    while ((2 << lg) * rows * nS <= kEntIt * kThreads && (2 << lg) <= kBins) ++lg;
-    const int per = 1 << lg;
+    // (row, slice) groups of entries: 2^lgt threads each, kEntIt entries a thread per batch
+    const int G = rows * nS;
+    int lgt = 0;
+    while ((G << (lgt + 1)) <= kThreads) ++lgt;
+    const int tpg = 1 << lgt;
+    const int gi = tid >> lgt;
+    int gr = 0, gt = 0;
+    if (gi < G) row_slice(gi, nS, &gr, &gt);
+    const int cover = tpg * kEntIt;  // entries of a group the batch covers
 
-    // ---- round trip 1: headers, the first `per` entries of every slice, candidate lists ----
+    // ---- round trip 1: headers, the other slices' entries, the candidate lists ----
     u32x4 hw = {0u, 0u, 0u, 0u};
-    const bool hload = tid < rows * nS * 2;
+    const bool hload = tid < 2 * G;
     if (hload) {
         int r, t;
         row_slice(tid >> 1, nS, &r, &t);
         hw = ldnt(reinterpret_cast<const u32x4*>(part_c(f, unit, t, r)) + (tid & 1));
     }
     uint32_t ent[kEntIt];
+    const bool merge_mine = gi < G && gt != own;
 #pragma unroll
     for (int it = 0; it < kEntIt; ++it) {
-        const int i = tid + it * kThreads;
-        const int rt = i >> lg;
-        ent[it] = 0u;
-        if (rt < rows * nS) {
-            int r, t;
-            row_slice(rt, nS, &r, &t);
-            ent[it] = ldnt(&part_c(f, unit, t, r)->ent[i & (per - 1)]);
-        }
+        const int x = (tid & (tpg - 1)) + it * tpg;
+        ent[it] = (merge_mine && x < kBins) ? ldnt(&part_c(f, unit, gt, gr)->ent[x]) : 0u;
     }
-    constexpr int kCandLoads = 2 * kMaxSlices * kTop / kThreads;  // 4
-    uint32_t ck_[kCandLoads];
-    int32_t ci_[kCandLoads];
+    // candidates: thread u of row r stages positions u and u + 256 of the row's slice-major list
+    const int cr = tid / kRowThreads, cu = tid % kRowThreads;
+    const int cwant = cr < rows ? (cr ? want1 : want0) : 0;
+    const bool cstage = cwant > 0 && nS * cwant <= kStageCap;  // (more: the row takes the general path)
+    // (a listed candidate has a finite value, so its key and the order word are non-zero; slots
+    // past a slice's list and the padding to a multiple of 8 hold 0)
+    const int nst = cstage ? nS * cwant : 0, nst8 = (nst + 7) & ~7;
+    uint64_t cord[2] = {0ull, 0ull};
 #pragma unroll
-    for (int it = 0; it < kCandLoads; ++it) {
-        const int i = tid + it * kThreads;
-        const int r = i >> 10, t = (i >> 6) & (kMaxSlices - 1), x = i & (kTop - 1);
-        ck_[it] = 0u;
-        ci_[it] = 0;
-        if (r < rows && t < nS && x < (r ? want1 : want0)) {
-            const RowPart* P = part_c(f, unit, t, r);
-            ck_[it] = ldnt(&P->top_key[x]);
-            ci_[it] = ldnt(&P->top_id[x]);
+    for (int it = 0; it < 2; ++it) {
+        const int p = cu + it * kRowThreads;
+        if (p < nst) {
+            const int t = p / cwant, x = p - t * cwant;
+            const RowPart* P = part_c(f, unit, t, cr);
+            const uint64_t o = ((uint64_t)ldnt(&P->top_key[x]) << 32) | (uint32_t)~ldnt(&P->top_id[x]);
+            cord[it] = x < (int)ldnt(&P->n_top) ? o : 0ull;
         }
     }
     if (tid < 2) {
         ss.n_spm[tid] = 0u;
-        ss.cross[tid] = kNone;
+        ss.crossed[tid] = 0;
     }
     if (tid < 8) {
         ss.agg_n[tid >> 2][tid & 3] = 0u;
@@ -417,8 +311,47 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
 #pragma unroll
         for (int x = 0; x < 4; ++x) ss.hdr[r][t][4 * w + x] = hw[x];
     }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int p = cu + it * kRowThreads;
+        if (p < nst8) ss.stage[cr][p] = cord[it];
+    }
     __syncthreads();
-    // ---- per-row flags from the headers; candidate list offsets (wave r) ----
+
+    // header digest, in every wave (uniform values without a serial walk): lane l < G reads the
+    // first header words of (row, slice) l
+    u32x4 hv = {0u, 0u, 0u, 0u};
+    int hr = 0;
+    if (lane < G) {
+        int ht;
+        row_slice(lane, nS, &hr, &ht);
+        hv = *reinterpret_cast<const u32x4*>(&ss.hdr[hr][ht][0]);
+    }
+    const bool more_ent = __ballot(lane < G && (int)hv[1] > cover) != 0;  // entries past the batch
+    const uint32_t nsp0 = wave_sum(hr == 0 ? hv[2] : 0u), nsp1 = wave_sum(hr == 1 ? hv[2] : 0u);
+    const uint32_t fl0 = wave_or(hr == 0 ? hv[0] : 0u), fl1 = wave_or(hr == 1 ? hv[0] : 0u);
+
+    // ---- the other slices' entries into this slice's histograms; per-row flags; specials;
+    //      the candidates' ranks ----
+    if (merge_mine) {
+        const int n = (int)ss.hdr[gr][gt][1];
+#pragma unroll
+        for (int it = 0; it < kEntIt; ++it) {
+            const int x = (tid & (tpg - 1)) + it * tpg;
+            if (x < n) atomicAdd(&sm.hist(gr)[ent[it] >> 16], ent[it] & 0xFFFFu);
+        }
+    }
+    for (int g = 0; more_ent && g < G; ++g) {  // entries past the batch (uniform loop; rare)
+        int r, t;
+        row_slice(g, nS, &r, &t);
+        const int n = (int)ss.hdr[r][t][1];
+        if (n <= cover || t == own) continue;
+        const RowPart* P = part_u(f, unit, t, r);
+        for (int x = cover + tid; x < n; x += kThreads) {
+            const uint32_t e = ldnt(&P->ent[x]);
+            atomicAdd(&sm.hist(r)[e >> 16], e & 0xFFFFu);
+        }
+    }
     if (wave < rows) {
         const int r = wave;
         RowView& rv = ss.rv[r];
@@ -429,12 +362,11 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
         const uint32_t cnt = lv ? ss.hdr[r][lane][4] : 0u;
         const uint32_t xcc = lv ? ss.hdr[r][lane][7] : ss.hdr[r][0][7];
         const uint32_t flo = wave_or(fl);
-        int ls;
-        wave_scan((int)ntop, &ls);
-        if (lv) ss.list_start[r][lane] = ls;
         const int rank = (int)wave_sum(cnt);
         const uint32_t nsp_all = wave_sum(nsp);
+        const int ncand = (int)wave_sum(ntop);
         const bool xbad = __ballot(xcc != ss.hdr[r][0][7]) != 0;
+        const int want = r ? want1 : want0;
         if (lane == 0) {
             rv.invT = inv_temperature(prm.temperature);
             rv.greedy = prm.temperature == 0.0f ? 1 : 0;
@@ -450,54 +382,20 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
             rv.Z = 1.0;
             rv.degenerate = 0;
             rv.bad = (flo & 1u) ? 1 : 0;
-            rv.overflow = ((flo & 2u) || nsp_all > (uint32_t)kSpMerge) ? 1 : 0;
+            // too many specials, or more candidates than the stage holds: the general path
+            rv.overflow = ((flo & 2u) || nsp_all > (uint32_t)kSpMerge || nS * want > kStageCap) ? 1 : 0;
             rv.has_special = nsp_all > 0u ? 1 : 0;
             rv.s_bits = ss.hdr[r][0][5];
             rv.rank_s = rank;
             rv.xcc_bad = xbad ? 1u : 0u;
             rv.e_s = 0.0;
-        }
-    }
-    // ---- candidates to the stage, then merged ----
-#pragma unroll
-    for (int it = 0; it < kCandLoads; ++it) {
-        const int i = tid + it * kThreads;
-        const int r = i >> 10, t = (i >> 6) & (kMaxSlices - 1), x = i & (kTop - 1);
-        if (r < rows && t < nS && x < (int)ss.hdr[r][t][3] && x < (r ? want1 : want0)) {
-            st.key[r][t * kTop + x] = ck_[it];
-            st.id[r][t * kTop + x] = ci_[it];
-        }
-    }
-    __syncthreads();
-    merge_candidates(ss, st, nS, rows, want0, want1);
-    __syncthreads();
-    // ---- the merged histograms: zero, then every slice's entries; the rows' specials ----
-    for (int i = tid; i < rows * kHistRow / 4; i += kThreads)
-        reinterpret_cast<u32x4*>(&sm.hraw[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < kEntIt; ++it) {
-        const int i = tid + it * kThreads;
-        const int rt = i >> lg;
-        if (rt < rows * nS) {
-            int r, t;
-            row_slice(rt, nS, &r, &t);
-            if ((i & (per - 1)) < (int)ss.hdr[r][t][1]) atomicAdd(&sm.hist(r)[ent[it] >> 16], ent[it] & 0xFFFFu);
-        }
-    }
-    for (int rt = 0; rt < rows * nS; ++rt) {  // entries past the preloaded ones (uniform loop)
-        int r, t;
-        row_slice(rt, nS, &r, &t);
-        const int n = (int)ss.hdr[r][t][1];
-        if (n <= per) continue;
-        const RowPart* P = part_u(f, unit, t, r);
-        for (int x = per + tid; x < n; x += kThreads) {
-            const uint32_t e = ldnt(&P->ent[x]);
-            atomicAdd(&sm.hist(r)[e >> 16], e & 0xFFFFu);
+            rv.m = 0.0f;
+            rv.nm = min(ncand, want);
         }
     }
     for (int r = 0; r < rows; ++r) {  // specials (uniform loop; rows without them skip)
-        if (!ss.rv[r].has_special || ss.rv[r].overflow || ss.rv[r].bad) continue;
+        const uint32_t nsp_all = r ? nsp1 : nsp0, flo = r ? fl1 : fl0;
+        if (nsp_all == 0u || nsp_all > (uint32_t)kSpMerge || (flo & 3u)) continue;
         for (int i = tid; i < nS * kSpecial; i += kThreads) {
             const int t = i / kSpecial, x = i % kSpecial;
             if (x >= min((int)ss.hdr[r][t][2], kSpecial)) continue;
@@ -514,197 +412,265 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
             atomicMax(&ss.agg_key[r][g], k);
         }
     }
+    // candidate ranks in token order (key desc, id asc) over every slice's list of the row:
+    // the stage in batches of 8 (invalid slots hold 0, below every listed candidate)
+    if (nst > 0 && (cord[0] != 0ull || cord[1] != 0ull)) {
+        const uint64_t o0 = cord[0], o1 = cord[1];
+        int r0 = 0, r1 = 0;
+        const uint64_t* sl = ss.stage[cr];
+#pragma unroll 2
+        for (int q = 0; q < nst8; q += 8) {
+            uint64_t v[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) v[d] = sl[q + d];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                r0 += v[d] > o0 ? 1 : 0;
+                r1 += v[d] > o1 ? 1 : 0;
+            }
+        }
+        if (o0 != 0ull && r0 < cwant) {
+            ss.okey[cr][r0] = (uint32_t)(o0 >> 32);
+            ss.oid[cr][r0] = (int32_t)~(uint32_t)o0;
+        }
+        if (o1 != 0ull && r1 < cwant) {
+            ss.okey[cr][r1] = (uint32_t)(o1 >> 32);
+            ss.oid[cr][r1] = (int32_t)~(uint32_t)o1;
+        }
+    }
     __syncthreads();
 
-    // ---- pass A (counts): maximum, finite count, top-k cut; threads [256 r, 256 r + 256) ----
+    // ---- pass A (counts): maximum, finite count, top-k cut, the compact list of occupied
+    //      slots; threads [256 r, 256 r + 256), twelve consecutive slots each ----
     const int r = tid / kRowThreads;
     const int u = tid % kRowThreads;
     const bool live_row = r < rows;
-    RowView& rv = ss.rv[live_row ? r : 0];
+    const int rr0 = live_row ? r : 0;
+    RowView& rv = ss.rv[rr0];
     const int s0 = u * kSlotsPer;
-    // the count of slot i of this thread (read again where needed: registers are scarce here)
-    auto cnt_at = [&](int i) -> uint32_t {
-        const int s = s0 + i;
-        if (!live_row || s >= kSlots) return 0u;
-        const int b = slot_bin(s);
-        return b >= 0 ? sm.hist(r)[b] : ss.agg_n[r][slot_agg(s)];
-    };
-    int first = kNone;
-    uint32_t nloc = 0;
+    // (flags read before the scan: single threads update them after it)
+    const bool proc = live_row && !rv.bad && !rv.overflow;  // uniform per row
+    const bool greedy = live_row && rv.greedy;
+    const bool has_k = live_row && rv.has_k, has_p = live_row && rv.has_p, has_sp = live_row && rv.has_special;
+    uint32_t c[kSlotsPer];
+    uint32_t nloc = 0, nz = 0;
+    int first = -1;
 #pragma unroll
     for (int i = 0; i < kSlotsPer; ++i) {
-        const uint32_t n = cnt_at(i);
-        if (n != 0u && first == kNone) first = s0 + i;
-        nloc += n;
+        const int s = s0 + i;
+        const int b = slot_bin(s);
+        c[i] = (!live_row || s >= kSlots) ? 0u : (b >= 0 ? sm.hist(rr0)[b] : ss.agg_n[rr0][slot_agg(s)]);
+        nloc += c[i];
+        nz += c[i] != 0u ? 1u : 0u;
+        if (c[i] != 0u && first < 0) first = i;
     }
-    const int max_slot = row_min(first, ss.wi);
-    uint32_t cinc, nfin;
-    const uint32_t cexc = row_scan(nloc, ss.wu, &cinc, &nfin);
-    const bool proc = live_row && !rv.bad && !rv.overflow;  // uniform per row
-    float m = 0.0f;
-    if (live_row && max_slot != kNone) {
-        const int b = slot_bin(max_slot);
-        m = key16_value(b >= 0 ? bin_key(b) : ss.agg_key[r][slot_agg(max_slot)]);
-    }
-    const double invT = live_row ? rv.invT : 0.0;
-    const bool greedy = live_row && rv.greedy;
+    uint64_t pinc, ptot;
+    const uint64_t pexc = row_scan_u64(((uint64_t)nz << 32) | nloc, ss.wq, &pinc, &ptot);
+    const uint32_t cexc = (uint32_t)pexc, cinc = (uint32_t)pinc, nfin = (uint32_t)ptot;
+    const int zexc = (int)(pexc >> 32), n_occ = (int)(ptot >> 32);
     const int top_k = prm.top_k;
-    const bool k_over = live_row && rv.has_k && (uint32_t)top_k > nfin;
-    if (u == 0 && live_row) {
+    const bool k_over = has_k && (uint32_t)top_k > nfin;
+    if (live_row && u == 0) {
         rv.n_finite = nfin;
-        rv.m = m;
         if (nfin == 0u) rv.bad = 1;
         if (!greedy && k_over) rv.overflow = 1;  // -inf tokens would be kept
     }
+    if (live_row && cexc == 0u && nloc != 0u) {  // the first occupied slot: the maximum
+        const int s = s0 + first;
+        const int b = slot_bin(s);
+        rv.m = key16_value(b >= 0 ? bin_key(b) : ss.agg_key[r][slot_agg(s)]);
+    }
     const bool cuts = proc && !greedy && nfin > 0u && !k_over;  // uniform per row
-    if (cuts && rv.has_k && cexc < (uint32_t)top_k && cinc >= (uint32_t)top_k) {
-        uint32_t cum = cexc;
+    // the thread whose counts hold the top_k-th element places the top-k cut from the list
+    const bool k_thread = cuts && has_k && cexc < (uint32_t)top_k && cinc >= (uint32_t)top_k;
+    // the compact list, written over the histogram row (every count is read by now)
+    if (live_row) {
+        int o = zexc;
+#pragma unroll
+        for (int i = 0; i < kSlotsPer; ++i)
+            if (c[i] != 0u) sm.hist(r)[o++] = ((uint32_t)(s0 + i) << kListShift) | c[i];
+    }
+    __syncthreads();
+    if (prm.top_k > 0 && prm.top_k < a.V) {  // (uniform: both rows take the request's top_k)
+        if (k_thread) {
+            uint32_t cum = cexc;
 #pragma unroll 1
-        for (int i = 0; i < kSlotsPer; ++i) {
-            const uint32_t ci = cnt_at(i);
-            if (ci != 0u && cum + ci >= (uint32_t)top_k && cum < (uint32_t)top_k) {
-                const int s = s0 + i;
-                const int b = slot_bin(s);
-                if (b < 0) {
-                    rv.overflow = 1;  // the cut falls among specials: the general path
-                } else {
-                    rv.ck = Cut{bin_key(b), (int)((uint32_t)top_k - cum), -1, 0, 0, (int)cum, s};
-                    rv.n_kept = top_k;
+            for (int p = zexc; p < zexc + (int)nz; ++p) {
+                const uint32_t le = sm.hist(r)[p];
+                const uint32_t n = le & kListCount;
+                if (cum + n >= (uint32_t)top_k) {
+                    const int s = (int)(le >> kListShift);
+                    const int b = slot_bin(s);
+                    if (b < 0) {
+                        rv.overflow = 1;  // the cut falls among specials: the general path
+                    } else {
+                        rv.ck = Cut{bin_key(b), (int)((uint32_t)top_k - cum), -1, 0, 0, (int)cum, s};
+                        rv.n_kept = top_k;
+                    }
+                    break;
                 }
+                cum += n;
             }
-            cum += ci;
         }
+        __syncthreads();
     }
-    // the specials' masses (one wave per row with specials)
-    if (cuts && rv.has_special && (u >> 6) == 1) {
-        const int n = min((int)ss.n_spm[r], kSpMerge);
-        double ms[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int i = lane; i < n; i += kWave) {
-            const uint32_t k = ss.spk[r][i];
-            const double e = mass_lean(key16_value(k), m, invT);
-            const int g = agg_of_key(k);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) ms[x] += g == x ? e : 0.0;
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const double sx = wave_sum(ms[x]);
-            if (lane == 0) ss.agg_m[r][x] = sx;
-        }
-    }
-    __syncthreads();
 
-    // ---- pass B (masses): the kept mass, the nucleus cut and the normaliser ----
-    const bool cuts2 = cuts && !rv.overflow;
-    const int ks = (cuts2 && rv.has_k) ? rv.ck.slot : kNone;
-    const uint32_t take_k = (cuts2 && rv.has_k) ? (uint32_t)rv.ck.take : 0u;
-    const int rr0 = live_row ? r : 0;
-    const uint32_t* hist_r = sm.hist(rr0);
-    int last_i = -1;
-    Pick pk;
-    double wloc = 0.0;
-    if (cuts2 && nloc != 0u)
-        wloc = sweep_run<false>(hist_r, ss.agg_n[rr0], ss.agg_m[rr0], s0, m, invT, ks, take_k, 0.0, 0u, -1.0, -1, &last_i, &pk);
-    double winc, Skept;
-    const double wexc = row_scan(wloc, ss.wd, &winc, &Skept);
-    // the thread whose run holds top_p * S: [exc, inc] of neighbouring threads tile [0, S] (exc
-    // of one thread is inc of the one before, bit for bit), so one exists; the first one if
-    // rounding makes more
-    const double need = (double)prm.top_p * Skept;
-    if (cuts2) {
-        if (rv.has_p && wexc < need && winc >= need) atomicMin(&ss.cross[r], u);
-        ss.xbase[tid] = wexc;
-        ss.xcbase[tid] = cexc;
-        if (u == 0) {
-            rv.S_kept = Skept;
-            if (!rv.has_k) rv.n_kept = (int)nfin;
-            if (!rv.has_p) {
-                rv.S = Skept;
-                rv.n_nuc = rv.has_k ? top_k : (int)nfin;
+    // ---- the specials' masses (one wave per row with specials; rare) ----
+    const bool any_sp = (ss.rv[0].has_special && !ss.rv[0].overflow) || (rows > 1 && ss.rv[1].has_special && !ss.rv[1].overflow);
+    if (any_sp) {
+        if (cuts && has_sp && (u >> 6) == 1) {
+            const int n = min((int)ss.n_spm[r], kSpMerge);
+            const float m = rv.m;
+            const double invT = rv.invT;
+            double ms[4] = {0.0, 0.0, 0.0, 0.0};
+            for (int i = lane; i < n; i += kWave) {
+                const uint32_t k = ss.spk[r][i];
+                const double e = mass_lean(key16_value(k), m, invT);
+                const int g = agg_of_key(k);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) ms[x] += g == x ? e : 0.0;
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const double sx = wave_sum(ms[x]);
+                if (lane == 0) ss.agg_m[r][x] = sx;
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
-    // the crossing thread of each row settles the nucleus cut, its inputs read back from LDS
-    if (cuts2 && rv.has_p && u == ss.cross[r]) {
-        const double base = ss.xbase[tid], need2 = (double)prm.top_p * rv.S_kept;
-        const uint32_t cbase = ss.xcbase[tid];
-        const float mr = rv.m;
-        const double it = rv.invT;
-        const int ks2 = rv.has_k ? rv.ck.slot : kNone;
-        const uint32_t tk2 = rv.has_k ? (uint32_t)rv.ck.take : 0u;
-        int lst;
-        sweep_run<true>(hist_r, ss.agg_n[rr0], ss.agg_m[rr0], s0, mr, it, ks2, tk2, base, cbase, need2, -1, &lst, &pk);
-        bool partial = true;
-        if (pk.i < 0) {  // rounding: the run ends short of the scan's total; its last kept slot, whole
-            sweep_run<true>(hist_r, ss.agg_n[rr0], ss.agg_m[rr0], s0, mr, it, ks2, tk2, base, cbase, -1.0, s0 + lst, &lst,
-                            &pk);
-            partial = false;
+
+    // ---- the entries again for the owners of the cut ties (own slice included), in flight
+    //      while the masses are summed ----
+    uint32_t e2[kEntIt];
+#pragma unroll
+    for (int it = 0; it < kEntIt; ++it) {
+        const int x = (tid & (tpg - 1)) + it * tpg;
+        e2[it] = (gi < G && x < kBins) ? ldnt(&part_c(f, unit, gt, gr)->ent[x]) : 0u;
+    }
+
+    // ---- pass B (masses): the compact list spread evenly over the row's threads ----
+    const bool cuts2 = cuts && !rv.overflow;
+    const int ks = (cuts2 && has_k) ? rv.ck.slot : kNone;
+    const uint32_t take_k = (cuts2 && has_k) ? (uint32_t)rv.ck.take : 0u;
+    const float m = live_row ? rv.m : 0.0f;
+    const double invT = live_row ? rv.invT : 0.0;
+    const int per = (n_occ + kRowThreads - 1) / kRowThreads;
+    const int lo = min(u * per, n_occ), hi = min(lo + per, n_occ);
+    double wloc = 0.0;
+    uint32_t kloc = 0u;
+    if (cuts2) {
+#pragma unroll 1
+        for (int p = lo; p < hi; ++p) {
+            const uint32_t le = sm.hist(r)[p];
+            const int s = (int)(le >> kListShift);
+            if (s > ks) break;
+            const uint32_t n = s == ks ? take_k : (le & kListCount);
+            const int b = slot_bin(s);
+            wloc += b >= 0 ? (double)n * mass_lean(key16_value(bin_key(b)), m, invT) : ss.agg_m[r][slot_agg(s)];
+            kloc += n;
         }
-        const int s = s0 + pk.i;
-        const int b = pk.i >= 0 ? slot_bin(s) : -1;
+    }
+    // the drafted token's mass in each row (thread 255 of the row) and the masses of the draft
+    // row's leading candidates (its last wave), for the final step
+    const bool tok = dw && s_tok >= 0 && s_tok < a.V;
+    if (tok && live_row && !greedy && u == kRowThreads - 1) {
+        const uint32_t sb = rv.s_bits;  // exp((z_s - m) / T)
+        rv.e_s = ((sb & 0x7FFFu) < 0x7F80u && nfin > 0u) ? mass_lean(__uint_as_float(sb << 16), m, invT) : 0.0;
+    }
+    if (dw && r == 1 && cuts2 && a.F > 0 && a.C < 1.0f && u >= kRowThreads - kWave) {
+        const int l = u - (kRowThreads - kWave);
+        if (l < min(a.F, rv.nm)) ss.cand_e[l] = mass_lean(key16_value(ss.okey[1][l]), m, invT);
+    }
+    const Scan2 sc = row_scan2(wloc, kloc, ss);
+    const double Skept = sc.wtot;
+    const double need = (double)prm.top_p * Skept;
+    if (cuts2 && u == 0) {
+        rv.S_kept = Skept;
+        if (!has_k) rv.n_kept = (int)nfin;
+        if (!has_p) {
+            rv.S = Skept;
+            rv.n_nuc = has_k ? top_k : (int)nfin;
+        }
+    }
+    // the one thread whose interval (exc, inc] holds top_p * S places the nucleus cut
+    if (cuts2 && has_p && sc.wexc < need && need <= sc.winc) {
+        double cum = sc.wexc;
+        uint32_t ccum = sc.kexc;
+        int pick_s = -1;
+        double above = 0.0, pe = 0.0;
+        uint32_t pn = 0u, pcab = 0u;
+        bool partial = false;
+#pragma unroll 1
+        for (int p = lo; p < hi; ++p) {
+            const uint32_t le = sm.hist(r)[p];
+            const int s = (int)(le >> kListShift);
+            if (s > ks) break;
+            const uint32_t n = s == ks ? take_k : (le & kListCount);
+            const int b = slot_bin(s);
+            const double e = b >= 0 ? mass_lean(key16_value(bin_key(b)), m, invT) : 0.0;
+            const double w = b >= 0 ? (double)n * e : ss.agg_m[r][slot_agg(s)];
+            // the last kept slot stands in when rounding leaves the run short of need
+            pick_s = s;
+            above = cum;
+            pe = e;
+            pn = n;
+            pcab = ccum;
+            if (w > 0.0 && cum + w >= need) {
+                partial = true;
+                break;
+            }
+            cum += w;
+            ccum += n;
+        }
+        const int b = pick_s >= 0 ? slot_bin(pick_s) : -1;
         if (b < 0) {
             rv.overflow = 1;  // the cut falls among specials (or nowhere): the general path
         } else {
-            int take = (int)pk.n;
-            if (partial && pk.e > 0.0) {
-                const double q = ceil((need2 - pk.above) / pk.e);
-                take = q < 1.0 ? 1 : (q > (double)pk.n ? (int)pk.n : (int)q);
+            int take = (int)pn;
+            if (partial && pe > 0.0) {
+                const double q = ceil((need - above) / pe);
+                take = q < 1.0 ? 1 : (q > (double)pn ? (int)pn : (int)q);
             }
-            rv.cp = Cut{bin_key(b), take, -1, 0, 0, (int)pk.cabove, s};
-            rv.S = pk.above + (double)take * pk.e;
-            rv.n_nuc = (int)pk.cabove + take;
+            rv.cp = Cut{bin_key(b), take, -1, 0, 0, (int)pcab, pick_s};
+            rv.S = above + (double)take * pe;
+            rv.n_nuc = (int)pcab + take;
         }
+        ss.crossed[r] = 1;
     }
-    if (cuts2 && rv.has_p && u == 0 && ss.cross[r] == kNone) rv.overflow = 1;  // (not reached: see above)
     __syncthreads();
 
-    // ---- owners of the cut ties: every slice's count at each cut bin ----
-    // cut bins of (row, cut) as four scalars: CBIN(rr, cc)
+    // ---- owners of the cut ties: every slice's count at each cut bin; the downweighted set
+    //      and the drafted token's probabilities ----
     auto cut_bin = [&](int rr, int cc) {
         const RowView& v = ss.rv[rr];
         const bool ok = rr < rows && !v.bad && !v.overflow && !v.greedy;
-        const Cut& c = cc ? v.cp : v.ck;
-        return (ok && (cc ? v.has_p : v.has_k) && c.key != 0u) ? bin_of_key(c.key) : -1;
+        const Cut& ct = cc ? v.cp : v.ck;
+        return (ok && (cc ? v.has_p : v.has_k) && ct.key != 0u && ct.slot != kNone) ? bin_of_key(ct.key) : -1;
     };
     const int cb00 = cut_bin(0, 0), cb01 = cut_bin(0, 1), cb10 = cut_bin(1, 0), cb11 = cut_bin(1, 1);
 #define CBIN(rr, cc) ((rr) ? ((cc) ? cb11 : cb10) : ((cc) ? cb01 : cb00))
     const bool any_cut = cb00 >= 0 || cb01 >= 0 || cb10 >= 0 || cb11 >= 0;
-    if (any_cut) {
-        // the entries are read again from L2 (held in registers through the mass passes they
-        // would not fit the count kernel's register budget): the preload's batch, then any past it
-        uint32_t e2[kEntIt];
+    if (any_cut && gi < G) {
+        const int n = (int)ss.hdr[gr][gt][1];
+        const int c0b = CBIN(gr, 0), c1b = CBIN(gr, 1);
 #pragma unroll
         for (int it = 0; it < kEntIt; ++it) {
-            const int i = tid + it * kThreads;
-            const int rt = i >> lg;
-            e2[it] = 0u;
-            if (rt < rows * nS) {
-                int rr, t;
-                row_slice(rt, nS, &rr, &t);
-                if ((i & (per - 1)) < (int)ss.hdr[rr][t][1] && (CBIN(rr, 0) >= 0 || CBIN(rr, 1) >= 0))
-                    e2[it] = ldnt(&part_c(f, unit, t, rr)->ent[i & (per - 1)]);
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < kEntIt; ++it) {
-            const int i = tid + it * kThreads;
-            const int rt = i >> lg;
-            if (rt < rows * nS && e2[it] != 0u) {
-                int rr, t;
-                row_slice(rt, nS, &rr, &t);
+            const int x = (tid & (tpg - 1)) + it * tpg;
+            if (x < n) {
                 const int b = (int)(e2[it] >> 16);
-                if (b == CBIN(rr, 0)) ss.pc[rr][0][t] = e2[it] & 0xFFFFu;
-                if (b == CBIN(rr, 1)) ss.pc[rr][1][t] = e2[it] & 0xFFFFu;
+                if (b == c0b) ss.pc[gr][0][gt] = e2[it] & 0xFFFFu;
+                if (b == c1b) ss.pc[gr][1][gt] = e2[it] & 0xFFFFu;
             }
         }
-        for (int rt = 0; rt < rows * nS; ++rt) {  // entries past the batch (uniform loop; rare)
+    }
+    if (any_cut && more_ent) {
+        for (int g = 0; g < G; ++g) {  // entries past the batch (uniform loop; rare)
             int rr, t;
-            row_slice(rt, nS, &rr, &t);
+            row_slice(g, nS, &rr, &t);
             const int n = (int)ss.hdr[rr][t][1];
-            if (n <= per || (CBIN(rr, 0) < 0 && CBIN(rr, 1) < 0)) continue;
+            if (n <= cover || (CBIN(rr, 0) < 0 && CBIN(rr, 1) < 0)) continue;
             const RowPart* P = part_u(f, unit, t, rr);
-            for (int x = per + tid; x < n; x += kThreads) {
+            for (int x = cover + tid; x < n; x += kThreads) {
                 const uint32_t e3 = ldnt(&P->ent[x]);
                 const int b = (int)(e3 >> 16);
                 if (b == CBIN(rr, 0)) ss.pc[rr][0][t] = e3 & 0xFFFFu;
@@ -712,7 +678,62 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
             }
         }
     }
+    if (wave == 4 && rows > 1) {  // the draft row: downweighted set, then the token's probability
+        RowView& v = ss.rv[1];
+        // (every field read once, up front)
+        const bool vok = !v.greedy && !v.bad && !v.overflow;
+        const double S = v.S, e_s = v.e_s;
+        const int n_nuc = v.n_nuc, nm = v.nm, rank_s = v.rank_s;
+        const uint32_t sb = v.s_bits;
+        const bool hk = v.has_k, hp = v.has_p;
+        const uint32_t kk = v.ck.key, kp = v.cp.key;
+        const int tk = v.ck.take, tp = v.cp.take;
+        const bool want_set = dw && a.F > 0 && a.C < 1.0f && vok;
+        int n = 0;
+        double Cd = 1.0, Z = 1.0;
+        uint32_t kF = 0xFFFFFFFFu;
+        int idF = -1;
+        bool degen = false;
+        if (want_set) {
+            const int n0 = min(min(a.F, n_nuc), nm);
+            const double ec = lane < n0 ? ss.cand_e[lane] : 0.0;
+            n = last_lane(__ballot(lane < n0 && ec > 0.0)) + 1;
+            const double psum = wave_sum(lane < n ? ec / S : 0.0);
+            if (n > 0) {
+                kF = ss.okey[1][n - 1];
+                idF = ss.oid[1][n - 1];
+                const double Zc = 1.0 - (1.0 - (double)a.C) * psum;
+                if (Zc > 0.0) {
+                    Cd = (double)a.C;
+                    Z = Zc;
+                } else {
+                    degen = true;
+                }
+            }
+        }
+        if (lane == 0) {
+            if (tok && !v.greedy) {
+                const double p = prob_of_s(sb, rank_s, hk, kk, tk, hp, kp, tp, S, e_s);
+                const double fct = (n > 0 && e_s > 0.0 && in_cut_id(kF, idF, key16(sb), s_tok)) ? Cd : 1.0;
+                ss.ps = (p * fct) / Z;
+            }
+            if (want_set) {
+                v.nset = n;
+                v.kF = kF;
+                v.idF = idF;
+                v.C = Cd;
+                v.Z = Z;
+                v.degenerate = degen ? 1 : 0;
+            }
+        }
+    }
+    if (wave == 5 && tok && lane == 0 && !ss.rv[0].greedy) {  // the target row's probability
+        const RowView& v = ss.rv[0];
+        ss.qs = prob_of_s(v.s_bits, v.rank_s, v.has_k, v.ck.key, v.ck.take, v.has_p, v.cp.key, v.cp.take, v.S, v.e_s);
+    }
+    if (wave == 6 && lane < rows && ss.rv[lane].greedy) ss.rv[lane].argmax = ss.rv[lane].nm > 0 ? ss.oid[lane][0] : -1;
     __syncthreads();
+    if (cuts2 && has_p && u == 0 && !ss.crossed[r]) rv.overflow = 1;  // (no thread placed it)
     if (wave < 4 && any_cut) {  // wave 2 rr + c settles row rr's cut c
         const int rr = wave >> 1, cc = wave & 1;
         if (CBIN(rr, cc) >= 0) {
@@ -720,52 +741,15 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
             const int nt = lane < nS ? (int)ss.pc[rr][cc][lane] : 0;
             int tex;
             const int tin = wave_scan(nt, &tex);
-            const int own = first_lane(__ballot(lane < nS && tin >= cut.take));
-            const int before = wave_bcast(tex, own < 0 ? 0 : own);
+            const int own_l = first_lane(__ballot(lane < nS && tin >= cut.take));
+            const int before = wave_bcast(tex, own_l < 0 ? 0 : own_l);
             if (lane == 0) {
-                cut.owner = own < 0 ? nS - 1 : own;
-                cut.owner_take = own < 0 ? 0 : cut.take - before;
+                cut.owner = own_l < 0 ? nS - 1 : own_l;
+                cut.owner_take = own_l < 0 ? 0 : cut.take - before;
             }
         }
     }
 #undef CBIN
-    __syncthreads();
-    // ---- greedy argmax, the downweighted set, the drafted token's probabilities ----
-    if (wave < rows && lane == 0 && ss.rv[wave].greedy) ss.rv[wave].argmax = ss.rv[wave].nm > 0 ? ss.oid[wave][0] : -1;
-    if (dw && rows > 1 && wave == 1) {
-        RowView& v = ss.rv[1];
-        const bool want_set = a.F > 0 && a.C < 1.0f && !v.greedy && !v.bad && !v.overflow;
-        if (want_set) {
-            const int n0 = min(min(a.F, v.n_nuc), v.nm);
-            const double e2 = lane < n0 ? mass_lean(key16_value(ss.okey[1][lane]), v.m, v.invT) : 0.0;
-            const int n = last_lane(__ballot(lane < n0 && e2 > 0.0)) + 1;
-            const double ps = wave_sum(lane < n ? e2 / v.S : 0.0);
-            if (lane == 0) {
-                v.nset = n;
-                if (n > 0) {
-                    v.kF = ss.okey[1][n - 1];
-                    v.idF = ss.oid[1][n - 1];
-                    const double Cd = (double)a.C;
-                    const double Z = 1.0 - (1.0 - Cd) * ps;
-                    if (Z > 0.0) {
-                        v.C = Cd;
-                        v.Z = Z;
-                    } else {
-                        v.degenerate = 1;
-                    }
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (dw && s_tok >= 0 && s_tok < a.V && wave < rows && lane == 0 && !ss.rv[wave].greedy) {
-        RowView& v = ss.rv[wave];
-        const uint32_t sb = v.s_bits;  // the drafted token's mass exp((z_s - m) / T)
-        v.e_s = ((sb & 0x7FFFu) < 0x7F80u && v.n_finite > 0u) ? mass_lean(__uint_as_float(sb << 16), v.m, v.invT) : 0.0;
-        const double p = prob_of_s(ss, wave, s_tok, wave == 1);
-        if (wave == 0) ss.qs = p;
-        else ss.ps = p;
-    }
     __syncthreads();
 }
 
