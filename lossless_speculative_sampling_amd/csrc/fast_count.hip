@@ -20,9 +20,11 @@ struct CountSmem {
     uint32_t sp_key[2][kSpecial];
     int32_t sp_id[2][kSpecial];
     uint32_t n_sp[2];
-    uint32_t top_key[2][kTop];
-    int32_t top_id[2][kTop];
-    uint32_t n_top[2];
+    uint32_t th_tau[2];  // each row's candidate threshold (Threshold) from the entry scan
+    int32_t th_need[2];
+    int32_t th_ties[2];
+    uint64_t red64[kWaves];
+    uint32_t n_ent[2];   // occupied bins per row (entries published)
     uint32_t cnt_s[2];
     uint32_t flags[2];
     uint32_t neginf[2];
@@ -158,36 +160,40 @@ __device__ __forceinline__ TopMarks top_marks(const Threshold& th, int c0, int V
 }
 
 // The first L[r] elements (token order: key desc, id asc) of each row r in this slice (none for
-// L[r] = 0), sorted, into sm.top_key[r] / sm.top_id[r]; sm.n_top[r] gets their number.  One
-// pass marks every thread's elements at or above each row's threshold; one workgroup scan of
-// both rows' mark counts (at most L[r] <= 64 each, packed in 16-bit halves) gives each marked
-// element its slot in thread order, so no atomics; the elements at a threshold of which only
-// some are needed follow in token order (rare); then wave r sorts row r's list, both at once.
-// The caller synchronises afterwards.
-__device__ __forceinline__ void local_tops(CountSmem& sm, const int (&L)[2], int c0, int V, const u32x4 (&vq)[kLoads],
-                                           const u32x4 (&vp)[kLoads]) {
+// L[r] = 0), in no particular order, straight into the rows' records (top_key / top_id); returns
+// their numbers in n.  The threshold of a row comes from the entry scan (sm.th_*) or, for a row
+// with values outside the bins (slow), from the segment counts.  One pass marks every thread's
+// elements above each row's threshold (and at it when every element there is needed); one
+// workgroup scan of both rows' mark counts (at most L[r] <= 64 each, packed in 16-bit halves)
+// gives each marked element its slot in thread order; the elements at a threshold of which only
+// some are needed follow in token order (rare).  The settle step ranks the lists itself.
+__device__ __forceinline__ void local_tops(const FastArgs& f, CountSmem& sm, int unit, int slice, const int (&L)[2],
+                                           const bool (&slow)[2], int c0, int V, const u32x4 (&vq)[kLoads],
+                                           const u32x4 (&vp)[kLoads], int (&n)[2]) {
     Threshold th[2] = {{0u, 0, 0}, {0u, 0, 0}};
     uint32_t cand[2] = {0u, 0u}, ties[2] = {0u, 0u};
-    if (L[0] > 0) {
-        th[0] = local_threshold(sm, 0, L[0]);
-        const TopMarks m = top_marks(th[0], c0, V, vq);
-        cand[0] = m.cand;
-        ties[0] = m.ties;
-    }
-    if (L[1] > 0) {
-        th[1] = local_threshold(sm, 1, L[1]);
-        const TopMarks m = top_marks(th[1], c0, V, vp);
-        cand[1] = m.cand;
-        ties[1] = m.ties;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (L[r] <= 0) continue;
+        th[r] = slow[r] ? local_threshold(sm, r, L[r]) : Threshold{sm.th_tau[r], sm.th_need[r], sm.th_ties[r]};
+        // (uniform values: kept in scalar registers)
+        th[r].tau = __builtin_amdgcn_readfirstlane(th[r].tau);
+        th[r].need = __builtin_amdgcn_readfirstlane(th[r].need);
+        th[r].ties = __builtin_amdgcn_readfirstlane(th[r].ties);
+        const TopMarks m = top_marks(th[r], c0, V, r ? vp : vq);
+        cand[r] = m.cand;
+        ties[r] = m.ties;
     }
     int total;
     const int before = block_exclusive_scan<int>(__popc(cand[0]) | (__popc(cand[1]) << 16), sm.scan, &total);
-    int n[2] = {total & 0xFFFF, total >> 16};
+    n[0] = total & 0xFFFF;
+    n[1] = total >> 16;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        int slot = r ? before >> 16 : before & 0xFFFF;
         const uint32_t m = cand[r];
         if (m == 0u) continue;
+        RowPart* P = part_of(f, unit, slice, r);
+        int slot = r ? before >> 16 : before & 0xFFFF;
 #pragma unroll
         for (int q = 0; q < kLoads; ++q) {
 #pragma unroll
@@ -195,8 +201,8 @@ __device__ __forceinline__ void local_tops(CountSmem& sm, const int (&L)[2], int
                 if (!((m >> (q * 8 + e)) & 1u)) continue;
                 if (slot < kTop) {
                     const uint32_t w = r ? vp[q][e >> 1] : vq[q][e >> 1];
-                    sm.top_key[r][slot] = key16((w >> (16 * (e & 1))) & 0xFFFFu);
-                    sm.top_id[r][slot] = col_of(c0, q, e);
+                    P->top_key[slot] = key16((w >> (16 * (e & 1))) & 0xFFFFu);
+                    P->top_id[slot] = col_of(c0, q, e);
                 }
                 ++slot;
             }
@@ -206,6 +212,7 @@ __device__ __forceinline__ void local_tops(CountSmem& sm, const int (&L)[2], int
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         if (L[r] <= 0 || th[r].ties == th[r].need) continue;
+        RowPart* P = part_of(f, unit, slice, r);
         int need_left = th[r].need;
         for (int q = 0; q < kLoads && need_left > 0; ++q) {
             const uint32_t mq = (ties[r] >> (q * 8)) & 0xFFu;
@@ -217,8 +224,8 @@ __device__ __forceinline__ void local_tops(CountSmem& sm, const int (&L)[2], int
                 const int rank = pre + k++;
                 const int slot = n[r] + rank;
                 if (rank < need_left && slot < kTop) {
-                    sm.top_key[r][slot] = th[r].tau;
-                    sm.top_id[r][slot] = col_of(c0, q, e);
+                    P->top_key[slot] = th[r].tau;
+                    P->top_id[slot] = col_of(c0, q, e);
                 }
             }
             const int took = min(cnt, need_left);
@@ -226,26 +233,8 @@ __device__ __forceinline__ void local_tops(CountSmem& sm, const int (&L)[2], int
             need_left -= took;
         }
     }
-    __syncthreads();
-    // sort (key desc, id asc): each lane ranks its entry against the list through broadcast reads
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    if (wave < 2 && (wave ? L[1] : L[0]) > 0) {
-        const int r = wave;
-        const int cnt = min(wave ? n[1] : n[0], kTop);
-        const bool live = lane < cnt;
-        const uint32_t mk = live ? sm.top_key[r][lane] : 0u;
-        const int mi = live ? sm.top_id[r][lane] : 0;
-        const uint64_t ord = ((uint64_t)mk << 32) | (uint32_t)~mi;  // ids are non-negative
-        int rank = 0;
-#pragma unroll 4
-        for (int y = 0; y < cnt; ++y)
-            rank += (((uint64_t)sm.top_key[r][y] << 32) | (uint32_t)~sm.top_id[r][y]) > ord ? 1 : 0;
-        if (live) {
-            sm.top_key[r][rank] = mk;
-            sm.top_id[r][rank] = mi;
-        }
-        if (lane == 0) sm.n_top[r] = (uint32_t)cnt;
-    }
+    n[0] = min(n[0], kTop);
+    n[1] = min(n[1], kTop);
 }
 
 // Elements of each row in this slice with the draft token's key that precede the token (token
@@ -298,26 +287,35 @@ __device__ __forceinline__ void local_ranks(CountSmem& sm, bool two, int c0, int
     if (threadIdx.x < (unsigned)rows) sm.cnt_s[threadIdx.x] = (packed >> (16 * threadIdx.x)) & 0xFFFFu;
 }
 
-// Publishes both rows' slice summaries (RowPart): the occupied bins as (bin, count) entries in
-// ascending bin order, the groups of 64 bins the slice holds, the specials, the candidate list,
-// the drafted token's value and rank, and the header.  Thread t reads bins [6t, 6t + 6); one
-// workgroup scan of both rows' entry counts (16-bit halves) places every entry.
-__device__ __forceinline__ void publish_sparse(const FastArgs& f, CountSmem& sm, int unit, int slice, bool two) {
+// Places both rows' occupied bins as (bin, count) entries in ascending bin order (returns this
+// thread's exclusive scan word for write_entries) and collects the groups of 64 bins the slice
+// holds; thread t reads bins [6t, 6t + 6).  One workgroup scan of both rows' entry and element
+// counts places every entry and tells each thread how many of the row's binned elements lie
+// above its bins, so for a row listing L > 0 candidates without values outside the bins (fast)
+// the thread holding the L-th element from the top records it as the row's threshold (sm.th_*:
+// key, elements taken at it, elements there; 0 when the slice holds fewer than L).  n_ent gets
+// the entry counts (sm.n_ent).
+__device__ __forceinline__ uint32_t scan_entries(CountSmem& sm, bool two, const int (&L)[2], const bool (&fast)[2]) {
     constexpr int kPer = 6;
     constexpr int kPubThreads = kBins / kPer;  // 480
     static_assert(kPer * kPubThreads == kBins && kPubThreads <= kThreads, "bins per thread");
     const int rows = two ? 2 : 1;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    uint32_t cnt[2][kPer];
-    int nz[2] = {0, 0};
+    const int wave = tid / kWave;
+    // (the counts are read again after the scan: the columns stay live in registers meanwhile)
+    uint32_t nz[2] = {0u, 0u}, cs[2] = {0u, 0u};
     uint64_t gm[2] = {0ull, 0ull};
+    const int b0 = tid < kPubThreads ? tid * kPer : 0;  // (reads are unconditional, then masked)
+    const bool mine = tid < kPubThreads;
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            cnt[r][i] = (r < rows && tid < kPubThreads) ? sm.hist(r)[tid * kPer + i] : 0u;
-            if (cnt[r][i] != 0u) {
+            const uint32_t c0 = sm.hist(r)[b0 + i];
+            const uint32_t c = (r < rows && mine) ? c0 : 0u;
+            cs[r] += c;
+            if (c != 0u) {
                 ++nz[r];
                 gm[r] |= 1ull << ((tid * kPer + i) / kGroup);
             }
@@ -330,29 +328,89 @@ __device__ __forceinline__ void publish_sparse(const FastArgs& f, CountSmem& sm,
             atomicOr(&sm.grp[r][1], hi);
         }
     }
-    int total;
-    const int before = block_exclusive_scan<int>(nz[0] | (nz[1] << 16), sm.scan, &total);
+    // entries (12 bits) and elements (15 bits) of both rows in one 64-bit scan (one barrier)
+    const uint64_t v = (uint64_t)nz[0] | ((uint64_t)cs[0] << 12) | ((uint64_t)nz[1] << 27) | ((uint64_t)cs[1] << 39);
+    uint64_t exc;
+    const uint64_t inc = wave_scan(v, &exc);
+    if (lane == kWave - 1) sm.red64[wave] = inc;
+    __syncthreads();
+    uint64_t before = 0ull, total = 0ull;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const uint64_t x = sm.red64[w];
+        if (w < wave) before += x;
+        total += x;
+    }
+    exc += before;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
+        const int sh = r ? 27 : 0;
+        if (tid == 0) sm.n_ent[r] = (uint32_t)((total >> sh) & 0xFFFu);
         if (r >= rows) break;
-        RowPart* P = part_of(f, unit, slice, r);
-        int o = (before >> (16 * r)) & 0xFFFF;
+        if (fast[r] && L[r] > 0) {
+            uint32_t cnt[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (cnt[r][i] != 0u) P->ent[o++] = ((uint32_t)(tid * kPer + i) << 16) | cnt[r][i];
+            for (int i = 0; i < kPer; ++i) cnt[i] = mine ? sm.hist(r)[b0 + i] : 0u;
+            const uint32_t all = (uint32_t)(total >> (sh + 12)) & 0x7FFFu;
+            const uint32_t below = (uint32_t)(exc >> (sh + 12)) & 0x7FFFu;
+            const uint32_t above = all - below - cs[r];  // binned elements in higher bins
+            if (above < (uint32_t)L[r] && above + cs[r] >= (uint32_t)L[r]) {
+                uint32_t cum = above;
+                bool done = false;
+#pragma unroll
+                for (int i = kPer - 1; i >= 0; --i) {
+                    if (!done && cnt[i] != 0u && cum + cnt[i] >= (uint32_t)L[r]) {
+                        done = true;
+                        sm.th_tau[r] = bin_key(tid * kPer + i);
+                        sm.th_need[r] = (int)((uint32_t)L[r] - cum);
+                        sm.th_ties[r] = (int)cnt[i];
+                    }
+                    cum += cnt[i];
+                }
+            }
+        }
+    }
+    return (uint32_t)(exc & 0xFFFu) | ((uint32_t)((exc >> 27) & 0xFFFu) << 12);
+}
+
+// Writes both rows' entries at the places the scan gave them (pos: this thread's first entry of
+// row 0 and of row 1, 12 bits each).
+__device__ __forceinline__ void write_entries(const FastArgs& f, const CountSmem& sm, int unit, int slice, bool two,
+                                              uint32_t pos) {
+    constexpr int kPer = 6;
+    constexpr int kPubThreads = kBins / kPer;
+    const int tid = threadIdx.x;
+    if (tid >= kPubThreads) return;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (r == 1 && !two) break;
+        RowPart* P = part_of(f, unit, slice, r);
+        int o = (int)((pos >> (r ? 12 : 0)) & 0xFFFu);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const uint32_t c = sm.hist(r)[tid * kPer + i];
+            if (c != 0u) P->ent[o++] = ((uint32_t)(tid * kPer + i) << 16) | c;
+        }
+    }
+}
+
+// The rest of both rows' slice summaries (RowPart): the specials, the drafted token's value and
+// rank, and the header (after the candidates, whose number it holds).
+__device__ __forceinline__ void publish_header(const FastArgs& f, CountSmem& sm, int unit, int slice, bool two,
+                                               const int (&n_top)[2]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (r == 1 && !two) break;
+        RowPart* P = part_of(f, unit, slice, r);
         const int nsp = min((int)sm.n_sp[r], kSpecial);
         if (tid < nsp) {
             P->sp_key[tid] = sm.sp_key[r][tid];
             P->sp_id[tid] = sm.sp_id[r][tid];
         }
-        if (tid < (int)sm.n_top[r]) {
-            P->top_key[tid] = sm.top_key[r][tid];
-            P->top_id[tid] = sm.top_id[r][tid];
-        }
         if (tid == r) {
             const uint32_t flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u) | (sm.rare[r] ? 4u : 0u);
-            reinterpret_cast<u32x4*>(P)[0] = u32x4{flags, (uint32_t)((total >> (16 * r)) & 0xFFFF), (uint32_t)nsp,
-                                                    sm.n_top[r]};
+            reinterpret_cast<u32x4*>(P)[0] = u32x4{flags, sm.n_ent[r], (uint32_t)nsp, (uint32_t)n_top[r]};
             reinterpret_cast<u32x4*>(P)[1] = u32x4{sm.cnt_s[r], sm.s_bits[r], sm.neginf[r], sm.xcc};
             P->groups[0] = sm.grp[r][0];
             P->groups[1] = sm.grp[r][1];
@@ -492,7 +550,7 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
         U->accept = accept;
         U->status = status;
         U->fallback = fallback;
-        U->u_res = sm.u_res;
+        U->u_res = param_ok ? sm.u_res : 0.0;  // (no draws for a request with bad parameters)
         if (param_ok) {
             for (int r = 0; r < (two ? 2 : 1); ++r) {
                 const RowView& rv = us.rv[r];
@@ -654,7 +712,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     const int c0 = slice * kSliceCols;
     // the draft row of position j: verified (j < K) or, at the bonus position, only listed for
     // the outcome cache
-    const bool two = !f.uniform && (j < a.K || (f.cache && f.fan.f[j] > 0));
+    // (uniform: kept in a scalar register)
+    const bool two = __builtin_amdgcn_readfirstlane((!f.uniform && (j < a.K || (f.cache && f.fan.f[j] > 0))) ? 1 : 0) != 0;
     const spec_params prm = a.params[P.b];
     const bool param_ok = params_ok(prm);
     const size_t stride = (size_t)a.V;
@@ -667,9 +726,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     const bool tok_ok = j == a.K || (s_tok >= 0 && s_tok < a.V);
 
     // the draws of position j (acceptance, residual / bonus: words 0 and 1 of one Philox
-    // block), in the shadow of the first loads (wave 1 only; the empty asm keeps them here
-    // rather than where the settle step reads them)
-    double u_acc = 0.0, u_res = 0.0;
+    // block), in the shadow of the first loads (wave 1 only), kept in LDS for the settle step
     if (param_ok) {  // (a request with bad parameters is reported without its summaries)
         // (without a draft row the second set re-reads the target and goes unused: unconditional
         // loads keep the compiler's waits exact)
@@ -678,9 +735,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
         load_slice(two ? drow : trow, c0, a.V, vp);
         if (threadIdx.x / kWave == 1) {
             const Block4 x = philox4x64_10(a.round, (uint64_t)P.b, (uint64_t)j, 0, a.seed, 0);
-            u_acc = word_to_uniform(x.w[0]);
-            u_res = word_to_uniform(x.w[1]);
-            asm volatile("" ::"s"(u_acc), "s"(u_res));
+            if (threadIdx.x == kWave) {
+                sm.u_acc = word_to_uniform(x.w[0]);
+                sm.u_res = word_to_uniform(x.w[1]);
+            }
         }
         for (int i = threadIdx.x; i < 2 * kHistRow / 4; i += blockDim.x)
             reinterpret_cast<u32x4*>(&sm.hraw[0][0])[i] = u32x4{0, 0, 0, 0};
@@ -712,23 +770,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
         if (rare0) count_rare(sm, 0, c0, a.V, vq);
         if (rare1) count_rare(sm, 1, c0, a.V, vp);
         if (threadIdx.x < 2) {
-            sm.n_top[threadIdx.x] = 0;
             sm.cnt_s[threadIdx.x] = 0;
             sm.rare[threadIdx.x] = threadIdx.x == 0 ? rare0 : rare1;
+            sm.th_tau[threadIdx.x] = 0u;
+            sm.th_need[threadIdx.x] = 0;
+            sm.th_ties[threadIdx.x] = 0;
         }
         __syncthreads();
-        // passes over the columns (registers) first, so the columns are dead for the summaries
+        // the summaries; passes over the columns (registers) while they are still live
         const bool holds_s = j < a.K && tok_ok && s_tok >= c0;  // at or after this slice: count its key
-        const int want_q = list_len(a, prm, false), want_p = two ? draft_list_len(f, prm, j) : 0;
-        if (want_q > 0 || want_p > 0) {
-            seg_counts(sm, two ? 2 : 1);
-            __syncthreads();
-            const int want[2] = {want_q, want_p};
-            local_tops(sm, want, c0, a.V, vq, vp);
-        }
+        const int want[2] = {list_len(a, prm, false), two ? draft_list_len(f, prm, j) : 0};
+        // rows with values outside the bins find their candidate threshold from segment counts
+        const bool slow[2] = {want[0] > 0 && sm.n_sp[0] > 0u, want[1] > 0 && sm.n_sp[1] > 0u};
+        const bool fast[2] = {!slow[0], !slow[1]};
+        int n_top[2] = {0, 0};
+        const uint32_t ent_pos = scan_entries(sm, two, want, fast);
+        if (slow[0] || slow[1]) seg_counts(sm, two ? 2 : 1);
         if (holds_s) local_ranks(sm, two, c0, s_tok, vq, vp);
         __syncthreads();
-        publish_sparse(f, sm, unit, slice, two);
+        if (want[0] > 0 || want[1] > 0) local_tops(f, sm, unit, slice, want, slow, c0, a.V, vq, vp, n_top);
+        write_entries(f, sm, unit, slice, two, ent_pos);
+        publish_header(f, sm, unit, slice, two, n_top);
     }
 
     // ---- unit rendezvous: the last slice of the unit settles it ----
@@ -742,10 +804,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     }
     __syncthreads();
     if (!sm.last) return;
-    if (threadIdx.x == kWave) {  // read after the settle step's first barrier
-        sm.u_acc = u_acc;
-        sm.u_res = u_res;
-    }
     settle_unit(f, sm, P, prm, param_ok, two, s_tok, tok_ok);
 
     // ---- request rendezvous: the last unit of the request decides k ----
