@@ -48,12 +48,23 @@ def measured_traffic(kernel_bytes_per_launch):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds_target=15.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, seconds_target=15.0, nthreads=0):
     """The oracle as it stands on the host cores, on a bounded sample of the same workload."""
     import numpy as np
 
     import oracle
-    nthreads = oracle.threads_used(0)
+    nthreads = oracle.threads_used(nthreads)
     wc = w.without_cache_row()
     fan = np.array(oracle.fanout(w.K, w.budget, w.a, w.r)[1], np.int32)
     t0 = time.perf_counter()
@@ -69,7 +80,64 @@ def cpu_baseline(w, seconds_target=15.0):
             break
     return {"value": w.B * w.K * steps / el, "unit": "verified positions/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{steps} full steps (B={w.B}, K={w.K}, V={w.V}: verify with sampled draft tokens + cache "
-                      f"build + lookup) in {el:.1f} s, fp64, std::thread over requests/rows"}
+                      f"build + lookup) in {el:.1f} s, fp64, std::thread over requests/rows",
+            "cpu_model": cpu_model()}
+
+
+def read_ceiling(step_bytes, copies, dev, reps=50):
+    """Measured plain streaming read of step_bytes (rotated over `copies` buffers, so from HBM):
+    the bandwidth the call's own rate is set against besides the spec peak."""
+    import torch
+
+    from lossless_speculative_sampling_amd import capi
+    bufs = [torch.empty(step_bytes // 16 * 16, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for i in range(5):
+        capi.spec_read_ceiling(bufs[i % copies], sink)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        capi.spec_read_ceiling(bufs[i % copies], sink)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+    del bufs
+    return {"bytes": step_bytes // 16 * 16, "avg_ms": ms, "GBps": step_bytes / (ms * 1e-3) / 1e9,
+            "kernel": "spec_read_ceiling (16-byte non-temporal loads, 2048 x 256 threads)"}
+
+
+def acceptance_reports(w, run_round, B, K, rounds=100):
+    """Secondary reports over `rounds` verification rounds of the same inputs (rounds differ only in
+    their draws): per-request and all-request cache hit rates at C = 0.3 and at C = 1 (no
+    downweight), the all-hit rate next to the product of the per-request rates, and the k
+    histogram next to the acceptance-length law a^j (1 - a) (a^K at j = K)."""
+    import numpy as np
+    out = {}
+    ks = None
+    for C in (w.C, 1.0):
+        hits, kk = [], []
+        for i in range(rounds):
+            k, hit = run_round(10_000 + i, C)
+            hits.append(hit)
+            kk.append(k)
+        hits = np.array(hits, np.float64)
+        per = hits.mean(axis=0)
+        out[f"C={C:g}"] = {"per_request_hit_rate": [round(float(x), 4) for x in per],
+                           "mean_hit_rate": float(per.mean()), "all_hit_rate": float(hits.min(axis=1).mean()),
+                           "product_of_per_request_rates": float(np.prod(per)), "rounds": rounds}
+        if ks is None:
+            ks = np.array(kk)
+    hist = np.bincount(ks.ravel(), minlength=K + 1)[: K + 1]
+    trials = int(ks.sum() + (ks < K).sum())  # positions tested: accepted ones plus the first rejection
+    a_hat = float(ks.sum() / trials) if trials else 0.0
+
+    def law(a):
+        return [a ** j * (1 - a) for j in range(K)] + [a ** K]
+    out["k_histogram"] = {"C": w.C, "samples": int(ks.size), "observed": (hist / ks.size).round(4).tolist(),
+                          "a_fit": a_hat, "law_a_fit": [round(x, 4) for x in law(a_hat)],
+                          "a_config": w.a, "law_a_config": [round(x, 4) for x in law(w.a)]}
+    return out
 
 
 def timed_oracle(run, unit_count, unit, sample, seconds_target=10.0, max_reps=200):
@@ -172,13 +240,19 @@ def bench_other(name, args):
         import oracle
         nb = min(B, 16)
         tok_np = tokens[:nb].cpu().numpy()
+        flagged = [0, 0]
 
         def run(nthreads, rep):
-            oracle.verify(None if uniform else w.draft[:nb], w.target[:nb], w.dtype, K, w.params()[:nb], F=w.F,
-                          C=float(np.float32(w.C)), tokens=None if uniform else tok_np, seed=w.seed, round_=rep,
-                          nthreads=nthreads, uniform_draft=uniform)
+            r = oracle.verify(None if uniform else w.draft[:nb], w.target[:nb], w.dtype, K, w.params()[:nb], F=w.F,
+                              C=float(np.float32(w.C)), tokens=None if uniform else tok_np, seed=w.seed, round_=rep,
+                              nthreads=nthreads, uniform_draft=uniform)
+            flagged[0] += int((r.flags != 0).sum())
+            flagged[1] += nb
         res["cpu_baseline"] = timed_oracle(run, nb * K, "verified positions/s",
                                            f"{nb} requests of the workload (K={K}, V={V})")
+        res["cpu_baseline"]["cpu_model"] = cpu_model()
+        res["reports"] = {"flagged_near_ties": {"flagged": flagged[0], "requests": flagged[1],
+                                                "sample": "the oracle runs of the CPU baseline (rounds 0, 1, ...)"}}
     print(json.dumps(res), flush=True)
 
 
@@ -466,6 +540,25 @@ def main():
 
     achieved = step_bytes / (verify_ms * 1e-3) / 1e9
     positions = B * K
+    ceiling = read_ceiling(step_bytes, copies, dev)
+
+    # secondary reports (untimed): hit rates, k histogram
+    hit_t = torch.empty(B, dtype=torch.uint8, device=dev)
+
+    def run_round(rnd, C):
+        d, t = drafts[0], targets[0]
+        rc = L.saguaro_verify_cache(d.data_ptr(), t.data_ptr(), capi.SPEC_BF16, B, K, V, prm.data_ptr(), w.F,
+                                    ctypes.c_float(C), tokens.data_ptr(), w.seed, rnd, 0, w.budget, w.a, w.r, None,
+                                    out.k.data_ptr(), out.tstar.data_ptr(), out.resid_mass.data_ptr(),
+                                    out.status.data_ptr(), cache.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        rc |= L.saguaro_cache_lookup(0, cache.data_ptr(), ctypes.cast(fan_c, ctypes.c_void_p), K, B,
+                                     out.k.data_ptr(), out.tstar.data_ptr(), slot.data_ptr(), hit_t.data_ptr(),
+                                     batch.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"library call failed rc={rc}")
+        return out.k.cpu().numpy().copy(), hit_t.cpu().numpy().copy()
+    reports = acceptance_reports(w, run_round, B, K)
+    placement = int(((out.status & capi.ST_PLACEMENT) != 0).sum().item())
     res = {
         "metric": "verified positions/sec and achieved HBM GB/s (% peak), B=16 K=5 V=128256 bf16",
         "value": positions / (ms_step * 1e-3),
@@ -486,12 +579,29 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(step_bytes),
                      "algorithmic_bytes_per_launch": step_bytes, "avg_launch_ms": verify_ms,
-                     "p10_ms": vt[len(vt) // 10], "p90_ms": vt[(len(vt) * 9) // 10]},
+                     "p10_ms": vt[len(vt) // 10], "p90_ms": vt[(len(vt) * 9) // 10],
+                     "read_ceiling": ceiling, "frac_of_read_ceiling": achieved / ceiling["GBps"]},
         "secondary": {"logit_GBps_whole_step": step_bytes / (ms_step * 1e-3) / 1e9,
-                      "committed_tokens_per_s": float(out.k.float().add(1).sum().item()) / (ms_step * 1e-3)},
+                      "committed_tokens_per_s": float(out.k.float().add(1).sum().item()) / (ms_step * 1e-3),
+                      "requests_with_placement_status": placement},
+        "reports": reports,
     }
     if not args.no_cpu_baseline:
+        import oracle
         res["cpu_baseline"] = cpu_baseline(w)
+        one = cpu_baseline(w, seconds_target=5.0, nthreads=1)
+        res["cpu_baseline"]["single_thread"] = {"value": one["value"], "unit": one["unit"], "sample": one["sample"]}
+        # near-tie requests the oracle flags (parity excludes them) on the report rounds' inputs
+        tok_np = tokens.cpu().numpy()
+        wc = w.without_cache_row()
+        nfl, nreq = 0, 0
+        for i in range(20):
+            r = oracle.verify(wc.draft, wc.target, w.dtype, K, w.params(), F=w.F, C=float(np.float32(w.C)),
+                              tokens=tok_np, seed=w.seed, round_=10_000 + i)
+            nfl += int((r.flags != 0).sum())
+            nreq += B
+        res["reports"]["flagged_near_ties"] = {"flagged": nfl, "requests": nreq,
+                                               "sample": "20 of the report rounds, C = 0.3, given tokens"}
     print(json.dumps(res), flush=True)
 
 

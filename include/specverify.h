@@ -311,6 +311,13 @@ int pyramid_verify(const void* draft_logits, int draft_rows, const void* verifie
                    float* out_resid_mass, uint32_t* out_status, float* out_div, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 
+/* spec_read_ceiling - measurement helper, not part of the method: one plain streaming read of
+ * `bytes` bytes of device memory at `data` (16-byte aligned, bytes a multiple of 16), the
+ * bandwidth ceiling a verification call that reads the same number of logit bytes is compared
+ * against.  sink: [1] uint32 device word, written only if the xor of the data equals a fixed
+ * value (never in practice).  Returns SPEC_EINVAL for a null pointer, zero or unaligned sizes. */
+int spec_read_ceiling(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ ST_PLACEMENT = 512
 
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
            "saguaro_cache_lookup", "saguaro_verify_cache", "saguaro_backup_plan", "mirror_signpost_workspace_bytes",
-           "mirror_signposts", "mirror_tree_lookup", "pyramid_verify")
+           "mirror_signposts", "mirror_tree_lookup", "pyramid_verify", "spec_read_ceiling")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -72,6 +72,7 @@ class Lib:
         L.saguaro_verify_cache.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
                                            ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                            _P]
+        L.spec_read_ceiling.argtypes = [_P, ctypes.c_size_t, _P, _P]
         for fn in EXPORTS[1:]:
             getattr(L, fn).restype = _I
 
@@ -411,3 +412,13 @@ def pyramid_verify(draft: Optional[torch.Tensor], verifier: torch.Tensor, K: int
                                     _ptr(workspace), workspace.numel(), _stream(stream))
     _check("pyramid_verify", rc)
     return out, div
+
+
+def spec_read_ceiling(data: torch.Tensor, sink: torch.Tensor, stream: Optional[int] = None) -> None:
+    """One plain streaming read of every byte of `data` (contiguous, 16-byte aligned, a multiple
+    of 16 bytes): the bandwidth ceiling a call reading as many bytes is set against."""
+    _need(data.is_contiguous(), "data must be contiguous")
+    _need(sink.dtype == torch.int32 and sink.numel() >= 1, "sink must hold one int32")
+    nbytes = data.numel() * data.element_size()
+    rc = load().cdll.spec_read_ceiling(_ptr(data), nbytes, _ptr(sink), _stream(stream))
+    _check("spec_read_ceiling", rc)

@@ -47,6 +47,7 @@ struct ResSmem {
     double redd[kWaves];
     int32_t redi[kWaves];
     int last;
+    int misplaced;  // the request's workgroups arrived from more than one XCD
     int fc;
     int fscan[kWaves];
     double ftarget, fbase, fW;
@@ -590,7 +591,7 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
         a.out_k[b] = k;
         a.out_t[b] = best != 0x7FFFFFFF ? best : last;
         if (a.out_W) a.out_W[b] = k == K ? 0.0f : (float)W;
-        if (a.out_status) a.out_status[b] = status;
+        if (a.out_status) a.out_status[b] = status | (sm.misplaced ? kStPlacement : 0u);
     }
 }
 
@@ -602,15 +603,21 @@ __device__ __forceinline__ void fallback_unit(const VerifyArgs& a, int b, int j,
 }
 
 // Request arrival in the XCD's L2; true for the last of `expected` workgroups (which resets
-// the counter for the next call).
+// the counter for the next call).  The 64-bit counter holds the arrivals (bits 0-7) and, in
+// seven bits per XCD from bit 8, the arrivals from each XCD: when the last arriver's own XCD
+// did not see every arrival, the request's workgroups did not share one L2 and sm.misplaced
+// is set (the outputs then carry kStPlacement).
 __device__ __forceinline__ bool arrive_last(const FastArgs& f, ResSmem& sm, int b, int expected) {
     drain_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned* rc = reinterpret_cast<unsigned*>(f.ws + f.L.res_ctr + (size_t)b * 128);
-        const unsigned old = l2_fetch_add(rc, 1u);
-        sm.last = (old + 1 == (unsigned)expected) ? 1 : 0;
-        if (sm.last) *rc = 0u;
+        uint64_t* rc = reinterpret_cast<uint64_t*>(f.ws + f.L.res_ctr + (size_t)b * 128);
+        const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0x7u;  // XCC_ID
+        const uint64_t add = 1ull + (1ull << (8 + 7 * xcc));
+        const uint64_t now = l2_fetch_add64(rc, add) + add;
+        sm.last = ((now & 0xFFull) == (uint64_t)expected) ? 1 : 0;
+        sm.misplaced = ((now >> (8 + 7 * xcc)) & 0x7Full) != (uint64_t)expected ? 1 : 0;
+        if (sm.last) *rc = 0ull;
     }
     __syncthreads();
     return sm.last != 0;
@@ -656,7 +663,7 @@ __device__ __forceinline__ void general_request(const FastArgs& f, ResSmem& sm, 
     a.out_k[b] = k;
     a.out_t[b] = t;
     if (a.out_W) a.out_W[b] = W;
-    if (a.out_status) a.out_status[b] = st | extra;
+    if (a.out_status) a.out_status[b] = st | extra | (sm.misplaced ? kStPlacement : 0u);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_resolve_kernel(FastArgs f) {

@@ -150,3 +150,13 @@ def test_mirror_entry_points_argument_errors():
     assert L.mirror_tree_lookup(fake, fake, 0, 10, 7, fake, fake, fake, fake, fake, None, None) == capi.SPEC_EINVAL
     assert L.mirror_tree_lookup(fake, fake, 4, 0, 7, fake, fake, fake, fake, fake, None, None) == capi.SPEC_EINVAL
     assert L.mirror_tree_lookup(fake, fake, 4, 10, 1025, fake, fake, fake, fake, fake, None, None) == capi.SPEC_EINVAL
+
+
+def test_read_ceiling_argument_errors():
+    L = capi.load().cdll
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.spec_read_ceiling(None, 16, fake, None) == capi.SPEC_EINVAL
+    assert L.spec_read_ceiling(fake, 16, None, None) == capi.SPEC_EINVAL
+    assert L.spec_read_ceiling(fake, 0, fake, None) == capi.SPEC_EINVAL
+    assert L.spec_read_ceiling(fake, 24, fake, None) == capi.SPEC_EINVAL                       # not a multiple of 16
+    assert L.spec_read_ceiling(ctypes.c_void_p((1 << 20) + 8), 32, fake, None) == capi.SPEC_EINVAL  # unaligned

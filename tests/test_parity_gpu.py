@@ -548,3 +548,28 @@ def test_llama_two_hundred_rounds_given_tokens():
         one = _work(w.draft[b:b + 1], w.target[b:b + 1], w.dtype, w.K, w.temperature[b], w.top_k[b], w.top_p[b],
                     seed=w.seed)
         check_verify(one, tokens=tok[b:b + 1], round_=rnd, label=f"llama round {rnd}")
+
+
+def test_placement_status_stays_clear():
+    """The bf16 path's rendezvous assume that every workgroup of a unit (count kernel) and of a
+    request (resolve kernel) runs on one XCD; a unit or request that saw more than one XCD
+    reports SPEC_ST_PLACEMENT.  The bit stays clear at the headline size (fused call, ten
+    rounds) and at the branch-tree size (512 chains, five rounds)."""
+    rng = np.random.default_rng(7)
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
+    prm = capi.params_tensor(w.temperature, w.top_k, w.top_p)
+    tok = dev(rng.integers(0, w.V, size=(w.B, w.K)).astype(np.int32))
+    d, t = dev(w.draft), dev(w.target)
+    for rnd in range(10):
+        out, _, _ = capi.saguaro_verify_cache(d, t, w.K, prm, tok, w.budget, w.a, w.r, F=w.F, C=w.C, seed=w.seed,
+                                              round_=rnd)
+        st = out.status.cpu().numpy().astype(np.uint32)
+        assert ((st & capi.ST_PLACEMENT) == 0).all(), f"placement status in round {rnd}: {st}"
+    tw = synth.tree(n_req=64)
+    tprm = capi.params_tensor(tw.temperature, tw.top_k, tw.top_p)
+    dd, tt, tk = dev(tw.draft), dev(tw.target), dev(tw.tokens.astype(np.int32))
+    for rnd in range(5):
+        out = capi.spec_verify(dd, tt, tw.K, tprm, tk, F=tw.F, C=tw.C, seed=tw.seed, round_=rnd)
+        st = out.status.cpu().numpy().astype(np.uint32)
+        assert ((st & capi.ST_PLACEMENT) == 0).all(), f"placement status in tree round {rnd}"
+    say("[placement] clear: 10 headline rounds, 5 branch-tree rounds")
