@@ -78,6 +78,7 @@ enum { SPEC_FP32 = 0, SPEC_BF16 = 1 };
 #define SPEC_MAX_F 64          /* largest downweighted set */
 #define SPEC_MAX_FANOUT 1024   /* largest cache width for one depth */
 #define SPEC_MAX_KAPPA 16      /* most signposts per request */
+#define SPEC_NOALLOC_SCRATCH_BYTES (32u << 20)  /* static scratch of saguaro_verify_cache_noalloc, per GPU */
 
 /* Per-request processing, applied to the draft AND the target rows of that request ([SpS]
  * section 6: temperature, top-k and nucleus act on both distributions before the correction).
@@ -132,8 +133,10 @@ enum {
 
 /* Bytes of scratch spec_verify needs for B requests of K draft positions over V tokens (pure
  * host function).  The workspace must be zero-filled before its first use; every call that
- * completes leaves its arrival counters at zero again, so it can be reused without clearing.
- * It carries no results between calls.  One workspace serves one call at a time. */
+ * completes leaves its arrival counters at zero again, so it can be reused without clearing
+ * for the same (B, K, V); the counters' places depend on the shape, so a workspace taken over
+ * for another shape is zero-filled again first.  It carries no results between calls.  One
+ * workspace serves one call at a time. */
 size_t spec_workspace_bytes(int B, int K, int V);
 
 /* spec_verify - batched speculative-sampling verification ([SpS] sections 1 and 3; [SSD]
@@ -310,6 +313,22 @@ int pyramid_verify(const void* draft_logits, int draft_rows, const void* verifie
                    uint64_t seed, uint64_t round, uint32_t flags, int32_t* out_k, int32_t* out_tstar,
                    float* out_resid_mass, uint32_t* out_status, float* out_div, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
+
+/* saguaro_verify_cache_noalloc - saguaro_verify_cache for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and outputs without the workspace: a static device array of
+ * SPEC_NOALLOC_SCRATCH_BYTES inside the library takes its place (each GPU the library runs on
+ * holds one until the process ends; the call allocates nothing).  Calls on one GPU share that
+ * scratch: the call clears what must start at zero with a fill kernel on `stream` (so shapes
+ * may change between calls), and calls that overlap on one GPU (e.g. on two streams) race.
+ * Returns SPEC_EWORKSPACE when spec_workspace_bytes(B, K, V) exceeds the scratch (e.g. B = 16,
+ * K = 5, V = 128256 needs 18.5 MiB and fits; B = 32 at that K and V does not), SPEC_EHIP when
+ * the scratch's device address cannot be had, otherwise the codes of saguaro_verify_cache. */
+int saguaro_verify_cache_noalloc(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
+                                 const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,
+                                 uint64_t round, uint32_t flags, int budget, double a, double r,
+                                 int32_t* out_fanout_host, int32_t* out_k, int32_t* out_tstar, float* out_resid_mass,
+                                 uint32_t* out_status, int32_t* out_cache, hipStream_t stream);
 
 /* spec_read_ceiling - measurement helper, not part of the method: one plain streaming read of
  * `bytes` bytes of device memory at `data` (16-byte aligned, bytes a multiple of 16), the

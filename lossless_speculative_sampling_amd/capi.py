@@ -23,6 +23,7 @@ SPEC_UNIFORM_DRAFT = 2
 SPEC_ASSISTED = 4
 SPEC_MAX_F = 64
 SPEC_MAX_KAPPA = 16
+SPEC_NOALLOC_SCRATCH_BYTES = 32 << 20
 ST_EMPTY_RESIDUAL = 8
 ST_OUTSIDE_DRAFT_SUPPORT = 16
 ST_BAD_LOGIT = 32
@@ -33,7 +34,8 @@ ST_PLACEMENT = 512
 
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
            "saguaro_cache_lookup", "saguaro_verify_cache", "saguaro_backup_plan", "mirror_signpost_workspace_bytes",
-           "mirror_signposts", "mirror_tree_lookup", "pyramid_verify", "spec_read_ceiling")
+           "mirror_signposts", "mirror_tree_lookup", "pyramid_verify", "spec_read_ceiling",
+           "saguaro_verify_cache_noalloc")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -73,6 +75,8 @@ class Lib:
                                            ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                            _P]
         L.spec_read_ceiling.argtypes = [_P, ctypes.c_size_t, _P, _P]
+        L.saguaro_verify_cache_noalloc.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
+                                                   ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P]
         for fn in EXPORTS[1:]:
             getattr(L, fn).restype = _I
 
@@ -289,6 +293,27 @@ def saguaro_verify_cache(draft: torch.Tensor, target: torch.Tensor, K: int, para
     _check("saguaro_verify_cache", rc)
     out.tokens = tokens
     return out, cache[:, :budget], list(fan)
+
+
+def saguaro_verify_cache_noalloc(draft: torch.Tensor, target: torch.Tensor, K: int, params: torch.Tensor,
+                                 tokens: torch.Tensor, budget: int, a: float, r: float, out: VerifyOut,
+                                 cache: torch.Tensor, F: int = 0, C: float = 1.0, seed: int = 0, round_: int = 0,
+                                 flags: int = 0, stream=None):
+    """saguaro_verify_cache on the library's static scratch (no workspace); the caller passes the
+    outputs (out, cache [B][>= budget]).  Returns the fan-out list."""
+    code = _verify_inputs(draft, target, K, params, tokens, draft_rows=K + 1)
+    B, Kd, V = draft.shape
+    _verify_out(out, B)
+    _need(cache.dtype == torch.int32 and cache.dim() == 2 and cache.shape[0] == B and cache.shape[1] >= budget,
+          f"cache must be int32 [{B}][>= {budget}]")
+    fan = (ctypes.c_int32 * (K + 1))()
+    rc = load().cdll.saguaro_verify_cache_noalloc(_ptr(draft), _ptr(target), code, B, K, V, _ptr(params), F,
+                                                  ctypes.c_float(C), _ptr(tokens), seed, round_, flags, budget, a, r,
+                                                  ctypes.cast(fan, _P), _ptr(out.k), _ptr(out.tstar),
+                                                  _ptr(out.resid_mass), _ptr(out.status), _ptr(cache),
+                                                  _stream(stream))
+    _check("saguaro_verify_cache_noalloc", rc)
+    return list(fan)
 
 
 def saguaro_cache_lookup(mode: int, cache: torch.Tensor, fanout_or_shape, K: int, B: int, k: torch.Tensor,

@@ -1,7 +1,9 @@
 // The C ABI: argument validation, workspace layout and kernel launches.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
+#include "fast_common.h"
 #include "fastpath.h"
 #include "generic.h"
 #include "mirror.h"
@@ -182,25 +184,42 @@ int saguaro_cache_build(const void* draft_logits, int dtype, int B, int K, int V
     return launch_status();
 }
 
-int saguaro_verify_cache(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
-                         const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed, uint64_t round,
-                         uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host, int32_t* out_k,
-                         int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status, int32_t* out_cache,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// The host-detectable argument errors of saguaro_verify_cache (workspace aside), and the fan-out.
+int verify_cache_args(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
+                      const spec_params* params, int F, float C, const int32_t* draft_tokens, uint32_t flags,
+                      int budget, double a, double r, const int32_t* out_k, const int32_t* out_tstar,
+                      const int32_t* out_cache, CacheArgs* c) {
     if (!draft_logits || !target_logits || !params || !draft_tokens || !out_k || !out_tstar || !out_cache)
         return SPEC_EINVAL;
     if (B < 1 || K < 1 || V < 1) return SPEC_EINVAL;
     if (F < 0 || F > SPEC_MAX_F || !(C >= 0.0f && C <= 1.0f)) return SPEC_EINVAL;
     if ((flags & ~(uint32_t)SPEC_SAMPLE_DRAFT) != 0) return SPEC_EINVAL;
     if (!valid_dtype(dtype)) return SPEC_EDTYPE;
-    CacheArgs c{};
-    const int frc = fanout_host(K, budget, a, r, c.fanout.f);
+    const int frc = fanout_host(K, budget, a, r, c->fanout.f);
     if (frc != SPEC_OK) return frc;
-    c.fanout.off[0] = 0;
+    c->fanout.off[0] = 0;
     for (int k = 0; k <= K; ++k) {
-        if (c.fanout.f[k] > SPEC_MAX_FANOUT) return SPEC_EINVAL;
-        c.fanout.off[k + 1] = c.fanout.off[k] + c.fanout.f[k];
+        if (c->fanout.f[k] > SPEC_MAX_FANOUT) return SPEC_EINVAL;
+        c->fanout.off[k + 1] = c->fanout.off[k] + c->fanout.f[k];
     }
+    return SPEC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int saguaro_verify_cache(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
+                         const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed, uint64_t round,
+                         uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host, int32_t* out_k,
+                         int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status, int32_t* out_cache,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    CacheArgs c{};
+    const int arc = verify_cache_args(draft_logits, target_logits, dtype, B, K, V, params, F, C, draft_tokens, flags,
+                                      budget, a, r, out_k, out_tstar, out_cache, &c);
+    if (arc != SPEC_OK) return arc;
     const size_t need = spec_workspace_bytes(B, K, V);
     if (!workspace || workspace_bytes < need) return SPEC_EWORKSPACE;
     if (out_fanout_host) std::memcpy(out_fanout_host, c.fanout.f, sizeof(int32_t) * (K + 1));
@@ -295,3 +314,82 @@ int mirror_tree_lookup(const int32_t* tree_tokens, const int32_t* tree_parents, 
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------------------------
+// saguaro_verify_cache without a caller workspace, for callers that cannot allocate device
+// memory: the library's own static device scratch stands in for it.  The scratch is one
+// file-scope device array; each GPU that loads the library holds its own copy until the
+// process ends.  On the host the array's name only stands for the symbol: its device address
+// comes from hipGetSymbolAddress, taken once per device with that device current and kept per
+// device, and only that address reaches kernels.  Calls on one GPU share its scratch, which
+// keeps what the last call left there: the arrival counters and request records that must
+// start at zero are cleared at the start of every call by a fill kernel on the call's stream
+// (shapes may change from call to call).  Calls that overlap on one GPU race on the scratch.
+// ------------------------------------------------------------------------------------------
+namespace {
+constexpr size_t kNoallocBytes = (size_t)SPEC_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoallocBytes % 256 == 0, "whole 256-byte blocks");
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoallocBytes];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint4* __restrict__ p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+namespace {
+// The current device's address of the scratch array (nullptr if it cannot be had).
+char* scratch_of_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return static_cast<char*>(g_scratch_ptr[dev]);
+}
+
+// Zeroes [begin, end) of the scratch (begin 16-byte aligned; end rounded up to 16 bytes, within
+// the scratch by the size check).
+void zero_range(char* base, size_t begin, size_t end, hipStream_t stream) {
+    const size_t n16 = (end - begin + 15) / 16;
+    if (n16 == 0) return;
+    const unsigned grid = (unsigned)std::min<size_t>((n16 + 255) / 256, 1024);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<uint4*>(base + begin),
+                       n16);
+}
+}  // namespace
+
+extern "C" int saguaro_verify_cache_noalloc(const void* draft_logits, const void* target_logits, int dtype, int B,
+                                            int K, int V, const spec_params* params, int F, float C,
+                                            int32_t* draft_tokens, uint64_t seed, uint64_t round, uint32_t flags,
+                                            int budget, double a, double r, int32_t* out_fanout_host, int32_t* out_k,
+                                            int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status,
+                                            int32_t* out_cache, hipStream_t stream) {
+    CacheArgs c{};
+    const int arc = verify_cache_args(draft_logits, target_logits, dtype, B, K, V, params, F, C, draft_tokens, flags,
+                                      budget, a, r, out_k, out_tstar, out_cache, &c);
+    if (arc != SPEC_OK) return arc;
+    const size_t need = spec_workspace_bytes(B, K, V);
+    if (need > kNoallocBytes) return SPEC_EWORKSPACE;  // the shape needs more than the static scratch
+    char* ws = scratch_of_current_device();
+    if (!ws) return SPEC_EHIP;
+    // what must start at zero: the bf16 path's arrival counters (the start of its workspace) and
+    // request records; everything else is written before it is read
+    const int units = B * (K + 1);
+    const int nS = (V + fast::kSliceCols - 1) / fast::kSliceCols;
+    const size_t gen = align_up((size_t)units * sizeof(UnitRec), 256);
+    const fast::Layout L = fast::layout(B, units, nS);
+    zero_range(ws, gen + L.unit_ctr, gen + L.parts, stream);
+    zero_range(ws, gen + L.reqs, gen + L.reqs + (size_t)B * sizeof(fast::ReqFast), stream);
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    return saguaro_verify_cache(draft_logits, target_logits, dtype, B, K, V, params, F, C, draft_tokens, seed, round,
+                                flags, budget, a, r, out_fanout_host, out_k, out_tstar, out_resid_mass, out_status,
+                                out_cache, ws, kNoallocBytes, stream);
+}
