@@ -277,7 +277,10 @@ int saguaro_cache_lookup(int mode, const int32_t* cache, const int32_t* fanout_o
     } else {
         return SPEC_EINVAL;
     }
-    hipLaunchKernelGGL(cache_lookup_kernel, dim3(1), dim3(1024), 0, stream, l);
+    // one workgroup, a thread per request up to 1024 (whole waves: a single wave needs no barrier
+    // wait in the batch count)
+    const unsigned threads = (unsigned)std::min(1024, (B + kWave - 1) / kWave * kWave);
+    hipLaunchKernelGGL(cache_lookup_kernel, dim3(1), dim3(threads), 0, stream, l);
     return launch_status();
 }
 

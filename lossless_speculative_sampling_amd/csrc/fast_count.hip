@@ -748,6 +748,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
             sm.neginf[threadIdx.x] = 0;
             sm.grp[threadIdx.x][0] = 0;
             sm.grp[threadIdx.x][1] = 0;
+            sm.cnt_s[threadIdx.x] = 0;
+            sm.th_tau[threadIdx.x] = 0u;
+            sm.th_need[threadIdx.x] = 0;
+            sm.th_ties[threadIdx.x] = 0;
         }
         if (threadIdx.x == 2) sm.xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;  // XCC_ID
         // the rows' values at the draft token (every slice counts the token's key), zero without
@@ -769,14 +773,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
         const bool rare1 = two && (sm.hraw[1][kHistLead - 1] | sm.hraw[1][kHistLead + kBins]) != 0;
         if (rare0) count_rare(sm, 0, c0, a.V, vq);
         if (rare1) count_rare(sm, 1, c0, a.V, vp);
-        if (threadIdx.x < 2) {
-            sm.cnt_s[threadIdx.x] = 0;
-            sm.rare[threadIdx.x] = threadIdx.x == 0 ? rare0 : rare1;
-            sm.th_tau[threadIdx.x] = 0u;
-            sm.th_need[threadIdx.x] = 0;
-            sm.th_ties[threadIdx.x] = 0;
-        }
-        __syncthreads();
+        if (threadIdx.x < 2) sm.rare[threadIdx.x] = threadIdx.x == 0 ? rare0 : rare1;  // (read after later barriers)
+        if (rare0 || rare1) __syncthreads();  // the second pass's counts and specials
         // the summaries; passes over the columns (registers) while they are still live
         const bool holds_s = j < a.K && tok_ok && s_tok >= c0;  // at or after this slice: count its key
         const int want[2] = {list_len(a, prm, false), two ? draft_list_len(f, prm, j) : 0};

@@ -269,13 +269,14 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
         row_slice(tid >> 1, nS, &r, &t);
         hw = ldnt(reinterpret_cast<const u32x4*>(part_c(f, unit, t, r)) + (tid & 1));
     }
+    // (every load is issued, at a clamped index of a valid record, so none waits on a branch;
+    // which of them count is decided where they are used)
     uint32_t ent[kEntIt];
     const bool merge_mine = gi < G && gt != own;
+    const uint32_t* ebase = part_c(f, unit, gt, gr)->ent;  // (gi >= G: the unit's first record, unused)
+    const int x0 = tid & (tpg - 1);
 #pragma unroll
-    for (int it = 0; it < kEntIt; ++it) {
-        const int x = (tid & (tpg - 1)) + it * tpg;
-        ent[it] = (merge_mine && x < kBins) ? ldnt(&part_c(f, unit, gt, gr)->ent[x]) : 0u;
-    }
+    for (int it = 0; it < kEntIt; ++it) ent[it] = ldnt(ebase + min(x0 + it * tpg, kBins - 1));
     // candidates: thread u of row r stages positions u and u + 256 of the row's slice-major list
     const int cr = tid / kRowThreads, cu = tid % kRowThreads;
     const int cwant = cr < rows ? (cr ? want1 : want0) : 0;
@@ -335,11 +336,10 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     //      the candidates' ranks ----
     if (merge_mine) {
         const int n = (int)ss.hdr[gr][gt][1];
+        const int nv = n > x0 ? (n - x0 + tpg - 1) >> lgt : 0;  // this thread's entries below n
 #pragma unroll
-        for (int it = 0; it < kEntIt; ++it) {
-            const int x = (tid & (tpg - 1)) + it * tpg;
-            if (x < n) atomicAdd(&sm.hist(gr)[ent[it] >> 16], ent[it] & 0xFFFFu);
-        }
+        for (int it = 0; it < kEntIt; ++it)
+            if (it < nv) atomicAdd(&sm.hist(gr)[ent[it] >> 16], ent[it] & 0xFFFFu);
     }
     for (int g = 0; more_ent && g < G; ++g) {  // entries past the batch (uniform loop; rare)
         int r, t;
@@ -449,9 +449,14 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     RowView& rv = ss.rv[rr0];
     const int s0 = u * kSlotsPer;
     // (flags read before the scan: single threads update them after it)
-    const bool proc = live_row && !rv.bad && !rv.overflow;  // uniform per row
-    const bool greedy = live_row && rv.greedy;
-    const bool has_k = live_row && rv.has_k, has_p = live_row && rv.has_p, has_sp = live_row && rv.has_special;
+    // (read unconditionally and combined without short-circuits: no branch waits on each read)
+    // (uniform in each wave: kept in scalar registers)
+    const int f_bad = __builtin_amdgcn_readfirstlane(rv.bad), f_ovf = __builtin_amdgcn_readfirstlane(rv.overflow),
+              f_gr = __builtin_amdgcn_readfirstlane(rv.greedy), f_hk = __builtin_amdgcn_readfirstlane(rv.has_k),
+              f_hp = __builtin_amdgcn_readfirstlane(rv.has_p), f_hs = __builtin_amdgcn_readfirstlane(rv.has_special);
+    const bool proc = live_row & (f_bad == 0) & (f_ovf == 0);  // uniform per row
+    const bool greedy = live_row & (f_gr != 0);
+    const bool has_k = live_row & (f_hk != 0), has_p = live_row & (f_hp != 0), has_sp = live_row & (f_hs != 0);
     uint32_t c[kSlotsPer];
     uint32_t nloc = 0, nz = 0;
     int first = -1;
@@ -543,10 +548,7 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     //      while the masses are summed ----
     uint32_t e2[kEntIt];
 #pragma unroll
-    for (int it = 0; it < kEntIt; ++it) {
-        const int x = (tid & (tpg - 1)) + it * tpg;
-        e2[it] = (gi < G && x < kBins) ? ldnt(&part_c(f, unit, gt, gr)->ent[x]) : 0u;
-    }
+    for (int it = 0; it < kEntIt; ++it) e2[it] = ldnt(ebase + min(x0 + it * tpg, kBins - 1));
 
     // ---- pass B (masses): the compact list spread evenly over the row's threads ----
     const bool cuts2 = cuts && !rv.overflow;
@@ -652,11 +654,11 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     const bool any_cut = cb00 >= 0 || cb01 >= 0 || cb10 >= 0 || cb11 >= 0;
     if (any_cut && gi < G) {
         const int n = (int)ss.hdr[gr][gt][1];
+        const int nv = n > x0 ? (n - x0 + tpg - 1) >> lgt : 0;
         const int c0b = CBIN(gr, 0), c1b = CBIN(gr, 1);
 #pragma unroll
         for (int it = 0; it < kEntIt; ++it) {
-            const int x = (tid & (tpg - 1)) + it * tpg;
-            if (x < n) {
+            if (it < nv) {
                 const int b = (int)(e2[it] >> 16);
                 if (b == c0b) ss.pc[gr][0][gt] = e2[it] & 0xFFFFu;
                 if (b == c1b) ss.pc[gr][1][gt] = e2[it] & 0xFFFFu;

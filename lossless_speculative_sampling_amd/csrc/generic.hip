@@ -107,12 +107,18 @@ __global__ __launch_bounds__(1024) void cache_lookup_kernel(LookupArgs a) {
         if (a.mode == 0) {
             const int k = a.k[b], t = a.tstar[b];
             if (k >= 0 && k <= a.K && t >= 0) {
+                // the depth-k list in batches of eight independent loads (no load waits for the
+                // comparison of the one before); the first match is the slot
                 const int32_t* c = a.cache + (size_t)b * a.budget + a.fanout.off[k];
-                for (int f = 0; f < a.fanout.f[k]; ++f)
-                    if (c[f] == t) {
-                        res = a.fanout.off[k] + f;
-                        break;
-                    }
+                const int n = a.fanout.f[k];
+                for (int f0 = 0; f0 < n && res < 0; f0 += 8) {
+                    int32_t v[8];
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) v[d] = f0 + d < n ? c[f0 + d] : -1;
+#pragma unroll
+                    for (int d = 7; d >= 0; --d)
+                        if (v[d] == t) res = a.fanout.off[k] + f0 + d;
+                }
             }
         } else {
             const int kappa = a.kappa, gamma = a.gamma;
