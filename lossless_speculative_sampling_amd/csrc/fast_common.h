@@ -267,7 +267,10 @@ __device__ __forceinline__ bool params_ok(const spec_params& prm) {
     return prm.temperature >= 0.0f && !isinf(prm.temperature) && prm.top_p > 0.0f;
 }
 
-// Columns [c0, c0 + kSliceCols) of a row, 16 bytes per load.
+// Columns [c0, c0 + kSliceCols) of a row, 16 bytes per load.  STREAM: non-temporal loads (the
+// count kernel's single pass, which should not push the slices' freshly written summaries out
+// of L2).
+template <bool STREAM = false>
 __device__ __forceinline__ void load_slice(const uint16_t* row, int c0, int V, u32x4 (&v)[kLoads]) {
     // every load is issued, so the loads stay straight-line code and a wait for an earlier load
     // need not wait for these; a vector past the row re-reads the row's first one, and every
@@ -275,7 +278,8 @@ __device__ __forceinline__ void load_slice(const uint16_t* row, int c0, int V, u
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
         const int col = col_of(c0, q, 0);
-        v[q] = *reinterpret_cast<const u32x4*>(row + (col < V ? col : 0));
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + (col < V ? col : 0));
+        v[q] = STREAM ? __builtin_nontemporal_load(p) : *p;
     }
 }
 

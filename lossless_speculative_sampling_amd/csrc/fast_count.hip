@@ -731,8 +731,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
         // (without a draft row the second set re-reads the target and goes unused: unconditional
         // loads keep the compiler's waits exact)
         u32x4 vq[kLoads], vp[kLoads];
-        load_slice(trow, c0, a.V, vq);
-        load_slice(two ? drow : trow, c0, a.V, vp);
+        load_slice<true>(trow, c0, a.V, vq);
+        load_slice<true>(two ? drow : trow, c0, a.V, vp);
         if (threadIdx.x / kWave == 1) {
             const Block4 x = philox4x64_10(a.round, (uint64_t)P.b, (uint64_t)j, 0, a.seed, 0);
             if (threadIdx.x == kWave) {
