@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Throughput of the verification + Saguaro outcome-cache hot path on one MI355X.
 
-One step = the whole path over one batch: saguaro_verify_cache (temperature / nucleus processing
-of 16 requests x (6 draft + 6 target) rows of V = 128256 bf16 logits, sigma_{4, 0.3} downweight,
-acceptance scan, residual / bonus sampling, and the outcome cache with fan-out 32 over the 6
-draft rows, in one pass over the logits) and saguaro_cache_lookup.  Inputs are synthetic (Zipf-shaped rows, see
+One step = the whole path over one batch in one call, saguaro_verify_cache_lookup: temperature /
+nucleus processing of 16 requests x (6 draft + 6 target) rows of V = 128256 bf16 logits,
+sigma_{4, 0.3} downweight, acceptance scan, residual / bonus sampling, the outcome cache with
+fan-out 32 over the 6 draft rows (one pass over the logits), and the lookup of the verified
+outcomes in that cache.  Inputs are synthetic (Zipf-shaped rows, see
 lossless_speculative_sampling_amd/synth.py) and already resident in HBM; R copies of the batch
 totalling more than twice the 256 MB Infinity Cache are rotated so reads come from HBM.
 
@@ -493,27 +494,24 @@ def main():
     cache = torch.empty((B, w.budget), dtype=torch.int32, device=dev)
     import ctypes
     L = capi.load().cdll
-    fan_c = (ctypes.c_int32 * (K + 1))(*fan)
     slot = torch.empty(B, dtype=torch.int32, device=dev)
     hit = torch.empty(B, dtype=torch.uint8, device=dev)
     batch = torch.empty(2, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
 
     def step(i, ev=None):
-        """One pass of the hot path: verification and the outcome cache in one call over the
-        logits, then the cache lookup of the verified outcomes."""
+        """One pass of the hot path in one call over the logits: verification, the outcome cache
+        and the cache lookup of the verified outcomes (saguaro_verify_cache_lookup)."""
         d, t = drafts[i % copies], targets[i % copies]
         if ev is not None:
             ev[0].record()
-        rc = L.saguaro_verify_cache(d.data_ptr(), t.data_ptr(), capi.SPEC_BF16, B, K, V, prm.data_ptr(), w.F,
-                                    ctypes.c_float(w.C), tokens.data_ptr(), w.seed, i, 0, w.budget, w.a, w.r, None,
-                                    out.k.data_ptr(), out.tstar.data_ptr(), out.resid_mass.data_ptr(),
-                                    out.status.data_ptr(), cache.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        rc = L.saguaro_verify_cache_lookup(d.data_ptr(), t.data_ptr(), capi.SPEC_BF16, B, K, V, prm.data_ptr(), w.F,
+                                           ctypes.c_float(w.C), tokens.data_ptr(), w.seed, i, 0, w.budget, w.a, w.r,
+                                           None, out.k.data_ptr(), out.tstar.data_ptr(), out.resid_mass.data_ptr(),
+                                           out.status.data_ptr(), cache.data_ptr(), slot.data_ptr(), hit.data_ptr(),
+                                           batch.data_ptr(), ws.data_ptr(), ws.numel(), stream)
         if ev is not None:
             ev[1].record()
-        rc |= L.saguaro_cache_lookup(0, cache.data_ptr(), ctypes.cast(fan_c, ctypes.c_void_p), K, B,
-                                     out.k.data_ptr(), out.tstar.data_ptr(), slot.data_ptr(), hit.data_ptr(),
-                                     batch.data_ptr(), stream)
         if rc != 0:
             raise RuntimeError(f"library call failed rc={rc}")
 
@@ -547,13 +545,11 @@ def main():
 
     def run_round(rnd, C):
         d, t = drafts[0], targets[0]
-        rc = L.saguaro_verify_cache(d.data_ptr(), t.data_ptr(), capi.SPEC_BF16, B, K, V, prm.data_ptr(), w.F,
-                                    ctypes.c_float(C), tokens.data_ptr(), w.seed, rnd, 0, w.budget, w.a, w.r, None,
-                                    out.k.data_ptr(), out.tstar.data_ptr(), out.resid_mass.data_ptr(),
-                                    out.status.data_ptr(), cache.data_ptr(), ws.data_ptr(), ws.numel(), stream)
-        rc |= L.saguaro_cache_lookup(0, cache.data_ptr(), ctypes.cast(fan_c, ctypes.c_void_p), K, B,
-                                     out.k.data_ptr(), out.tstar.data_ptr(), slot.data_ptr(), hit_t.data_ptr(),
-                                     batch.data_ptr(), stream)
+        rc = L.saguaro_verify_cache_lookup(d.data_ptr(), t.data_ptr(), capi.SPEC_BF16, B, K, V, prm.data_ptr(), w.F,
+                                           ctypes.c_float(C), tokens.data_ptr(), w.seed, rnd, 0, w.budget, w.a, w.r,
+                                           None, out.k.data_ptr(), out.tstar.data_ptr(), out.resid_mass.data_ptr(),
+                                           out.status.data_ptr(), cache.data_ptr(), slot.data_ptr(), hit_t.data_ptr(),
+                                           batch.data_ptr(), ws.data_ptr(), ws.numel(), stream)
         if rc != 0:
             raise RuntimeError(f"library call failed rc={rc}")
         return out.k.cpu().numpy().copy(), hit_t.cpu().numpy().copy()
@@ -575,7 +571,7 @@ def main():
         "config": {"workload": "saguaro verify + outcome cache: B=16 requests, K=5, V=128256 bf16 Zipf logits, "
                                "top-p 0.95, T~U[0.6,1], sigma F=4 C=0.3, fan-out budget 32 (a=0.7, r=1)",
                    "B": B, "K": K, "V": V, "logit_bytes_per_step": step_bytes, "input_copies_rotated": copies},
-        "roofline": {"bound": "hbm", "kernel": "saguaro_verify_cache (fast_count_kernel + fast_resolve_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "saguaro_verify_cache_lookup (fast_count_kernel + fast_resolve_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(step_bytes),
                      "algorithmic_bytes_per_launch": step_bytes, "avg_launch_ms": verify_ms,

@@ -314,6 +314,24 @@ int pyramid_verify(const void* draft_logits, int draft_rows, const void* verifie
                    float* out_resid_mass, uint32_t* out_status, float* out_div, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 
+/* saguaro_verify_cache_lookup - one round of Saguaro's verification and outcome cache in one
+ * call: saguaro_verify_cache followed by the lookup of the verified outcomes in the cache just
+ * built ([SSD] sections 5.1 and 7.1).  Outputs are exactly those of
+ *   saguaro_verify_cache(..., out_cache, workspace, workspace_bytes, stream)
+ *   saguaro_cache_lookup(0, out_cache, fanout, K, B, out_k, out_tstar, out_slot, out_hit, out_batch, stream)
+ * where fanout is the call's fan-out (returned in out_fanout_host).  On the bf16 path the lookup
+ * runs inside the verification's last kernel, as each request's outcome is settled (one kernel
+ * launch fewer); elsewhere the two calls run one after the other.
+ *   out_slot [B] int32, out_hit [B] uint8, out_batch [2] int32 (nullable): as saguaro_cache_lookup
+ *   workspace  spec_workspace_bytes(B, K, V) bytes, same contract as spec_verify
+ * Return codes: as saguaro_verify_cache (SPEC_EINVAL also for a null out_slot or out_hit). */
+int saguaro_verify_cache_lookup(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
+                                const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,
+                                uint64_t round, uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host,
+                                int32_t* out_k, int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status,
+                                int32_t* out_cache, int32_t* out_slot, uint8_t* out_hit, int32_t* out_batch,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* saguaro_verify_cache_noalloc - saguaro_verify_cache for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments and outputs without the workspace: a static device array of

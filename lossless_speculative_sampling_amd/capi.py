@@ -35,7 +35,7 @@ ST_PLACEMENT = 512
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
            "saguaro_cache_lookup", "saguaro_verify_cache", "saguaro_backup_plan", "mirror_signpost_workspace_bytes",
            "mirror_signposts", "mirror_tree_lookup", "pyramid_verify", "spec_read_ceiling",
-           "saguaro_verify_cache_noalloc")
+           "saguaro_verify_cache_noalloc", "saguaro_verify_cache_lookup")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -75,6 +75,9 @@ class Lib:
                                            ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                            _P]
         L.spec_read_ceiling.argtypes = [_P, ctypes.c_size_t, _P, _P]
+        L.saguaro_verify_cache_lookup.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
+                                                  ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                  ctypes.c_size_t, _P]
         L.saguaro_verify_cache_noalloc.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
                                                    ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P]
         for fn in EXPORTS[1:]:
@@ -293,6 +296,42 @@ def saguaro_verify_cache(draft: torch.Tensor, target: torch.Tensor, K: int, para
     _check("saguaro_verify_cache", rc)
     out.tokens = tokens
     return out, cache[:, :budget], list(fan)
+
+
+def saguaro_verify_cache_lookup(draft: torch.Tensor, target: torch.Tensor, K: int, params: torch.Tensor,
+                                tokens: torch.Tensor, budget: int, a: float, r: float, F: int = 0, C: float = 1.0,
+                                seed: int = 0, round_: int = 0, flags: int = 0, workspace: Optional[torch.Tensor] = None,
+                                out: Optional[VerifyOut] = None, cache: Optional[torch.Tensor] = None, stream=None):
+    """saguaro_verify_cache and the mode-0 lookup of its outcomes in one call.  Returns (VerifyOut,
+    cache [B][budget], fan-out list, slot [B] int32, hit [B] uint8, batch [2] int32)."""
+    code = _verify_inputs(draft, target, K, params, tokens, draft_rows=K + 1)
+    B, Kd, V = draft.shape
+    dev = draft.device
+    if out is None:
+        out = VerifyOut(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                        torch.empty(B, dtype=torch.float32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                        tokens)
+    _verify_out(out, B)
+    if workspace is None:
+        workspace = new_workspace(B, K, V, dev)
+    _workspace(workspace)
+    if cache is None:
+        cache = torch.empty((B, max(budget, 1)), dtype=torch.int32, device=dev)
+    _need(cache.dtype == torch.int32 and cache.dim() == 2 and cache.shape[0] == B and cache.shape[1] >= budget,
+          f"cache must be int32 [{B}][>= {budget}]")
+    slot = torch.empty(B, dtype=torch.int32, device=dev)
+    hit = torch.empty(B, dtype=torch.uint8, device=dev)
+    batch = torch.empty(2, dtype=torch.int32, device=dev)
+    fan = (ctypes.c_int32 * (K + 1))()
+    rc = load().cdll.saguaro_verify_cache_lookup(_ptr(draft), _ptr(target), code, B, K, V, _ptr(params), F,
+                                                 ctypes.c_float(C), _ptr(tokens), seed, round_, flags, budget, a, r,
+                                                 ctypes.cast(fan, _P), _ptr(out.k), _ptr(out.tstar),
+                                                 _ptr(out.resid_mass), _ptr(out.status), _ptr(cache), _ptr(slot),
+                                                 _ptr(hit), _ptr(batch), _ptr(workspace), workspace.numel(),
+                                                 _stream(stream))
+    _check("saguaro_verify_cache_lookup", rc)
+    out.tokens = tokens
+    return out, cache[:, :budget], list(fan), slot, hit, batch
 
 
 def saguaro_verify_cache_noalloc(draft: torch.Tensor, target: torch.Tensor, K: int, params: torch.Tensor,

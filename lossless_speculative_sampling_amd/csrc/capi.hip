@@ -247,6 +247,44 @@ int saguaro_verify_cache(const void* draft_logits, const void* target_logits, in
     return launch_status();
 }
 
+int saguaro_verify_cache_lookup(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
+                                const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,
+                                uint64_t round, uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host,
+                                int32_t* out_k, int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status,
+                                int32_t* out_cache, int32_t* out_slot, uint8_t* out_hit, int32_t* out_batch,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    CacheArgs c{};
+    const int arc = verify_cache_args(draft_logits, target_logits, dtype, B, K, V, params, F, C, draft_tokens, flags,
+                                      budget, a, r, out_k, out_tstar, out_cache, &c);
+    if (arc != SPEC_OK) return arc;
+    if (!out_slot || !out_hit) return SPEC_EINVAL;
+    const size_t need = spec_workspace_bytes(B, K, V);
+    if (!workspace || workspace_bytes < need) return SPEC_EWORKSPACE;
+    c.draft = draft_logits;
+    c.dtype = dtype;
+    c.B = B;
+    c.K = K;
+    c.V = V;
+    c.tokens = draft_tokens;
+    c.budget = budget;
+    c.out_cache = out_cache;
+    VerifyArgs v{draft_logits, target_logits, K + 1, dtype, B, K, V, params, F, C, draft_tokens, seed,
+                 round, flags, out_k, out_tstar, out_resid_mass, out_status, static_cast<UnitRec*>(workspace)};
+    if (budget > 0 && fast::fast_cache_applies(v, c) && fast::fast_lookup_fuses(v)) {
+        if (out_fanout_host) std::memcpy(out_fanout_host, c.fanout.f, sizeof(int32_t) * (K + 1));
+        const size_t gen = align_up((size_t)B * (K + 1) * sizeof(UnitRec), 256);
+        const fast::LookupOut lk{out_slot, out_hit, out_batch};
+        return fast::fast_verify_cache_lookup(v, c, lk, static_cast<char*>(workspace) + gen, workspace_bytes - gen,
+                                              stream);
+    }
+    // otherwise the two calls one after the other
+    const int vrc = saguaro_verify_cache(draft_logits, target_logits, dtype, B, K, V, params, F, C, draft_tokens, seed,
+                                         round, flags, budget, a, r, out_fanout_host, out_k, out_tstar, out_resid_mass,
+                                         out_status, out_cache, workspace, workspace_bytes, stream);
+    if (vrc != SPEC_OK) return vrc;
+    return saguaro_cache_lookup(0, out_cache, c.fanout.f, K, B, out_k, out_tstar, out_slot, out_hit, out_batch, stream);
+}
+
 int saguaro_cache_lookup(int mode, const int32_t* cache, const int32_t* fanout_or_shape, int K, int B,
                          const int32_t* k, const int32_t* tstar, int32_t* out_slot, uint8_t* out_hit,
                          int32_t* out_batch, hipStream_t stream) {

@@ -150,7 +150,7 @@ struct ReqFast {        // written by the last unit of the request in the count 
 };
 
 struct Layout {
-    size_t unit_ctr, req_ctr, res_ctr, parts, units, reqs, idcut, chunks, gen, cache_gen, div, total;
+    size_t unit_ctr, req_ctr, res_ctr, batch_ctr, parts, units, reqs, idcut, chunks, gen, cache_gen, div, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -161,6 +161,7 @@ __host__ __device__ inline Layout layout(int B, int units, int nS) {
     L.unit_ctr = o; o += align256((size_t)units * 128);   // unit arrival counters (count kernel)
     L.req_ctr = o;  o += align256((size_t)B * 128);       // request arrival counters (count kernel)
     L.res_ctr = o;  o += align256((size_t)B * 128);       // request arrival counters (resolve kernel)
+    L.batch_ctr = o; o += 256;                             // requests looked up / hits (fused lookup)
     L.parts = o;    o += align256((size_t)units * nS * 2 * sizeof(RowPart));
     L.units = o;    o += align256((size_t)units * sizeof(UnitFast));
     L.reqs = o;     o += align256((size_t)B * sizeof(ReqFast));
@@ -186,6 +187,11 @@ struct FastArgs {
     int budget;
     int32_t* out_cache;
     Fanout fan;
+    // the cache lookup of the verified outcomes, fused (lookup != 0): as saguaro_cache_lookup mode 0
+    int lookup;
+    int32_t* out_slot;
+    uint8_t* out_hit;
+    int32_t* out_batch;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -486,11 +486,67 @@ __device__ __forceinline__ void scan_block(ResSmem& sm, double w, int col, doubl
     __syncthreads();  // sm.redd / sm.scan / sm.fscan are reused by the next block
 }
 
+// The outcome-cache lookup of request b's verified outcome (k, t*), fused into this kernel
+// (saguaro_cache_lookup mode 0; SSD reading notes, section 7.1): the slot of t* in the cache's
+// depth-k list, or a miss.  The batch's hit count and all-hit flag come from one counter of
+// every request's (hit, arrival), added at system scope because the requests' workgroups run
+// on every XCD; the last request writes them and clears the counter.  One thread.
+// The first eight entries of request b's depth-k cache list (-1 past the list), loaded ahead.
+struct LookupHead {
+    int32_t v[8];
+};
+__device__ __forceinline__ LookupHead lookup_head(const FastArgs& f, int b, int k) {
+    LookupHead h;
+    const bool ok = k >= 0 && k <= f.a.K;
+    const int32_t* c = f.out_cache + (size_t)b * f.budget + (ok ? f.fan.off[k] : 0);
+    const int n = ok ? f.fan.f[k] : 0;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) h.v[d] = d < n ? ldnt(c + d) : -1;
+    return h;
+}
+__device__ __forceinline__ void lookup_request(const FastArgs& f, int b, int k, int t, const LookupHead& head) {
+    const VerifyArgs& a = f.a;
+    int res = -1;
+    if (k >= 0 && k <= a.K && t >= 0) {
+        // the depth-k list in batches of eight independent loads, the first batch loaded ahead
+        // (rows written by this kernel's workgroups of the request reach L2 before their arrival)
+        const int32_t* c = f.out_cache + (size_t)b * f.budget + f.fan.off[k];
+        const int n = f.fan.f[k];
+#pragma unroll
+        for (int d = 7; d >= 0; --d)
+            if (head.v[d] == t) res = f.fan.off[k] + d;
+        for (int f0 = 8; f0 < n && res < 0; f0 += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) v[d] = f0 + d < n ? ldnt(c + f0 + d) : -1;
+#pragma unroll
+            for (int d = 7; d >= 0; --d)
+                if (v[d] == t) res = f.fan.off[k] + f0 + d;
+        }
+    }
+    f.out_slot[b] = res;
+    f.out_hit[b] = res >= 0 ? 1 : 0;
+    uint64_t* bc = reinterpret_cast<uint64_t*>(f.ws + f.L.batch_ctr);
+    const uint64_t add = 1ull | ((uint64_t)(res >= 0 ? 1 : 0) << 32);
+    const uint64_t now = __hip_atomic_fetch_add(bc, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) + add;
+    if ((uint32_t)now == (uint32_t)a.B) {
+        const int hits = (int)(now >> 32);
+        if (f.out_batch) {
+            f.out_batch[0] = hits;
+            f.out_batch[1] = hits == a.B ? 1 : 0;
+        }
+        __hip_atomic_store(bc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);  // ready for the next call
+    }
+}
+
 // The last workgroup of the request draws t* by inverse CDF over the residual (or q_K), in
 // token order: one wave picks the 512-column chunk from the chunk sums (each lane sums up to 8
 // consecutive chunks), then the workgroup scans that chunk's exact values.  u is the draw.
 __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm, int b, int k, uint32_t status, double v) {
     const VerifyArgs& a = f.a;
+    // the fused lookup's first cache entries, loaded while t* is drawn
+    LookupHead head{};
+    if (f.lookup && threadIdx.x == 0) head = lookup_head(f, b, k);
     const int K = a.K;
     const int n = f.nS * kChunks;
     const double* ch = reinterpret_cast<const double*>(f.ws + f.L.chunks) + (size_t)b * f.nS * kChunks;
@@ -588,10 +644,12 @@ __device__ __forceinline__ void finalize_residual(const FastArgs& f, ResSmem& sm
         }
     }
     if (threadIdx.x == 0) {
+        const int t = best != 0x7FFFFFFF ? best : last;
         a.out_k[b] = k;
-        a.out_t[b] = best != 0x7FFFFFFF ? best : last;
+        a.out_t[b] = t;
         if (a.out_W) a.out_W[b] = k == K ? 0.0f : (float)W;
         if (a.out_status) a.out_status[b] = status | (sm.misplaced ? kStPlacement : 0u);
+        if (f.lookup) lookup_request(f, b, k, t, head);
     }
 }
 
@@ -664,6 +722,7 @@ __device__ __forceinline__ void general_request(const FastArgs& f, ResSmem& sm, 
     a.out_t[b] = t;
     if (a.out_W) a.out_W[b] = W;
     if (a.out_status) a.out_status[b] = st | extra | (sm.misplaced ? kStPlacement : 0u);
+    if (f.lookup) lookup_request(f, b, k, t, lookup_head(f, b, k));
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_resolve_kernel(FastArgs f) {
@@ -707,7 +766,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         __syncthreads();
     }
     const int mode = (int)req[0];
-    if (mode == 0) return;  // decided by the count kernel
+    if (mode == 0) {  // decided by the count kernel
+        // the fused lookup once every cache row of the request is written (units w <= K)
+        if (f.lookup && w <= a.K && arrive_last(f, sm, b, a.K + 1) && threadIdx.x == 0)
+        {
+            const int k = ldnt(&a.out_k[b]);
+            lookup_request(f, b, k, ldnt(&a.out_t[b]), lookup_head(f, b, k));
+        }
+        return;
+    }
     if (mode == 2) {
         if (w <= a.K) general_request(f, sm, b, w, req[2]);
         return;

@@ -67,6 +67,17 @@ int fast_verify(const VerifyArgs& a, void* ws, size_t ws_bytes, hipStream_t stre
 // says whether every depth's list fits the per-slice candidate lists.
 bool fast_cache_applies(const VerifyArgs& a, const CacheArgs& c);
 int fast_verify_cache(const VerifyArgs& a, const CacheArgs& c, void* ws, size_t ws_bytes, hipStream_t stream);
+// The same with the cache lookup of the outcomes (saguaro_cache_lookup mode 0) fused into the
+// resolve kernel; fast_lookup_fuses says whether it applies (otherwise the caller launches the
+// lookup after the call).
+struct LookupOut {
+    int32_t* slot;
+    uint8_t* hit;
+    int32_t* batch;
+};
+bool fast_lookup_fuses(const VerifyArgs& a);
+int fast_verify_cache_lookup(const VerifyArgs& a, const CacheArgs& c, const LookupOut& l, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 }  // namespace fast
 }  // namespace sv

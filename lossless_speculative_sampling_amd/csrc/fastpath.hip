@@ -44,7 +44,8 @@ bool fast_fuzzy_applies(const VerifyArgs& a) {
     return fast_path_applies(a) && !(a.flags & SPEC_ASSISTED) && a.K < kWave;
 }
 
-static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t ws_bytes, hipStream_t stream,
+                       const LookupOut* lk = nullptr) {
     const FastPlan p = fast_plan(a.B, a.K, a.V);
     if (ws_bytes < p.ws_bytes) return SPEC_EWORKSPACE;
     FastArgs f;
@@ -59,6 +60,10 @@ static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t
     f.out_cache = c ? c->out_cache : nullptr;
     if (c) f.fan = c->fanout;
     else f.fan = Fanout{};
+    f.lookup = lk ? 1 : 0;
+    f.out_slot = lk ? lk->slot : nullptr;
+    f.out_hit = lk ? lk->hit : nullptr;
+    f.out_batch = lk ? lk->batch : nullptr;
     launch_count(f, p.grid, stream);
     if (a.tau) launch_diverge(f, p.grid_diverge, stream);
     launch_resolve(f, p.grid_resolve, stream);
@@ -78,6 +83,18 @@ bool fast_cache_applies(const VerifyArgs& a, const CacheArgs& c) {
 
 int fast_verify_cache(const VerifyArgs& a, const CacheArgs& c, void* ws, size_t ws_bytes, hipStream_t stream) {
     return launch_fast(a, &c, ws, ws_bytes, stream);
+}
+
+// Every workgroup that writes a request's cache rows in the resolve kernel (unit w <= K) meets
+// the request's others at its arrival counter: needs K + 1 <= 2 nS (the residual's workgroups).
+bool fast_lookup_fuses(const VerifyArgs& a) {
+    const int nS = (a.V + kSliceCols - 1) / kSliceCols;
+    return a.K + 1 <= 2 * nS && !a.tau;
+}
+
+int fast_verify_cache_lookup(const VerifyArgs& a, const CacheArgs& c, const LookupOut& l, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    return launch_fast(a, &c, ws, ws_bytes, stream, &l);
 }
 
 }  // namespace fast

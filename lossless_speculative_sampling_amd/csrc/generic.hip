@@ -99,12 +99,27 @@ __global__ __launch_bounds__(kRowThreads) void cache_build_kernel(CacheArgs a) {
 }
 
 // saguaro_cache_lookup: a single workgroup loops over the requests and reduces the batch stats.
+constexpr int kLookupRow = 32;  // cache rows up to this width are loaded whole
+
 __global__ __launch_bounds__(1024) void cache_lookup_kernel(LookupArgs a) {
     __shared__ int red[32];
     int hits = 0;
     for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
         int res = -1;
-        if (a.mode == 0) {
+        if (a.mode == 0 && a.budget <= kLookupRow) {
+            // a short cache row is loaded whole, alongside (k, t*): one round trip to memory
+            int32_t v[kLookupRow];
+            const int32_t* c = a.cache + (size_t)b * a.budget;
+#pragma unroll
+            for (int f = 0; f < kLookupRow; ++f) v[f] = f < a.budget ? c[f] : -1;
+            const int k = a.k[b], t = a.tstar[b];
+            if (k >= 0 && k <= a.K && t >= 0) {
+                const int lo = a.fanout.off[k], hi = lo + a.fanout.f[k];
+#pragma unroll
+                for (int f = kLookupRow - 1; f >= 0; --f)
+                    if (f >= lo && f < hi && v[f] == t) res = f;
+            }
+        } else if (a.mode == 0) {
             const int k = a.k[b], t = a.tstar[b];
             if (k >= 0 && k <= a.K && t >= 0) {
                 // the depth-k list in batches of eight independent loads (no load waits for the

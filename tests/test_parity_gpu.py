@@ -573,3 +573,45 @@ def test_placement_status_stays_clear():
         st = out.status.cpu().numpy().astype(np.uint32)
         assert ((st & capi.ST_PLACEMENT) == 0).all(), f"placement status in tree round {rnd}"
     say("[placement] clear: 10 headline rounds, 5 branch-tree rounds")
+
+
+def _fused_lookup_case(w, tok, rnd, C=None):
+    """saguaro_verify_cache_lookup against saguaro_verify_cache + saguaro_cache_lookup (mode 0)."""
+    C = w.C if C is None else C
+    d, t = dev(w.draft), dev(w.target)
+    prm = capi.params_tensor(w.temperature, w.top_k, w.top_p)
+    ref, ref_cache, fan = capi.saguaro_verify_cache(d, t, w.K, prm, tok, w.budget, w.a, w.r, F=w.F, C=C, seed=w.seed,
+                                                    round_=rnd)
+    rslot, rhit, rbatch = capi.saguaro_cache_lookup(0, ref_cache.contiguous(), fan, w.K, w.B, ref.k, ref.tstar)
+    out, cache, fan2, slot, hit, batch = capi.saguaro_verify_cache_lookup(d, t, w.K, prm, tok, w.budget, w.a, w.r,
+                                                                          F=w.F, C=C, seed=w.seed, round_=rnd)
+    torch.cuda.synchronize()
+    assert fan2 == fan
+    for name in ("k", "tstar", "status"):
+        assert torch.equal(getattr(out, name), getattr(ref, name)), name
+    assert torch.equal(out.resid_mass, ref.resid_mass)
+    assert torch.equal(cache, ref_cache)
+    assert torch.equal(slot, rslot) and torch.equal(hit, rhit) and torch.equal(batch, rbatch), \
+        f"lookup differs: {slot.cpu().numpy()} vs {rslot.cpu().numpy()}, batch {batch.cpu().numpy()} {rbatch.cpu().numpy()}"
+    return out, cache, fan, slot, hit, batch
+
+
+def test_fused_lookup_matches_the_two_calls():
+    """The lookup fused into the verification call equals the separate lookup: the headline shape over
+    six rounds at C = 0.3 and C = 1, a small bf16 shape, a shape whose drafts outnumber the residual's
+    workgroups (two-call path inside) and the general path; one round also against the oracle."""
+    rng = np.random.default_rng(11)
+    w = synth.saguaro(B=16, K=5, V=128256, cache_row=True)
+    tok = dev(rng.integers(0, w.V, size=(w.B, w.K)).astype(np.int32))
+    tok[:, 0] = dev(synth.bf16_bits_to_f32(w.draft[:, 0]).argmax(axis=1).astype(np.int32))  # often accepted
+    for rnd in range(6):
+        out, cache, fan, slot, hit, batch = _fused_lookup_case(w, tok, rnd, C=(w.C if rnd % 2 == 0 else 1.0))
+    oslot, ohit, obatch = oracle.cache_lookup(0, cache.cpu().numpy(), np.array(fan, np.int32), w.K, w.B,
+                                              out.k.cpu().numpy(), out.tstar.cpu().numpy())
+    assert (slot.cpu().numpy() == oslot).all() and (batch.cpu().numpy() == obatch).all()
+    for shape in ((4, 3, 16392), (3, 7, 16392), (3, 2, 4099)):
+        B, K, V = shape
+        w2 = synth.saguaro(B=B, K=K, V=V, cache_row=True)
+        tok2 = dev(rng.integers(0, V, size=(B, K)).astype(np.int32))
+        _fused_lookup_case(w2, tok2, 2)
+    say("[fused lookup] equal to the two calls on every case")
