@@ -124,10 +124,24 @@ __device__ __forceinline__ Threshold local_threshold(const CountSmem& sm, int r,
     return th;
 }
 
+// Word i (= 4 q + d: load q, word d) of this thread's columns of a row, for an index that differs
+// between lanes: a select over the loads, then over the words (no indexed register access).
+__device__ __forceinline__ uint32_t word_at(const u32x4 (&v)[kLoads], int i) {
+    // (masks rather than selects, which the compiler would turn back into an indexed access of a
+    // register array placed in scratch memory)
+    uint32_t w = 0u;
+#pragma unroll
+    for (int qq = 0; qq < kLoads; ++qq)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) w |= v[qq][d] & (0u - (uint32_t)(i == qq * 4 + d));
+    return w;
+}
+
 // Marks this thread's elements of one row: cand for those above the threshold key (and at it
-// when every element there is needed), ties for those at it otherwise.  Pairs of values whose
-// larger order key is below tau - 1 (-0 has the packed key 0x7FFF, one below +0) are skipped
-// two at a time.
+// when every element there is needed), ties for those at it otherwise.  One pass over the words
+// finds those holding a value whose order key is at least tau - 1 (-0 has the packed key 0x7FFF,
+// one below +0); only those words are examined element by element (few: the threshold leaves at
+// most a few dozen elements of the slice above it).
 struct TopMarks {
     uint32_t cand, ties;
 };
@@ -135,7 +149,7 @@ __device__ __forceinline__ TopMarks top_marks(const Threshold& th, int c0, int V
     const uint32_t tau = th.tau;
     const bool all_ties = th.ties == th.need;
     const uint16_t lo_t = tau > 0u ? (uint16_t)(tau - 1u) : (uint16_t)0;
-    uint32_t cand = 0u, ties = 0u;
+    uint32_t words = 0u;  // bit 4 q + d: word d of load q holds a key >= lo_t
 #pragma unroll
     for (int q = 0; q < kLoads; ++q)
 #pragma unroll
@@ -143,20 +157,39 @@ __device__ __forceinline__ TopMarks top_marks(const Threshold& th, int c0, int V
             const uint32_t w = v[q][d];
             const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, w) >> (i16x2)(int16_t)15);
             const u16x2 k2 = __builtin_bit_cast(u16x2, w ^ (neg | 0x80008000u));
-            if (max(k2[0], k2[1]) < lo_t) continue;
-#pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-                const int e = 2 * d + e2;
-                const uint32_t h = e2 ? (w >> 16) : (w & 0xFFFFu);
-                if (col_of(c0, q, e) >= V || (h & 0x7FFFu) >= 0x7F80u) continue;  // past the row, inf, NaN
-                const uint32_t k = key16(h);
-                const bool at = k == tau && th.need > 0;
-                const bool c = k > tau || (at && all_ties);
-                cand |= (c ? 1u : 0u) << (q * 8 + e);
-                ties |= (at && !c ? 1u : 0u) << (q * 8 + e);
-            }
+            words |= (max(k2[0], k2[1]) >= lo_t ? 1u : 0u) << (q * 4 + d);
         }
+    uint32_t cand = 0u, ties = 0u;
+    while (words != 0u) {
+        const int i = __builtin_ctz(words);
+        words &= words - 1u;
+        const uint32_t w = word_at(v, i);
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+            const int b = 2 * i + e2;  // element bit: 8 q + e
+            const uint32_t h = e2 ? (w >> 16) : (w & 0xFFFFu);
+            if (col_of(c0, b >> 3, b & 7) >= V || (h & 0x7FFFu) >= 0x7F80u) continue;  // past the row, inf, NaN
+            const uint32_t k = key16(h);
+            const bool at = k == tau && th.need > 0;
+            const bool c = k > tau || (at && all_ties);
+            cand |= (c ? 1u : 0u) << b;
+            ties |= (at && !c ? 1u : 0u) << b;
+        }
+    }
     return TopMarks{cand, ties};
+}
+
+// This thread's marked elements of a row (bit 8 q + e of m) into the row's candidate list from
+// slot on, in bit order (a lane holds one or two at most, mostly).
+__device__ __forceinline__ void write_marked(RowPart* P, uint32_t m, int slot, int c0, const u32x4 (&v)[kLoads]) {
+    while (m != 0u && slot < kTop) {
+        const int b = __builtin_ctz(m);
+        m &= m - 1u;
+        const uint32_t w = word_at(v, b >> 1);
+        P->top_key[slot] = key16((w >> (16 * (b & 1))) & 0xFFFFu);
+        P->top_id[slot] = col_of(c0, b >> 3, b & 7);
+        ++slot;
+    }
 }
 
 // The first L[r] elements (token order: key desc, id asc) of each row r in this slice (none for
@@ -180,7 +213,7 @@ __device__ __forceinline__ void local_tops(const FastArgs& f, CountSmem& sm, int
         th[r].tau = __builtin_amdgcn_readfirstlane(th[r].tau);
         th[r].need = __builtin_amdgcn_readfirstlane(th[r].need);
         th[r].ties = __builtin_amdgcn_readfirstlane(th[r].ties);
-        const TopMarks m = top_marks(th[r], c0, V, r ? vp : vq);
+        const TopMarks m = r ? top_marks(th[r], c0, V, vp) : top_marks(th[r], c0, V, vq);
         cand[r] = m.cand;
         ties[r] = m.ties;
     }
@@ -194,19 +227,8 @@ __device__ __forceinline__ void local_tops(const FastArgs& f, CountSmem& sm, int
         if (m == 0u) continue;
         RowPart* P = part_of(f, unit, slice, r);
         int slot = r ? before >> 16 : before & 0xFFFF;
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (!((m >> (q * 8 + e)) & 1u)) continue;
-                if (slot < kTop) {
-                    const uint32_t w = r ? vp[q][e >> 1] : vq[q][e >> 1];
-                    P->top_key[slot] = key16((w >> (16 * (e & 1))) & 0xFFFFu);
-                    P->top_id[slot] = col_of(c0, q, e);
-                }
-                ++slot;
-            }
-        }
+        if (r) write_marked(P, m, slot, c0, vp);
+        else write_marked(P, m, slot, c0, vq);
     }
     // then the first `need` elements at tau in token order (uniform loop; rare)
 #pragma unroll
