@@ -59,6 +59,8 @@ struct Cut {       // a cut in token order: keep key > key, and the first `take`
     int slot;         // scan slot of `key`
 };
 
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
 struct RowView {   // the settled view of one row
     int bad, overflow, greedy, argmax;
     float m;
@@ -413,8 +415,32 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
         }
     }
     // candidate ranks in token order (key desc, id asc) over every slice's list of the row:
-    // the stage in batches of 8 (invalid slots hold 0, below every listed candidate)
-    if (nst > 0 && (cord[0] != 0ull || cord[1] != 0ull)) {
+    // rank = staged order words above the candidate's (invalid slots hold 0, below every
+    // listed candidate).  Up to 128 candidates, T = 2, 4 or 8 consecutive threads share one
+    // candidate, each comparing it with every T-th pair of the stage, and their partial ranks
+    // are summed across the group; beyond that each thread ranks its own two against the
+    // whole stage in batches of 8.
+    const int T = nst <= 32 ? 8 : nst <= 64 ? 4 : nst <= 128 ? 2 : 1;  // (uniform per wave)
+    if (T > 1) {
+        const int pc = cu / T, part = cu & (T - 1);
+        const uint64_t o = pc < nst ? ss.stage[cr][pc] : 0ull;
+        int rk = 0;
+        if (o != 0ull) {
+            const u64x2* sl2 = reinterpret_cast<const u64x2*>(ss.stage[cr]);
+#pragma unroll 4
+            for (int q = part; q < nst8 / 2; q += T) {
+                const u64x2 v = sl2[q];
+                rk += (v[0] > o ? 1 : 0) + (v[1] > o ? 1 : 0);
+            }
+        }
+        rk += dpp<kDppQuadSwap1>(rk);
+        if (T >= 4) rk += dpp<kDppQuadSwap2>(rk);
+        if (T >= 8) rk += dpp<kDppRowHalfMirror>(rk);
+        if (part == 0 && o != 0ull && rk < cwant) {
+            ss.okey[cr][rk] = (uint32_t)(o >> 32);
+            ss.oid[cr][rk] = (int32_t)~(uint32_t)o;
+        }
+    } else if (nst > 0 && (cord[0] != 0ull || cord[1] != 0ull)) {
         const uint64_t o0 = cord[0], o1 = cord[1];
         int r0 = 0, r1 = 0;
         const uint64_t* sl = ss.stage[cr];
