@@ -28,7 +28,7 @@ struct CountSmem {
     uint32_t cnt_s[2];
     uint32_t flags[2];
     uint32_t neginf[2];
-    uint32_t grp[2][2];  // groups of 64 bins the slice holds, per row
+    alignas(8) uint32_t grp[2][2];  // groups of 64 bins the slice holds, per row (low word first)
     int32_t scan[kWaves + 1];
     double redd[kWaves];
     int32_t redi[kWaves];
@@ -327,9 +327,15 @@ __device__ __forceinline__ uint32_t scan_entries(CountSmem& sm, bool two, const 
     const int wave = tid / kWave;
     // (the counts are read again after the scan: the columns stay live in registers meanwhile)
     uint32_t nz[2] = {0u, 0u}, cs[2] = {0u, 0u};
-    uint64_t gm[2] = {0ull, 0ull};
     const int b0 = tid < kPubThreads ? tid * kPer : 0;  // (reads are unconditional, then masked)
     const bool mine = tid < kPubThreads;
+    // groups of 64 bins holding elements: a wave's 6 x 64 bins are exactly groups 6 w .. 6 w + 5,
+    // and a thread's bins lie in group b0 / 64 or the next, below bin `split`
+    static_assert(kWave * kPer == 6 * kGroup, "a wave covers six whole groups");
+    const int bt = tid * kPer;  // (past the bins for tid >= kPubThreads: gw stays 0 there)
+    const int gl = (bt >> 6) - 6 * wave;
+    const int split = (((bt >> 6) + 1) << 6) - bt;
+    uint32_t gw[2] = {0u, 0u};
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -337,18 +343,14 @@ __device__ __forceinline__ uint32_t scan_entries(CountSmem& sm, bool two, const 
             const uint32_t c0 = sm.hist(r)[b0 + i];
             const uint32_t c = (r < rows && mine) ? c0 : 0u;
             cs[r] += c;
-            if (c != 0u) {
-                ++nz[r];
-                gm[r] |= 1ull << ((tid * kPer + i) / kGroup);
-            }
+            nz[r] += c != 0u ? 1u : 0u;
+            gw[r] |= c != 0u ? (i < split ? 1u : 2u) : 0u;
         }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        const uint32_t lo = wave_or((uint32_t)gm[r]), hi = wave_or((uint32_t)(gm[r] >> 32));
-        if (lane == 0 && r < rows && (lo | hi) != 0u) {
-            atomicOr(&sm.grp[r][0], lo);
-            atomicOr(&sm.grp[r][1], hi);
-        }
+        const uint32_t w6 = wave_or(gw[r] << gl);  // bit x: group 6 w + x
+        if (lane == 0 && r < rows && w6 != 0u)
+            atomicOr(reinterpret_cast<unsigned long long*>(&sm.grp[r][0]), (unsigned long long)w6 << (6 * wave));
     }
     // entries (12 bits) and elements (15 bits) of both rows in one 64-bit scan (one barrier)
     const uint64_t v = (uint64_t)nz[0] | ((uint64_t)cs[0] << 12) | ((uint64_t)nz[1] << 27) | ((uint64_t)cs[1] << 39);
