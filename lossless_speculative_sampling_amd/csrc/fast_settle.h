@@ -28,6 +28,14 @@ constexpr int kSlotHN = kSlotTN + 1 + kNegBins, kSlots = kSlotHN + 1;  // 2820, 
 constexpr int kRowThreads = kThreads / 2;                            // a row's share of the workgroup
 constexpr int kSlotsPer = (kSlots + kRowThreads - 1) / kRowThreads;    // 12 consecutive slots per thread
 static_assert(kSlotsPer * kRowThreads >= kSlots, "slots covered");
+// the row threads' slot kinds in pass A (see there)
+constexpr int kBinThreads = (kNegBins + kSlotsPer - 1) / kSlotsPer;     // 118 per sign
+constexpr int kBinTail = kNegBins - (kBinThreads - 1) * kSlotsPer;      // 4
+constexpr int kTinyThread = 1 + kBinThreads;                           // 119
+constexpr int kNegThread0 = kTinyThread + 1;                           // 120
+constexpr int kHugeNegThread = kNegThread0 + kBinThreads;              // 238
+static_assert(kHugeNegThread < kRowThreads && kBinTail > 0 && kBinTail <= kSlotsPer, "pass A thread kinds");
+static_assert(kSlotTP - kSlotHP - 1 == kNegBins && kSlotHN - kSlotTN - 1 == kNegBins, "bins per sign");
 constexpr int kSpMerge = 256;   // specials of one row merged in LDS (more: the general path)
 constexpr int kEntIt = 12;      // sparse entries each thread loads per batch
 constexpr int kStageCap = 512;  // staged candidates per row: every slice's list
@@ -473,7 +481,21 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     const bool live_row = r < rows;
     const int rr0 = live_row ? r : 0;
     RowView& rv = ss.rv[rr0];
-    const int s0 = u * kSlotsPer;
+    // this thread's slots, consecutive in slot (descending key) order and of one kind: thread 0
+    // the huge positive values; threads 1 .. kBinThreads the positive bins (the last one the
+    // remaining kBinTail); the next thread the tiny positive values, zero and the tiny negative
+    // values; then the negative bins (the first thread the kBinTail highest); then the huge
+    // negative values.  A bin thread reads its counts at fixed offsets from one address.
+    const bool pos_t = u >= 1 && u <= kBinThreads;
+    const bool neg_t = u >= kNegThread0 && u < kHugeNegThread;
+    const int s0 = u == 0 ? kSlotHP
+                 : pos_t ? 1 + kSlotsPer * (u - 1)
+                 : u == kTinyThread ? kSlotTP
+                 : neg_t ? (u == kNegThread0 ? kSlotTN + 1 : kSlotTN + 1 + kBinTail + kSlotsPer * (u - kNegThread0 - 1))
+                 : u == kHugeNegThread ? kSlotHN : kSlots;
+    const int nb = pos_t ? (u == kBinThreads ? kBinTail : kSlotsPer) : neg_t ? (u == kNegThread0 ? kBinTail : kSlotsPer) : 0;
+    // bin of slot s0 (bins descend with the slot); bin - 11 >= 0 for every bin thread
+    const int bb = pos_t ? kBins - s0 : neg_t ? kSlotHN - 1 - s0 : kSlotsPer - 1;
     // (flags read before the scan: single threads update them after it)
     // (read unconditionally and combined without short-circuits: no branch waits on each read)
     // (uniform in each wave: kept in scalar registers)
@@ -486,11 +508,16 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     uint32_t c[kSlotsPer];
     uint32_t nloc = 0, nz = 0;
     int first = -1;
+    const uint32_t* hb = sm.hist(rr0) + (bb - (kSlotsPer - 1));
+    const uint32_t a0 = ss.agg_n[rr0][0], a1 = ss.agg_n[rr0][1], a2 = ss.agg_n[rr0][2], a3 = ss.agg_n[rr0][3];
+    const uint32_t cz = sm.hist(rr0)[kZeroBin];
 #pragma unroll
     for (int i = 0; i < kSlotsPer; ++i) {
-        const int s = s0 + i;
-        const int b = slot_bin(s);
-        c[i] = (!live_row || s >= kSlots) ? 0u : (b >= 0 ? sm.hist(rr0)[b] : ss.agg_n[rr0][slot_agg(s)]);
+        uint32_t v = i < nb ? hb[kSlotsPer - 1 - i] : 0u;
+        if (i == 0) v = u == 0 ? a0 : u == kTinyThread ? a1 : u == kHugeNegThread ? a3 : v;
+        if (i == 1) v = u == kTinyThread ? cz : v;
+        if (i == 2) v = u == kTinyThread ? a2 : v;
+        c[i] = live_row ? v : 0u;
         nloc += c[i];
         nz += c[i] != 0u ? 1u : 0u;
         if (c[i] != 0u && first < 0) first = i;
