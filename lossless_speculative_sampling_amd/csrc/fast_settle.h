@@ -702,21 +702,28 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
         const Cut& ct = cc ? v.cp : v.ck;
         return (ok && (cc ? v.has_p : v.has_k) && ct.key != 0u && ct.slot != kNone) ? bin_of_key(ct.key) : -1;
     };
-    const int cb00 = cut_bin(0, 0), cb01 = cut_bin(0, 1), cb10 = cut_bin(1, 0), cb11 = cut_bin(1, 1);
+    // (lane 2 rr + cc of every wave works out cut cc of row rr: one round of LDS reads, not four)
+    const int cbl = lane < 4 ? cut_bin(lane >> 1, lane & 1) : -1;
+    const int cb00 = __builtin_amdgcn_readlane(cbl, 0), cb01 = __builtin_amdgcn_readlane(cbl, 1),
+              cb10 = __builtin_amdgcn_readlane(cbl, 2), cb11 = __builtin_amdgcn_readlane(cbl, 3);
 #define CBIN(rr, cc) ((rr) ? ((cc) ? cb11 : cb10) : ((cc) ? cb01 : cb00))
     const bool any_cut = cb00 >= 0 || cb01 >= 0 || cb10 >= 0 || cb11 >= 0;
     if (any_cut && gi < G) {
         const int n = (int)ss.hdr[gr][gt][1];
         const int nv = n > x0 ? (n - x0 + tpg - 1) >> lgt : 0;
         const int c0b = CBIN(gr, 0), c1b = CBIN(gr, 1);
+        // a slice row lists a bin at most once and never with count 0: the count found at each
+        // cut bin (0: none), without a branch per entry
+        uint32_t h0 = 0u, h1 = 0u;
 #pragma unroll
         for (int it = 0; it < kEntIt; ++it) {
-            if (it < nv) {
-                const int b = (int)(e2[it] >> 16);
-                if (b == c0b) ss.pc[gr][0][gt] = e2[it] & 0xFFFFu;
-                if (b == c1b) ss.pc[gr][1][gt] = e2[it] & 0xFFFFu;
-            }
+            const uint32_t e = it < nv ? e2[it] : 0xFFFFFFFFu;  // (bin 0xFFFF is no cut bin)
+            const int b = (int)(e >> 16);
+            h0 = b == c0b ? (e & 0xFFFFu) : h0;
+            h1 = b == c1b ? (e & 0xFFFFu) : h1;
         }
+        if (h0 != 0u) ss.pc[gr][0][gt] = h0;
+        if (h1 != 0u) ss.pc[gr][1][gt] = h1;
     }
     if (any_cut && more_ent) {
         for (int g = 0; g < G; ++g) {  // entries past the batch (uniform loop; rare)
