@@ -106,6 +106,7 @@ struct SettleSmem {
     double agg_m[2][4];
     uint32_t pc[2][2][kMaxSlices];    // per-slice counts at the top-k / nucleus cut bins
     double cand_e[kTop];              // masses of the draft row's leading candidates
+    double cand_pre[kTop];            // and their inclusive prefix sums in token order
     uint64_t wq[2][4];                // per-row wave partials of the scans
     double wd[2][4];
     uint32_t wk[2][4];
@@ -632,9 +633,13 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
         const uint32_t sb = rv.s_bits;  // exp((z_s - m) / T)
         rv.e_s = ((sb & 0x7FFFu) < 0x7F80u && nfin > 0u) ? mass_lean(__uint_as_float(sb << 16), m, invT) : 0.0;
     }
-    if (dw && r == 1 && cuts2 && a.F > 0 && a.C < 1.0f && u >= kRowThreads - kWave) {
+    if (dw && r == 1 && cuts2 && a.F > 0 && a.C < 1.0f && u >= kRowThreads - kWave) {  // (a whole wave)
         const int l = u - (kRowThreads - kWave);
-        if (l < min(a.F, rv.nm)) ss.cand_e[l] = mass_lean(key16_value(ss.okey[1][l]), m, invT);
+        const double ec = l < min(a.F, rv.nm) ? mass_lean(key16_value(ss.okey[1][l]), m, invT) : 0.0;
+        double ex;
+        const double ei = wave_scan(ec, &ex);
+        ss.cand_e[l] = ec;
+        ss.cand_pre[l] = ei;
     }
     const Scan2 sc = row_scan2(wloc, kloc, ss);
     const double Skept = sc.wtot;
@@ -760,7 +765,8 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
             const int n0 = min(min(a.F, n_nuc), nm);
             const double ec = lane < n0 ? ss.cand_e[lane] : 0.0;
             n = last_lane(__ballot(lane < n0 && ec > 0.0)) + 1;
-            const double psum = wave_sum(lane < n ? ec / S : 0.0);
+            // (the masses fall in token order: the set is a prefix of the candidates)
+            const double psum = n > 0 ? ss.cand_pre[n - 1] / S : 0.0;
             if (n > 0) {
                 kF = ss.okey[1][n - 1];
                 idF = ss.oid[1][n - 1];
