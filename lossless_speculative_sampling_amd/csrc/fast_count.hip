@@ -514,32 +514,26 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
         const bool vd = P.j < a.K;      // the drafted token is verified here
         const bool vrow = vd && two;     // against a draft row (not the uniform draft)
         settle_rows(f, sm, unit, P.slice, P.j, two ? 2 : 1, prm, vd, s_tok);
-        const bool bad = us.rv[0].bad || (vrow && us.rv[1].bad);
-        fallback = (!bad && (us.rv[0].overflow || (vrow && us.rv[1].overflow))) ? 1 : 0;
+        // every value the outcome needs, read at once and combined without branches (a chain of
+        // dependent reads and branches costs a round trip each)
+        const RowView& v0 = us.rv[0];
+        const RowView& v1 = us.rv[1];
+        const int bad0 = v0.bad, bad1 = v1.bad, ov0 = v0.overflow, ov1 = v1.overflow, dg1 = v1.degenerate;
+        const int gr0 = v0.greedy, am0 = v0.argmax;
+        const uint32_t xb0 = v0.xcc_bad, xb1 = v1.xcc_bad;
+        const double ps_row = us.ps, qs = us.qs, u = sm.u_acc;
+        const bool bad = (bad0 != 0) | (vrow & (bad1 != 0));
+        const bool ovf = (ov0 != 0) | (vrow & (ov1 != 0));
         // the unit's slices did not share one XCD's L2: the request is redone by the general path
-        if (us.rv[0].xcc_bad || (two && us.rv[1].xcc_bad)) {
-            fallback = 1;
-            if (threadIdx.x == 0) atomicOr(&reinterpret_cast<ReqFast*>(f.ws + f.L.reqs)[P.b].pad, (int32_t)kStPlacement);
-        }
-        if (bad) {
-            status = kStBadLogit;
-        } else if (!fallback) {
-            if (vrow && us.rv[1].degenerate) status |= kStDegenerate;
-            if (!tok_ok) {
-                status |= kStBadToken;
-            } else if (vd) {
-                if (us.rv[0].greedy) {
-                    accept = (s_tok == us.rv[0].argmax) ? 1 : 0;
-                } else {
-                    const double ps = f.uniform ? 1.0 / (double)a.V : us.ps, qs = us.qs;
-                    if (!(ps > 0.0)) status |= kStOutside;
-                    const double u = sm.u_acc;
-                    accept = (u * ps < qs) ? 1 : 0;
-                }
-            } else {
-                accept = 1;  // bonus position
-            }
-        }
+        const bool misplaced = (xb0 != 0u) | (two & (xb1 != 0u));
+        fallback = ((!bad & ovf) | misplaced) ? 1 : 0;
+        if (misplaced && threadIdx.x == 0) atomicOr(&reinterpret_cast<ReqFast*>(f.ws + f.L.reqs)[P.b].pad, (int32_t)kStPlacement);
+        const double ps = f.uniform ? 1.0 / (double)a.V : ps_row;
+        const int acc_v = gr0 ? (s_tok == am0 ? 1 : 0) : (u * ps < qs ? 1 : 0);
+        const uint32_t st = ((vrow & (dg1 != 0)) ? kStDegenerate : 0u) | (!tok_ok ? kStBadToken : 0u) |
+                            ((tok_ok & vd & (gr0 == 0) & !(ps > 0.0)) ? kStOutside : 0u);
+        status = bad ? kStBadLogit : fallback ? 0u : st;
+        accept = (bad | (fallback != 0) | !tok_ok) ? 0 : (vd ? acc_v : 1);  // (the bonus position accepts)
     }
     // the outcome cache's depth-j list: the first F_j candidates of the draft row in token order,
     // less the drafted token; rows the candidate lists cannot settle (NaN or +inf, too many
@@ -548,7 +542,7 @@ __device__ __forceinline__ void settle_unit(const FastArgs& f, CountSmem& sm, co
         const int Fj = f.fan.f[P.j];
         const int want = Fj + (P.j < a.K ? 1 : 0);
         const RowView& rv = us.rv[1];
-        const bool general = !param_ok || rv.bad || rv.overflow || rv.nm < min(want, a.V);
+        const bool general = !param_ok | (rv.bad != 0) | (rv.overflow != 0) | (rv.nm < min(want, a.V));
         if (threadIdx.x == 0) reinterpret_cast<int32_t*>(f.ws + f.L.cache_gen)[unit] = general ? 1 : 0;
         if (!general && threadIdx.x < kWave) {
             const int lane = threadIdx.x;
