@@ -177,6 +177,7 @@ __host__ __device__ inline Layout layout(int B, int units, int nS) {
 struct FastArgs {
     VerifyArgs a;
     int nS;
+    int halves;  // resolve workgroups per slice of the residual: 2 (halves of the chunks) or 1
     int units;
     char* ws;
     Layout L;
@@ -317,6 +318,8 @@ __device__ __forceinline__ uint32_t hist_offsets2(uint32_t w) {
 
 void launch_count(const FastArgs& f, int grid, hipStream_t stream);
 void launch_resolve(const FastArgs& f, int grid, hipStream_t stream);
+// Workgroups of the resolve kernel the current device holds at once (occupancy x CUs).
+int resolve_resident();
 void launch_diverge(const FastArgs& f, int grid, hipStream_t stream);
 
 }  // namespace fast

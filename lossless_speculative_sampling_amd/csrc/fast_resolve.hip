@@ -5,6 +5,8 @@
 // order (DeepMind speculative-sampling page, sections 1 and 3; SSD reading notes, section
 // 2.2).  Requests whose units the counts could not settle run the general algorithm.
 #include "fast_common.h"
+
+#include <atomic>
 #include "rowproc.h"
 
 namespace sv {
@@ -381,7 +383,7 @@ __device__ __forceinline__ double tab_at(const char* base, uint32_t off) {
 // Residual of unit k over this workgroup's half of the slice (its half of the loads), per
 // 512-column chunk: table lookups for every element; a thread's 8 columns of one chunk that
 // met a marker are recomputed exactly.
-__device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, int b, int slice, int half, int c0, bool two,
+__device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, int b, int slice, int half, int halves, int c0, bool two,
                                                bool uni, const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads]) {
     const double pu = 1.0 / (double)f.a.V;  // the uniform draft's probability
     const VerifyArgs& a = f.a;
@@ -395,7 +397,7 @@ __device__ __forceinline__ void residual_slice(const FastArgs& f, ResSmem& sm, i
     static_assert(kLoads % 2 == 0, "halves of a slice");
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) {
-        if (q / (kLoads / 2) != half) continue;
+        if (halves == 2 && q / (kLoads / 2) != half) continue;
         double s = 0.0;
         const int cq = col_of(c0, q, 0);
         if (cq < a.V) {
@@ -728,10 +730,11 @@ __device__ __forceinline__ void general_request(const FastArgs& f, ResSmem& sm, 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void fast_resolve_kernel(FastArgs f) {
     __shared__ ResSmem sm;
     const VerifyArgs& a = f.a;
-    // placement as in the count kernel (request b on XCD b % 8), R = max(2 nS, K + 1)
-    // workgroups per request; workgroup w of a request is half w % 2 of slice w / 2 of unit k
-    // (residual) or unit w (general algorithm, cache rows)
-    const int R = max(2 * f.nS, a.K + 1);
+    // placement as in the count kernel (request b on XCD b % 8), R = max(H nS, K + 1)
+    // workgroups per request (H = f.halves); workgroup w of a request is half w % H of slice
+    // w / H of unit k (residual) or unit w (general algorithm, cache rows)
+    const int H = f.halves;
+    const int R = max(H * f.nS, a.K + 1);
     const int x = blockIdx.x % kXcd, l = blockIdx.x / kXcd;
     const int b = (l / R) * kXcd + x, w = l % R;
     if (b >= a.B) return;
@@ -744,14 +747,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const bool pre = (a.K + 1) * kRecWords <= kThreads;  // otherwise loaded once k is known
     const int pj = (int)threadIdx.x / kRecWords, pw = (int)threadIdx.x % kRecWords;
     uint32_t pre_word = 0u;
-    if (pre && pj <= a.K && (w >> 1) < f.nS) {
+    const int wslice = H == 2 ? w >> 1 : w;  // the slice of the residual this workgroup sums
+    if (pre && pj <= a.K && wslice < f.nS) {
         const int uj = b * (a.K + 1) + pj;
         const UnitFast* Uj = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + uj;
         if (pw < kWCut) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->rq) + pw);
         else if (pw < kWFlag) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->cut[0][0]) + (pw - kWCut));
-        else if (pw < kWDraw) pre_word = ldnt(&part_of(f, uj, w >> 1, pw - kWFlag)->flags);
+        else if (pw < kWDraw) pre_word = ldnt(&part_of(f, uj, wslice, pw - kWFlag)->flags);
         else if (pw < kWGrp) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->u_res) + (pw - kWDraw));
-        else if (pw < kWGrp + 4) pre_word = ldnt(&part_of(f, uj, w >> 1, (pw - kWGrp) >> 1)->groups[(pw - kWGrp) & 1]);
+        else if (pw < kWGrp + 4) pre_word = ldnt(&part_of(f, uj, wslice, (pw - kWGrp) >> 1)->groups[(pw - kWGrp) & 1]);
     }
     // the request's decision and this unit's cache flag, loaded together
     static_assert(sizeof(ReqFast) == 16, "one 16-byte record");
@@ -782,7 +786,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     // mode 1: the residual of unit k, slice w / 2; each half of the slice's loads is summed by
     // its own workgroup (both load the whole slice: the owner of a cut orders its ties over it)
     const int k = (int)req[1];
-    const int slice = w >> 1, half = w & 1;
+    const int slice = wslice, half = H == 2 ? w & 1 : 0;
     if (slice >= f.nS) return;
     const int unit = b * (a.K + 1) + k;
     const uint32_t status = req[2];
@@ -849,8 +853,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         const bool writer = (uc.key == 0u || uc.explicit_id >= 0) ? slice == 0 : slice == uc.owner;
         if (writer && half == 0) reinterpret_cast<int32_t*>(f.ws + f.L.idcut)[b * 4 + threadIdx.x] = sm.eff[r][c];
     }
-    residual_slice(f, sm, b, slice, half, c0, two, uni, vq, vp);
-    if (!arrive_last(f, sm, b, 2 * f.nS)) return;
+    residual_slice(f, sm, b, slice, half, H, c0, two, uni, vq, vp);
+    if (!arrive_last(f, sm, b, H * f.nS)) return;
     finalize_residual(f, sm, b, k, status, sm.u_res);
 }
 
@@ -1224,6 +1228,23 @@ void launch_diverge(const FastArgs& f, int grid, hipStream_t stream) {
 
 void launch_resolve(const FastArgs& f, int grid, hipStream_t stream) {
     hipLaunchKernelGGL(fast_resolve_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, f);
+}
+
+int resolve_resident() {
+    // per device, worked out once (0 until then: a failed query keeps two workgroups per slice)
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1 << 30;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fast_resolve_kernel, kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 || cus <= 0)
+        return 1 << 30;
+    v = per_cu * cus;
+    cached[dev].store(v, std::memory_order_relaxed);
+    return v;
 }
 
 }  // namespace fast

@@ -23,7 +23,13 @@ FastPlan fast_plan(int B, int K, int V) {
     p.units = B * (K + 1);
     const int reqs_per_xcd = (B + kXcd - 1) / kXcd;
     p.grid = kXcd * reqs_per_xcd * (K + 1) * p.nS;
-    p.grid_resolve = kXcd * reqs_per_xcd * max(2 * p.nS, K + 1);  // two workgroups per slice
+    // two workgroups per slice of the residual when they all fit on the device at once (the
+    // residual pass's latency halves); beyond one round of workgroups, one per slice (half as many
+    // fixed phases).  Two also whenever a request has more cache rows than slices, so that every
+    // workgroup writing a cache row is one of the residual's (the fused lookup's rendezvous).
+    const int two_grid = kXcd * reqs_per_xcd * max(2 * p.nS, K + 1);
+    p.halves = (two_grid <= resolve_resident() || K + 1 > p.nS) ? 2 : 1;
+    p.grid_resolve = p.halves == 2 ? two_grid : kXcd * reqs_per_xcd * max(p.nS, K + 1);
     p.grid_diverge = kXcd * reqs_per_xcd * p.nS * K;               // one per slice of every drafted position
     p.ws_bytes = layout(B, p.units, p.nS).total;
     return p;
@@ -51,6 +57,7 @@ static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t
     FastArgs f;
     f.a = a;
     f.nS = p.nS;
+    f.halves = p.halves;
     f.units = p.units;
     f.ws = static_cast<char*>(ws);
     f.L = layout(a.B, p.units, p.nS);
