@@ -286,8 +286,19 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     const bool merge_mine = gi < G && gt != own;
     const uint32_t* ebase = part_c(f, unit, gt, gr)->ent;  // (gi >= G: the unit's first record, unused)
     const int x0 = tid & (tpg - 1);
+    // thread x0 of a group takes entries [x0 kEntIt, x0 kEntIt + kEntIt) in 16-byte loads (a
+    // start inside the list ends inside it: kBins is a multiple of kEntIt; later starts read
+    // entry 0 and count none)
+    static_assert(kBins % kEntIt == 0 && kEntIt % 4 == 0, "whole 16-byte loads within a list");
+    const int e0 = x0 * kEntIt < kBins ? x0 * kEntIt : 0;
 #pragma unroll
-    for (int it = 0; it < kEntIt; ++it) ent[it] = ldnt(ebase + min(x0 + it * tpg, kBins - 1));
+    for (int it = 0; it < kEntIt; it += 4) {
+        const u32x4 v = ldnt(reinterpret_cast<const u32x4*>(ebase + e0 + it));
+        ent[it] = v[0];
+        ent[it + 1] = v[1];
+        ent[it + 2] = v[2];
+        ent[it + 3] = v[3];
+    }
     // candidates: thread u of row r stages positions u and u + 256 of the row's slice-major list
     const int cr = tid / kRowThreads, cu = tid % kRowThreads;
     const int cwant = cr < rows ? (cr ? want1 : want0) : 0;
@@ -347,7 +358,7 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     //      the candidates' ranks ----
     if (merge_mine) {
         const int n = (int)ss.hdr[gr][gt][1];
-        const int nv = n > x0 ? (n - x0 + tpg - 1) >> lgt : 0;  // this thread's entries below n
+        const int nv = min(max(n - x0 * kEntIt, 0), kEntIt);  // this thread's entries below n
 #pragma unroll
         for (int it = 0; it < kEntIt; ++it)
             if (it < nv) atomicAdd(&sm.hist(gr)[ent[it] >> 16], ent[it] & 0xFFFFu);
@@ -602,7 +613,13 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     //      while the masses are summed ----
     uint32_t e2[kEntIt];
 #pragma unroll
-    for (int it = 0; it < kEntIt; ++it) e2[it] = ldnt(ebase + min(x0 + it * tpg, kBins - 1));
+    for (int it = 0; it < kEntIt; it += 4) {
+        const u32x4 v = ldnt(reinterpret_cast<const u32x4*>(ebase + e0 + it));
+        e2[it] = v[0];
+        e2[it + 1] = v[1];
+        e2[it + 2] = v[2];
+        e2[it + 3] = v[3];
+    }
 
     // ---- pass B (masses): the compact list spread evenly over the row's threads ----
     const bool cuts2 = cuts && !rv.overflow;
@@ -715,7 +732,7 @@ __device__ __forceinline__ void settle_rows(const FastArgs& f, Smem& sm, int uni
     const bool any_cut = cb00 >= 0 || cb01 >= 0 || cb10 >= 0 || cb11 >= 0;
     if (any_cut && gi < G) {
         const int n = (int)ss.hdr[gr][gt][1];
-        const int nv = n > x0 ? (n - x0 + tpg - 1) >> lgt : 0;
+        const int nv = min(max(n - x0 * kEntIt, 0), kEntIt);
         const int c0b = CBIN(gr, 0), c1b = CBIN(gr, 1);
         // a slice row lists a bin at most once and never with count 0: the count found at each
         // cut bin (0: none), without a branch per entry
