@@ -285,25 +285,39 @@ __device__ __forceinline__ void local_ranks(CountSmem& sm, bool two, int c0, int
         }
         return;
     }
+    // Equal keys are equal bf16 bit patterns, except that -0 and +0 share one key: a word's two
+    // values are compared with the token's pattern at once (the sign bits masked off for zero),
+    // and a 16-bit half is zero exactly when ((x & 0x7FFF) + 0x7FFF) | x has its top bit clear.
+    // Loads past the token's column hold no element before it (a uniform skip); in the load that
+    // holds it, each thread masks the elements at or after it.
+    const int q_tok = (s_tok - c0) / (kThreads * 8);  // the load holding the token's column
     uint32_t packed = 0;  // row 0 in the low half, row 1 in the high half (each < 2^16)
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         if (r == 1 && !two) break;
         const uint32_t h_s = sm.s_bits[r];
-        if ((h_s & 0x7FFFu) >= 0x7F80u) continue;
-        const uint32_t ks = key16(h_s);
+        if ((h_s & 0x7FFFu) >= 0x7F80u) continue;  // (a non-finite token value has no rank)
+        const uint32_t pat = (h_s & 0x7FFFu) == 0u ? 0u : h_s;
+        const uint32_t keep = pat == 0u ? 0x7FFF7FFFu : 0xFFFFFFFFu;
+        const uint32_t pat2 = pat * 0x10001u;
         const u32x4(&v)[kLoads] = r == 0 ? vq : vp;
-        uint32_t cnt = 0;
+        uint32_t miss = 0, slots = 0;  // compared halves that differ, halves compared
 #pragma unroll
-        for (int q = 0; q < kLoads; ++q)
+        for (int q = 0; q < kLoads; ++q) {
+            if (q > q_tok) break;
+            // elements of this thread's 8 columns of load q that precede the token: 8 below q_tok
+            const int rel = q < q_tok ? 8 : min(max(s_tok - col_of(c0, q, 0), 0), 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = col_of(c0, q, e);
-                const uint32_t w = v[q][e >> 1];
-                const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-                cnt += (col < s_tok && (h & 0x7FFFu) < 0x7F80u && key16(h) == ks) ? 1u : 0u;
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t y = (v[q][d] & keep) ^ pat2;
+                const uint32_t t = ((y & 0x7FFF7FFFu) + 0x7FFF7FFFu) | y;
+                const int left = rel - 2 * d;  // elements of word d before the token: 2, 1 or 0
+                const uint32_t vm = left >= 2 ? 0x80008000u : (left == 1 ? 0x8000u : 0u);
+                miss += (uint32_t)__popc(t & vm);
+                slots += (uint32_t)__popc(vm);
             }
-        packed += cnt << (16 * r);
+        }
+        packed += (slots - miss) << (16 * r);
     }
     packed = block_sum<uint32_t>(packed, reinterpret_cast<uint32_t*>(sm.redi));
     if (threadIdx.x < (unsigned)rows) sm.cnt_s[threadIdx.x] = (packed >> (16 * threadIdx.x)) & 0xFFFFu;
