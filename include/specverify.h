@@ -348,6 +348,24 @@ int saguaro_verify_cache_noalloc(const void* draft_logits, const void* target_lo
                                  int32_t* out_fanout_host, int32_t* out_k, int32_t* out_tstar, float* out_resid_mass,
                                  uint32_t* out_status, int32_t* out_cache, hipStream_t stream);
 
+/* saguaro_verify_cache_lookup_timed - measurement helper, not part of the method:
+ * saguaro_verify_cache_lookup with the same arguments and outputs, plus two HIP events
+ * (created by the caller, with timing enabled) that bound the execution of the kernel that reads
+ * every logit: the start and stop events of the bf16 path's count kernel launch (elsewhere,
+ * events recorded on `stream` before and after the verification, ahead of the lookup).
+ * hipEventElapsedTime of the pair gives that kernel's duration; the call's outputs and the work
+ * done are unchanged.
+ * Return codes as saguaro_verify_cache_lookup, SPEC_EINVAL also for a null event, SPEC_EHIP
+ * when an event cannot be recorded. */
+int saguaro_verify_cache_lookup_timed(const void* draft_logits, const void* target_logits, int dtype, int B, int K,
+                                      int V, const spec_params* params, int F, float C, int32_t* draft_tokens,
+                                      uint64_t seed, uint64_t round, uint32_t flags, int budget, double a, double r,
+                                      int32_t* out_fanout_host, int32_t* out_k, int32_t* out_tstar,
+                                      float* out_resid_mass, uint32_t* out_status, int32_t* out_cache,
+                                      int32_t* out_slot, uint8_t* out_hit, int32_t* out_batch, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream, hipEvent_t count_before,
+                                      hipEvent_t count_after);
+
 /* spec_read_ceiling - measurement helper, not part of the method: one plain streaming read of
  * `bytes` bytes of device memory at `data` (16-byte aligned, bytes a multiple of 16), the
  * bandwidth ceiling a verification call that reads the same number of logit bytes is compared

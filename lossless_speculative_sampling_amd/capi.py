@@ -35,7 +35,7 @@ ST_PLACEMENT = 512
 EXPORTS = ("spec_workspace_bytes", "spec_verify", "saguaro_downweight", "saguaro_fanout", "saguaro_cache_build",
            "saguaro_cache_lookup", "saguaro_verify_cache", "saguaro_backup_plan", "mirror_signpost_workspace_bytes",
            "mirror_signposts", "mirror_tree_lookup", "pyramid_verify", "spec_read_ceiling",
-           "saguaro_verify_cache_noalloc", "saguaro_verify_cache_lookup")
+           "saguaro_verify_cache_noalloc", "saguaro_verify_cache_lookup", "saguaro_verify_cache_lookup_timed")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -78,6 +78,7 @@ class Lib:
         L.saguaro_verify_cache_lookup.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
                                                   ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                   ctypes.c_size_t, _P]
+        L.saguaro_verify_cache_lookup_timed.argtypes = L.saguaro_verify_cache_lookup.argtypes + [_P, _P]
         L.saguaro_verify_cache_noalloc.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, ctypes.c_float, _P, _U64, _U64,
                                                    ctypes.c_uint32, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P]
         for fn in EXPORTS[1:]:

@@ -247,12 +247,15 @@ int saguaro_verify_cache(const void* draft_logits, const void* target_logits, in
     return launch_status();
 }
 
-int saguaro_verify_cache_lookup(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
-                                const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,
-                                uint64_t round, uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host,
-                                int32_t* out_k, int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status,
-                                int32_t* out_cache, int32_t* out_slot, uint8_t* out_hit, int32_t* out_batch,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+// saguaro_verify_cache_lookup, with optional events around the count kernel of the bf16 path
+int verify_cache_lookup_impl(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
+                             const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,
+                             uint64_t round, uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host,
+                             int32_t* out_k, int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status,
+                             int32_t* out_cache, int32_t* out_slot, uint8_t* out_hit, int32_t* out_batch,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             const fast::CountEvents* ev) {
     CacheArgs c{};
     const int arc = verify_cache_args(draft_logits, target_logits, dtype, B, K, V, params, F, C, draft_tokens, flags,
                                       budget, a, r, out_k, out_tstar, out_cache, &c);
@@ -275,15 +278,46 @@ int saguaro_verify_cache_lookup(const void* draft_logits, const void* target_log
         const size_t gen = align_up((size_t)B * (K + 1) * sizeof(UnitRec), 256);
         const fast::LookupOut lk{out_slot, out_hit, out_batch};
         return fast::fast_verify_cache_lookup(v, c, lk, static_cast<char*>(workspace) + gen, workspace_bytes - gen,
-                                              stream);
+                                              stream, ev);
     }
-    // otherwise the two calls one after the other
+    // otherwise the two calls one after the other (events around the whole first call)
+    if (ev && ev->before && hipEventRecord(ev->before, stream) != hipSuccess) return SPEC_EHIP;
     const int vrc = saguaro_verify_cache(draft_logits, target_logits, dtype, B, K, V, params, F, C, draft_tokens, seed,
                                          round, flags, budget, a, r, out_fanout_host, out_k, out_tstar, out_resid_mass,
                                          out_status, out_cache, workspace, workspace_bytes, stream);
     if (vrc != SPEC_OK) return vrc;
+    if (ev && ev->after && hipEventRecord(ev->after, stream) != hipSuccess) return SPEC_EHIP;
     return saguaro_cache_lookup(0, out_cache, c.fanout.f, K, B, out_k, out_tstar, out_slot, out_hit, out_batch, stream);
 }
+}  // namespace
+
+int saguaro_verify_cache_lookup(const void* draft_logits, const void* target_logits, int dtype, int B, int K, int V,
+                                const spec_params* params, int F, float C, int32_t* draft_tokens, uint64_t seed,
+                                uint64_t round, uint32_t flags, int budget, double a, double r, int32_t* out_fanout_host,
+                                int32_t* out_k, int32_t* out_tstar, float* out_resid_mass, uint32_t* out_status,
+                                int32_t* out_cache, int32_t* out_slot, uint8_t* out_hit, int32_t* out_batch,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return verify_cache_lookup_impl(draft_logits, target_logits, dtype, B, K, V, params, F, C, draft_tokens, seed, round,
+                                    flags, budget, a, r, out_fanout_host, out_k, out_tstar, out_resid_mass, out_status,
+                                    out_cache, out_slot, out_hit, out_batch, workspace, workspace_bytes, stream, nullptr);
+}
+
+int saguaro_verify_cache_lookup_timed(const void* draft_logits, const void* target_logits, int dtype, int B, int K,
+                                      int V, const spec_params* params, int F, float C, int32_t* draft_tokens,
+                                      uint64_t seed, uint64_t round, uint32_t flags, int budget, double a, double r,
+                                      int32_t* out_fanout_host, int32_t* out_k, int32_t* out_tstar,
+                                      float* out_resid_mass, uint32_t* out_status, int32_t* out_cache,
+                                      int32_t* out_slot, uint8_t* out_hit, int32_t* out_batch, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream, hipEvent_t count_before,
+                                      hipEvent_t count_after) {
+    if (!count_before || !count_after) return SPEC_EINVAL;
+    const fast::CountEvents ev{count_before, count_after};
+    return verify_cache_lookup_impl(draft_logits, target_logits, dtype, B, K, V, params, F, C, draft_tokens, seed, round,
+                                    flags, budget, a, r, out_fanout_host, out_k, out_tstar, out_resid_mass, out_status,
+                                    out_cache, out_slot, out_hit, out_batch, workspace, workspace_bytes, stream, &ev);
+}
+
+
 
 int saguaro_cache_lookup(int mode, const int32_t* cache, const int32_t* fanout_or_shape, int K, int B,
                          const int32_t* k, const int32_t* tstar, int32_t* out_slot, uint8_t* out_hit,

@@ -316,7 +316,7 @@ __device__ __forceinline__ uint32_t hist_offsets2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, x) + __builtin_bit_cast(u16x2, add));
 }
 
-void launch_count(const FastArgs& f, int grid, hipStream_t stream);
+void launch_count(const FastArgs& f, int grid, hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 void launch_resolve(const FastArgs& f, int grid, hipStream_t stream);
 // Workgroups of the resolve kernel the current device holds at once (occupancy x CUs).
 int resolve_resident();

@@ -1,6 +1,8 @@
 // Count kernel of the bf16 verification path: every slice of every (request, position) unit
 // loads its token columns of the target row (and the draft row), counts every distinct bf16
 // value in LDS and publishes a compact summary for the resolve kernel.
+#include <hip/hip_ext.h>
+
 #include "fast_settle.h"
 
 namespace sv {
@@ -863,8 +865,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     if (sm.last) decide_request(f, P.b);
 }
 
-void launch_count(const FastArgs& f, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL(fast_count_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, f);
+void launch_count(const FastArgs& f, int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    if (start || stop)  // (the events bound the kernel's own execution)
+        hipExtLaunchKernelGGL(fast_count_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, start, stop, 0u, f);
+    else
+        hipLaunchKernelGGL(fast_count_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, f);
 }
 
 }  // namespace fast

@@ -77,8 +77,13 @@ struct LookupOut {
     int32_t* batch;
 };
 bool fast_lookup_fuses(const VerifyArgs& a);
+// Optional HIP events that bound the count kernel's execution (the launch's start and stop
+// events, for timing that kernel on its own); null: none.
+struct CountEvents {
+    hipEvent_t before, after;
+};
 int fast_verify_cache_lookup(const VerifyArgs& a, const CacheArgs& c, const LookupOut& l, void* ws, size_t ws_bytes,
-                             hipStream_t stream);
+                             hipStream_t stream, const CountEvents* ev = nullptr);
 
 }  // namespace fast
 }  // namespace sv

@@ -51,7 +51,7 @@ bool fast_fuzzy_applies(const VerifyArgs& a) {
 }
 
 static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t ws_bytes, hipStream_t stream,
-                       const LookupOut* lk = nullptr) {
+                       const LookupOut* lk = nullptr, const CountEvents* ev = nullptr) {
     const FastPlan p = fast_plan(a.B, a.K, a.V);
     if (ws_bytes < p.ws_bytes) return SPEC_EWORKSPACE;
     FastArgs f;
@@ -71,7 +71,7 @@ static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t
     f.out_slot = lk ? lk->slot : nullptr;
     f.out_hit = lk ? lk->hit : nullptr;
     f.out_batch = lk ? lk->batch : nullptr;
-    launch_count(f, p.grid, stream);
+    launch_count(f, p.grid, stream, ev ? ev->before : nullptr, ev ? ev->after : nullptr);
     if (a.tau) launch_diverge(f, p.grid_diverge, stream);
     launch_resolve(f, p.grid_resolve, stream);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
@@ -100,8 +100,8 @@ bool fast_lookup_fuses(const VerifyArgs& a) {
 }
 
 int fast_verify_cache_lookup(const VerifyArgs& a, const CacheArgs& c, const LookupOut& l, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
-    return launch_fast(a, &c, ws, ws_bytes, stream, &l);
+                             hipStream_t stream, const CountEvents* ev) {
+    return launch_fast(a, &c, ws, ws_bytes, stream, &l, ev);
 }
 
 }  // namespace fast

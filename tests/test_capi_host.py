@@ -160,3 +160,13 @@ def test_read_ceiling_argument_errors():
     assert L.spec_read_ceiling(fake, 0, fake, None) == capi.SPEC_EINVAL
     assert L.spec_read_ceiling(fake, 24, fake, None) == capi.SPEC_EINVAL                       # not a multiple of 16
     assert L.spec_read_ceiling(ctypes.c_void_p((1 << 20) + 8), 32, fake, None) == capi.SPEC_EINVAL  # unaligned
+
+
+def test_timed_lookup_requires_both_events():
+    # the measurement helper checks its events before any other argument or launch
+    L = capi.load().cdll
+    fake = ctypes.c_void_p(1 << 20)
+    args = [fake, fake, capi.SPEC_BF16, 16, 5, 128256, fake, 4, ctypes.c_float(0.3), fake, 1, 0, 0, 32, 0.7, 1.0, None,
+            fake, fake, None, None, fake, fake, fake, None, fake, 1 << 30, None]
+    assert L.saguaro_verify_cache_lookup_timed(*args, None, fake) == capi.SPEC_EINVAL
+    assert L.saguaro_verify_cache_lookup_timed(*args, fake, None) == capi.SPEC_EINVAL
