@@ -642,7 +642,8 @@ __device__ __forceinline__ void decide_packed(const FastArgs& f, int b, uint64_t
     for (int j = 0; j < K && j <= k; ++j)
         if ((word >> (kCountBits + kCodeBits * j)) & 64u) outside = kStOutside;
     ReqFast* R = reinterpret_cast<ReqFast*>(f.ws + f.L.reqs) + b;
-    const uint32_t place = (uint32_t)ldnt(&R->pad);  // set by a unit whose slices were misplaced
+    // set by a unit whose slices were misplaced (which also sends the request to the general path)
+    const uint32_t place = any_fb ? (uint32_t)ldnt(&R->pad) : 0u;
     int mode = 0, t = -1, kk = 0;
     uint32_t status;
     if (any_fb) {
@@ -701,7 +702,8 @@ __device__ __forceinline__ void decide_request(const FastArgs& f, int b) {
     if (k < 0) k = K;
     const uint32_t outside = wave_or((lane < K && lane <= k) ? (st & kStOutside) : 0u);
     ReqFast* R = reinterpret_cast<ReqFast*>(f.ws + f.L.reqs) + b;
-    const uint32_t place = (uint32_t)ldnt(&R->pad);  // set by a unit whose slices were misplaced
+    // set by a unit whose slices were misplaced (which also sends the request to the general path)
+    const uint32_t place = any_fb ? (uint32_t)ldnt(&R->pad) : 0u;
     int mode = 0, t = -1, kk = 0;
     uint32_t status;
     if (any_fb) {
@@ -740,6 +742,10 @@ __device__ __forceinline__ void decide_request(const FastArgs& f, int b) {
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void fast_count_kernel(FastArgs f) {
     __shared__ CountSmem sm;
     const VerifyArgs& a = f.a;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && f.lookup && f.out_batch) {
+        f.out_batch[0] = 0;  // the fused lookup's batch hit count and all-hit flag, which the
+        f.out_batch[1] = 1;  // resolve kernel's requests add into
+    }
     const Place P = place_of(f);
     if (P.b >= a.B) return;
     const int j = P.j, slice = P.slice, unit = P.unit;

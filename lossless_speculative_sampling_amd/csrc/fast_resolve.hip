@@ -490,9 +490,7 @@ __device__ __forceinline__ void scan_block(ResSmem& sm, double w, int col, doubl
 
 // The outcome-cache lookup of request b's verified outcome (k, t*), fused into this kernel
 // (saguaro_cache_lookup mode 0; SSD reading notes, section 7.1): the slot of t* in the cache's
-// depth-k list, or a miss.  The batch's hit count and all-hit flag come from one counter of
-// every request's (hit, arrival), added at system scope because the requests' workgroups run
-// on every XCD; the last request writes them and clears the counter.  One thread.
+// depth-k list, or a miss, added into the batch's hit count and all-hit flag.  One thread.
 // The first eight entries of request b's depth-k cache list (-1 past the list), loaded ahead.
 struct LookupHead {
     int32_t v[8];
@@ -528,16 +526,11 @@ __device__ __forceinline__ void lookup_request(const FastArgs& f, int b, int k, 
     }
     f.out_slot[b] = res;
     f.out_hit[b] = res >= 0 ? 1 : 0;
-    uint64_t* bc = reinterpret_cast<uint64_t*>(f.ws + f.L.batch_ctr);
-    const uint64_t add = 1ull | ((uint64_t)(res >= 0 ? 1 : 0) << 32);
-    const uint64_t now = __hip_atomic_fetch_add(bc, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) + add;
-    if ((uint32_t)now == (uint32_t)a.B) {
-        const int hits = (int)(now >> 32);
-        if (f.out_batch) {
-            f.out_batch[0] = hits;
-            f.out_batch[1] = hits == a.B ? 1 : 0;
-        }
-        __hip_atomic_store(bc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);  // ready for the next call
+    // the batch's hit count and all-hit flag, which the count kernel set to {0, 1}: added into at
+    // system scope (the requests' workgroups run on every XCD), results unused (no round trip)
+    if (f.out_batch) {
+        (void)__hip_atomic_fetch_add(&f.out_batch[0], res >= 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (res < 0) (void)__hip_atomic_fetch_and(&f.out_batch[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
