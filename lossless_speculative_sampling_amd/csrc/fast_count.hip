@@ -3,6 +3,8 @@
 // value in LDS and publishes a compact summary for the resolve kernel.
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "fast_settle.h"
 
 namespace sv {
@@ -748,6 +750,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     }
     const Place P = place_of(f);
     if (P.b >= a.B) return;
+    // when the whole grid is resident at once, slices issue ahead of the settle steps that
+    // share their CU (see the settle below)
+    if (f.slice_prio) __builtin_amdgcn_s_setprio(1);
     const int j = P.j, slice = P.slice, unit = P.unit;
     const int c0 = slice * kSliceCols;
     // the draft row of position j: verified (j < K) or, at the bonus position, only listed for
@@ -842,6 +847,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     }
     __syncthreads();
     if (!sm.last) return;
+    // The settling workgroup is the unit's last slice to arrive.  With the whole grid resident
+    // (one round of workgroups), the call ends with the last unit's settle, which starts when
+    // that unit's last slice arrives: slices then issue ahead of settles, so the last ones
+    // arrive sooner (measured on the B = 16, K = 5, V = 128256 call: 58.9 -> 57.0 us).  Over
+    // several rounds the work is throughput-bound and a slower settle holds its slot longer
+    // (measured 4% slower on 512 chains at V = 151936), so there all waves keep one priority.
+    if (f.slice_prio) __builtin_amdgcn_s_setprio(0);
     settle_unit(f, sm, P, prm, param_ok, two, s_tok, tok_ok);
 
     // ---- request rendezvous: the last unit of the request decides k ----
@@ -869,6 +881,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
     }
     __syncthreads();
     if (sm.last) decide_request(f, P.b);
+}
+
+int count_resident() {
+    // per device, worked out once (0 until then; a failed query counts as not resident)
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fast_count_kernel, kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 || cus <= 0)
+        return 0;
+    v = per_cu * cus;
+    cached[dev].store(v, std::memory_order_relaxed);
+    return v;
 }
 
 void launch_count(const FastArgs& f, int grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {

@@ -53,6 +53,7 @@ struct FastPlan {
     int grid;        // workgroups of the count kernel
     int grid_resolve;// workgroups of the resolve kernel
     int halves;      // resolve workgroups per slice of the residual (2: each sums half the chunks)
+    int slice_prio;  // the count grid is resident at once (one round of workgroups)
     int grid_diverge;// workgroups of the divergence kernel (fuzzy acceptance)
     size_t ws_bytes; // fast workspace bytes
 };

@@ -31,6 +31,7 @@ FastPlan fast_plan(int B, int K, int V) {
     p.halves = (two_grid <= resolve_resident() || K + 1 > p.nS) ? 2 : 1;
     p.grid_resolve = p.halves == 2 ? two_grid : kXcd * reqs_per_xcd * max(p.nS, K + 1);
     p.grid_diverge = kXcd * reqs_per_xcd * p.nS * K;               // one per slice of every drafted position
+    p.slice_prio = p.grid <= count_resident() ? 1 : 0;
     p.ws_bytes = layout(B, p.units, p.nS).total;
     return p;
 }
@@ -58,6 +59,7 @@ static int launch_fast(const VerifyArgs& a, const CacheArgs* c, void* ws, size_t
     f.a = a;
     f.nS = p.nS;
     f.halves = p.halves;
+    f.slice_prio = p.slice_prio;
     f.units = p.units;
     f.ws = static_cast<char*>(ws);
     f.L = layout(a.B, p.units, p.nS);
