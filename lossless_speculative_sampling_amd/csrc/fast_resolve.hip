@@ -289,6 +289,61 @@ __device__ __forceinline__ void group_entries(ResSmem& sm, bool two, const RowTa
     }
 }
 
+// The table entry of one bin of row r as this slice sees it (the formula of group_entries), with
+// the tie roles of an owned cut key or set boundary.
+__device__ __forceinline__ void bin_entry(ResSmem& sm, int r, const RowTab& t, int bin, double e) {
+    const uint32_t key = bin_key(bin);
+    const bool real = bin / kGroup != kZeroGroup;  // (zero never reaches its bins)
+    double v = 0.0;
+    if (key >= t.klow && key <= t.kmax && (key > t.kk || t.keep_k) && (key > t.kp || t.keep_p)) {
+        const double pv = e * t.inv_S;
+        v = pv;
+        if (r == 1) {
+            const bool in_set = t.set_on && e > 0.0 && (key > t.kF || (key == t.kF && t.keep_F));
+            v = (pv * (in_set ? t.C : 1.0)) * t.inv_Z;
+        }
+        if (real && (key == t.own_F || key == t.own_k || key == t.own_p)) {
+            const uint32_t off = 8u * (uint32_t)(kHistLead + bin);
+            if (key == t.own_F) sm.tie[r][0] = TieRole{off, t.idF, pv * t.inv_Z};
+            if (key == t.own_k) sm.tie[r][1] = TieRole{off, 0, 0.0};
+            if (key == t.own_p) sm.tie[r][2] = TieRole{off, 0, 0.0};
+        }
+    }
+    sm.u.tab[r][kHistLead + bin] = v;
+}
+
+// The residual's tables from the slice's own occupied bins: the (bin, count) entries the count
+// kernel published for it (ent0, ent1: entries t % 256 and t % 256 + 256 of row t / 256, loaded
+// with the slice's columns; n_ent: that row's entry count).  Every element of the slice falls in
+// one of them (or is a value outside the bins, which the padding words' markers send to the exact
+// formula), so no other entry is read: one exp per occupied bin instead of one per bin of every
+// group the slice holds between the cuts and the maximum.
+constexpr int kHalf = kThreads / 2;  // a row's share of the workgroup
+__device__ __forceinline__ void sparse_tables(ResSmem& sm, bool two, int slice, const RowPart* pr, uint32_t n_ent,
+                                              uint32_t ent0, uint32_t ent1) {
+    const int r = (int)threadIdx.x / kHalf, i = (int)threadIdx.x % kHalf;
+    const int ownerF = (two && sm.rf[1].nS > 0) ? sm.rf[1].idF / kSliceCols : -1;
+    if (r == 0 || two) {
+        const RowTab t = row_tab(sm, r, slice, ownerF);
+        const float m = sm.rf[r].m;
+        const double invT = sm.rf[0].invT;
+        const int n = (int)min(n_ent, (uint32_t)kBins);
+        if (i < n) bin_entry(sm, r, t, (int)(ent0 >> 16), mass_of(key16_value(bin_key((int)(ent0 >> 16))), m, invT));
+        if (i + kHalf < n)
+            bin_entry(sm, r, t, (int)(ent1 >> 16), mass_of(key16_value(bin_key((int)(ent1 >> 16))), m, invT));
+        for (int x = i + 2 * kHalf; x < n; x += kHalf) {  // (rare: over 512 occupied bins)
+            const int bin = (int)(ldnt(&pr->ent[x]) >> 16);
+            bin_entry(sm, r, t, bin, mass_of(key16_value(bin_key(bin)), m, invT));
+        }
+    }
+    // padding words: values outside the exact bins
+    if ((int)threadIdx.x < (two ? 4 : 2)) {
+        const int rr = threadIdx.x >> 1;
+        const double v = (sm.flags[rr] & 4u) ? (rr == 0 ? kMarkQ : kMarkP) : 0.0;
+        sm.u.tab[rr][(threadIdx.x & 1) ? kHistLead + kBins : kHistLead - 1] = v;
+    }
+}
+
 // Builds both tables: the listed groups two per wave and step (independent exp chains; rows
 // with the same maximum share their exps), then the zero groups and the padding words.  The
 // masses are exp((z - m) / T) with each row's own maximum, as final_prob forms them.
@@ -809,6 +864,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     u32x4 vq[kLoads], vp[kLoads];
     load_slice(trow, c0, a.V, vq);
     load_slice(two ? drow : trow, c0, a.V, vp);
+    // the slice's occupied bins of each row (thread t: row t / 256, entries t % 256 and t % 256 + 256;
+    // within the record's entry array whatever the count, which is checked where they are used)
+    const RowPart* pr = part_of(f, unit, slice, (int)threadIdx.x / kHalf);
+    const uint32_t n_ent = ldnt(&pr->n_ent);
+    const uint32_t ent0 = ldnt(&pr->ent[threadIdx.x % kHalf]);
+    const uint32_t ent1 = ldnt(&pr->ent[threadIdx.x % kHalf + kHalf]);
     // the record into LDS; without a draft row its cuts keep everything and its flags are 0
     if (rec_slot >= 0) {
         if (rec_slot < kWCut) {
@@ -832,10 +893,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         sm.inv[r][0] = 1.0 / sm.rf[r].S;
         sm.inv[r][1] = 1.0 / sm.rf[r].Z;
     }
-    if (threadIdx.x >= kWave && threadIdx.x < 2 * kWave) table_groups(sm, two, true);
-    __syncthreads();  // 1 / S and 1 / Z, the group list
+    __syncthreads();  // 1 / S and 1 / Z
     // the tables need no column of the slice: they are built while its loads are in flight
-    build_tables(sm, two, slice);
+    sparse_tables(sm, two, slice, pr, n_ent, ent0, ent1);
     // this slice's id cut at each cut key; the owner of a histogram cut publishes its id for
     // the finaliser (explicit cuts and no cut come from slice 0)
     slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);
