@@ -861,15 +861,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     }
     // (without a draft row the second set re-reads the target and goes unused: unconditional
     // loads keep the waits above exact)
-    u32x4 vq[kLoads], vp[kLoads];
-    load_slice(trow, c0, a.V, vq);
-    load_slice(two ? drow : trow, c0, a.V, vp);
     // the slice's occupied bins of each row (thread t: row t / 256, entries t % 256 and t % 256 + 256;
-    // within the record's entry array whatever the count, which is checked where they are used)
+    // within the record's entry array whatever the count, which is checked where they are used),
+    // issued ahead of the columns: loads complete in order, so the tables wait only for these
     const RowPart* pr = part_of(f, unit, slice, (int)threadIdx.x / kHalf);
     const uint32_t n_ent = ldnt(&pr->n_ent);
     const uint32_t ent0 = ldnt(&pr->ent[threadIdx.x % kHalf]);
     const uint32_t ent1 = ldnt(&pr->ent[threadIdx.x % kHalf + kHalf]);
+    u32x4 vq[kLoads], vp[kLoads];
+    load_slice(trow, c0, a.V, vq);
+    load_slice(two ? drow : trow, c0, a.V, vp);
     // the record into LDS; without a draft row its cuts keep everything and its flags are 0
     if (rec_slot >= 0) {
         if (rec_slot < kWCut) {
