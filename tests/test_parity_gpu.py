@@ -306,6 +306,25 @@ def test_fast_ties_and_large_sets():
     check_verify(w, tokens=_oracle_tokens(w), label="fast-ties")
 
 
+# Rows whose values spread over most of the bf16 bins: ~1,500-2,000 distinct values per slice row,
+# so a slice lists more (bin, count) entries than one batch of the settle's merge covers and more
+# than the resolve kernel's first two entries per thread (the loops over the remaining entries)
+@pytest.mark.parametrize("V", [40000, 131072])
+def test_fast_wide_value_spread(V):
+    rng = np.random.default_rng(4242 + V)
+    B, K = 12, 3
+    t = rng.uniform(-30, 30, (B, K + 1, V)).astype(np.float32)
+    t[B // 2:] = 8 * rng.standard_normal((B - B // 2, K + 1, V), dtype=np.float32)
+    d = t[:, :K] + 1.5 * rng.standard_normal((B, K, V), dtype=np.float32)
+    T = rng.choice([0.6, 1.0, 3.0, 20.0], B)
+    tk = rng.choice([0, 700, 5000], B)
+    tp = rng.choice([0.5, 0.95, 1.0], B)
+    w = _work(synth.f32_to_bf16_bits(d), synth.f32_to_bf16_bits(t), synth.BF16, K, T, tk, tp, F=4, C=0.3)
+    o, _ = check_verify(w, tokens=_oracle_tokens(w), label=f"fast-wide V={V}")
+    assert (o.k < K).sum() >= 3  # the residual pass runs for several requests
+    check_verify(w, tokens=rng.integers(0, V, (B, K)), label=f"fast-wide-random V={V}")
+
+
 def test_fast_cut_on_signed_zeros():
     # most of each row is +0 or -0, so the nucleus (and the downweighted set) end inside the
     # zero key, whose elements the owner slice orders one by one
