@@ -788,10 +788,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     if (b >= a.B) return;
     // what the residual needs of every unit (k picks one): row statistics, cuts, this slice's
     // flags and the draw, one 32-bit word per thread, issued before the decision's own load
+    // (the slice's group masks are not among them: its tables come from its entries)
     static_assert(offsetof(UnitFast, rp) == offsetof(UnitFast, rq) + sizeof(RowFinal), "rq, rp adjacent");
     constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
-    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWDraw = kWFlag + 2, kWGrp = kWDraw + 2, kRecWords = 64;
-    static_assert(kWGrp + 4 <= kRecWords, "one unit's words in a wave");
+    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWDraw = kWFlag + 2, kWEnd = kWDraw + 2, kRecWords = 64;
+    static_assert(kWEnd <= kRecWords, "one unit's words in a wave");
     const bool pre = (a.K + 1) * kRecWords <= kThreads;  // otherwise loaded once k is known
     const int pj = (int)threadIdx.x / kRecWords, pw = (int)threadIdx.x % kRecWords;
     uint32_t pre_word = 0u;
@@ -802,8 +803,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         if (pw < kWCut) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->rq) + pw);
         else if (pw < kWFlag) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->cut[0][0]) + (pw - kWCut));
         else if (pw < kWDraw) pre_word = ldnt(&part_of(f, uj, wslice, pw - kWFlag)->flags);
-        else if (pw < kWGrp) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->u_res) + (pw - kWDraw));
-        else if (pw < kWGrp + 4) pre_word = ldnt(&part_of(f, uj, wslice, (pw - kWGrp) >> 1)->groups[(pw - kWGrp) & 1]);
+        else if (pw < kWEnd) pre_word = ldnt(reinterpret_cast<const uint32_t*>(&Uj->u_res) + (pw - kWDraw));
     }
     // the request's decision and this unit's cache flag, loaded together
     static_assert(sizeof(ReqFast) == 16, "one 16-byte record");
@@ -850,14 +850,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     uint32_t rec_word = pre_word;
     int rec_slot = pj == k ? pw : -1;
     if (!pre) {
-        rec_slot = (int)threadIdx.x < kWGrp + 4 ? (int)threadIdx.x : -1;
+        rec_slot = (int)threadIdx.x < kWEnd ? (int)threadIdx.x : -1;
         const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + unit;
         const int x = (int)threadIdx.x;
         if (x < kWCut) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->rq) + x);
         else if (x < kWFlag) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + (x - kWCut));
         else if (x < kWDraw) rec_word = ldnt(&part_of(f, unit, slice, x - kWFlag)->flags);
-        else if (x < kWGrp) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->u_res) + (x - kWDraw));
-        else if (x < kWGrp + 4) rec_word = ldnt(&part_of(f, unit, slice, (x - kWGrp) >> 1)->groups[(x - kWGrp) & 1]);
+        else if (x < kWEnd) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->u_res) + (x - kWDraw));
     }
     // (without a draft row the second set re-reads the target and goes unused: unconditional
     // loads keep the waits above exact)
@@ -881,10 +880,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
             reinterpret_cast<uint32_t*>(&sm.cut[0][0])[x] = keep_all ? (x % kCut == 1 ? 0xFFFFFFFFu : 0u) : rec_word;
         } else if (rec_slot < kWDraw) {
             sm.flags[rec_slot - kWFlag] = (rec_slot == kWFlag || two) ? rec_word : 0u;
-        } else if (rec_slot < kWGrp) {
+        } else if (rec_slot < kWEnd) {
             reinterpret_cast<uint32_t*>(&sm.u_res)[rec_slot - kWDraw] = rec_word;
-        } else {
-            sm.grp[(rec_slot - kWGrp) >> 1][(rec_slot - kWGrp) & 1] = rec_word;  // row 1's unread without two
         }
     }
     if (threadIdx.x >= kWave && threadIdx.x < kWave + 6) sm.tie[(threadIdx.x - kWave) / 3][(threadIdx.x - kWave) % 3].off = kNoTie;
