@@ -92,15 +92,14 @@ struct alignas(16) RowPart {  // one slice of one row, written by the count kern
     uint32_t s_bits;    // bf16 bits of the row at the draft token (0 without a token)
     uint32_t n_neginf;
     uint32_t xcc;       // XCD the slice's workgroup ran on
-    uint32_t groups[2]; // bit g (low word first): the slice holds elements in group g of 64 bins
-    uint32_t pad[2];
+    uint32_t pad[4];    // (the candidates start 16-byte aligned)
     uint32_t top_key[kTop];
     int32_t top_id[kTop];
     uint32_t sp_key[kSpecial];
     int32_t sp_id[kSpecial];
     uint32_t ent[kBins];  // occupied bins in ascending order: (bin << 16) | count
 };
-static_assert(offsetof(RowPart, groups) == 32 && offsetof(RowPart, top_key) % 16 == 0, "header: 2 x 16 bytes");
+static_assert(offsetof(RowPart, pad) == 32 && offsetof(RowPart, top_key) % 16 == 0, "header: 2 x 16 bytes");
 static_assert(offsetof(RowPart, ent) % 16 == 0, "entries 16-byte aligned");
 
 struct RowFinal {  // enough to evaluate any element's processed probability

@@ -32,7 +32,6 @@ struct CountSmem {
     uint32_t cnt_s[2];
     uint32_t flags[2];
     uint32_t neginf[2];
-    alignas(8) uint32_t grp[2][2];  // groups of 64 bins the slice holds, per row (low word first)
     int32_t scan[kWaves + 1];
     double redd[kWaves];
     int32_t redi[kWaves];
@@ -328,8 +327,7 @@ __device__ __forceinline__ void local_ranks(CountSmem& sm, bool two, int c0, int
 }
 
 // Places both rows' occupied bins as (bin, count) entries in ascending bin order (returns this
-// thread's exclusive scan word for write_entries) and collects the groups of 64 bins the slice
-// holds; thread t reads bins [6t, 6t + 6).  One workgroup scan of both rows' entry and element
+// thread's exclusive scan word for write_entries); thread t reads bins [6t, 6t + 6).  One workgroup scan of both rows' entry and element
 // counts places every entry and tells each thread how many of the row's binned elements lie
 // above its bins, so for a row listing L > 0 candidates without values outside the bins (fast)
 // the thread holding the L-th element from the top records it as the row's threshold (sm.th_*:
@@ -347,13 +345,6 @@ __device__ __forceinline__ uint32_t scan_entries(CountSmem& sm, bool two, const 
     uint32_t nz[2] = {0u, 0u}, cs[2] = {0u, 0u};
     const int b0 = tid < kPubThreads ? tid * kPer : 0;  // (reads are unconditional, then masked)
     const bool mine = tid < kPubThreads;
-    // groups of 64 bins holding elements: a wave's 6 x 64 bins are exactly groups 6 w .. 6 w + 5,
-    // and a thread's bins lie in group b0 / 64 or the next, below bin `split`
-    static_assert(kWave * kPer == 6 * kGroup, "a wave covers six whole groups");
-    const int bt = tid * kPer;  // (past the bins for tid >= kPubThreads: gw stays 0 there)
-    const int gl = (bt >> 6) - 6 * wave;
-    const int split = (((bt >> 6) + 1) << 6) - bt;
-    uint32_t gw[2] = {0u, 0u};
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -362,14 +353,7 @@ __device__ __forceinline__ uint32_t scan_entries(CountSmem& sm, bool two, const 
             const uint32_t c = (r < rows && mine) ? c0 : 0u;
             cs[r] += c;
             nz[r] += c != 0u ? 1u : 0u;
-            gw[r] |= c != 0u ? (i < split ? 1u : 2u) : 0u;
         }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const uint32_t w6 = wave_or(gw[r] << gl);  // bit x: group 6 w + x
-        if (lane == 0 && r < rows && w6 != 0u)
-            atomicOr(reinterpret_cast<unsigned long long*>(&sm.grp[r][0]), (unsigned long long)w6 << (6 * wave));
-    }
     // entries (12 bits) and elements (15 bits) of both rows in one 64-bit scan (one barrier)
     const uint64_t v = (uint64_t)nz[0] | ((uint64_t)cs[0] << 12) | ((uint64_t)nz[1] << 27) | ((uint64_t)cs[1] << 39);
     uint64_t exc;
@@ -454,8 +438,6 @@ __device__ __forceinline__ void publish_header(const FastArgs& f, CountSmem& sm,
             const uint32_t flags = (sm.flags[r] & 1u) | ((int)sm.n_sp[r] > kSpecial ? 2u : 0u) | (sm.rare[r] ? 4u : 0u);
             reinterpret_cast<u32x4*>(P)[0] = u32x4{flags, sm.n_ent[r], (uint32_t)nsp, (uint32_t)n_top[r]};
             reinterpret_cast<u32x4*>(P)[1] = u32x4{sm.cnt_s[r], sm.s_bits[r], sm.neginf[r], sm.xcc};
-            P->groups[0] = sm.grp[r][0];
-            P->groups[1] = sm.grp[r][1];
         }
     }
 }
@@ -791,8 +773,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6, 8))
             sm.n_sp[threadIdx.x] = 0;
             sm.flags[threadIdx.x] = 0;
             sm.neginf[threadIdx.x] = 0;
-            sm.grp[threadIdx.x][0] = 0;
-            sm.grp[threadIdx.x][1] = 0;
             sm.cnt_s[threadIdx.x] = 0;
             sm.th_tau[threadIdx.x] = 0u;
             sm.th_need[threadIdx.x] = 0;

@@ -36,13 +36,9 @@ struct ResSmem {
     UnitRec urec;
     RowFinal rf[2];
     double inv[2][2];              // [row][1 / S, 1 / Z]
-    int glist[kGroups];            // groups whose entries need exps, ascending
-    int gcount;
-    uint64_t gzero[2];             // groups wholly below a row's cuts (entries 0)
     TieRole tie[2][3];             // [row][set boundary, top-k tie, top-p tie] this slice decides
     UnitCut cut[2][2];
     uint32_t flags[2];             // this slice's RowPart flags of each row
-    uint32_t grp[2][2];            // this slice's groups of each row (RowPart::groups)
     int eff[2][2];                 // this slice's id cut at each cut key (V-1 all, -1 none)
     uint64_t nth_scan[kWaves][4];  // per-wave match counts of the owned cut keys
     int32_t scan[kWaves + 1];
@@ -185,37 +181,6 @@ constexpr double kMarkQ = 1e300;    // in the target table: (q - p)+ and q becom
 constexpr double kMarkP = -1e300;   // in the draft table: (q - p)+ becomes huge
 constexpr double kMarkSeen = 1e299;
 
-// The groups of 64 bins whose table entries need exps: those between the lower of a row's
-// cuts and its maximum (a compact list, ascending), and per row the groups wholly below its
-// cuts, whose entries are 0.  Groups above a row's maximum hold none of its elements.  With
-// sm.grp loaded (slice_groups), groups the slice holds none of in a row are left out for that
-// row.  (One wave; the caller synchronises.)
-__device__ __forceinline__ void table_groups(ResSmem& sm, bool two, bool slice_groups) {
-    const int lane = threadIdx.x & (kWave - 1);
-    bool need = false, z0 = false, z1 = false;
-    if (lane < kGroups) {
-        const uint32_t glo = bin_key(lane * kGroup), ghi = bin_key(lane * kGroup + kGroup - 1);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (r == 1 && !two) break;
-            const uint32_t gw = sm.grp[r][lane >> 5];
-            if (slice_groups && !((gw >> (lane & 31)) & 1u)) continue;  // none of row r's elements
-            const uint32_t klow = max(sm.cut[r][0].key, sm.cut[r][1].key);
-            const uint32_t kmax = key16(__float_as_uint(sm.rf[r].m) >> 16);
-            if (ghi >= klow && glo <= kmax) need = true;
-            else if (ghi < klow) (r == 0 ? z0 : z1) = true;
-        }
-    }
-    const uint64_t m = __ballot(need);
-    if (need) sm.glist[__popcll(m & ((1ull << lane) - 1ull))] = lane;
-    const uint64_t m0 = __ballot(z0 && !need), m1 = __ballot(z1 && !need);
-    if (lane == 0) {
-        sm.gcount = __popcll(m);
-        sm.gzero[0] = m0;
-        sm.gzero[1] = m1;
-    }
-}
-
 // What the table entries of one row depend on, read once into registers (the entries are
 // written to LDS, so values left in LDS would be re-read after every entry).
 struct RowTab {
@@ -254,46 +219,15 @@ __device__ __forceinline__ RowTab row_tab(const ResSmem& sm, int r, int slice, i
     return t;
 }
 
-// Per-bin values of both rows for this slice: q = e / S, p' = ((e / S) * f) / Z (as
-// final_prob), with every cut key resolved as this slice sees it.  Where this slice decides
-// elements of a bin one by one (it holds the last kept element at a cut key, or the draft
-// row's downweighted-set boundary) the entry holds the value of the earliest elements and a
-// tie role records where and how the later ones differ.  The padding words hold a marker when
-// the slice has values outside the exact bins.
-__device__ __forceinline__ void group_entries(ResSmem& sm, bool two, const RowTab (&rt)[2], int g, const double (&e)[2]) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int bin = g * kGroup + lane;
-    const uint32_t key = bin_key(bin);
-    // zero never reaches its bins (the packed offsets send it to the padding words)
-    const bool real = g != kZeroGroup;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        if (r == 1 && !two) break;
-        const RowTab& t = rt[r];
-        double v = 0.0;
-        if (key >= t.klow && key <= t.kmax && (key > t.kk || t.keep_k) && (key > t.kp || t.keep_p)) {
-            const double pv = e[r] * t.inv_S;
-            v = pv;
-            if (r == 1) {
-                const bool in_set = t.set_on && e[r] > 0.0 && (key > t.kF || (key == t.kF && t.keep_F));
-                v = (pv * (in_set ? t.C : 1.0)) * t.inv_Z;
-            }
-            if (real && (key == t.own_F || key == t.own_k || key == t.own_p)) {
-                const uint32_t off = 8u * (uint32_t)(kHistLead + bin);
-                if (key == t.own_F) sm.tie[r][0] = TieRole{off, t.idF, pv * t.inv_Z};
-                if (key == t.own_k) sm.tie[r][1] = TieRole{off, 0, 0.0};  // threshold: the id cut, below
-                if (key == t.own_p) sm.tie[r][2] = TieRole{off, 0, 0.0};
-            }
-        }
-        sm.u.tab[r][kHistLead + bin] = v;
-    }
-}
-
-// The table entry of one bin of row r as this slice sees it (the formula of group_entries), with
-// the tie roles of an owned cut key or set boundary.
+// The table entry of one bin of row r as this slice sees it: q = e / S, p' = ((e / S) * f) / Z
+// (as final_prob), with every cut key resolved as this slice sees it.  Where this slice decides
+// elements of the bin one by one (it holds the last kept element at a cut key, or the draft
+// row's downweighted-set boundary) the entry holds the value of the earliest elements and a tie
+// role records where and how the later ones differ.
 __device__ __forceinline__ void bin_entry(ResSmem& sm, int r, const RowTab& t, int bin, double e) {
     const uint32_t key = bin_key(bin);
-    const bool real = bin / kGroup != kZeroGroup;  // (zero never reaches its bins)
+    // zero never reaches its group's bins (the packed offsets send it to the padding words)
+    const bool real = bin / kGroup != kZeroGroup;
     double v = 0.0;
     if (key >= t.klow && key <= t.kmax && (key > t.kk || t.keep_k) && (key > t.kp || t.keep_p)) {
         const double pv = e * t.inv_S;
@@ -319,6 +253,19 @@ __device__ __forceinline__ void bin_entry(ResSmem& sm, int r, const RowTab& t, i
 // formula), so no other entry is read: one exp per occupied bin instead of one per bin of every
 // group the slice holds between the cuts and the maximum.
 constexpr int kHalf = kThreads / 2;  // a row's share of the workgroup
+
+struct SliceEnt {     // this thread's share of the slice's entries (see sparse_tables)
+    const RowPart* pr;  // the record of row threadIdx.x / kHalf
+    uint32_t n, e0, e1; // that row's entry count; entries threadIdx.x % kHalf and that + kHalf
+};
+__device__ __forceinline__ SliceEnt load_slice_ent(const FastArgs& f, int unit, int slice) {
+    SliceEnt e;
+    e.pr = part_of(f, unit, slice, (int)threadIdx.x / kHalf);
+    e.n = ldnt(&e.pr->n_ent);
+    e.e0 = ldnt(&e.pr->ent[threadIdx.x % kHalf]);
+    e.e1 = ldnt(&e.pr->ent[threadIdx.x % kHalf + kHalf]);
+    return e;
+}
 __device__ __forceinline__ void sparse_tables(ResSmem& sm, bool two, int slice, const RowPart* pr, uint32_t n_ent,
                                               uint32_t ent0, uint32_t ent1) {
     const int r = (int)threadIdx.x / kHalf, i = (int)threadIdx.x % kHalf;
@@ -341,50 +288,6 @@ __device__ __forceinline__ void sparse_tables(ResSmem& sm, bool two, int slice, 
         const int rr = threadIdx.x >> 1;
         const double v = (sm.flags[rr] & 4u) ? (rr == 0 ? kMarkQ : kMarkP) : 0.0;
         sm.u.tab[rr][(threadIdx.x & 1) ? kHistLead + kBins : kHistLead - 1] = v;
-    }
-}
-
-// Builds both tables: the listed groups two per wave and step (independent exp chains; rows
-// with the same maximum share their exps), then the zero groups and the padding words.  The
-// masses are exp((z - m) / T) with each row's own maximum, as final_prob forms them.
-__device__ __forceinline__ void build_tables(ResSmem& sm, bool two, int slice) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int ownerF = (two && sm.rf[1].nS > 0) ? sm.rf[1].idF / kSliceCols : -1;
-    const RowTab rt[2] = {row_tab(sm, 0, slice, ownerF), row_tab(sm, 1, slice, ownerF)};
-    const int n = sm.gcount;
-    const float m0 = sm.rf[0].m, m1 = sm.rf[1].m;
-    const bool share = two && m0 == m1;
-    const double invT = sm.rf[0].invT;
-    for (int i = wave; i < n; i += 2 * kWaves) {
-        const bool hb = i + kWaves < n;
-        const int ga = sm.glist[i], gb = hb ? sm.glist[i + kWaves] : ga;
-        const float za = key16_value(bin_key(ga * kGroup + lane)), zb = key16_value(bin_key(gb * kGroup + lane));
-        double ea[2], eb[2];
-        ea[0] = mass_of(za, m0, invT);
-        eb[0] = mass_of(zb, m0, invT);
-        if (share) {
-            ea[1] = ea[0];
-            eb[1] = eb[0];
-        } else if (two) {
-            ea[1] = mass_of(za, m1, invT);
-            eb[1] = mass_of(zb, m1, invT);
-        } else {
-            ea[1] = eb[1] = 0.0;
-        }
-        group_entries(sm, two, rt, ga, ea);
-        if (hb) group_entries(sm, two, rt, gb, eb);
-    }
-    const uint64_t z0 = sm.gzero[0], z1 = two ? sm.gzero[1] : 0ull;
-    for (int g = wave; g < kGroups; g += kWaves) {
-        if ((z0 >> g) & 1ull) sm.u.tab[0][kHistLead + g * kGroup + lane] = 0.0;
-        if ((z1 >> g) & 1ull) sm.u.tab[1][kHistLead + g * kGroup + lane] = 0.0;
-    }
-    // padding words: values outside the exact bins
-    if ((int)threadIdx.x < (two ? 4 : 2)) {
-        const int r = threadIdx.x >> 1;
-        const double v = (sm.flags[r] & 4u) ? (r == 0 ? kMarkQ : kMarkP) : 0.0;
-        sm.u.tab[r][(threadIdx.x & 1) ? kHistLead + kBins : kHistLead - 1] = v;
     }
 }
 
@@ -1044,7 +947,7 @@ struct DivList {
 __device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& sm, int c0, bool two,
                                                   const u32x4 (&vq)[kLoads], const u32x4 (&vp)[kLoads],
                                                   DivList& dl, const LogTab& lt, const uint16_t* trow,
-                                                  const uint16_t* drow) {
+                                                  const uint16_t* drow, const SliceEnt& ent) {
     const double pu = 1.0 / (double)f.a.V;
     const VerifyArgs& a = f.a;
     const char* tq = reinterpret_cast<const char*>(&sm.u.tab[0][0]);
@@ -1104,14 +1007,22 @@ __device__ __forceinline__ double divergence_slice(const FastArgs& f, ResSmem& s
             }
         }
     }
-    // every value an element inside the exact bins reads lies in a listed group (the groups
-    // wholly below a row's cuts hold 0, which stays 0), or is a tie's alternative
+    // every value an element inside the exact bins reads is the entry of one of the slice's own
+    // occupied bins (each listed once per row: every entry turns exactly once; 0 stays 0), or a
+    // tie's alternative
     __syncthreads();
-    const int lane = threadIdx.x & (kWave - 1);
-    for (int i = (int)threadIdx.x / kWave; i < sm.gcount; i += kWaves) {
-        const int idx = kHistLead + sm.glist[i] * kGroup + lane;
-        sm.u.tab[0][idx] = xlog2x_tab(sm.u.tab[0][idx], lt);
-        if (two) sm.u.tab[1][idx] = xlog2x_tab(sm.u.tab[1][idx], lt);
+    {
+        const int r = (int)threadIdx.x / kHalf, i = (int)threadIdx.x % kHalf;
+        if (r == 0 || two) {
+            const int n = (int)min(ent.n, (uint32_t)kBins);
+            double* tab = sm.u.tab[r] + kHistLead;
+            if (i < n) tab[ent.e0 >> 16] = xlog2x_tab(tab[ent.e0 >> 16], lt);
+            if (i + kHalf < n) tab[ent.e1 >> 16] = xlog2x_tab(tab[ent.e1 >> 16], lt);
+            for (int x = i + 2 * kHalf; x < n; x += kHalf) {  // (rare: over 512 occupied bins)
+                const uint32_t bin = ldnt(&ent.pr->ent[x]) >> 16;
+                tab[bin] = xlog2x_tab(tab[bin], lt);
+            }
+        }
     }
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
@@ -1199,19 +1110,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int unit = b * (a.K + 1) + j;
     const bool two = !f.uniform;
     constexpr int kRf = (int)(sizeof(RowFinal) / 4), kCut = (int)(sizeof(UnitCut) / 4);
-    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWGrp = kWFlag + 2, kWEnd = kWGrp + 4;
+    constexpr int kWCut = 2 * kRf, kWFlag = kWCut + 4 * kCut, kWEnd = kWFlag + 2;
     static_assert(kWEnd <= kThreads, "one record word per thread");
     const UnitFast* U = reinterpret_cast<const UnitFast*>(f.ws + f.L.units) + unit;
     const int t = (int)threadIdx.x;
     uint32_t rec_word = 0u;
     if (t < kWCut) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->rq) + t);
     else if (t < kWFlag) rec_word = ldnt(reinterpret_cast<const uint32_t*>(&U->cut[0][0]) + (t - kWCut));
-    else if (t < kWGrp) rec_word = ldnt(&part_of(f, unit, slice, t - kWFlag)->flags);
-    else if (t < kWEnd && (t < kWGrp + 2 || two)) rec_word = ldnt(&part_of(f, unit, slice, (t - kWGrp) >> 1)->groups[(t - kWGrp) & 1]);
+    else if (t < kWEnd) rec_word = ldnt(&part_of(f, unit, slice, t - kWFlag)->flags);
     const int c0 = slice * kSliceCols;
     const size_t stride = (size_t)a.V;
     const uint16_t* trow = static_cast<const uint16_t*>(a.target) + ((size_t)b * (a.K + 1) + j) * stride;
     const uint16_t* drow = two ? static_cast<const uint16_t*>(a.draft) + ((size_t)b * a.draft_rows + j) * stride : trow;
+    // the slice's occupied bins, ahead of its columns (the tables wait only for them)
+    const SliceEnt ent = load_slice_ent(f, unit, slice);
     u32x4 vq[kLoads], vp[kLoads];
     load_slice(trow, c0, a.V, vq);
     load_slice(drow, c0, a.V, vp);
@@ -1222,10 +1134,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         const int y = t - kWCut;
         const bool keep_all = !two && y >= 2 * kCut;  // no draft row: UnitCut{0, -1, 0, 0}
         reinterpret_cast<uint32_t*>(&sm.cut[0][0])[y] = keep_all ? (y % kCut == 1 ? 0xFFFFFFFFu : 0u) : rec_word;
-    } else if (t < kWGrp) {
-        sm.flags[t - kWFlag] = (t == kWFlag || two) ? rec_word : 0u;
     } else if (t < kWEnd) {
-        sm.grp[(t - kWGrp) >> 1][(t - kWGrp) & 1] = rec_word;
+        sm.flags[t - kWFlag] = (t == kWFlag || two) ? rec_word : 0u;
     }
     if (t >= kWave && t < kWave + 6) sm.tie[(t - kWave) / 3][(t - kWave) % 3].off = kNoTie;
     __syncthreads();
@@ -1233,12 +1143,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         sm.inv[t][0] = 1.0 / sm.rf[t].S;
         sm.inv[t][1] = 1.0 / sm.rf[t].Z;
     }
-    if (t >= kWave && t < 2 * kWave) table_groups(sm, two, true);
-    __syncthreads();
-    build_tables(sm, two, slice);
+    __syncthreads();  // 1 / S and 1 / Z
+    // the tables need no column of the slice: they are built while its loads are in flight
+    sparse_tables(sm, two, slice, ent.pr, ent.n, ent.e0, ent.e1);
     slice_id_cuts(sm, vq, vp, c0, a.V, slice, two);
     __syncthreads();
-    const double part = block_sum<double>(divergence_slice(f, sm, c0, two, vq, vp, dl, lt, trow, drow), sm.redd);
+    const double part = block_sum<double>(divergence_slice(f, sm, c0, two, vq, vp, dl, lt, trow, drow, ent), sm.redd);
     double* parts = reinterpret_cast<double*>(f.ws + f.L.div);
     if (t == 0) parts[(size_t)unit * f.nS + slice] = part;
     // the position's arrival (its nS workgroups), then the request's (its K positions)
