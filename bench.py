@@ -9,7 +9,7 @@ outcomes in that cache.  Inputs are synthetic (Zipf-shaped rows, see
 lossless_speculative_sampling_amd/synth.py) and already resident in HBM; R copies of the batch
 totalling more than twice the 256 MB Infinity Cache are rotated so reads come from HBM.
 
-Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus N > 1 is refused: the path runs on one GPU (no multi-GPU path).
 """
 from __future__ import annotations
 
@@ -448,7 +448,7 @@ def main():
                     help="run only a plain device copy of known size (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        print("bench.py: the path runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
